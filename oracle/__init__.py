@@ -1,0 +1,137 @@
+"""fp64 CPU oracle for chunkwise causal linear attention — TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import this
+package.  It shares no code with the HIP library: the recurrence itself is plain C
+(``linattn_oracle.c``, built with gcc), and ``forms.py`` holds two independent fp64
+restatements used to pin it (brute-force masked attention and the parallel form).
+
+Pins (see tests/test_oracle_pins.py): brute force on tiny inputs, the parallel form,
+gamma = 1 reducing to plain (Katharopoulos) linear attention, closed forms, a hand-worked
+fixture under tests/golden/, split/resume, chained single steps and linearity.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "linattn_oracle.c")
+_LIB = os.path.join(_HERE, "liblinattn_oracle.so")
+
+DECAY_CODES = {"none": 0, "gamma": 1, "gate": 2, "token": 3}
+PHI_ELU1, NORMALIZE = 1, 2
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (fp64, OpenMP, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+                        "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", _SRC, "-o", tmp,
+                        "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        p, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_fwd.argtypes = [p, p, p, c_int, p, c_int, p, p, p, i64, p,
+                                   i64, i64, i64, i64, i64, c_int, c_int]
+        lib.oracle_fwd.restype = c_int
+        lib.oracle_step.argtypes = [p, p, p, c_int, p, c_int, p, p, i64, i64, i64, i64,
+                                    c_int, c_int]
+        lib.oracle_step.restype = c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(x: np.ndarray) -> int:
+    if x.dtype == np.uint16:
+        return 1
+    if x.dtype == np.float32:
+        return 0
+    raise TypeError("oracle inputs are fp32 arrays or bf16 bit patterns (uint16)")
+
+
+def fwd(q, k, v, decay=None, decay_kind="none", init=None, *, phi_elu1=False,
+        normalize=False, rows: Optional[Sequence[int]] = None, want_out=True,
+        want_final=True, nthreads=0):
+    """Run the recurrence.  q, k: [B,H,T,dk]; v: [B,H,T,dv] (fp32 or uint16 bf16 bits).
+
+    decay: gamma [H], gate [B,H,T,dk] or per-token [B,H,T] fp32 (per decay_kind).
+    init: [B,H,dk,dv+n] (fp32 or fp64) or None.  rows: token indices to record.
+    Returns (out fp64 [B,H,len(rows) or T,dv] or None, final fp64 [B,H,dk,dv+n] or None).
+    """
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("q, k, v must share one dtype")
+    B, H, T, dk = q.shape
+    dv = v.shape[3]
+    if k.shape != q.shape or v.shape[:3] != (B, H, T):
+        raise ValueError("shape mismatch")
+    kind = DECAY_CODES[decay_kind]
+    dec = None if decay is None else np.ascontiguousarray(decay, dtype=np.float32)
+    if kind and dec is None:
+        raise ValueError("decay values missing")
+    ncol = dv + (1 if normalize else 0)
+    ini = None
+    if init is not None:
+        ini = np.ascontiguousarray(init, dtype=np.float64)
+        if ini.shape != (B, H, dk, ncol):
+            raise ValueError(f"init must be {(B, H, dk, ncol)}")
+    rows_arr = None
+    nrows = T
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        if np.any(np.diff(rows_arr) <= 0) or (rows_arr.size and (rows_arr[0] < 0 or rows_arr[-1] >= T)):
+            raise ValueError("rows must be ascending token indices")
+        nrows = rows_arr.size
+    out = np.empty((B, H, nrows, dv), dtype=np.float64) if want_out else None
+    fin = np.empty((B, H, dk, ncol), dtype=np.float64) if want_final else None
+    flags = (PHI_ELU1 if phi_elu1 else 0) | (NORMALIZE if normalize else 0)
+    rc = _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(dec), kind, _ptr(ini),
+                            _ptr(out), _ptr(rows_arr), nrows, _ptr(fin), B, H, T, dk, dv,
+                            flags, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_fwd failed")
+    return out, fin
+
+
+def step(q, k, v, state, decay=None, decay_kind="none", *, phi_elu1=False, normalize=False,
+         nthreads=0):
+    """One decoding step.  q, k: [B,H,dk]; v: [B,H,dv]; decay: gamma [H], gate [B,H,dk],
+    per-token [B,H]; state fp64 [B,H,dk,dv+n] (updated in place).  Returns out [B,H,dv]."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dt = _dtype_code(q)
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    if state.dtype != np.float64 or not state.flags.c_contiguous:
+        raise TypeError("state must be a contiguous fp64 array")
+    dec = None if decay is None else np.ascontiguousarray(decay, dtype=np.float32)
+    out = np.empty((B, H, dv), dtype=np.float64)
+    flags = (PHI_ELU1 if phi_elu1 else 0) | (NORMALIZE if normalize else 0)
+    rc = _load().oracle_step(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(dec),
+                             DECAY_CODES[decay_kind], _ptr(state), _ptr(out), B, H, dk, dv,
+                             flags, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_step failed")
+    return out

@@ -1,0 +1,181 @@
+"""Seeded synthetic workloads for chunkwise causal linear attention.
+
+This module only draws random inputs and describes workload shapes. It holds none of
+the method's arithmetic, so both the fp64 oracle (under ``oracle/``) and the HIP path
+(``chunkwise_causal_linear_amd``) can consume exactly the same tensors.
+
+The five named workloads mirror the shapes the source pages time or describe:
+  * plain causal linear attention with the elu+1 feature map and the z normaliser
+    (textbook chapter 1.6, "linear attention" section and its parallel/recurrent code);
+  * RetNet-style retention at hidden 1024 with 4 heads, batch 32, length 2048 (the
+    fla-org getting-started guide's MultiScaleRetention example);
+  * decayed and GLA-gated attention at batch 8, head dim 128, length 8192 / 16384 (the
+    Triton fused-kernel blog post's H100 timing paragraph);
+  * a million-token retention sequence (the FLA long-sequence blog post, ">1M tokens").
+
+Every tensor is drawn from numpy's PCG64 with a fixed seed, one independent child
+stream per (batch, head) pair (``SeedSequence.spawn``), so the result does not depend on
+how many threads generate it. bf16 tensors are stored as raw ``uint16`` bit patterns,
+rounded from fp32 to nearest-even.
+"""
+from __future__ import annotations
+
+import concurrent.futures as _fut
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import numpy as np
+
+DECAY_NONE, DECAY_GAMMA, DECAY_GATE = "none", "gamma", "gate"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    T: int
+    dk: int
+    dv: int
+    chunk: int
+    dtype: str          # "f32" or "bf16" (q, k, v and out)
+    decay: str          # DECAY_NONE | DECAY_GAMMA | DECAY_GATE
+    phi_elu1: bool      # feature map elu(x)+1 on q and k, else identity
+    normalize: bool     # o = S phi(q) / (z^T phi(q))
+    qk_scale: float     # q, k ~ N(0,1) * qk_scale
+    init_sigma: float   # 0 -> no initial state, else fp32 N(0, sigma^2)
+    gamma_exp: str = "" # how gamma_h is formed (documentation only)
+    seed: int = 0
+
+    @property
+    def token_heads(self) -> int:
+        return self.B * self.H * self.T
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+def _gammas_offset(H: int, step: float) -> np.ndarray:
+    """gamma_h = 1 - 2^(-5 - h*step), computed in fp64, rounded once to fp32."""
+    h = np.arange(H, dtype=np.float64)
+    return (1.0 - np.exp2(-5.0 - h * step)).astype(np.float32)
+
+
+WORKLOADS = {
+    "plain_f32": Workload("plain_f32", 1, 1, 256, 64, 64, 64, "f32", DECAY_NONE, True, True,
+                          1.0, 0.0, seed=1001),
+    "retention_d256": Workload("retention_d256", 32, 4, 2048, 256, 256, 64, "bf16", DECAY_GAMMA,
+                               False, False, 1.0 / math.sqrt(256), 0.0,
+                               gamma_exp="1-2^(-5-h)", seed=1002),
+    "decayed_d128": Workload("decayed_d128", 8, 16, 8192, 128, 128, 64, "bf16", DECAY_GAMMA,
+                             False, False, 1.0 / math.sqrt(128), 0.0,
+                             gamma_exp="1-2^(-5-h*8/H)", seed=1003),
+    "gla_d128": Workload("gla_d128", 8, 16, 16384, 128, 128, 64, "bf16", DECAY_GATE,
+                         False, False, 1.0 / math.sqrt(128), 0.0, seed=1004),
+    "long_retention": Workload("long_retention", 1, 8, 1 << 20, 128, 128, 128, "bf16",
+                               DECAY_GAMMA, False, False, 1.0 / math.sqrt(128), 0.1,
+                               gamma_exp="1-2^(-5-h)", seed=1005),
+}
+# The headline throughput workload.
+HEADLINE = "gla_d128"
+
+
+def gamma_for(w: Workload) -> Optional[np.ndarray]:
+    if w.decay != DECAY_GAMMA:
+        return None
+    if w.gamma_exp == "1-2^(-5-h*8/H)":
+        return _gammas_offset(w.H, 8.0 / w.H)
+    return _gammas_offset(w.H, 1.0)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even); returns the uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _per_head(w: Workload, stream: int, fill):
+    """Run fill(rng, b, h) for every (b, h) with an independent child generator."""
+    ss = np.random.SeedSequence([w.seed, stream])
+    children = ss.spawn(w.B * w.H)
+    jobs = [(b, h, np.random.Generator(np.random.PCG64(children[b * w.H + h])))
+            for b in range(w.B) for h in range(w.H)]
+    if len(jobs) == 1:
+        b, h, g = jobs[0]
+        fill(g, b, h)
+        return
+    with _fut.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(lambda j: fill(j[2], j[0], j[1]), jobs))
+
+
+def _normal_tensor(w: Workload, stream: int, d: int, scale: float, as_bf16: bool) -> np.ndarray:
+    out = np.empty((w.B, w.H, w.T, d), dtype=np.uint16 if as_bf16 else np.float32)
+
+    def fill(g, b, h):
+        x = g.standard_normal((w.T, d), dtype=np.float32)
+        if scale != 1.0:
+            x *= np.float32(scale)
+        out[b, h] = f32_to_bf16_bits(x) if as_bf16 else x
+
+    _per_head(w, stream, fill)
+    return out
+
+
+def _gate_tensor(w: Workload, stream: int) -> np.ndarray:
+    """alpha = sigmoid(x)^(1/16), x ~ N(0,1); evaluated in fp64, rounded once to fp32."""
+    out = np.empty((w.B, w.H, w.T, w.dk), dtype=np.float32)
+
+    def fill(g, b, h):
+        x = g.standard_normal((w.T, w.dk), dtype=np.float64)
+        out[b, h] = np.power(1.0 / (1.0 + np.exp(-x)), 1.0 / 16.0).astype(np.float32)
+
+    _per_head(w, stream, fill)
+    return out
+
+
+def generate(w: Workload) -> dict:
+    """Draw the inputs of workload ``w``.
+
+    Returns numpy arrays in the library's layouts: q, k [B,H,T,dk]; v [B,H,T,dv]
+    (uint16 bf16 bits or float32); 'decay' = gamma [H] fp32, gate [B,H,T,dk] fp32 or
+    None; 'init' = fp32 [B,H,dk,dv+n] or None (n = 1 with the normaliser).
+    Draw order: q, k, v, then the gate or the initial state.
+    """
+    bf = w.dtype == "bf16"
+    q = _normal_tensor(w, 1, w.dk, w.qk_scale, bf)
+    k = _normal_tensor(w, 2, w.dk, w.qk_scale, bf)
+    v = _normal_tensor(w, 3, w.dv, 1.0, bf)
+    if w.decay == DECAY_GATE:
+        decay = _gate_tensor(w, 4)
+    else:
+        decay = gamma_for(w)
+    init = None
+    if w.init_sigma > 0:
+        ncol = w.dv + (1 if w.normalize else 0)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 5])))
+        init = g.standard_normal((w.B, w.H, w.dk, ncol), dtype=np.float32)
+        init *= np.float32(w.init_sigma)
+    return {"q": q, "k": k, "v": v, "decay": decay, "init": init}
+
+
+def small(name: str, **kw) -> Workload:
+    """A named workload shrunk to oracle-friendly sizes (keeps dtype, decay, phi, norm)."""
+    return WORKLOADS[name].with_(**kw)
+
+
+def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of stored inputs (bf16 bits or fp32) to fp64."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
