@@ -1,0 +1,161 @@
+"""Chunkwise causal linear attention for MI355X (gfx950): thin Python binding.
+
+Every step of the computation runs in the HIP library ``lib/libfla_linattn.so``
+(C ABI: include/fla_linattn.h).  This module only marshals torch tensors into
+pointers, sizes and flags, and raises when the library is missing or a call fails.
+There is no CPU fallback.
+
+torch is imported before the library is loaded so that the HIP runtime torch ships
+(soname libamdhip64.so.7) is the one the library binds to: one runtime per process,
+shared streams and device pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libfla_linattn.so")
+
+FLA_OK, FLA_ERR_INVALID_ARG, FLA_ERR_UNSUPPORTED, FLA_ERR_DEVICE = 0, -1, -2, -3
+FLA_BF16 = 1 << 0
+FLA_DECAY_GAMMA = 1 << 1
+FLA_DECAY_GATE = 1 << 2
+FLA_PHI_ELU1 = 1 << 3
+FLA_NORMALIZE = 1 << 4
+
+EXPORTED = ("fla_linattn_fwd", "fla_linattn_fwd_segments", "fla_linattn_step",
+            "fla_status_string", "fla_linattn_segments_for")
+
+_lib = None
+
+
+class FlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def load_library():
+    """Load the HIP library (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"HIP library not built: {LIB_PATH} is missing "
+                          "(python -m chunkwise_causal_linear_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, u32, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int
+    lib.fla_linattn_fwd.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, u32, p]
+    lib.fla_linattn_fwd.restype = c_int
+    lib.fla_linattn_fwd_segments.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64,
+                                             u32, i64, p]
+    lib.fla_linattn_fwd_segments.restype = c_int
+    lib.fla_linattn_step.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, u32, p]
+    lib.fla_linattn_step.restype = c_int
+    lib.fla_status_string.argtypes = [c_int]
+    lib.fla_status_string.restype = ctypes.c_char_p
+    lib.fla_linattn_segments_for.argtypes = [i64, i64, i64, i64, i64, i64, u32,
+                                             ctypes.POINTER(i64)]
+    lib.fla_linattn_segments_for.restype = c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fla_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def flags_for(dtype: torch.dtype, decay_kind: str, phi_elu1: bool, normalize: bool) -> int:
+    f = FLA_BF16 if dtype == torch.bfloat16 else 0
+    f |= {"none": 0, "gamma": FLA_DECAY_GAMMA, "gate": FLA_DECAY_GATE}[decay_kind]
+    if phi_elu1:
+        f |= FLA_PHI_ELU1
+    if normalize:
+        f |= FLA_NORMALIZE
+    return f
+
+
+def _decay_kind(decay: Optional[torch.Tensor], decay_kind: Optional[str]) -> str:
+    if decay_kind is not None:
+        return decay_kind
+    if decay is None:
+        return "none"
+    return "gamma" if decay.dim() == 1 else "gate"
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch.Tensor] = None,
+        *, decay_kind: Optional[str] = None, init_state: Optional[torch.Tensor] = None,
+        out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+        want_final: bool = True, chunk: int = 64, phi_elu1: bool = False,
+        normalize: bool = False, n_segments: Optional[int] = None,
+        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise forward.  q, k [B,H,T,dk]; v [B,H,T,dv] (bf16 or fp32, on the GPU);
+    decay: gamma [H] or gate [B,H,T,dk] (fp32); init/final state fp32 [B,H,dk,dv(+1)].
+    Returns (out, final_state)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    kind = _decay_kind(decay, decay_kind)
+    ncol = dv + (1 if normalize else 0)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and want_final:
+        final_state = torch.empty((B, H, dk, ncol), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, out, decay, init_state, final_state):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    flags = flags_for(q.dtype, kind, phi_elu1, normalize)
+    lib = load_library()
+    if n_segments is None:
+        rc = lib.fla_linattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(init_state),
+                                 _ptr(out), _ptr(final_state), B, H, T, dk, dv, chunk, flags,
+                                 _stream(stream))
+    else:
+        rc = lib.fla_linattn_fwd_segments(_ptr(q), _ptr(k), _ptr(v), _ptr(decay),
+                                          _ptr(init_state), _ptr(out), _ptr(final_state), B, H,
+                                          T, dk, dv, chunk, flags, int(n_segments),
+                                          _stream(stream))
+    if rc != FLA_OK:
+        raise FlaError("fla_linattn_fwd", rc)
+    return out, final_state
+
+
+def step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor,
+         decay: Optional[torch.Tensor] = None, *, decay_kind: Optional[str] = None,
+         out: Optional[torch.Tensor] = None, phi_elu1: bool = False, normalize: bool = False,
+         stream=None) -> torch.Tensor:
+    """One decoding token: q, k [B,H,dk]; v [B,H,dv]; state fp32 [B,H,dk,dv(+1)] updated in
+    place; decay gamma [H] or gate [B,H,dk].  Returns out [B,H,dv]."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if decay_kind is None:
+        decay_kind = "none" if decay is None else ("gamma" if decay.dim() == 1 else "gate")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    flags = flags_for(q.dtype, decay_kind, phi_elu1, normalize)
+    rc = load_library().fla_linattn_step(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(state),
+                                         _ptr(out), B, H, dk, dv, flags, _stream(stream))
+    if rc != FLA_OK:
+        raise FlaError("fla_linattn_step", rc)
+    return out
+
+
+def segments_for(B, H, T, dk, dv, chunk, flags) -> int:
+    n = ctypes.c_int64(0)
+    rc = load_library().fla_linattn_segments_for(B, H, T, dk, dv, chunk, flags, ctypes.byref(n))
+    if rc != FLA_OK:
+        raise FlaError("fla_linattn_segments_for", rc)
+    return int(n.value)

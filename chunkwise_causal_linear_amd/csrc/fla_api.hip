@@ -1,0 +1,367 @@
+// C ABI of the chunkwise causal linear attention library: validation, schedule choice,
+// launches, plus the small kernels around the fused chunk kernel (segment scan, state
+// fill/copy, one-token decode step).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fla_linattn.h"
+#include "dispatch.hpp"
+
+namespace fla {
+namespace {
+
+constexpr int kStepThreads = 256;
+constexpr int kScanThreads = 256;
+constexpr int64_t kMaxGrid = (int64_t)1 << 31;
+
+bool is_pow2_dim(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+bool is_chunk(int64_t c) { return c == 16 || c == 32 || c == 64 || c == 128; }
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+ChunkLauncher find_launcher(bool bf16, int64_t dk, int64_t chunk, int decay, bool norm) {
+  const int c = (int)chunk;
+  if (bf16) {
+    switch (dk) {
+    case 16: return chunk_launcher_bf16_16(c, decay, norm);
+    case 32: return chunk_launcher_bf16_32(c, decay, norm);
+    case 64: return chunk_launcher_bf16_64(c, decay, norm);
+    case 128: return chunk_launcher_bf16_128(c, decay, norm);
+    case 256: return chunk_launcher_bf16_256(c, decay, norm);
+    }
+  } else {
+    switch (dk) {
+    case 16: return chunk_launcher_f32_16(c, decay, norm);
+    case 32: return chunk_launcher_f32_32(c, decay, norm);
+    case 64: return chunk_launcher_f32_64(c, decay, norm);
+    case 128: return chunk_launcher_f32_128(c, decay, norm);
+    case 256: return chunk_launcher_f32_256(c, decay, norm);
+    }
+  }
+  return nullptr;
+}
+
+int decay_kind(uint32_t flags) {
+  if (flags & FLA_DECAY_GAMMA) return DECAY_GAMMA;
+  if (flags & FLA_DECAY_GATE) return DECAY_GATE;
+  return DECAY_NONE;
+}
+
+// Shape and flag checks shared by the forward and step calls.
+int check_common(int64_t B, int64_t H, int64_t dk, int64_t dv, uint32_t flags,
+                 const float *gate_or_gamma) {
+  if (flags & ~FLA_ALL_FLAGS) return FLA_ERR_INVALID_ARG;
+  if ((flags & FLA_DECAY_GAMMA) && (flags & FLA_DECAY_GATE)) return FLA_ERR_INVALID_ARG;
+  const bool has_decay = (flags & (FLA_DECAY_GAMMA | FLA_DECAY_GATE)) != 0;
+  if (has_decay != (gate_or_gamma != nullptr)) return FLA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || B > (1 << 24) || H > (1 << 24)) return FLA_ERR_INVALID_ARG;
+  if (dk < 1 || dv < 1) return FLA_ERR_INVALID_ARG;
+  if (!aligned(gate_or_gamma, (flags & FLA_DECAY_GATE) ? 16 : 4)) return FLA_ERR_INVALID_ARG;
+  if (!is_pow2_dim(dk) || !is_pow2_dim(dv)) return FLA_ERR_UNSUPPORTED;
+  return FLA_OK;
+}
+
+// Segment count: one streaming workgroup per (b, h, value slice) when that already gives
+// at least one workgroup per CU; otherwise cut the sequence so ~1024 workgroups exist,
+// keeping at least 8 chunks per segment.
+int64_t auto_segments(int64_t B, int64_t H, int64_t T, int64_t dv, int64_t chunk) {
+  const int64_t nvs = (dv + kSlice - 1) / kSlice;
+  const int64_t units = B * H * nvs;
+  if (units >= 256) return 1;
+  const int64_t nch = (T + chunk - 1) / chunk;
+  int64_t p = 1024 / units;
+  if (p > nch / 8) p = nch / 8;
+  return p < 1 ? 1 : p;
+}
+
+// ---------------------------------------------------------------------------------
+// small kernels
+
+// dst[i] = src ? src[i] : 0 (state copy / zero fill).
+__global__ void state_fill_kernel(float *dst, const float *src, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+// Scan over segments (elementwise per state entry): on entry ws[bh][s] holds segment s's
+// end state from a zero start and dec[bh][s][c] the product of its decays; on exit ws[bh][s]
+// holds segment s's true start state, and fin (if any) the state after the last segment.
+__global__ void segment_scan_kernel(float *ws, const float *dec, const float *init, float *fin,
+                                    int64_t nbh, int nseg, int dk, int ncol) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = (int64_t)dk * ncol;
+  if (i >= nbh * per) return;
+  const int64_t bh = i / per, ce = i % per;
+  const int c = (int)(ce / ncol);
+  float run = init ? init[i] : 0.f;
+  float *w = ws + bh * nseg * per + ce;
+  const float *d = dec + bh * nseg * dk + c;
+  for (int s = 0; s < nseg; ++s) {
+    const float e = w[(int64_t)s * per];
+    w[(int64_t)s * per] = run;
+    run = d[(int64_t)s * dk] * run + e;
+  }
+  if (fin) fin[i] = run;
+}
+
+template <typename TIn> __device__ __forceinline__ float ld_in(const TIn *p, int64_t i);
+template <> __device__ __forceinline__ float ld_in<float>(const float *p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ld_in<__bf16>(const __bf16 *p, int64_t i) {
+  return (float)p[i];
+}
+
+// One decoding token per (b, h): h <- diag(g) h + phi(k) v^T, z <- g z + phi(k),
+// o = h^T phi(q) (/ z^T phi(q)).  Threads own value columns, so state rows are read
+// and written coalesced.
+template <typename TIn>
+__global__ __launch_bounds__(kStepThreads) void step_kernel(const TIn *q, const TIn *k,
+                                                            const TIn *v, const float *decay,
+                                                            int kind, float *state, TIn *out,
+                                                            int H, int dk, int dv, int phi_elu1,
+                                                            int norm) {
+  __shared__ float sq[256], sk[256], sg[256], sz[256];
+  __shared__ float sden;
+  const int bh = blockIdx.x, h = bh % H, tid = threadIdx.x;
+  const int ncol = dv + (norm ? 1 : 0);
+  float *st = state + (int64_t)bh * dk * ncol;
+  for (int c = tid; c < dk; c += blockDim.x) {
+    float qv = ld_in(q, (int64_t)bh * dk + c), kv = ld_in(k, (int64_t)bh * dk + c);
+    if (phi_elu1) {
+      qv = qv > 0.f ? qv + 1.f : __expf(qv);
+      kv = kv > 0.f ? kv + 1.f : __expf(kv);
+    }
+    sq[c] = qv;
+    sk[c] = kv;
+    sg[c] = kind == DECAY_GAMMA ? decay[h] : (kind == DECAY_GATE ? decay[(int64_t)bh * dk + c] : 1.f);
+  }
+  __syncthreads();
+  if (norm) {
+    for (int c = tid; c < dk; c += blockDim.x) {
+      const float z = sg[c] * st[(int64_t)c * ncol + dv] + sk[c];
+      sz[c] = z;
+      st[(int64_t)c * ncol + dv] = z;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float d = 0.f;
+      for (int c = 0; c < dk; ++c) d += sz[c] * sq[c];
+      sden = d;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < dv; e += blockDim.x) {
+    const float ve = ld_in(v, (int64_t)bh * dv + e);
+    float acc = 0.f;
+    for (int c = 0; c < dk; ++c) {
+      float *p = st + (int64_t)c * ncol + e;
+      const float hn = sg[c] * *p + sk[c] * ve;
+      *p = hn;
+      acc += hn * sq[c];
+    }
+    if (norm) acc = acc / sden;
+    out[(int64_t)bh * dv + e] = (TIn)acc;
+  }
+}
+
+unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+int launch_fill(float *dst, const float *src, int64_t n, hipStream_t s) {
+  if (n <= 0) return FLA_OK;
+  void *args[] = {&dst, &src, &n};
+  if (hipLaunchKernel(reinterpret_cast<const void *>(&state_fill_kernel), dim3(blocks_for(n, 256)),
+                      dim3(256), args, 0, s) != hipSuccess)
+    return FLA_ERR_DEVICE;
+  return FLA_OK;
+}
+
+int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+             const float *init_state, void *out, float *final_state, int64_t B, int64_t H,
+             int64_t T, int64_t dk, int64_t dv, int64_t chunk, uint32_t flags,
+             int64_t n_segments, void *stream) {
+  int rc = check_common(B, H, dk, dv, flags, gate_or_gamma);
+  if (rc != FLA_OK) return rc;
+  if (T < 0 || n_segments < 0) return FLA_ERR_INVALID_ARG;
+  if (T > 0 && (!q || !k || !v || !out)) return FLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(init_state, 16) || !aligned(final_state, 16))
+    return FLA_ERR_INVALID_ARG;
+  if (!is_chunk(chunk)) return FLA_ERR_UNSUPPORTED;
+  if (B * H > ((int64_t)1 << 26) || T > ((int64_t)1 << 40) / (B * H)) return FLA_ERR_INVALID_ARG;
+  const bool bf16 = (flags & FLA_BF16) != 0;
+  const bool norm = (flags & FLA_NORMALIZE) != 0;
+  const int kind = decay_kind(flags);
+  const ChunkLauncher launch = find_launcher(bf16, dk, chunk, kind, norm);
+  if (!launch) return FLA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ncol = dv + (norm ? 1 : 0);
+  const int64_t nbh = B * H;
+  const int64_t state_elems = nbh * dk * ncol;
+
+  if (T == 0) {
+    if (final_state && final_state != init_state) return launch_fill(final_state, init_state, state_elems, s);
+    return FLA_OK;
+  }
+
+  const int64_t nch = (T + chunk - 1) / chunk;
+  int64_t nseg = n_segments == 0 ? auto_segments(B, H, T, dv, chunk) : n_segments;
+  if (nseg > nch) nseg = nch;
+  const int64_t seg_chunks = (nch + nseg - 1) / nseg;
+  const int64_t seg_len = seg_chunks * chunk;
+  nseg = (T + seg_len - 1) / seg_len;
+  const int64_t nvs = (dv + kSlice - 1) / kSlice;
+  const int64_t nunits = nbh * nseg;
+  const int64_t grid = ((nunits + 7) / 8) * 8 * nvs;
+  if (grid >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
+
+  ChunkArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.decay = gate_or_gamma;
+  a.out = out;
+  a.T = T;
+  a.seg_len = seg_len;
+  a.H = (int)H; a.dv = (int)dv; a.ncol = (int)ncol;
+  a.nseg = (int)nseg; a.nvs = (int)nvs; a.nunits = (int)nunits;
+  a.phi_elu1 = (flags & FLA_PHI_ELU1) ? 1 : 0;
+
+  if (nseg == 1) {
+    // The z column is read by every value slice and written by slice 0 only: an in-place
+    // resume with several slices reads a private copy of the start state.
+    float *tmp = nullptr;
+    const float *ini = init_state;
+    if (init_state && init_state == final_state && norm && nvs > 1) {
+      if (hipMallocAsync(reinterpret_cast<void **>(&tmp), state_elems * sizeof(float), s) != hipSuccess)
+        return FLA_ERR_DEVICE;
+      if (launch_fill(tmp, init_state, state_elems, s) != FLA_OK) {
+        (void)hipFreeAsync(tmp, s);
+        return FLA_ERR_DEVICE;
+      }
+      ini = tmp;
+    }
+    a.init = ini;
+    a.init_bh_stride = dk * ncol;
+    a.init_seg_stride = 0;
+    a.fin = final_state;
+    a.fin_bh_stride = dk * ncol;
+    a.fin_seg_stride = 0;
+    a.seg_decay = nullptr;
+    a.state_only = 0;
+    rc = launch(a, (unsigned)grid, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
+    if (tmp && hipFreeAsync(tmp, s) != hipSuccess) rc = FLA_ERR_DEVICE;
+    return rc;
+  }
+
+  // Segment schedule: (A) end state of every segment from a zero start, (B) scan over
+  // segments, (C) outputs of every segment from its start state.
+  const int64_t ws_states = nbh * nseg * dk * ncol;
+  const int64_t ws_dec = nbh * nseg * dk;
+  float *ws = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void **>(&ws), (ws_states + ws_dec) * sizeof(float), s) != hipSuccess)
+    return FLA_ERR_DEVICE;
+  float *wdec = ws + ws_states;
+
+  a.init = nullptr;
+  a.init_bh_stride = 0;
+  a.init_seg_stride = 0;
+  a.fin = ws;
+  a.fin_bh_stride = nseg * dk * ncol;
+  a.fin_seg_stride = dk * ncol;
+  a.seg_decay = wdec;
+  a.state_only = 1;
+  rc = launch(a, (unsigned)grid, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
+
+  if (rc == FLA_OK) {
+    const int64_t n = nbh * dk * ncol;
+    int nseg_i = (int)nseg, dk_i = (int)dk, ncol_i = (int)ncol;
+    const float *ini = init_state;
+    float *fin = final_state;
+    int64_t nbh_v = nbh;
+    void *args[] = {&ws, &wdec, &ini, &fin, &nbh_v, &nseg_i, &dk_i, &ncol_i};
+    if (hipLaunchKernel(reinterpret_cast<const void *>(&segment_scan_kernel),
+                        dim3(blocks_for(n, kScanThreads)), dim3(kScanThreads), args, 0, s) != hipSuccess)
+      rc = FLA_ERR_DEVICE;
+  }
+  if (rc == FLA_OK) {
+    a.init = ws;
+    a.init_bh_stride = nseg * dk * ncol;
+    a.init_seg_stride = dk * ncol;
+    a.fin = nullptr;
+    a.seg_decay = nullptr;
+    a.state_only = 0;
+    rc = launch(a, (unsigned)grid, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
+  }
+  if (hipFreeAsync(ws, s) != hipSuccess) rc = FLA_ERR_DEVICE;
+  return rc;
+}
+
+} // namespace
+} // namespace fla
+
+extern "C" {
+
+const char *fla_status_string(int status) {
+  switch (status) {
+  case FLA_OK: return "ok";
+  case FLA_ERR_INVALID_ARG: return "invalid argument";
+  case FLA_ERR_UNSUPPORTED: return "unsupported shape or option";
+  case FLA_ERR_DEVICE: return "device launch or allocation failed";
+  default: return "unknown status";
+  }
+}
+
+int fla_linattn_fwd(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+                    const float *init_state, void *out, float *final_state, int64_t B,
+                    int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk,
+                    uint32_t flags, void *stream) {
+  return fla::fwd_impl(q, k, v, gate_or_gamma, init_state, out, final_state, B, H, T, dk, dv,
+                       chunk, flags, 0, stream);
+}
+
+int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
+                             const float *gate_or_gamma, const float *init_state, void *out,
+                             float *final_state, int64_t B, int64_t H, int64_t T, int64_t dk,
+                             int64_t dv, int64_t chunk, uint32_t flags, int64_t n_segments,
+                             void *stream) {
+  return fla::fwd_impl(q, k, v, gate_or_gamma, init_state, out, final_state, B, H, T, dk, dv,
+                       chunk, flags, n_segments, stream);
+}
+
+int fla_linattn_segments_for(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                             int64_t chunk, uint32_t flags, int64_t *n_segments) {
+  if (!n_segments || T < 0) return FLA_ERR_INVALID_ARG;
+  const bool has_decay = (flags & (FLA_DECAY_GAMMA | FLA_DECAY_GATE)) != 0;
+  static const float dummy[4] = {0.f, 0.f, 0.f, 0.f};
+  int rc = fla::check_common(B, H, dk, dv, flags, has_decay ? dummy : nullptr);
+  if (rc != FLA_OK) return rc;
+  if (!fla::is_chunk(chunk)) return FLA_ERR_UNSUPPORTED;
+  const int64_t nch = (T + chunk - 1) / chunk;
+  int64_t p = T == 0 ? 1 : fla::auto_segments(B, H, T, dv, chunk);
+  if (p > nch && nch > 0) p = nch;
+  *n_segments = p;
+  return FLA_OK;
+}
+
+int fla_linattn_step(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+                     float *state, void *out, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                     uint32_t flags, void *stream) {
+  int rc = fla::check_common(B, H, dk, dv, flags, gate_or_gamma);
+  if (rc != FLA_OK) return rc;
+  if (!q || !k || !v || !out || !state) return FLA_ERR_INVALID_ARG;
+  if (!fla::aligned(q, 16) || !fla::aligned(k, 16) || !fla::aligned(v, 16) ||
+      !fla::aligned(out, 16) || !fla::aligned(state, 16))
+    return FLA_ERR_INVALID_ARG;
+  const int64_t nbh = B * H;
+  if (nbh >= fla::kMaxGrid) return FLA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float *dec = gate_or_gamma;
+  int kind = fla::decay_kind(flags);
+  int Hi = (int)H, dki = (int)dk, dvi = (int)dv;
+  int phi = (flags & FLA_PHI_ELU1) ? 1 : 0, norm = (flags & FLA_NORMALIZE) ? 1 : 0;
+  void *args[] = {const_cast<void **>(&q), const_cast<void **>(&k), const_cast<void **>(&v),
+                  &dec, &kind, &state, &out, &Hi, &dki, &dvi, &phi, &norm};
+  const void *fn = (flags & FLA_BF16) ? reinterpret_cast<const void *>(&fla::step_kernel<__bf16>)
+                                      : reinterpret_cast<const void *>(&fla::step_kernel<float>);
+  if (hipLaunchKernel(fn, dim3((unsigned)nbh), dim3(fla::kStepThreads), args, 0, s) != hipSuccess)
+    return FLA_ERR_DEVICE;
+  return FLA_OK;
+}
+
+} // extern "C"

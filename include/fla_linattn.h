@@ -1,0 +1,125 @@
+/*
+ * fla_linattn.h — C ABI of the MI355X (gfx950) chunkwise causal linear attention library.
+ *
+ * The operation (forward pass, "chunk" mode) is causal linear attention with an
+ * optional decay, per (batch b, head h):
+ *
+ *     S_t = G_t (.) S_{t-1} + v_t phi(k_t)^T          (state, d_v x d_k)
+ *     z_t = G_t (.) z_{t-1} + phi(k_t)                 (normaliser, only with FLA_NORMALIZE)
+ *     o_t = S_t phi(q_t)            or   S_t phi(q_t) / (z_t^T phi(q_t))
+ *
+ * Sources: the textbook chapter 1.6 "Long context and efficient attention", section
+ * "linear attention" (recurrence, normaliser, elu+1 feature map, parallel = recurrent),
+ * and the Flash Linear Attention posts (RetNet retention with a per-head decay gamma,
+ * GLA with a per-token per-key gate alpha_t, "chunk" mode forward).  G_t is 1 (plain
+ * linear attention), gamma_h (FLA_DECAY_GAMMA) or alpha_t (FLA_DECAY_GATE); the gate
+ * multiplies key column c of S for every value row, the old state is decayed before
+ * the current token is added, and z decays with the same G_t.
+ *
+ * Layouts (all row-major, contiguous, device memory of the current HIP device):
+ *   q, k    [B][H][T][dk]   bf16 (FLA_BF16) or fp32
+ *   v, out  [B][H][T][dv]   same dtype as q
+ *   gamma   [H]             fp32, values in [0, 1]
+ *   gate    [B][H][T][dk]   fp32, values in (0, 1]
+ *   state   [B][H][dk][dv + n] fp32, n = 1 with FLA_NORMALIZE (column dv holds z);
+ *           this is h = S^T, so state[b][h][c][e] = S[e][c].
+ *
+ * Ownership: every pointer belongs to the caller; the library keeps none after a call
+ * returns and holds no global mutable state.  Calls are asynchronous on `stream`
+ * (a hipStream_t; NULL = the default stream) and never synchronise the host.  Inputs
+ * are read-only.  Errors found on the host are returned before anything is enqueued;
+ * faults during execution surface at the caller's next synchronisation.
+ */
+#ifndef FLA_LINATTN_H
+#define FLA_LINATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every call. */
+enum fla_status {
+  FLA_OK = 0,
+  FLA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad or conflicting flags */
+  FLA_ERR_UNSUPPORTED = -2, /* valid request outside the built shape set */
+  FLA_ERR_DEVICE = -3       /* a HIP launch or stream-ordered allocation failed */
+};
+
+/* Flag bits. */
+#define FLA_BF16 (1u << 0)        /* q, k, v, out are bf16; otherwise fp32 */
+#define FLA_DECAY_GAMMA (1u << 1) /* gate_or_gamma = const float[H] */
+#define FLA_DECAY_GATE (1u << 2)  /* gate_or_gamma = const float[B][H][T][dk] */
+#define FLA_PHI_ELU1 (1u << 3)    /* phi(x) = elu(x) + 1 on q and k; otherwise identity */
+#define FLA_NORMALIZE (1u << 4)   /* divide by z_t^T phi(q_t); the state carries z */
+#define FLA_ALL_FLAGS (FLA_BF16 | FLA_DECAY_GAMMA | FLA_DECAY_GATE | FLA_PHI_ELU1 | FLA_NORMALIZE)
+
+/*
+ * fla_linattn_fwd — chunkwise forward pass over T tokens.
+ *
+ *   q, k, v, out : see layouts above; 16-byte aligned.  May be NULL only when T == 0.
+ *   gate_or_gamma: gamma [H] with FLA_DECAY_GAMMA (4-byte aligned), gate [B][H][T][dk]
+ *                  with FLA_DECAY_GATE (16-byte aligned), NULL with neither bit.
+ *   init_state   : [B][H][dk][dv+n] fp32, or NULL for a zero initial state (16-byte aligned).
+ *   final_state  : [B][H][dk][dv+n] fp32 written with the state after token T-1, or NULL.
+ *                  May alias init_state (in-place resume).
+ *   B, H >= 1; T >= 0; dk, dv in {16, 32, 64, 128, 256}; chunk in {16, 32, 64, 128}.
+ *   flags        : FLA_* bits; at most one decay bit.
+ *   stream       : hipStream_t or NULL.
+ *
+ * T == 0 leaves out untouched and writes init_state (or zeros) to final_state.
+ * The chunk size changes the rounding, never the mathematical result.  Combinations
+ * whose on-chip tiles do not fit the 160 KiB LDS of a gfx950 CU (large dk with large
+ * chunk, mostly in fp32) return FLA_ERR_UNSUPPORTED.
+ * Gate range: each chunk's product of alpha along the chunk must stay above ~1e-30
+ * (per-key log-decay > -69 per chunk) or the fp32 factorisation overflows.
+ */
+int fla_linattn_fwd(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+                    const float *init_state, void *out, float *final_state, int64_t B,
+                    int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk,
+                    uint32_t flags, void *stream);
+
+/*
+ * fla_linattn_fwd_segments — fla_linattn_fwd with an explicit choice of schedule.
+ *   n_segments == 0: automatic (same as fla_linattn_fwd).
+ *   n_segments == 1: one workgroup per (b, h, 64-wide value slice) streams all chunks.
+ *   n_segments  > 1: the sequence is cut into that many segments of whole chunks; the
+ *                    segments' end states are combined by a scan, then every segment
+ *                    produces its outputs from its own start state (three launches and a
+ *                    stream-ordered workspace of B*H*n_segments*dk*(dv+n+1)*4 bytes).
+ * Both schedules compute the same function; they differ in rounding only.
+ */
+int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
+                             const float *gate_or_gamma, const float *init_state, void *out,
+                             float *final_state, int64_t B, int64_t H, int64_t T, int64_t dk,
+                             int64_t dv, int64_t chunk, uint32_t flags, int64_t n_segments,
+                             void *stream);
+
+/*
+ * fla_linattn_step — one token of recurrent decoding (the T == 1 case of the forward
+ * pass), updating the state in place.
+ *   q, k : [B][H][dk]; v, out: [B][H][dv] (bf16 with FLA_BF16, else fp32); 16-byte aligned.
+ *   gate_or_gamma: gamma [H] or gate [B][H][dk] per the decay bit, else NULL.
+ *   state: fp32 [B][H][dk][dv+n], read and written (required).
+ *   dk, dv in {16, 32, 64, 128, 256}.
+ */
+int fla_linattn_step(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+                     float *state, void *out, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                     uint32_t flags, void *stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char *fla_status_string(int status);
+
+/*
+ * fla_linattn_segments_for — the segment count fla_linattn_fwd would choose for a shape
+ * (1 = single streaming launch).  Returns a status; *n_segments is set on FLA_OK.
+ */
+int fla_linattn_segments_for(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                             int64_t chunk, uint32_t flags, int64_t *n_segments);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLA_LINATTN_H */

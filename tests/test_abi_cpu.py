@@ -1,0 +1,123 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared symbol, and
+rejects bad requests on the host before any device work (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fla_linattn.h")
+
+torch = pytest.importorskip("torch")
+import chunkwise_causal_linear_amd as fla  # noqa: E402
+
+BOGUS = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced on error paths
+MISALIGNED = ctypes.c_void_p((1 << 20) + 2)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(fla_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fla.LIB_PATH):
+        pytest.skip("HIP library not built")
+    return fla.load_library()
+
+
+def test_header_declares_the_exported_set():
+    assert declared_functions() == sorted(fla.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fla.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (fla_\w+)$", out, re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_library_is_built_for_gfx950():
+    if not os.path.exists(fla.LIB_PATH):
+        pytest.skip("HIP library not built")
+    blob = open(fla.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_status_strings(lib):
+    assert fla.status_string(0) == "ok"
+    for s in (-1, -2, -3, 42):
+        assert isinstance(fla.status_string(s), str) and fla.status_string(s)
+
+
+def fwd_raw(lib, *, q=BOGUS, k=BOGUS, v=BOGUS, gate=None, init=None, out=BOGUS, fin=None,
+            B=1, H=1, T=64, dk=64, dv=64, chunk=64, flags=0):
+    return lib.fla_linattn_fwd(q, k, v, gate, init, out, fin, B, H, T, dk, dv, chunk, flags, None)
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(flags=1 << 7), fla.FLA_ERR_INVALID_ARG),                       # unknown flag bit
+    (dict(flags=fla.FLA_DECAY_GAMMA | fla.FLA_DECAY_GATE, gate=BOGUS), fla.FLA_ERR_INVALID_ARG),
+    (dict(flags=fla.FLA_DECAY_GAMMA), fla.FLA_ERR_INVALID_ARG),          # decay bit, no values
+    (dict(gate=BOGUS), fla.FLA_ERR_INVALID_ARG),                          # values, no decay bit
+    (dict(q=None), fla.FLA_ERR_INVALID_ARG),
+    (dict(out=None), fla.FLA_ERR_INVALID_ARG),
+    (dict(B=0), fla.FLA_ERR_INVALID_ARG),
+    (dict(H=0), fla.FLA_ERR_INVALID_ARG),
+    (dict(T=-1), fla.FLA_ERR_INVALID_ARG),
+    (dict(q=MISALIGNED), fla.FLA_ERR_INVALID_ARG),
+    (dict(fin=MISALIGNED), fla.FLA_ERR_INVALID_ARG),
+    (dict(flags=fla.FLA_DECAY_GATE, gate=MISALIGNED), fla.FLA_ERR_INVALID_ARG),
+    (dict(dk=48), fla.FLA_ERR_UNSUPPORTED),
+    (dict(dv=512), fla.FLA_ERR_UNSUPPORTED),
+    (dict(chunk=512), fla.FLA_ERR_UNSUPPORTED),
+    (dict(chunk=8), fla.FLA_ERR_UNSUPPORTED),
+    (dict(dk=256, chunk=128, flags=fla.FLA_BF16), fla.FLA_ERR_UNSUPPORTED),  # tiles > LDS
+    (dict(dk=256, chunk=64), fla.FLA_ERR_UNSUPPORTED),                       # fp32 tiles > LDS
+])
+def test_fwd_rejects_on_host(lib, kw, expected):
+    assert fwd_raw(lib, **kw) == expected
+
+
+def test_segments_override_rejects_negative(lib):
+    rc = lib.fla_linattn_fwd_segments(BOGUS, BOGUS, BOGUS, None, None, BOGUS, None, 1, 1, 64, 64,
+                                      64, 64, 0, -1, None)
+    assert rc == fla.FLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(state=None), fla.FLA_ERR_INVALID_ARG),
+    (dict(flags=1 << 9), fla.FLA_ERR_INVALID_ARG),
+    (dict(dk=24), fla.FLA_ERR_UNSUPPORTED),
+    (dict(q=MISALIGNED), fla.FLA_ERR_INVALID_ARG),
+    (dict(flags=fla.FLA_DECAY_GATE), fla.FLA_ERR_INVALID_ARG),
+])
+def test_step_rejects_on_host(lib, kw, expected):
+    a = dict(q=BOGUS, k=BOGUS, v=BOGUS, gate=None, state=BOGUS, out=BOGUS, B=1, H=1, dk=64,
+             dv=64, flags=0)
+    a.update(kw)
+    rc = lib.fla_linattn_step(a["q"], a["k"], a["v"], a["gate"], a["state"], a["out"], a["B"],
+                              a["H"], a["dk"], a["dv"], a["flags"], None)
+    assert rc == expected
+
+
+def test_schedule_choice(lib):
+    # enough (b, h, 64-wide value slice) units: one streaming launch
+    assert fla.segments_for(8, 16, 16384, 128, 128, 64, fla.FLA_BF16 | fla.FLA_DECAY_GATE) == 1
+    assert fla.segments_for(32, 4, 2048, 256, 256, 64, fla.FLA_BF16 | fla.FLA_DECAY_GAMMA) == 1
+    # 8 heads over a million tokens: the sequence is cut into segments
+    assert fla.segments_for(1, 8, 1 << 20, 128, 128, 128, fla.FLA_BF16 | fla.FLA_DECAY_GAMMA) == 64
+    # too short to cut
+    assert fla.segments_for(1, 1, 256, 64, 64, 64, fla.FLA_PHI_ELU1 | fla.FLA_NORMALIZE) == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(fla, "_lib", None)
+    monkeypatch.setattr(fla, "LIB_PATH", "/nonexistent/libfla_linattn.so")
+    with pytest.raises(ImportError):
+        fla.load_library()

@@ -179,3 +179,49 @@ def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f32(x).astype(np.float64)
     return np.asarray(x, dtype=np.float64)
+
+
+def generate_torch(w: Workload, device="cuda"):
+    """Draw the inputs of workload ``w`` directly on a device with torch's seeded generator
+    (for full-size runs, where numpy would take minutes).  Same layouts as ``generate``;
+    bf16 tensors are torch.bfloat16 (round-to-nearest-even from fp32).  Draw order: q, k,
+    v, then the gate's x or the initial state."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def normal(shape, scale):
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            x.mul_(scale)
+        return x.to(dt)
+
+    q = normal((w.B, w.H, w.T, w.dk), w.qk_scale)
+    k = normal((w.B, w.H, w.T, w.dk), w.qk_scale)
+    v = normal((w.B, w.H, w.T, w.dv), 1.0)
+    decay = None
+    if w.decay == DECAY_GATE:
+        decay = torch.empty((w.B, w.H, w.T, w.dk), device=device, dtype=torch.float32)
+        for b in range(w.B):  # fp64 per batch row keeps the temporary small
+            x = torch.randn((w.H, w.T, w.dk), generator=gen, device=device, dtype=torch.float64)
+            decay[b] = torch.sigmoid(x).pow(1.0 / 16.0).to(torch.float32)
+    elif w.decay == DECAY_GAMMA:
+        decay = torch.from_numpy(gamma_for(w)).to(device)
+    init = None
+    if w.init_sigma > 0:
+        ncol = w.dv + (1 if w.normalize else 0)
+        init = torch.randn((w.B, w.H, w.dk, ncol), generator=gen, device=device,
+                           dtype=torch.float32) * w.init_sigma
+    return {"q": q, "k": k, "v": v, "decay": decay, "init": init}
+
+
+def to_numpy_input(t):
+    """A torch input tensor as the oracle consumes it: fp32 array, or bf16 bit patterns."""
+    import torch
+
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
