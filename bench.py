@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunkwise causal linear attention forward pass on one MI355X.
+
+One step = one fla_linattn_fwd call (every stage of the path: load + feature map, decay
+factors, intra-chunk, chunk state, inter-chunk scan, output combine) over one batch of
+synthetic inputs already resident in HBM.  Default workload: the GLA-gated attention at
+B=8, H=16, T=16384, dk=dv=128, bf16, chunk 64.
+
+Prints ONE JSON line: tokens/s (B*T per second), with the roofline of the fused kernel
+(algorithmic bytes per launch / average launch time from HIP events on the launch
+stream) and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "chunkwise_causal_linear_amd", "csrc", f)
+                  for f in ("chunk_fwd.hpp", "chunk_inst.hip", "fla_api.hip")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w) -> tuple[float, float]:
+    """Bytes the method must move and MFMA FLOPs it must do for one forward pass.
+    Bytes: q, k, v, out once; the gate (fp32) once; gamma; the start state if given and the
+    end state.  FLOPs per token-head: 2 * [(C+1)/2 * (dk+dv) + 2 * dk * dv] (causal half
+    of the intra-chunk products, plus the state read-out and update)."""
+    s = 2 if w.dtype == "bf16" else 4
+    th = w.B * w.H * w.T
+    ncol = w.dv + (1 if w.normalize else 0)
+    b = th * (2 * w.dk + 2 * w.dv) * s
+    if w.decay == "gate":
+        b += th * w.dk * 4
+    elif w.decay == "gamma":
+        b += w.H * 4
+    state = w.B * w.H * w.dk * ncol * 4
+    b += state * (2 if w.init_sigma > 0 else 1)
+    f = th * 2.0 * ((w.chunk + 1) / 2.0 * (w.dk + w.dv) + 2.0 * w.dk * w.dv)
+    return float(b), f
+
+
+def kernel_name(w) -> str:
+    t = "__bf16" if w.dtype == "bf16" else "float"
+    d = {"none": 0, "gamma": 1, "gate": 2}[w.decay]
+    return f"chunk_fwd_kernel<{t}, {w.dk}, {w.chunk}, {d}, {str(w.normalize).lower()}>"
+
+
+def cpu_baseline(w, inp, out_gpu, fin_gpu, budget_s: float):
+    """Time the fp64 oracle on a bounded sample: the first heads of batch 0, full length,
+    as many as fit ~budget_s of CPU work; also report the GPU's error on that sample."""
+    import numpy as np
+    import oracle
+    from workloads import to_numpy_input
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    env_threads = os.environ.get("OMP_NUM_THREADS")
+    if env_threads and env_threads.isdigit():
+        threads = max(1, min(threads, int(env_threads)))
+    # ~2.5 GFLOP/s per core for the fp64 recurrence (4 flops per state entry per token)
+    per_head = 4.0 * w.T * w.dk * (w.dv + 1)
+    n_heads = int(max(1, min(w.H, budget_s * 2.5e9 * threads / per_head)))
+    sl = (slice(0, 1), slice(0, n_heads))
+
+    def part(t):
+        return None if t is None else to_numpy_input(t[sl])
+
+    dec = inp["decay"]
+    dec_s = None if dec is None else (part(dec) if w.decay == "gate" else to_numpy_input(dec[:n_heads]))
+    ini = part(inp["init"])
+    q, k, v = part(inp["q"]), part(inp["k"]), part(inp["v"])
+    t0 = time.perf_counter()
+    ro, rf = oracle.fwd(q, k, v, dec_s, w.decay, ini, phi_elu1=w.phi_elu1,
+                        normalize=w.normalize, nthreads=threads)
+    dt = time.perf_counter() - t0
+    o = out_gpu[sl].float().cpu().numpy().astype(np.float64)
+    f = fin_gpu[sl].cpu().numpy().astype(np.float64)
+    err_o = float(np.max(np.abs(o - ro)) / max(np.max(np.abs(ro)), 1e-300))
+    err_f = float(np.max(np.abs(f - rf)) / max(np.max(np.abs(rf)), 1e-300))
+    token_heads = w.T * n_heads
+    return {
+        "value": token_heads / dt / w.H,   # tokens/s: H heads make one token
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"batch 0, heads 0..{n_heads - 1} of {w.H}, all {w.T} tokens "
+                  f"({token_heads} token-heads, fp64 recurrence, {dt:.1f} s)",
+    }, {"max_rel_err_out": err_o, "max_rel_err_final": err_f,
+        "sample_heads": n_heads}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None, help="workload name (default: headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards over (batch, head) or sequence segments across GPUs as "
+              "described in the design notes, but no multi-GPU run is part of it.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunkwise_causal_linear_amd as fla
+    from workloads import HEADLINE, WORKLOADS, generate_torch
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    torch.cuda.set_device(0)
+    inp = generate_torch(w, "cuda")
+    out = torch.empty((w.B, w.H, w.T, w.dv), dtype=inp["q"].dtype, device="cuda")
+    ncol = w.dv + (1 if w.normalize else 0)
+    fin = torch.empty((w.B, w.H, w.dk, ncol), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fla.fwd(inp["q"], inp["k"], inp["v"], inp["decay"], decay_kind=w.decay,
+                init_state=inp["init"], out=out, final_state=fin, chunk=w.chunk,
+                phi_elu1=w.phi_elu1, normalize=w.normalize, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: HIP events on the stream the kernels are launched on
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    nseg = fla.segments_for(w.B, w.H, w.T, w.dk, w.dv, w.chunk,
+                            fla.flags_for(inp["q"].dtype, w.decay, w.phi_elu1, w.normalize))
+    alg_bytes, alg_flops = algorithmic(w)
+    tokens = w.B * w.T
+    achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tc = json.load(f)
+        rec = tc.get("workloads", {}).get(w.name)
+        if rec and tc.get("kernel_source_hash") == kernel_source_hash():
+            traffic = rec.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    res = {
+        "metric": "chunked linear-attn fwd tokens/s + roofline % (MFMA/HBM), B8 H16 T16384 d128",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded torch generator on the GPU; shapes and distributions of the workload)",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+            "chunk": w.chunk, "decay": w.decay, "phi": "elu+1" if w.phi_elu1 else "identity",
+            "normalize": w.normalize, "init_state": w.init_sigma > 0, "segments": nseg,
+            "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel_name(w) + (" (+ segment passes)" if nseg > 1 else ""),
+            "achieved": achieved_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "mfma_tflops": alg_flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": alg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
+        },
+        "wall_s_timed_region": t_wall,
+    }
+    if not args.no_cpu_baseline:
+        cb, parity = cpu_baseline(w, inp, out, fin, args.cpu_budget)
+        res["cpu_baseline"] = cb
+        res["parity_on_sample"] = parity
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
