@@ -4,32 +4,36 @@
 // product of the decays inside the chunk (e^{lambda_i}), unrolling the recurrence
 // S_t = G_t (.) S_{t-1} + v_t phi(k_t)^T (textbook chapter 1.6, "linear attention";
 // RetNet gamma / GLA gate per the FLA posts; chunk mode = the chapter's remark on
-// decay-masked linear attention trained in matmul-friendly chunks) gives
-//     O     = tril(Qt Kt^T) V + Qt H_n              Qt = phi(q) b,  Kt = phi(k) / b
-//     H_n+1 = diag(b_{L-1}) H_n + Kh^T V            Kh = phi(k) b_{L-1} / b
-// where H = S^T (dk x dv) is the state before the chunk.  For a per-head gamma the
-// decay is applied instead as the mask gamma^{i-j} on the intra-chunk scores, the row
-// scale gamma^{i+1} on Q H and gamma^{L-1-j} on Kh, which never overflows.
+// decay-masked linear attention trained in matmul-friendly chunks) gives, with the
+// state H = S^T (dk x dv) before the chunk:
+//   gate:  O = tril(Qt Kt^T) V + Qt H,        H <- diag(b_{L-1}) (H + Kt^T V)
+//          Qt = phi(q) (.) b,  Kt = phi(k) / b
+//   gamma: O = (tril(phi(q) phi(k)^T) (.) gamma^{i-j}) V + diag(gamma^{i+1}) phi(q) H,
+//          H <- gamma^L H + phi(k)^T diag(gamma^{L-1-j}) V          (no overflow)
+//   none:  the gamma form with gamma = 1.
+// The normaliser z is the state column of an all-ones value: den = A 1 + Qt z.
 //
-// One workgroup (4 waves) owns one (b, h, 64-wide slice of dv) and walks the chunks in
-// order; the state never leaves the chip: wave w keeps H[:, 16w:16w+16] in fp32 MFMA
-// accumulators.  Per chunk:
-//   S1  load q, k, v, gate tiles (registers, prefetched one chunk ahead), apply phi;
-//   S2  decay factors (gate: column cumulative product through LDS; gamma: power table);
-//       write Qt, Kt (row-major), Kh^T and V^T (transposed) to LDS as MFMA operands;
-//   S3  A^T = Kt Qt^T tile by tile (MFMA), causal mask / decay mask, then
-//       O^T += V^T A^T (MFMA; A^T goes from accumulators straight into operands);
-//   S6  O^T += H^T Qt^T (MFMA, H converted from the accumulators), normalise, store;
-//   S4/S5 H = diag(b_{L-1}) H + Kh^T V (MFMA into the same accumulators).
-// Outputs are computed transposed (O^T tiles) so each lane stores 4 adjacent values.
-// The normaliser z is handled as an extra value tile whose V is all ones.
+// Workgroup = 8 waves for one (b, h, segment, 64-wide slice of dv):
+//   waves 0..3 (consumers) each own 16 value columns: the fp32 state H[:, 16w:16w+16]
+//     lives in MFMA accumulators for the whole sequence; per chunk they run
+//     S3  A^T = Kt Qt^T tile by tile, causal / decay mask, O^T += V^T A^T,
+//     S6  O^T += H^T Qt^T (H converted to MFMA operands in registers), normalise, store,
+//     S4/S5  H <- decay (H + Kt^T V) (or gamma^L H + Kt^T V');
+//   waves 4..7 (producers) prefetch q, k, v, gate one or two chunks ahead in registers,
+//     apply phi (S1) and the decay factors (S2: per-key cumulative product down the chunk
+//     by a wave-level shuffle scan), and write Qt, Kt, V row-major into an LDS stage.
+// With two LDS stages producers prepare chunk n+1 while consumers compute chunk n
+// (one barrier per chunk).  Kt^T and V^T operands are read from the row-major tiles
+// with the gfx950 LDS transpose load (ds_read_b64_tr_b16), so no tile is ever written
+// transposed.  Outputs are computed transposed (O^T tiles): each lane stores 4
+// adjacent values of one output row.
 //
 // MFMA operand convention (v_mfma_f32_16x16x32_bf16): lane l = 16 g + li supplies row
 // (A) or column (B) li; its 8 K-slots hold k = 32u + 4g + s (s < 4) and
-// k = 32u + 16 + 4g + (s - 4) (s >= 4).  This matches the accumulator layout (lane holds
-// rows 4g + r of column li) of two adjacent 16-row tiles, so a result tile pair becomes an
-// operand without a shuffle.  fp32 (v_mfma_f32_16x16x4_f32): four MFMAs per 16-k block,
-// MFMA r using k = 16u + 4g + r in lane group g.
+// k = 32u + 16 + 4g + (s - 4) (s >= 4).  That is the accumulator layout (lane holds
+// rows 4g + r of column li) of two adjacent 16-row tiles, so result tiles become
+// operands without a shuffle.  fp32 (v_mfma_f32_16x16x4_f32): four MFMAs per 16-k
+// block, MFMA r using k = 16u + 4g + r in lane group g.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,13 +45,13 @@ namespace fla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum : int { DECAY_NONE = 0, DECAY_GAMMA = 1, DECAY_GATE = 2 };
 
-constexpr int kThreads = 256;   // 4 waves
-constexpr int kSlice = 64;      // value columns per workgroup (16 per wave)
+constexpr int kThreads = 512;   // 4 consumer + 4 producer waves
+constexpr int kSlice = 64;      // value columns per workgroup (16 per consumer wave)
 constexpr int kMaxLds = 163840; // gfx950 LDS per workgroup
 
 struct ChunkArgs {
@@ -72,9 +76,9 @@ template <typename TIn, int DK, int C, int DECAY, bool NORM>
 struct Cfg {
   static constexpr int ES = sizeof(TIn);
   static constexpr bool BF = (ES == 2);
-  static constexpr int PAD = BF ? 8 : 4; // 16 bytes of row padding
+  static constexpr int PAD = 16 / ES;    // 16 bytes of row padding
   static constexpr int LQ = DK + PAD;    // row stride (elements) of Qt, Kt
-  static constexpr int LT = C + PAD;     // row stride of Kh^T, V^T
+  static constexpr int LV = kSlice + PAD;// row stride of V
   static constexpr int NB = C / 16;      // 16-row blocks per chunk
   static constexpr int NCB = DK / 16;    // 16-row blocks of the state
   static constexpr int TPU = BF ? 2 : 1; // 16-blocks per MFMA K unit
@@ -82,27 +86,31 @@ struct Cfg {
   static constexpr int NU_C = (NB + TPU - 1) / TPU;
   static constexpr bool HI_DK = !(BF && DK == 16);
   static constexpr bool HI_C = !(BF && C == 16);
-  // q/k/gate loader: thread -> (8-column group, RPT consecutive rows)
-  static constexpr int CG = DK / 8;
-  static constexpr int GROUPS = C * CG;
-  static constexpr int RPT = GROUPS >= kThreads ? GROUPS / kThreads : 1;
+  // producer mapping for q/k/gate: wave p owns columns [p W, (p+1) W); a lane owns G
+  // consecutive columns and RPT consecutive rows; LPR lanes share a row.
+  static constexpr int W = DK / 4;
+  static constexpr int G = W >= 8 ? 8 : W;
+  static constexpr int LPR = W / G;
+  static constexpr int RP = 64 / LPR;
+  static constexpr int RPT = C >= RP ? C / RP : 1;
   static constexpr int NRG = C / RPT;
-  static constexpr int ACTIVE = GROUPS >= kThreads ? kThreads : GROUPS;
-  // v loader: 8 column groups across the 64-wide slice
-  static constexpr int VGROUPS = C * (kSlice / 8);
-  static constexpr int RPTV = VGROUPS >= kThreads ? VGROUPS / kThreads : 1;
-  static constexpr int VACTIVE = VGROUPS >= kThreads ? kThreads : VGROUPS;
-  // LDS map (bytes)
+  static constexpr int PACTIVE = NRG * LPR;
+  // producer mapping for v: 8 columns per lane, 8 lanes per row, 256 producer lanes
+  static constexpr int RPTV = C >= 32 ? C / 32 : 1;
+  static constexpr int VACTIVE = C >= 32 ? 256 : C * 8;
+  // registers held per prefetched chunk (32-bit words per producer lane)
+  static constexpr int STAGE_WORDS = 2 * RPT * G * ES / 4 + (DECAY == DECAY_GATE ? RPT * G : 0) +
+                                     RPTV * 8 * ES / 4;
+  static constexpr int PF = (STAGE_WORDS <= 80 && C <= 64 && !NORM) ? 2 : 1; // chunks ahead
+  // LDS map (bytes): [STAGES] x {Qt, Kt, V, eL}, then the gamma power table
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_K = OFF_Q + C * LQ * ES;
-  static constexpr int OFF_KH = OFF_K + C * LQ * ES;
-  static constexpr int OFF_V = OFF_KH + DK * LT * ES;
-  static constexpr int OFF_SCAN = OFF_V + kSlice * LT * ES;
-  static constexpr int SCAN_BYTES = DECAY == DECAY_GATE ? NRG * DK * 4 : 0;
-  static constexpr int OFF_EL = OFF_SCAN + SCAN_BYTES;
-  static constexpr int EL_BYTES = DECAY == DECAY_GATE ? DK * 4 : 0;
-  static constexpr int OFF_PW = OFF_EL + EL_BYTES;
+  static constexpr int OFF_V = OFF_K + C * LQ * ES;
+  static constexpr int OFF_EL = OFF_V + C * LV * ES;
+  static constexpr int STAGE_BYTES = OFF_EL + (DECAY == DECAY_GATE ? DK * 4 : 0);
   static constexpr int PW_BYTES = DECAY == DECAY_GAMMA ? ((C + 4) / 4) * 16 : 0;
+  static constexpr int STAGES = 2 * STAGE_BYTES + PW_BYTES <= kMaxLds ? 2 : 1;
+  static constexpr int OFF_PW = STAGES * STAGE_BYTES;
   static constexpr int LDS = OFF_PW + PW_BYTES;
   static constexpr bool FITS = LDS <= kMaxLds;
 };
@@ -110,100 +118,59 @@ struct Cfg {
 // ---------------------------------------------------------------------------------
 // small helpers
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 __device__ __forceinline__ float phi_f(float x, int elu1) {
   return elu1 ? (x > 0.f ? x + 1.f : __expf(x)) : x;
 }
-
 __device__ __forceinline__ float rcp_f(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// Eight consecutive input elements as fp32.
-template <typename TIn> struct Raw8;
-template <> struct Raw8<__bf16> {
-  uint4 d;
-  __device__ __forceinline__ void zero() { d = make_uint4(0, 0, 0, 0); }
-  __device__ __forceinline__ void load(const __bf16 *p) { d = *reinterpret_cast<const uint4 *>(p); }
-  __device__ __forceinline__ void to_f32(float f[8]) const {
-    f[0] = bf_lo(d.x); f[1] = bf_hi(d.x); f[2] = bf_lo(d.y); f[3] = bf_hi(d.y);
-    f[4] = bf_lo(d.z); f[5] = bf_hi(d.z); f[6] = bf_lo(d.w); f[7] = bf_hi(d.w);
-  }
-};
-template <> struct Raw8<float> {
-  float4 a, b;
-  __device__ __forceinline__ void zero() { a = make_float4(0, 0, 0, 0); b = a; }
-  __device__ __forceinline__ void load(const float *p) {
-    a = reinterpret_cast<const float4 *>(p)[0];
-    b = reinterpret_cast<const float4 *>(p)[1];
-  }
-  __device__ __forceinline__ void to_f32(float f[8]) const {
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-  }
-};
-struct Gate8 {
-  float4 a, b;
-  __device__ __forceinline__ void ones() { a = make_float4(1, 1, 1, 1); b = a; }
-  __device__ __forceinline__ void load(const float *p) {
-    a = reinterpret_cast<const float4 *>(p)[0];
-    b = reinterpret_cast<const float4 *>(p)[1];
-  }
-  __device__ __forceinline__ void to_f32(float f[8]) const {
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-  }
-};
-
-// Store 8 fp32 values as 8 consecutive elements of TIn in LDS.
-template <typename TIn>
-__device__ __forceinline__ void st8(TIn *p, const float f[8]) {
-  if constexpr (sizeof(TIn) == 2) {
-    bf16x8 x;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (__bf16)f[i];
-    *reinterpret_cast<bf16x8 *>(p) = x;
+// N consecutive 32-bit words from global memory (N = 2, 4 or 8).
+template <int N>
+__device__ __forceinline__ void ld_words(uint32_t *w, const void *p) {
+  if constexpr (N == 2) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    w[0] = x.x; w[1] = x.y;
   } else {
-    reinterpret_cast<float4 *>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
-    reinterpret_cast<float4 *>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+    static_assert(N % 4 == 0, "word count");
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const uint4 x = reinterpret_cast<const uint4 *>(p)[i / 4];
+      w[i] = x.x; w[i + 1] = x.y; w[i + 2] = x.z; w[i + 3] = x.w;
+    }
   }
 }
 
-// Store N (1..16) consecutive values to LDS with the widest natural stores.
+// Unpack N elements of TIn held in 32-bit words to fp32.
 template <typename TIn, int N>
-__device__ __forceinline__ void stN(TIn *p, const float *f) {
+__device__ __forceinline__ void unpack(float *f, const uint32_t *w) {
   if constexpr (sizeof(TIn) == 2) {
-    if constexpr (N % 8 == 0) {
 #pragma unroll
-      for (int o = 0; o < N; o += 8) {
-        bf16x8 x;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = (__bf16)f[o + i];
-        *reinterpret_cast<bf16x8 *>(p + o) = x;
-      }
-    } else if constexpr (N == 4) {
-      bf16x4 x;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = (__bf16)f[i];
-      *reinterpret_cast<bf16x4 *>(p) = x;
-    } else if constexpr (N == 2) {
-      bf16x2 x;
-      x[0] = (__bf16)f[0];
-      x[1] = (__bf16)f[1];
-      *reinterpret_cast<bf16x2 *>(p) = x;
-    } else {
-      static_assert(N == 1, "unsupported width");
-      p[0] = (__bf16)f[0];
+    for (int i = 0; i < N / 2; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   } else {
-    if constexpr (N % 4 == 0) {
 #pragma unroll
-      for (int o = 0; o < N; o += 4)
-        *reinterpret_cast<float4 *>(p + o) = make_float4(f[o], f[o + 1], f[o + 2], f[o + 3]);
-    } else if constexpr (N == 2) {
-      *reinterpret_cast<float2 *>(p) = make_float2(f[0], f[1]);
+    for (int i = 0; i < N; ++i) f[i] = __uint_as_float(w[i]);
+  }
+}
+
+// Store N (4 or 8) fp32 values as consecutive TIn elements in LDS.
+template <typename TIn, int N>
+__device__ __forceinline__ void st_lds(TIn *p, const float *f) {
+  if constexpr (sizeof(TIn) == 2) {
+    if constexpr (N == 8) {
+      bf16x8 x;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (__bf16)f[i];
+      *reinterpret_cast<bf16x8 *>(p) = x;
     } else {
-      static_assert(N == 1, "unsupported width");
-      p[0] = f[0];
+      static_assert(N == 4, "width");
+      *reinterpret_cast<bf16x4 *>(p) = bf16x4{(__bf16)f[0], (__bf16)f[1], (__bf16)f[2], (__bf16)f[3]};
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      *reinterpret_cast<float4 *>(p + i) = make_float4(f[i], f[i + 1], f[i + 2], f[i + 3]);
   }
 }
 
@@ -217,18 +184,38 @@ __device__ __forceinline__ Frag<TIn> ld_frag(const TIn *row, int u, int g) {
   if constexpr (sizeof(TIn) == 2) {
     const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(row + 32 * u + 4 * g);
     bf16x4 hi;
-    if constexpr (HI) {
-      hi = *reinterpret_cast<const bf16x4 *>(row + 32 * u + 16 + 4 * g);
-    } else {
-      hi = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-    }
+    if constexpr (HI) hi = *reinterpret_cast<const bf16x4 *>(row + 32 * u + 16 + 4 * g);
+    else hi = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   } else {
     return *reinterpret_cast<const f32x4 *>(row + 16 * u + 4 * g);
   }
 }
 
-// Operand fragment from accumulator tiles (rows 4g+r of column li): unit = tiles t0,t1.
+// Operand fragment whose K index runs down the rows of a row-major LDS tile (stride ld):
+// lane (g, li) gets column col0 + li at the rows of K unit u.  bf16: two LDS transpose
+// loads (in each 16-lane group lane q addresses row r0 + q/4, columns col0 + 4 (q%4);
+// lane p receives column col0 + p of rows r0..r0+3).  fp32: four scalar loads.
+template <typename TIn, bool HI>
+__device__ __forceinline__ Frag<TIn> ld_frag_t(const TIn *tile, int ld, int col0, int u, int g,
+                                               int li) {
+  if constexpr (sizeof(TIn) == 2) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const int r0 = 32 * u + 4 * g + (li >> 2);
+    const int c = col0 + 4 * (li & 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + r0 * ld + c));
+    i16x4 hi = {0, 0, 0, 0};
+    if constexpr (HI)
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + (r0 + 16) * ld + c));
+    const bf16x4 l = __builtin_bit_cast(bf16x4, lo), h = __builtin_bit_cast(bf16x4, hi);
+    return bf16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+  } else {
+    const TIn *p = tile + (16 * u + 4 * g) * ld + col0 + li;
+    return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+  }
+}
+
+// Operand fragment from accumulator tiles (rows 4g+r of column li).
 __device__ __forceinline__ bf16x8 acc_frag_bf(const f32x4 &t0, const f32x4 &t1) {
   return bf16x8{(__bf16)t0[0], (__bf16)t0[1], (__bf16)t0[2], (__bf16)t0[3],
                 (__bf16)t1[0], (__bf16)t1[1], (__bf16)t1[2], (__bf16)t1[3]};
@@ -245,13 +232,26 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, f32x4 a, f32x4 b) {
   return acc;
 }
 
+// Scale the K-slots of a fragment by per-slot factors s[].
+__device__ __forceinline__ bf16x8 scale_frag(bf16x8 f, const float *s) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)((float)f[i] * s[i]);
+  return r;
+}
+__device__ __forceinline__ f32x4 scale_frag(f32x4 f, const float *s) {
+  return f32x4{f[0] * s[0], f[1] * s[1], f[2] * s[2], f[3] * s[3]};
+}
+
 template <typename TIn>
-__device__ __forceinline__ Frag<TIn> ones_frag() {
+__device__ __forceinline__ Frag<TIn> frag_from(const float *s) {
   if constexpr (sizeof(TIn) == 2) {
-    const __bf16 o = (__bf16)1.f;
-    return bf16x8{o, o, o, o, o, o, o, o};
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)s[i];
+    return r;
   } else {
-    return f32x4{1.f, 1.f, 1.f, 1.f};
+    return f32x4{s[0], s[1], s[2], s[3]};
   }
 }
 
@@ -266,20 +266,27 @@ __device__ __forceinline__ void st_out4(TIn *p, f32x4 o) {
 }
 
 // ---------------------------------------------------------------------------------
+// Producer: raw chunk data held in registers between its load and its preparation.
+
+template <typename TIn, int DK, int C, int DECAY, bool NORM>
+struct Staged {
+  using K = Cfg<TIn, DK, C, DECAY, NORM>;
+  static constexpr int QW = K::G * K::ES / 4; // words per row of q or k
+  uint32_t q[K::RPT][QW], k[K::RPT][QW];
+  uint32_t a[DECAY == DECAY_GATE ? K::RPT : 1][K::G];
+  uint32_t v[K::RPTV][2 * K::ES];             // 8 elements
+};
+
+// ---------------------------------------------------------------------------------
 // The fused chunk kernel.
 
 template <typename TIn, int DK, int C, int DECAY, bool NORM>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
   using K = Cfg<TIn, DK, C, DECAY, NORM>;
   using F = Frag<TIn>;
+  using St = Staged<TIn, DK, C, DECAY, NORM>;
   static_assert(K::FITS, "tiles exceed LDS");
   __shared__ __attribute__((aligned(16))) unsigned char smem[K::LDS];
-  TIn *sQ = reinterpret_cast<TIn *>(smem + K::OFF_Q);
-  TIn *sK = reinterpret_cast<TIn *>(smem + K::OFF_K);
-  TIn *sKh = reinterpret_cast<TIn *>(smem + K::OFF_KH);
-  TIn *sV = reinterpret_cast<TIn *>(smem + K::OFF_V);
-  float *sScan = reinterpret_cast<float *>(smem + K::OFF_SCAN);
-  float *sEL = reinterpret_cast<float *>(smem + K::OFF_EL);
   float *sPw = reinterpret_cast<float *>(smem + K::OFF_PW);
 
   // ---- which (b, h, segment, value slice): sibling slices share an XCD (id mod 8)
@@ -293,9 +300,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
   const int h = bh % a.H;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, li = lane & 15;
-  const int ecol = vs * kSlice + 16 * wave + li;    // this lane's value column
-  const bool wave_on = (vs * kSlice + 16 * wave) < a.dv;
+  const bool producer = wave >= 4;
   const bool state_only = a.state_only != 0;
 
   const int64_t t_begin = (int64_t)seg * a.seg_len;
@@ -303,31 +308,183 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
   if (t_end > a.T) t_end = a.T;
   const int nch = t_end > t_begin ? (int)((t_end - t_begin + C - 1) / C) : 0;
 
-  const TIn *gq = static_cast<const TIn *>(a.q) + (int64_t)bh * a.T * DK;
-  const TIn *gk = static_cast<const TIn *>(a.k) + (int64_t)bh * a.T * DK;
-  const TIn *gv = static_cast<const TIn *>(a.v) + (int64_t)bh * a.T * a.dv + vs * kSlice;
-  const float *ggate = (DECAY == DECAY_GATE) ? a.decay + (int64_t)bh * a.T * DK : nullptr;
-  TIn *gout = static_cast<TIn *>(a.out) + (int64_t)bh * a.T * a.dv;
-
-  // ---- gamma power table pw[n] = gamma^n, n = 0..C, and per-lane mask/scale tables
-  float dm[(DECAY == DECAY_GAMMA) ? K::NB : 1][4];
-  float rs[(DECAY == DECAY_GAMMA) ? K::NB : 1];
   if constexpr (DECAY == DECAY_GAMMA) {
-    const float gm = a.decay[h];
-    if (tid <= C) sPw[tid] = tid == 0 ? 1.f : exp2f((float)tid * log2f(gm));
-    __syncthreads();
-#pragma unroll
-    for (int d = 0; d < K::NB; ++d) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int x = 16 * d + li - 4 * g - r;
-        dm[d][r] = x >= 0 ? sPw[x] : 0.f;
-      }
-      rs[d] = sPw[16 * d + li + 1];
+    // gamma^n, n = 0..C, read by both roles
+    if (tid <= C) {
+      const float gm = a.decay[h];
+      sPw[tid] = tid == 0 ? 1.f : exp2f((float)tid * log2f(gm));
     }
+    __syncthreads();
   }
 
-  // ---- state: wave w holds H[:, 16w:16w+16] of this slice as NCB accumulator tiles
+  if (producer) {
+    // =========================== producer waves ===========================
+    const int p = wave - 4, ptid = tid - 256;
+    const int cgl = lane % K::LPR, rg = lane / K::LPR;
+    const int col0 = p * K::W + cgl * K::G;
+    const int row0 = rg * K::RPT;
+    const bool ld_on = lane < K::PACTIVE;
+    const int vcg = ptid & 7, vrg = ptid >> 3;
+    const int vrow0 = vrg * K::RPTV;
+    const bool vld_on = ptid < K::VACTIVE && (vs * kSlice + 8 * vcg) < a.dv;
+    const TIn *gq = static_cast<const TIn *>(a.q) + (int64_t)bh * a.T * DK + col0;
+    const TIn *gk = static_cast<const TIn *>(a.k) + (int64_t)bh * a.T * DK + col0;
+    const TIn *gv = static_cast<const TIn *>(a.v) + (int64_t)bh * a.T * a.dv + vs * kSlice + 8 * vcg;
+    const float *gg = (DECAY == DECAY_GATE) ? a.decay + (int64_t)bh * a.T * DK + col0 : nullptr;
+    float dprod[K::G];
+#pragma unroll
+    for (int c = 0; c < K::G; ++c) dprod[c] = 1.f;
+
+    auto load = [&](St &s, int n) {
+      const int64_t t0 = t_begin + (int64_t)n * C;
+      const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
+#pragma unroll
+      for (int r = 0; r < K::RPT; ++r) {
+        const int row = row0 + r;
+        // zero first, then load in place (an if/else of fp32 vector loads here crashes
+        // the gfx950 compiler's machine copy propagation)
+#pragma unroll
+        for (int i = 0; i < St::QW; ++i) { s.q[r][i] = 0u; s.k[r][i] = 0u; }
+        if constexpr (DECAY == DECAY_GATE) {
+#pragma unroll
+          for (int i = 0; i < K::G; ++i) s.a[r][i] = 0x3f800000u; // 1.0f
+        }
+        if (ld_on && row < L) {
+          const int64_t off = (t0 + row) * DK;
+          if (!state_only) ld_words<St::QW>(s.q[r], gq + off);
+          ld_words<St::QW>(s.k[r], gk + off);
+          if constexpr (DECAY == DECAY_GATE) ld_words<K::G>(s.a[r], gg + off);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < K::RPTV; ++r) {
+        const int row = vrow0 + r;
+#pragma unroll
+        for (int i = 0; i < 2 * K::ES; ++i) s.v[r][i] = 0u;
+        if (vld_on && row < L) ld_words<2 * K::ES>(s.v[r], gv + (t0 + row) * a.dv);
+      }
+    };
+
+    auto prep = [&](const St &s, int n) {
+      const int64_t t0 = t_begin + (int64_t)n * C;
+      const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
+      unsigned char *base = smem + (n % K::STAGES) * K::STAGE_BYTES;
+      TIn *sQ = reinterpret_cast<TIn *>(base + K::OFF_Q);
+      TIn *sK = reinterpret_cast<TIn *>(base + K::OFF_K);
+      TIn *sV = reinterpret_cast<TIn *>(base + K::OFF_V);
+      float *sEL = reinterpret_cast<float *>(base + K::OFF_EL);
+      // gate: b_i = local cumulative product over this lane's rows times the product of
+      // the row groups above it (inclusive shuffle scan across lanes rg*LPR + cgl)
+      float bc[DECAY == DECAY_GATE ? K::RPT : 1][K::G];
+      if constexpr (DECAY == DECAY_GATE) {
+#pragma unroll
+        for (int r = 0; r < K::RPT; ++r) {
+          unpack<float, K::G>(bc[r], s.a[r]);
+          if (r > 0) {
+#pragma unroll
+            for (int c = 0; c < K::G; ++c) bc[r][c] *= bc[r - 1][c];
+          }
+        }
+        float inc[K::G];
+#pragma unroll
+        for (int c = 0; c < K::G; ++c) inc[c] = bc[K::RPT - 1][c];
+#pragma unroll
+        for (int d = 1; d < K::NRG; d *= 2) {
+#pragma unroll
+          for (int c = 0; c < K::G; ++c) {
+            const float o = __shfl_up(inc[c], d * K::LPR, 64);
+            if (rg >= d) inc[c] *= o;
+          }
+        }
+        const int last = (K::NRG - 1) * K::LPR + cgl;
+#pragma unroll
+        for (int c = 0; c < K::G; ++c) {
+          const float tot = __shfl(inc[c], last, 64);
+          float ex = __shfl_up(inc[c], K::LPR, 64);
+          ex = rg == 0 ? 1.f : ex;
+#pragma unroll
+          for (int r = 0; r < K::RPT; ++r) bc[r][c] *= ex;
+          if (ld_on && rg == 0) sEL[col0 + c] = tot;
+          dprod[c] *= tot;
+        }
+      } else if constexpr (DECAY == DECAY_GAMMA) {
+        dprod[0] *= sPw[L];
+      }
+      if (ld_on) {
+#pragma unroll
+        for (int r = 0; r < K::RPT; ++r) {
+          const int row = row0 + r;
+          const bool valid = row < L;
+          float qv[K::G], kv[K::G];
+          unpack<TIn, K::G>(kv, s.k[r]);
+          unpack<TIn, K::G>(qv, s.q[r]);
+#pragma unroll
+          for (int c = 0; c < K::G; ++c) {
+            float kk = valid ? phi_f(kv[c], a.phi_elu1) : 0.f;
+            float qq = valid ? phi_f(qv[c], a.phi_elu1) : 0.f;
+            if constexpr (DECAY == DECAY_GATE) {
+              const float bb = bc[r][c];
+              qq *= bb;
+              kk *= rcp_f(bb);
+            }
+            kv[c] = kk;
+            qv[c] = qq;
+          }
+          st_lds<TIn, K::G>(sK + row * K::LQ + col0, kv);
+          if (!state_only) st_lds<TIn, K::G>(sQ + row * K::LQ + col0, qv);
+        }
+      }
+      if (ptid < K::VACTIVE) {
+#pragma unroll
+        for (int r = 0; r < K::RPTV; ++r) {
+          float vv[8];
+          unpack<TIn, 8>(vv, s.v[r]);
+          st_lds<TIn, 8>(sV + (vrow0 + r) * K::LV + 8 * vcg, vv);
+        }
+      }
+    };
+
+    if constexpr (K::PF == 2) {
+      St s0, s1;
+      if (nch > 0) load(s0, 0);
+      if (nch > 1) load(s1, 1);
+      for (int n = 0; n < nch; n += 2) {
+        prep(s0, n);
+        if (n + 2 < nch) load(s0, n + 2);
+        __syncthreads();
+        if constexpr (K::STAGES == 1) __syncthreads();
+        if (n + 1 < nch) {
+          prep(s1, n + 1);
+          if (n + 3 < nch) load(s1, n + 3);
+          __syncthreads();
+          if constexpr (K::STAGES == 1) __syncthreads();
+        }
+      }
+    } else {
+      St s0;
+      if (nch > 0) load(s0, 0);
+      for (int n = 0; n < nch; ++n) {
+        prep(s0, n);
+        if (n + 1 < nch) load(s0, n + 1);
+        __syncthreads();
+        if constexpr (K::STAGES == 1) __syncthreads();
+      }
+    }
+    if (a.seg_decay && vs == 0 && ld_on && rg == 0) {
+      float *sd = a.seg_decay + ((int64_t)bh * a.nseg + seg) * DK + col0;
+#pragma unroll
+      for (int c = 0; c < K::G; ++c) sd[c] = (DECAY == DECAY_GAMMA) ? dprod[0] : dprod[c];
+    }
+    return;
+  }
+
+  // =========================== consumer waves ===========================
+  const int g = lane >> 4, li = lane & 15;
+  const int ecol = vs * kSlice + 16 * wave + li; // this lane's value column
+  const bool wave_on = (vs * kSlice + 16 * wave) < a.dv;
+  TIn *gout = static_cast<TIn *>(a.out) + (int64_t)bh * a.T * a.dv;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
   f32x4 Hs[K::NCB];
   f32x4 Zs[NORM ? K::NCB : 1];
   {
@@ -343,166 +500,41 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
       }
     }
   }
-  float dprod = 1.f; // product of the chunk decays (thread c < DK), for segment decay
-
-  // ---- loader registers (one chunk ahead)
-  const int cg = tid % K::CG, rg = tid / K::CG;
-  const int row0 = rg * K::RPT;
-  const bool ld_on = tid < K::ACTIVE;
-  const int vcg = tid % (kSlice / 8), vrg = tid / (kSlice / 8);
-  const int vrow0 = vrg * K::RPTV;
-  const bool vld_on = tid < K::VACTIVE && (vs * kSlice + 8 * vcg) < a.dv;
-
-  Raw8<TIn> rq[K::RPT], rk[K::RPT], rv[K::RPTV];
-  Gate8 ra[DECAY == DECAY_GATE ? K::RPT : 1];
-
-  auto load_chunk = [&](int n) {
-    const int64_t t0 = t_begin + (int64_t)n * C;
-    const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
-#pragma unroll
-    for (int r = 0; r < K::RPT; ++r) {
-      const int row = row0 + r;
-      const bool on = ld_on && row < L;
-      const int64_t off = (t0 + row) * DK + cg * 8;
-      // zero first, then load in place (an if/else of fp32 vector loads here crashes
-      // the gfx950 compiler's machine copy propagation)
-      rq[r].zero();
-      rk[r].zero();
-      if constexpr (DECAY == DECAY_GATE) ra[r].ones();
-      if (on) {
-        if (!state_only) rq[r].load(gq + off);
-        rk[r].load(gk + off);
-        if constexpr (DECAY == DECAY_GATE) ra[r].load(ggate + off);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < K::RPTV; ++r) {
-      const int row = vrow0 + r;
-      rv[r].zero();
-      if (vld_on && row < L) rv[r].load(gv + (t0 + row) * a.dv + 8 * vcg);
-    }
-  };
-
-  if (nch > 0) load_chunk(0);
 
   for (int n = 0; n < nch; ++n) {
+    __syncthreads(); // stage n % STAGES holds chunk n
     const int64_t t0 = t_begin + (int64_t)n * C;
     const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
-    __syncthreads(); // previous chunk's LDS tiles are no longer read
-
-    // ---------------- S1 + S2: feature map, decay factors, operand tiles -> LDS
-    {
-      float qv[K::RPT][8], kv[K::RPT][8];
-#pragma unroll
-      for (int r = 0; r < K::RPT; ++r) {
-        const bool valid = (row0 + r) < L;
-        rq[r].to_f32(qv[r]);
-        rk[r].to_f32(kv[r]);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          qv[r][c] = valid ? phi_f(qv[r][c], a.phi_elu1) : 0.f;
-          kv[r][c] = valid ? phi_f(kv[r][c], a.phi_elu1) : 0.f;
-        }
-      }
-      float kh[8][K::RPT]; // Kh values, transposed for the column-major store
-      if constexpr (DECAY == DECAY_GATE) {
-        float bc[K::RPT][8];
-#pragma unroll
-        for (int r = 0; r < K::RPT; ++r) ra[r].to_f32(bc[r]);
-#pragma unroll
-        for (int r = 1; r < K::RPT; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) bc[r][c] *= bc[r - 1][c];
-        if (ld_on) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) sScan[rg * DK + cg * 8 + c] = bc[K::RPT - 1][c];
-        }
-        __syncthreads();
-        float pre[8], tot[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) pre[c] = tot[c] = 1.f;
-        for (int r2 = 0; r2 < K::NRG; ++r2) {
-          if (r2 == rg) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) tot[c] = pre[c];
-          }
-          const float4 s0 = *reinterpret_cast<const float4 *>(sScan + r2 * DK + cg * 8);
-          const float4 s1 = *reinterpret_cast<const float4 *>(sScan + r2 * DK + cg * 8 + 4);
-          pre[0] *= s0.x; pre[1] *= s0.y; pre[2] *= s0.z; pre[3] *= s0.w;
-          pre[4] *= s1.x; pre[5] *= s1.y; pre[6] *= s1.z; pre[7] *= s1.w;
-        }
-        // now pre = product over all row groups (chunk total), tot = exclusive prefix
-        if (ld_on && rg == 0) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) sEL[cg * 8 + c] = pre[c];
-        }
-#pragma unroll
-        for (int r = 0; r < K::RPT; ++r) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const float bb = tot[c] * bc[r][c];
-            const float ib = rcp_f(bb);
-            qv[r][c] *= bb;
-            kh[c][r] = kv[r][c] * (pre[c] * ib);
-            kv[r][c] *= ib;
-          }
-        }
-      } else if constexpr (DECAY == DECAY_GAMMA) {
-#pragma unroll
-        for (int r = 0; r < K::RPT; ++r) {
-          const int row = row0 + r;
-          const float sc = row < L ? sPw[L - 1 - row] : 0.f;
-#pragma unroll
-          for (int c = 0; c < 8; ++c) kh[c][r] = kv[r][c] * sc;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < K::RPT; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) kh[c][r] = kv[r][c];
-      }
-      if (ld_on) {
-#pragma unroll
-        for (int r = 0; r < K::RPT; ++r) {
-          if (!state_only) {
-            st8<TIn>(sQ + (row0 + r) * K::LQ + cg * 8, qv[r]);
-            st8<TIn>(sK + (row0 + r) * K::LQ + cg * 8, kv[r]);
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) stN<TIn, K::RPT>(sKh + (cg * 8 + c) * K::LT + row0, kh[c]);
-      }
-      if (tid < K::VACTIVE) {
-        float vv[K::RPTV][8];
-#pragma unroll
-        for (int r = 0; r < K::RPTV; ++r) rv[r].to_f32(vv[r]);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float col[K::RPTV];
-#pragma unroll
-          for (int r = 0; r < K::RPTV; ++r) col[r] = vv[r][c];
-          stN<TIn, K::RPTV>(sV + (8 * vcg + c) * K::LT + vrow0, col);
-        }
-      }
-    }
-    __syncthreads(); // operand tiles ready
-
-    if (n + 1 < nch) load_chunk(n + 1); // in flight during this chunk's MFMA work
-
-    // decay of the state across this chunk, per state row (key) c
-    if (a.seg_decay && tid < DK) {
-      if constexpr (DECAY == DECAY_GATE) dprod *= sEL[tid];
-      else if constexpr (DECAY == DECAY_GAMMA) dprod *= sPw[L];
-    }
+    const unsigned char *base = smem + (n % K::STAGES) * K::STAGE_BYTES;
+    const TIn *sQ = reinterpret_cast<const TIn *>(base + K::OFF_Q);
+    const TIn *sK = reinterpret_cast<const TIn *>(base + K::OFF_K);
+    const TIn *sV = reinterpret_cast<const TIn *>(base + K::OFF_V);
+    const float *sEL = reinterpret_cast<const float *>(base + K::OFF_EL);
 
     if (wave_on) {
-      const TIn *vrow = sV + (16 * wave + li) * K::LT;
+      // V^T operand fragments (rows e = 16 wave + li, K = tokens)
       F vf[K::NU_C];
 #pragma unroll
-      for (int u = 0; u < K::NU_C; ++u) vf[u] = ld_frag<TIn, K::HI_C>(vrow, u, g);
+      for (int u = 0; u < K::NU_C; ++u) vf[u] = ld_frag_t<TIn, K::HI_C>(sV, K::LV, 16 * wave, u, g, li);
 
       // ---------------- S3 + S6: outputs of this chunk
       if (!state_only) {
+        F hf[K::NU_DK], zf[NORM ? K::NU_DK : 1];
+#pragma unroll
+        for (int u = 0; u < K::NU_DK; ++u) {
+          if constexpr (K::BF) {
+            if constexpr (K::HI_DK) {
+              hf[u] = acc_frag_bf(Hs[2 * u], Hs[2 * u + 1]);
+              if constexpr (NORM) zf[u] = acc_frag_bf(Zs[2 * u], Zs[2 * u + 1]);
+            } else {
+              hf[u] = acc_frag_bf(Hs[0], zero4);
+              if constexpr (NORM) zf[u] = acc_frag_bf(Zs[0], zero4);
+            }
+          } else {
+            hf[u] = Hs[u];
+            if constexpr (NORM) zf[u] = Zs[u];
+          }
+        }
 #pragma unroll
         for (int ib = 0; ib < K::NB; ++ib) {
           if (16 * ib >= L) break;
@@ -511,8 +543,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
           for (int u = 0; u < K::NU_DK; ++u) qf[u] = ld_frag<TIn, K::HI_DK>(qrow, u, g);
 
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          f32x4 accd = {0.f, 0.f, 0.f, 0.f};
+          f32x4 acc = zero4, accd = zero4;
           // intra-chunk: A^T tiles (rows j, cols i) for j-blocks <= ib
 #pragma unroll
           for (int ju = 0; ju < K::NU_C; ++ju) {
@@ -521,18 +552,19 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
             for (int s = 0; s < K::TPU; ++s) {
               const int jb = ju * K::TPU + s;
-              f32x4 x = {0.f, 0.f, 0.f, 0.f};
+              f32x4 x = zero4;
               if (jb <= ib) {
                 const TIn *krow = sK + (16 * jb + li) * K::LQ;
 #pragma unroll
                 for (int u = 0; u < K::NU_DK; ++u) x = mma(x, ld_frag<TIn, K::HI_DK>(krow, u, g), qf[u]);
-                // element (j = 16 jb + 4g + r, i = 16 ib + li): causal mask and decay mask
+                // element (j = 16 jb + 4g + r, i = 16 ib + li)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
+                  const int dij = 16 * (ib - jb) + li - 4 * g - r; // i - j
                   if constexpr (DECAY == DECAY_GAMMA) {
-                    x[r] *= dm[ib - jb][r];
+                    x[r] = dij >= 0 ? x[r] * sPw[dij] : 0.f;
                   } else {
-                    if (jb == ib && (4 * g + r) > li) x[r] = 0.f;
+                    if (dij < 0) x[r] = 0.f;
                   }
                 }
               }
@@ -542,71 +574,81 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
             if constexpr (K::BF) af = acc_frag_bf(st[0], st[1]);
             else af = st[0];
             acc = mma(acc, vf[ju], af);
-            if constexpr (NORM) accd = mma(accd, ones_frag<TIn>(), af);
+            if constexpr (NORM) {
+              const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+              accd = mma(accd, frag_from<TIn>(one), af);
+            }
           }
-          // inter-chunk: H^T Qt^T with H taken from the accumulators
-          f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
-          f32x4 accd2 = {0.f, 0.f, 0.f, 0.f};
+          // inter-chunk: H^T Qt^T
+          f32x4 acc2 = zero4, accd2 = zero4;
 #pragma unroll
           for (int u = 0; u < K::NU_DK; ++u) {
-            F hf, zf;
-            if constexpr (K::BF) {
-              const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-              if constexpr (K::HI_DK) {
-                hf = acc_frag_bf(Hs[2 * u], Hs[2 * u + 1]);
-                if constexpr (NORM) zf = acc_frag_bf(Zs[2 * u], Zs[2 * u + 1]);
-              } else {
-                hf = acc_frag_bf(Hs[0], zero4);
-                if constexpr (NORM) zf = acc_frag_bf(Zs[0], zero4);
-              }
-            } else {
-              hf = Hs[u];
-              if constexpr (NORM) zf = Zs[u];
-            }
-            acc2 = mma(acc2, hf, qf[u]);
-            if constexpr (NORM) accd2 = mma(accd2, zf, qf[u]);
+            acc2 = mma(acc2, hf[u], qf[u]);
+            if constexpr (NORM) accd2 = mma(accd2, zf[u], qf[u]);
           }
           if constexpr (DECAY == DECAY_GAMMA) {
-            acc2 *= rs[ib];
-            if constexpr (NORM) accd2 *= rs[ib];
+            const float rsc = sPw[16 * ib + li + 1];
+            acc2 *= rsc;
+            if constexpr (NORM) accd2 *= rsc;
           }
           acc += acc2;
           if constexpr (NORM) {
             accd += accd2;
-            const float inv = rcp_f(accd[0]); // every row of the ones tile holds the denominator
-            acc *= inv;
+            acc *= rcp_f(accd[0]); // every row of the ones tile holds the denominator
           }
           const int i = 16 * ib + li;
           if (i < L) st_out4<TIn>(gout + (t0 + i) * a.dv + vs * kSlice + 16 * wave + 4 * g, acc);
         }
       }
 
-      // ---------------- S4 + S5: H <- diag(decay over chunk) H + Kh^T V
+      // ---------------- S4 + S5: state update
+      F vu[K::NU_C], wz[NORM ? K::NU_C : 1];
+#pragma unroll
+      for (int u = 0; u < K::NU_C; ++u) {
+        if constexpr (DECAY == DECAY_GAMMA) {
+          // V' = diag(gamma^{L-1-j}) V over this fragment's K slots j
+          float sc[8];
+#pragma unroll
+          for (int s = 0; s < (K::BF ? 8 : 4); ++s) {
+            const int j = K::BF ? (32 * u + (s < 4 ? 0 : 16) + 4 * g + (s & 3)) : (16 * u + 4 * g + s);
+            sc[s] = j < L ? sPw[L - 1 - j] : 0.f;
+          }
+          vu[u] = scale_frag(vf[u], sc);
+          if constexpr (NORM) wz[u] = frag_from<TIn>(sc);
+        } else {
+          vu[u] = vf[u];
+          if constexpr (NORM) {
+            const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+            wz[u] = frag_from<TIn>(one);
+          }
+        }
+      }
 #pragma unroll
       for (int cb = 0; cb < K::NCB; ++cb) {
+        if constexpr (DECAY == DECAY_GAMMA) {
+          const float gl = sPw[L];
+          Hs[cb] *= gl;
+          if constexpr (NORM) Zs[cb] *= gl;
+        }
+#pragma unroll
+        for (int u = 0; u < K::NU_C; ++u) {
+          const F kf = ld_frag_t<TIn, K::HI_C>(sK, K::LQ, 16 * cb, u, g, li);
+          Hs[cb] = mma(Hs[cb], kf, vu[u]);
+          if constexpr (NORM) Zs[cb] = mma(Zs[cb], kf, wz[u]);
+        }
         if constexpr (DECAY == DECAY_GATE) {
           const float4 el = *reinterpret_cast<const float4 *>(sEL + 16 * cb + 4 * g);
           Hs[cb][0] *= el.x; Hs[cb][1] *= el.y; Hs[cb][2] *= el.z; Hs[cb][3] *= el.w;
           if constexpr (NORM) {
             Zs[cb][0] *= el.x; Zs[cb][1] *= el.y; Zs[cb][2] *= el.z; Zs[cb][3] *= el.w;
           }
-        } else if constexpr (DECAY == DECAY_GAMMA) {
-          const float gl = sPw[L];
-          Hs[cb] *= gl;
-          if constexpr (NORM) Zs[cb] *= gl;
-        }
-        const TIn *khrow = sKh + (16 * cb + li) * K::LT;
-#pragma unroll
-        for (int u = 0; u < K::NU_C; ++u) {
-          const F kf = ld_frag<TIn, K::HI_C>(khrow, u, g);
-          Hs[cb] = mma(Hs[cb], kf, vf[u]);
-          if constexpr (NORM) Zs[cb] = mma(Zs[cb], kf, ones_frag<TIn>());
         }
       }
     }
+    if constexpr (K::STAGES == 1) __syncthreads(); // stage free for the next chunk
   }
 
-  // ---- end state and segment decay
+  // ---- end state
   if (a.fin && wave_on) {
     float *fo = a.fin + (int64_t)bh * a.fin_bh_stride + (int64_t)seg * a.fin_seg_stride;
 #pragma unroll
@@ -621,8 +663,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
       }
     }
   }
-  if (a.seg_decay && vs == 0 && tid < DK)
-    a.seg_decay[((int64_t)bh * a.nseg + seg) * DK + tid] = dprod;
 }
 
 } // namespace fla

@@ -77,8 +77,8 @@ def fwd_raw(lib, *, q=BOGUS, k=BOGUS, v=BOGUS, gate=None, init=None, out=BOGUS, 
     (dict(dv=512), fla.FLA_ERR_UNSUPPORTED),
     (dict(chunk=512), fla.FLA_ERR_UNSUPPORTED),
     (dict(chunk=8), fla.FLA_ERR_UNSUPPORTED),
-    (dict(dk=256, chunk=128, flags=fla.FLA_BF16), fla.FLA_ERR_UNSUPPORTED),  # tiles > LDS
-    (dict(dk=256, chunk=64), fla.FLA_ERR_UNSUPPORTED),                       # fp32 tiles > LDS
+    (dict(dk=256, chunk=128), fla.FLA_ERR_UNSUPPORTED),                      # fp32 tiles > LDS
+    (dict(dk=128, chunk=128), fla.FLA_ERR_UNSUPPORTED),                      # fp32 tiles > LDS
 ])
 def test_fwd_rejects_on_host(lib, kw, expected):
     assert fwd_raw(lib, **kw) == expected

@@ -95,17 +95,16 @@ CHUNKS = [16, 32, 64, 128]
 
 
 def _supported(dtype, dk, chunk, decay):
-    """The library's LDS budget for one workgroup (160 KiB on gfx950): operand tiles
-    Qt, Kt [C][dk+pad], Kh^T [dk][C+pad], V^T [64][C+pad], plus the decay scratch."""
+    """The library's LDS budget for one workgroup (160 KiB on gfx950): one stage of the
+    row-major operand tiles Qt, Kt [C][dk+pad] and V [C][64+pad], the per-key chunk
+    decay (gate) and the gamma power table."""
     es = 2 if dtype == "bf16" else 4
     pad = 16 // es
-    lds = (2 * chunk * (dk + pad) + (dk + 64) * (chunk + pad)) * es
+    stage = (2 * chunk * (dk + pad) + chunk * (64 + pad)) * es
     if decay == "gate":
-        rpt = max(1, chunk * dk // 8 // 256)
-        lds += (chunk // rpt) * dk * 4 + dk * 4
-    elif decay == "gamma":
-        lds += ((chunk + 4) // 4) * 16
-    return lds <= 163840
+        stage += dk * 4
+    pw = ((chunk + 4) // 4) * 16 if decay == "gamma" else 0
+    return stage + pw <= 163840
 
 
 SWEEP = []
@@ -132,10 +131,10 @@ def test_shape_sweep(dtype, dk, dv, chunk, T, decay, norm, init):
 
 
 def test_unsupported_combination_raises():
-    q = torch.zeros((1, 1, 64, 256), dtype=torch.float32, device="cuda")
-    v = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda")
+    q = torch.zeros((1, 1, 128, 256), dtype=torch.float32, device="cuda")
+    v = torch.zeros((1, 1, 128, 64), dtype=torch.float32, device="cuda")
     with pytest.raises(fla.FlaError) as e:
-        fla.fwd(q, q, v, chunk=64)
+        fla.fwd(q, q, v, chunk=128)
     assert e.value.status == fla.FLA_ERR_UNSUPPORTED
 
 
