@@ -105,6 +105,27 @@ def cpu_baseline(w, inp, out_gpu, fin_gpu, budget_s: float):
         "sample_heads": n_heads}
 
 
+def copy_calibration(torch, steps, warmup):
+    """A plain copy of 1 GiB: reads and writes exactly 2^30 bytes per launch."""
+    n = 1 << 30
+    src = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+                      "ms_per_copy": ms, "copy_GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +135,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 1 GiB device copy instead (HBM reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters and the achievable copy rate)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -124,6 +148,11 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch, args.steps, args.warmup)
+        return
+
     import chunkwise_causal_linear_amd as fla
     from workloads import HEADLINE, WORKLOADS, generate_torch
 

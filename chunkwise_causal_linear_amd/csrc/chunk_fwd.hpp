@@ -13,13 +13,13 @@
 //   none:  the gamma form with gamma = 1.
 // The normaliser z is the state column of an all-ones value: den = A 1 + Qt z.
 //
-// Workgroup = 8 waves for one (b, h, segment, 64-wide slice of dv):
-//   waves 0..3 (consumers) each own 16 value columns: the fp32 state H[:, 16w:16w+16]
-//     lives in MFMA accumulators for the whole sequence; per chunk they run
+// Workgroup = 6 or 8 waves for one (b, h, segment, 64-wide slice of dv):
+//   consumer waves (2 for dk <= 128, else 4) each own 32 or 16 value columns: their
+//     slice of the fp32 state H lives in MFMA accumulators for the whole sequence; per chunk they run
 //     S3  A^T = Kt Qt^T tile by tile, causal / decay mask, O^T += V^T A^T,
 //     S6  O^T += H^T Qt^T (H converted to MFMA operands in registers), normalise, store,
 //     S4/S5  H <- decay (H + Kt^T V) (or gamma^L H + Kt^T V');
-//   waves 4..7 (producers) prefetch q, k, v, gate one or two chunks ahead in registers,
+//   4 producer waves prefetch q, k, v, gate one or two chunks ahead in registers,
 //     apply phi (S1) and the decay factors (S2: per-key cumulative product down the chunk
 //     by a wave-level shuffle scan), and write Qt, Kt, V row-major into an LDS stage.
 // With two LDS stages producers prepare chunk n+1 while consumers compute chunk n
@@ -50,7 +50,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum : int { DECAY_NONE = 0, DECAY_GAMMA = 1, DECAY_GATE = 2 };
 
-constexpr int kThreads = 512;   // 4 consumer + 4 producer waves
+constexpr int kMaxThreads = 512; // consumer + 4 producer waves
 constexpr int kSlice = 64;      // value columns per workgroup (16 per consumer wave)
 constexpr int kMaxLds = 163840; // gfx950 LDS per workgroup
 
@@ -86,10 +86,30 @@ struct Cfg {
   static constexpr int NU_C = (NB + TPU - 1) / TPU;
   static constexpr bool HI_DK = !(BF && DK == 16);
   static constexpr bool HI_C = !(BF && C == 16);
+  // consumer waves: NCW waves, each owning ET 16-column tiles of the 64-wide value slice
+  // (two tiles per wave share every Qt/Kt operand fragment when the state fits)
+#ifdef FLA_FORCE_NCW
+  static constexpr int NCW = FLA_FORCE_NCW;
+#else
+  // the gate's producers are VALU-heavy: give two SIMDs to producers alone
+  static constexpr int NCW = (DECAY == DECAY_GATE && DK <= 128) ? 2 : 4;
+#endif
+  static constexpr int ET = 4 / NCW;
+  static constexpr int NT = 64 * (NCW + 4);     // + 4 producer waves
+  // keep the Kt fragments of earlier row blocks in registers (unrolled row-block loop)
+#ifdef FLA_FORCE_KCACHE
+  static constexpr bool KCACHE = FLA_FORCE_KCACHE;
+#else
+  static constexpr bool KCACHE = DK <= 128 && C <= 64 && ET == 1;
+#endif
   // producer mapping for q/k/gate: wave p owns columns [p W, (p+1) W); a lane owns G
   // consecutive columns and RPT consecutive rows; LPR lanes share a row.
   static constexpr int W = DK / 4;
+#ifdef FLA_FORCE_G
+  static constexpr int G = W >= FLA_FORCE_G ? FLA_FORCE_G : W;
+#else
   static constexpr int G = W >= 8 ? 8 : W;
+#endif
   static constexpr int LPR = W / G;
   static constexpr int RP = 64 / LPR;
   static constexpr int RPT = C >= RP ? C / RP : 1;
@@ -101,7 +121,7 @@ struct Cfg {
   // registers held per prefetched chunk (32-bit words per producer lane)
   static constexpr int STAGE_WORDS = 2 * RPT * G * ES / 4 + (DECAY == DECAY_GATE ? RPT * G : 0) +
                                      RPTV * 8 * ES / 4;
-  static constexpr int PF = (STAGE_WORDS <= 80 && C <= 64 && !NORM) ? 2 : 1; // chunks ahead
+  static constexpr int PF = (STAGE_WORDS <= 64 && C <= 64 && !NORM) ? 2 : 1; // chunks ahead
   // LDS map (bytes): [STAGES] x {Qt, Kt, V, eL}, then the gamma power table
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_K = OFF_Q + C * LQ * ES;
@@ -255,6 +275,15 @@ __device__ __forceinline__ Frag<TIn> frag_from(const float *s) {
   }
 }
 
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1 (compile-time indices).
+template <int B, int E, typename Fn>
+__device__ __forceinline__ void static_for(Fn &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Output store of 4 adjacent values (an O^T tile lane's rows 4g..4g+3).
 template <typename TIn>
 __device__ __forceinline__ void st_out4(TIn *p, f32x4 o) {
@@ -281,7 +310,7 @@ struct Staged {
 // The fused chunk kernel.
 
 template <typename TIn, int DK, int C, int DECAY, bool NORM>
-__global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
   using K = Cfg<TIn, DK, C, DECAY, NORM>;
   using F = Frag<TIn>;
   using St = Staged<TIn, DK, C, DECAY, NORM>;
@@ -300,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
   const int h = bh % a.H;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool producer = wave >= 4;
+  const bool producer = wave >= K::NCW;
   const bool state_only = a.state_only != 0;
 
   const int64_t t_begin = (int64_t)seg * a.seg_len;
@@ -319,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
 
   if (producer) {
     // =========================== producer waves ===========================
-    const int p = wave - 4, ptid = tid - 256;
+    const int p = wave - K::NCW, ptid = tid - 64 * K::NCW;
     const int cgl = lane % K::LPR, rg = lane / K::LPR;
     const int col0 = p * K::W + cgl * K::G;
     const int row0 = rg * K::RPT;
@@ -335,37 +364,53 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
     for (int c = 0; c < K::G; ++c) dprod[c] = 1.f;
 
-    auto load = [&](St &s, int n) {
-      const int64_t t0 = t_begin + (int64_t)n * C;
-      const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
+    // gate loads are issued separately so they can go out as soon as the scan has used
+    // the previous chunk's gate registers
+    auto load_gate = [&](St &s, int n) {
+      if constexpr (DECAY == DECAY_GATE) {
+        const int64_t t0 = t_begin + (int64_t)n * C;
+        const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
 #pragma unroll
-      for (int r = 0; r < K::RPT; ++r) {
-        const int row = row0 + r;
-        // zero first, then load in place (an if/else of fp32 vector loads here crashes
-        // the gfx950 compiler's machine copy propagation)
-#pragma unroll
-        for (int i = 0; i < St::QW; ++i) { s.q[r][i] = 0u; s.k[r][i] = 0u; }
-        if constexpr (DECAY == DECAY_GATE) {
+        for (int r = 0; r < K::RPT; ++r) {
+          const int row = row0 + r;
+          // zero first, then load in place (an if/else of fp32 vector loads here crashes
+          // the gfx950 compiler's machine copy propagation)
 #pragma unroll
           for (int i = 0; i < K::G; ++i) s.a[r][i] = 0x3f800000u; // 1.0f
+          if (ld_on && row < L) ld_words<K::G>(s.a[r], gg + (t0 + row) * DK);
         }
-        if (ld_on && row < L) {
-          const int64_t off = (t0 + row) * DK;
-          if (!state_only) ld_words<St::QW>(s.q[r], gq + off);
-          ld_words<St::QW>(s.k[r], gk + off);
-          if constexpr (DECAY == DECAY_GATE) ld_words<K::G>(s.a[r], gg + off);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < K::RPTV; ++r) {
-        const int row = vrow0 + r;
-#pragma unroll
-        for (int i = 0; i < 2 * K::ES; ++i) s.v[r][i] = 0u;
-        if (vld_on && row < L) ld_words<2 * K::ES>(s.v[r], gv + (t0 + row) * a.dv);
       }
     };
+    // q/k row r and v row r of chunk n
+    auto load_qk = [&](St &s, int n, int r) {
+      const int64_t t0 = t_begin + (int64_t)n * C;
+      const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
+      const int row = row0 + r;
+#pragma unroll
+      for (int i = 0; i < St::QW; ++i) { s.q[r][i] = 0u; s.k[r][i] = 0u; }
+      if (ld_on && row < L) {
+        const int64_t off = (t0 + row) * DK;
+        if (!state_only) ld_words<St::QW>(s.q[r], gq + off);
+        ld_words<St::QW>(s.k[r], gk + off);
+      }
+    };
+    auto load_v = [&](St &s, int n, int r) {
+      const int64_t t0 = t_begin + (int64_t)n * C;
+      const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
+      const int row = vrow0 + r;
+#pragma unroll
+      for (int i = 0; i < 2 * K::ES; ++i) s.v[r][i] = 0u;
+      if (vld_on && row < L) ld_words<2 * K::ES>(s.v[r], gv + (t0 + row) * a.dv);
+    };
+    auto load = [&](St &s, int n) {
+      load_gate(s, n);
+#pragma unroll
+      for (int r = 0; r < K::RPT; ++r) load_qk(s, n, r);
+#pragma unroll
+      for (int r = 0; r < K::RPTV; ++r) load_v(s, n, r);
+    };
 
-    auto prep = [&](const St &s, int n) {
+    auto prep = [&](St &s, int n, bool next) {
       const int64_t t0 = t_begin + (int64_t)n * C;
       const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
       unsigned char *base = smem + (n % K::STAGES) * K::STAGE_BYTES;
@@ -376,6 +421,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
       // gate: b_i = local cumulative product over this lane's rows times the product of
       // the row groups above it (inclusive shuffle scan across lanes rg*LPR + cgl)
       float bc[DECAY == DECAY_GATE ? K::RPT : 1][K::G];
+      float rb[DECAY == DECAY_GATE ? K::RPT : 1][K::G]; // 1 / b
       if constexpr (DECAY == DECAY_GATE) {
 #pragma unroll
         for (int r = 0; r < K::RPT; ++r) {
@@ -390,48 +436,75 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
         for (int c = 0; c < K::G; ++c) inc[c] = bc[K::RPT - 1][c];
 #pragma unroll
         for (int d = 1; d < K::NRG; d *= 2) {
+          const int src = (lane - d * K::LPR) < 0 ? 0 : 4 * (lane - d * K::LPR);
 #pragma unroll
           for (int c = 0; c < K::G; ++c) {
-            const float o = __shfl_up(inc[c], d * K::LPR, 64);
-            if (rg >= d) inc[c] *= o;
+            const float o = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(inc[c])));
+            inc[c] = rg >= d ? inc[c] * o : inc[c];
           }
         }
-        const int last = (K::NRG - 1) * K::LPR + cgl;
+        const int src_last = 4 * ((K::NRG - 1) * K::LPR + cgl);
+        const int src_prev = (lane - K::LPR) < 0 ? 0 : 4 * (lane - K::LPR);
+        float tot[K::G];
 #pragma unroll
         for (int c = 0; c < K::G; ++c) {
-          const float tot = __shfl(inc[c], last, 64);
-          float ex = __shfl_up(inc[c], K::LPR, 64);
-          ex = rg == 0 ? 1.f : ex;
+          tot[c] = __int_as_float(__builtin_amdgcn_ds_bpermute(src_last, __float_as_int(inc[c])));
+          const float pv = __int_as_float(__builtin_amdgcn_ds_bpermute(src_prev, __float_as_int(inc[c])));
+          const float ex = rg == 0 ? 1.f : pv;
 #pragma unroll
           for (int r = 0; r < K::RPT; ++r) bc[r][c] *= ex;
-          if (ld_on && rg == 0) sEL[col0 + c] = tot;
-          dprod[c] *= tot;
+          dprod[c] *= tot[c];
+          // one reciprocal per column: 1/b_r = (1/b_last) * prod_{s>r} alpha_s
+          rb[K::RPT - 1][c] = rcp_f(bc[K::RPT - 1][c]);
+#pragma unroll
+          for (int r = K::RPT - 2; r >= 0; --r)
+            rb[r][c] = rb[r + 1][c] * __uint_as_float(s.a[r + 1][c]);
         }
+        if (ld_on && rg == 0) st_lds<float, K::G>(sEL + col0, tot);
+        if (next) load_gate(s, n + K::PF);
       } else if constexpr (DECAY == DECAY_GAMMA) {
         dprod[0] *= sPw[L];
       }
-      if (ld_on) {
+      // feature map (compile-time choice), decay factors, bf16/fp32 tiles -> LDS
+      auto rows = [&](auto elu_c, auto full_c) {
+        constexpr bool ELU = decltype(elu_c)::value, FULL = decltype(full_c)::value;
 #pragma unroll
         for (int r = 0; r < K::RPT; ++r) {
           const int row = row0 + r;
-          const bool valid = row < L;
           float qv[K::G], kv[K::G];
           unpack<TIn, K::G>(kv, s.k[r]);
           unpack<TIn, K::G>(qv, s.q[r]);
 #pragma unroll
           for (int c = 0; c < K::G; ++c) {
-            float kk = valid ? phi_f(kv[c], a.phi_elu1) : 0.f;
-            float qq = valid ? phi_f(qv[c], a.phi_elu1) : 0.f;
+            float kk = kv[c], qq = qv[c];
+            if constexpr (ELU) {
+              kk = kk > 0.f ? kk + 1.f : __expf(kk);
+              qq = qq > 0.f ? qq + 1.f : __expf(qq);
+            }
+            if constexpr (!FULL) {
+              kk = row < L ? kk : 0.f;
+              qq = row < L ? qq : 0.f;
+            }
             if constexpr (DECAY == DECAY_GATE) {
-              const float bb = bc[r][c];
-              qq *= bb;
-              kk *= rcp_f(bb);
+              qq *= bc[r][c];
+              kk *= rb[r][c];
             }
             kv[c] = kk;
             qv[c] = qq;
           }
           st_lds<TIn, K::G>(sK + row * K::LQ + col0, kv);
           if (!state_only) st_lds<TIn, K::G>(sQ + row * K::LQ + col0, qv);
+        }
+      };
+      if (ld_on) {
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        if (a.phi_elu1) {
+          if (L == C) rows(T_{}, T_{});
+          else rows(T_{}, F_{});
+        } else {
+          if (L == C) rows(F_{}, T_{});
+          else rows(F_{}, F_{});
         }
       }
       if (ptid < K::VACTIVE) {
@@ -442,6 +515,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
           st_lds<TIn, 8>(sV + (vrow0 + r) * K::LV + 8 * vcg, vv);
         }
       }
+      if (next) {
+#pragma unroll
+        for (int r = 0; r < K::RPT; ++r) load_qk(s, n + K::PF, r);
+#pragma unroll
+        for (int r = 0; r < K::RPTV; ++r) load_v(s, n + K::PF, r);
+      }
     };
 
     if constexpr (K::PF == 2) {
@@ -449,13 +528,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
       if (nch > 0) load(s0, 0);
       if (nch > 1) load(s1, 1);
       for (int n = 0; n < nch; n += 2) {
-        prep(s0, n);
-        if (n + 2 < nch) load(s0, n + 2);
+        prep(s0, n, n + 2 < nch);
         __syncthreads();
         if constexpr (K::STAGES == 1) __syncthreads();
         if (n + 1 < nch) {
-          prep(s1, n + 1);
-          if (n + 3 < nch) load(s1, n + 3);
+          prep(s1, n + 1, n + 3 < nch);
           __syncthreads();
           if constexpr (K::STAGES == 1) __syncthreads();
         }
@@ -464,8 +541,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
       St s0;
       if (nch > 0) load(s0, 0);
       for (int n = 0; n < nch; ++n) {
-        prep(s0, n);
-        if (n + 1 < nch) load(s0, n + 1);
+        prep(s0, n, n + 1 < nch);
         __syncthreads();
         if constexpr (K::STAGES == 1) __syncthreads();
       }
@@ -480,12 +556,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
 
   // =========================== consumer waves ===========================
   const int g = lane >> 4, li = lane & 15;
-  const int ecol = vs * kSlice + 16 * wave + li; // this lane's value column
-  const bool wave_on = (vs * kSlice + 16 * wave) < a.dv;
+  const int e0 = vs * kSlice + 16 * K::ET * wave; // first value column of this wave
+  bool tile_on[K::ET];
+#pragma unroll
+  for (int t = 0; t < K::ET; ++t) tile_on[t] = e0 + 16 * t < a.dv;
+  const bool wave_on = tile_on[0];
   TIn *gout = static_cast<TIn *>(a.out) + (int64_t)bh * a.T * a.dv;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  f32x4 Hs[K::NCB];
+  f32x4 Hs[K::ET][K::NCB];
   f32x4 Zs[NORM ? K::NCB : 1];
   {
     const float *ini = a.init ? a.init + (int64_t)bh * a.init_bh_stride + (int64_t)seg * a.init_seg_stride
@@ -495,7 +574,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int c = 16 * cb + 4 * g + r;
-        Hs[cb][r] = (ini && ecol < a.dv) ? ini[(int64_t)c * a.ncol + ecol] : 0.f;
+#pragma unroll
+        for (int t = 0; t < K::ET; ++t) {
+          const int e = e0 + 16 * t + li;
+          Hs[t][cb][r] = (ini && e < a.dv) ? ini[(int64_t)c * a.ncol + e] : 0.f;
+        }
         if constexpr (NORM) Zs[cb][r] = ini ? ini[(int64_t)c * a.ncol + a.dv] : 0.f;
       }
     }
@@ -512,138 +595,191 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
     const float *sEL = reinterpret_cast<const float *>(base + K::OFF_EL);
 
     if (wave_on) {
-      // V^T operand fragments (rows e = 16 wave + li, K = tokens)
-      F vf[K::NU_C];
+      // V^T operand fragments (rows e, K = tokens); tiles past dv hold zeros
+      F vf[K::ET][K::NU_C];
 #pragma unroll
-      for (int u = 0; u < K::NU_C; ++u) vf[u] = ld_frag_t<TIn, K::HI_C>(sV, K::LV, 16 * wave, u, g, li);
+      for (int t = 0; t < K::ET; ++t)
+#pragma unroll
+        for (int u = 0; u < K::NU_C; ++u)
+          vf[t][u] = ld_frag_t<TIn, K::HI_C>(sV, K::LV, 16 * (K::ET * wave + t), u, g, li);
 
-      // ---------------- S3 + S6: outputs of this chunk
-      if (!state_only) {
-        F hf[K::NU_DK], zf[NORM ? K::NU_DK : 1];
-#pragma unroll
-        for (int u = 0; u < K::NU_DK; ++u) {
-          if constexpr (K::BF) {
-            if constexpr (K::HI_DK) {
-              hf[u] = acc_frag_bf(Hs[2 * u], Hs[2 * u + 1]);
-              if constexpr (NORM) zf[u] = acc_frag_bf(Zs[2 * u], Zs[2 * u + 1]);
-            } else {
-              hf[u] = acc_frag_bf(Hs[0], zero4);
-              if constexpr (NORM) zf[u] = acc_frag_bf(Zs[0], zero4);
-            }
-          } else {
-            hf[u] = Hs[u];
-            if constexpr (NORM) zf[u] = Zs[u];
-          }
-        }
-#pragma unroll
-        for (int ib = 0; ib < K::NB; ++ib) {
-          if (16 * ib >= L) break;
-          const TIn *qrow = sQ + (16 * ib + li) * K::LQ;
-          F qf[K::NU_DK];
-#pragma unroll
-          for (int u = 0; u < K::NU_DK; ++u) qf[u] = ld_frag<TIn, K::HI_DK>(qrow, u, g);
-
-          f32x4 acc = zero4, accd = zero4;
-          // intra-chunk: A^T tiles (rows j, cols i) for j-blocks <= ib
-#pragma unroll
-          for (int ju = 0; ju < K::NU_C; ++ju) {
-            if (ju * K::TPU > ib) break;
-            f32x4 st[K::TPU];
-#pragma unroll
-            for (int s = 0; s < K::TPU; ++s) {
-              const int jb = ju * K::TPU + s;
-              f32x4 x = zero4;
-              if (jb <= ib) {
-                const TIn *krow = sK + (16 * jb + li) * K::LQ;
-#pragma unroll
-                for (int u = 0; u < K::NU_DK; ++u) x = mma(x, ld_frag<TIn, K::HI_DK>(krow, u, g), qf[u]);
-                // element (j = 16 jb + 4g + r, i = 16 ib + li)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                  const int dij = 16 * (ib - jb) + li - 4 * g - r; // i - j
-                  if constexpr (DECAY == DECAY_GAMMA) {
-                    x[r] = dij >= 0 ? x[r] * sPw[dij] : 0.f;
-                  } else {
-                    if (dij < 0) x[r] = 0.f;
-                  }
-                }
-              }
-              st[s] = x;
-            }
-            F af;
-            if constexpr (K::BF) af = acc_frag_bf(st[0], st[1]);
-            else af = st[0];
-            acc = mma(acc, vf[ju], af);
-            if constexpr (NORM) {
-              const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-              accd = mma(accd, frag_from<TIn>(one), af);
-            }
-          }
-          // inter-chunk: H^T Qt^T
-          f32x4 acc2 = zero4, accd2 = zero4;
-#pragma unroll
-          for (int u = 0; u < K::NU_DK; ++u) {
-            acc2 = mma(acc2, hf[u], qf[u]);
-            if constexpr (NORM) accd2 = mma(accd2, zf[u], qf[u]);
-          }
-          if constexpr (DECAY == DECAY_GAMMA) {
-            const float rsc = sPw[16 * ib + li + 1];
-            acc2 *= rsc;
-            if constexpr (NORM) accd2 *= rsc;
-          }
-          acc += acc2;
-          if constexpr (NORM) {
-            accd += accd2;
-            acc *= rcp_f(accd[0]); // every row of the ones tile holds the denominator
-          }
-          const int i = 16 * ib + li;
-          if (i < L) st_out4<TIn>(gout + (t0 + i) * a.dv + vs * kSlice + 16 * wave + 4 * g, acc);
-        }
-      }
-
-      // ---------------- S4 + S5: state update
-      F vu[K::NU_C], wz[NORM ? K::NU_C : 1];
+      // operands of the state update: V (gamma: V' = diag(gamma^{L-1-j}) V) and, for z,
+      // the all-ones (gamma: decay) column
+      F vu[K::ET][K::NU_C], wz[NORM ? K::NU_C : 1];
 #pragma unroll
       for (int u = 0; u < K::NU_C; ++u) {
         if constexpr (DECAY == DECAY_GAMMA) {
-          // V' = diag(gamma^{L-1-j}) V over this fragment's K slots j
           float sc[8];
 #pragma unroll
-          for (int s = 0; s < (K::BF ? 8 : 4); ++s) {
-            const int j = K::BF ? (32 * u + (s < 4 ? 0 : 16) + 4 * g + (s & 3)) : (16 * u + 4 * g + s);
-            sc[s] = j < L ? sPw[L - 1 - j] : 0.f;
+          for (int q = 0; q < (K::BF ? 8 : 4); ++q) {
+            const int j = K::BF ? (32 * u + (q < 4 ? 0 : 16) + 4 * g + (q & 3)) : (16 * u + 4 * g + q);
+            sc[q] = j < L ? sPw[L - 1 - j] : 0.f;
           }
-          vu[u] = scale_frag(vf[u], sc);
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) vu[t][u] = scale_frag(vf[t][u], sc);
           if constexpr (NORM) wz[u] = frag_from<TIn>(sc);
         } else {
-          vu[u] = vf[u];
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) vu[t][u] = vf[t][u];
           if constexpr (NORM) {
             const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
             wz[u] = frag_from<TIn>(one);
           }
         }
       }
-#pragma unroll
-      for (int cb = 0; cb < K::NCB; ++cb) {
+      const float gl = (DECAY == DECAY_GAMMA) ? sPw[L] : 1.f;
+
+      // S4 + S5 for state row block cb: H <- decay (H + Kt^T V) (gamma: gamma^L H + Kt^T V')
+      auto state_block = [&](const int cb) {
         if constexpr (DECAY == DECAY_GAMMA) {
-          const float gl = sPw[L];
-          Hs[cb] *= gl;
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) Hs[t][cb] *= gl;
           if constexpr (NORM) Zs[cb] *= gl;
         }
 #pragma unroll
         for (int u = 0; u < K::NU_C; ++u) {
           const F kf = ld_frag_t<TIn, K::HI_C>(sK, K::LQ, 16 * cb, u, g, li);
-          Hs[cb] = mma(Hs[cb], kf, vu[u]);
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) Hs[t][cb] = mma(Hs[t][cb], kf, vu[t][u]);
           if constexpr (NORM) Zs[cb] = mma(Zs[cb], kf, wz[u]);
         }
         if constexpr (DECAY == DECAY_GATE) {
           const float4 el = *reinterpret_cast<const float4 *>(sEL + 16 * cb + 4 * g);
-          Hs[cb][0] *= el.x; Hs[cb][1] *= el.y; Hs[cb][2] *= el.z; Hs[cb][3] *= el.w;
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) {
+            Hs[t][cb][0] *= el.x; Hs[t][cb][1] *= el.y; Hs[t][cb][2] *= el.z; Hs[t][cb][3] *= el.w;
+          }
           if constexpr (NORM) {
             Zs[cb][0] *= el.x; Zs[cb][1] *= el.y; Zs[cb][2] *= el.z; Zs[cb][3] *= el.w;
           }
         }
+      };
+
+      // operand copies of the state before this chunk (for the inter-chunk term)
+      F hf[K::ET][K::NU_DK], zf[NORM ? K::NU_DK : 1];
+      if (!state_only) {
+#pragma unroll
+        for (int u = 0; u < K::NU_DK; ++u) {
+          if constexpr (K::BF) {
+#pragma unroll
+            for (int t = 0; t < K::ET; ++t) {
+              if constexpr (K::HI_DK) hf[t][u] = acc_frag_bf(Hs[t][2 * u], Hs[t][2 * u + 1]);
+              else hf[t][u] = acc_frag_bf(Hs[t][0], zero4);
+            }
+            if constexpr (NORM) {
+              if constexpr (K::HI_DK) zf[u] = acc_frag_bf(Zs[2 * u], Zs[2 * u + 1]);
+              else zf[u] = acc_frag_bf(Zs[0], zero4);
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < K::ET; ++t) hf[t][u] = Hs[t][u];
+            if constexpr (NORM) zf[u] = Zs[u];
+          }
+        }
       }
+
+      // ---------------- S3 + S6 for row block ib (outputs of this chunk)
+      F kc[K::KCACHE ? K::NB : 1][K::NU_DK]; // Kt fragments of row blocks seen so far
+      auto row_block = [&](const int ib) {
+        const TIn *qrow = sQ + (16 * ib + li) * K::LQ;
+        F qf[K::NU_DK];
+#pragma unroll
+        for (int u = 0; u < K::NU_DK; ++u) qf[u] = ld_frag<TIn, K::HI_DK>(qrow, u, g);
+        if constexpr (K::KCACHE) {
+          const TIn *krow = sK + (16 * ib + li) * K::LQ;
+#pragma unroll
+          for (int u = 0; u < K::NU_DK; ++u) kc[ib][u] = ld_frag<TIn, K::HI_DK>(krow, u, g);
+        }
+
+        f32x4 acc[K::ET];
+#pragma unroll
+        for (int t = 0; t < K::ET; ++t) acc[t] = zero4;
+        f32x4 accd = zero4;
+        // intra-chunk: A^T tiles (rows j, cols i) for j-blocks <= ib
+#pragma unroll
+        for (int ju = 0; ju < K::NU_C; ++ju) {
+          if (ju * K::TPU > ib) break;
+          f32x4 st[K::TPU];
+#pragma unroll
+          for (int s = 0; s < K::TPU; ++s) {
+            const int jb = ju * K::TPU + s;
+            f32x4 x = zero4;
+            if (jb <= ib) {
+              const TIn *krow = sK + (16 * jb + li) * K::LQ;
+#pragma unroll
+              for (int u = 0; u < K::NU_DK; ++u) {
+                F kfr;
+                if constexpr (K::KCACHE) kfr = kc[jb][u];
+                else kfr = ld_frag<TIn, K::HI_DK>(krow, u, g);
+                x = mma(x, kfr, qf[u]);
+              }
+              // element (j = 16 jb + 4g + r, i = 16 ib + li)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int dij = 16 * (ib - jb) + li - 4 * g - r; // i - j
+                if constexpr (DECAY == DECAY_GAMMA) {
+                  x[r] = dij >= 0 ? x[r] * sPw[dij] : 0.f;
+                } else {
+                  if (dij < 0) x[r] = 0.f;
+                }
+              }
+            }
+            st[s] = x;
+          }
+          F af;
+          if constexpr (K::BF) af = acc_frag_bf(st[0], st[1]);
+          else af = st[0];
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) acc[t] = mma(acc[t], vf[t][ju], af);
+          if constexpr (NORM) {
+            const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+            accd = mma(accd, frag_from<TIn>(one), af);
+          }
+        }
+        // inter-chunk: H^T Qt^T
+        float rsc = 1.f;
+        if constexpr (DECAY == DECAY_GAMMA) rsc = sPw[16 * ib + li + 1];
+        float inv = 1.f;
+        if constexpr (NORM) {
+          f32x4 accd2 = zero4;
+#pragma unroll
+          for (int u = 0; u < K::NU_DK; ++u) accd2 = mma(accd2, zf[u], qf[u]);
+          if constexpr (DECAY == DECAY_GAMMA) accd2 *= rsc;
+          accd += accd2;
+          inv = rcp_f(accd[0]); // every row of the ones tile holds the denominator
+        }
+        const int i = 16 * ib + li;
+#pragma unroll
+        for (int t = 0; t < K::ET; ++t) {
+          f32x4 acc2 = zero4;
+#pragma unroll
+          for (int u = 0; u < K::NU_DK; ++u) acc2 = mma(acc2, hf[t][u], qf[u]);
+          if constexpr (DECAY == DECAY_GAMMA) acc2 *= rsc;
+          f32x4 o = acc[t] + acc2;
+          if constexpr (NORM) o *= inv;
+          if (i < L && tile_on[t]) st_out4<TIn>(gout + (t0 + i) * a.dv + e0 + 16 * t + 4 * g, o);
+        }
+      };
+
+      if (!state_only) {
+        if constexpr (K::KCACHE) {
+#pragma unroll
+          for (int ib = 0; ib < K::NB; ++ib) {
+            if (16 * ib >= L) break;
+            row_block(ib);
+          }
+        } else {
+          // not unrolled: keeps the compiler from hoisting every row block's operand loads
+#pragma unroll 1
+          for (int ib = 0; ib < K::NB; ++ib) {
+            if (16 * ib >= L) break;
+            row_block(ib);
+          }
+        }
+      }
+      // compile-time block indices: a runtime index into the accumulator array would
+      // move it to scratch memory
+      static_for<0, K::NCB>([&](auto CB) { state_block(decltype(CB)::value); });
     }
     if constexpr (K::STAGES == 1) __syncthreads(); // stage free for the next chunk
   }
@@ -656,7 +792,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int c = 16 * cb + 4 * g + r;
-        if (ecol < a.dv) fo[(int64_t)c * a.ncol + ecol] = Hs[cb][r];
+#pragma unroll
+        for (int t = 0; t < K::ET; ++t) {
+          const int e = e0 + 16 * t + li;
+          if (e < a.dv) fo[(int64_t)c * a.ncol + e] = Hs[t][cb][r];
+        }
         if constexpr (NORM) {
           if (vs == 0 && wave == 0 && li == 0) fo[(int64_t)c * a.ncol + a.dv] = Zs[cb][r];
         }
