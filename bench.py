@@ -195,7 +195,7 @@ def main():
             tc = json.load(f)
         rec = tc.get("workloads", {}).get(w.name)
         if rec and tc.get("kernel_source_hash") == kernel_source_hash():
-            traffic = rec.get("hbm_bytes_per_launch")
+            traffic = rec.get("hbm_bytes_per_step")
     except (OSError, ValueError):
         pass
 
