@@ -78,7 +78,8 @@ struct Cfg {
   static constexpr bool BF = (ES == 2);
   static constexpr int PAD = 16 / ES;    // 16 bytes of row padding
   static constexpr int LQ = DK + PAD;    // row stride (elements) of Qt, Kt
-  static constexpr int LV = kSlice + PAD;// row stride of V
+  // row stride of V: 40 words (8 mod 32) keeps the transposed operand loads conflict-free
+  static constexpr int LV = kSlice + (BF ? 16 : 4);
   static constexpr int NB = C / 16;      // 16-row blocks per chunk
   static constexpr int NCB = DK / 16;    // 16-row blocks of the state
   static constexpr int TPU = BF ? 2 : 1; // 16-blocks per MFMA K unit
@@ -207,6 +208,25 @@ __device__ __forceinline__ Frag<TIn> ld_frag(const TIn *row, int u, int g) {
     if constexpr (HI) hi = *reinterpret_cast<const bf16x4 *>(row + 32 * u + 16 + 4 * g);
     else hi = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    return *reinterpret_cast<const f32x4 *>(row + 16 * u + 4 * g);
+  }
+}
+
+// Operand fragment under the contiguous K convention (lane group g holds k = 32u + 8g + s):
+// one 16-byte load.  Used where both operands of an MFMA come from LDS (the intra-chunk
+// score tiles), where it avoids the bank conflicts of two 8-byte loads.
+template <typename TIn, bool HI>
+__device__ __forceinline__ Frag<TIn> ld_frag_c(const TIn *row, int u, int g) {
+  if constexpr (sizeof(TIn) == 2) {
+    if constexpr (HI) {
+      return *reinterpret_cast<const bf16x8 *>(row + 32 * u + 8 * g);
+    } else {
+      const __bf16 z = (__bf16)0.f;
+      bf16x8 r = {z, z, z, z, z, z, z, z};
+      if (g < 2) r = *reinterpret_cast<const bf16x8 *>(row + 32 * u + 8 * g);
+      return r;
+    }
   } else {
     return *reinterpret_cast<const f32x4 *>(row + 16 * u + 4 * g);
   }
@@ -682,13 +702,19 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       F kc[K::KCACHE ? K::NB : 1][K::NU_DK]; // Kt fragments of row blocks seen so far
       auto row_block = [&](const int ib) {
         const TIn *qrow = sQ + (16 * ib + li) * K::LQ;
-        F qf[K::NU_DK];
+        // qf: split K convention (pairs with the state operand); qc: contiguous convention
+        // (pairs with Kt in the score tiles)
+        F qf[K::NU_DK], qc[K::NU_DK];
 #pragma unroll
-        for (int u = 0; u < K::NU_DK; ++u) qf[u] = ld_frag<TIn, K::HI_DK>(qrow, u, g);
+        for (int u = 0; u < K::NU_DK; ++u) {
+          qf[u] = ld_frag<TIn, K::HI_DK>(qrow, u, g);
+          if constexpr (K::BF) qc[u] = ld_frag_c<TIn, K::HI_DK>(qrow, u, g);
+          else qc[u] = qf[u];
+        }
         if constexpr (K::KCACHE) {
           const TIn *krow = sK + (16 * ib + li) * K::LQ;
 #pragma unroll
-          for (int u = 0; u < K::NU_DK; ++u) kc[ib][u] = ld_frag<TIn, K::HI_DK>(krow, u, g);
+          for (int u = 0; u < K::NU_DK; ++u) kc[ib][u] = ld_frag_c<TIn, K::HI_DK>(krow, u, g);
         }
 
         f32x4 acc[K::ET];
@@ -710,8 +736,8 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
               for (int u = 0; u < K::NU_DK; ++u) {
                 F kfr;
                 if constexpr (K::KCACHE) kfr = kc[jb][u];
-                else kfr = ld_frag<TIn, K::HI_DK>(krow, u, g);
-                x = mma(x, kfr, qf[u]);
+                else kfr = ld_frag_c<TIn, K::HI_DK>(krow, u, g);
+                x = mma(x, kfr, qc[u]);
               }
               // element (j = 16 jb + 4g + r, i = 16 ib + li)
 #pragma unroll
