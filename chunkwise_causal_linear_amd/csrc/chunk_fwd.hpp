@@ -47,6 +47,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 enum : int { DECAY_NONE = 0, DECAY_GAMMA = 1, DECAY_GATE = 2 };
 
@@ -123,17 +125,39 @@ struct Cfg {
   static constexpr int STAGE_WORDS = 2 * RPT * G * ES / 4 + (DECAY == DECAY_GATE ? RPT * G : 0) +
                                      RPTV * 8 * ES / 4;
   static constexpr int PF = (STAGE_WORDS <= 64 && C <= 64 && !NORM) ? 2 : 1; // chunks ahead
-  // LDS map (bytes): [STAGES] x {Qt, Kt, V, eL}, then the gamma power table
+  // LDS map (bytes): [STAGES] x {Qt, Kt, V, eL}, [2] x score tiles (shared-score
+  // schedule only), then the gamma power table
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_K = OFF_Q + C * LQ * ES;
   static constexpr int OFF_V = OFF_K + C * LQ * ES;
   static constexpr int OFF_EL = OFF_V + C * LV * ES;
   static constexpr int STAGE_BYTES = OFF_EL + (DECAY == DECAY_GATE ? DK * 4 : 0);
   static constexpr int PW_BYTES = DECAY == DECAY_GAMMA ? ((C + 4) / 4) * 16 : 0;
-  static constexpr int STAGES = 2 * STAGE_BYTES + PW_BYTES <= kMaxLds ? 2 : 1;
-  static constexpr int OFF_PW = STAGES * STAGE_BYTES;
+  // shared-score schedule: the masked score tiles of a chunk are computed once (split over
+  // the consumer waves) into an LDS buffer and consumed one chunk later, which needs a
+  // third stage.  Tile (ib, jb), jb <= ib, is number ib (ib + 1) / 2 + jb; one more tile
+  // takes the writes of idle slots.
+  static constexpr int NTILES = NB * (NB + 1) / 2;
+  static constexpr int SLOTS = (NTILES + NCW - 1) / NCW; // score tiles per consumer wave
+  static constexpr int PTILE = 256;                      // elements per score tile
+  static constexpr int PBUF_BYTES = (NTILES + 1) * PTILE * ES;
+#ifdef FLA_FORCE_SHARE
+  static constexpr bool SHARE = FLA_FORCE_SHARE && 3 * STAGE_BYTES + 2 * PBUF_BYTES + PW_BYTES <= kMaxLds;
+#else
+  static constexpr bool SHARE = 3 * STAGE_BYTES + 2 * PBUF_BYTES + PW_BYTES <= kMaxLds;
+#endif
+  static constexpr int STAGES = SHARE ? 3 : (2 * STAGE_BYTES + PW_BYTES <= kMaxLds ? 2 : 1);
+  static constexpr int OFF_P = STAGES * STAGE_BYTES;
+  static constexpr int OFF_PW = OFF_P + (SHARE ? 2 * PBUF_BYTES : 0);
   static constexpr int LDS = OFF_PW + PW_BYTES;
   static constexpr bool FITS = LDS <= kMaxLds;
+  // state row order (bf16, shared-score schedule): accumulator row m = 4g + r of state
+  // block cb = 2u + s holds key index 32u + 8g + 4s + r, so that the bf16 operand built
+  // from blocks 2u and 2u+1 has k = 32u + 8g + slot, the order of 16-byte LDS reads
+  static constexpr bool PERM = SHARE && BF && HI_DK;
+  __device__ static constexpr int state_row(int cb, int g, int r) {
+    return PERM ? 32 * (cb >> 1) + 8 * g + 4 * (cb & 1) + r : 16 * cb + 4 * g + r;
+  }
 };
 
 // ---------------------------------------------------------------------------------
@@ -233,16 +257,17 @@ __device__ __forceinline__ Frag<TIn> ld_frag_c(const TIn *row, int u, int g) {
 }
 
 // Operand fragment whose K index runs down the rows of a row-major LDS tile (stride ld):
-// lane (g, li) gets column col0 + li at the rows of K unit u.  bf16: two LDS transpose
-// loads (in each 16-lane group lane q addresses row r0 + q/4, columns col0 + 4 (q%4);
-// lane p receives column col0 + p of rows r0..r0+3).  fp32: four scalar loads.
-template <typename TIn, bool HI>
+// lane (g, li) gets column col0 + CS (li/4) + li%4 at the rows of K unit u (CS = 4: the
+// 16 consecutive columns from col0).  bf16: two LDS transpose loads (in each 16-lane group
+// lane q addresses row r0 + q/4, columns col0 + CS (q%4) .. +3; lane p receives element
+// p%4 of the group addressed by lanes 4y + p/4, y = 0..3).  fp32: four scalar loads.
+template <typename TIn, bool HI, int CS = 4>
 __device__ __forceinline__ Frag<TIn> ld_frag_t(const TIn *tile, int ld, int col0, int u, int g,
                                                int li) {
   if constexpr (sizeof(TIn) == 2) {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     const int r0 = 32 * u + 4 * g + (li >> 2);
-    const int c = col0 + 4 * (li & 3);
+    const int c = col0 + CS * (li & 3);
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + r0 * ld + c));
     i16x4 hi = {0, 0, 0, 0};
     if constexpr (HI)
@@ -250,8 +275,50 @@ __device__ __forceinline__ Frag<TIn> ld_frag_t(const TIn *tile, int ld, int col0
     const bf16x4 l = __builtin_bit_cast(bf16x4, lo), h = __builtin_bit_cast(bf16x4, hi);
     return bf16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
   } else {
+    static_assert(CS == 4, "fp32 tiles use consecutive columns");
     const TIn *p = tile + (16 * u + 4 * g) * ld + col0 + li;
     return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+  }
+}
+
+// Score tiles in LDS (shared-score schedule): a 16 x 16 tile of A^T (rows j, columns i)
+// is kept as its accumulator image, lane (g, li) owning elements li * 16 + 4g .. +3, which
+// is also where the P V operand fragment of that lane reads them.
+template <typename TIn>
+__device__ __forceinline__ void st_ptile(TIn *tile, int g, int li, f32x4 x) {
+  if constexpr (sizeof(TIn) == 2) {
+    *reinterpret_cast<bf16x4 *>(tile + li * 16 + 4 * g) =
+        bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+  } else {
+    *reinterpret_cast<f32x4 *>(tile + li * 16 + 4 * g) = x;
+  }
+}
+// B operand of O^T += V^T A^T for K unit (two 16-row tiles ta, tb; tb < 0: zeros).
+template <typename TIn, int TA, int TB>
+__device__ __forceinline__ Frag<TIn> ld_ptile(const TIn *buf, int g, int li) {
+  if constexpr (sizeof(TIn) == 2) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(buf + TA * 256 + li * 16 + 4 * g);
+    bf16x4 hi = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+    if constexpr (TB >= 0) hi = *reinterpret_cast<const bf16x4 *>(buf + TB * 256 + li * 16 + 4 * g);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    static_assert(TB < 0, "fp32 K units are one tile");
+    return *reinterpret_cast<const f32x4 *>(buf + TA * 256 + li * 16 + 4 * g);
+  }
+}
+
+// Output store of 4 adjacent values through a buffer resource: the hardware drops a
+// store whose byte offset lies past the resource's range, which masks the rows past
+// the end of a chunk and the columns past dv without a branch.
+constexpr int kBufWord3 = 0x00020000; // gfx9 buffer resource: 32-bit data format
+constexpr int kDropOffset = 0x7ff00000; // beyond any chunk's output range
+template <typename TIn>
+__device__ __forceinline__ void st_out4_buf(__amdgpu_buffer_rsrc_t rs, int off, f32x4 o) {
+  if constexpr (sizeof(TIn) == 2) {
+    const bf16x4 b = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), rs, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs, off, 0, 0);
   }
 }
 
@@ -566,6 +633,10 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
         if constexpr (K::STAGES == 1) __syncthreads();
       }
     }
+    // shared-score schedule: consumers finish the last chunk one barrier later
+    if constexpr (K::SHARE) {
+      if (nch > 0) __syncthreads();
+    }
     if (a.seg_decay && vs == 0 && ld_on && rg == 0) {
       float *sd = a.seg_decay + ((int64_t)bh * a.nseg + seg) * DK + col0;
 #pragma unroll
@@ -593,7 +664,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     for (int cb = 0; cb < K::NCB; ++cb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int c = 16 * cb + 4 * g + r;
+        const int c = K::state_row(cb, g, r);
 #pragma unroll
         for (int t = 0; t < K::ET; ++t) {
           const int e = e0 + 16 * t + li;
@@ -604,6 +675,236 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     }
   }
 
+  if constexpr (K::SHARE) {
+    // ------------- shared-score schedule: iteration n computes this wave's score tiles of
+    // chunk n (stage n % 3) into score buffer n % 2, and the outputs and state update of
+    // chunk n - 1, whose tiles every consumer wave finished before this iteration's barrier.
+    const int cw = __builtin_amdgcn_readfirstlane(wave);
+    int sib[K::SLOTS], sjb[K::SLOTS], sdst[K::SLOTS];
+    // gamma: gamma^{i-j} (0 above the diagonal) of each element of a tile
+    float fac[DECAY == DECAY_GAMMA ? K::SLOTS : 1][4];
+#pragma unroll
+    for (int s = 0; s < K::SLOTS; ++s) {
+      const int k = s * K::NCW + cw;
+      const int kk = k < K::NTILES ? k : 0;
+      int ib = 0;
+      while ((ib + 1) * (ib + 2) / 2 <= kk) ++ib;
+      sib[s] = ib;
+      sjb[s] = kk - ib * (ib + 1) / 2;
+      sdst[s] = k < K::NTILES ? k : K::NTILES;
+      if constexpr (DECAY == DECAY_GAMMA) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int dij = 16 * (ib - sjb[s]) + li - 4 * g - r; // i - j
+          fac[s][r] = dij >= 0 ? sPw[dij] : 0.f;
+        }
+      }
+    }
+    const int dl = li - 4 * g;
+    // gamma: V' row factors gamma^{C-1-j} of a full chunk
+    float vsc[DECAY == DECAY_GAMMA ? K::NU_C : 1][8];
+    if constexpr (DECAY == DECAY_GAMMA) {
+#pragma unroll
+      for (int u = 0; u < K::NU_C; ++u)
+#pragma unroll
+        for (int q = 0; q < (K::BF ? 8 : 4); ++q) {
+          const int j = K::BF ? (32 * u + (q < 4 ? 0 : 16) + 4 * g + (q & 3)) : (16 * u + 4 * g + q);
+          vsc[u][q] = j < C ? sPw[C - 1 - j] : 0.f;
+        }
+    }
+
+    auto scores = [&](int n) {
+      const unsigned char *base = smem + (n % K::STAGES) * K::STAGE_BYTES;
+      const TIn *sQ = reinterpret_cast<const TIn *>(base + K::OFF_Q);
+      const TIn *sK = reinterpret_cast<const TIn *>(base + K::OFF_K);
+      TIn *pb = reinterpret_cast<TIn *>(smem + K::OFF_P + (n & 1) * K::PBUF_BYTES);
+#pragma unroll
+      for (int s = 0; s < K::SLOTS; ++s) {
+        const TIn *qrow = sQ + (16 * sib[s] + li) * K::LQ;
+        const TIn *krow = sK + (16 * sjb[s] + li) * K::LQ;
+        f32x4 x = zero4;
+#pragma unroll
+        for (int u = 0; u < K::NU_DK; ++u)
+          x = mma(x, ld_frag_c<TIn, K::HI_DK>(krow, u, g), ld_frag_c<TIn, K::HI_DK>(qrow, u, g));
+        // element (j = 16 jb + 4g + r, i = 16 ib + li): keep i >= j
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (DECAY == DECAY_GAMMA) x[r] *= fac[s][r];
+          else x[r] = 16 * (sib[s] - sjb[s]) + dl - r >= 0 ? x[r] : 0.f;
+        }
+        st_ptile<TIn>(pb + sdst[s] * K::PTILE, g, li, x);
+      }
+    };
+
+    // outputs and state update of chunk m (FULL: m is not the last chunk, L = C); mid()
+    // runs between the two (the next chunk's score tiles, scheduled with the update)
+    auto rest = [&](int m, auto full_c, auto &&mid) {
+      constexpr bool FULL = decltype(full_c)::value;
+      const int64_t t0 = t_begin + (int64_t)m * C;
+      const int L = FULL ? C : (int)((t_end - t0) < C ? (t_end - t0) : C);
+      const unsigned char *base = smem + (m % K::STAGES) * K::STAGE_BYTES;
+      const TIn *sQ = reinterpret_cast<const TIn *>(base + K::OFF_Q);
+      const TIn *sK = reinterpret_cast<const TIn *>(base + K::OFF_K);
+      const TIn *sV = reinterpret_cast<const TIn *>(base + K::OFF_V);
+      const float *sEL = reinterpret_cast<const float *>(base + K::OFF_EL);
+      const TIn *pb = reinterpret_cast<const TIn *>(smem + K::OFF_P + (m & 1) * K::PBUF_BYTES);
+
+      // V^T operand fragments (rows e, K = tokens j); columns past dv hold zeros
+      F vf[K::ET][K::NU_C];
+#pragma unroll
+      for (int t = 0; t < K::ET; ++t)
+#pragma unroll
+        for (int u = 0; u < K::NU_C; ++u)
+          vf[t][u] = ld_frag_t<TIn, K::HI_C>(sV, K::LV, 16 * (K::ET * wave + t), u, g, li);
+      F vu[K::ET][K::NU_C], wz[NORM ? K::NU_C : 1];
+#pragma unroll
+      for (int u = 0; u < K::NU_C; ++u) {
+        if constexpr (DECAY == DECAY_GAMMA) {
+          float sc[8];
+#pragma unroll
+          for (int q = 0; q < (K::BF ? 8 : 4); ++q) {
+            const int j = K::BF ? (32 * u + (q < 4 ? 0 : 16) + 4 * g + (q & 3)) : (16 * u + 4 * g + q);
+            sc[q] = FULL ? vsc[u][q] : (j < L ? sPw[L - 1 - j] : 0.f);
+          }
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) vu[t][u] = scale_frag(vf[t][u], sc);
+          if constexpr (NORM) wz[u] = frag_from<TIn>(sc);
+        } else {
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) vu[t][u] = vf[t][u];
+          if constexpr (NORM) {
+            const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+            wz[u] = frag_from<TIn>(one);
+          }
+        }
+      }
+      const float gl = (DECAY == DECAY_GAMMA) ? sPw[L] : 1.f;
+
+      // the state before this chunk as operands of the inter-chunk term
+      F hf[K::ET][K::NU_DK], zf[NORM ? K::NU_DK : 1];
+#pragma unroll
+      for (int u = 0; u < K::NU_DK; ++u) {
+        if constexpr (K::BF) {
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) {
+            if constexpr (K::HI_DK) hf[t][u] = acc_frag_bf(Hs[t][2 * u], Hs[t][2 * u + 1]);
+            else hf[t][u] = acc_frag_bf(Hs[t][0], zero4);
+          }
+          if constexpr (NORM) {
+            if constexpr (K::HI_DK) zf[u] = acc_frag_bf(Zs[2 * u], Zs[2 * u + 1]);
+            else zf[u] = acc_frag_bf(Zs[0], zero4);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) hf[t][u] = Hs[t][u];
+          if constexpr (NORM) zf[u] = Zs[u];
+        }
+      }
+
+      // output rows of this chunk: stores past row L or column dv fall outside the range
+      const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+          gout + t0 * a.dv, (short)0, state_only ? 0 : L * a.dv * K::ES, kBufWord3);
+      static_for<0, K::NB>([&](auto IB) {
+        constexpr int ib = decltype(IB)::value;
+        // one row block's operands at a time (hoisting them all exceeds the registers)
+        __builtin_amdgcn_sched_barrier(0);
+        const TIn *qrow = sQ + (16 * ib + li) * K::LQ;
+        F qc[K::NU_DK];
+#pragma unroll
+        for (int u = 0; u < K::NU_DK; ++u) {
+          if constexpr (K::PERM) qc[u] = ld_frag_c<TIn, true>(qrow, u, g);
+          else qc[u] = ld_frag<TIn, K::HI_DK>(qrow, u, g);
+        }
+        f32x4 acc[K::ET];
+#pragma unroll
+        for (int t = 0; t < K::ET; ++t) acc[t] = zero4;
+        f32x4 accd = zero4;
+        // intra-chunk: O^T += V^T A^T over the K units of tokens j <= i
+        static_for<0, K::NU_C>([&](auto JU) {
+          constexpr int ju = decltype(JU)::value;
+          constexpr int jb = ju * K::TPU;
+          if constexpr (jb <= ib) {
+            constexpr int ta = ib * (ib + 1) / 2 + jb;
+            constexpr int tb = (K::TPU == 2 && jb + 1 <= ib) ? ta + 1 : -1;
+            const F pf = ld_ptile<TIn, ta, tb>(pb, g, li);
+#pragma unroll
+            for (int t = 0; t < K::ET; ++t) acc[t] = mma(acc[t], vf[t][ju], pf);
+            if constexpr (NORM) {
+              const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+              accd = mma(accd, frag_from<TIn>(one), pf);
+            }
+          }
+        });
+        // inter-chunk: O^T += H^T Qt^T
+        float rsc = 1.f;
+        if constexpr (DECAY == DECAY_GAMMA) rsc = sPw[16 * ib + li + 1];
+        float inv = 1.f;
+        if constexpr (NORM) {
+          f32x4 accd2 = zero4;
+#pragma unroll
+          for (int u = 0; u < K::NU_DK; ++u) accd2 = mma(accd2, zf[u], qc[u]);
+          if constexpr (DECAY == DECAY_GAMMA) accd2 *= rsc;
+          accd += accd2;
+          inv = rcp_f(accd[0]); // every row of the ones tile holds the denominator
+        }
+        const int i = 16 * ib + li;
+#pragma unroll
+        for (int t = 0; t < K::ET; ++t) {
+          f32x4 acc2 = zero4;
+#pragma unroll
+          for (int u = 0; u < K::NU_DK; ++u) acc2 = mma(acc2, hf[t][u], qc[u]);
+          if constexpr (DECAY == DECAY_GAMMA) acc2 *= rsc;
+          f32x4 o = acc[t] + acc2;
+          if constexpr (NORM) o *= inv;
+          const int off = tile_on[t] ? (i * a.dv + e0 + 16 * t + 4 * g) * K::ES : kDropOffset;
+          st_out4_buf<TIn>(ors, off, o);
+        }
+      });
+
+      mid();
+      // S4 + S5: H <- decay (H + Kt^T V) (gamma: gamma^L H + Kt^T V')
+      static_for<0, K::NCB>([&](auto CB) {
+        constexpr int cb = decltype(CB)::value;
+        if constexpr (DECAY == DECAY_GAMMA) {
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) Hs[t][cb] *= gl;
+          if constexpr (NORM) Zs[cb] *= gl;
+        }
+        constexpr int kcol = K::PERM ? 32 * (cb >> 1) + 4 * (cb & 1) : 16 * cb;
+#pragma unroll
+        for (int u = 0; u < K::NU_C; ++u) {
+          const F kf = ld_frag_t<TIn, K::HI_C, K::PERM ? 8 : 4>(sK, K::LQ, kcol, u, g, li);
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) Hs[t][cb] = mma(Hs[t][cb], kf, vu[t][u]);
+          if constexpr (NORM) Zs[cb] = mma(Zs[cb], kf, wz[u]);
+        }
+        if constexpr (DECAY == DECAY_GATE) {
+          const float4 el = *reinterpret_cast<const float4 *>(sEL + K::state_row(cb, g, 0));
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) {
+            Hs[t][cb][0] *= el.x; Hs[t][cb][1] *= el.y; Hs[t][cb][2] *= el.z; Hs[t][cb][3] *= el.w;
+          }
+          if constexpr (NORM) {
+            Zs[cb][0] *= el.x; Zs[cb][1] *= el.y; Zs[cb][2] *= el.z; Zs[cb][3] *= el.w;
+          }
+        }
+      });
+    };
+
+    if (nch > 0) {
+      __syncthreads(); // stage 0 holds chunk 0
+      scores(0);
+      for (int n = 1; n < nch; ++n) {
+        __syncthreads(); // stage n % 3 holds chunk n; score tiles of chunk n - 1 complete
+        rest(n - 1, std::true_type{}, [&] {
+          __builtin_amdgcn_sched_barrier(0); // keeps the row blocks' operands apart
+          scores(n);
+        });
+      }
+      __syncthreads();
+      rest(nch - 1, std::false_type{}, [] {});
+    }
+  } else {
   for (int n = 0; n < nch; ++n) {
     __syncthreads(); // stage n % STAGES holds chunk n
     const int64_t t0 = t_begin + (int64_t)n * C;
@@ -809,6 +1110,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     }
     if constexpr (K::STAGES == 1) __syncthreads(); // stage free for the next chunk
   }
+  }
 
   // ---- end state
   if (a.fin && wave_on) {
@@ -817,7 +1119,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     for (int cb = 0; cb < K::NCB; ++cb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int c = 16 * cb + 4 * g + r;
+        const int c = K::state_row(cb, g, r);
 #pragma unroll
         for (int t = 0; t < K::ET; ++t) {
           const int e = e0 + 16 * t + li;
