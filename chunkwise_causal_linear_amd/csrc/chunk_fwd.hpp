@@ -124,7 +124,11 @@ struct Cfg {
   // registers held per prefetched chunk (32-bit words per producer lane)
   static constexpr int STAGE_WORDS = 2 * RPT * G * ES / 4 + (DECAY == DECAY_GATE ? RPT * G : 0) +
                                      RPTV * 8 * ES / 4;
+#ifdef FLA_FORCE_PF
+  static constexpr int PF = FLA_FORCE_PF;
+#else
   static constexpr int PF = (STAGE_WORDS <= 64 && C <= 64 && !NORM) ? 2 : 1; // chunks ahead
+#endif
   // LDS map (bytes): [STAGES] x {Qt, Kt, V, eL}, [2] x score tiles (shared-score
   // schedule only), then the gamma power table
   static constexpr int OFF_Q = 0;
@@ -312,6 +316,32 @@ __device__ __forceinline__ Frag<TIn> ld_ptile(const TIn *buf, int g, int li) {
 // the end of a chunk and the columns past dv without a branch.
 constexpr int kBufWord3 = 0x00020000; // gfx9 buffer resource: 32-bit data format
 constexpr int kDropOffset = 0x7ff00000; // beyond any chunk's output range
+// Buffer resource for [base, base + bytes).  Both must be uniform across the wave (they
+// are: derived from the workgroup's unit and the chunk index); reading them through
+// readfirstlane keeps them in scalar registers, where the compiler could otherwise wrap
+// each load in a loop over the distinct values it cannot prove equal.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void *b = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
+}
+// N (2, 4 or 8) consecutive 32-bit words at byte offset off; zeros past the range.
+template <int N>
+__device__ __forceinline__ void ld_words_buf(uint32_t *w, __amdgpu_buffer_rsrc_t rs, int off) {
+  if constexpr (N == 2) {
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    w[0] = x[0]; w[1] = x[1];
+  } else {
+    static_assert(N % 4 == 0, "word count");
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4 * i, 0, 0);
+      w[i] = x[0]; w[i + 1] = x[1]; w[i + 2] = x[2]; w[i + 3] = x[3];
+    }
+  }
+}
 template <typename TIn>
 __device__ __forceinline__ void st_out4_buf(__amdgpu_buffer_rsrc_t rs, int off, f32x4 o) {
   if constexpr (sizeof(TIn) == 2) {
@@ -443,61 +473,59 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     const int vcg = ptid & 7, vrg = ptid >> 3;
     const int vrow0 = vrg * K::RPTV;
     const bool vld_on = ptid < K::VACTIVE && (vs * kSlice + 8 * vcg) < a.dv;
-    const TIn *gq = static_cast<const TIn *>(a.q) + (int64_t)bh * a.T * DK + col0;
-    const TIn *gk = static_cast<const TIn *>(a.k) + (int64_t)bh * a.T * DK + col0;
-    const TIn *gv = static_cast<const TIn *>(a.v) + (int64_t)bh * a.T * a.dv + vs * kSlice + 8 * vcg;
-    const float *gg = (DECAY == DECAY_GATE) ? a.decay + (int64_t)bh * a.T * DK + col0 : nullptr;
     float dprod[K::G];
 #pragma unroll
     for (int c = 0; c < K::G; ++c) dprod[c] = 1.f;
 
+    // Loads go through a buffer resource per chunk (range = the chunk's valid rows): rows
+    // past the end of the sequence and idle lanes read zeros without a branch, so the
+    // loads can be placed right where a row's registers fall free.
     // gate loads are issued separately so they can go out as soon as the scan has used
-    // the previous chunk's gate registers
+    // the previous chunk's gate registers; rows past L are set to 1 in prep
+    // (0 past the last chunk: the prefetch of a chunk that does not exist loads nothing,
+    // and staying unconditional keeps the loads' wait counts exact for the compiler)
+    auto chunk_len = [&](int n) {
+      const int64_t t0 = t_begin + (int64_t)n * C;
+      const int64_t l = t_end - t0;
+      return (int)(l < 0 ? 0 : (l < C ? l : C));
+    };
     auto load_gate = [&](St &s, int n) {
       if constexpr (DECAY == DECAY_GATE) {
         const int64_t t0 = t_begin + (int64_t)n * C;
-        const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
+        const auto rs = make_rsrc(a.decay + ((int64_t)bh * a.T + t0) * DK, chunk_len(n) * DK * 4);
 #pragma unroll
-        for (int r = 0; r < K::RPT; ++r) {
-          const int row = row0 + r;
-          // zero first, then load in place (an if/else of fp32 vector loads here crashes
-          // the gfx950 compiler's machine copy propagation)
-#pragma unroll
-          for (int i = 0; i < K::G; ++i) s.a[r][i] = 0x3f800000u; // 1.0f
-          if (ld_on && row < L) ld_words<K::G>(s.a[r], gg + (t0 + row) * DK);
-        }
+        for (int r = 0; r < K::RPT; ++r)
+          ld_words_buf<K::G>(s.a[r], rs, ld_on ? ((row0 + r) * DK + col0) * 4 : kDropOffset);
       }
     };
     // q/k row r and v row r of chunk n
     auto load_qk = [&](St &s, int n, int r) {
       const int64_t t0 = t_begin + (int64_t)n * C;
-      const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
-      const int row = row0 + r;
-#pragma unroll
-      for (int i = 0; i < St::QW; ++i) { s.q[r][i] = 0u; s.k[r][i] = 0u; }
-      if (ld_on && row < L) {
-        const int64_t off = (t0 + row) * DK;
-        if (!state_only) ld_words<St::QW>(s.q[r], gq + off);
-        ld_words<St::QW>(s.k[r], gk + off);
-      }
+      const int64_t o = ((int64_t)bh * a.T + t0) * DK;
+      const int bytes = chunk_len(n) * DK * K::ES;
+      const auto rq = make_rsrc(static_cast<const TIn *>(a.q) + o, state_only ? 0 : bytes);
+      const auto rk = make_rsrc(static_cast<const TIn *>(a.k) + o, bytes);
+      const int off = ld_on ? ((row0 + r) * DK + col0) * K::ES : kDropOffset;
+      ld_words_buf<St::QW>(s.q[r], rq, off);
+      ld_words_buf<St::QW>(s.k[r], rk, off);
     };
     auto load_v = [&](St &s, int n, int r) {
       const int64_t t0 = t_begin + (int64_t)n * C;
-      const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
-      const int row = vrow0 + r;
-#pragma unroll
-      for (int i = 0; i < 2 * K::ES; ++i) s.v[r][i] = 0u;
-      if (vld_on && row < L) ld_words<2 * K::ES>(s.v[r], gv + (t0 + row) * a.dv);
+      const auto rs = make_rsrc(static_cast<const TIn *>(a.v) + ((int64_t)bh * a.T + t0) * a.dv,
+                                chunk_len(n) * a.dv * K::ES);
+      ld_words_buf<2 * K::ES>(s.v[r], rs, vld_on ? ((vrow0 + r) * a.dv + vs * kSlice + 8 * vcg) * K::ES : kDropOffset);
     };
+    // same order as prep issues the next chunk's loads (v, gate, q/k rows): the loads
+    // then retire in the order they are used
     auto load = [&](St &s, int n) {
+#pragma unroll
+      for (int r = 0; r < K::RPTV; ++r) load_v(s, n, r);
       load_gate(s, n);
 #pragma unroll
       for (int r = 0; r < K::RPT; ++r) load_qk(s, n, r);
-#pragma unroll
-      for (int r = 0; r < K::RPTV; ++r) load_v(s, n, r);
     };
 
-    auto prep = [&](St &s, int n, bool next) {
+    auto prep = [&](St &s, int n) {
       const int64_t t0 = t_begin + (int64_t)n * C;
       const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
       unsigned char *base = smem + (n % K::STAGES) * K::STAGE_BYTES;
@@ -505,11 +533,30 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       TIn *sK = reinterpret_cast<TIn *>(base + K::OFF_K);
       TIn *sV = reinterpret_cast<TIn *>(base + K::OFF_V);
       float *sEL = reinterpret_cast<float *>(base + K::OFF_EL);
+      // V rows are copied as they are; the next chunk's V goes out at once
+      if (ptid < K::VACTIVE) {
+#pragma unroll
+        for (int r = 0; r < K::RPTV; ++r) {
+          uint32_t *dst = reinterpret_cast<uint32_t *>(sV + (vrow0 + r) * K::LV + 8 * vcg);
+#pragma unroll
+          for (int i = 0; i < 2 * K::ES; i += 4)
+            *reinterpret_cast<uint4 *>(dst + i) = make_uint4(s.v[r][i], s.v[r][i + 1], s.v[r][i + 2], s.v[r][i + 3]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < K::RPTV; ++r) load_v(s, n + K::PF, r);
       // gate: b_i = local cumulative product over this lane's rows times the product of
       // the row groups above it (inclusive shuffle scan across lanes rg*LPR + cgl)
       float bc[DECAY == DECAY_GATE ? K::RPT : 1][K::G];
       float rb[DECAY == DECAY_GATE ? K::RPT : 1][K::G]; // 1 / b
       if constexpr (DECAY == DECAY_GATE) {
+        if (L < C) {
+#pragma unroll
+          for (int r = 0; r < K::RPT; ++r)
+#pragma unroll
+            for (int i = 0; i < K::G; ++i)
+              if (row0 + r >= L) s.a[r][i] = 0x3f800000u; // 1.0f: no decay past the end
+        }
 #pragma unroll
         for (int r = 0; r < K::RPT; ++r) {
           unpack<float, K::G>(bc[r], s.a[r]);
@@ -548,7 +595,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
             rb[r][c] = rb[r + 1][c] * __uint_as_float(s.a[r + 1][c]);
         }
         if (ld_on && rg == 0) st_lds<float, K::G>(sEL + col0, tot);
-        if (next) load_gate(s, n + K::PF);
+        load_gate(s, n + K::PF);
       } else if constexpr (DECAY == DECAY_GAMMA) {
         dprod[0] *= sPw[L];
       }
@@ -581,6 +628,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           }
           st_lds<TIn, K::G>(sK + row * K::LQ + col0, kv);
           if (!state_only) st_lds<TIn, K::G>(sQ + row * K::LQ + col0, qv);
+          load_qk(s, n + K::PF, r); // this row's registers are free again
         }
       };
       if (ld_on) {
@@ -594,20 +642,6 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           else rows(F_{}, F_{});
         }
       }
-      if (ptid < K::VACTIVE) {
-#pragma unroll
-        for (int r = 0; r < K::RPTV; ++r) {
-          float vv[8];
-          unpack<TIn, 8>(vv, s.v[r]);
-          st_lds<TIn, 8>(sV + (vrow0 + r) * K::LV + 8 * vcg, vv);
-        }
-      }
-      if (next) {
-#pragma unroll
-        for (int r = 0; r < K::RPT; ++r) load_qk(s, n + K::PF, r);
-#pragma unroll
-        for (int r = 0; r < K::RPTV; ++r) load_v(s, n + K::PF, r);
-      }
     };
 
     if constexpr (K::PF == 2) {
@@ -615,11 +649,11 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       if (nch > 0) load(s0, 0);
       if (nch > 1) load(s1, 1);
       for (int n = 0; n < nch; n += 2) {
-        prep(s0, n, n + 2 < nch);
+        prep(s0, n);
         __syncthreads();
         if constexpr (K::STAGES == 1) __syncthreads();
         if (n + 1 < nch) {
-          prep(s1, n + 1, n + 3 < nch);
+          prep(s1, n + 1);
           __syncthreads();
           if constexpr (K::STAGES == 1) __syncthreads();
         }
@@ -628,7 +662,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       St s0;
       if (nch > 0) load(s0, 0);
       for (int n = 0; n < nch; ++n) {
-        prep(s0, n, n + 1 < nch);
+        prep(s0, n);
         __syncthreads();
         if constexpr (K::STAGES == 1) __syncthreads();
       }
