@@ -129,8 +129,10 @@ def copy_calibration(torch, steps, warmup):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: as many as fill about "
+                         "one second, so the GPU clocks have settled)")
     ap.add_argument("--workload", default=None, help="workload name (default: headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
@@ -150,7 +152,7 @@ def main():
     import torch
 
     if args.copy_calibration:
-        copy_calibration(torch, args.steps, args.warmup)
+        copy_calibration(torch, args.steps, 20 if args.warmup is None else args.warmup)
         return
 
     import chunkwise_causal_linear_amd as fla
@@ -169,8 +171,20 @@ def main():
                 init_state=inp["init"], out=out, final_state=fin, chunk=w.chunk,
                 phi_elu1=w.phi_elu1, normalize=w.normalize, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
+    warmup = args.warmup
+    if warmup is None:
+        # about a second of steps (at least 10), so the GPU clocks have settled
+        warmup, t0 = 0, time.perf_counter()
+        while True:
+            step()
+            warmup += 1
+            if warmup % 8 == 0:
+                torch.cuda.synchronize()
+                if warmup >= 10 and time.perf_counter() - t0 >= 1.0:
+                    break
+    else:
+        for _ in range(warmup):
+            step()
     torch.cuda.synchronize()
     # timed region: HIP events on the stream the kernels are launched on
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -205,7 +219,7 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",

@@ -159,6 +159,13 @@ struct Cfg {
   // block cb = 2u + s holds key index 32u + 8g + 4s + r, so that the bf16 operand built
   // from blocks 2u and 2u+1 has k = 32u + 8g + slot, the order of 16-byte LDS reads
   static constexpr bool PERM = SHARE && BF && HI_DK;
+  // scheduling fences in the shared-score consumer: between row blocks and before the
+  // next chunk's score tiles (needed to stay within the registers with two tiles a wave)
+#ifdef FLA_FORCE_FENCE
+  static constexpr int FENCE = FLA_FORCE_FENCE;
+#else
+  static constexpr int FENCE = ET >= 2 ? 3 : 1; // bit 0: row blocks, bit 1: scores
+#endif
   __device__ static constexpr int state_row(int cb, int g, int r) {
     return PERM ? 32 * (cb >> 1) + 8 * g + 4 * (cb & 1) + r : 16 * cb + 4 * g + r;
   }
@@ -841,7 +848,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       static_for<0, K::NB>([&](auto IB) {
         constexpr int ib = decltype(IB)::value;
         // one row block's operands at a time (hoisting them all exceeds the registers)
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (K::FENCE & 1) __builtin_amdgcn_sched_barrier(0);
         const TIn *qrow = sQ + (16 * ib + li) * K::LQ;
         F qc[K::NU_DK];
 #pragma unroll
@@ -931,7 +938,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       for (int n = 1; n < nch; ++n) {
         __syncthreads(); // stage n % 3 holds chunk n; score tiles of chunk n - 1 complete
         rest(n - 1, std::true_type{}, [&] {
-          __builtin_amdgcn_sched_barrier(0); // keeps the row blocks' operands apart
+          if constexpr (K::FENCE & 2) __builtin_amdgcn_sched_barrier(0);
           scores(n);
         });
       }
