@@ -45,6 +45,7 @@ namespace fla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -80,8 +81,6 @@ struct Cfg {
   static constexpr bool BF = (ES == 2);
   static constexpr int PAD = 16 / ES;    // 16 bytes of row padding
   static constexpr int LQ = DK + PAD;    // row stride (elements) of Qt, Kt
-  // row stride of V: 40 words (8 mod 32) keeps the transposed operand loads conflict-free
-  static constexpr int LV = kSlice + (BF ? 16 : 4);
   static constexpr int NB = C / 16;      // 16-row blocks per chunk
   static constexpr int NCB = DK / 16;    // 16-row blocks of the state
   static constexpr int TPU = BF ? 2 : 1; // 16-blocks per MFMA K unit
@@ -125,40 +124,83 @@ struct Cfg {
   static constexpr int STAGE_WORDS = 2 * RPT * G * ES / 4 + (DECAY == DECAY_GATE ? RPT * G : 0) +
                                      RPTV * 8 * ES / 4;
 #ifdef FLA_FORCE_PF
-  static constexpr int PF = FLA_FORCE_PF;
+  static constexpr int PF_BASE = FLA_FORCE_PF;
 #else
-  static constexpr int PF = (STAGE_WORDS <= 64 && C <= 64 && !NORM) ? 2 : 1; // chunks ahead
+  static constexpr int PF_BASE = (STAGE_WORDS <= 64 && C <= 64 && !NORM) ? 2 : 1;
 #endif
-  // LDS map (bytes): [STAGES] x {Qt, Kt, V, eL}, [2] x score tiles (shared-score
-  // schedule only), then the gamma power table
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_K = OFF_Q + C * LQ * ES;
-  static constexpr int OFF_V = OFF_K + C * LQ * ES;
-  static constexpr int OFF_EL = OFF_V + C * LV * ES;
-  static constexpr int STAGE_BYTES = OFF_EL + (DECAY == DECAY_GATE ? DK * 4 : 0);
-  static constexpr int PW_BYTES = DECAY == DECAY_GAMMA ? ((C + 4) / 4) * 16 : 0;
-  // shared-score schedule: the masked score tiles of a chunk are computed once (split over
-  // the consumer waves) into an LDS buffer and consumed one chunk later, which needs a
-  // third stage.  Tile (ib, jb), jb <= ib, is number ib (ib + 1) / 2 + jb; one more tile
-  // takes the writes of idle slots.
+  // Score tiles shared through LDS: the masked score tiles of a chunk are computed once,
+  // split over the consumer waves, into an LDS buffer that every wave reads for O += A V.
+  // Tile (ib, jb), jb <= ib, is number ib (ib + 1) / 2 + jb; when the slots outnumber the
+  // tiles one more tile takes the writes of the idle slots.
   static constexpr int NTILES = NB * (NB + 1) / 2;
   static constexpr int SLOTS = (NTILES + NCW - 1) / NCW; // score tiles per consumer wave
   static constexpr int PTILE = 256;                      // elements per score tile
-  static constexpr int PBUF_BYTES = (NTILES + 1) * PTILE * ES;
+  static constexpr int PBUF_BYTES = (NTILES + (SLOTS * NCW > NTILES ? 1 : 0)) * PTILE * ES;
+  static constexpr int PW_BYTES = DECAY == DECAY_GAMMA ? ((C + 4) / 4) * 16 : 0;
+  static constexpr int QT_BYTES = C * LQ * ES; // one Qt or Kt tile
+  static constexpr int EL_BYTES = DECAY == DECAY_GATE ? DK * 4 : 0;
+  // row stride of V: 40 words (8 mod 32) keeps the transposed operand loads conflict-free;
+  // 36 words where the split schedule needs the room
+  static constexpr int LV_W = kSlice + (BF ? 16 : 4);
+  static constexpr int LV_T = kSlice + (BF ? 8 : 4);
+  static constexpr int stage_bytes(int lv) { return 2 * QT_BYTES + C * lv * ES + EL_BYTES; }
+  static constexpr int split_bytes(int lv) {
+    return QT_BYTES + 2 * (QT_BYTES + C * lv * ES + EL_BYTES) + PBUF_BYTES + PW_BYTES;
+  }
+  // Schedules, by the LDS they need:
+  //  SHARE: three stages {Qt, Kt, V, eL} and two score buffers; iteration n computes the
+  //    score tiles of chunk n and the outputs and state update of chunk n - 1 (one barrier
+  //    a chunk);
+  //  SPLIT: one Qt tile, two {Kt, V, eL} stages and one score buffer; two barriers a chunk:
+  //    phase 1 the inter-chunk term and the score tiles, phase 2 O += A V, the output and
+  //    the state update; producers write Kt and V of the next chunk during phase 1 and its
+  //    Qt during phase 2;
+  //  otherwise the per-wave schedule: two stages (one where two do not fit), each consumer
+  //    wave computing the score tiles it needs itself.
 #ifdef FLA_FORCE_SHARE
-  static constexpr bool SHARE = FLA_FORCE_SHARE && 3 * STAGE_BYTES + 2 * PBUF_BYTES + PW_BYTES <= kMaxLds;
+  static constexpr bool SHARE_OK = FLA_FORCE_SHARE != 0;
 #else
-  static constexpr bool SHARE = 3 * STAGE_BYTES + 2 * PBUF_BYTES + PW_BYTES <= kMaxLds;
+  static constexpr bool SHARE_OK = true;
 #endif
-  static constexpr int STAGES = SHARE ? 3 : (2 * STAGE_BYTES + PW_BYTES <= kMaxLds ? 2 : 1);
-  static constexpr int OFF_P = STAGES * STAGE_BYTES;
-  static constexpr int OFF_PW = OFF_P + (SHARE ? 2 * PBUF_BYTES : 0);
+  static constexpr bool SHARE =
+      SHARE_OK && 3 * stage_bytes(LV_W) + 2 * PBUF_BYTES + PW_BYTES <= kMaxLds;
+  static constexpr bool SPLIT = SHARE_OK && !SHARE && split_bytes(LV_T) <= kMaxLds;
+  static constexpr int LV = (SPLIT && split_bytes(LV_W) > kMaxLds) ? LV_T : LV_W;
+  static constexpr int PF = SPLIT ? 1 : PF_BASE; // chunks the producers load ahead
+  // split schedule without a gate: Qt = phi(q) is formed when the Qt tile is free, from
+  // the q rows still in the staging registers (no copy held through phase 1)
+  static constexpr bool Q_LATE = SPLIT && DECAY != DECAY_GATE;
+  // LDS map (bytes).  SHARE / per-wave: [STAGES] x {Qt, Kt, V, eL}, [2] x score tiles
+  // (SHARE), gamma powers.  SPLIT: Qt, [2] x {Kt, V, eL}, score tiles, gamma powers.
+  static constexpr int OFF_Q = 0;
+  static constexpr int OFF_K = OFF_Q + QT_BYTES;
+  static constexpr int OFF_V = OFF_K + QT_BYTES;
+  static constexpr int OFF_EL = OFF_V + C * LV * ES;
+  static constexpr int STAGE_BYTES = OFF_EL + EL_BYTES;
+  static constexpr int KV_BYTES = QT_BYTES + C * LV * ES + EL_BYTES; // SPLIT {Kt, V, eL}
+  static constexpr int STAGES =
+      SHARE ? 3 : SPLIT ? 2 : (2 * STAGE_BYTES + PW_BYTES <= kMaxLds ? 2 : 1);
+  static constexpr int OFF_P = SPLIT ? QT_BYTES + 2 * KV_BYTES : STAGES * STAGE_BYTES;
+  static constexpr int OFF_PW = OFF_P + (SHARE ? 2 * PBUF_BYTES : SPLIT ? PBUF_BYTES : 0);
   static constexpr int LDS = OFF_PW + PW_BYTES;
   static constexpr bool FITS = LDS <= kMaxLds;
-  // state row order (bf16, shared-score schedule): accumulator row m = 4g + r of state
+  // byte offsets of the tiles of chunk n
+  __device__ static int q_at(int n) { return SPLIT ? 0 : (n % STAGES) * STAGE_BYTES + OFF_Q; }
+  __device__ static int k_at(int n) {
+    return SPLIT ? QT_BYTES + (n & 1) * KV_BYTES : (n % STAGES) * STAGE_BYTES + OFF_K;
+  }
+  __device__ static int v_at(int n) {
+    return SPLIT ? 2 * QT_BYTES + (n & 1) * KV_BYTES : (n % STAGES) * STAGE_BYTES + OFF_V;
+  }
+  __device__ static int el_at(int n) {
+    return SPLIT ? 2 * QT_BYTES + C * LV * ES + (n & 1) * KV_BYTES
+                 : (n % STAGES) * STAGE_BYTES + OFF_EL;
+  }
+  __device__ static int p_at(int n) { return OFF_P + (SHARE ? (n & 1) * PBUF_BYTES : 0); }
+  // state row order (bf16, shared score tiles): accumulator row m = 4g + r of state
   // block cb = 2u + s holds key index 32u + 8g + 4s + r, so that the bf16 operand built
   // from blocks 2u and 2u+1 has k = 32u + 8g + slot, the order of 16-byte LDS reads
-  static constexpr bool PERM = SHARE && BF && HI_DK;
+  static constexpr bool PERM = (SHARE || SPLIT) && BF && HI_DK;
   // scheduling fences in the shared-score consumer: between row blocks and before the
   // next chunk's score tiles (needed to stay within the registers with two tiles a wave)
 #ifdef FLA_FORCE_FENCE
@@ -207,6 +249,32 @@ __device__ __forceinline__ void unpack(float *f, const uint32_t *w) {
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) f[i] = __uint_as_float(w[i]);
+  }
+}
+
+// Pack N fp32 values as TIn elements into 32-bit words.
+template <typename TIn, int N>
+__device__ __forceinline__ void pack_words(uint32_t *w, const float *f) {
+  if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const bf16x2 b = {(__bf16)f[2 * i], (__bf16)f[2 * i + 1]};
+      w[i] = __builtin_bit_cast(uint32_t, b);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = __float_as_uint(f[i]);
+  }
+}
+// Store N (2, 4 or 8) 32-bit words to LDS.
+template <int N>
+__device__ __forceinline__ void st_words_lds(void *p, const uint32_t *w) {
+  if constexpr (N == 2) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      reinterpret_cast<uint4 *>(p)[i / 4] = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
   }
 }
 
@@ -292,29 +360,78 @@ __device__ __forceinline__ Frag<TIn> ld_frag_t(const TIn *tile, int ld, int col0
   }
 }
 
+// The same fragments from a lane base pointer (the lane-dependent part of the address
+// already added), so that every other offset is a compile-time constant that the
+// compiler folds into the LDS instruction.  Contiguous: base = row li, column 8g (bf16)
+// or 4g (fp32); transposed: base = row 4g + li/4, column CS (li%4) (bf16) or row 4g,
+// column li (fp32).
+template <typename TIn, bool HI>
+__device__ __forceinline__ Frag<TIn> ld_frag_c_at(const TIn *base, int u, int g) {
+  if constexpr (sizeof(TIn) == 2) {
+    if constexpr (HI) {
+      return *reinterpret_cast<const bf16x8 *>(base + 32 * u);
+    } else {
+      const __bf16 z = (__bf16)0.f;
+      bf16x8 r = {z, z, z, z, z, z, z, z};
+      if (g < 2) r = *reinterpret_cast<const bf16x8 *>(base + 32 * u);
+      return r;
+    }
+  } else {
+    return *reinterpret_cast<const f32x4 *>(base + 16 * u);
+  }
+}
+// split K convention (k = 32u + 4g + s, 32u + 16 + 4g + s - 4); base = row li, column 4g
+template <typename TIn, bool HI>
+__device__ __forceinline__ Frag<TIn> ld_frag_at(const TIn *base, int u) {
+  if constexpr (sizeof(TIn) == 2) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(base + 32 * u);
+    bf16x4 hi;
+    if constexpr (HI) hi = *reinterpret_cast<const bf16x4 *>(base + 32 * u + 16);
+    else hi = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    return *reinterpret_cast<const f32x4 *>(base + 16 * u);
+  }
+}
+template <typename TIn, bool HI>
+__device__ __forceinline__ Frag<TIn> ld_frag_t_at(const TIn *base, int ld, int col0, int u) {
+  if constexpr (sizeof(TIn) == 2) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const TIn *p = base + 32 * u * ld + col0;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+    i16x4 hi = {0, 0, 0, 0};
+    if constexpr (HI) hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 16 * ld));
+    const bf16x4 l = __builtin_bit_cast(bf16x4, lo), h = __builtin_bit_cast(bf16x4, hi);
+    return bf16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+  } else {
+    const TIn *p = base + 16 * u * ld + col0;
+    return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+  }
+}
+
 // Score tiles in LDS (shared-score schedule): a 16 x 16 tile of A^T (rows j, columns i)
 // is kept as its accumulator image, lane (g, li) owning elements li * 16 + 4g .. +3, which
 // is also where the P V operand fragment of that lane reads them.
 template <typename TIn>
-__device__ __forceinline__ void st_ptile(TIn *tile, int g, int li, f32x4 x) {
+__device__ __forceinline__ void st_ptile(TIn *ltile, f32x4 x) { // ltile: + li * 16 + 4g
   if constexpr (sizeof(TIn) == 2) {
-    *reinterpret_cast<bf16x4 *>(tile + li * 16 + 4 * g) =
-        bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+    *reinterpret_cast<bf16x4 *>(ltile) = bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
   } else {
-    *reinterpret_cast<f32x4 *>(tile + li * 16 + 4 * g) = x;
+    *reinterpret_cast<f32x4 *>(ltile) = x;
   }
 }
-// B operand of O^T += V^T A^T for K unit (two 16-row tiles ta, tb; tb < 0: zeros).
+// B operand of O^T += V^T A^T for K unit (two 16-row tiles ta, tb; tb < 0: zeros);
+// lbuf = score buffer + the lane's offset li * 16 + 4g.
 template <typename TIn, int TA, int TB>
-__device__ __forceinline__ Frag<TIn> ld_ptile(const TIn *buf, int g, int li) {
+__device__ __forceinline__ Frag<TIn> ld_ptile(const TIn *lbuf) {
   if constexpr (sizeof(TIn) == 2) {
-    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(buf + TA * 256 + li * 16 + 4 * g);
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(lbuf + TA * 256);
     bf16x4 hi = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-    if constexpr (TB >= 0) hi = *reinterpret_cast<const bf16x4 *>(buf + TB * 256 + li * 16 + 4 * g);
+    if constexpr (TB >= 0) hi = *reinterpret_cast<const bf16x4 *>(lbuf + TB * 256);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   } else {
     static_assert(TB < 0, "fp32 K units are one tile");
-    return *reinterpret_cast<const f32x4 *>(buf + TA * 256 + li * 16 + 4 * g);
+    return *reinterpret_cast<const f32x4 *>(lbuf + TA * 256);
   }
 }
 
@@ -349,13 +466,14 @@ __device__ __forceinline__ void ld_words_buf(uint32_t *w, __amdgpu_buffer_rsrc_t
     }
   }
 }
+// voff: the lane's byte offset; soff: the wave-uniform part (kDropOffset drops the store).
 template <typename TIn>
-__device__ __forceinline__ void st_out4_buf(__amdgpu_buffer_rsrc_t rs, int off, f32x4 o) {
+__device__ __forceinline__ void st_out4_buf(__amdgpu_buffer_rsrc_t rs, int voff, int soff, f32x4 o) {
   if constexpr (sizeof(TIn) == 2) {
     const bf16x4 b = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), rs, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), rs, voff, soff, 0);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs, voff, soff, 0);
   }
 }
 
@@ -452,7 +570,9 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
   const int bh = unit / a.nseg;
   const int h = bh % a.H;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // wave index through readfirstlane: the compiler then keeps everything derived from it
+  // (roles, value columns, tile masks) in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const bool producer = wave >= K::NCW;
   const bool state_only = a.state_only != 0;
 
@@ -506,15 +626,21 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       }
     };
     // q/k row r and v row r of chunk n
-    auto load_qk = [&](St &s, int n, int r) {
+    auto load_q = [&](St &s, int n, int r) {
       const int64_t t0 = t_begin + (int64_t)n * C;
-      const int64_t o = ((int64_t)bh * a.T + t0) * DK;
-      const int bytes = chunk_len(n) * DK * K::ES;
-      const auto rq = make_rsrc(static_cast<const TIn *>(a.q) + o, state_only ? 0 : bytes);
-      const auto rk = make_rsrc(static_cast<const TIn *>(a.k) + o, bytes);
-      const int off = ld_on ? ((row0 + r) * DK + col0) * K::ES : kDropOffset;
-      ld_words_buf<St::QW>(s.q[r], rq, off);
-      ld_words_buf<St::QW>(s.k[r], rk, off);
+      const auto rq = make_rsrc(static_cast<const TIn *>(a.q) + ((int64_t)bh * a.T + t0) * DK,
+                                state_only ? 0 : chunk_len(n) * DK * K::ES);
+      ld_words_buf<St::QW>(s.q[r], rq, ld_on ? ((row0 + r) * DK + col0) * K::ES : kDropOffset);
+    };
+    auto load_k = [&](St &s, int n, int r) {
+      const int64_t t0 = t_begin + (int64_t)n * C;
+      const auto rk = make_rsrc(static_cast<const TIn *>(a.k) + ((int64_t)bh * a.T + t0) * DK,
+                                chunk_len(n) * DK * K::ES);
+      ld_words_buf<St::QW>(s.k[r], rk, ld_on ? ((row0 + r) * DK + col0) * K::ES : kDropOffset);
+    };
+    auto load_qk = [&](St &s, int n, int r) {
+      load_q(s, n, r);
+      load_k(s, n, r);
     };
     auto load_v = [&](St &s, int n, int r) {
       const int64_t t0 = t_begin + (int64_t)n * C;
@@ -532,14 +658,48 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       for (int r = 0; r < K::RPT; ++r) load_qk(s, n, r);
     };
 
+    // split schedule: Qt rows of the chunk being prepared wait here for the Qt tile
+    uint32_t qkeep[K::SPLIT && !K::Q_LATE ? K::RPT : 1][St::QW];
+    // (Q_LATE: s holds chunk n's q rows; they are replaced by chunk n + 1's as they go)
+    auto store_q = [&](St &s, int n) {
+      if constexpr (K::Q_LATE) {
+        const int L = chunk_len(n);
+        TIn *sQ = reinterpret_cast<TIn *>(smem + K::q_at(n));
+        auto qrows = [&](auto elu_c) {
+          constexpr bool ELU = decltype(elu_c)::value;
+#pragma unroll
+          for (int r = 0; r < K::RPT; ++r) {
+            const int row = row0 + r;
+            float qv[K::G];
+            unpack<TIn, K::G>(qv, s.q[r]);
+#pragma unroll
+            for (int c = 0; c < K::G; ++c) {
+              float qq = qv[c];
+              if constexpr (ELU) qq = qq > 0.f ? qq + 1.f : __expf(qq);
+              qv[c] = row < L ? qq : 0.f;
+            }
+            if (ld_on) st_lds<TIn, K::G>(sQ + row * K::LQ + col0, qv);
+            load_q(s, n + 1, r);
+          }
+        };
+        if (a.phi_elu1) qrows(std::true_type{});
+        else qrows(std::false_type{});
+      } else if constexpr (K::SPLIT) {
+        if (ld_on) {
+          TIn *sQ = reinterpret_cast<TIn *>(smem + K::q_at(n));
+#pragma unroll
+          for (int r = 0; r < K::RPT; ++r) st_words_lds<St::QW>(sQ + (row0 + r) * K::LQ + col0, qkeep[r]);
+        }
+      }
+    };
+
+    // prepares chunk n (n may be one past the last chunk: L = 0, nothing loaded or read)
     auto prep = [&](St &s, int n) {
-      const int64_t t0 = t_begin + (int64_t)n * C;
-      const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
-      unsigned char *base = smem + (n % K::STAGES) * K::STAGE_BYTES;
-      TIn *sQ = reinterpret_cast<TIn *>(base + K::OFF_Q);
-      TIn *sK = reinterpret_cast<TIn *>(base + K::OFF_K);
-      TIn *sV = reinterpret_cast<TIn *>(base + K::OFF_V);
-      float *sEL = reinterpret_cast<float *>(base + K::OFF_EL);
+      const int L = chunk_len(n);
+      TIn *sQ = reinterpret_cast<TIn *>(smem + K::q_at(n));
+      TIn *sK = reinterpret_cast<TIn *>(smem + K::k_at(n));
+      TIn *sV = reinterpret_cast<TIn *>(smem + K::v_at(n));
+      float *sEL = reinterpret_cast<float *>(smem + K::el_at(n));
       // V rows are copied as they are; the next chunk's V goes out at once
       if (ptid < K::VACTIVE) {
 #pragma unroll
@@ -614,7 +774,11 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           const int row = row0 + r;
           float qv[K::G], kv[K::G];
           unpack<TIn, K::G>(kv, s.k[r]);
-          unpack<TIn, K::G>(qv, s.q[r]);
+          if constexpr (!K::Q_LATE) unpack<TIn, K::G>(qv, s.q[r]);
+          else {
+#pragma unroll
+            for (int c = 0; c < K::G; ++c) qv[c] = 0.f; // formed later from s.q
+          }
 #pragma unroll
           for (int c = 0; c < K::G; ++c) {
             float kk = kv[c], qq = qv[c];
@@ -634,8 +798,11 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
             qv[c] = qq;
           }
           st_lds<TIn, K::G>(sK + row * K::LQ + col0, kv);
-          if (!state_only) st_lds<TIn, K::G>(sQ + row * K::LQ + col0, qv);
-          load_qk(s, n + K::PF, r); // this row's registers are free again
+          if constexpr (K::Q_LATE) {
+          } else if constexpr (K::SPLIT) pack_words<TIn, K::G>(qkeep[r], qv);
+          else if (!state_only) st_lds<TIn, K::G>(sQ + row * K::LQ + col0, qv);
+          if constexpr (K::Q_LATE) load_k(s, n + K::PF, r);
+          else load_qk(s, n + K::PF, r); // this row's registers are free again
         }
       };
       if (ld_on) {
@@ -651,7 +818,21 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       }
     };
 
-    if constexpr (K::PF == 2) {
+    if constexpr (K::SPLIT) {
+      // barriers: A_n (chunk n in place) and B_n (phase 1 of chunk n done) for every chunk
+      St s0;
+      if (nch > 0) {
+        load(s0, 0);
+        prep(s0, 0);
+        store_q(s0, 0);
+      }
+      for (int n = 0; n < nch; ++n) {
+        __syncthreads(); // A_n
+        prep(s0, n + 1); // Kt, V of chunk n + 1 into the stage chunk n - 1 used
+        __syncthreads(); // B_n: Qt of chunk n read
+        store_q(s0, n + 1);
+      }
+    } else if constexpr (K::PF == 2) {
       St s0, s1;
       if (nch > 0) load(s0, 0);
       if (nch > 1) load(s1, 1);
@@ -716,14 +897,16 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     }
   }
 
-  if constexpr (K::SHARE) {
-    // ------------- shared-score schedule: iteration n computes this wave's score tiles of
-    // chunk n (stage n % 3) into score buffer n % 2, and the outputs and state update of
-    // chunk n - 1, whose tiles every consumer wave finished before this iteration's barrier.
-    const int cw = __builtin_amdgcn_readfirstlane(wave);
+  if constexpr (K::SHARE || K::SPLIT) {
+    // ---------------- consumer waves, score tiles shared through LDS ----------------
+    const int cw = wave;
+    // score tiles of this wave: tile k = s * NCW + cw of slot s; a slot past the last tile
+    // computes tile 0 into the discard tile
     int sib[K::SLOTS], sjb[K::SLOTS], sdst[K::SLOTS];
-    // gamma: gamma^{i-j} (0 above the diagonal) of each element of a tile
-    float fac[DECAY == DECAY_GAMMA ? K::SLOTS : 1][4];
+    // gamma: gamma^{i-j} (0 above the diagonal) of each element of a tile, held in
+    // registers when the slots are few
+    constexpr bool FAC_REG = DECAY == DECAY_GAMMA && K::SLOTS <= 5;
+    float fac[FAC_REG ? K::SLOTS : 1][4];
 #pragma unroll
     for (int s = 0; s < K::SLOTS; ++s) {
       const int k = s * K::NCW + cw;
@@ -733,7 +916,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       sib[s] = ib;
       sjb[s] = kk - ib * (ib + 1) / 2;
       sdst[s] = k < K::NTILES ? k : K::NTILES;
-      if constexpr (DECAY == DECAY_GAMMA) {
+      if constexpr (FAC_REG) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int dij = 16 * (ib - sjb[s]) + li - 4 * g - r; // i - j
@@ -754,50 +937,56 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
         }
     }
 
+    // this wave's masked score tiles of chunk n -> its score buffer
+    // Lane parts of the LDS addresses (elements).  Every access is tile base (uniform) +
+    // lane part + a compile-time offset; for the score slots the uniform part is formed per
+    // chunk in scalar registers and kept opaque, so that the compiler holds no per-slot
+    // vector registers through the loop.
+    const int lc = li * K::LQ + (K::BF ? 8 : 4) * g;                  // contiguous rows
+    const int ls = li * K::LQ + 4 * g;                                // split-convention rows
+    const int lkt = K::BF ? (4 * g + (li >> 2)) * K::LQ + (K::PERM ? 8 : 4) * (li & 3)
+                          : 4 * g * K::LQ + li;                       // Kt^T
+    const int lvt = K::BF ? (4 * g + (li >> 2)) * K::LV + 4 * (li & 3)
+                          : 4 * g * K::LV + li;                       // V^T
+    const int lp = li * 16 + 4 * g;                                   // score tiles
+    const int lel = K::PERM ? 8 * g : 4 * g;                          // eL
     auto scores = [&](int n) {
-      const unsigned char *base = smem + (n % K::STAGES) * K::STAGE_BYTES;
-      const TIn *sQ = reinterpret_cast<const TIn *>(base + K::OFF_Q);
-      const TIn *sK = reinterpret_cast<const TIn *>(base + K::OFF_K);
-      TIn *pb = reinterpret_cast<TIn *>(smem + K::OFF_P + (n & 1) * K::PBUF_BYTES);
 #pragma unroll
       for (int s = 0; s < K::SLOTS; ++s) {
-        const TIn *qrow = sQ + (16 * sib[s] + li) * K::LQ;
-        const TIn *krow = sK + (16 * sjb[s] + li) * K::LQ;
+        const int qo = __builtin_amdgcn_readfirstlane(K::q_at(n) + 16 * sib[s] * K::LQ * K::ES);
+        const int ko = __builtin_amdgcn_readfirstlane(K::k_at(n) + 16 * sjb[s] * K::LQ * K::ES);
+        const int po = __builtin_amdgcn_readfirstlane(K::p_at(n) + sdst[s] * K::PTILE * K::ES);
+        const TIn *qrow = reinterpret_cast<const TIn *>(smem + qo) + lc;
+        const TIn *krow = reinterpret_cast<const TIn *>(smem + ko) + lc;
+        TIn *ptile = reinterpret_cast<TIn *>(smem + po) + lp;
         f32x4 x = zero4;
 #pragma unroll
         for (int u = 0; u < K::NU_DK; ++u)
-          x = mma(x, ld_frag_c<TIn, K::HI_DK>(krow, u, g), ld_frag_c<TIn, K::HI_DK>(qrow, u, g));
+          x = mma(x, ld_frag_c_at<TIn, K::HI_DK>(krow, u, g), ld_frag_c_at<TIn, K::HI_DK>(qrow, u, g));
         // element (j = 16 jb + 4g + r, i = 16 ib + li): keep i >= j
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if constexpr (DECAY == DECAY_GAMMA) x[r] *= fac[s][r];
-          else x[r] = 16 * (sib[s] - sjb[s]) + dl - r >= 0 ? x[r] : 0.f;
+          const int dij = 16 * (sib[s] - sjb[s]) + dl - r;
+          if constexpr (FAC_REG) x[r] *= fac[s][r];
+          else if constexpr (DECAY == DECAY_GAMMA) x[r] = dij >= 0 ? x[r] * sPw[dij] : 0.f;
+          else x[r] = dij >= 0 ? x[r] : 0.f;
         }
-        st_ptile<TIn>(pb + sdst[s] * K::PTILE, g, li, x);
+        st_ptile<TIn>(ptile, x);
       }
     };
 
-    // outputs and state update of chunk m (FULL: m is not the last chunk, L = C); mid()
-    // runs between the two (the next chunk's score tiles, scheduled with the update)
-    auto rest = [&](int m, auto full_c, auto &&mid) {
+    // V^T operand fragments of chunk m (rows e, K = tokens j; columns past dv hold zeros)
+    // and the state-update operands (gamma: V' = diag(gamma^{L-1-j}) V; z: the all-ones
+    // or decay column)
+    F vf[K::ET][K::NU_C], vu[K::ET][K::NU_C], wz[NORM ? K::NU_C : 1];
+    auto v_operands = [&](const TIn *sV, int L, auto full_c) {
       constexpr bool FULL = decltype(full_c)::value;
-      const int64_t t0 = t_begin + (int64_t)m * C;
-      const int L = FULL ? C : (int)((t_end - t0) < C ? (t_end - t0) : C);
-      const unsigned char *base = smem + (m % K::STAGES) * K::STAGE_BYTES;
-      const TIn *sQ = reinterpret_cast<const TIn *>(base + K::OFF_Q);
-      const TIn *sK = reinterpret_cast<const TIn *>(base + K::OFF_K);
-      const TIn *sV = reinterpret_cast<const TIn *>(base + K::OFF_V);
-      const float *sEL = reinterpret_cast<const float *>(base + K::OFF_EL);
-      const TIn *pb = reinterpret_cast<const TIn *>(smem + K::OFF_P + (m & 1) * K::PBUF_BYTES);
-
-      // V^T operand fragments (rows e, K = tokens j); columns past dv hold zeros
-      F vf[K::ET][K::NU_C];
+      const TIn *vb = sV + lvt + 16 * K::ET * wave;
 #pragma unroll
       for (int t = 0; t < K::ET; ++t)
 #pragma unroll
         for (int u = 0; u < K::NU_C; ++u)
-          vf[t][u] = ld_frag_t<TIn, K::HI_C>(sV, K::LV, 16 * (K::ET * wave + t), u, g, li);
-      F vu[K::ET][K::NU_C], wz[NORM ? K::NU_C : 1];
+          vf[t][u] = ld_frag_t_at<TIn, K::HI_C>(vb, K::LV, 16 * t, u);
 #pragma unroll
       for (int u = 0; u < K::NU_C; ++u) {
         if constexpr (DECAY == DECAY_GAMMA) {
@@ -819,10 +1008,11 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           }
         }
       }
-      const float gl = (DECAY == DECAY_GAMMA) ? sPw[L] : 1.f;
+    };
 
-      // the state before this chunk as operands of the inter-chunk term
-      F hf[K::ET][K::NU_DK], zf[NORM ? K::NU_DK : 1];
+    // the state before a chunk as operands of the inter-chunk term
+    F hf[K::ET][K::NU_DK], zf[NORM ? K::NU_DK : 1];
+    auto state_operands = [&]() {
 #pragma unroll
       for (int u = 0; u < K::NU_DK; ++u) {
         if constexpr (K::BF) {
@@ -841,69 +1031,42 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           if constexpr (NORM) zf[u] = Zs[u];
         }
       }
+    };
 
-      // output rows of this chunk: stores past row L or column dv fall outside the range
-      const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-          gout + t0 * a.dv, (short)0, state_only ? 0 : L * a.dv * K::ES, kBufWord3);
-      static_for<0, K::NB>([&](auto IB) {
-        constexpr int ib = decltype(IB)::value;
-        // one row block's operands at a time (hoisting them all exceeds the registers)
-        if constexpr (K::FENCE & 1) __builtin_amdgcn_sched_barrier(0);
-        const TIn *qrow = sQ + (16 * ib + li) * K::LQ;
-        F qc[K::NU_DK];
+    // Qt operand fragments of row block ib (the order matching hf)
+    auto q_operands = [&](F *qc, const TIn *sQ, int ib) {
 #pragma unroll
-        for (int u = 0; u < K::NU_DK; ++u) {
-          if constexpr (K::PERM) qc[u] = ld_frag_c<TIn, true>(qrow, u, g);
-          else qc[u] = ld_frag<TIn, K::HI_DK>(qrow, u, g);
-        }
-        f32x4 acc[K::ET];
+      for (int u = 0; u < K::NU_DK; ++u) {
+        if constexpr (K::PERM) qc[u] = ld_frag_c_at<TIn, true>(sQ + lc + 16 * ib * K::LQ, u, g);
+        else qc[u] = ld_frag_at<TIn, K::HI_DK>(sQ + ls + 16 * ib * K::LQ, u);
+      }
+    };
+
+    // O^T += V^T A^T for row block IB from the score buffer pb
+    auto intra = [&](f32x4 *acc, f32x4 &accd, const TIn *pb, auto IB) {
+      constexpr int ib = decltype(IB)::value;
 #pragma unroll
-        for (int t = 0; t < K::ET; ++t) acc[t] = zero4;
-        f32x4 accd = zero4;
-        // intra-chunk: O^T += V^T A^T over the K units of tokens j <= i
-        static_for<0, K::NU_C>([&](auto JU) {
-          constexpr int ju = decltype(JU)::value;
-          constexpr int jb = ju * K::TPU;
-          if constexpr (jb <= ib) {
-            constexpr int ta = ib * (ib + 1) / 2 + jb;
-            constexpr int tb = (K::TPU == 2 && jb + 1 <= ib) ? ta + 1 : -1;
-            const F pf = ld_ptile<TIn, ta, tb>(pb, g, li);
+      for (int t = 0; t < K::ET; ++t) acc[t] = zero4;
+      accd = zero4;
+      static_for<0, K::NU_C>([&](auto JU) {
+        constexpr int ju = decltype(JU)::value;
+        constexpr int jb = ju * K::TPU;
+        if constexpr (jb <= ib) {
+          constexpr int ta = ib * (ib + 1) / 2 + jb;
+          constexpr int tb = (K::TPU == 2 && jb + 1 <= ib) ? ta + 1 : -1;
+          const F pf = ld_ptile<TIn, ta, tb>(pb + lp);
 #pragma unroll
-            for (int t = 0; t < K::ET; ++t) acc[t] = mma(acc[t], vf[t][ju], pf);
-            if constexpr (NORM) {
-              const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-              accd = mma(accd, frag_from<TIn>(one), pf);
-            }
+          for (int t = 0; t < K::ET; ++t) acc[t] = mma(acc[t], vf[t][ju], pf);
+          if constexpr (NORM) {
+            const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+            accd = mma(accd, frag_from<TIn>(one), pf);
           }
-        });
-        // inter-chunk: O^T += H^T Qt^T
-        float rsc = 1.f;
-        if constexpr (DECAY == DECAY_GAMMA) rsc = sPw[16 * ib + li + 1];
-        float inv = 1.f;
-        if constexpr (NORM) {
-          f32x4 accd2 = zero4;
-#pragma unroll
-          for (int u = 0; u < K::NU_DK; ++u) accd2 = mma(accd2, zf[u], qc[u]);
-          if constexpr (DECAY == DECAY_GAMMA) accd2 *= rsc;
-          accd += accd2;
-          inv = rcp_f(accd[0]); // every row of the ones tile holds the denominator
-        }
-        const int i = 16 * ib + li;
-#pragma unroll
-        for (int t = 0; t < K::ET; ++t) {
-          f32x4 acc2 = zero4;
-#pragma unroll
-          for (int u = 0; u < K::NU_DK; ++u) acc2 = mma(acc2, hf[t][u], qc[u]);
-          if constexpr (DECAY == DECAY_GAMMA) acc2 *= rsc;
-          f32x4 o = acc[t] + acc2;
-          if constexpr (NORM) o *= inv;
-          const int off = tile_on[t] ? (i * a.dv + e0 + 16 * t + 4 * g) * K::ES : kDropOffset;
-          st_out4_buf<TIn>(ors, off, o);
         }
       });
+    };
 
-      mid();
-      // S4 + S5: H <- decay (H + Kt^T V) (gamma: gamma^L H + Kt^T V')
+    // S4 + S5 for chunk m: H <- decay (H + Kt^T V) (gamma: gamma^L H + Kt^T V')
+    auto state_update = [&](const TIn *sK, const float *sEL, float gl) {
       static_for<0, K::NCB>([&](auto CB) {
         constexpr int cb = decltype(CB)::value;
         if constexpr (DECAY == DECAY_GAMMA) {
@@ -914,13 +1077,13 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
         constexpr int kcol = K::PERM ? 32 * (cb >> 1) + 4 * (cb & 1) : 16 * cb;
 #pragma unroll
         for (int u = 0; u < K::NU_C; ++u) {
-          const F kf = ld_frag_t<TIn, K::HI_C, K::PERM ? 8 : 4>(sK, K::LQ, kcol, u, g, li);
+          const F kf = ld_frag_t_at<TIn, K::HI_C>(sK + lkt, K::LQ, kcol, u);
 #pragma unroll
           for (int t = 0; t < K::ET; ++t) Hs[t][cb] = mma(Hs[t][cb], kf, vu[t][u]);
           if constexpr (NORM) Zs[cb] = mma(Zs[cb], kf, wz[u]);
         }
         if constexpr (DECAY == DECAY_GATE) {
-          const float4 el = *reinterpret_cast<const float4 *>(sEL + K::state_row(cb, g, 0));
+          const float4 el = *reinterpret_cast<const float4 *>(sEL + lel + K::state_row(cb, 0, 0));
 #pragma unroll
           for (int t = 0; t < K::ET; ++t) {
             Hs[t][cb][0] *= el.x; Hs[t][cb][1] *= el.y; Hs[t][cb][2] *= el.z; Hs[t][cb][3] *= el.w;
@@ -932,18 +1095,143 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       });
     };
 
-    if (nch > 0) {
-      __syncthreads(); // stage 0 holds chunk 0
-      scores(0);
-      for (int n = 1; n < nch; ++n) {
-        __syncthreads(); // stage n % 3 holds chunk n; score tiles of chunk n - 1 complete
-        rest(n - 1, std::true_type{}, [&] {
-          if constexpr (K::FENCE & 2) __builtin_amdgcn_sched_barrier(0);
-          scores(n);
+    // output rows of chunk m: stores past row L or column dv fall outside the range
+    auto out_rsrc = [&](int64_t t0, int L) {
+      return make_rsrc(gout + t0 * a.dv, state_only ? 0 : L * a.dv * K::ES);
+    };
+    // lane part of an output offset in a vector register, the row block and tile part
+    // (uniform) in the scalar offset
+    const int out_lane = (li * a.dv + 4 * g) * K::ES;
+    auto store_out = [&](__amdgpu_buffer_rsrc_t ors, int ib, int t, f32x4 o) {
+      const int soff = __builtin_amdgcn_readfirstlane(
+          tile_on[t] ? (16 * ib * a.dv + e0 + 16 * t) * K::ES : kDropOffset);
+      st_out4_buf<TIn>(ors, out_lane, soff, o);
+    };
+
+    if constexpr (K::SHARE) {
+      // Iteration n computes this wave's score tiles of chunk n (stage n % 3) into score
+      // buffer n % 2, and the outputs and state update of chunk n - 1, whose tiles every
+      // consumer wave finished before this iteration's barrier.  mid() runs between the
+      // outputs and the state update (the next chunk's score tiles, scheduled with it).
+      auto rest = [&](int m, auto full_c, auto &&mid) {
+        constexpr bool FULL = decltype(full_c)::value;
+        const int64_t t0 = t_begin + (int64_t)m * C;
+        const int L = FULL ? C : (int)((t_end - t0) < C ? (t_end - t0) : C);
+        const TIn *sQ = reinterpret_cast<const TIn *>(smem + K::q_at(m));
+        const TIn *pb = reinterpret_cast<const TIn *>(smem + K::p_at(m));
+        v_operands(reinterpret_cast<const TIn *>(smem + K::v_at(m)), L, full_c);
+        const float gl = (DECAY == DECAY_GAMMA) ? (FULL ? sPw[C] : sPw[L]) : 1.f;
+        state_operands();
+        const auto ors = out_rsrc(t0, L);
+        static_for<0, K::NB>([&](auto IB) {
+          constexpr int ib = decltype(IB)::value;
+          // one row block's operands at a time (hoisting them all exceeds the registers)
+          if constexpr (K::FENCE & 1) __builtin_amdgcn_sched_barrier(0);
+          F qc[K::NU_DK];
+          q_operands(qc, sQ, ib);
+          f32x4 acc[K::ET], accd;
+          intra(acc, accd, pb, IB);
+          // inter-chunk: O^T += H^T Qt^T
+          float rsc = 1.f;
+          if constexpr (DECAY == DECAY_GAMMA) rsc = sPw[16 * ib + li + 1];
+          float inv = 1.f;
+          if constexpr (NORM) {
+            f32x4 accd2 = zero4;
+#pragma unroll
+            for (int u = 0; u < K::NU_DK; ++u) accd2 = mma(accd2, zf[u], qc[u]);
+            if constexpr (DECAY == DECAY_GAMMA) accd2 *= rsc;
+            accd += accd2;
+            inv = rcp_f(accd[0]); // every row of the ones tile holds the denominator
+          }
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) {
+            f32x4 acc2 = zero4;
+#pragma unroll
+            for (int u = 0; u < K::NU_DK; ++u) acc2 = mma(acc2, hf[t][u], qc[u]);
+            if constexpr (DECAY == DECAY_GAMMA) acc2 *= rsc;
+            f32x4 o = acc[t] + acc2;
+            if constexpr (NORM) o *= inv;
+            store_out(ors, ib, t, o);
+          }
         });
+        mid();
+        state_update(reinterpret_cast<const TIn *>(smem + K::k_at(m)),
+                     reinterpret_cast<const float *>(smem + K::el_at(m)), gl);
+      };
+
+      if (nch > 0) {
+        __syncthreads(); // stage 0 holds chunk 0
+        scores(0);
+        for (int n = 1; n < nch; ++n) {
+          __syncthreads(); // stage n % 3 holds chunk n; score tiles of chunk n - 1 complete
+          rest(n - 1, std::true_type{}, [&] {
+            if constexpr (K::FENCE & 2) __builtin_amdgcn_sched_barrier(0);
+            scores(n);
+          });
+        }
+        __syncthreads();
+        rest(nch - 1, std::false_type{}, [] {});
       }
-      __syncthreads();
-      rest(nch - 1, std::false_type{}, [] {});
+    } else {
+      // Split schedule, two barriers a chunk.  Phase 1: the inter-chunk term of every row
+      // block from the state before the chunk, and this wave's score tiles.  Phase 2:
+      // O += A V, the outputs, the state update.
+      for (int n = 0; n < nch; ++n) {
+        const int64_t t0 = t_begin + (int64_t)n * C;
+        const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
+        const TIn *sQ = reinterpret_cast<const TIn *>(smem + K::q_at(n));
+        const TIn *pb = reinterpret_cast<const TIn *>(smem + K::p_at(n));
+        __syncthreads(); // Qt, Kt, V of chunk n in place
+        state_operands();
+        f32x4 inter[K::NB][K::ET];
+        f32x4 dinter[NORM ? K::NB : 1];
+        static_for<0, K::NB>([&](auto IB) {
+          constexpr int ib = decltype(IB)::value;
+          F qc[K::NU_DK];
+          q_operands(qc, sQ, ib);
+          float rsc = 1.f;
+          if constexpr (DECAY == DECAY_GAMMA) rsc = sPw[16 * ib + li + 1];
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) {
+            f32x4 x = zero4;
+#pragma unroll
+            for (int u = 0; u < K::NU_DK; ++u) x = mma(x, hf[t][u], qc[u]);
+            if constexpr (DECAY == DECAY_GAMMA) x *= rsc;
+            inter[ib][t] = x;
+          }
+          if constexpr (NORM) {
+            f32x4 x = zero4;
+#pragma unroll
+            for (int u = 0; u < K::NU_DK; ++u) x = mma(x, zf[u], qc[u]);
+            if constexpr (DECAY == DECAY_GAMMA) x *= rsc;
+            dinter[ib] = x;
+          }
+        });
+        scores(n);
+        __syncthreads(); // score tiles complete; Qt free for the next chunk
+        v_operands(reinterpret_cast<const TIn *>(smem + K::v_at(n)), L, std::false_type{});
+        const float gl = (DECAY == DECAY_GAMMA) ? sPw[L] : 1.f;
+        const auto ors = out_rsrc(t0, L);
+        static_for<0, K::NB>([&](auto IB) {
+          constexpr int ib = decltype(IB)::value;
+          if constexpr (K::FENCE & 1) __builtin_amdgcn_sched_barrier(0);
+          f32x4 acc[K::ET], accd;
+          intra(acc, accd, pb, IB);
+          float inv = 1.f;
+          if constexpr (NORM) {
+            accd += dinter[ib];
+            inv = rcp_f(accd[0]);
+          }
+#pragma unroll
+          for (int t = 0; t < K::ET; ++t) {
+            f32x4 o = acc[t] + inter[ib][t];
+            if constexpr (NORM) o *= inv;
+            store_out(ors, ib, t, o);
+          }
+        });
+        state_update(reinterpret_cast<const TIn *>(smem + K::k_at(n)),
+                     reinterpret_cast<const float *>(smem + K::el_at(n)), gl);
+      }
     }
   } else {
   for (int n = 0; n < nch; ++n) {

@@ -130,6 +130,24 @@ def test_shape_sweep(dtype, dk, dv, chunk, T, decay, norm, init):
     check(w, inp, f"sweep {dtype} dk={dk} dv={dv} C={chunk} T={T} {decay} norm={norm}")
 
 
+# Large tiles take the two-barrier schedule (one Qt tile, double-buffered Kt/V), small ones
+# the shared-score schedule: every decay kind and the normaliser on representatives of each,
+# with a ragged sequence end and value widths of half a slice (some consumer waves own no
+# valid column) and of two slices.
+SCHEDULE_SHAPES = [("bf16", 128, 128), ("bf16", 256, 64), ("f32", 128, 64), ("bf16", 64, 128),
+                   ("bf16", 128, 64), ("f32", 32, 64)]
+SCHEDULE_CASES = [(dt, dk, c, dec, norm) for (dt, dk, c) in SCHEDULE_SHAPES
+                  for dec in ("none", "gamma", "gate") for norm in (False, True)]
+
+
+@pytest.mark.parametrize("dtype,dk,chunk,decay,norm", SCHEDULE_CASES)
+def test_schedules(dtype, dk, chunk, decay, norm):
+    i = SCHEDULE_CASES.index((dtype, dk, chunk, decay, norm))
+    w, inp = small_case(dtype, decay, dk, 32 if i % 2 == 0 else 128, 2 * chunk + 7, B=1, H=2,
+                        chunk=chunk, phi=norm, norm=norm, init=True, seed=500 + i)
+    check(w, inp, f"schedule {dtype} dk={dk} C={chunk} {decay} norm={norm}")
+
+
 def test_unsupported_combination_raises():
     q = torch.zeros((1, 1, 128, 256), dtype=torch.float32, device="cuda")
     v = torch.zeros((1, 1, 128, 64), dtype=torch.float32, device="cuda")
