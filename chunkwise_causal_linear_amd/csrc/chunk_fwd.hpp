@@ -925,9 +925,15 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       }
     }
     const int dl = li - 4 * g;
-    // gamma: V' row factors gamma^{C-1-j} of a full chunk
-    float vsc[DECAY == DECAY_GAMMA ? K::NU_C : 1][8];
-    if constexpr (DECAY == DECAY_GAMMA) {
+    // gamma: V' row factors gamma^{C-1-j} of a full chunk (held in registers, or read from
+    // the power table where they are used)
+#ifdef FLA_VSC_REG
+    constexpr bool VSC_REG = FLA_VSC_REG;
+#else
+    constexpr bool VSC_REG = false;
+#endif
+    float vsc[VSC_REG && DECAY == DECAY_GAMMA ? K::NU_C : 1][8];
+    if constexpr (VSC_REG && DECAY == DECAY_GAMMA) {
 #pragma unroll
       for (int u = 0; u < K::NU_C; ++u)
 #pragma unroll
@@ -979,14 +985,17 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     // and the state-update operands (gamma: V' = diag(gamma^{L-1-j}) V; z: the all-ones
     // or decay column)
     F vf[K::ET][K::NU_C], vu[K::ET][K::NU_C], wz[NORM ? K::NU_C : 1];
-    auto v_operands = [&](const TIn *sV, int L, auto full_c) {
-      constexpr bool FULL = decltype(full_c)::value;
+    auto v_operands = [&](const TIn *sV) {
       const TIn *vb = sV + lvt + 16 * K::ET * wave;
 #pragma unroll
       for (int t = 0; t < K::ET; ++t)
 #pragma unroll
         for (int u = 0; u < K::NU_C; ++u)
           vf[t][u] = ld_frag_t_at<TIn, K::HI_C>(vb, K::LV, 16 * t, u);
+    };
+    // (formed right before the state update: the scaling need not wait for vf earlier)
+    auto update_operands = [&](int L, auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
       for (int u = 0; u < K::NU_C; ++u) {
         if constexpr (DECAY == DECAY_GAMMA) {
@@ -994,7 +1003,8 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
           for (int q = 0; q < (K::BF ? 8 : 4); ++q) {
             const int j = K::BF ? (32 * u + (q < 4 ? 0 : 16) + 4 * g + (q & 3)) : (16 * u + 4 * g + q);
-            sc[q] = FULL ? vsc[u][q] : (j < L ? sPw[L - 1 - j] : 0.f);
+            if constexpr (VSC_REG) sc[q] = FULL ? vsc[u][q] : (j < L ? sPw[L - 1 - j] : 0.f);
+            else sc[q] = FULL ? sPw[C - 1 - j] : (j < L ? sPw[L - 1 - j] : 0.f);
           }
 #pragma unroll
           for (int t = 0; t < K::ET; ++t) vu[t][u] = scale_frag(vf[t][u], sc);
@@ -1119,7 +1129,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
         const int L = FULL ? C : (int)((t_end - t0) < C ? (t_end - t0) : C);
         const TIn *sQ = reinterpret_cast<const TIn *>(smem + K::q_at(m));
         const TIn *pb = reinterpret_cast<const TIn *>(smem + K::p_at(m));
-        v_operands(reinterpret_cast<const TIn *>(smem + K::v_at(m)), L, full_c);
+        v_operands(reinterpret_cast<const TIn *>(smem + K::v_at(m)));
         const float gl = (DECAY == DECAY_GAMMA) ? (FULL ? sPw[C] : sPw[L]) : 1.f;
         state_operands();
         const auto ors = out_rsrc(t0, L);
@@ -1155,6 +1165,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           }
         });
         mid();
+        update_operands(L, full_c);
         state_update(reinterpret_cast<const TIn *>(smem + K::k_at(m)),
                      reinterpret_cast<const float *>(smem + K::el_at(m)), gl);
       };
@@ -1209,7 +1220,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
         });
         scores(n);
         __syncthreads(); // score tiles complete; Qt free for the next chunk
-        v_operands(reinterpret_cast<const TIn *>(smem + K::v_at(n)), L, std::false_type{});
+        v_operands(reinterpret_cast<const TIn *>(smem + K::v_at(n)));
         const float gl = (DECAY == DECAY_GAMMA) ? sPw[L] : 1.f;
         const auto ors = out_rsrc(t0, L);
         static_for<0, K::NB>([&](auto IB) {
@@ -1229,6 +1240,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
             store_out(ors, ib, t, o);
           }
         });
+        update_operands(L, std::false_type{});
         state_update(reinterpret_cast<const TIn *>(smem + K::k_at(n)),
                      reinterpret_cast<const float *>(smem + K::el_at(n)), gl);
       }
