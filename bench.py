@@ -59,7 +59,7 @@ def algorithmic(w) -> tuple[float, float]:
 def kernel_name(w) -> str:
     t = "__bf16" if w.dtype == "bf16" else "float"
     d = {"none": 0, "gamma": 1, "gate": 2}[w.decay]
-    return f"chunk_fwd_kernel<{t}, {w.dk}, {w.chunk}, {d}, {str(w.normalize).lower()}>"
+    return f"chunk_fwd_kernel<{t}, {w.dk}, {w.chunk}, {d}, {str(w.normalize).lower()}, false>"
 
 
 def cpu_baseline(w, inp, out_gpu, fin_gpu, budget_s: float):

@@ -551,7 +551,8 @@ struct Staged {
 // ---------------------------------------------------------------------------------
 // The fused chunk kernel.
 
-template <typename TIn, int DK, int C, int DECAY, bool NORM>
+// SO: end states only (the first pass of the segment schedule; a.state_only is 1).
+template <typename TIn, int DK, int C, int DECAY, bool NORM, bool SO>
 __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
   using K = Cfg<TIn, DK, C, DECAY, NORM>;
   using F = Frag<TIn>;
@@ -574,7 +575,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
   // (roles, value columns, tile masks) in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const bool producer = wave >= K::NCW;
-  const bool state_only = a.state_only != 0;
+  constexpr bool state_only = SO;
 
   const int64_t t_begin = (int64_t)seg * a.seg_len;
   int64_t t_end = t_begin + a.seg_len;
@@ -1118,7 +1119,28 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       st_out4_buf<TIn>(ors, out_lane, soff, o);
     };
 
-    if constexpr (K::SHARE) {
+    // end states only (first pass of the segment schedule): the state update of every
+    // chunk, with the same barriers as the producers
+    auto state_only_loop = [&]() {
+      for (int n = 0; n < nch; ++n) {
+        const int64_t t0 = t_begin + (int64_t)n * C;
+        const int L = (int)((t_end - t0) < C ? (t_end - t0) : C);
+        __syncthreads();
+        v_operands(reinterpret_cast<const TIn *>(smem + K::v_at(n)));
+        update_operands(L, std::false_type{});
+        state_update(reinterpret_cast<const TIn *>(smem + K::k_at(n)),
+                     reinterpret_cast<const float *>(smem + K::el_at(n)),
+                     (DECAY == DECAY_GAMMA) ? sPw[L] : 1.f);
+        if constexpr (K::SPLIT) __syncthreads();
+      }
+      if constexpr (K::SHARE) {
+        if (nch > 0) __syncthreads();
+      }
+    };
+
+    if constexpr (SO) {
+      state_only_loop();
+    } else if constexpr (K::SHARE) {
       // Iteration n computes this wave's score tiles of chunk n (stage n % 3) into score
       // buffer n % 2, and the outputs and state update of chunk n - 1, whose tiles every
       // consumer wave finished before this iteration's barrier.  mid() runs between the

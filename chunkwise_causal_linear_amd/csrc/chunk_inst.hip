@@ -23,8 +23,10 @@ template <int C, int DECAY, bool NORM>
 hipError_t launch_impl(const ChunkArgs &a, unsigned grid, hipStream_t s) {
   ChunkArgs copy = a;
   void *args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void *>(&chunk_fwd_kernel<TIn, DK, C, DECAY, NORM>),
-                         dim3(grid), dim3(Cfg<TIn, DK, C, DECAY, NORM>::NT), args, 0, s);
+  const void *fn = a.state_only
+                       ? reinterpret_cast<const void *>(&chunk_fwd_kernel<TIn, DK, C, DECAY, NORM, true>)
+                       : reinterpret_cast<const void *>(&chunk_fwd_kernel<TIn, DK, C, DECAY, NORM, false>);
+  return hipLaunchKernel(fn, dim3(grid), dim3(Cfg<TIn, DK, C, DECAY, NORM>::NT), args, 0, s);
 }
 
 template <int C, int DECAY, bool NORM>
