@@ -440,6 +440,12 @@ __device__ __forceinline__ Frag<TIn> ld_ptile(const TIn *lbuf) {
 // the end of a chunk and the columns past dv without a branch.
 constexpr int kBufWord3 = 0x00020000; // gfx9 buffer resource: 32-bit data format
 constexpr int kDropOffset = 0x7ff00000; // beyond any chunk's output range
+// Keeps the vector-memory instructions on either side in program order (everything else
+// may still move across).  The producers issue each chunk's loads in the order they are
+// consumed; vmcnt retires loads in issue order, so a load the scheduler moved later would
+// make the wait for an earlier one drain everything behind it.
+__device__ __forceinline__ void vmem_order() { __builtin_amdgcn_sched_barrier(0x078F); }
+
 // Buffer resource for [base, base + bytes).  Both must be uniform across the wave (they
 // are: derived from the workgroup's unit and the chunk index); reading them through
 // readfirstlane keeps them in scalar registers, where the compiler could otherwise wrap
@@ -654,9 +660,20 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     auto load = [&](St &s, int n) {
 #pragma unroll
       for (int r = 0; r < K::RPTV; ++r) load_v(s, n, r);
+      vmem_order();
       load_gate(s, n);
+      vmem_order();
 #pragma unroll
-      for (int r = 0; r < K::RPT; ++r) load_qk(s, n, r);
+      for (int r = 0; r < K::RPT; ++r) {
+        if constexpr (K::Q_LATE) load_k(s, n, r);
+        else load_qk(s, n, r);
+      }
+      vmem_order();
+      if constexpr (K::Q_LATE) {
+#pragma unroll
+        for (int r = 0; r < K::RPT; ++r) load_q(s, n, r);
+        vmem_order();
+      }
     };
 
     // split schedule: Qt rows of the chunk being prepared wait here for the Qt tile
@@ -680,11 +697,14 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
               qv[c] = row < L ? qq : 0.f;
             }
             if (ld_on) st_lds<TIn, K::G>(sQ + row * K::LQ + col0, qv);
-            load_q(s, n + 1, r);
           }
         };
         if (a.phi_elu1) qrows(std::true_type{});
         else qrows(std::false_type{});
+        // the next chunk's q rows, outside the branch so that their wait counts stay exact
+#pragma unroll
+        for (int r = 0; r < K::RPT; ++r) load_q(s, n + 1, r);
+        vmem_order();
       } else if constexpr (K::SPLIT) {
         if (ld_on) {
           TIn *sQ = reinterpret_cast<TIn *>(smem + K::q_at(n));
@@ -713,6 +733,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < K::RPTV; ++r) load_v(s, n + K::PF, r);
+      vmem_order();
       // gate: b_i = local cumulative product over this lane's rows times the product of
       // the row groups above it (inclusive shuffle scan across lanes rg*LPR + cgl)
       float bc[DECAY == DECAY_GATE ? K::RPT : 1][K::G];
@@ -764,6 +785,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
         }
         if (ld_on && rg == 0) st_lds<float, K::G>(sEL + col0, tot);
         load_gate(s, n + K::PF);
+        vmem_order();
       } else if constexpr (DECAY == DECAY_GAMMA) {
         dprod[0] *= sPw[L];
       }
@@ -802,8 +824,10 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           if constexpr (K::Q_LATE) {
           } else if constexpr (K::SPLIT) pack_words<TIn, K::G>(qkeep[r], qv);
           else if (!state_only) st_lds<TIn, K::G>(sQ + row * K::LQ + col0, qv);
-          if constexpr (K::Q_LATE) load_k(s, n + K::PF, r);
-          else load_qk(s, n + K::PF, r); // this row's registers are free again
+          if constexpr (!K::SPLIT) {
+            load_qk(s, n + K::PF, r); // this row's registers are free
+            vmem_order();
+          }
         }
       };
       if (ld_on) {
@@ -816,6 +840,17 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           if (L == C) rows(F_{}, T_{});
           else rows(F_{}, F_{});
         }
+      }
+      // Split schedule: the next chunk's q/k rows after the branches above (inside them,
+      // the compiler's wait counts for these loads turn conservative across that loop's
+      // two barriers; the one-barrier loops keep exact counts with the loads per row).
+      if constexpr (K::SPLIT) {
+#pragma unroll
+        for (int r = 0; r < K::RPT; ++r) {
+          if constexpr (K::Q_LATE) load_k(s, n + K::PF, r);
+          else load_qk(s, n + K::PF, r);
+        }
+        vmem_order();
       }
     };
 
@@ -837,15 +872,14 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       St s0, s1;
       if (nch > 0) load(s0, 0);
       if (nch > 1) load(s1, 1);
+      static_assert(K::STAGES >= 2, "two chunks ahead needs two stages");
       for (int n = 0; n < nch; n += 2) {
         prep(s0, n);
         __syncthreads();
-        if constexpr (K::STAGES == 1) __syncthreads();
-        if (n + 1 < nch) {
-          prep(s1, n + 1);
-          __syncthreads();
-          if constexpr (K::STAGES == 1) __syncthreads();
-        }
+        // unconditional: past the last chunk it loads nothing and fills a stage no consumer
+        // reads (keeps the loads' wait counts exact); only the barrier follows the chunks
+        prep(s1, n + 1);
+        if (n + 1 < nch) __syncthreads();
       }
     } else {
       St s0;
