@@ -938,10 +938,35 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     // score tiles of this wave: tile k = s * NCW + cw of slot s; a slot past the last tile
     // computes tile 0 into the discard tile
     int sib[K::SLOTS], sjb[K::SLOTS], sdst[K::SLOTS];
-    // gamma: gamma^{i-j} (0 above the diagonal) of each element of a tile, held in
-    // registers when the slots are few
-    constexpr bool FAC_REG = DECAY == DECAY_GAMMA && K::SLOTS <= 5;
-    float fac[FAC_REG ? K::SLOTS : 1][4];
+    const int dl = li - 4 * g;
+    // Gamma powers in the loop.  Split schedule: no table reads; each power is a lane part
+    // gamma^0..31 (vector registers) times gamma^{16k} (uniform: scalar registers).
+    // Shared-score schedule (which runs at the register limit, where the compiler's schedule
+    // measured best this way): mask factors in registers, V' factors and row scales from the
+    // power table.
+    auto uni = [](float x) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+    };
+    constexpr bool GM = DECAY == DECAY_GAMMA;
+    constexpr bool GF = GM && K::SPLIT;
+    float g16[GF ? K::NB + 1 : 1];  // gamma^{16k}, k = 0..NB (gamma^C = g16[NB])
+    float vpl[4], fdiag[4], foff[4], lrow = 1.f;
+    float smul[K::SLOTS];
+    bool sdiag[K::SLOTS];
+    float fac[GM && !GF ? K::SLOTS : 1][4]; // gamma^{i-j} (0 above the diagonal) per element
+    if constexpr (GF) {
+#pragma unroll
+      for (int k = 0; k <= K::NB; ++k) g16[k] = uni(sPw[16 * k]);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) vpl[qq] = sPw[15 - 4 * g - qq]; // V' lane part
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = dl - r; // i - j inside a diagonal tile
+        fdiag[r] = d >= 0 ? sPw[d] : 0.f;
+        foff[r] = K::NB >= 2 ? sPw[16 + d] : 0.f; // off-diagonal: times gamma^{16 (ib - jb - 1)}
+      }
+      lrow = sPw[li + 1];
+    }
 #pragma unroll
     for (int s = 0; s < K::SLOTS; ++s) {
       const int k = s * K::NCW + cw;
@@ -951,31 +976,16 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       sib[s] = ib;
       sjb[s] = kk - ib * (ib + 1) / 2;
       sdst[s] = k < K::NTILES ? k : K::NTILES;
-      if constexpr (FAC_REG) {
+      sdiag[s] = sib[s] == sjb[s];
+      smul[s] = 0.f;
+      if constexpr (GF) smul[s] = uni(sdiag[s] ? 0.f : sPw[16 * (sib[s] - sjb[s] - 1)]);
+      if constexpr (GM && !GF) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int dij = 16 * (ib - sjb[s]) + li - 4 * g - r; // i - j
+          const int dij = 16 * (sib[s] - sjb[s]) + dl - r;
           fac[s][r] = dij >= 0 ? sPw[dij] : 0.f;
         }
       }
-    }
-    const int dl = li - 4 * g;
-    // gamma: V' row factors gamma^{C-1-j} of a full chunk (held in registers, or read from
-    // the power table where they are used)
-#ifdef FLA_VSC_REG
-    constexpr bool VSC_REG = FLA_VSC_REG;
-#else
-    constexpr bool VSC_REG = false;
-#endif
-    float vsc[VSC_REG && DECAY == DECAY_GAMMA ? K::NU_C : 1][8];
-    if constexpr (VSC_REG && DECAY == DECAY_GAMMA) {
-#pragma unroll
-      for (int u = 0; u < K::NU_C; ++u)
-#pragma unroll
-        for (int q = 0; q < (K::BF ? 8 : 4); ++q) {
-          const int j = K::BF ? (32 * u + (q < 4 ? 0 : 16) + 4 * g + (q & 3)) : (16 * u + 4 * g + q);
-          vsc[u][q] = j < C ? sPw[C - 1 - j] : 0.f;
-        }
     }
 
     // this wave's masked score tiles of chunk n -> its score buffer
@@ -1004,13 +1014,17 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
         for (int u = 0; u < K::NU_DK; ++u)
           x = mma(x, ld_frag_c_at<TIn, K::HI_DK>(krow, u, g), ld_frag_c_at<TIn, K::HI_DK>(qrow, u, g));
-        // element (j = 16 jb + 4g + r, i = 16 ib + li): keep i >= j
+        // element (j = 16 jb + 4g + r, i = 16 ib + li): keep i >= j (gamma: times gamma^{i-j})
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int dij = 16 * (sib[s] - sjb[s]) + dl - r;
-          if constexpr (FAC_REG) x[r] *= fac[s][r];
-          else if constexpr (DECAY == DECAY_GAMMA) x[r] = dij >= 0 ? x[r] * sPw[dij] : 0.f;
-          else x[r] = dij >= 0 ? x[r] : 0.f;
+          if constexpr (GF) {
+            x[r] *= sdiag[s] ? fdiag[r] : smul[s] * foff[r];
+          } else if constexpr (GM) {
+            x[r] *= fac[s][r];
+          } else {
+            const int dij = 16 * (sib[s] - sjb[s]) + dl - r;
+            x[r] = dij >= 0 ? x[r] : 0.f;
+          }
         }
         st_ptile<TIn>(ptile, x);
       }
@@ -1038,8 +1052,15 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
           for (int q = 0; q < (K::BF ? 8 : 4); ++q) {
             const int j = K::BF ? (32 * u + (q < 4 ? 0 : 16) + 4 * g + (q & 3)) : (16 * u + 4 * g + q);
-            if constexpr (VSC_REG) sc[q] = FULL ? vsc[u][q] : (j < L ? sPw[L - 1 - j] : 0.f);
-            else sc[q] = FULL ? sPw[C - 1 - j] : (j < L ? sPw[L - 1 - j] : 0.f);
+            if constexpr (FULL && GF) {
+              // gamma^{C-1-j} = gamma^{15-4g-(q%4)} gamma^{16k}
+              const int kq = K::BF ? C / 16 - 1 - 2 * u - (q >> 2) : C / 16 - 1 - u;
+              sc[q] = kq >= 0 ? vpl[q & 3] * g16[kq < 0 ? 0 : kq] : 0.f;
+            } else if constexpr (FULL) {
+              sc[q] = sPw[C - 1 - j];
+            } else {
+              sc[q] = j < L ? sPw[L - 1 - j] : 0.f;
+            }
           }
 #pragma unroll
           for (int t = 0; t < K::ET; ++t) vu[t][u] = scale_frag(vf[t][u], sc);
@@ -1186,7 +1207,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
         const TIn *sQ = reinterpret_cast<const TIn *>(smem + K::q_at(m));
         const TIn *pb = reinterpret_cast<const TIn *>(smem + K::p_at(m));
         v_operands(reinterpret_cast<const TIn *>(smem + K::v_at(m)));
-        const float gl = (DECAY == DECAY_GAMMA) ? (FULL ? sPw[C] : sPw[L]) : 1.f;
+        const float gl = GM ? (FULL ? sPw[C] : sPw[L]) : 1.f;
         state_operands();
         const auto ors = out_rsrc(t0, L);
         static_for<0, K::NB>([&](auto IB) {
@@ -1199,7 +1220,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           intra(acc, accd, pb, IB);
           // inter-chunk: O^T += H^T Qt^T
           float rsc = 1.f;
-          if constexpr (DECAY == DECAY_GAMMA) rsc = sPw[16 * ib + li + 1];
+          if constexpr (GM) rsc = sPw[16 * ib + li + 1];
           float inv = 1.f;
           if constexpr (NORM) {
             f32x4 accd2 = zero4;
@@ -1257,7 +1278,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           F qc[K::NU_DK];
           q_operands(qc, sQ, ib);
           float rsc = 1.f;
-          if constexpr (DECAY == DECAY_GAMMA) rsc = sPw[16 * ib + li + 1];
+          if constexpr (GM) rsc = g16[ib] * lrow; // gamma^{16 ib + li + 1}
 #pragma unroll
           for (int t = 0; t < K::ET; ++t) {
             f32x4 x = zero4;
@@ -1277,7 +1298,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
         scores(n);
         __syncthreads(); // score tiles complete; Qt free for the next chunk
         v_operands(reinterpret_cast<const TIn *>(smem + K::v_at(n)));
-        const float gl = (DECAY == DECAY_GAMMA) ? sPw[L] : 1.f;
+        const float gl = GM ? (L == C ? g16[K::NB] : sPw[L]) : 1.f;
         const auto ors = out_rsrc(t0, L);
         static_for<0, K::NB>([&](auto IB) {
           constexpr int ib = decltype(IB)::value;
@@ -1296,7 +1317,8 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
             store_out(ors, ib, t, o);
           }
         });
-        update_operands(L, std::false_type{});
+        if (L == C) update_operands(L, std::true_type{});
+        else update_operands(L, std::false_type{});
         state_update(reinterpret_cast<const TIn *>(smem + K::k_at(n)),
                      reinterpret_cast<const float *>(smem + K::el_at(n)), gl);
       }
