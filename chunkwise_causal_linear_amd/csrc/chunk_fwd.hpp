@@ -201,6 +201,14 @@ struct Cfg {
   // block cb = 2u + s holds key index 32u + 8g + 4s + r, so that the bf16 operand built
   // from blocks 2u and 2u+1 has k = 32u + 8g + slot, the order of 16-byte LDS reads
   static constexpr bool PERM = (SHARE || SPLIT) && BF && HI_DK;
+  // score tiles by row-block pairs: consumer wave w computes every tile of row blocks w and
+  // NB-1-w (NB + 1 tiles, the same for every wave), each Qt row block and Kt column block
+  // read once (code specialised per wave)
+#ifdef FLA_FORCE_PAIRS
+  static constexpr bool PAIRS = FLA_FORCE_PAIRS && NB == 2 * NCW;
+#else
+  static constexpr bool PAIRS = SPLIT && NB == 2 * NCW;
+#endif
   // scheduling fences in the shared-score consumer: between row blocks and before the
   // next chunk's score tiles (needed to stay within the registers with two tiles a wave)
 #ifdef FLA_FORCE_FENCE
@@ -1030,6 +1038,65 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       }
     };
 
+    // Row-block-pair variant (K::PAIRS): wave W computes tiles (B, jb), jb <= B, and
+    // (A, jb), jb <= A, with A = W, B = NB - 1 - W; each Kt block is read once for both.
+    auto scores_pair = [&](int n, auto W_c) {
+      constexpr int A = decltype(W_c)::value, B = K::NB - 1 - A;
+      const TIn *sQ = reinterpret_cast<const TIn *>(smem + K::q_at(n)) + lc;
+      const TIn *sK = reinterpret_cast<const TIn *>(smem + K::k_at(n)) + lc;
+      TIn *pb = reinterpret_cast<TIn *>(smem + K::p_at(n)) + lp;
+      // row block B's fragments stay in registers; A's (at most NB / 2 tiles) are re-read
+      F qb[K::NU_DK];
+#pragma unroll
+      for (int u = 0; u < K::NU_DK; ++u) qb[u] = ld_frag_c_at<TIn, K::HI_DK>(sQ + 16 * B * K::LQ, u, g);
+      auto tile = [&](const F *qf, const F *kf, auto IB, auto JB) {
+        constexpr int ib = decltype(IB)::value, jb = decltype(JB)::value;
+        f32x4 x = zero4;
+#pragma unroll
+        for (int u = 0; u < K::NU_DK; ++u) x = mma(x, kf[u], qf[u]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (ib == jb) {
+            if constexpr (GF) x[r] *= fdiag[r];
+            else if constexpr (GM) x[r] = dl - r >= 0 ? x[r] * sPw[dl - r < 0 ? 0 : dl - r] : 0.f;
+            else x[r] = dl - r >= 0 ? x[r] : 0.f;
+          } else if constexpr (GF) {
+            // (x * a) * b: a precomputed product would be a loop invariant per (ib - jb, r)
+            x[r] = (x[r] * g16[ib - jb - 1]) * foff[r];
+          } else if constexpr (GM) {
+            x[r] *= sPw[16 * (ib - jb) + dl - r];
+          }
+        }
+        st_ptile<TIn>(pb + (ib * (ib + 1) / 2 + jb) * K::PTILE, x);
+      };
+      static_for<0, B + 1>([&](auto JB) {
+        constexpr int jb = decltype(JB)::value;
+        F kf[K::NU_DK];
+#pragma unroll
+        for (int u = 0; u < K::NU_DK; ++u) kf[u] = ld_frag_c_at<TIn, K::HI_DK>(sK + 16 * jb * K::LQ, u, g);
+        tile(qb, kf, std::integral_constant<int, B>{}, JB);
+        if constexpr (jb <= A) {
+          F qa[K::NU_DK];
+#pragma unroll
+          for (int u = 0; u < K::NU_DK; ++u) qa[u] = ld_frag_c_at<TIn, K::HI_DK>(sQ + 16 * A * K::LQ, u, g);
+          tile(qa, kf, std::integral_constant<int, A>{}, JB);
+        }
+      });
+    };
+    auto scores_any = [&](int n) {
+      if constexpr (K::PAIRS) {
+        static_assert(K::NCW == 2 || K::NCW == 4, "pairs");
+        switch (cw) {
+        case 0: scores_pair(n, std::integral_constant<int, 0>{}); break;
+        case 1: scores_pair(n, std::integral_constant<int, 1>{}); break;
+        case 2: if constexpr (K::NCW == 4) scores_pair(n, std::integral_constant<int, 2>{}); break;
+        default: if constexpr (K::NCW == 4) scores_pair(n, std::integral_constant<int, 3>{}); break;
+        }
+      } else {
+        scores(n);
+      }
+    };
+
     // V^T operand fragments of chunk m (rows e, K = tokens j; columns past dv hold zeros)
     // and the state-update operands (gamma: V' = diag(gamma^{L-1-j}) V; z: the all-ones
     // or decay column)
@@ -1270,6 +1337,9 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
         const TIn *sQ = reinterpret_cast<const TIn *>(smem + K::q_at(n));
         const TIn *pb = reinterpret_cast<const TIn *>(smem + K::p_at(n));
         __syncthreads(); // Qt, Kt, V of chunk n in place
+        // score tiles first: the inter-chunk results below then live only from there to
+        // phase 2, not through the score tiles
+        scores_any(n);
         state_operands();
         f32x4 inter[K::NB][K::ET];
         f32x4 dinter[NORM ? K::NB : 1];
@@ -1295,7 +1365,6 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
             dinter[ib] = x;
           }
         });
-        scores(n);
         __syncthreads(); // score tiles complete; Qt free for the next chunk
         v_operands(reinterpret_cast<const TIn *>(smem + K::v_at(n)));
         const float gl = GM ? (L == C ? g16[K::NB] : sPw[L]) : 1.f;
