@@ -39,8 +39,8 @@ def kernel_source_hash() -> str:
 
 def algorithmic(w) -> tuple[float, float]:
     """Bytes the method must move and MFMA FLOPs it must do for one forward pass.
-    Bytes: q, k, v, out once; the gate (fp32) once; gamma; the start state if given and the
-    end state.  FLOPs per token-head: 2 * [(C+1)/2 * (dk+dv) + 2 * dk * dv] (causal half
+    Bytes: q, k, v, out once; the gate or per-token decay (fp32) once; gamma; the start
+    state if given and the end state.  FLOPs per token-head: 2 * [(C+1)/2 * (dk+dv) + 2 * dk * dv] (causal half
     of the intra-chunk products, plus the state read-out and update)."""
     s = 2 if w.dtype == "bf16" else 4
     th = w.B * w.H * w.T
@@ -48,6 +48,8 @@ def algorithmic(w) -> tuple[float, float]:
     b = th * (2 * w.dk + 2 * w.dv) * s
     if w.decay == "gate":
         b += th * w.dk * 4
+    elif w.decay == "token":
+        b += th * 4
     elif w.decay == "gamma":
         b += w.H * 4
     state = w.B * w.H * w.dk * ncol * 4
@@ -58,7 +60,7 @@ def algorithmic(w) -> tuple[float, float]:
 
 def kernel_name(w) -> str:
     t = "__bf16" if w.dtype == "bf16" else "float"
-    d = {"none": 0, "gamma": 1, "gate": 2}[w.decay]
+    d = {"none": 0, "gamma": 1, "gate": 2, "token": 3}[w.decay]
     return f"chunk_fwd_kernel<{t}, {w.dk}, {w.chunk}, {d}, {str(w.normalize).lower()}, false>"
 
 
@@ -82,7 +84,7 @@ def cpu_baseline(w, inp, out_gpu, fin_gpu, budget_s: float):
             return None if t is None else to_numpy_input(t[sl])
 
         dec = inp["decay"]
-        dec_s = None if dec is None else (part(dec) if w.decay == "gate" else to_numpy_input(dec[hs]))
+        dec_s = None if dec is None else (part(dec) if w.decay in ("gate", "token") else to_numpy_input(dec[hs]))
         q, k, v, ini = part(inp["q"]), part(inp["k"]), part(inp["v"]), part(inp["init"])
         t0 = time.perf_counter()
         ro, rf = oracle.fwd(q, k, v, dec_s, w.decay, ini, phi_elu1=w.phi_elu1,

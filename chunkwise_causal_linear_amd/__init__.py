@@ -26,6 +26,7 @@ FLA_DECAY_GAMMA = 1 << 1
 FLA_DECAY_GATE = 1 << 2
 FLA_PHI_ELU1 = 1 << 3
 FLA_NORMALIZE = 1 << 4
+FLA_DECAY_TOKEN = 1 << 5
 
 EXPORTED = ("fla_linattn_fwd", "fla_linattn_fwd_segments", "fla_linattn_step",
             "fla_status_string", "fla_linattn_segments_for")
@@ -81,7 +82,8 @@ def _stream(stream) -> ctypes.c_void_p:
 
 def flags_for(dtype: torch.dtype, decay_kind: str, phi_elu1: bool, normalize: bool) -> int:
     f = FLA_BF16 if dtype == torch.bfloat16 else 0
-    f |= {"none": 0, "gamma": FLA_DECAY_GAMMA, "gate": FLA_DECAY_GATE}[decay_kind]
+    f |= {"none": 0, "gamma": FLA_DECAY_GAMMA, "gate": FLA_DECAY_GATE,
+          "token": FLA_DECAY_TOKEN}[decay_kind]
     if phi_elu1:
         f |= FLA_PHI_ELU1
     if normalize:
@@ -94,7 +96,7 @@ def _decay_kind(decay: Optional[torch.Tensor], decay_kind: Optional[str]) -> str
         return decay_kind
     if decay is None:
         return "none"
-    return "gamma" if decay.dim() == 1 else "gate"
+    return {1: "gamma", 3: "token"}.get(decay.dim(), "gate")
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch.Tensor] = None,
@@ -104,7 +106,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch
         normalize: bool = False, n_segments: Optional[int] = None,
         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise forward.  q, k [B,H,T,dk]; v [B,H,T,dv] (bf16 or fp32, on the GPU);
-    decay: gamma [H] or gate [B,H,T,dk] (fp32); init/final state fp32 [B,H,dk,dv(+1)].
+    decay: gamma [H], gate [B,H,T,dk] or per-token scalar [B,H,T] (fp32); init/final state
+    fp32 [B,H,dk,dv(+1)].
     Returns (out, final_state)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -138,11 +141,12 @@ def step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor,
          out: Optional[torch.Tensor] = None, phi_elu1: bool = False, normalize: bool = False,
          stream=None) -> torch.Tensor:
     """One decoding token: q, k [B,H,dk]; v [B,H,dv]; state fp32 [B,H,dk,dv(+1)] updated in
-    place; decay gamma [H] or gate [B,H,dk].  Returns out [B,H,dv]."""
+    place; decay gamma [H], gate [B,H,dk] or per-token scalar [B,H].  Returns out [B,H,dv]."""
     B, H, dk = q.shape
     dv = v.shape[-1]
     if decay_kind is None:
-        decay_kind = "none" if decay is None else ("gamma" if decay.dim() == 1 else "gate")
+        decay_kind = ("none" if decay is None
+                      else {1: "gamma", 2: "token"}.get(decay.dim(), "gate"))
     if out is None:
         out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
     flags = flags_for(q.dtype, decay_kind, phi_elu1, normalize)

@@ -51,7 +51,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-enum : int { DECAY_NONE = 0, DECAY_GAMMA = 1, DECAY_GATE = 2 };
+// DECAY_TOKEN: a per-token scalar gate alpha_t (one value per token and head), handled
+// as the per-key gate with alpha_t on every key column
+enum : int { DECAY_NONE = 0, DECAY_GAMMA = 1, DECAY_GATE = 2, DECAY_TOKEN = 3 };
 
 constexpr int kMaxThreads = 512; // consumer + 4 producer waves
 constexpr int kSlice = 64;      // value columns per workgroup (16 per consumer wave)
@@ -94,7 +96,7 @@ struct Cfg {
   static constexpr int NCW = FLA_FORCE_NCW;
 #else
   // the gate's producers are VALU-heavy: give two SIMDs to producers alone
-  static constexpr int NCW = (DECAY == DECAY_GATE && DK <= 128) ? 2 : 4;
+  static constexpr int NCW = ((DECAY == DECAY_GATE || DECAY == DECAY_TOKEN) && DK <= 128) ? 2 : 4;
 #endif
   static constexpr int ET = 4 / NCW;
   static constexpr int NT = 64 * (NCW + 4);     // + 4 producer waves
@@ -121,7 +123,10 @@ struct Cfg {
   static constexpr int RPTV = C >= 32 ? C / 32 : 1;
   static constexpr int VACTIVE = C >= 32 ? 256 : C * 8;
   // registers held per prefetched chunk (32-bit words per producer lane)
-  static constexpr int STAGE_WORDS = 2 * RPT * G * ES / 4 + (DECAY == DECAY_GATE ? RPT * G : 0) +
+  // gated kinds: the producers scan GS columns of the gate (the token gate is one column)
+  static constexpr bool GATED = DECAY == DECAY_GATE || DECAY == DECAY_TOKEN;
+  static constexpr int GS = DECAY == DECAY_TOKEN ? 1 : G;
+  static constexpr int STAGE_WORDS = 2 * RPT * G * ES / 4 + (GATED ? RPT * GS : 0) +
                                      RPTV * 8 * ES / 4;
 #ifdef FLA_FORCE_PF
   static constexpr int PF_BASE = FLA_FORCE_PF;
@@ -138,7 +143,7 @@ struct Cfg {
   static constexpr int PBUF_BYTES = (NTILES + (SLOTS * NCW > NTILES ? 1 : 0)) * PTILE * ES;
   static constexpr int PW_BYTES = DECAY == DECAY_GAMMA ? ((C + 4) / 4) * 16 : 0;
   static constexpr int QT_BYTES = C * LQ * ES; // one Qt or Kt tile
-  static constexpr int EL_BYTES = DECAY == DECAY_GATE ? DK * 4 : 0;
+  static constexpr int EL_BYTES = GATED ? DK * 4 : 0;
   // row stride of V: 40 words (8 mod 32) keeps the transposed operand loads conflict-free;
   // 36 words where the split schedule needs the room
   static constexpr int LV_W = kSlice + (BF ? 16 : 4);
@@ -169,7 +174,7 @@ struct Cfg {
   static constexpr int PF = SPLIT ? 1 : PF_BASE; // chunks the producers load ahead
   // split schedule without a gate: Qt = phi(q) is formed when the Qt tile is free, from
   // the q rows still in the staging registers (no copy held through phase 1)
-  static constexpr bool Q_LATE = SPLIT && DECAY != DECAY_GATE;
+  static constexpr bool Q_LATE = SPLIT && !GATED;
   // LDS map (bytes).  SHARE / per-wave: [STAGES] x {Qt, Kt, V, eL}, [2] x score tiles
   // (SHARE), gamma powers.  SPLIT: Qt, [2] x {Kt, V, eL}, score tiles, gamma powers.
   static constexpr int OFF_Q = 0;
@@ -465,10 +470,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
   void *b = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
   return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
 }
-// N (2, 4 or 8) consecutive 32-bit words at byte offset off; zeros past the range.
+// N (1, 2, 4 or 8) consecutive 32-bit words at byte offset off; zeros past the range.
 template <int N>
 __device__ __forceinline__ void ld_words_buf(uint32_t *w, __amdgpu_buffer_rsrc_t rs, int off) {
-  if constexpr (N == 2) {
+  if constexpr (N == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+  } else if constexpr (N == 2) {
     const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
     w[0] = x[0]; w[1] = x[1];
   } else {
@@ -558,7 +565,7 @@ struct Staged {
   using K = Cfg<TIn, DK, C, DECAY, NORM>;
   static constexpr int QW = K::G * K::ES / 4; // words per row of q or k
   uint32_t q[K::RPT][QW], k[K::RPT][QW];
-  uint32_t a[DECAY == DECAY_GATE ? K::RPT : 1][K::G];
+  uint32_t a[K::GATED ? K::RPT : 1][K::GS];
   uint32_t v[K::RPTV][2 * K::ES];             // 8 elements
 };
 
@@ -638,6 +645,13 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
         for (int r = 0; r < K::RPT; ++r)
           ld_words_buf<K::G>(s.a[r], rs, ld_on ? ((row0 + r) * DK + col0) * 4 : kDropOffset);
+      } else if constexpr (DECAY == DECAY_TOKEN) {
+        // one value per row ([B][H][T])
+        const int64_t t0 = t_begin + (int64_t)n * C;
+        const auto rs = make_rsrc(a.decay + (int64_t)bh * a.T + t0, chunk_len(n) * 4);
+#pragma unroll
+        for (int r = 0; r < K::RPT; ++r)
+          ld_words_buf<1>(s.a[r], rs, ld_on ? (row0 + r) * 4 : kDropOffset);
       }
     };
     // q/k row r and v row r of chunk n
@@ -744,41 +758,42 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       vmem_order();
       // gate: b_i = local cumulative product over this lane's rows times the product of
       // the row groups above it (inclusive shuffle scan across lanes rg*LPR + cgl)
-      float bc[DECAY == DECAY_GATE ? K::RPT : 1][K::G];
-      float rb[DECAY == DECAY_GATE ? K::RPT : 1][K::G]; // 1 / b
-      if constexpr (DECAY == DECAY_GATE) {
+      // (token gate: one column, the same for every key)
+      float bc[K::GATED ? K::RPT : 1][K::GS];
+      float rb[K::GATED ? K::RPT : 1][K::GS]; // 1 / b
+      if constexpr (K::GATED) {
         if (L < C) {
 #pragma unroll
           for (int r = 0; r < K::RPT; ++r)
 #pragma unroll
-            for (int i = 0; i < K::G; ++i)
+            for (int i = 0; i < K::GS; ++i)
               if (row0 + r >= L) s.a[r][i] = 0x3f800000u; // 1.0f: no decay past the end
         }
 #pragma unroll
         for (int r = 0; r < K::RPT; ++r) {
-          unpack<float, K::G>(bc[r], s.a[r]);
+          unpack<float, K::GS>(bc[r], s.a[r]);
           if (r > 0) {
 #pragma unroll
-            for (int c = 0; c < K::G; ++c) bc[r][c] *= bc[r - 1][c];
+            for (int c = 0; c < K::GS; ++c) bc[r][c] *= bc[r - 1][c];
           }
         }
-        float inc[K::G];
+        float inc[K::GS];
 #pragma unroll
-        for (int c = 0; c < K::G; ++c) inc[c] = bc[K::RPT - 1][c];
+        for (int c = 0; c < K::GS; ++c) inc[c] = bc[K::RPT - 1][c];
 #pragma unroll
         for (int d = 1; d < K::NRG; d *= 2) {
           const int src = (lane - d * K::LPR) < 0 ? 0 : 4 * (lane - d * K::LPR);
 #pragma unroll
-          for (int c = 0; c < K::G; ++c) {
+          for (int c = 0; c < K::GS; ++c) {
             const float o = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(inc[c])));
             inc[c] = rg >= d ? inc[c] * o : inc[c];
           }
         }
         const int src_last = 4 * ((K::NRG - 1) * K::LPR + cgl);
         const int src_prev = (lane - K::LPR) < 0 ? 0 : 4 * (lane - K::LPR);
-        float tot[K::G];
+        float tot[K::GS];
 #pragma unroll
-        for (int c = 0; c < K::G; ++c) {
+        for (int c = 0; c < K::GS; ++c) {
           tot[c] = __int_as_float(__builtin_amdgcn_ds_bpermute(src_last, __float_as_int(inc[c])));
           const float pv = __int_as_float(__builtin_amdgcn_ds_bpermute(src_prev, __float_as_int(inc[c])));
           const float ex = rg == 0 ? 1.f : pv;
@@ -791,7 +806,12 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           for (int r = K::RPT - 2; r >= 0; --r)
             rb[r][c] = rb[r + 1][c] * __uint_as_float(s.a[r + 1][c]);
         }
-        if (ld_on && rg == 0) st_lds<float, K::G>(sEL + col0, tot);
+        if (ld_on && rg == 0) {
+          float totg[K::G];
+#pragma unroll
+          for (int c = 0; c < K::G; ++c) totg[c] = tot[K::GS == 1 ? 0 : c];
+          st_lds<float, K::G>(sEL + col0, totg);
+        }
         load_gate(s, n + K::PF);
         vmem_order();
       } else if constexpr (DECAY == DECAY_GAMMA) {
@@ -821,9 +841,9 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
               kk = row < L ? kk : 0.f;
               qq = row < L ? qq : 0.f;
             }
-            if constexpr (DECAY == DECAY_GATE) {
-              qq *= bc[r][c];
-              kk *= rb[r][c];
+            if constexpr (K::GATED) {
+              qq *= bc[r][K::GS == 1 ? 0 : c];
+              kk *= rb[r][K::GS == 1 ? 0 : c];
             }
             kv[c] = kk;
             qv[c] = qq;
@@ -905,7 +925,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     if (a.seg_decay && vs == 0 && ld_on && rg == 0) {
       float *sd = a.seg_decay + ((int64_t)bh * a.nseg + seg) * DK + col0;
 #pragma unroll
-      for (int c = 0; c < K::G; ++c) sd[c] = (DECAY == DECAY_GAMMA) ? dprod[0] : dprod[c];
+      for (int c = 0; c < K::G; ++c) sd[c] = (DECAY == DECAY_GATE) ? dprod[c] : dprod[0];
     }
     return;
   }
@@ -1215,7 +1235,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           for (int t = 0; t < K::ET; ++t) Hs[t][cb] = mma(Hs[t][cb], kf, vu[t][u]);
           if constexpr (NORM) Zs[cb] = mma(Zs[cb], kf, wz[u]);
         }
-        if constexpr (DECAY == DECAY_GATE) {
+        if constexpr (K::GATED) {
           const float4 el = *reinterpret_cast<const float4 *>(sEL + lel + K::state_row(cb, 0, 0));
 #pragma unroll
           for (int t = 0; t < K::ET; ++t) {
@@ -1316,12 +1336,12 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
 
       if (nch > 0) {
         __syncthreads(); // stage 0 holds chunk 0
-        scores(0);
+        scores_any(0);
         for (int n = 1; n < nch; ++n) {
           __syncthreads(); // stage n % 3 holds chunk n; score tiles of chunk n - 1 complete
           rest(n - 1, std::true_type{}, [&] {
             if constexpr (K::FENCE & 2) __builtin_amdgcn_sched_barrier(0);
-            scores(n);
+            scores_any(n);
           });
         }
         __syncthreads();
@@ -1452,7 +1472,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           for (int t = 0; t < K::ET; ++t) Hs[t][cb] = mma(Hs[t][cb], kf, vu[t][u]);
           if constexpr (NORM) Zs[cb] = mma(Zs[cb], kf, wz[u]);
         }
-        if constexpr (DECAY == DECAY_GATE) {
+        if constexpr (K::GATED) {
           const float4 el = *reinterpret_cast<const float4 *>(sEL + 16 * cb + 4 * g);
 #pragma unroll
           for (int t = 0; t < K::ET; ++t) {

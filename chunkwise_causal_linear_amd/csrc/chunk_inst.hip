@@ -41,6 +41,7 @@ ChunkLauncher pick_dn(int decay, bool norm) {
   case DECAY_NONE: return norm ? pick<C, DECAY_NONE, true>() : pick<C, DECAY_NONE, false>();
   case DECAY_GAMMA: return norm ? pick<C, DECAY_GAMMA, true>() : pick<C, DECAY_GAMMA, false>();
   case DECAY_GATE: return norm ? pick<C, DECAY_GATE, true>() : pick<C, DECAY_GATE, false>();
+  case DECAY_TOKEN: return norm ? pick<C, DECAY_TOKEN, true>() : pick<C, DECAY_TOKEN, false>();
   default: return nullptr;
   }
 }

@@ -43,15 +43,19 @@ ChunkLauncher find_launcher(bool bf16, int64_t dk, int64_t chunk, int decay, boo
 int decay_kind(uint32_t flags) {
   if (flags & FLA_DECAY_GAMMA) return DECAY_GAMMA;
   if (flags & FLA_DECAY_GATE) return DECAY_GATE;
+  if (flags & FLA_DECAY_TOKEN) return DECAY_TOKEN;
   return DECAY_NONE;
 }
+
+constexpr uint32_t kDecayBits = FLA_DECAY_GAMMA | FLA_DECAY_GATE | FLA_DECAY_TOKEN;
 
 // Shape and flag checks shared by the forward and step calls.
 int check_common(int64_t B, int64_t H, int64_t dk, int64_t dv, uint32_t flags,
                  const float *gate_or_gamma) {
   if (flags & ~FLA_ALL_FLAGS) return FLA_ERR_INVALID_ARG;
-  if ((flags & FLA_DECAY_GAMMA) && (flags & FLA_DECAY_GATE)) return FLA_ERR_INVALID_ARG;
-  const bool has_decay = (flags & (FLA_DECAY_GAMMA | FLA_DECAY_GATE)) != 0;
+  const uint32_t dbits = flags & kDecayBits;
+  if (dbits & (dbits - 1)) return FLA_ERR_INVALID_ARG; // at most one decay kind
+  const bool has_decay = dbits != 0;
   if (has_decay != (gate_or_gamma != nullptr)) return FLA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || B > (1 << 24) || H > (1 << 24)) return FLA_ERR_INVALID_ARG;
   if (dk < 1 || dv < 1) return FLA_ERR_INVALID_ARG;
@@ -131,7 +135,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(const TIn *q, const 
     }
     sq[c] = qv;
     sk[c] = kv;
-    sg[c] = kind == DECAY_GAMMA ? decay[h] : (kind == DECAY_GATE ? decay[(int64_t)bh * dk + c] : 1.f);
+    sg[c] = kind == DECAY_GAMMA   ? decay[h]
+            : kind == DECAY_GATE  ? decay[(int64_t)bh * dk + c]
+            : kind == DECAY_TOKEN ? decay[bh]
+                                  : 1.f;
   }
   __syncthreads();
   if (norm) {
@@ -327,7 +334,7 @@ int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
 int fla_linattn_segments_for(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                              int64_t chunk, uint32_t flags, int64_t *n_segments) {
   if (!n_segments || T < 0) return FLA_ERR_INVALID_ARG;
-  const bool has_decay = (flags & (FLA_DECAY_GAMMA | FLA_DECAY_GATE)) != 0;
+  const bool has_decay = (flags & fla::kDecayBits) != 0;
   static const float dummy[4] = {0.f, 0.f, 0.f, 0.f};
   int rc = fla::check_common(B, H, dk, dv, flags, has_decay ? dummy : nullptr);
   if (rc != FLA_OK) return rc;

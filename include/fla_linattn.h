@@ -12,15 +12,17 @@
  * "linear attention" (recurrence, normaliser, elu+1 feature map, parallel = recurrent),
  * and the Flash Linear Attention posts (RetNet retention with a per-head decay gamma,
  * GLA with a per-token per-key gate alpha_t, "chunk" mode forward).  G_t is 1 (plain
- * linear attention), gamma_h (FLA_DECAY_GAMMA) or alpha_t (FLA_DECAY_GATE); the gate
- * multiplies key column c of S for every value row, the old state is decayed before
- * the current token is added, and z decays with the same G_t.
+ * linear attention), gamma_h (FLA_DECAY_GAMMA), alpha_t (FLA_DECAY_GATE) or a per-token
+ * scalar a_t (FLA_DECAY_TOKEN: one decay per token and head, the data-dependent form of
+ * the retention decay); the gate multiplies key column c of S for every value row, the
+ * old state is decayed before the current token is added, and z decays with the same G_t.
  *
  * Layouts (all row-major, contiguous, device memory of the current HIP device):
  *   q, k    [B][H][T][dk]   bf16 (FLA_BF16) or fp32
  *   v, out  [B][H][T][dv]   same dtype as q
  *   gamma   [H]             fp32, values in [0, 1]
  *   gate    [B][H][T][dk]   fp32, values in (0, 1]
+ *   token   [B][H][T]       fp32, values in (0, 1] (per-token scalar decay)
  *   state   [B][H][dk][dv + n] fp32, n = 1 with FLA_NORMALIZE (column dv holds z);
  *           this is h = S^T, so state[b][h][c][e] = S[e][c].
  *
@@ -53,14 +55,17 @@ enum fla_status {
 #define FLA_DECAY_GATE (1u << 2)  /* gate_or_gamma = const float[B][H][T][dk] */
 #define FLA_PHI_ELU1 (1u << 3)    /* phi(x) = elu(x) + 1 on q and k; otherwise identity */
 #define FLA_NORMALIZE (1u << 4)   /* divide by z_t^T phi(q_t); the state carries z */
-#define FLA_ALL_FLAGS (FLA_BF16 | FLA_DECAY_GAMMA | FLA_DECAY_GATE | FLA_PHI_ELU1 | FLA_NORMALIZE)
+#define FLA_DECAY_TOKEN (1u << 5) /* gate_or_gamma = const float[B][H][T] (scalar per token) */
+#define FLA_ALL_FLAGS \
+  (FLA_BF16 | FLA_DECAY_GAMMA | FLA_DECAY_GATE | FLA_PHI_ELU1 | FLA_NORMALIZE | FLA_DECAY_TOKEN)
 
 /*
  * fla_linattn_fwd — chunkwise forward pass over T tokens.
  *
  *   q, k, v, out : see layouts above; 16-byte aligned.  May be NULL only when T == 0.
  *   gate_or_gamma: gamma [H] with FLA_DECAY_GAMMA (4-byte aligned), gate [B][H][T][dk]
- *                  with FLA_DECAY_GATE (16-byte aligned), NULL with neither bit.
+ *                  with FLA_DECAY_GATE (16-byte aligned), token [B][H][T] with
+ *                  FLA_DECAY_TOKEN (4-byte aligned), NULL with no decay bit.
  *   init_state   : [B][H][dk][dv+n] fp32, or NULL for a zero initial state (16-byte aligned).
  *   final_state  : [B][H][dk][dv+n] fp32 written with the state after token T-1, or NULL.
  *                  May alias init_state (in-place resume).
@@ -72,8 +77,9 @@ enum fla_status {
  * The chunk size changes the rounding, never the mathematical result.  Combinations
  * whose on-chip tiles do not fit the 160 KiB LDS of a gfx950 CU (large dk with large
  * chunk, mostly in fp32) return FLA_ERR_UNSUPPORTED.
- * Gate range: each chunk's product of alpha along the chunk must stay above ~1e-30
- * (per-key log-decay > -69 per chunk) or the fp32 factorisation overflows.
+ * Gate range (FLA_DECAY_GATE and FLA_DECAY_TOKEN): each chunk's product of the decays
+ * along the chunk must stay above ~1e-30 (log-decay > -69 per chunk) or the fp32
+ * factorisation overflows.
  */
 int fla_linattn_fwd(const void *q, const void *k, const void *v, const float *gate_or_gamma,
                     const float *init_state, void *out, float *final_state, int64_t B,
@@ -100,7 +106,7 @@ int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
  * fla_linattn_step — one token of recurrent decoding (the T == 1 case of the forward
  * pass), updating the state in place.
  *   q, k : [B][H][dk]; v, out: [B][H][dv] (bf16 with FLA_BF16, else fp32); 16-byte aligned.
- *   gate_or_gamma: gamma [H] or gate [B][H][dk] per the decay bit, else NULL.
+ *   gate_or_gamma: gamma [H], gate [B][H][dk] or token [B][H] per the decay bit, else NULL.
  *   state: fp32 [B][H][dk][dv+n], read and written (required).
  *   dk, dv in {16, 32, 64, 128, 256}.
  */

@@ -63,6 +63,9 @@ def fwd_raw(lib, *, q=BOGUS, k=BOGUS, v=BOGUS, gate=None, init=None, out=BOGUS, 
 @pytest.mark.parametrize("kw,expected", [
     (dict(flags=1 << 7), fla.FLA_ERR_INVALID_ARG),                       # unknown flag bit
     (dict(flags=fla.FLA_DECAY_GAMMA | fla.FLA_DECAY_GATE, gate=BOGUS), fla.FLA_ERR_INVALID_ARG),
+    (dict(flags=fla.FLA_DECAY_TOKEN | fla.FLA_DECAY_GATE, gate=BOGUS), fla.FLA_ERR_INVALID_ARG),
+    (dict(flags=fla.FLA_DECAY_TOKEN | fla.FLA_DECAY_GAMMA, gate=BOGUS), fla.FLA_ERR_INVALID_ARG),
+    (dict(flags=fla.FLA_DECAY_TOKEN), fla.FLA_ERR_INVALID_ARG),          # token bit, no values
     (dict(flags=fla.FLA_DECAY_GAMMA), fla.FLA_ERR_INVALID_ARG),          # decay bit, no values
     (dict(gate=BOGUS), fla.FLA_ERR_INVALID_ARG),                          # values, no decay bit
     (dict(q=None), fla.FLA_ERR_INVALID_ARG),
@@ -96,6 +99,8 @@ def test_segments_override_rejects_negative(lib):
     (dict(dk=24), fla.FLA_ERR_UNSUPPORTED),
     (dict(q=MISALIGNED), fla.FLA_ERR_INVALID_ARG),
     (dict(flags=fla.FLA_DECAY_GATE), fla.FLA_ERR_INVALID_ARG),
+    (dict(flags=fla.FLA_DECAY_TOKEN), fla.FLA_ERR_INVALID_ARG),
+    (dict(flags=fla.FLA_DECAY_TOKEN | fla.FLA_DECAY_GATE, gate=BOGUS), fla.FLA_ERR_INVALID_ARG),
 ])
 def test_step_rejects_on_host(lib, kw, expected):
     a = dict(q=BOGUS, k=BOGUS, v=BOGUS, gate=None, state=BOGUS, out=BOGUS, B=1, H=1, dk=64,

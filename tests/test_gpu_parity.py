@@ -70,7 +70,7 @@ def check(w, inp, tag, **kw):
 
 # ---------------------------------------------------------------------------------------
 # flag combinations at one shape (several chunks and a ragged tail)
-FLAG_COMBOS = list(itertools.product(["f32", "bf16"], ["none", "gamma", "gate"],
+FLAG_COMBOS = list(itertools.product(["f32", "bf16"], ["none", "gamma", "gate", "token"],
                                      [False, True], [False, True]))
 
 
@@ -137,7 +137,7 @@ def test_shape_sweep(dtype, dk, dv, chunk, T, decay, norm, init):
 SCHEDULE_SHAPES = [("bf16", 128, 128), ("bf16", 256, 64), ("f32", 128, 64), ("bf16", 64, 128),
                    ("bf16", 128, 64), ("f32", 32, 64)]
 SCHEDULE_CASES = [(dt, dk, c, dec, norm) for (dt, dk, c) in SCHEDULE_SHAPES
-                  for dec in ("none", "gamma", "gate") for norm in (False, True)]
+                  for dec in ("none", "gamma", "gate", "token") for norm in (False, True)]
 
 
 @pytest.mark.parametrize("dtype,dk,chunk,decay,norm", SCHEDULE_CASES)
@@ -158,12 +158,13 @@ def test_unsupported_combination_raises():
 
 # ---------------------------------------------------------------------------------------
 # schedules: segment path against the oracle and against the streaming path
-@pytest.mark.parametrize("decay", ["none", "gamma", "gate"])
+@pytest.mark.parametrize("decay", ["none", "gamma", "gate", "token"])
 @pytest.mark.parametrize("nseg", [2, 3, 7])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_segment_schedule(decay, nseg, dtype):
     w, inp = small_case(dtype, decay, 64, 128, 16 * 32 + 9, B=1, H=2, chunk=32,
-                        phi=True, norm=(decay == "gate"), init=True, seed=100 + nseg)
+                        phi=True, norm=(decay in ("gate", "token")), init=True,
+                        seed=100 + nseg)
     check(w, inp, f"segments={nseg} {dtype} {decay}", n_segments=nseg)
     o1, f1 = run_gpu(w, inp, n_segments=1)
     o2, f2 = run_gpu(w, inp, n_segments=nseg)
@@ -225,7 +226,8 @@ def test_split_resume_matches_one_pass():
 
 
 @pytest.mark.parametrize("dtype,decay,norm", [("f32", "gate", True), ("bf16", "gamma", False),
-                                              ("f32", "none", True), ("bf16", "gate", False)])
+                                              ("f32", "none", True), ("bf16", "gate", False),
+                                              ("f32", "token", True), ("bf16", "token", False)])
 def test_step_chain_matches_oracle(dtype, decay, norm):
     w, inp = small_case(dtype, decay, 64, 32, 20, B=2, H=3, phi=norm, norm=norm, init=True,
                         seed=12)
@@ -236,6 +238,7 @@ def test_step_chain_matches_oracle(dtype, decay, norm):
     outs = []
     for t in range(w.T):
         d = None if dec is None else (dec if decay == "gamma" else dec[:, :, t].contiguous())
+        # token: [B,H] per step; gate: [B,H,dk]
         outs.append(fla.step(q[:, :, t].contiguous(), k[:, :, t].contiguous(),
                              v[:, :, t].contiguous(), state, d, decay_kind=decay,
                              phi_elu1=norm, normalize=norm))
@@ -244,6 +247,21 @@ def test_step_chain_matches_oracle(dtype, decay, norm):
     ro, rf = run_oracle(w, inp)
     assert rel_err(o, ro) <= TOL[dtype]
     assert rel_err(to_host(state), rf) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,dk,chunk", [("bf16", 128, 64), ("f32", 64, 32), ("bf16", 32, 16)])
+def test_token_decay_equals_broadcast_gate(dtype, dk, chunk):
+    """A per-token scalar decay is the per-key gate with every key column equal: both
+    library paths against each other, and against the oracle."""
+    w, inp = small_case(dtype, "token", dk, 64, 3 * chunk + 11, B=2, H=2, chunk=chunk,
+                        init=True, seed=40 + dk)
+    check(w, inp, f"token {dtype} dk={dk} C={chunk}")
+    ot, ft = run_gpu(w, inp)
+    wg = w.with_(decay="gate")
+    ig = dict(inp, decay=np.ascontiguousarray(
+        np.broadcast_to(inp["decay"][..., None], inp["decay"].shape + (dk,))))
+    og, fg = run_gpu(wg, ig)
+    assert rel_err(ot, og) <= TOL[dtype] and rel_err(ft, fg) <= TOL[dtype]
 
 
 def test_single_hip_runtime_in_process():

@@ -1,4 +1,4 @@
-"""Full-size parity on the five named workloads, in the launch configuration the benchmark
+"""Full-size parity on the named workloads, in the launch configuration the benchmark
 times (one fla_linattn_fwd call with the library's automatic schedule).
 
 The oracle runs every head of every workload; the million-token workload records a

@@ -28,7 +28,7 @@ from typing import Optional
 
 import numpy as np
 
-DECAY_NONE, DECAY_GAMMA, DECAY_GATE = "none", "gamma", "gate"
+DECAY_NONE, DECAY_GAMMA, DECAY_GATE, DECAY_TOKEN = "none", "gamma", "gate", "token"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -41,7 +41,7 @@ class Workload:
     dv: int
     chunk: int
     dtype: str          # "f32" or "bf16" (q, k, v and out)
-    decay: str          # DECAY_NONE | DECAY_GAMMA | DECAY_GATE
+    decay: str          # DECAY_NONE | DECAY_GAMMA | DECAY_GATE | DECAY_TOKEN
     phi_elu1: bool      # feature map elu(x)+1 on q and k, else identity
     normalize: bool     # o = S phi(q) / (z^T phi(q))
     qk_scale: float     # q, k ~ N(0,1) * qk_scale
@@ -74,6 +74,9 @@ WORKLOADS = {
                              gamma_exp="1-2^(-5-h*8/H)", seed=1003),
     "gla_d128": Workload("gla_d128", 8, 16, 16384, 128, 128, 64, "bf16", DECAY_GATE,
                          False, False, 1.0 / math.sqrt(128), 0.0, seed=1004),
+    "token_decay_d128": Workload("token_decay_d128", 8, 16, 16384, 128, 128, 64, "bf16",
+                                 DECAY_TOKEN, False, False, 1.0 / math.sqrt(128), 0.0,
+                                 seed=1006),
     "long_retention": Workload("long_retention", 1, 8, 1 << 20, 128, 128, 128, "bf16",
                                DECAY_GAMMA, False, False, 1.0 / math.sqrt(128), 0.1,
                                gamma_exp="1-2^(-5-h)", seed=1005),
@@ -132,12 +135,14 @@ def _normal_tensor(w: Workload, stream: int, d: int, scale: float, as_bf16: bool
     return out
 
 
-def _gate_tensor(w: Workload, stream: int) -> np.ndarray:
-    """alpha = sigmoid(x)^(1/16), x ~ N(0,1); evaluated in fp64, rounded once to fp32."""
-    out = np.empty((w.B, w.H, w.T, w.dk), dtype=np.float32)
+def _gate_tensor(w: Workload, stream: int, per_key: bool = True) -> np.ndarray:
+    """alpha = sigmoid(x)^(1/16), x ~ N(0,1); evaluated in fp64, rounded once to fp32.
+    Shape [B,H,T,dk] (per-key gate) or [B,H,T] (per-token scalar decay)."""
+    tail = (w.dk,) if per_key else ()
+    out = np.empty((w.B, w.H, w.T) + tail, dtype=np.float32)
 
     def fill(g, b, h):
-        x = g.standard_normal((w.T, w.dk), dtype=np.float64)
+        x = g.standard_normal((w.T,) + tail, dtype=np.float64)
         out[b, h] = np.power(1.0 / (1.0 + np.exp(-x)), 1.0 / 16.0).astype(np.float32)
 
     _per_head(w, stream, fill)
@@ -148,16 +153,16 @@ def generate(w: Workload) -> dict:
     """Draw the inputs of workload ``w``.
 
     Returns numpy arrays in the library's layouts: q, k [B,H,T,dk]; v [B,H,T,dv]
-    (uint16 bf16 bits or float32); 'decay' = gamma [H] fp32, gate [B,H,T,dk] fp32 or
-    None; 'init' = fp32 [B,H,dk,dv+n] or None (n = 1 with the normaliser).
+    (uint16 bf16 bits or float32); 'decay' = gamma [H] fp32, gate [B,H,T,dk] fp32,
+    per-token decay [B,H,T] fp32 or None; 'init' = fp32 [B,H,dk,dv+n] or None (n = 1 with the normaliser).
     Draw order: q, k, v, then the gate or the initial state.
     """
     bf = w.dtype == "bf16"
     q = _normal_tensor(w, 1, w.dk, w.qk_scale, bf)
     k = _normal_tensor(w, 2, w.dk, w.qk_scale, bf)
     v = _normal_tensor(w, 3, w.dv, 1.0, bf)
-    if w.decay == DECAY_GATE:
-        decay = _gate_tensor(w, 4)
+    if w.decay in (DECAY_GATE, DECAY_TOKEN):
+        decay = _gate_tensor(w, 4, per_key=w.decay == DECAY_GATE)
     else:
         decay = gamma_for(w)
     init = None
@@ -202,10 +207,11 @@ def generate_torch(w: Workload, device="cuda"):
     k = normal((w.B, w.H, w.T, w.dk), w.qk_scale)
     v = normal((w.B, w.H, w.T, w.dv), 1.0)
     decay = None
-    if w.decay == DECAY_GATE:
-        decay = torch.empty((w.B, w.H, w.T, w.dk), device=device, dtype=torch.float32)
+    if w.decay in (DECAY_GATE, DECAY_TOKEN):
+        tail = (w.dk,) if w.decay == DECAY_GATE else ()
+        decay = torch.empty((w.B, w.H, w.T) + tail, device=device, dtype=torch.float32)
         for b in range(w.B):  # fp64 per batch row keeps the temporary small
-            x = torch.randn((w.H, w.T, w.dk), generator=gen, device=device, dtype=torch.float64)
+            x = torch.randn((w.H, w.T) + tail, generator=gen, device=device, dtype=torch.float64)
             decay[b] = torch.sigmoid(x).pow(1.0 / 16.0).to(torch.float32)
     elif w.decay == DECAY_GAMMA:
         decay = torch.from_numpy(gamma_for(w)).to(device)
