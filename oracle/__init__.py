@@ -8,6 +8,9 @@ restatements used to pin it (brute-force masked attention and the parallel form)
 Pins (see tests/test_oracle_pins.py): brute force on tiny inputs, the parallel form,
 gamma = 1 reducing to plain (Katharopoulos) linear attention, closed forms, a hand-worked
 fixture under tests/golden/, split/resume, chained single steps and linearity.
+The backward (``bwd``, back-propagation through the same recurrence in C) is pinned in
+tests/test_oracle_bwd_pins.py by central finite differences of the pinned forward and by
+the closed-form matrix gradients of plain causal linear attention.
 """
 from __future__ import annotations
 
@@ -51,6 +54,9 @@ def _load():
         lib.oracle_step.argtypes = [p, p, p, c_int, p, c_int, p, p, i64, i64, i64, i64,
                                     c_int, c_int]
         lib.oracle_step.restype = c_int
+        lib.oracle_bwd.argtypes = [p, p, p, c_int, p, c_int, p, p, p, p, p, p, p, p,
+                                   i64, i64, i64, i64, i64, c_int, c_int]
+        lib.oracle_bwd.restype = c_int
         _lib = lib
     return _lib
 
@@ -135,3 +141,53 @@ def step(q, k, v, state, decay=None, decay_kind="none", *, phi_elu1=False, norma
     if rc != 0:
         raise RuntimeError("oracle_step failed")
     return out
+
+
+def bwd(q, k, v, dout, decay=None, decay_kind="none", init=None, dfinal=None, *,
+        phi_elu1=False, want_dgate=True, nthreads=0):
+    """Gradients of L = sum(dout * o) + sum(dfinal * h_T) (no normaliser) by back-
+    propagation through the recurrence.  q, k, v, dout as in ``fwd`` (dout shares q's
+    dtype); init, dfinal: [B,H,dk,dv] or None.
+
+    Returns a dict of fp64 arrays: dq, dk [B,H,T,dk]; dv [B,H,T,dv]; dgate shaped like the
+    decay (None without one, or when want_dgate is false); dinit [B,H,dk,dv].
+    """
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dout = np.ascontiguousarray(dout)
+    dt = _dtype_code(q)
+    if any(_dtype_code(x) != dt for x in (k, v, dout)):
+        raise TypeError("q, k, v, dout must share one dtype")
+    B, H, T, dk = q.shape
+    dv = v.shape[3]
+    if k.shape != q.shape or v.shape[:3] != (B, H, T) or dout.shape != v.shape:
+        raise ValueError("shape mismatch")
+    kind = DECAY_CODES[decay_kind]
+    dec = None if decay is None else np.ascontiguousarray(decay, dtype=np.float32)
+    if kind and dec is None:
+        raise ValueError("decay values missing")
+
+    def state(x):
+        if x is None:
+            return None
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        if x.shape != (B, H, dk, dv):
+            raise ValueError(f"state must be {(B, H, dk, dv)}")
+        return x
+
+    ini, dfin = state(init), state(dfinal)
+    dq = np.empty((B, H, T, dk))
+    dkk = np.empty((B, H, T, dk))
+    dvv = np.empty((B, H, T, dv))
+    dg = None
+    if kind and want_dgate:
+        dg = np.empty(dec.shape, dtype=np.float64)
+    dini = np.empty((B, H, dk, dv))
+    rc = _load().oracle_bwd(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(dec), kind, _ptr(ini),
+                            _ptr(dout), _ptr(dfin), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg),
+                            _ptr(dini), B, H, T, dk, dv, PHI_ELU1 if phi_elu1 else 0,
+                            int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_bwd failed")
+    return {"dq": dq, "dk": dkk, "dv": dvv, "dgate": dg, "dinit": dini}

@@ -188,3 +188,171 @@ int oracle_step(const void *q, const void *k, const void *v, int dtype, const fl
   return oracle_fwd(q, k, v, dtype, decay, decay_kind, state, out, NULL, 1, state, B, H, 1,
                     dk, dv, flags, nthreads);
 }
+
+/*
+ * oracle_bwd: reverse-mode derivative of oracle_fwd (without the normaliser), by back-
+ * propagation through time over the same recurrence, one head at a time.
+ *
+ * The loss is L = sum_t dout_t . o_t + sum dfinal (.) h_T with h_t = S_t^T [dk][dv] and
+ * o_t = h_t^T phi(q_t).  Chain rule on h_t = diag(g_t) h_{t-1} + phi(k_t) v_t^T:
+ *   dh_t   = phi(q_t) dout_t^T + diag(g_{t+1}) dh_{t+1}     (dh_{T-1} starts from dfinal)
+ *   dphi(q_t) = h_t dout_t,  dphi(k_t) = dh_t v_t,  dv_t = dh_t^T phi(k_t),
+ *   dg_t[c] = sum_e dh_t[c][e] h_{t-1}[c][e]  (h_{-1} = init),  dinit = diag(g_0) dh_0,
+ * and dq = dphi(q) phi'(q), dk = dphi(k) phi'(k) with phi'(x) = 1 (identity) or
+ * (x > 0 ? 1 : e^x) (elu + 1).  A per-token decay gathers dg over c; gamma over t, c and
+ * the batch.
+ *
+ * The forward states h_t of one head are kept (T * dk * dv doubles), split into blocks
+ * of 16 value columns that run in parallel; the sums over value columns (dq, dk, dg) are
+ * taken block by block in a fixed order, so results do not depend on the thread count.
+ *   dout: like v; dfinal, init: fp64 [B][H][dk][dv] or NULL.
+ *   dq, dk: fp64 [B][H][T][dk]; dv: fp64 [B][H][T][dv]; dgate: fp64, shaped like the
+ *   decay (gamma [H], gate [B][H][T][dk], token [B][H][T]) or NULL; dinit fp64
+ *   [B][H][dk][dv] or NULL.  Returns 0, or -1 on bad arguments or memory.
+ */
+int oracle_bwd(const void *q, const void *k, const void *v, int dtype, const float *decay,
+               int decay_kind, const double *init, const void *dout, const double *dfinal,
+               double *dq, double *dk_out, double *dv_out, double *dgate, double *dinit,
+               int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int flags,
+               int nthreads) {
+  if (!q || !k || !v || !dout || !dq || !dk_out || !dv_out) return -1;
+  if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1) return -1;
+  if (decay_kind != OR_DECAY_NONE && !decay) return -1;
+  if (flags & OR_NORMALIZE) return -1;
+  const int elu1 = (flags & OR_PHI_ELU1) != 0;
+  const int64_t nblk = (dv + EBLK - 1) / EBLK;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  if (dgate && decay_kind == OR_DECAY_GAMMA)
+    for (int64_t h = 0; h < H; ++h) dgate[h] = 0.0;
+  /* per-head scratch: states per block [nblk][T][dk][EBLK], block partial sums */
+  const size_t hs_n = (size_t)nblk * (size_t)T * (size_t)dk * EBLK;
+  const size_t part_n = (size_t)nblk * (size_t)T * (size_t)dk;
+  double *hs = (double *)malloc(sizeof(double) * (hs_n ? hs_n : 1));
+  double *pq = (double *)malloc(sizeof(double) * (part_n ? part_n : 1));
+  double *pk = (double *)malloc(sizeof(double) * (part_n ? part_n : 1));
+  double *pg = (double *)malloc(sizeof(double) * (part_n ? part_n : 1));
+  double *gall = (double *)malloc(sizeof(double) * (size_t)(T * dk > 0 ? T * dk : 1));
+  if (!hs || !pq || !pk || !pg || !gall) {
+    free(hs); free(pq); free(pk); free(pg); free(gall);
+    return -1;
+  }
+  int bad = 0;
+  for (int64_t bh = 0; bh < B * H && !bad; ++bh) {
+    const int64_t b = bh / H, h = bh % H;
+    for (int64_t t = 0; t < T; ++t)
+      for (int64_t c = 0; c < dk; ++c)
+        gall[t * dk + c] = gate_of(decay, decay_kind, b, h, t, c, H, T, dk);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t eb = 0; eb < nblk; ++eb) {
+      const int64_t e0 = eb * EBLK, ne = (dv - e0) < EBLK ? (dv - e0) : EBLK;
+      double *hb = hs + (size_t)eb * (size_t)T * (size_t)dk * EBLK; /* [T][dk][EBLK] */
+      double *S = (double *)malloc(sizeof(double) * (size_t)(dk * EBLK)); /* h[c][e] */
+      double *dS = (double *)malloc(sizeof(double) * (size_t)(dk * EBLK));
+      double *qb = (double *)malloc(sizeof(double) * (size_t)dk);
+      double *kb = (double *)malloc(sizeof(double) * (size_t)dk);
+      if (!S || !dS || !qb || !kb) {
+#pragma omp atomic write
+        bad = 1;
+        free(S); free(dS); free(qb); free(kb);
+        continue;
+      }
+      const double *h0 = init ? init + bh * dk * dv : NULL;
+      for (int64_t c = 0; c < dk; ++c)
+        for (int64_t e = 0; e < EBLK; ++e)
+          S[c * EBLK + e] = (h0 && e < ne) ? h0[c * dv + e0 + e] : 0.0;
+      /* forward: h_t for every t, and the block's share of dphi(q_t) = h_t dout_t */
+      for (int64_t t = 0; t < T; ++t) {
+        const int64_t qk_off = (bh * T + t) * dk, v_off = (bh * T + t) * dv;
+        for (int64_t c = 0; c < dk; ++c) kb[c] = phi(widen(k, dtype, qk_off + c), elu1);
+        for (int64_t c = 0; c < dk; ++c) {
+          const double gc = gall[t * dk + c];
+          double *Sc = S + c * EBLK;
+          for (int64_t e = 0; e < ne; ++e)
+            Sc[e] = gc * Sc[e] + kb[c] * widen(v, dtype, v_off + e0 + e);
+        }
+        memcpy(hb + (size_t)t * dk * EBLK, S, sizeof(double) * (size_t)(dk * EBLK));
+        double *pqt = pq + ((size_t)eb * T + t) * dk;
+        for (int64_t c = 0; c < dk; ++c) {
+          double s = 0.0;
+          for (int64_t e = 0; e < ne; ++e) s += S[c * EBLK + e] * widen(dout, dtype, v_off + e0 + e);
+          pqt[c] = s;
+        }
+      }
+      /* reverse: dh_t, then dphi(k_t), dv_t, dg_t from it */
+      const double *dF = dfinal ? dfinal + bh * dk * dv : NULL;
+      for (int64_t c = 0; c < dk; ++c)
+        for (int64_t e = 0; e < EBLK; ++e)
+          dS[c * EBLK + e] = (dF && e < ne) ? dF[c * dv + e0 + e] : 0.0;
+      for (int64_t t = T - 1; t >= 0; --t) {
+        const int64_t qk_off = (bh * T + t) * dk, v_off = (bh * T + t) * dv;
+        for (int64_t c = 0; c < dk; ++c) {
+          qb[c] = phi(widen(q, dtype, qk_off + c), elu1);
+          kb[c] = phi(widen(k, dtype, qk_off + c), elu1);
+        }
+        for (int64_t c = 0; c < dk; ++c)
+          for (int64_t e = 0; e < ne; ++e)
+            dS[c * EBLK + e] += qb[c] * widen(dout, dtype, v_off + e0 + e);
+        double *pkt = pk + ((size_t)eb * T + t) * dk;
+        double *pgt = pg + ((size_t)eb * T + t) * dk;
+        const double *hprev = t > 0 ? hb + (size_t)(t - 1) * dk * EBLK : NULL;
+        for (int64_t c = 0; c < dk; ++c) {
+          double sk = 0.0, sg = 0.0;
+          for (int64_t e = 0; e < ne; ++e) {
+            const double d = dS[c * EBLK + e];
+            sk += d * widen(v, dtype, v_off + e0 + e);
+            sg += d * (hprev ? hprev[c * EBLK + e] : (h0 ? h0[c * dv + e0 + e] : 0.0));
+          }
+          pkt[c] = sk;
+          pgt[c] = sg;
+        }
+        for (int64_t e = 0; e < ne; ++e) {
+          double s = 0.0;
+          for (int64_t c = 0; c < dk; ++c) s += dS[c * EBLK + e] * kb[c];
+          dv_out[v_off + e0 + e] = s;
+        }
+        for (int64_t c = 0; c < dk; ++c) {
+          const double gc = gall[t * dk + c];
+          for (int64_t e = 0; e < ne; ++e) dS[c * EBLK + e] *= gc;
+        }
+      }
+      if (dinit) {
+        double *di = dinit + bh * dk * dv;
+        for (int64_t c = 0; c < dk; ++c)
+          for (int64_t e = 0; e < ne; ++e) di[c * dv + e0 + e] = dS[c * EBLK + e];
+      }
+      free(S); free(dS); free(qb); free(kb);
+    }
+    if (bad) break;
+    /* gather the blocks in order; chain rule through phi */
+    for (int64_t t = 0; t < T; ++t) {
+      const int64_t qk_off = (bh * T + t) * dk;
+      double gtok = 0.0;
+      for (int64_t c = 0; c < dk; ++c) {
+        double sq = 0.0, sk = 0.0, sg = 0.0;
+        for (int64_t eb = 0; eb < nblk; ++eb) {
+          const size_t i = ((size_t)eb * T + t) * dk + c;
+          sq += pq[i];
+          sk += pk[i];
+          sg += pg[i];
+        }
+        const double xq = widen(q, dtype, qk_off + c), xk = widen(k, dtype, qk_off + c);
+        const double fq = elu1 ? (xq > 0.0 ? 1.0 : exp(xq)) : 1.0;
+        const double fk = elu1 ? (xk > 0.0 ? 1.0 : exp(xk)) : 1.0;
+        dq[qk_off + c] = sq * fq;
+        dk_out[qk_off + c] = sk * fk;
+        if (dgate) {
+          if (decay_kind == OR_DECAY_GATE) dgate[qk_off + c] = sg;
+          else gtok += sg;
+        }
+      }
+      if (dgate && decay_kind == OR_DECAY_TOKEN) dgate[bh * T + t] = gtok;
+      if (dgate && decay_kind == OR_DECAY_GAMMA) dgate[h] += gtok;
+    }
+  }
+  free(hs); free(pq); free(pk); free(pg); free(gall);
+  return bad ? -1 : 0;
+}
