@@ -29,7 +29,7 @@ FLA_NORMALIZE = 1 << 4
 FLA_DECAY_TOKEN = 1 << 5
 
 EXPORTED = ("fla_linattn_fwd", "fla_linattn_fwd_segments", "fla_linattn_step",
-            "fla_status_string", "fla_linattn_segments_for")
+            "fla_status_string", "fla_linattn_segments_for", "fla_linattn_bwd")
 
 _lib = None
 
@@ -62,6 +62,9 @@ def load_library():
     lib.fla_linattn_segments_for.argtypes = [i64, i64, i64, i64, i64, i64, u32,
                                              ctypes.POINTER(i64)]
     lib.fla_linattn_segments_for.restype = c_int
+    lib.fla_linattn_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64,
+                                    i64, u32, p]
+    lib.fla_linattn_bwd.restype = c_int
     _lib = lib
     return lib
 
@@ -163,3 +166,35 @@ def segments_for(B, H, T, dk, dv, chunk, flags) -> int:
     if rc != FLA_OK:
         raise FlaError("fla_linattn_segments_for", rc)
     return int(n.value)
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+        decay: Optional[torch.Tensor] = None, *, decay_kind: Optional[str] = None,
+        init_state: Optional[torch.Tensor] = None, dfinal: Optional[torch.Tensor] = None,
+        want_dgate: bool = True, want_dinit: bool = True, chunk: int = 64,
+        phi_elu1: bool = False, stream=None):
+    """Chunkwise backward.  Inputs as in ``fwd`` (no normaliser); dout [B,H,T,dv] in q's
+    dtype; dfinal fp32 [B,H,dk,dv] or None.  Returns (dq, dk, dv, dgate, dinit): dgate is
+    shaped like the gate / per-token decay (None for gamma, no decay, or not wanted); dinit
+    fp32 [B,H,dk,dv] (None if not wanted)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    kind = _decay_kind(decay, decay_kind)
+    for t in (q, k, v, dout, decay, init_state, dfinal):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    dq, dkk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dgate = None
+    if want_dgate and kind in ("gate", "token"):
+        dgate = torch.empty_like(decay, dtype=torch.float32)
+    dinit = None
+    if want_dinit:
+        dinit = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    flags = flags_for(q.dtype, kind, phi_elu1, False)
+    rc = load_library().fla_linattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(init_state),
+                                        _ptr(dout), _ptr(dfinal), _ptr(dq), _ptr(dkk), _ptr(dvv),
+                                        _ptr(dgate), _ptr(dinit), B, H, T, dk, dv, chunk, flags,
+                                        _stream(stream))
+    if rc != FLA_OK:
+        raise FlaError("fla_linattn_bwd", rc)
+    return dq, dkk, dvv, dgate, dinit

@@ -1,7 +1,7 @@
 """Build the HIP library (gfx950) in-tree: chunkwise_causal_linear_amd/lib/libfla_linattn.so.
 
-The fused chunk kernel is instantiated per (input dtype, key dimension) in separate
-objects compiled in parallel; the C ABI (include/fla_linattn.h) lives in fla_api.hip.
+The fused chunk kernel is instantiated per (input dtype, key dimension) and the backward
+kernels per (input dtype, contraction width) in separate objects compiled in parallel; the C ABI (include/fla_linattn.h) lives in fla_api.hip.
 Usage: python -m chunkwise_causal_linear_amd.build [-j N]
 """
 from __future__ import annotations
@@ -30,6 +30,7 @@ COMMON = [
 ]
 DTYPES = [("bf16", 1), ("f32", 0)]
 DKS = [16, 32, 64, 128, 256]
+BWD_DYS = [64, 128, 256]
 
 
 def _units():
@@ -39,6 +40,11 @@ def _units():
             obj = os.path.join(OBJDIR, f"chunk_{tname}_{dk}.o")
             units.append((os.path.join(CSRC, "chunk_inst.hip"), obj,
                           [f"-DFLA_TIN_BF16={flag}", f"-DFLA_DK={dk}"]))
+    for tname, flag in DTYPES:
+        for dy in BWD_DYS:
+            obj = os.path.join(OBJDIR, f"bwd_{tname}_{dy}.o")
+            units.append((os.path.join(CSRC, "bwd_inst.hip"), obj,
+                          [f"-DFLA_TIN_BF16={flag}", f"-DFLA_BWD_DY={dy}"]))
     units.append((os.path.join(CSRC, "fla_api.hip"), os.path.join(OBJDIR, "fla_api.o"), []))
     return units
 

@@ -1,0 +1,655 @@
+// Chunkwise causal linear attention, backward — gfx950 kernels.
+//
+// Reverse-mode derivative of the recurrence h_t = diag(g_t) h_{t-1} + phi(k_t) v_t^T,
+// o_t = h_t^T phi(q_t) (h = S^T, dk x dv; the decayed linear attention of the textbook
+// chapter 1.6 "linear attention" section with the RetNet / GLA decays of the FLA posts),
+// for the loss L = sum dout . o + sum dfinal (.) h_T.  Per chunk of C rows with b the
+// inclusive product of the decays inside the chunk, bL = b[L-1], Qb = phi(q) b,
+// Kb = phi(k) / b, and H (dH) the state (its gradient) at the chunk's start (end):
+//   dphi(q) = b (.) ( tril(dO V^T) Kb + dO H^T ),         H  <- diag(bL) (H + Kb^T V)
+//   dv      = triu(Kb Qb^T) dO + Kb diag(bL) dH,           dH <- diag(bL) dH + Qb^T dO
+//   dphi(k) = (1/b) (.) ( triu(V dO^T) Qb + V (diag(bL) dH)^T )
+// (triu: query rows at or after the key row).  The gate's gradient follows from
+// d log b_t = phi(q_t) dphi(q_t) - phi(k_t) dphi(k_t) summed over later tokens, plus the
+// final state's term sum_e dfinal (.) h_T; d alpha = d log alpha / alpha.
+//
+// All three are one scan pattern, "role" R:
+//   out[r][x] = post[r][x] * ( sum_{s ~ r} (X_r . Y_s) Z[s][x] + sum_y X[r][y] S[y][x] ),
+//   S (fp32, [DY][64] per workgroup, in MFMA accumulators) updated with Y^T Z per chunk,
+// with  DQ: X = dO, Y = V, Z = Kb, S = H^T, forward in time, post = b;
+//       DK: X = V, Y = dO, Z = Qb, S = dH^T, reverse, post = 1/b;
+//       DV: X = Kb, Y = Qb, Z = dO, S = dH,  reverse, post = 1.
+// One workgroup (4 waves) owns one (b, h, 64-wide slice of the output dimension); wave w
+// owns output columns 16w..16w+15.  Per chunk: the decay is scanned down the chunk,
+// operand tiles are formed in LDS from registers prefetched one chunk ahead, the C x C
+// score tiles are computed once (shared through LDS), then each wave forms its output
+// tiles and updates its state columns.  MFMA conventions are the forward kernel's.
+#pragma once
+
+#include "chunk_fwd.hpp"
+
+namespace fla {
+
+enum : int { BWD_DQ = 0, BWD_DK = 1, BWD_DV = 2 };
+
+struct BwdArgs {
+  const void *q, *k, *v, *dout;
+  const float *decay;  // gamma [H], gate [B][H][T][dk], token [B][H][T], or null
+  const float *init;   // [B][H][dk][dv] or null (read by DQ)
+  const float *dfinal; // [B][H][dk][dv] or null (read by DV, DK, and DQ for its term)
+  void *grad_q, *grad_k, *grad_v; // outputs in the input dtype
+  float *dgate;        // gate: [B][H][T][dk] (written by DK) or null
+  float *dinit;        // [B][H][dk][dv] (written by DV) or null
+  float *rq;           // workspace [B][H][T][dk]: phi(q) dphi(q) (DQ writes, DK reads) or null
+  float *fterm;        // workspace [B][H][dk]: sum_e dfinal h_T (DQ writes, DK reads) or null
+  float *tpart;        // workspace [B][H][nsl][T]: per-slice d log a_t (token) or null
+  int64_t T;
+  int H, dk, dv;
+  int nsl;             // 64-wide slices of the output dimension
+  int nunits;          // B * H * nsl
+  int phi_elu1;
+  int want_dg;         // DQ: write rq (and fterm with dfinal); DK: write the decay gradient
+};
+
+template <typename TIn, int ROLE, int DY, int DECAY>
+struct BwdCfg {
+  static constexpr int C = 64, XW = 64, NT = 256;
+  static constexpr int ES = sizeof(TIn);
+  static constexpr int VE = 16 / ES;             // elements per 16-byte vector
+  static constexpr int KU = ES == 2 ? 32 : 16;   // MFMA K unit
+  static constexpr int LDX = DY + VE;            // X, Y row stride (elements)
+  static constexpr int LDZ = XW + VE;            // Z row stride
+  static constexpr bool REV = ROLE != BWD_DQ;
+  static constexpr bool HAS_B = DECAY != DECAY_NONE;
+  static constexpr bool GATE = DECAY == DECAY_GATE;
+  static constexpr bool TOKEN = DECAY == DECAY_TOKEN;
+  // b tile columns: per-key gate over the decayed dimension, else one column
+  static constexpr int GW = GATE ? (ROLE == BWD_DV ? DY : XW) : 1;
+  static constexpr bool HAS_AUX = ROLE != BWD_DV; // phi(q) (DQ) / phi(k) then r (DK)
+  static constexpr bool HAS_RQ = ROLE == BWD_DK && (GATE || TOKEN);
+  // bf16 dq / dk roles carry the rounded MFMA operands as hi + lo pairs (scores, Z, state)
+  // so their outputs, and the decay gradient summed from them over the sequence, keep
+  // close to fp32 accuracy; the dv role rounds once, like the forward pass
+  static constexpr bool SPLIT = ES == 2 && ROLE != BWD_DV;
+  // register prefetch: 16-byte vectors per thread
+  static constexpr int NVX = C * DY / VE / NT;
+  static constexpr int NVZ = C * XW / VE / NT;
+  static constexpr int NVG = GATE ? C * GW / 4 / NT : 0;
+  static constexpr int NVR = HAS_RQ ? C * XW / 4 / NT : 0;
+  static_assert(NVX >= 1 && NVZ >= 1, "tile too small for the thread count");
+  // gate scan: NSEG row segments of SEGR rows per column
+  static constexpr int NSEG = GATE ? NT / GW : 1;
+  static constexpr int SEGR = C / NSEG;
+  // LDS (bytes)
+  static constexpr int OFF_X = 0;
+  static constexpr int OFF_Y = OFF_X + C * LDX * ES;
+  static constexpr int OFF_Z = OFF_Y + C * LDX * ES;
+  static constexpr int OFF_ZL = OFF_Z + C * LDZ * ES;                 // Z lo (SPLIT)
+  static constexpr int OFF_P = OFF_ZL + (SPLIT ? C * LDZ * ES : 0);
+  static constexpr int OFF_PL = OFF_P + 16 * 256 * ES;                // score lo (SPLIT)
+  static constexpr int OFF_B = OFF_PL + (SPLIT ? 16 * 256 * ES : 0);
+  static constexpr int OFF_BL = OFF_B + (HAS_B ? C * GW * 4 : 0);
+  static constexpr int OFF_AUX = OFF_BL + (HAS_B ? GW * 4 : 0);
+  static constexpr int OFF_RQ = OFF_AUX + (HAS_AUX ? C * XW * 4 : 0);
+  static constexpr int OFF_TOT = OFF_RQ + (HAS_RQ ? C * XW * 4 : 0);
+  static constexpr int TOT_W = (GATE ? GW : 1) > 64 ? (GATE ? GW : 1) : 64;
+  static constexpr int LDS = OFF_TOT + 4 * TOT_W * 4;
+  static constexpr bool FITS = LDS <= kMaxLds;
+};
+
+// fp32 values rounded to bf16 and back (the hi part of a hi + lo split)
+__device__ __forceinline__ f32x4 bf_round4(f32x4 x) {
+  return f32x4{(float)(__bf16)x[0], (float)(__bf16)x[1], (float)(__bf16)x[2], (float)(__bf16)x[3]};
+}
+
+__device__ __forceinline__ float phi_d(float phi_val, int elu1) {
+  // derivative of phi in terms of phi(x): identity -> 1; elu+1 -> 1 (x > 0, phi > 1)
+  // or e^x = phi(x) (x <= 0)
+  return elu1 ? fminf(phi_val, 1.f) : 1.f;
+}
+
+// Score-tile operand (A, row r = li, K = s) for K unit u of row block RB: tiles TA, TB of
+// the row-major 16x16 score images (negative = zeros).  bf16: two tiles per unit.
+template <typename TIn, int TA, int TB>
+__device__ __forceinline__ Frag<TIn> ld_ptile2(const TIn *lbuf) {
+  if constexpr (sizeof(TIn) == 2) {
+    const __bf16 z = (__bf16)0.f;
+    bf16x4 lo = {z, z, z, z}, hi = {z, z, z, z};
+    if constexpr (TA >= 0) lo = *reinterpret_cast<const bf16x4 *>(lbuf + TA * 256);
+    if constexpr (TB >= 0) hi = *reinterpret_cast<const bf16x4 *>(lbuf + TB * 256);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    static_assert(TB < 0, "fp32 K units are one tile");
+    if constexpr (TA >= 0) return *reinterpret_cast<const f32x4 *>(lbuf + TA * 256);
+    else return f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Allowed score tiles (row block rb of the output rows r, column block sb of the summed
+// rows s): s <= r (forward roles) or s >= r (reverse roles).
+template <bool REV>
+__host__ __device__ constexpr bool tile_on(int rb, int sb) { return REV ? sb >= rb : sb <= rb; }
+template <bool REV>
+__host__ __device__ constexpr int tile_pos(int rb, int sb) { // index among the allowed tiles
+  int n = 0;
+  for (int i = 0; i < 16; ++i) {
+    if (i == rb * 4 + sb) return n;
+    if (tile_on<REV>(i / 4, i % 4)) ++n;
+  }
+  return -1;
+}
+
+template <typename TIn, int ROLE, int DY, int DECAY>
+__global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
+  using K = BwdCfg<TIn, ROLE, DY, DECAY>;
+  constexpr int C = K::C, XW = K::XW, VE = K::VE, KU = K::KU;
+  constexpr int LDX = K::LDX, LDZ = K::LDZ, GW = K::GW;
+  constexpr bool REV = K::REV;
+  constexpr int NYB = DY / 16;         // 16-row blocks of the state
+  constexpr int NZU = C / KU;          // K units over the chunk rows
+  __shared__ __attribute__((aligned(16))) unsigned char lds[K::LDS];
+  TIn *sX = reinterpret_cast<TIn *>(lds + K::OFF_X);
+  TIn *sY = reinterpret_cast<TIn *>(lds + K::OFF_Y);
+  TIn *sZ = reinterpret_cast<TIn *>(lds + K::OFF_Z);
+  TIn *sP = reinterpret_cast<TIn *>(lds + K::OFF_P);
+  TIn *sZL = reinterpret_cast<TIn *>(lds + K::OFF_ZL);
+  TIn *sPL = reinterpret_cast<TIn *>(lds + K::OFF_PL);
+  float *sB = reinterpret_cast<float *>(lds + K::OFF_B);
+  float *sBL = reinterpret_cast<float *>(lds + K::OFF_BL);
+  float *sA = reinterpret_cast<float *>(lds + K::OFF_AUX);
+  float *sR = reinterpret_cast<float *>(lds + K::OFF_RQ);
+  float *sT = reinterpret_cast<float *>(lds + K::OFF_TOT);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, li = lane & 15;
+
+  // unit -> (b h, slice); sibling slices of one head on the same XCD (ids = mod 8)
+  int unit = blockIdx.x;
+  if ((a.nunits & 7) == 0) unit = (unit & 7) * (a.nunits >> 3) + (unit >> 3);
+  const int slice = unit % a.nsl;
+  const int64_t bh = unit / a.nsl;
+  const int h = (int)(bh % a.H);
+  const int64_t T = a.T;
+  const int dk = a.dk, dv = a.dv;
+  const int nchunks = (int)((T + C - 1) / C);
+  const int elu1 = a.phi_elu1;
+  const bool want_dg = a.want_dg != 0;
+
+  // sources: X, Y rows of DY elements; Z and AUX 64-column slices
+  const TIn *srcX, *srcY, *srcZ, *srcA = nullptr;
+  int ldz;
+  if constexpr (ROLE == BWD_DQ) {
+    srcX = (const TIn *)a.dout + bh * T * dv; srcY = (const TIn *)a.v + bh * T * dv;
+    srcZ = (const TIn *)a.k + bh * T * dk; srcA = (const TIn *)a.q + bh * T * dk;
+    ldz = dk;
+  } else if constexpr (ROLE == BWD_DK) {
+    srcX = (const TIn *)a.v + bh * T * dv; srcY = (const TIn *)a.dout + bh * T * dv;
+    srcZ = (const TIn *)a.q + bh * T * dk; srcA = (const TIn *)a.k + bh * T * dk;
+    ldz = dk;
+  } else {
+    srcX = (const TIn *)a.k + bh * T * dk; srcY = (const TIn *)a.q + bh * T * dk;
+    srcZ = (const TIn *)a.dout + bh * T * dv;
+    ldz = dv;
+  }
+  const int zoff = slice * XW;                      // first output column
+  const int goff = (ROLE == BWD_DV) ? 0 : zoff;     // first gate column
+
+  auto chunk_len = [&](int n) -> int {
+    const int64_t l = T - (int64_t)n * C;
+    return (int)(l < C ? l : C);
+  };
+
+  // ---- gamma: b[r] = gamma^(r+1) for the whole kernel -----------------------------
+  if constexpr (DECAY == DECAY_GAMMA) {
+    if (wave == 0) {
+      float x = a.decay[h];
+      for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_up(x, d);
+        if (lane >= d) x *= o;
+      }
+      sB[lane] = x;
+    }
+  }
+
+  // ---- register prefetch of one chunk ---------------------------------------------
+  uint32_t rX[K::NVX][4], rY[K::NVX][4], rZ[K::NVZ][4];
+  uint32_t rA[K::HAS_AUX ? K::NVZ : 1][4];
+  uint32_t rG[K::NVG > 0 ? K::NVG : 1][4];
+  uint32_t rR[K::NVR > 0 ? K::NVR : 1][4];
+  float rTok = 1.f;
+  auto load = [&](int n) {
+    const int L = chunk_len(n);
+    const int64_t t0 = (int64_t)n * C;
+    constexpr int VPRX = DY / VE, VPRZ = XW / VE;
+#pragma unroll
+    for (int j = 0; j < K::NVX; ++j) {
+      const int vi = tid + 256 * j, r = vi / VPRX, c = (vi % VPRX) * VE;
+      uint4 x = make_uint4(0, 0, 0, 0), y = x;
+      if (r < L) {
+        x = *reinterpret_cast<const uint4 *>(srcX + (t0 + r) * DY + c);
+        y = *reinterpret_cast<const uint4 *>(srcY + (t0 + r) * DY + c);
+      }
+      rX[j][0] = x.x; rX[j][1] = x.y; rX[j][2] = x.z; rX[j][3] = x.w;
+      rY[j][0] = y.x; rY[j][1] = y.y; rY[j][2] = y.z; rY[j][3] = y.w;
+    }
+#pragma unroll
+    for (int j = 0; j < K::NVZ; ++j) {
+      const int vi = tid + 256 * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
+      uint4 z = make_uint4(0, 0, 0, 0), x = z;
+      if (r < L) {
+        z = *reinterpret_cast<const uint4 *>(srcZ + (t0 + r) * ldz + zoff + c);
+        if constexpr (K::HAS_AUX)
+          x = *reinterpret_cast<const uint4 *>(srcA + (t0 + r) * dk + zoff + c);
+      }
+      rZ[j][0] = z.x; rZ[j][1] = z.y; rZ[j][2] = z.z; rZ[j][3] = z.w;
+      if constexpr (K::HAS_AUX) {
+        rA[j][0] = x.x; rA[j][1] = x.y; rA[j][2] = x.z; rA[j][3] = x.w;
+      }
+    }
+    if constexpr (K::GATE) {
+      constexpr int VPRG = GW / 4;
+      const float *gsrc = a.decay + bh * T * dk + goff;
+#pragma unroll
+      for (int j = 0; j < K::NVG; ++j) {
+        const int vi = tid + 256 * j, r = vi / VPRG, c = (vi % VPRG) * 4;
+        uint4 x = make_uint4(0x3f800000u, 0x3f800000u, 0x3f800000u, 0x3f800000u); // 1.0f
+        if (r < L) x = *reinterpret_cast<const uint4 *>(gsrc + (t0 + r) * dk + c);
+        rG[j][0] = x.x; rG[j][1] = x.y; rG[j][2] = x.z; rG[j][3] = x.w;
+      }
+    }
+    if constexpr (K::TOKEN) {
+      rTok = 1.f;
+      if (tid < L) rTok = a.decay[bh * T + t0 + tid];
+    }
+    if constexpr (K::HAS_RQ) {
+      if (want_dg) {
+        constexpr int VPRR = XW / 4;
+#pragma unroll
+        for (int j = 0; j < K::NVR; ++j) {
+          const int vi = tid + 256 * j, r = vi / VPRR, c = (vi % VPRR) * 4;
+          uint4 x = make_uint4(0, 0, 0, 0);
+          if (r < L) x = *reinterpret_cast<const uint4 *>(a.rq + (bh * T + t0 + r) * dk + zoff + c);
+          rR[j][0] = x.x; rR[j][1] = x.y; rR[j][2] = x.z; rR[j][3] = x.w;
+        }
+      }
+    }
+  };
+
+  // ---- state: S[y][x] for y in DY, x = 16 wave + li; tile yb holds rows 16yb + 4g + q
+  f32x4 S[NYB];
+  {
+    const float *s0 = (ROLE == BWD_DQ) ? a.init : a.dfinal;
+#pragma unroll
+    for (int yb = 0; yb < NYB; ++yb) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int y = 16 * yb + 4 * g + qq, x = 16 * wave + li;
+        float val = 0.f;
+        if (s0) {
+          if constexpr (ROLE == BWD_DV) val = s0[(bh * dk + y) * dv + zoff + x];
+          else val = s0[(bh * dk + zoff + x) * dv + y];
+        }
+        S[yb][qq] = val;
+      }
+    }
+  }
+
+  // decay-gradient carry (DK): per column (gate) or per slice (token)
+  float carry = 0.f;
+  if constexpr (ROLE == BWD_DK && K::GATE) {
+    if (want_dg && a.fterm) carry = a.fterm[bh * dk + goff + (tid & 63)];
+  }
+  if constexpr (ROLE == BWD_DK && K::TOKEN) {
+    if (want_dg && a.fterm && wave == 0) {
+      float x = a.fterm[bh * dk + goff + lane];
+      for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+      carry = x;
+    }
+  }
+  float araw[K::GATE && ROLE == BWD_DK ? K::SEGR : 1];
+  (void)araw;
+
+  if (nchunks > 0) load(REV ? nchunks - 1 : 0);
+
+  for (int it = 0; it < nchunks; ++it) {
+    const int n = REV ? nchunks - 1 - it : it;
+    const int L = chunk_len(n);
+    const int64_t t0 = (int64_t)n * C;
+
+    // ---- 1. decay inside the chunk: b = inclusive product down the rows -----------
+    if constexpr (K::GATE) {
+      constexpr int VPRG = GW / 4;
+#pragma unroll
+      for (int j = 0; j < K::NVG; ++j) {
+        const int vi = tid + 256 * j, r = vi / VPRG, c = (vi % VPRG) * 4;
+        *reinterpret_cast<uint4 *>(sB + r * GW + c) = make_uint4(rG[j][0], rG[j][1], rG[j][2], rG[j][3]);
+      }
+      __syncthreads();
+      const int col = tid % GW, seg = tid / GW;
+      float p = 1.f;
+#pragma unroll
+      for (int i = 0; i < K::SEGR; ++i) {
+        const int r = seg * K::SEGR + i;
+        const float al = sB[r * GW + col];
+        if constexpr (ROLE == BWD_DK) araw[i] = al;
+        p *= al;
+        sB[r * GW + col] = p;
+      }
+      if constexpr (K::NSEG > 1) {
+        sT[seg * K::TOT_W + col] = p;
+        __syncthreads();
+        float pre = 1.f;
+        for (int s2 = 0; s2 < seg; ++s2) pre *= sT[s2 * K::TOT_W + col];
+        if (seg > 0) {
+#pragma unroll
+          for (int i = 0; i < K::SEGR; ++i) sB[(seg * K::SEGR + i) * GW + col] *= pre;
+        }
+        if (seg == K::NSEG - 1) sBL[col] = p * pre;
+      } else {
+        sBL[col] = p;
+      }
+    } else if constexpr (K::TOKEN) {
+      if (wave == 0) {
+        float x = rTok;
+        for (int d = 1; d < 64; d <<= 1) {
+          const float o = __shfl_up(x, d);
+          if (lane >= d) x *= o;
+        }
+        sB[lane] = x;
+        if (lane == 63) sBL[0] = x; // padded rows carry 1: b[63] = b[L-1]
+      }
+    }
+    __syncthreads();
+    // chunk decay bL of a column (gate) or of the chunk
+    auto bl_at = [&](int idx) -> float {
+      if constexpr (K::GATE) return sBL[idx];
+      else if constexpr (K::TOKEN) return sBL[0];
+      else if constexpr (DECAY == DECAY_GAMMA) return sB[L - 1];
+      else return 1.f;
+    };
+    auto b_at = [&](int r, int col) -> float {
+      if constexpr (K::GATE) return sB[r * GW + col];
+      else if constexpr (K::HAS_B) return sB[r];
+      else return 1.f;
+    };
+
+    // ---- 2. operand tiles -----------------------------------------------------------
+    {
+      constexpr int VPRX = DY / VE, VPRZ = XW / VE;
+#pragma unroll
+      for (int j = 0; j < K::NVX; ++j) {
+        const int vi = tid + 256 * j, r = vi / VPRX, c = (vi % VPRX) * VE;
+        if constexpr (ROLE == BWD_DV) {
+          float fx[VE], fy[VE];
+          unpack<TIn, VE>(fx, rX[j]);
+          unpack<TIn, VE>(fy, rY[j]);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) {
+            const float bb = b_at(r, c + e);
+            const bool ok = r < L;
+            fx[e] = ok ? phi_f(fx[e], elu1) / bb : 0.f;
+            fy[e] = ok ? phi_f(fy[e], elu1) * bb : 0.f;
+          }
+          st_lds<TIn, VE>(sX + r * LDX + c, fx);
+          st_lds<TIn, VE>(sY + r * LDX + c, fy);
+        } else {
+          st_words_lds<4>(sX + r * LDX + c, rX[j]);
+          st_words_lds<4>(sY + r * LDX + c, rY[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < K::NVZ; ++j) {
+        const int vi = tid + 256 * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
+        if constexpr (ROLE == BWD_DV) {
+          st_words_lds<4>(sZ + r * LDZ + c, rZ[j]);
+        } else {
+          float fz[VE], fa[VE];
+          unpack<TIn, VE>(fz, rZ[j]);
+          unpack<TIn, VE>(fa, rA[j]);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) {
+            const float bb = b_at(r, c + e);
+            const bool ok = r < L;
+            const float pz = phi_f(fz[e], elu1);
+            fz[e] = ok ? (ROLE == BWD_DQ ? pz / bb : pz * bb) : 0.f;
+            fa[e] = ok ? phi_f(fa[e], elu1) : 0.f;
+          }
+          st_lds<TIn, VE>(sZ + r * LDZ + c, fz);
+          if constexpr (K::SPLIT) {
+            float fl[VE];
+#pragma unroll
+            for (int e = 0; e < VE; ++e) fl[e] = fz[e] - (float)(TIn)fz[e];
+            st_lds<TIn, VE>(sZL + r * LDZ + c, fl);
+          }
+#pragma unroll
+          for (int e = 0; e < VE; e += 4)
+            *reinterpret_cast<float4 *>(sA + r * XW + c + e) = make_float4(fa[e], fa[e + 1], fa[e + 2], fa[e + 3]);
+        }
+      }
+      if constexpr (K::HAS_RQ) {
+        if (want_dg) {
+          constexpr int VPRR = XW / 4;
+#pragma unroll
+          for (int j = 0; j < K::NVR; ++j) {
+            const int vi = tid + 256 * j, r = vi / VPRR, c = (vi % VPRR) * 4;
+            *reinterpret_cast<uint4 *>(sR + r * XW + c) = make_uint4(rR[j][0], rR[j][1], rR[j][2], rR[j][3]);
+          }
+        }
+      }
+    }
+    // ---- 3. prefetch the next chunk -------------------------------------------------
+    if (it + 1 < nchunks) load(REV ? n - 1 : n + 1);
+    __syncthreads();
+
+    // ---- 4. score tiles: image of tile (rb, sb) holds P[r][s] = X_r . Y_s, masked ----
+    static_for<0, 16>([&](auto I) {
+      constexpr int rb = I / 4, sb = I % 4;
+      if constexpr (tile_on<REV>(rb, sb)) {
+        if (tile_pos<REV>(rb, sb) % 4 == wave) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          const TIn *ya = sY + (16 * sb + li) * LDX + (sizeof(TIn) == 2 ? 8 : 4) * g;
+          const TIn *xb = sX + (16 * rb + li) * LDX + (sizeof(TIn) == 2 ? 8 : 4) * g;
+#pragma unroll
+          for (int u = 0; u < DY / KU; ++u)
+            acc = mma(acc, ld_frag_c_at<TIn, true>(ya, u, g), ld_frag_c_at<TIn, true>(xb, u, g));
+          // acc[qq] = P[r = 16 rb + li][s = 16 sb + 4g + qq]
+          if constexpr (rb == sb) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int s = 4 * g + qq;
+              const bool keep = REV ? (s >= li) : (s <= li);
+              if (!keep) acc[qq] = 0.f;
+            }
+          }
+          st_ptile<TIn>(sP + I * 256 + li * 16 + 4 * g, acc);
+          if constexpr (K::SPLIT) {
+            f32x4 lo;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) lo[qq] = acc[qq] - (float)(TIn)acc[qq];
+            st_ptile<TIn>(sPL + I * 256 + li * 16 + 4 * g, lo);
+          }
+        }
+      }
+    });
+    __syncthreads();
+
+    // ---- 5. output tiles and the state ----------------------------------------------
+    const int x = 16 * wave + li; // this lane's output column in the slice
+    if constexpr (ROLE == BWD_DK) {
+      const float d = bl_at(x);
+#pragma unroll
+      for (int yb = 0; yb < NYB; ++yb) S[yb] *= d;
+    } else if constexpr (ROLE == BWD_DV) {
+#pragma unroll
+      for (int yb = 0; yb < NYB; ++yb)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) S[yb][qq] *= bl_at(16 * yb + 4 * g + qq);
+    }
+    Frag<TIn> zf[NZU], zl[K::SPLIT ? NZU : 1];
+#pragma unroll
+    for (int u = 0; u < NZU; ++u) {
+      zf[u] = ld_frag_t<TIn, true>(sZ, LDZ, 16 * wave, u, g, li);
+      if constexpr (K::SPLIT) zl[u] = ld_frag_t<TIn, true>(sZL, LDZ, 16 * wave, u, g, li);
+    }
+
+    static_for<0, 4>([&](auto RB) {
+      constexpr int rb = RB;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      // intra-chunk: sum over allowed s of P[r][s] Z[s][x]
+      static_for<0, NZU>([&](auto U) {
+        constexpr int u = U;
+        if constexpr (sizeof(TIn) == 2) {
+          constexpr int TA = tile_on<REV>(rb, 2 * u) ? rb * 4 + 2 * u : -1;
+          constexpr int TB = tile_on<REV>(rb, 2 * u + 1) ? rb * 4 + 2 * u + 1 : -1;
+          if constexpr (TA >= 0 || TB >= 0) {
+            const Frag<TIn> ph = ld_ptile2<TIn, TA, TB>(sP + li * 16 + 4 * g);
+            acc = mma(acc, ph, zf[u]);
+            if constexpr (K::SPLIT) {
+              acc = mma(acc, ld_ptile2<TIn, TA, TB>(sPL + li * 16 + 4 * g), zf[u]);
+              acc = mma(acc, ph, zl[u]);
+            }
+          }
+        } else {
+          constexpr int TA = tile_on<REV>(rb, u) ? rb * 4 + u : -1;
+          if constexpr (TA >= 0) acc = mma(acc, ld_ptile2<TIn, TA, -1>(sP + li * 16 + 4 * g), zf[u]);
+        }
+      });
+      // inter-chunk: sum over y of X[r][y] S[y][x]
+      const TIn *xa = sX + (16 * rb + li) * LDX + 4 * g;
+#pragma unroll
+      for (int u = 0; u < DY / KU; ++u) {
+        Frag<TIn> sf;
+        const Frag<TIn> xf = ld_frag_at<TIn, true>(xa, u);
+        if constexpr (sizeof(TIn) == 2) sf = acc_frag_bf(S[2 * u], S[2 * u + 1]);
+        else sf = S[u];
+        acc = mma(acc, xf, sf);
+        if constexpr (K::SPLIT) {
+          const f32x4 l0 = S[2 * u] - bf_round4(S[2 * u]), l1 = S[2 * u + 1] - bf_round4(S[2 * u + 1]);
+          acc = mma(acc, xf, acc_frag_bf(l0, l1));
+        }
+      }
+      // acc[qq] = out[r = 16 rb + 4g + qq][x]
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int r = 16 * rb + 4 * g + qq;
+        const int64_t t = t0 + r;
+        if constexpr (ROLE == BWD_DQ) {
+          const float dqb = acc[qq] * b_at(r, x);
+          const float qb = sA[r * XW + x];
+          if (r < L) {
+            ((TIn *)a.grad_q)[(bh * T + t) * dk + zoff + x] = (TIn)(dqb * phi_d(qb, elu1));
+            if (want_dg) a.rq[(bh * T + t) * dk + zoff + x] = qb * dqb;
+          }
+        } else if constexpr (ROLE == BWD_DK) {
+          const float dkb = acc[qq] / b_at(r, x);
+          const float kb = sA[r * XW + x];
+          if (r < L) ((TIn *)a.grad_k)[(bh * T + t) * dk + zoff + x] = (TIn)(dkb * phi_d(kb, elu1));
+          if constexpr (K::HAS_RQ) sA[r * XW + x] = (r < L) ? sR[r * XW + x] - kb * dkb : 0.f;
+        } else {
+          if (r < L) ((TIn *)a.grad_v)[(bh * T + t) * dv + zoff + x] = (TIn)acc[qq];
+        }
+      }
+    });
+
+    // state update: S[y][x] += sum_s Y[s][y] Z[s][x]
+#pragma unroll
+    for (int yb = 0; yb < NYB; ++yb) {
+#pragma unroll
+      for (int u = 0; u < NZU; ++u)
+      {
+        const Frag<TIn> yf = ld_frag_t<TIn, true>(sY, LDX, 16 * yb, u, g, li);
+        S[yb] = mma(S[yb], yf, zf[u]);
+        if constexpr (K::SPLIT) S[yb] = mma(S[yb], yf, zl[u]);
+      }
+    }
+    if constexpr (ROLE == BWD_DQ) {
+      const float d = bl_at(x);
+#pragma unroll
+      for (int yb = 0; yb < NYB; ++yb) S[yb] *= d;
+    }
+
+    // ---- 6. decay gradient (DK): reverse cumulative sum of r over later tokens ------
+    if constexpr (ROLE == BWD_DK && K::GATE) {
+      if (want_dg) {
+        __syncthreads();
+        const int col = tid & 63, seg = tid >> 6; // K::SEGR = 16 rows per segment
+        float cs[K::SEGR];
+        float acc = 0.f;
+#pragma unroll
+        for (int i = K::SEGR - 1; i >= 0; --i) {
+          acc += sA[(seg * K::SEGR + i) * XW + col];
+          cs[i] = acc;
+        }
+        sT[seg * K::TOT_W + col] = acc;
+        __syncthreads();
+        float suffix = 0.f, total = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < K::NSEG; ++s2) {
+          const float v2 = sT[s2 * K::TOT_W + col];
+          total += v2;
+          if (s2 > seg) suffix += v2;
+        }
+#pragma unroll
+        for (int i = 0; i < K::SEGR; ++i) {
+          const int r = seg * K::SEGR + i;
+          if (r < L) a.dgate[(bh * T + t0 + r) * dk + goff + col] = (cs[i] + suffix + carry) / araw[i];
+        }
+        carry += total;
+      }
+    }
+    if constexpr (ROLE == BWD_DK && K::TOKEN) {
+      if (want_dg) {
+        __syncthreads();
+        {
+          const int r = tid >> 2, part = tid & 3;
+          float sum = 0.f;
+#pragma unroll
+          for (int c2 = 0; c2 < 16; ++c2) sum += sA[r * XW + part * 16 + c2];
+          sum += __shfl_xor(sum, 1);
+          sum += __shfl_xor(sum, 2);
+          if (part == 0) sT[r] = sum;
+        }
+        __syncthreads();
+        if (wave == 0) {
+          float xs = sT[lane];
+          for (int d = 1; d < 64; d <<= 1) {
+            const float o = __shfl_down(xs, d);
+            if (lane + d < 64) xs += o;
+          }
+          if (lane < L) a.tpart[(bh * a.nsl + slice) * T + t0 + lane] = xs + carry;
+          carry += __shfl(xs, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue ---------------------------------------------------------------------
+  const int x = 16 * wave + li;
+  if constexpr (ROLE == BWD_DQ) {
+    if (want_dg && a.fterm) {
+      float part = 0.f;
+      if (a.dfinal) {
+#pragma unroll
+        for (int yb = 0; yb < NYB; ++yb)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+            part += a.dfinal[(bh * dk + zoff + x) * dv + 16 * yb + 4 * g + qq] * S[yb][qq];
+      }
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (g == 0) a.fterm[bh * dk + zoff + x] = part;
+    }
+  } else if constexpr (ROLE == BWD_DV) {
+    if (a.dinit) {
+#pragma unroll
+      for (int yb = 0; yb < NYB; ++yb)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          a.dinit[(bh * dk + 16 * yb + 4 * g + qq) * dv + zoff + x] = S[yb][qq];
+    }
+  }
+}
+
+} // namespace fla

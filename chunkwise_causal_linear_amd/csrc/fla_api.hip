@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/fla_linattn.h"
+#include "bwd_dispatch.hpp"
 #include "dispatch.hpp"
 
 namespace fla {
@@ -77,8 +78,36 @@ int64_t auto_segments(int64_t B, int64_t H, int64_t T, int64_t dv, int64_t chunk
   return p < 1 ? 1 : p;
 }
 
+BwdLauncher find_bwd(bool bf16, int64_t dy, int role, int decay) {
+  if (bf16) {
+    switch (dy) {
+    case 64: return bwd_launcher_bf16_64(role, decay);
+    case 128: return bwd_launcher_bf16_128(role, decay);
+    case 256: return bwd_launcher_bf16_256(role, decay);
+    }
+  } else {
+    switch (dy) {
+    case 64: return bwd_launcher_f32_64(role, decay);
+    case 128: return bwd_launcher_f32_128(role, decay);
+    case 256: return bwd_launcher_f32_256(role, decay);
+    }
+  }
+  return nullptr;
+}
+
 // ---------------------------------------------------------------------------------
 // small kernels
+
+// Per-token decay gradient: d alpha_t = (sum over key slices of d log a_t) / alpha_t.
+__global__ void token_dgate_kernel(const float *tpart, const float *decay, float *dgate,
+                                   int64_t BH, int64_t T, int nsl) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= BH * T) return;
+  const int64_t bh = i / T, t = i % T;
+  float s = 0.f;
+  for (int p = 0; p < nsl; ++p) s += tpart[(bh * nsl + p) * T + t];
+  dgate[i] = s / decay[i];
+}
 
 // dst[i] = src ? src[i] : 0 (state copy / zero fill).
 __global__ void state_fill_kernel(float *dst, const float *src, int64_t n) {
@@ -180,10 +209,18 @@ int launch_fill(float *dst, const float *src, int64_t n, hipStream_t s) {
   return FLA_OK;
 }
 
+// An empty sequence has an empty per-token decay, which callers may pass as NULL.
+const float *nonnull_decay_if_empty(const float *decay, int64_t T, uint32_t flags) {
+  static const float kUnused[4] = {1.f, 1.f, 1.f, 1.f}; // never read: nothing is launched on it
+  if (T == 0 && !decay && (flags & (FLA_DECAY_GATE | FLA_DECAY_TOKEN))) return kUnused;
+  return decay;
+}
+
 int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_gamma,
              const float *init_state, void *out, float *final_state, int64_t B, int64_t H,
              int64_t T, int64_t dk, int64_t dv, int64_t chunk, uint32_t flags,
              int64_t n_segments, void *stream) {
+  gate_or_gamma = nonnull_decay_if_empty(gate_or_gamma, T, flags);
   int rc = check_common(B, H, dk, dv, flags, gate_or_gamma);
   if (rc != FLA_OK) return rc;
   if (T < 0 || n_segments < 0) return FLA_ERR_INVALID_ARG;
@@ -299,10 +336,109 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   return rc;
 }
 
+int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+             const float *init_state, const void *dout, const float *dfinal_state, void *dq,
+             void *dk_out, void *dv_out, float *dgate, float *dinit_state, int64_t B, int64_t H,
+             int64_t T, int64_t dk, int64_t dv, int64_t chunk, uint32_t flags, void *stream) {
+  gate_or_gamma = nonnull_decay_if_empty(gate_or_gamma, T, flags);
+  int rc = check_common(B, H, dk, dv, flags, gate_or_gamma);
+  if (rc != FLA_OK) return rc;
+  if (T < 0) return FLA_ERR_INVALID_ARG;
+  const int kind = decay_kind(flags);
+  const bool per_token_grad = kind == DECAY_GATE || kind == DECAY_TOKEN;
+  if (dgate && !per_token_grad) return FLA_ERR_INVALID_ARG; // no gradient for gamma / none
+  if (T > 0 && (!q || !k || !v || !dout || !dq || !dk_out || !dv_out)) return FLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk_out, 16) || !aligned(dv_out, 16) ||
+      !aligned(init_state, 16) || !aligned(dfinal_state, 16) || !aligned(dinit_state, 16) ||
+      !aligned(dgate, 16))
+    return FLA_ERR_INVALID_ARG;
+  if (flags & FLA_NORMALIZE) return FLA_ERR_UNSUPPORTED;
+  if (chunk != 64) return FLA_ERR_UNSUPPORTED;
+  if (dk < 64 || dv < 64) return FLA_ERR_UNSUPPORTED;
+  if (B * H > ((int64_t)1 << 26) || T > ((int64_t)1 << 40) / (B * H)) return FLA_ERR_INVALID_ARG;
+  const bool bf16 = (flags & FLA_BF16) != 0;
+  const BwdLauncher lq = find_bwd(bf16, dv, BWD_DQ, kind);
+  const BwdLauncher lk = find_bwd(bf16, dv, BWD_DK, kind);
+  const BwdLauncher lv = find_bwd(bf16, dk, BWD_DV, kind);
+  if (!lq || !lk || !lv) return FLA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nbh = B * H;
+  if (T == 0) {
+    if (dinit_state) return launch_fill(dinit_state, dfinal_state, nbh * dk * dv, s);
+    return FLA_OK;
+  }
+  const int64_t nslk = dk / kSlice, nslv = dv / kSlice;
+  if (nbh * (nslk > nslv ? nslk : nslv) >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
+
+  // workspace for the decay gradient: phi(q) dphi(q) per token and key, the final state's
+  // term per key, and (per-token decay) one partial sum per key slice and token
+  const bool want_dg = dgate != nullptr;
+  const int64_t n_rq = want_dg ? nbh * T * dk : 0;
+  const int64_t n_ft = (want_dg && dfinal_state) ? nbh * dk : 0;
+  const int64_t n_tp = (want_dg && kind == DECAY_TOKEN) ? nbh * nslk * T : 0;
+  float *ws = nullptr;
+  if (n_rq + n_ft + n_tp > 0 &&
+      hipMallocAsync(reinterpret_cast<void **>(&ws), (n_rq + n_ft + n_tp) * sizeof(float), s) != hipSuccess)
+    return FLA_ERR_DEVICE;
+
+  BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.dout = dout;
+  a.decay = gate_or_gamma;
+  a.init = init_state;
+  a.dfinal = dfinal_state;
+  a.grad_q = dq; a.grad_k = dk_out; a.grad_v = dv_out;
+  a.dgate = dgate;
+  a.dinit = dinit_state;
+  a.rq = want_dg ? ws : nullptr;
+  a.fterm = n_ft ? ws + n_rq : nullptr;
+  a.tpart = n_tp ? ws + n_rq + n_ft : nullptr;
+  a.T = T;
+  a.H = (int)H; a.dk = (int)dk; a.dv = (int)dv;
+  a.phi_elu1 = (flags & FLA_PHI_ELU1) ? 1 : 0;
+  a.want_dg = want_dg ? 1 : 0;
+
+  rc = FLA_OK;
+  // dphi(q) (forward in time; writes dq and the workspace terms)
+  a.nsl = (int)nslk; a.nunits = (int)(nbh * nslk);
+  if (lq(a, (unsigned)a.nunits, s) != hipSuccess) rc = FLA_ERR_DEVICE;
+  // dv and the initial state's gradient (reverse)
+  if (rc == FLA_OK) {
+    a.nsl = (int)nslv; a.nunits = (int)(nbh * nslv);
+    if (lv(a, (unsigned)a.nunits, s) != hipSuccess) rc = FLA_ERR_DEVICE;
+  }
+  // dphi(k) and the decay gradient (reverse)
+  if (rc == FLA_OK) {
+    a.nsl = (int)nslk; a.nunits = (int)(nbh * nslk);
+    if (lk(a, (unsigned)a.nunits, s) != hipSuccess) rc = FLA_ERR_DEVICE;
+  }
+  if (rc == FLA_OK && n_tp) {
+    const float *tp = a.tpart;
+    const float *dec = gate_or_gamma;
+    int64_t nbh_v = nbh, T_v = T;
+    int nsl_i = (int)nslk;
+    void *args[] = {&tp, &dec, &dgate, &nbh_v, &T_v, &nsl_i};
+    if (hipLaunchKernel(reinterpret_cast<const void *>(&token_dgate_kernel),
+                        dim3(blocks_for(nbh * T, 256)), dim3(256), args, 0, s) != hipSuccess)
+      rc = FLA_ERR_DEVICE;
+  }
+  if (ws && hipFreeAsync(ws, s) != hipSuccess) rc = FLA_ERR_DEVICE;
+  return rc;
+}
+
 } // namespace
 } // namespace fla
 
 extern "C" {
+
+int fla_linattn_bwd(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+                    const float *init_state, const void *dout, const float *dfinal_state,
+                    void *dq, void *dk, void *dv, float *dgate, float *dinit_state, int64_t B,
+                    int64_t H, int64_t T, int64_t dk_dim, int64_t dv_dim, int64_t chunk,
+                    uint32_t flags, void *stream) {
+  return fla::bwd_impl(q, k, v, gate_or_gamma, init_state, dout, dfinal_state, dq, dk, dv, dgate,
+                       dinit_state, B, H, T, dk_dim, dv_dim, chunk, flags, stream);
+}
 
 const char *fla_status_string(int status) {
   switch (status) {

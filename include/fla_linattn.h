@@ -114,6 +114,35 @@ int fla_linattn_step(const void *q, const void *k, const void *v, const float *g
                      float *state, void *out, int64_t B, int64_t H, int64_t dk, int64_t dv,
                      uint32_t flags, void *stream);
 
+/*
+ * fla_linattn_bwd — gradients of the forward pass (chunkwise backward), for the loss
+ * L = sum(dout (.) out) + sum(dfinal_state (.) final_state), by the reverse-mode chain rule
+ * through the recurrence above (no normaliser).
+ *
+ *   q, k, v, gate_or_gamma, init_state: the forward call's inputs (layouts above).
+ *   dout         : [B][H][T][dv], dtype of q; the gradient arriving at out.
+ *   dfinal_state : fp32 [B][H][dk][dv] gradient arriving at final_state, or NULL (zero).
+ *   dq, dk, dv   : written, shaped and typed like q, k, v.
+ *   dgate        : fp32, written with the gradient of the per-key gate [B][H][T][dk]
+ *                  (FLA_DECAY_GATE) or of the per-token decay [B][H][T] (FLA_DECAY_TOKEN);
+ *                  NULL skips it.  Must be NULL with FLA_DECAY_GAMMA (gamma is a constant
+ *                  of the model here) or without a decay.
+ *   dinit_state  : fp32 [B][H][dk][dv] written with the gradient of init_state (whether or
+ *                  not init_state was given), or NULL.
+ *   All pointers 16-byte aligned, except gamma and the per-token decay (4 bytes).
+ *   dk, dv in {64, 128, 256} (fp32: up to 128); chunk = 64; FLA_NORMALIZE is not supported.
+ *   Three chunk-scan launches (dq forward in time; dv, then dk and dgate in reverse) and,
+ *   when dgate is requested, a stream-ordered workspace of 4 (B H T dk + B H dk) bytes
+ *   (+ 4 B H T dk/64 for the per-token decay).
+ * Returns FLA_ERR_UNSUPPORTED for shapes or flags outside that set.  The gate range
+ * condition of the forward pass applies.
+ */
+int fla_linattn_bwd(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+                    const float *init_state, const void *dout, const float *dfinal_state,
+                    void *dq, void *dk, void *dv, float *dgate, float *dinit_state, int64_t B,
+                    int64_t H, int64_t T, int64_t dk_dim, int64_t dv_dim, int64_t chunk,
+                    uint32_t flags, void *stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char *fla_status_string(int status);
 

@@ -111,6 +111,33 @@ def test_step_rejects_on_host(lib, kw, expected):
     assert rc == expected
 
 
+def bwd_raw(lib, *, q=BOGUS, k=BOGUS, v=BOGUS, gate=None, init=None, do=BOGUS, dfin=None,
+            dq=BOGUS, dk=BOGUS, dv=BOGUS, dg=None, dinit=None, B=1, H=1, T=64, dkd=64, dvd=64,
+            chunk=64, flags=0):
+    return lib.fla_linattn_bwd(q, k, v, gate, init, do, dfin, dq, dk, dv, dg, dinit, B, H, T,
+                               dkd, dvd, chunk, flags, None)
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(flags=fla.FLA_NORMALIZE), fla.FLA_ERR_UNSUPPORTED),
+    (dict(chunk=32), fla.FLA_ERR_UNSUPPORTED),
+    (dict(dkd=32), fla.FLA_ERR_UNSUPPORTED),
+    (dict(dvd=16), fla.FLA_ERR_UNSUPPORTED),
+    (dict(dkd=256), fla.FLA_ERR_UNSUPPORTED),                      # fp32 tiles > LDS
+    (dict(flags=fla.FLA_DECAY_GAMMA, gate=BOGUS, dg=BOGUS), fla.FLA_ERR_INVALID_ARG),
+    (dict(dg=BOGUS), fla.FLA_ERR_INVALID_ARG),                     # no decay, no gradient
+    (dict(flags=fla.FLA_DECAY_GATE), fla.FLA_ERR_INVALID_ARG),     # gate bit, no values
+    (dict(dq=None), fla.FLA_ERR_INVALID_ARG),
+    (dict(do=None), fla.FLA_ERR_INVALID_ARG),
+    (dict(do=MISALIGNED), fla.FLA_ERR_INVALID_ARG),
+    (dict(dinit=MISALIGNED), fla.FLA_ERR_INVALID_ARG),
+    (dict(T=-1), fla.FLA_ERR_INVALID_ARG),
+    (dict(flags=1 << 8), fla.FLA_ERR_INVALID_ARG),
+])
+def test_bwd_rejects_on_host(lib, kw, expected):
+    assert bwd_raw(lib, **kw) == expected
+
+
 def test_schedule_choice(lib):
     # enough (b, h, 64-wide value slice) units: one streaming launch
     assert fla.segments_for(8, 16, 16384, 128, 128, 64, fla.FLA_BF16 | fla.FLA_DECAY_GATE) == 1

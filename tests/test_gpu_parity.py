@@ -180,6 +180,14 @@ def test_empty_sequence_copies_init():
     assert np.all(f == 0)
 
 
+@pytest.mark.parametrize("decay", ["gate", "token"])
+def test_empty_sequence_with_empty_per_token_decay(decay):
+    w, inp = small_case("bf16", decay, 64, 64, 0, init=True, seed=17)
+    o, f = run_gpu(w, inp)
+    assert o.shape == (2, 2, 0, 64)
+    assert np.array_equal(f, inp["init"].astype(np.float64))
+
+
 def test_single_token():
     w, inp = small_case("f32", "gate", 32, 16, 1, phi=True, norm=True, init=True, seed=8)
     check(w, inp, "T=1")

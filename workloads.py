@@ -174,6 +174,34 @@ def generate(w: Workload) -> dict:
     return {"q": q, "k": k, "v": v, "decay": decay, "init": init}
 
 
+def generate_grads(w: Workload, with_dfinal: bool = True) -> dict:
+    """Upstream gradients for the backward pass: dout ~ N(0,1) in the workload's dtype
+    [B,H,T,dv] and, if asked, dfinal ~ N(0,1) fp32 [B,H,dk,dv].  Streams 6 and 7 of the
+    workload's seed, so they are independent of the forward inputs."""
+    dout = _normal_tensor(w, 6, w.dv, 1.0, w.dtype == "bf16")
+    dfinal = None
+    if with_dfinal:
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 7])))
+        dfinal = g.standard_normal((w.B, w.H, w.dk, w.dv), dtype=np.float32)
+    return {"dout": dout, "dfinal": dfinal}
+
+
+def generate_grads_torch(w: Workload, device="cuda", with_dfinal: bool = True) -> dict:
+    """Device-side counterpart of generate_grads (torch's seeded generator, seed + 1)."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed + 1)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dout = torch.randn((w.B, w.H, w.T, w.dv), generator=gen, device=device,
+                       dtype=torch.float32).to(dt)
+    dfinal = None
+    if with_dfinal:
+        dfinal = torch.randn((w.B, w.H, w.dk, w.dv), generator=gen, device=device,
+                             dtype=torch.float32)
+    return {"dout": dout, "dfinal": dfinal}
+
+
 def small(name: str, **kw) -> Workload:
     """A named workload shrunk to oracle-friendly sizes (keeps dtype, decay, phi, norm)."""
     return WORKLOADS[name].with_(**kw)
