@@ -9,6 +9,10 @@ B=8, H=16, T=16384, dk=dv=128, bf16, chunk 64.
 Prints ONE JSON line: tokens/s (B*T per second), with the roofline of the fused kernel
 (algorithmic bytes per launch / average launch time from HIP events on the launch
 stream) and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+--mode bwd times the chunkwise backward instead (one step = one fla_linattn_bwd call:
+dq, dk, dv, the decay gradient and the initial state's gradient, for upstream gradients
+on the output and the final state), with the same roofline and oracle legs.
 """
 from __future__ import annotations
 
@@ -55,6 +59,27 @@ def algorithmic(w) -> tuple[float, float]:
     state = w.B * w.H * w.dk * ncol * 4
     b += state * (2 if w.init_sigma > 0 else 1)
     f = th * 2.0 * ((w.chunk + 1) / 2.0 * (w.dk + w.dv) + 2.0 * w.dk * w.dv)
+    return float(b), f
+
+
+def algorithmic_bwd(w) -> tuple[float, float]:
+    """Bytes and MFMA FLOPs of one backward pass.  Bytes: q, k, v, dout read once; dq, dk, dv
+    written once; the gate / per-token decay read once and its gradient written once
+    (gamma: read only); dfinal read, the start state read if given, dinit written.
+    FLOPs per token-head (three chunk scans, causal halves of the C x C products):
+    2 * [(C+1)/2 * (3 dv + 3 dk) + 6 dk dv]."""
+    s = 2 if w.dtype == "bf16" else 4
+    th = w.B * w.H * w.T
+    b = th * (3 * w.dk + 3 * w.dv) * s
+    if w.decay == "gate":
+        b += 2 * th * w.dk * 4
+    elif w.decay == "token":
+        b += 2 * th * 4
+    elif w.decay == "gamma":
+        b += w.H * 4
+    state = w.B * w.H * w.dk * w.dv * 4
+    b += state * (3 if w.init_sigma > 0 else 2)
+    f = th * 2.0 * ((w.chunk + 1) / 2.0 * (3 * w.dk + 3 * w.dv) + 6.0 * w.dk * w.dv)
     return float(b), f
 
 
@@ -115,6 +140,140 @@ def cpu_baseline(w, inp, out_gpu, fin_gpu, budget_s: float):
         "sample_batches": nbatch}
 
 
+def cpu_baseline_bwd(w, inp, grads, got, budget_s: float):
+    """The fp64 oracle's backward on whole batches until about budget_s, and the GPU's
+    error on that sample (max |g - g_ref| / max |g_ref| per gradient)."""
+    import numpy as np
+    import oracle
+    from workloads import to_numpy_input
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    env_threads = os.environ.get("OMP_NUM_THREADS")
+    if env_threads and env_threads.isdigit():
+        threads = max(1, min(threads, int(env_threads)))
+    dt = 0.0
+    nbatch = 0
+    err, mag = {}, {}
+    while nbatch < w.B and (nbatch == 0 or dt < budget_s):
+        sl = slice(nbatch, nbatch + 1)
+
+        def part(t):
+            return None if t is None else to_numpy_input(t[sl])
+
+        dec = inp["decay"]
+        dec_s = None if dec is None else (part(dec) if w.decay in ("gate", "token")
+                                          else to_numpy_input(dec))
+        ini = part(inp["init"])
+        t0 = time.perf_counter()
+        ref = oracle.bwd(part(inp["q"]), part(inp["k"]), part(inp["v"]), part(grads["dout"]),
+                         dec_s, w.decay, ini, part(grads["dfinal"]), phi_elu1=w.phi_elu1,
+                         nthreads=threads)
+        dt += time.perf_counter() - t0
+        for n, t in got.items():
+            if t is None or ref.get(n) is None:
+                continue
+            g = t[sl].double().cpu().numpy()
+            err[n] = max(err.get(n, 0.0), float(np.max(np.abs(g - ref[n]))))
+            mag[n] = max(mag.get(n, 0.0), float(np.max(np.abs(ref[n]))))
+        nbatch += 1
+    token_heads = w.T * w.H * nbatch
+    return {
+        "value": token_heads / dt / w.H,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"batches 0..{nbatch - 1} of {w.B}, all {w.H} heads, all {w.T} tokens "
+                  f"({token_heads} token-heads, fp64 back-propagation, {dt:.1f} s)",
+    }, {f"max_rel_err_{n}": err[n] / max(mag[n], 1e-300) for n in err} | {"sample_batches": nbatch}
+
+
+def timed(torch, step, steps, warmup, stream):
+    """Warm-up (about a second of steps unless given), then `steps` steps between HIP events
+    on the launch stream.  Returns (ms per step, warm-up steps, wall seconds)."""
+    if warmup is None:
+        warmup, t0 = 0, time.perf_counter()
+        while True:
+            step()
+            warmup += 1
+            if warmup % 8 == 0:
+                torch.cuda.synchronize()
+                if warmup >= 10 and time.perf_counter() - t0 >= 1.0:
+                    break
+    else:
+        for _ in range(warmup):
+            step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, warmup, time.perf_counter() - t_wall0
+
+
+def bench_bwd(torch, fla, w, args):
+    from workloads import generate_grads_torch, generate_torch
+
+    inp = generate_torch(w, "cuda")
+    grads = generate_grads_torch(w, "cuda")
+    stream = torch.cuda.current_stream()
+    got = {}
+
+    def step():
+        dq, dk, dv, dg, di = fla.bwd(inp["q"], inp["k"], inp["v"], grads["dout"], inp["decay"],
+                                     decay_kind=w.decay, init_state=inp["init"],
+                                     dfinal=grads["dfinal"], phi_elu1=w.phi_elu1,
+                                     chunk=w.chunk, stream=stream)
+        got.update(dq=dq, dk=dk, dv=dv, dgate=dg, dinit=di)
+
+    ms, warmup, t_wall = timed(torch, step, args.steps, args.warmup, stream)
+    alg_bytes, alg_flops = algorithmic_bwd(w)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "chunked linear-attn bwd tokens/s + roofline % (HBM), " + w.name,
+        "value": w.B * w.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded torch generator on the GPU; shapes and distributions of the workload)",
+        "config": {
+            "workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "T": w.T, "dk": w.dk,
+            "dv": w.dv, "chunk": w.chunk, "decay": w.decay,
+            "phi": "elu+1" if w.phi_elu1 else "identity", "init_state": w.init_sigma > 0,
+            "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "chunk_bwd_kernel: dq, dv, dk launches (+ per-token decay epilogue)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "mfma_tflops": alg_flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": alg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
+        },
+        "wall_s_timed_region": t_wall,
+    }
+    if not args.no_cpu_baseline:
+        cb, parity = cpu_baseline_bwd(w, inp, grads, got, args.cpu_budget)
+        res["cpu_baseline"] = cb
+        res["parity_on_sample"] = parity
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration(torch, steps, warmup):
     """A plain copy of 1 GiB: reads and writes exactly 2^30 bytes per launch."""
     n = 1 << 30
@@ -144,6 +303,8 @@ def main():
                     help="untimed steps before the timed ones (default: as many as fill about "
                          "one second, so the GPU clocks have settled)")
     ap.add_argument("--workload", default=None, help="workload name (default: headline)")
+    ap.add_argument("--mode", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward pass (default) or the chunkwise backward")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -170,6 +331,9 @@ def main():
 
     w = WORKLOADS[args.workload or HEADLINE]
     torch.cuda.set_device(0)
+    if args.mode == "bwd":
+        bench_bwd(torch, fla, w, args)
+        return
     inp = generate_torch(w, "cuda")
     out = torch.empty((w.B, w.H, w.T, w.dv), dtype=inp["q"].dtype, device="cuda")
     ncol = w.dv + (1 if w.normalize else 0)
@@ -181,32 +345,8 @@ def main():
                 init_state=inp["init"], out=out, final_state=fin, chunk=w.chunk,
                 phi_elu1=w.phi_elu1, normalize=w.normalize, stream=stream)
 
-    warmup = args.warmup
-    if warmup is None:
-        # about a second of steps (at least 10), so the GPU clocks have settled
-        warmup, t0 = 0, time.perf_counter()
-        while True:
-            step()
-            warmup += 1
-            if warmup % 8 == 0:
-                torch.cuda.synchronize()
-                if warmup >= 10 and time.perf_counter() - t0 >= 1.0:
-                    break
-    else:
-        for _ in range(warmup):
-            step()
-    torch.cuda.synchronize()
     # timed region: HIP events on the stream the kernels are launched on
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t_wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms, warmup, t_wall = timed(torch, step, args.steps, args.warmup, stream)
 
     nseg = fla.segments_for(w.B, w.H, w.T, w.dk, w.dv, w.chunk,
                             fla.flags_for(inp["q"].dtype, w.decay, w.phi_elu1, w.normalize))
