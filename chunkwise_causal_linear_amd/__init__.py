@@ -27,9 +27,11 @@ FLA_DECAY_GATE = 1 << 2
 FLA_PHI_ELU1 = 1 << 3
 FLA_NORMALIZE = 1 << 4
 FLA_DECAY_TOKEN = 1 << 5
+FLA_LAYOUT_BTHD = 1 << 6
 
 EXPORTED = ("fla_linattn_fwd", "fla_linattn_fwd_segments", "fla_linattn_step",
-            "fla_status_string", "fla_linattn_segments_for", "fla_linattn_bwd")
+            "fla_status_string", "fla_linattn_segments_for", "fla_linattn_bwd",
+            "fla_linattn_fwd_varlen")
 
 _lib = None
 
@@ -65,6 +67,9 @@ def load_library():
     lib.fla_linattn_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64,
                                     i64, u32, p]
     lib.fla_linattn_bwd.restype = c_int
+    lib.fla_linattn_fwd_varlen.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64,
+                                           u32, p]
+    lib.fla_linattn_fwd_varlen.restype = c_int
     _lib = lib
     return lib
 
@@ -106,24 +111,33 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch
         *, decay_kind: Optional[str] = None, init_state: Optional[torch.Tensor] = None,
         out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
         want_final: bool = True, chunk: int = 64, phi_elu1: bool = False,
-        normalize: bool = False, n_segments: Optional[int] = None,
+        normalize: bool = False, n_segments: Optional[int] = None, layout: str = "bhtd",
         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise forward.  q, k [B,H,T,dk]; v [B,H,T,dv] (bf16 or fp32, on the GPU);
     decay: gamma [H], gate [B,H,T,dk] or per-token scalar [B,H,T] (fp32); init/final state
-    fp32 [B,H,dk,dv(+1)].
+    fp32 [B,H,dk,dv(+1)].  layout="bthd": token-major q, k [B,T,H,dk], v and out
+    [B,T,H,dv], gate [B,T,H,dk], per-token decay [B,T,H].
     Returns (out, final_state)."""
-    B, H, T, dk = q.shape
+    if layout == "bthd":
+        B, T, H, dk = q.shape
+    elif layout == "bhtd":
+        B, H, T, dk = q.shape
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
     dv = v.shape[-1]
     kind = _decay_kind(decay, decay_kind)
     ncol = dv + (1 if normalize else 0)
     if out is None:
-        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+        out = torch.empty((B, T, H, dv) if layout == "bthd" else (B, H, T, dv), dtype=q.dtype,
+                          device=q.device)
     if final_state is None and want_final:
         final_state = torch.empty((B, H, dk, ncol), dtype=torch.float32, device=q.device)
     for t in (q, k, v, out, decay, init_state, final_state):
         if t is not None and not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
     flags = flags_for(q.dtype, kind, phi_elu1, normalize)
+    if layout == "bthd":
+        flags |= FLA_LAYOUT_BTHD
     lib = load_library()
     if n_segments is None:
         rc = lib.fla_linattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(init_state),
@@ -198,3 +212,38 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
     if rc != FLA_OK:
         raise FlaError("fla_linattn_bwd", rc)
     return dq, dkk, dvv, dgate, dinit
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+               decay: Optional[torch.Tensor] = None, *, decay_kind: Optional[str] = None,
+               init_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               final_state: Optional[torch.Tensor] = None, want_final: bool = True,
+               chunk: int = 64, phi_elu1: bool = False, normalize: bool = False,
+               stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward over packed sequences.  q, k [total,H,dk]; v [total,H,dv]; cu_seqlens int64
+    [N+1] on the GPU (sequence s = tokens cu[s]..cu[s+1]-1); decay: gamma [H], gate
+    [total,H,dk] or per-token [total,H]; states fp32 [N,H,dk,dv(+1)].  Returns (out, final)."""
+    total, H, dk = q.shape
+    dv = v.shape[-1]
+    n = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int64 or n < 1:
+        raise ValueError("cu_seqlens must be an int64 tensor of N + 1 offsets")
+    if decay_kind is None:
+        decay_kind = ("none" if decay is None
+                      else {1: "gamma", 2: "token"}.get(decay.dim(), "gate"))
+    ncol = dv + (1 if normalize else 0)
+    if out is None:
+        out = torch.empty((total, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and want_final:
+        final_state = torch.empty((n, H, dk, ncol), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, out, decay, init_state, final_state, cu_seqlens):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    flags = flags_for(q.dtype, decay_kind, phi_elu1, normalize) | FLA_LAYOUT_BTHD
+    rc = load_library().fla_linattn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(decay),
+                                               _ptr(init_state), _ptr(out), _ptr(final_state),
+                                               _ptr(cu_seqlens), n, total, H, dk, dv, chunk,
+                                               flags, _stream(stream))
+    if rc != FLA_OK:
+        raise FlaError("fla_linattn_fwd_varlen", rc)
+    return out, final_state

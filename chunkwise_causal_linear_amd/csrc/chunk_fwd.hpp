@@ -75,6 +75,9 @@ struct ChunkArgs {
   int nseg, nvs, nunits;   // nunits = B * H * nseg
   int phi_elu1;
   int state_only;          // 1: only the end state (and segment decay), no outputs
+  int bthd;                // 1: q, k, v, out, gate in token-major [B][T][H][d] (or packed
+                           //    [total][H][d] with cu_seqlens); 0: [B][H][T][d]
+  const int64_t *cu_seqlens; // packed sequences: [B + 1] token offsets (bthd only), or null
 };
 
 template <typename TIn, int DK, int C, int DECAY, bool NORM>
@@ -573,7 +576,7 @@ struct Staged {
 // The fused chunk kernel.
 
 // SO: end states only (the first pass of the segment schedule; a.state_only is 1).
-template <typename TIn, int DK, int C, int DECAY, bool NORM, bool SO>
+template <typename TIn, int DK, int C, int DECAY, bool NORM, bool SO, bool BTHD>
 __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
   using K = Cfg<TIn, DK, C, DECAY, NORM>;
   using F = Frag<TIn>;
@@ -598,9 +601,39 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
   const bool producer = wave >= K::NCW;
   constexpr bool state_only = SO;
 
+  // Token addressing.  [B][H][T][d]: the unit's tokens are contiguous rows of d.
+  // [B][T][H][d] / packed [total][H][d]: row t of head h of sequence b sits at token
+  // s0 + t of the token-major array (s0 = b T, or cu_seqlens[b], clamped to the array),
+  // so consecutive rows are H d elements apart.  Every element offset below is
+  // base + t * RS + column.
+  int64_t Tu = a.T, s0 = 0;
+  if constexpr (BTHD) {
+    const int b = bh / a.H;
+    if (a.cu_seqlens) {
+      s0 = a.cu_seqlens[b];
+      int64_t e = a.cu_seqlens[b + 1];
+      s0 = s0 < 0 ? 0 : (s0 > a.T ? a.T : s0);
+      e = e < s0 ? s0 : (e > a.T ? a.T : e);
+      Tu = e - s0;
+    } else {
+      s0 = (int64_t)b * a.T;
+    }
+  }
+  const int RS_QK = BTHD ? a.H * DK : DK;          // row strides (elements)
+  const int RS_V = BTHD ? a.H * a.dv : a.dv;
+  const int RS_T = BTHD ? a.H : 1;                 // per-token decay
+  const int64_t base_qk = BTHD ? (s0 * a.H + h) * DK : (int64_t)bh * a.T * DK;
+  const int64_t base_v = BTHD ? (s0 * a.H + h) * a.dv : (int64_t)bh * a.T * a.dv;
+  const int64_t base_t = BTHD ? s0 * a.H + h : (int64_t)bh * a.T;
+  // byte range of L rows of d elements at row stride rs
+  auto rows_bytes = [](int L, int rs, int d, int es) -> int {
+    if constexpr (BTHD) return L > 0 ? ((L - 1) * rs + d) * es : 0;
+    else return L * d * es;
+  };
+
   const int64_t t_begin = (int64_t)seg * a.seg_len;
   int64_t t_end = t_begin + a.seg_len;
-  if (t_end > a.T) t_end = a.T;
+  if (t_end > Tu) t_end = Tu;
   const int nch = t_end > t_begin ? (int)((t_end - t_begin + C - 1) / C) : 0;
 
   if constexpr (DECAY == DECAY_GAMMA) {
@@ -641,31 +674,31 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     auto load_gate = [&](St &s, int n) {
       if constexpr (DECAY == DECAY_GATE) {
         const int64_t t0 = t_begin + (int64_t)n * C;
-        const auto rs = make_rsrc(a.decay + ((int64_t)bh * a.T + t0) * DK, chunk_len(n) * DK * 4);
+        const auto rs = make_rsrc(a.decay + base_qk + t0 * RS_QK, rows_bytes(chunk_len(n), RS_QK, DK, 4));
 #pragma unroll
         for (int r = 0; r < K::RPT; ++r)
-          ld_words_buf<K::G>(s.a[r], rs, ld_on ? ((row0 + r) * DK + col0) * 4 : kDropOffset);
+          ld_words_buf<K::G>(s.a[r], rs, ld_on ? ((row0 + r) * RS_QK + col0) * 4 : kDropOffset);
       } else if constexpr (DECAY == DECAY_TOKEN) {
         // one value per row ([B][H][T])
         const int64_t t0 = t_begin + (int64_t)n * C;
-        const auto rs = make_rsrc(a.decay + (int64_t)bh * a.T + t0, chunk_len(n) * 4);
+        const auto rs = make_rsrc(a.decay + base_t + t0 * RS_T, rows_bytes(chunk_len(n), RS_T, 1, 4));
 #pragma unroll
         for (int r = 0; r < K::RPT; ++r)
-          ld_words_buf<1>(s.a[r], rs, ld_on ? (row0 + r) * 4 : kDropOffset);
+          ld_words_buf<1>(s.a[r], rs, ld_on ? (row0 + r) * RS_T * 4 : kDropOffset);
       }
     };
     // q/k row r and v row r of chunk n
     auto load_q = [&](St &s, int n, int r) {
       const int64_t t0 = t_begin + (int64_t)n * C;
-      const auto rq = make_rsrc(static_cast<const TIn *>(a.q) + ((int64_t)bh * a.T + t0) * DK,
-                                state_only ? 0 : chunk_len(n) * DK * K::ES);
-      ld_words_buf<St::QW>(s.q[r], rq, ld_on ? ((row0 + r) * DK + col0) * K::ES : kDropOffset);
+      const auto rq = make_rsrc(static_cast<const TIn *>(a.q) + base_qk + t0 * RS_QK,
+                                state_only ? 0 : rows_bytes(chunk_len(n), RS_QK, DK, K::ES));
+      ld_words_buf<St::QW>(s.q[r], rq, ld_on ? ((row0 + r) * RS_QK + col0) * K::ES : kDropOffset);
     };
     auto load_k = [&](St &s, int n, int r) {
       const int64_t t0 = t_begin + (int64_t)n * C;
-      const auto rk = make_rsrc(static_cast<const TIn *>(a.k) + ((int64_t)bh * a.T + t0) * DK,
-                                chunk_len(n) * DK * K::ES);
-      ld_words_buf<St::QW>(s.k[r], rk, ld_on ? ((row0 + r) * DK + col0) * K::ES : kDropOffset);
+      const auto rk = make_rsrc(static_cast<const TIn *>(a.k) + base_qk + t0 * RS_QK,
+                                rows_bytes(chunk_len(n), RS_QK, DK, K::ES));
+      ld_words_buf<St::QW>(s.k[r], rk, ld_on ? ((row0 + r) * RS_QK + col0) * K::ES : kDropOffset);
     };
     auto load_qk = [&](St &s, int n, int r) {
       load_q(s, n, r);
@@ -673,9 +706,9 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     };
     auto load_v = [&](St &s, int n, int r) {
       const int64_t t0 = t_begin + (int64_t)n * C;
-      const auto rs = make_rsrc(static_cast<const TIn *>(a.v) + ((int64_t)bh * a.T + t0) * a.dv,
-                                chunk_len(n) * a.dv * K::ES);
-      ld_words_buf<2 * K::ES>(s.v[r], rs, vld_on ? ((vrow0 + r) * a.dv + vs * kSlice + 8 * vcg) * K::ES : kDropOffset);
+      const auto rs = make_rsrc(static_cast<const TIn *>(a.v) + base_v + t0 * RS_V,
+                                rows_bytes(chunk_len(n), RS_V, a.dv, K::ES));
+      ld_words_buf<2 * K::ES>(s.v[r], rs, vld_on ? ((vrow0 + r) * RS_V + vs * kSlice + 8 * vcg) * K::ES : kDropOffset);
     };
     // same order as prep issues the next chunk's loads (v, gate, q/k rows): the loads
     // then retire in the order they are used
@@ -937,7 +970,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
   for (int t = 0; t < K::ET; ++t) tile_on[t] = e0 + 16 * t < a.dv;
   const bool wave_on = tile_on[0];
-  TIn *gout = static_cast<TIn *>(a.out) + (int64_t)bh * a.T * a.dv;
+  TIn *gout = static_cast<TIn *>(a.out) + base_v;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   f32x4 Hs[K::ET][K::NCB];
@@ -1250,14 +1283,14 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
 
     // output rows of chunk m: stores past row L or column dv fall outside the range
     auto out_rsrc = [&](int64_t t0, int L) {
-      return make_rsrc(gout + t0 * a.dv, state_only ? 0 : L * a.dv * K::ES);
+      return make_rsrc(gout + t0 * RS_V, state_only ? 0 : rows_bytes(L, RS_V, a.dv, K::ES));
     };
     // lane part of an output offset in a vector register, the row block and tile part
     // (uniform) in the scalar offset
-    const int out_lane = (li * a.dv + 4 * g) * K::ES;
+    const int out_lane = (li * RS_V + 4 * g) * K::ES;
     auto store_out = [&](__amdgpu_buffer_rsrc_t ors, int ib, int t, f32x4 o) {
       const int soff = __builtin_amdgcn_readfirstlane(
-          tile_on[t] ? (16 * ib * a.dv + e0 + 16 * t) * K::ES : kDropOffset);
+          tile_on[t] ? (16 * ib * RS_V + e0 + 16 * t) * K::ES : kDropOffset);
       st_out4_buf<TIn>(ors, out_lane, soff, o);
     };
 
@@ -1592,7 +1625,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           if constexpr (DECAY == DECAY_GAMMA) acc2 *= rsc;
           f32x4 o = acc[t] + acc2;
           if constexpr (NORM) o *= inv;
-          if (i < L && tile_on[t]) st_out4<TIn>(gout + (t0 + i) * a.dv + e0 + 16 * t + 4 * g, o);
+          if (i < L && tile_on[t]) st_out4<TIn>(gout + (t0 + i) * RS_V + e0 + 16 * t + 4 * g, o);
         }
       };
 

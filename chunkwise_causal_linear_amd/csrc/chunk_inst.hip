@@ -23,9 +23,13 @@ template <int C, int DECAY, bool NORM>
 hipError_t launch_impl(const ChunkArgs &a, unsigned grid, hipStream_t s) {
   ChunkArgs copy = a;
   void *args[] = {&copy};
-  const void *fn = a.state_only
-                       ? reinterpret_cast<const void *>(&chunk_fwd_kernel<TIn, DK, C, DECAY, NORM, true>)
-                       : reinterpret_cast<const void *>(&chunk_fwd_kernel<TIn, DK, C, DECAY, NORM, false>);
+  const void *fn;
+  if (a.bthd)
+    fn = a.state_only ? reinterpret_cast<const void *>(&chunk_fwd_kernel<TIn, DK, C, DECAY, NORM, true, true>)
+                      : reinterpret_cast<const void *>(&chunk_fwd_kernel<TIn, DK, C, DECAY, NORM, false, true>);
+  else
+    fn = a.state_only ? reinterpret_cast<const void *>(&chunk_fwd_kernel<TIn, DK, C, DECAY, NORM, true, false>)
+                      : reinterpret_cast<const void *>(&chunk_fwd_kernel<TIn, DK, C, DECAY, NORM, false, false>);
   return hipLaunchKernel(fn, dim3(grid), dim3(Cfg<TIn, DK, C, DECAY, NORM>::NT), args, 0, s);
 }
 

@@ -216,13 +216,17 @@ const float *nonnull_decay_if_empty(const float *decay, int64_t T, uint32_t flag
   return decay;
 }
 
+// cu_seqlens: packed sequences (token-major layout, B = number of sequences, T = total
+// tokens); null for B sequences of T tokens each.
 int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_gamma,
              const float *init_state, void *out, float *final_state, int64_t B, int64_t H,
              int64_t T, int64_t dk, int64_t dv, int64_t chunk, uint32_t flags,
-             int64_t n_segments, void *stream) {
+             int64_t n_segments, const int64_t *cu_seqlens, void *stream) {
   gate_or_gamma = nonnull_decay_if_empty(gate_or_gamma, T, flags);
   int rc = check_common(B, H, dk, dv, flags, gate_or_gamma);
   if (rc != FLA_OK) return rc;
+  const bool bthd = cu_seqlens != nullptr || (flags & FLA_LAYOUT_BTHD) != 0;
+  if (bthd && H * (dk > dv ? dk : dv) > ((int64_t)1 << 20)) return FLA_ERR_UNSUPPORTED;
   if (T < 0 || n_segments < 0) return FLA_ERR_INVALID_ARG;
   if (T > 0 && (!q || !k || !v || !out)) return FLA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
@@ -247,6 +251,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
 
   const int64_t nch = (T + chunk - 1) / chunk;
   int64_t nseg = n_segments == 0 ? auto_segments(B, H, T, dv, chunk) : n_segments;
+  if (cu_seqlens) nseg = 1; // packed sequences: one streaming workgroup per (sequence, head, slice)
   if (nseg > nch) nseg = nch;
   const int64_t seg_chunks = (nch + nseg - 1) / nseg;
   const int64_t seg_len = seg_chunks * chunk;
@@ -265,6 +270,8 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   a.H = (int)H; a.dv = (int)dv; a.ncol = (int)ncol;
   a.nseg = (int)nseg; a.nvs = (int)nvs; a.nunits = (int)nunits;
   a.phi_elu1 = (flags & FLA_PHI_ELU1) ? 1 : 0;
+  a.bthd = bthd ? 1 : 0;
+  a.cu_seqlens = cu_seqlens;
 
   if (nseg == 1) {
     // The z column is read by every value slice and written by slice 0 only: an in-place
@@ -353,7 +360,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
       !aligned(init_state, 16) || !aligned(dfinal_state, 16) || !aligned(dinit_state, 16) ||
       !aligned(dgate, 16))
     return FLA_ERR_INVALID_ARG;
-  if (flags & FLA_NORMALIZE) return FLA_ERR_UNSUPPORTED;
+  if (flags & (FLA_NORMALIZE | FLA_LAYOUT_BTHD)) return FLA_ERR_UNSUPPORTED;
   if (chunk != 64) return FLA_ERR_UNSUPPORTED;
   if (dk < 64 || dv < 64) return FLA_ERR_UNSUPPORTED;
   if (B * H > ((int64_t)1 << 26) || T > ((int64_t)1 << 40) / (B * H)) return FLA_ERR_INVALID_ARG;
@@ -455,7 +462,16 @@ int fla_linattn_fwd(const void *q, const void *k, const void *v, const float *ga
                     int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk,
                     uint32_t flags, void *stream) {
   return fla::fwd_impl(q, k, v, gate_or_gamma, init_state, out, final_state, B, H, T, dk, dv,
-                       chunk, flags, 0, stream);
+                       chunk, flags, 0, nullptr, stream);
+}
+
+int fla_linattn_fwd_varlen(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+                           const float *init_state, void *out, float *final_state,
+                           const int64_t *cu_seqlens, int64_t n_seqs, int64_t total_T, int64_t H,
+                           int64_t dk, int64_t dv, int64_t chunk, uint32_t flags, void *stream) {
+  if (!cu_seqlens || !fla::aligned(cu_seqlens, 8)) return FLA_ERR_INVALID_ARG;
+  return fla::fwd_impl(q, k, v, gate_or_gamma, init_state, out, final_state, n_seqs, H, total_T,
+                       dk, dv, chunk, flags | FLA_LAYOUT_BTHD, 0, cu_seqlens, stream);
 }
 
 int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
@@ -464,7 +480,7 @@ int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
                              int64_t dv, int64_t chunk, uint32_t flags, int64_t n_segments,
                              void *stream) {
   return fla::fwd_impl(q, k, v, gate_or_gamma, init_state, out, final_state, B, H, T, dk, dv,
-                       chunk, flags, n_segments, stream);
+                       chunk, flags, n_segments, nullptr, stream);
 }
 
 int fla_linattn_segments_for(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,

@@ -25,6 +25,9 @@
  *   token   [B][H][T]       fp32, values in (0, 1] (per-token scalar decay)
  *   state   [B][H][dk][dv + n] fp32, n = 1 with FLA_NORMALIZE (column dv holds z);
  *           this is h = S^T, so state[b][h][c][e] = S[e][c].
+ * With FLA_LAYOUT_BTHD (forward calls) the per-token tensors are token-major instead, as
+ * the projections of a [B][T][hidden] activation produce them: q, k, gate [B][T][H][dk],
+ * v, out [B][T][H][dv], per-token decay [B][T][H]; gamma and the states are unchanged.
  *
  * Ownership: every pointer belongs to the caller; the library keeps none after a call
  * returns and holds no global mutable state.  Calls are asynchronous on `stream`
@@ -56,8 +59,10 @@ enum fla_status {
 #define FLA_PHI_ELU1 (1u << 3)    /* phi(x) = elu(x) + 1 on q and k; otherwise identity */
 #define FLA_NORMALIZE (1u << 4)   /* divide by z_t^T phi(q_t); the state carries z */
 #define FLA_DECAY_TOKEN (1u << 5) /* gate_or_gamma = const float[B][H][T] (scalar per token) */
-#define FLA_ALL_FLAGS \
-  (FLA_BF16 | FLA_DECAY_GAMMA | FLA_DECAY_GATE | FLA_PHI_ELU1 | FLA_NORMALIZE | FLA_DECAY_TOKEN)
+#define FLA_LAYOUT_BTHD (1u << 6) /* token-major q, k, v, out, gate: [B][T][H][d] (see below) */
+#define FLA_ALL_FLAGS                                                                      \
+  (FLA_BF16 | FLA_DECAY_GAMMA | FLA_DECAY_GATE | FLA_PHI_ELU1 | FLA_NORMALIZE |           \
+   FLA_DECAY_TOKEN | FLA_LAYOUT_BTHD)
 
 /*
  * fla_linattn_fwd — chunkwise forward pass over T tokens.
@@ -103,12 +108,30 @@ int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
                              void *stream);
 
 /*
+ * fla_linattn_fwd_varlen — fla_linattn_fwd over packed variable-length sequences.
+ *   q, k, gate: [total_T][H][dk]; v, out: [total_T][H][dv]; per-token decay [total_T][H]
+ *   (token-major, FLA_LAYOUT_BTHD implied); sequence s owns tokens cu_seqlens[s] ..
+ *   cu_seqlens[s+1]-1.
+ *   cu_seqlens   : device int64 [n_seqs + 1], 8-byte aligned, non-decreasing from 0 to
+ *                  total_T.  Values are clamped to [0, total_T] on the device, so a bad array
+ *                  gives wrong results, never an out-of-range access.
+ *   init_state, final_state: [n_seqs][H][dk][dv + n] fp32 (one state per sequence), or NULL.
+ *   Other arguments as fla_linattn_fwd (B = n_seqs, T = total_T).  One streaming workgroup
+ *   per (sequence, head, 64-wide value slice); sequences are independent.
+ */
+int fla_linattn_fwd_varlen(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+                           const float *init_state, void *out, float *final_state,
+                           const int64_t *cu_seqlens, int64_t n_seqs, int64_t total_T, int64_t H,
+                           int64_t dk, int64_t dv, int64_t chunk, uint32_t flags, void *stream);
+
+/*
  * fla_linattn_step — one token of recurrent decoding (the T == 1 case of the forward
  * pass), updating the state in place.
  *   q, k : [B][H][dk]; v, out: [B][H][dv] (bf16 with FLA_BF16, else fp32); 16-byte aligned.
  *   gate_or_gamma: gamma [H], gate [B][H][dk] or token [B][H] per the decay bit, else NULL.
  *   state: fp32 [B][H][dk][dv+n], read and written (required).
- *   dk, dv in {16, 32, 64, 128, 256}.
+ *   dk, dv in {16, 32, 64, 128, 256}.  One token is laid out the same way in either
+ *   layout, so FLA_LAYOUT_BTHD changes nothing here.
  */
 int fla_linattn_step(const void *q, const void *k, const void *v, const float *gate_or_gamma,
                      float *state, void *out, int64_t B, int64_t H, int64_t dk, int64_t dv,
@@ -134,7 +157,8 @@ int fla_linattn_step(const void *q, const void *k, const void *v, const float *g
  *   Three chunk-scan launches (dq forward in time; dv, then dk and dgate in reverse) and,
  *   when dgate is requested, a stream-ordered workspace of 4 (B H T dk + B H dk) bytes
  *   (+ 4 B H T dk/64 for the per-token decay).
- * Returns FLA_ERR_UNSUPPORTED for shapes or flags outside that set.  The gate range
+ * Returns FLA_ERR_UNSUPPORTED for shapes or flags outside that set (also for
+ * FLA_LAYOUT_BTHD: the backward takes the [B][H][T][d] layout).  The gate range
  * condition of the forward pass applies.
  */
 int fla_linattn_bwd(const void *q, const void *k, const void *v, const float *gate_or_gamma,

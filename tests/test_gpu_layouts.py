@@ -1,0 +1,159 @@
+"""GPU parity of the token-major layout ([B][T][H][d], FLA_LAYOUT_BTHD) and of packed
+variable-length sequences (fla_linattn_fwd_varlen) against the fp64 oracle, and against
+the [B][H][T][d] path: the same arithmetic on the same values, so results must agree
+bit for bit.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from parity_util import TOL, rel_err, to_device, to_host
+from workloads import Workload, generate
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import chunkwise_causal_linear_amd as fla  # noqa: E402
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def case(dtype, decay, dk, dv, T, *, B=2, H=3, chunk=64, phi=False, norm=False, init=True,
+         seed=0):
+    w = Workload("layout", B, H, T, dk, dv, chunk, dtype, decay, phi, norm,
+                 1.0 if dtype == "f32" else dk ** -0.5, 0.1 if init else 0.0,
+                 gamma_exp="1-2^(-5-h)", seed=seed)
+    return w, generate(w)
+
+
+def bthd(x):
+    """[B,H,T,...] -> [B,T,H,...] (contiguous)."""
+    return None if x is None else np.ascontiguousarray(np.swapaxes(x, 1, 2))
+
+
+def dev(w, x):
+    return to_device(x, bf16=(w.dtype == "bf16"))
+
+
+def run_bhtd(w, inp, **kw):
+    out, fin = fla.fwd(dev(w, inp["q"]), dev(w, inp["k"]), dev(w, inp["v"]),
+                       to_device(inp["decay"]), decay_kind=w.decay,
+                       init_state=to_device(inp["init"]), chunk=w.chunk, phi_elu1=w.phi_elu1,
+                       normalize=w.normalize, **kw)
+    torch.cuda.synchronize()
+    return to_host(out), to_host(fin)
+
+
+def run_bthd(w, inp, **kw):
+    dec = inp["decay"] if w.decay in ("none", "gamma") else bthd(inp["decay"])
+    out, fin = fla.fwd(dev(w, bthd(inp["q"])), dev(w, bthd(inp["k"])), dev(w, bthd(inp["v"])),
+                       to_device(dec), decay_kind=w.decay, init_state=to_device(inp["init"]),
+                       chunk=w.chunk, phi_elu1=w.phi_elu1, normalize=w.normalize,
+                       layout="bthd", **kw)
+    torch.cuda.synchronize()
+    return np.swapaxes(to_host(out), 1, 2), to_host(fin)
+
+
+COMBOS = list(itertools.product(["f32", "bf16"], ["none", "gamma", "gate", "token"],
+                                [False, True]))
+
+
+@pytest.mark.parametrize("dtype,decay,norm", COMBOS)
+def test_bthd_matches_bhtd_and_oracle(dtype, decay, norm):
+    i = COMBOS.index((dtype, decay, norm))
+    w, inp = case(dtype, decay, 64, 128, 3 * 64 + 9, phi=norm, norm=norm, seed=700 + i)
+    say(f"[bthd] {dtype} {decay} norm={norm}")
+    o1, f1 = run_bthd(w, inp)
+    o0, f0 = run_bhtd(w, inp)
+    assert np.array_equal(o1, o0) and np.array_equal(f1, f0)
+    ro, rf = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["decay"], w.decay, inp["init"],
+                        phi_elu1=w.phi_elu1, normalize=w.normalize)
+    assert rel_err(o1, ro) <= TOL[dtype] and rel_err(f1, rf) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dk,dv,chunk", [(128, 128, 64), (256, 64, 32), (32, 256, 128),
+                                         (16, 16, 16)])
+def test_bthd_shapes(dk, dv, chunk):
+    w, inp = case("bf16", "gate", dk, dv, 2 * chunk + 5, chunk=chunk, seed=720 + dk + dv)
+    say(f"[bthd] dk={dk} dv={dv} C={chunk}")
+    o1, f1 = run_bthd(w, inp)
+    o0, f0 = run_bhtd(w, inp)
+    assert np.array_equal(o1, o0) and np.array_equal(f1, f0)
+
+
+@pytest.mark.parametrize("nseg", [2, 5])
+def test_bthd_segments(nseg):
+    w, inp = case("bf16", "gamma", 128, 128, 20 * 64 + 3, B=1, H=2, seed=740 + nseg)
+    say(f"[bthd] segments={nseg}")
+    o1, f1 = run_bthd(w, inp, n_segments=nseg)
+    o0, f0 = run_bhtd(w, inp, n_segments=nseg)
+    assert np.array_equal(o1, o0) and np.array_equal(f1, f0)
+
+
+LENGTHS = [0, 1, 63, 64, 65, 200, 7, 129]
+
+
+def pack(w, inp, lengths):
+    """Per-sequence BHTD inputs (B=1) from one long draw, packed token-major."""
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    seqs = []
+    for s in range(len(lengths)):
+        sl = slice(int(cu[s]), int(cu[s + 1]))
+        d = {n: inp[n][:, :, sl] for n in ("q", "k", "v")}
+        d["decay"] = (inp["decay"] if w.decay in ("none", "gamma")
+                      else inp["decay"][:, :, sl])
+        seqs.append(d)
+    packed = {n: np.ascontiguousarray(np.swapaxes(inp[n][0], 0, 1)) for n in ("q", "k", "v")}
+    packed["decay"] = (inp["decay"] if w.decay in ("none", "gamma")
+                       else np.ascontiguousarray(np.swapaxes(inp["decay"][0], 0, 1)))
+    return cu, seqs, packed
+
+
+@pytest.mark.parametrize("dtype,decay,norm", [("bf16", "gate", False), ("f32", "token", True),
+                                              ("bf16", "gamma", False), ("f32", "none", True)])
+def test_varlen(dtype, decay, norm):
+    i = ["gate", "token", "gamma", "none"].index(decay)
+    total = sum(LENGTHS)
+    w, inp = case(dtype, decay, 64, 128, total, B=1, H=2, phi=norm, norm=norm, init=False,
+                  seed=760 + i)
+    cu, seqs, packed = pack(w, inp, LENGTHS)
+    ncol = w.dv + (1 if norm else 0)
+    rng = np.random.default_rng(761 + i)
+    init = (0.1 * rng.standard_normal((len(LENGTHS), w.H, w.dk, ncol))).astype(np.float32)
+    say(f"[varlen] {dtype} {decay} norm={norm} lengths={LENGTHS}")
+    out, fin = fla.fwd_varlen(dev(w, packed["q"]), dev(w, packed["k"]), dev(w, packed["v"]),
+                              to_device(cu), to_device(packed["decay"]), decay_kind=decay,
+                              init_state=to_device(init), phi_elu1=norm, normalize=norm)
+    torch.cuda.synchronize()
+    out, fin = to_host(out), to_host(fin)
+    for s, d in enumerate(seqs):
+        o_s = np.swapaxes(out[cu[s]:cu[s + 1]], 0, 1)[None]
+        ws = w.with_(T=LENGTHS[s])
+        dd = dict(d, init=init[s:s + 1])
+        o0, f0 = run_bhtd(ws, dd)
+        assert np.array_equal(o_s, o0), s
+        assert np.array_equal(fin[s:s + 1], f0), s
+        ro, rf = oracle.fwd(d["q"], d["k"], d["v"], d["decay"], decay, init[s:s + 1],
+                            phi_elu1=norm, normalize=norm)
+        assert rel_err(o_s, ro) <= TOL[dtype] and rel_err(fin[s:s + 1], rf) <= TOL[dtype], s
+
+
+def test_varlen_bad_offsets_are_clamped():
+    """Offsets outside [0, total] or decreasing are clamped: no fault, sequences of
+    length zero keep their initial state."""
+    w, inp = case("f32", "none", 64, 64, 100, B=1, H=1, init=False, seed=780)
+    cu = np.array([0, 50, 40, 1000, -5], dtype=np.int64)
+    _, _, packed = pack(w, inp, [100])
+    out, fin = fla.fwd_varlen(dev(w, packed["q"]), dev(w, packed["k"]), dev(w, packed["v"]),
+                              to_device(cu))
+    torch.cuda.synchronize()
+    fin = to_host(fin)
+    assert np.all(np.isfinite(fin))
+    assert np.all(fin[1] == 0) and np.all(fin[3] == 0)   # [50, 50) and [100, 100)
