@@ -29,8 +29,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+# the forward kernel's sources: counters taken on another version of them do not apply
 KERNEL_SOURCES = [os.path.join(ROOT, "chunkwise_causal_linear_amd", "csrc", f)
-                  for f in ("chunk_fwd.hpp", "chunk_inst.hip", "fla_api.hip")]
+                  for f in ("chunk_fwd.hpp", "chunk_inst.hip", "dispatch.hpp")]
 
 
 def kernel_source_hash() -> str:
@@ -274,6 +275,97 @@ def bench_bwd(torch, fla, w, args):
     print(json.dumps(res), flush=True)
 
 
+def bench_varlen(torch, fla, args):
+    """Forward over packed variable-length sequences (one fla_linattn_fwd_varlen call)."""
+    import numpy as np
+    import oracle
+    from workloads import generate_torch, to_numpy_input, varlen_workload
+
+    w, lengths = varlen_workload(args.varlen)
+    cu_h = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    n = len(lengths)
+    inp = generate_torch(w, "cuda")       # [1, H, total, d]: one long draw, then packed
+    packed = {k: inp[k][0].transpose(0, 1).contiguous() for k in ("q", "k", "v")}
+    packed["decay"] = (inp["decay"][0].transpose(0, 1).contiguous()
+                       if w.decay in ("gate", "token") else inp["decay"])
+    cu = torch.from_numpy(cu_h).cuda()
+    out = torch.empty((w.T, w.H, w.dv), dtype=inp["q"].dtype, device="cuda")
+    fin = torch.empty((n, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fla.fwd_varlen(packed["q"], packed["k"], packed["v"], cu, packed["decay"],
+                       decay_kind=w.decay, out=out, final_state=fin, chunk=w.chunk,
+                       stream=stream)
+
+    ms, warmup, t_wall = timed(torch, step, args.steps, args.warmup, stream)
+    alg_bytes, alg_flops = algorithmic(w)
+    alg_bytes += (n - 1) * w.H * w.dk * w.dv * 4  # one end state per sequence
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "chunked linear-attn fwd tokens/s + roofline % (HBM), packed sequences, " + w.name,
+        "value": w.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded torch generator on the GPU; log-uniform sequence lengths)",
+        "config": {
+            "workload": w.name, "n_seqs": n, "total_tokens": int(w.T), "H": w.H, "dk": w.dk,
+            "dv": w.dv, "chunk": w.chunk, "decay": w.decay, "layout": "packed [total][H][d]",
+            "len_min": int(lengths.min()), "len_max": int(lengths.max()),
+            "len_mean": float(lengths.mean()), "global_batch": n, "seq_len": int(lengths.max()),
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel_name(w) + " [token-major, packed]",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "mfma_tflops": alg_flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": alg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
+        },
+        "wall_s_timed_region": t_wall,
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        dt, eo, mo, ef, mf, done, toks = 0.0, 0.0, 0.0, 0.0, 0.0, 0, 0
+        while done < n and (done == 0 or dt < args.cpu_budget):
+            s0, s1 = int(cu_h[done]), int(cu_h[done + 1])
+            part = lambda t: to_numpy_input(t[:, :, s0:s1])
+            dec = inp["decay"]
+            dec_s = part(dec) if w.decay in ("gate", "token") else (None if dec is None else to_numpy_input(dec))
+            t0 = time.perf_counter()
+            ro, rf = oracle.fwd(part(inp["q"]), part(inp["k"]), part(inp["v"]), dec_s, w.decay,
+                                None, nthreads=threads)
+            dt += time.perf_counter() - t0
+            o = out[s0:s1].transpose(0, 1)[None].float().cpu().numpy().astype(np.float64)
+            f = fin[done:done + 1].cpu().numpy().astype(np.float64)
+            eo, mo = max(eo, float(np.max(np.abs(o - ro))) if s1 > s0 else 0.0), max(mo, float(np.max(np.abs(ro))) if s1 > s0 else 0.0)
+            ef, mf = max(ef, float(np.max(np.abs(f - rf)))), max(mf, float(np.max(np.abs(rf))))
+            toks += s1 - s0
+            done += 1
+        res["cpu_baseline"] = {"value": toks / dt, "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"sequences 0..{done - 1} of {n} ({toks} tokens, all "
+                                         f"{w.H} heads, fp64 recurrence, {dt:.1f} s)"}
+        res["parity_on_sample"] = {"max_rel_err_out": eo / max(mo, 1e-300),
+                                   "max_rel_err_final": ef / max(mf, 1e-300),
+                                   "sample_sequences": done}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration(torch, steps, warmup):
     """A plain copy of 1 GiB: reads and writes exactly 2^30 bytes per launch."""
     n = 1 << 30
@@ -305,6 +397,11 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: headline)")
     ap.add_argument("--mode", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward pass (default) or the chunkwise backward")
+    ap.add_argument("--layout", choices=("bhtd", "bthd"), default="bhtd",
+                    help="forward: [B][H][T][d] (default) or token-major [B][T][H][d] inputs")
+    ap.add_argument("--varlen", default=None,
+                    help="forward over packed variable-length sequences (workload name, "
+                         "e.g. varlen_gla_d128)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -329,21 +426,38 @@ def main():
     import chunkwise_causal_linear_amd as fla
     from workloads import HEADLINE, WORKLOADS, generate_torch
 
-    w = WORKLOADS[args.workload or HEADLINE]
     torch.cuda.set_device(0)
+    if args.varlen:
+        bench_varlen(torch, fla, args)
+        return
+    w = WORKLOADS[args.workload or HEADLINE]
     if args.mode == "bwd":
         bench_bwd(torch, fla, w, args)
         return
     inp = generate_torch(w, "cuda")
-    out = torch.empty((w.B, w.H, w.T, w.dv), dtype=inp["q"].dtype, device="cuda")
     ncol = w.dv + (1 if w.normalize else 0)
     fin = torch.empty((w.B, w.H, w.dk, ncol), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.layout == "bthd":
+        # the same values in token-major order; the oracle leg reads [B][H][T][d] views
+        tin = {n: (None if inp[n] is None else inp[n].transpose(1, 2).contiguous())
+               for n in ("q", "k", "v")}
+        tin["decay"] = (inp["decay"].transpose(1, 2).contiguous()
+                        if w.decay in ("gate", "token") else inp["decay"])
+        out_t = torch.empty((w.B, w.T, w.H, w.dv), dtype=inp["q"].dtype, device="cuda")
+        out = out_t.transpose(1, 2)
 
-    def step():
-        fla.fwd(inp["q"], inp["k"], inp["v"], inp["decay"], decay_kind=w.decay,
-                init_state=inp["init"], out=out, final_state=fin, chunk=w.chunk,
-                phi_elu1=w.phi_elu1, normalize=w.normalize, stream=stream)
+        def step():
+            fla.fwd(tin["q"], tin["k"], tin["v"], tin["decay"], decay_kind=w.decay,
+                    init_state=inp["init"], out=out_t, final_state=fin, chunk=w.chunk,
+                    phi_elu1=w.phi_elu1, normalize=w.normalize, layout="bthd", stream=stream)
+    else:
+        out = torch.empty((w.B, w.H, w.T, w.dv), dtype=inp["q"].dtype, device="cuda")
+
+        def step():
+            fla.fwd(inp["q"], inp["k"], inp["v"], inp["decay"], decay_kind=w.decay,
+                    init_state=inp["init"], out=out, final_state=fin, chunk=w.chunk,
+                    phi_elu1=w.phi_elu1, normalize=w.normalize, stream=stream)
 
     # timed region: HIP events on the stream the kernels are launched on
     ms, warmup, t_wall = timed(torch, step, args.steps, args.warmup, stream)
@@ -380,6 +494,7 @@ def main():
             "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
             "chunk": w.chunk, "decay": w.decay, "phi": "elu+1" if w.phi_elu1 else "identity",
             "normalize": w.normalize, "init_state": w.init_sigma > 0, "segments": nseg,
+            "layout": "[B][T][H][d]" if args.layout == "bthd" else "[B][H][T][d]",
             "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU",
         },
         "roofline": {

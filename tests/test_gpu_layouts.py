@@ -157,3 +157,39 @@ def test_varlen_bad_offsets_are_clamped():
     fin = to_host(fin)
     assert np.all(np.isfinite(fin))
     assert np.all(fin[1] == 0) and np.all(fin[3] == 0)   # [50, 50) and [100, 100)
+
+
+def test_full_size_bthd_headline_matches_bhtd():
+    """The GLA workload at full size in token-major order: bitwise the [B][H][T][d] result."""
+    from workloads import WORKLOADS, generate_torch
+    w = WORKLOADS["gla_d128"]
+    say(f"[bthd-full] {w}")
+    inp = generate_torch(w, "cuda")
+    o0, f0 = fla.fwd(inp["q"], inp["k"], inp["v"], inp["decay"], decay_kind="gate")
+    t = {n: inp[n].transpose(1, 2).contiguous() for n in ("q", "k", "v", "decay")}
+    o1, f1 = fla.fwd(t["q"], t["k"], t["v"], t["decay"], decay_kind="gate", layout="bthd")
+    torch.cuda.synchronize()
+    assert torch.equal(o1.transpose(1, 2), o0) and torch.equal(f1, f0)
+
+
+def test_full_size_varlen_workload():
+    """The packed-sequence workload in the launch configuration bench.py times; the oracle
+    checks the longest, the shortest and the last sequence."""
+    from workloads import generate_torch, to_numpy_input, varlen_workload
+    w, lengths = varlen_workload("varlen_gla_d128")
+    say(f"[varlen-full] {w.name}: {len(lengths)} sequences, {w.T} tokens")
+    cu_h = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    inp = generate_torch(w, "cuda")
+    packed = {k: inp[k][0].transpose(0, 1).contiguous() for k in ("q", "k", "v", "decay")}
+    out, fin = fla.fwd_varlen(packed["q"], packed["k"], packed["v"], to_device(cu_h),
+                              packed["decay"], decay_kind="gate")
+    torch.cuda.synchronize()
+    for s in sorted({int(np.argmax(lengths)), int(np.argmin(lengths)), len(lengths) - 1}):
+        s0, s1 = int(cu_h[s]), int(cu_h[s + 1])
+        part = lambda t: to_numpy_input(t[:, :, s0:s1])
+        ro, rf = oracle.fwd(part(inp["q"]), part(inp["k"]), part(inp["v"]), part(inp["decay"]),
+                            "gate", None)
+        o = to_host(out[s0:s1].transpose(0, 1)[None])
+        eo, ef = rel_err(o, ro), rel_err(to_host(fin[s:s + 1]), rf)
+        say(f"[varlen-full] sequence {s} ({s1 - s0} tokens): out {eo:.2e} final {ef:.2e}")
+        assert eo <= TOL["bf16"] and ef <= TOL["bf16"]

@@ -84,6 +84,29 @@ WORKLOADS = {
 # The headline throughput workload.
 HEADLINE = "gla_d128"
 
+# Packed variable-length sequences (token-major [total][H][d]): the GLA workload's head
+# shape over n_seqs sequences whose lengths are log-uniform in [lo, hi] (seeded).
+VARLEN = {
+    "varlen_gla_d128": dict(H=16, dk=128, dv=128, chunk=64, dtype="bf16", decay=DECAY_GATE,
+                            n_seqs=24, lo=64, hi=16384, seed=1007),
+}
+
+
+def varlen_lengths(n_seqs: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Sequence lengths, log-uniform in [lo, hi], int64."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 8])))
+    x = np.exp(g.uniform(np.log(lo), np.log(hi), n_seqs))
+    return np.rint(x).astype(np.int64)
+
+
+def varlen_workload(name: str):
+    """(Workload over the concatenated tokens with B = 1, lengths) for a VARLEN entry."""
+    d = VARLEN[name]
+    lengths = varlen_lengths(d["n_seqs"], d["lo"], d["hi"], d["seed"])
+    w = Workload(name, 1, d["H"], int(lengths.sum()), d["dk"], d["dv"], d["chunk"], d["dtype"],
+                 d["decay"], False, False, 1.0 / math.sqrt(d["dk"]), 0.0, seed=d["seed"])
+    return w, lengths
+
 
 def gamma_for(w: Workload) -> Optional[np.ndarray]:
     if w.decay != DECAY_GAMMA:
