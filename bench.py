@@ -84,10 +84,10 @@ def algorithmic_bwd(w) -> tuple[float, float]:
     return float(b), f
 
 
-def kernel_name(w) -> str:
+def kernel_name(w, bthd: bool = False) -> str:
     t = "__bf16" if w.dtype == "bf16" else "float"
     d = {"none": 0, "gamma": 1, "gate": 2, "token": 3}[w.decay]
-    return f"chunk_fwd_kernel<{t}, {w.dk}, {w.chunk}, {d}, {str(w.normalize).lower()}, false>"
+    return f"chunk_fwd_kernel<{t}, {w.dk}, {w.chunk}, {d}, {str(w.normalize).lower()}, false, {'true' if bthd else 'false'}>"
 
 
 def cpu_baseline(w, inp, out_gpu, fin_gpu, budget_s: float):
@@ -324,7 +324,7 @@ def bench_varlen(torch, fla, args):
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": kernel_name(w) + " [token-major, packed]",
+            "kernel": kernel_name(w, True) + " [packed sequences]",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -471,7 +471,7 @@ def main():
     try:
         with open(TRAFFIC_FILE) as f:
             tc = json.load(f)
-        rec = tc.get("workloads", {}).get(w.name)
+        rec = tc.get("workloads", {}).get(w.name) if args.layout == "bhtd" else None
         if rec and tc.get("kernel_source_hash") == kernel_source_hash():
             traffic = rec.get("hbm_bytes_per_step")
     except (OSError, ValueError):
@@ -499,7 +499,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": kernel_name(w) + (" (+ segment passes)" if nseg > 1 else ""),
+            "kernel": kernel_name(w, args.layout == "bthd") + (" (+ segment passes)" if nseg > 1 else ""),
             "achieved": achieved_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
