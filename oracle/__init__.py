@@ -11,6 +11,9 @@ fixture under tests/golden/, split/resume, chained single steps and linearity.
 The backward (``bwd``, back-propagation through the same recurrence in C) is pinned in
 tests/test_oracle_bwd_pins.py by central finite differences of the pinned forward and by
 the closed-form matrix gradients of plain causal linear attention.
+The gated delta rule (``gdn_fwd``, C) is pinned in tests/test_oracle_gdn_pins.py by exact
+recall, the reduction to decayed linear attention for orthogonal keys, the beta = 0
+closed form and an independent chunked (UT-transform) form.
 """
 from __future__ import annotations
 
@@ -57,6 +60,9 @@ def _load():
         lib.oracle_bwd.argtypes = [p, p, p, c_int, p, c_int, p, p, p, p, p, p, p, p,
                                    i64, i64, i64, i64, i64, c_int, c_int]
         lib.oracle_bwd.restype = c_int
+        lib.oracle_gdn_fwd.argtypes = [p, p, p, c_int, p, p, p, p, p, i64, i64, i64, i64, i64,
+                                       c_int]
+        lib.oracle_gdn_fwd.restype = c_int
         _lib = lib
     return _lib
 
@@ -191,3 +197,31 @@ def bwd(q, k, v, dout, decay=None, decay_kind="none", init=None, dfinal=None, *,
     if rc != 0:
         raise RuntimeError("oracle_bwd failed")
     return {"dq": dq, "dk": dkk, "dv": dvv, "dgate": dg, "dinit": dini}
+
+
+def gdn_fwd(q, k, v, alpha, beta, init=None, *, want_out=True, want_final=True, nthreads=0):
+    """Gated delta rule, token by token.  q, k [B,H,T,dk]; v [B,H,T,dv] (fp32 or bf16 bits);
+    alpha, beta fp32 [B,H,T]; init [B,H,dk,dv] or None.  Returns (out fp64 [B,H,T,dv],
+    final fp64 [B,H,dk,dv])."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("q, k, v must share one dtype")
+    B, H, T, dk = q.shape
+    dv = v.shape[3]
+    al = np.ascontiguousarray(alpha, dtype=np.float32)
+    be = np.ascontiguousarray(beta, dtype=np.float32)
+    if al.shape != (B, H, T) or be.shape != (B, H, T):
+        raise ValueError("alpha and beta must be [B,H,T]")
+    ini = None if init is None else np.ascontiguousarray(init, dtype=np.float64)
+    if ini is not None and ini.shape != (B, H, dk, dv):
+        raise ValueError(f"init must be {(B, H, dk, dv)}")
+    out = np.empty((B, H, T, dv)) if want_out else None
+    fin = np.empty((B, H, dk, dv)) if want_final else None
+    rc = _load().oracle_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(al), _ptr(be), _ptr(ini),
+                                _ptr(out), _ptr(fin), B, H, T, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_gdn_fwd failed")
+    return out, fin

@@ -124,3 +124,44 @@ def parallel(q, k, v, decay=None, kind="none", init=None, *, phi_elu1=False,
         if normalize:
             den = den + (Qd @ h0[..., dv:]).squeeze(-1)
     return num / den[..., None] if normalize else num
+
+
+def gdn_chunked(q, k, v, alpha, beta, init=None, *, chunk=16):
+    """Gated delta rule in chunk form (an independent restatement used to pin the recurrent
+    oracle).  Writing the update as h_t = alpha_t h_{t-1} + k^_t u_t^T (h = S^T) with the
+    pseudo-value u_t = beta_t (v_t - alpha_t h_{t-1}^T k^_t), the u of one chunk solve the
+    unit lower-triangular system (I + A) U = diag(beta) V - diag(beta g) K^ H with
+    A_tj = beta_t (g_t / g_j) k^_t . k^_j (j < t) and g the cumulative product of alpha in
+    the chunk; then O = diag(g) Q H + (M (.) Q K^^T) U with M_tj = g_t / g_j (j <= t), and
+    H <- g_L H + (diag(g_L / g) K^)^T U.  fp64, numpy solve."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    al = np.asarray(alpha, dtype=np.float64)
+    be = np.asarray(beta, dtype=np.float64)
+    B, H, T, dk = q.shape
+    dv = v.shape[3]
+    out = np.zeros((B, H, T, dv))
+    fin = np.zeros((B, H, dk, dv))
+    nrm = np.maximum(np.sqrt(np.sum(k * k, axis=-1, keepdims=True)), 1e-12)
+    kh = k / nrm
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk, dv)) if init is None else np.array(init[b, h], dtype=np.float64)
+            for t0 in range(0, T, chunk):
+                sl = slice(t0, min(T, t0 + chunk))
+                Q, K, V = q[b, h, sl], kh[b, h, sl], v[b, h, sl]
+                a, bt = al[b, h, sl], be[b, h, sl]
+                L = Q.shape[0]
+                g = np.cumprod(a)
+                ratio = g[:, None] / g[None, :]
+                A = np.tril(bt[:, None] * ratio * (K @ K.T), -1)
+                rhs_v = bt[:, None] * V
+                rhs_k = (bt * g)[:, None] * K
+                Tm = np.linalg.solve(np.eye(L) + A, np.eye(L))
+                U = Tm @ rhs_v - (Tm @ rhs_k) @ S
+                M = np.tril(ratio)
+                out[b, h, sl] = g[:, None] * (Q @ S) + (M * (Q @ K.T)) @ U
+                S = g[-1] * S + ((g[-1] / g)[:, None] * K).T @ U
+            fin[b, h] = S
+    return out, fin

@@ -356,3 +356,92 @@ int oracle_bwd(const void *q, const void *k, const void *v, int dtype, const flo
   free(hs); free(pq); free(pk); free(pg); free(gall);
   return bad ? -1 : 0;
 }
+
+/*
+ * oracle_gdn_fwd: the gated delta rule, token by token, in fp64 (textbook chapter 1.6,
+ * section "gated delta rule"): with the unit-norm key k^_t = k_t / max(|k_t|, 1e-12),
+ *     S_t = alpha_t S_{t-1} (I - beta_t k^_t k^_t^T) + beta_t v_t k^_t^T,   o_t = S_t q_t,
+ * i.e. decay the memory, remove what it stores under k^_t (a beta_t share of the
+ * prediction S k^_t) and write beta_t v_t there.  q is used as given.  The state is kept
+ * as h = S^T ([dk][dv]); value rows of S (columns e of h) evolve independently, so blocks
+ * of 16 of them run in parallel.
+ *   q, k: [B][H][T][dk]; v: [B][H][T][dv] (fp32 or bf16 bits); alpha, beta: fp32 [B][H][T].
+ *   init, final_state: fp64 [B][H][dk][dv] or NULL (final may alias init).
+ *   out: fp64 [B][H][T][dv] or NULL.  Returns 0, or -1 on bad arguments or memory.
+ */
+int oracle_gdn_fwd(const void *q, const void *k, const void *v, int dtype, const float *alpha,
+                   const float *beta, const double *init, double *out, double *final_state,
+                   int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int nthreads) {
+  if (!q || !k || !v || !alpha || !beta || B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1) return -1;
+  const int64_t nblk = (dv + EBLK - 1) / EBLK;
+  const int64_t ntask = B * H * nblk;
+  double *init_copy = NULL;
+  if (init && init == final_state) {
+    size_t n = (size_t)(B * H * dk * dv);
+    init_copy = (double *)malloc(n * sizeof(double));
+    if (!init_copy) return -1;
+    memcpy(init_copy, init, n * sizeof(double));
+    init = init_copy;
+  }
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t task = 0; task < ntask; ++task) {
+    const int64_t bh = task / nblk, eb = task % nblk;
+    const int64_t e0 = eb * EBLK, ne = (dv - e0) < EBLK ? (dv - e0) : EBLK;
+    double *S = (double *)malloc(sizeof(double) * (size_t)(EBLK * dk)); /* S[e][c] */
+    double *kh = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *qv = (double *)malloc(sizeof(double) * (size_t)dk);
+    if (!S || !kh || !qv) {
+#pragma omp atomic write
+      bad = 1;
+      free(S); free(kh); free(qv);
+      continue;
+    }
+    const double *h0 = init ? init + bh * dk * dv : NULL;
+    for (int64_t e = 0; e < ne; ++e)
+      for (int64_t c = 0; c < dk; ++c) S[e * dk + c] = h0 ? h0[c * dv + e0 + e] : 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      const int64_t qk_off = (bh * T + t) * dk, v_off = (bh * T + t) * dv;
+      double nrm = 0.0;
+      for (int64_t c = 0; c < dk; ++c) {
+        kh[c] = widen(k, dtype, qk_off + c);
+        qv[c] = widen(q, dtype, qk_off + c);
+        nrm += kh[c] * kh[c];
+      }
+      nrm = sqrt(nrm);
+      const double den = nrm > 1e-12 ? nrm : 1e-12;
+      for (int64_t c = 0; c < dk; ++c) kh[c] /= den;
+      const double al = (double)alpha[bh * T + t], be = (double)beta[bh * T + t];
+      for (int64_t e = 0; e < ne; ++e) {
+        double *Se = S + e * dk;
+        double pred = 0.0; /* (S_{t-1} k^)_e */
+        for (int64_t c = 0; c < dk; ++c) pred += Se[c] * kh[c];
+        const double ve = widen(v, dtype, v_off + e0 + e);
+        for (int64_t c = 0; c < dk; ++c)
+          Se[c] = al * (Se[c] - be * pred * kh[c]) + be * ve * kh[c];
+      }
+      if (out) {
+        double *o = out + (bh * T + t) * dv + e0;
+        for (int64_t e = 0; e < ne; ++e) {
+          const double *Se = S + e * dk;
+          double s = 0.0;
+          for (int64_t c = 0; c < dk; ++c) s += Se[c] * qv[c];
+          o[e] = s;
+        }
+      }
+    }
+    if (final_state) {
+      double *hf = final_state + bh * dk * dv;
+      for (int64_t e = 0; e < ne; ++e)
+        for (int64_t c = 0; c < dk; ++c) hf[c * dv + e0 + e] = S[e * dk + c];
+    }
+    free(S); free(kh); free(qv);
+  }
+  free(init_copy);
+  return bad ? -1 : 0;
+}
