@@ -366,6 +366,95 @@ def bench_varlen(torch, fla, args):
     print(json.dumps(res), flush=True)
 
 
+def bench_gdn(torch, fla, args):
+    """Gated delta rule forward (one fla_gdn_fwd call per step)."""
+    import numpy as np
+    import oracle
+    from workloads import GDN, generate_gdn_torch, to_numpy_input
+
+    w = GDN[args.gdn]
+    inp = generate_gdn_torch(w, "cuda")
+    out = torch.empty((w.B, w.H, w.T, w.dv), dtype=inp["q"].dtype, device="cuda")
+    fin = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fla.gdn_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                    init_state=inp["init"], out=out, final_state=fin, chunk=w.chunk,
+                    stream=stream)
+
+    ms, warmup, t_wall = timed(torch, step, args.steps, args.warmup, stream)
+    s = 2 if w.dtype == "bf16" else 4
+    th = w.B * w.H * w.T
+    # q, k, v read, out written; alpha and beta read; end state written (start state read)
+    alg_bytes = th * (2 * w.dk + 2 * w.dv) * s + th * 8 + w.B * w.H * w.dk * w.dv * 4 * (
+        2 if w.init_sigma > 0 else 1)
+    # per token-head: K^K^T and QK^T (causal halves, dk each), the solve's W = T K^ and
+    # U0 = T V (causal halves), U = U0 - W H, O = P U + Q H, the state update
+    c = w.chunk
+    alg_flops = th * 2.0 * ((c + 1) / 2.0 * (2 * w.dk + w.dk + w.dv + w.dv) + 3.0 * w.dk * w.dv)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    t = "__bf16" if w.dtype == "bf16" else "float"
+    res = {
+        "metric": "gated delta rule chunk fwd tokens/s + roofline % (HBM), " + w.name,
+        "value": w.B * w.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded torch generator on the GPU; alpha = sigmoid(x)^(1/16), beta = sigmoid(y))",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+            "chunk": w.chunk, "init_state": w.init_sigma > 0, "global_batch": w.B,
+            "seq_len": w.T, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"gdn_fwd_kernel<{t}, {w.dk}>",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "mfma_tflops": alg_flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": alg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
+        },
+        "wall_s_timed_region": t_wall,
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        dt, eo, mo, ef, mf, nb = 0.0, 0.0, 0.0, 0.0, 0.0, 0
+        while nb < w.B and (nb == 0 or dt < args.cpu_budget):
+            sl = slice(nb, nb + 1)
+            part = lambda x: None if x is None else to_numpy_input(x[sl])
+            t0 = time.perf_counter()
+            ro, rf = oracle.gdn_fwd(part(inp["q"]), part(inp["k"]), part(inp["v"]),
+                                    part(inp["alpha"]), part(inp["beta"]), part(inp["init"]),
+                                    nthreads=threads)
+            dt += time.perf_counter() - t0
+            o = out[sl].float().cpu().numpy().astype(np.float64)
+            f = fin[sl].cpu().numpy().astype(np.float64)
+            eo, mo = max(eo, float(np.max(np.abs(o - ro)))), max(mo, float(np.max(np.abs(ro))))
+            ef, mf = max(ef, float(np.max(np.abs(f - rf)))), max(mf, float(np.max(np.abs(rf))))
+            nb += 1
+        res["cpu_baseline"] = {"value": w.T * nb / dt, "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"batches 0..{nb - 1} of {w.B}, all {w.H} heads, all "
+                                         f"{w.T} tokens (fp64 recurrence, {dt:.1f} s)"}
+        res["parity_on_sample"] = {"max_rel_err_out": eo / max(mo, 1e-300),
+                                   "max_rel_err_final": ef / max(mf, 1e-300),
+                                   "sample_batches": nb}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration(torch, steps, warmup):
     """A plain copy of 1 GiB: reads and writes exactly 2^30 bytes per launch."""
     n = 1 << 30
@@ -399,6 +488,8 @@ def main():
                     help="time the forward pass (default) or the chunkwise backward")
     ap.add_argument("--layout", choices=("bhtd", "bthd"), default="bhtd",
                     help="forward: [B][H][T][d] (default) or token-major [B][T][H][d] inputs")
+    ap.add_argument("--gdn", default=None,
+                    help="gated delta rule forward (workload name, e.g. gdn_d128)")
     ap.add_argument("--varlen", default=None,
                     help="forward over packed variable-length sequences (workload name, "
                          "e.g. varlen_gla_d128)")
@@ -427,6 +518,9 @@ def main():
     from workloads import HEADLINE, WORKLOADS, generate_torch
 
     torch.cuda.set_device(0)
+    if args.gdn:
+        bench_gdn(torch, fla, args)
+        return
     if args.varlen:
         bench_varlen(torch, fla, args)
         return

@@ -31,7 +31,7 @@ FLA_LAYOUT_BTHD = 1 << 6
 
 EXPORTED = ("fla_linattn_fwd", "fla_linattn_fwd_segments", "fla_linattn_step",
             "fla_status_string", "fla_linattn_segments_for", "fla_linattn_bwd",
-            "fla_linattn_fwd_varlen")
+            "fla_linattn_fwd_varlen", "fla_gdn_fwd")
 
 _lib = None
 
@@ -70,6 +70,8 @@ def load_library():
     lib.fla_linattn_fwd_varlen.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64,
                                            u32, p]
     lib.fla_linattn_fwd_varlen.restype = c_int
+    lib.fla_gdn_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, u32, p]
+    lib.fla_gdn_fwd.restype = c_int
     _lib = lib
     return lib
 
@@ -246,4 +248,29 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: to
                                                flags, _stream(stream))
     if rc != FLA_OK:
         raise FlaError("fla_linattn_fwd_varlen", rc)
+    return out, final_state
+
+
+def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+            beta: torch.Tensor, *, init_state: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+            want_final: bool = True, chunk: int = 64,
+            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gated delta rule forward.  q, k [B,H,T,dk]; v [B,H,T,dv] (bf16 or fp32); alpha, beta
+    fp32 [B,H,T]; states fp32 [B,H,dk,dv].  Returns (out, final_state)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and want_final:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, alpha, beta, out, init_state, final_state):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    flags = FLA_BF16 if q.dtype == torch.bfloat16 else 0
+    rc = load_library().fla_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                     _ptr(init_state), _ptr(out), _ptr(final_state), B, H, T, dk,
+                                     dv, chunk, flags, _stream(stream))
+    if rc != FLA_OK:
+        raise FlaError("fla_gdn_fwd", rc)
     return out, final_state

@@ -45,6 +45,7 @@ def _units():
             obj = os.path.join(OBJDIR, f"bwd_{tname}_{dy}.o")
             units.append((os.path.join(CSRC, "bwd_inst.hip"), obj,
                           [f"-DFLA_TIN_BF16={flag}", f"-DFLA_BWD_DY={dy}"]))
+    units.append((os.path.join(CSRC, "gdn_inst.hip"), os.path.join(OBJDIR, "gdn_inst.o"), []))
     units.append((os.path.join(CSRC, "fla_api.hip"), os.path.join(OBJDIR, "fla_api.o"), []))
     return units
 

@@ -7,8 +7,13 @@
 #include "../../include/fla_linattn.h"
 #include "bwd_dispatch.hpp"
 #include "dispatch.hpp"
+#include "gdn_fwd.hpp"
 
 namespace fla {
+
+using GdnLauncher = hipError_t (*)(const GdnArgs &, unsigned grid, hipStream_t);
+GdnLauncher gdn_launcher(bool bf16, int dk); // gdn_inst.hip
+
 namespace {
 
 constexpr int kStepThreads = 256;
@@ -433,10 +438,54 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   return rc;
 }
 
+int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+             const float *init_state, void *out, float *final_state, int64_t B, int64_t H,
+             int64_t T, int64_t dk, int64_t dv, int64_t chunk, uint32_t flags, void *stream) {
+  if (flags & ~FLA_BF16) return FLA_ERR_INVALID_ARG; // no decay / feature-map / layout options
+  if (B < 1 || H < 1 || B > (1 << 24) || H > (1 << 24) || T < 0) return FLA_ERR_INVALID_ARG;
+  if (dk < 1 || dv < 1) return FLA_ERR_INVALID_ARG;
+  if (T > 0 && (!q || !k || !v || !out || !alpha || !beta)) return FLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(alpha, 4) ||
+      !aligned(beta, 4))
+    return FLA_ERR_INVALID_ARG;
+  if (chunk != 64) return FLA_ERR_UNSUPPORTED;
+  if (dv % kSlice != 0 || dv > 256) return FLA_ERR_UNSUPPORTED;
+  if (B * H > ((int64_t)1 << 26) || T > ((int64_t)1 << 40) / (B * H)) return FLA_ERR_INVALID_ARG;
+  const GdnLauncher launch = gdn_launcher((flags & FLA_BF16) != 0, (int)dk);
+  if (!launch) return FLA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nbh = B * H;
+  if (T == 0) {
+    if (final_state && final_state != init_state) return launch_fill(final_state, init_state, nbh * dk * dv, s);
+    return FLA_OK;
+  }
+  const int64_t nvs = dv / kSlice;
+  if (nbh * nvs >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
+  GdnArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.alpha = alpha; a.beta = beta;
+  a.init = init_state;
+  a.fin = final_state;
+  a.out = out;
+  a.T = T;
+  a.H = (int)H; a.dv = (int)dv;
+  a.nvs = (int)nvs;
+  a.nunits = (int)(nbh * nvs);
+  return launch(a, (unsigned)a.nunits, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
+}
+
 } // namespace
 } // namespace fla
 
 extern "C" {
+
+int fla_gdn_fwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                const float *init_state, void *out, float *final_state, int64_t B, int64_t H,
+                int64_t T, int64_t dk, int64_t dv, int64_t chunk, uint32_t flags, void *stream) {
+  return fla::gdn_impl(q, k, v, alpha, beta, init_state, out, final_state, B, H, T, dk, dv,
+                       chunk, flags, stream);
+}
 
 int fla_linattn_bwd(const void *q, const void *k, const void *v, const float *gate_or_gamma,
                     const float *init_state, const void *dout, const float *dfinal_state,

@@ -167,6 +167,24 @@ int fla_linattn_bwd(const void *q, const void *k, const void *v, const float *ga
                     int64_t H, int64_t T, int64_t dk_dim, int64_t dv_dim, int64_t chunk,
                     uint32_t flags, void *stream);
 
+/*
+ * fla_gdn_fwd — gated delta rule, chunkwise forward (textbook chapter 1.6, section "gated
+ * delta rule"; the Gated DeltaNet op the FLA posts list).  Per (b, h), with the unit-norm
+ * key k^_t = k_t / max(|k_t|, 1e-12) (normalised inside the call, as the chapter's reference
+ * code does) and q used as given:
+ *     S_t = alpha_t S_{t-1} (I - beta_t k^_t k^_t^T) + beta_t v_t k^_t^T,   o_t = S_t q_t,
+ * i.e. decay the memory, replace a beta_t share of what it stores under k^_t by v_t.
+ *   q, k  : [B][H][T][dk]; v, out: [B][H][T][dv] (bf16 with FLA_BF16, else fp32); 16-byte aligned.
+ *   alpha : fp32 [B][H][T], the decay in (0, 1] (each chunk's product of alpha must stay
+ *           above ~1e-30); beta: fp32 [B][H][T], the write strength in [0, 1]; 4-byte aligned.
+ *   init_state, final_state: fp32 [B][H][dk][dv] (h = S^T as above) or NULL; may alias.
+ *   dk in {64, 128} (fp32: 64); dv in {64, 128, 256}; chunk = 64; flags: FLA_BF16 only.
+ * One workgroup per (b, h, 64-wide value slice) streams the chunks; no workspace.
+ */
+int fla_gdn_fwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                const float *init_state, void *out, float *final_state, int64_t B, int64_t H,
+                int64_t T, int64_t dk, int64_t dv, int64_t chunk, uint32_t flags, void *stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char *fla_status_string(int status);
 

@@ -168,3 +168,23 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(fla, "LIB_PATH", "/nonexistent/libfla_linattn.so")
     with pytest.raises(ImportError):
         fla.load_library()
+
+
+def test_gdn_rejects_on_host(lib):
+    def gdn(**kw):
+        a = dict(q=BOGUS, k=BOGUS, v=BOGUS, al=BOGUS, be=BOGUS, init=None, out=BOGUS, fin=None,
+                 B=1, H=1, T=64, dk=64, dv=64, chunk=64, flags=0)
+        a.update(kw)
+        return lib.fla_gdn_fwd(a["q"], a["k"], a["v"], a["al"], a["be"], a["init"], a["out"],
+                               a["fin"], a["B"], a["H"], a["T"], a["dk"], a["dv"], a["chunk"],
+                               a["flags"], None)
+    assert gdn(flags=fla.FLA_DECAY_GATE) == fla.FLA_ERR_INVALID_ARG
+    assert gdn(flags=fla.FLA_NORMALIZE) == fla.FLA_ERR_INVALID_ARG
+    assert gdn(al=None) == fla.FLA_ERR_INVALID_ARG
+    assert gdn(be=ctypes.c_void_p((1 << 20) + 2)) == fla.FLA_ERR_INVALID_ARG
+    assert gdn(q=MISALIGNED) == fla.FLA_ERR_INVALID_ARG
+    assert gdn(T=-1) == fla.FLA_ERR_INVALID_ARG
+    assert gdn(chunk=32) == fla.FLA_ERR_UNSUPPORTED
+    assert gdn(dk=32) == fla.FLA_ERR_UNSUPPORTED
+    assert gdn(dv=96) == fla.FLA_ERR_UNSUPPORTED
+    assert gdn(dk=128) == fla.FLA_ERR_UNSUPPORTED                     # fp32 dk = 128

@@ -92,6 +92,44 @@ VARLEN = {
 }
 
 
+# Gated delta rule (NEXT-3): the headline's shape; alpha = sigmoid(x)^(1/16) per token and
+# head (the GLA gate recipe, one column), beta = sigmoid(y); x, y ~ N(0, 1).
+GDN = {
+    "gdn_d128": Workload("gdn_d128", 8, 16, 16384, 128, 128, 64, "bf16", DECAY_TOKEN, False,
+                         False, 1.0 / math.sqrt(128), 0.0, seed=1008),
+}
+
+
+def generate_gdn(w: Workload) -> dict:
+    """Inputs of a gated-delta workload (numpy, library layouts): q, k, v as ``generate``
+    (streams 1-3), alpha [B,H,T] (stream 4), beta [B,H,T] (stream 9), init (stream 5) or
+    None (no value column for a normaliser)."""
+    d = generate(w.with_(normalize=False))
+    d["alpha"] = d.pop("decay")
+    beta = np.empty((w.B, w.H, w.T), dtype=np.float32)
+
+    def fill(g, b, h):
+        y = g.standard_normal(w.T, dtype=np.float64)
+        beta[b, h] = (1.0 / (1.0 + np.exp(-y))).astype(np.float32)
+
+    _per_head(w, 9, fill)
+    d["beta"] = beta
+    return d
+
+
+def generate_gdn_torch(w: Workload, device="cuda") -> dict:
+    """Device-side counterpart of generate_gdn (torch's seeded generator)."""
+    import torch
+
+    d = generate_torch(w.with_(normalize=False), device)
+    d["alpha"] = d.pop("decay")
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed + 2)
+    y = torch.randn((w.B, w.H, w.T), generator=gen, device=device, dtype=torch.float64)
+    d["beta"] = torch.sigmoid(y).to(torch.float32)
+    return d
+
+
 def varlen_lengths(n_seqs: int, lo: int, hi: int, seed: int) -> np.ndarray:
     """Sequence lengths, log-uniform in [lo, hi], int64."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 8])))
