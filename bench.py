@@ -415,7 +415,7 @@ def bench_gdn(torch, fla, args):
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": f"gdn_fwd_kernel<{t}, {w.dk}>",
+            "kernel": f"gdn_prep_kernel<{t}, {w.dk}> + gdn_state_kernel<{t}, {w.dk}>",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

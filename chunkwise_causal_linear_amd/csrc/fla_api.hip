@@ -12,7 +12,10 @@
 namespace fla {
 
 using GdnLauncher = hipError_t (*)(const GdnArgs &, unsigned grid, hipStream_t);
-GdnLauncher gdn_launcher(bool bf16, int dk); // gdn_inst.hip
+struct GdnLaunchers {
+  GdnLauncher prep, state;
+};
+GdnLaunchers gdn_launchers(bool bf16, int dk); // gdn_inst.hip
 
 namespace {
 
@@ -452,8 +455,9 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
   if (chunk != 64) return FLA_ERR_UNSUPPORTED;
   if (dv % kSlice != 0 || dv > 256) return FLA_ERR_UNSUPPORTED;
   if (B * H > ((int64_t)1 << 26) || T > ((int64_t)1 << 40) / (B * H)) return FLA_ERR_INVALID_ARG;
-  const GdnLauncher launch = gdn_launcher((flags & FLA_BF16) != 0, (int)dk);
-  if (!launch) return FLA_ERR_UNSUPPORTED;
+  const bool bf16 = (flags & FLA_BF16) != 0;
+  const GdnLaunchers launch = gdn_launchers(bf16, (int)dk);
+  if (!launch.prep || !launch.state) return FLA_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t nbh = B * H;
   if (T == 0) {
@@ -461,7 +465,14 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
     return FLA_OK;
   }
   const int64_t nvs = dv / kSlice;
-  if (nbh * nvs >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
+  const int64_t nch = (T + 63) / 64;
+  if (nbh * nvs >= kMaxGrid || nbh * nch >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
+  // workspace: W = T diag(beta g) K^ per chunk (input type) and U0 = T diag(beta) V (fp32)
+  const int64_t w_bytes = nbh * T * dk * (bf16 ? 2 : 4);
+  const int64_t u_bytes = nbh * T * dv * 4;
+  char *ws = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void **>(&ws), w_bytes + u_bytes, s) != hipSuccess)
+    return FLA_ERR_DEVICE;
   GdnArgs a{};
   a.q = q; a.k = k; a.v = v;
   a.alpha = alpha; a.beta = beta;
@@ -471,8 +482,16 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
   a.T = T;
   a.H = (int)H; a.dv = (int)dv;
   a.nvs = (int)nvs;
+  a.nch = (int)nch;
+  a.w = ws;
+  a.u0 = reinterpret_cast<float *>(ws + w_bytes);
+  int rc = FLA_OK;
+  a.nunits = (int)(nbh * nch);
+  if (launch.prep(a, (unsigned)a.nunits, s) != hipSuccess) rc = FLA_ERR_DEVICE;
   a.nunits = (int)(nbh * nvs);
-  return launch(a, (unsigned)a.nunits, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
+  if (rc == FLA_OK && launch.state(a, (unsigned)a.nunits, s) != hipSuccess) rc = FLA_ERR_DEVICE;
+  if (hipFreeAsync(ws, s) != hipSuccess) rc = FLA_ERR_DEVICE;
+  return rc;
 }
 
 } // namespace

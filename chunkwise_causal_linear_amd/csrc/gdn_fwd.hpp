@@ -1,4 +1,4 @@
-// Gated delta rule, chunkwise forward — gfx950 kernel.
+// Gated delta rule, chunkwise forward — gfx950 kernels.
 //
 // Recurrence (textbook chapter 1.6, section "gated delta rule"), with the unit-norm key
 // k^_t = k_t / max(|k_t|, 1e-12) and h = S^T (dk x dv):
@@ -12,13 +12,14 @@
 //     U = U0 - W H,
 //     O = diag(g) Q H + (M (.) Q K^^T) U,        M_tj = g_t / g_j (j <= t),
 //     H <- g_L H + K^^T diag(g_L / g) U.
-// One workgroup (4 waves) owns one (b, h, 64-wide slice of dv); wave w owns value columns
-// 16w..16w+15 of the slice, whose state rows live in MFMA accumulators for the whole
-// sequence.  Per chunk: k normalised and the decay scanned while the tiles go to LDS;
-// K^ K^^T on MFMA gives A; the 16 x 16 diagonal blocks of T are inverted by forward
-// substitution (one wave each), the off-diagonal blocks follow block row by block row with
-// fp32 MFMA; then W, U0, the score tiles, U, the outputs and the state on bf16 (or fp32)
-// MFMA.  The next chunk's inputs are prefetched into registers meanwhile.
+// W and U0 do not depend on the state, so they are formed for every chunk at once by a
+// pre-pass (one workgroup per (b, h, chunk): K^ K^^T on MFMA gives A; the 16 x 16 diagonal
+// blocks of T are inverted by forward substitution, one wave each, and the off-diagonal
+// blocks follow block row by block row with fp32 MFMA; then W and U0 on MFMA, written to a
+// workspace: W in the input type, U0 in fp32).  The state pass streams the chunks, one
+// workgroup per (b, h, 64-wide slice of dv) with its state columns in MFMA accumulators:
+// per chunk the masked scores, U = U0 - W H, the outputs and the state update, three
+// barriers, the next chunk's inputs prefetched into registers meanwhile.
 #pragma once
 
 #include "chunk_bwd.hpp" // shared MFMA / LDS fragment helpers
@@ -31,10 +32,13 @@ struct GdnArgs {
   const float *init;         // [B][H][dk][dv] or null
   float *fin;                // [B][H][dk][dv] or null
   void *out;                 // [B][H][T][dv]
+  void *w;                   // workspace [B][H][T][dk], input type
+  float *u0;                 // workspace [B][H][T][dv], fp32
   int64_t T;
   int H, dv;
   int nvs;                   // 64-wide value slices
-  int nunits;                // B * H * nvs
+  int nch;                   // chunks per (b, h)
+  int nunits;                // state pass: B * H * nvs; pre-pass: B * H * nch
 };
 
 template <typename TIn, int DK>
@@ -46,51 +50,303 @@ struct GdnCfg {
   static constexpr int LDK = DK + VE;  // Q, K^, W rows
   static constexpr int LDV = XW + VE;  // V, U, Us rows
   static constexpr int LDT = C + VE;   // Tb, Tg rows
-  static constexpr int NVQ = C * DK / VE / NT;  // 16-byte vectors per thread (q, k)
+  static constexpr int NVQ = C * DK / VE / NT;  // 16-byte vectors per thread (q, k, W)
   static constexpr int NVV = C * XW / VE / NT;  // (v slice)
   static constexpr int VPRQ = DK / VE;          // vectors per q/k row
+  static constexpr int NCB = DK / 16;           // 16-row blocks of the state
+  static constexpr int NZU = C / KU;            // K units over the chunk rows
   static_assert(NVQ >= 1 && NVV >= 1 && VPRQ <= 64, "tile shape");
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_K = OFF_Q + C * LDK * ES;
-  static constexpr int OFF_W = OFF_K + C * LDK * ES;
-  static constexpr int OFF_V = OFF_W + C * LDK * ES;
-  static constexpr int OFF_TB = OFF_V + C * LDV * ES;
-  static constexpr int OFF_TG = OFF_TB + C * LDT * ES;
-  static constexpr int OFF_R = OFF_TG + C * LDT * ES;  // region: A, T (fp32), later U, Us, P
-  static constexpr int R_FP32 = 2 * C * C * 4;
-  static constexpr int R_LATE = 2 * C * LDV * ES + 16 * 256 * ES;
-  static constexpr int R_BYTES = R_FP32 > R_LATE ? R_FP32 : R_LATE;
-  static constexpr int OFF_AF = OFF_R;                   // A, fp32 [C][C]
-  static constexpr int OFF_TF = OFF_R + C * C * 4;       // T, fp32 [C][C]
-  static constexpr int OFF_U = OFF_R;                    // U [C][LDV]
-  static constexpr int OFF_US = OFF_U + C * LDV * ES;    // U (.) g_L / g
-  static constexpr int OFF_P = OFF_US + C * LDV * ES;    // masked scores, 16 tile images
-  static constexpr int OFF_G = OFF_R + R_BYTES;          // g [C], beta [C]
-  static constexpr int OFF_BETA = OFF_G + C * 4;
-  static constexpr int LDS = OFF_BETA + C * 4;
-  static constexpr bool FITS = LDS <= kMaxLds;
+  // pre-pass LDS
+  static constexpr int P_K = 0;
+  static constexpr int P_V = P_K + C * LDK * ES;
+  static constexpr int P_TB = P_V + C * LDV * ES;
+  static constexpr int P_TG = P_TB + C * LDT * ES;
+  static constexpr int P_A = P_TG + C * LDT * ES;   // A, fp32 [C][C]
+  static constexpr int P_T = P_A + C * C * 4;       // T, fp32 [C][C]
+  static constexpr int P_G = P_T + C * C * 4;       // g [C], beta [C]
+  static constexpr int P_BETA = P_G + C * 4;
+  static constexpr int P_LDS = P_BETA + C * 4;
+  // state-pass LDS
+  static constexpr int S_Q = 0;
+  static constexpr int S_K = S_Q + C * LDK * ES;
+  static constexpr int S_W = S_K + C * LDK * ES;
+  static constexpr int S_U = S_W + C * LDK * ES;    // U [C][LDV]
+  static constexpr int S_US = S_U + C * LDV * ES;   // U (.) g_L / g
+  static constexpr int S_P = S_US + C * LDV * ES;   // masked scores, 16 tile images
+  static constexpr int S_G = S_P + 16 * 256 * ES;   // g [C]
+  static constexpr int S_LDS = S_G + C * 4;
+  static constexpr bool FITS = P_LDS <= kMaxLds && S_LDS <= kMaxLds;
 };
 
+namespace gdn {
+
+// k^ rows of one chunk (registers, 16-byte vectors in row-major order) into LDS; the
+// VPRQ vectors of a row sit in VPRQ consecutive lanes, which reduce its squared norm.
 template <typename TIn, int DK>
-__global__ void __launch_bounds__(256) gdn_fwd_kernel(GdnArgs a) {
+__device__ __forceinline__ void stage_khat(const uint32_t (*rk)[4], TIn *sK, int tid) {
   using K = GdnCfg<TIn, DK>;
-  constexpr int C = K::C, XW = K::XW, VE = K::VE, KU = K::KU;
+  constexpr int VE = K::VE;
+#pragma unroll
+  for (int j = 0; j < K::NVQ; ++j) {
+    const int vi = tid + 256 * j, r = vi / K::VPRQ, c = (vi % K::VPRQ) * VE;
+    float fk[VE];
+    unpack<TIn, VE>(fk, rk[j]);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) ss += fk[e] * fk[e];
+#pragma unroll
+    for (int d = 1; d < K::VPRQ; d <<= 1) ss += __shfl_xor(ss, d);
+    const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) fk[e] *= inv;
+    st_lds<TIn, VE>(sK + r * K::LDK + c, fk);
+  }
+}
+
+// Raw tile rows (registers) into LDS.
+template <typename TIn, int NV, int VPR, int LD>
+__device__ __forceinline__ void stage_raw(const uint32_t (*rx)[4], TIn *s, int tid) {
+  constexpr int VE = 16 / sizeof(TIn);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int vi = tid + 256 * j, r = vi / VPR, c = (vi % VPR) * VE;
+    st_words_lds<4>(s + r * LD + c, rx[j]);
+  }
+}
+
+// g = inclusive product of alpha down the chunk (wave 0; rows past the end carry 1).
+__device__ __forceinline__ float decay_scan(float alpha, int lane) {
+  float x = alpha;
+  for (int d = 1; d < 64; d <<= 1) {
+    const float o = __shfl_up(x, d);
+    if (lane >= d) x *= o;
+  }
+  return x;
+}
+
+// Masked score tiles P[t][j] = (g_t / g_j) q_t . k^_j (j <= t); the image of tile (tb, jb) is
+// row-major [t][j].  10 tiles over the 4 waves.
+template <typename TIn, int DK>
+__device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const float *sG, TIn *sP,
+                                       int wave, int g, int li) {
+  using K = GdnCfg<TIn, DK>;
+  static_for<0, 16>([&](auto I) {
+    constexpr int tb = I / 4, jb = I % 4;
+    if constexpr (jb <= tb) {
+      constexpr int pos = tb * (tb + 1) / 2 + jb;
+      if (pos % 4 == wave) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const TIn *kj = sK + (16 * jb + li) * K::LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
+        const TIn *qt = sQ + (16 * tb + li) * K::LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
+#pragma unroll
+        for (int u = 0; u < DK / K::KU; ++u)
+          acc = mma(acc, ld_frag_c_at<TIn, true>(kj, u, g), ld_frag_c_at<TIn, true>(qt, u, g));
+        // acc[qq]: j = 16 jb + 4g + qq, t = 16 tb + li
+        const int t = 16 * tb + li;
+        const float gt = sG[t];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int j = 16 * jb + 4 * g + qq;
+          acc[qq] = (j <= t) ? gt / sG[j] * acc[qq] : 0.f;
+        }
+        st_ptile<TIn>(sP + I * 256 + li * 16 + 4 * g, acc);
+      }
+    }
+  });
+}
+
+} // namespace gdn
+
+// ---- pre-pass: W and U0 of one chunk ---------------------------------------------------
+template <typename TIn, int DK>
+__global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
+  using K = GdnCfg<TIn, DK>;
+  constexpr int C = K::C, XW = K::XW, VE = K::VE, KU = K::KU, NCB = K::NCB, NZU = K::NZU;
   constexpr int LDK = K::LDK, LDV = K::LDV, LDT = K::LDT;
-  constexpr int NCB = DK / 16;   // state row blocks
-  __shared__ __attribute__((aligned(16))) unsigned char lds[K::LDS];
-  TIn *sQ = reinterpret_cast<TIn *>(lds + K::OFF_Q);
-  TIn *sK = reinterpret_cast<TIn *>(lds + K::OFF_K);
-  TIn *sW = reinterpret_cast<TIn *>(lds + K::OFF_W);
-  TIn *sV = reinterpret_cast<TIn *>(lds + K::OFF_V);
-  TIn *sTb = reinterpret_cast<TIn *>(lds + K::OFF_TB);
-  TIn *sTg = reinterpret_cast<TIn *>(lds + K::OFF_TG);
-  float *sAf = reinterpret_cast<float *>(lds + K::OFF_AF);
-  float *sTf = reinterpret_cast<float *>(lds + K::OFF_TF);
-  TIn *sU = reinterpret_cast<TIn *>(lds + K::OFF_U);
-  TIn *sUs = reinterpret_cast<TIn *>(lds + K::OFF_US);
-  TIn *sP = reinterpret_cast<TIn *>(lds + K::OFF_P);
-  float *sG = reinterpret_cast<float *>(lds + K::OFF_G);
-  float *sBeta = reinterpret_cast<float *>(lds + K::OFF_BETA);
+  __shared__ __attribute__((aligned(16))) unsigned char lds[K::P_LDS];
+  TIn *sK = reinterpret_cast<TIn *>(lds + K::P_K);
+  TIn *sV = reinterpret_cast<TIn *>(lds + K::P_V);
+  TIn *sTb = reinterpret_cast<TIn *>(lds + K::P_TB);
+  TIn *sTg = reinterpret_cast<TIn *>(lds + K::P_TG);
+  float *sA = reinterpret_cast<float *>(lds + K::P_A);
+  float *sT = reinterpret_cast<float *>(lds + K::P_T);
+  float *sG = reinterpret_cast<float *>(lds + K::P_G);
+  float *sBeta = reinterpret_cast<float *>(lds + K::P_BETA);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int n = blockIdx.x % a.nch;
+  const int64_t bh = blockIdx.x / a.nch;
+  const int64_t T = a.T, t0 = (int64_t)n * C;
+  const int dv = a.dv;
+  const int L = (int)((T - t0) < C ? (T - t0) : C);
+  const TIn *gk = static_cast<const TIn *>(a.k) + (bh * T + t0) * DK;
+  const TIn *gv = static_cast<const TIn *>(a.v) + (bh * T + t0) * dv;
+
+  // k^ and the decay
+  {
+    uint32_t rk[K::NVQ][4];
+#pragma unroll
+    for (int j = 0; j < K::NVQ; ++j) {
+      const int vi = tid + 256 * j, r = vi / K::VPRQ, c = (vi % K::VPRQ) * VE;
+      uint4 y = make_uint4(0, 0, 0, 0);
+      if (r < L) y = *reinterpret_cast<const uint4 *>(gk + r * DK + c);
+      rk[j][0] = y.x; rk[j][1] = y.y; rk[j][2] = y.z; rk[j][3] = y.w;
+    }
+    gdn::stage_khat<TIn, DK>(rk, sK, tid);
+    if (wave == 0) {
+      const float al = lane < L ? a.alpha[bh * T + t0 + lane] : 1.f; // past the end: 1, 0
+      const float be = lane < L ? a.beta[bh * T + t0 + lane] : 0.f;
+      sG[lane] = gdn::decay_scan(al, lane);
+      sBeta[lane] = be;
+    }
+  }
+  __syncthreads();
+
+  // A = strictly lower (beta_t g_t / g_j) k^_t . k^_j, fp32: 10 tiles over 4 waves
+  static_for<0, 16>([&](auto I) {
+    constexpr int tb = I / 4, jb = I % 4;
+    if constexpr (jb <= tb) {
+      constexpr int pos = tb * (tb + 1) / 2 + jb;
+      if (pos % 4 == wave) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const TIn *at = sK + (16 * tb + li) * LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
+        const TIn *bj = sK + (16 * jb + li) * LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
+#pragma unroll
+        for (int u = 0; u < DK / KU; ++u)
+          acc = mma(acc, ld_frag_c_at<TIn, true>(bj, u, g), ld_frag_c_at<TIn, true>(at, u, g));
+        // acc[qq] = k^_j . k^_t with j = 16 jb + 4g + qq, t = 16 tb + li
+        const int t = 16 * tb + li;
+        const float bt = sBeta[t] * sG[t];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int j = 16 * jb + 4 * g + qq;
+          sA[t * C + j] = (j < t) ? bt / sG[j] * acc[qq] : 0.f;
+        }
+      }
+    }
+  });
+  __syncthreads();
+
+  // diagonal blocks of T = (I + A)^-1 by forward substitution: lanes 0..15 of wave w
+  // invert block w, one column each
+  if (li == lane) {
+    const int base = 16 * wave;
+    float col[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = (i == li) ? 1.f : 0.f;
+#pragma unroll
+      for (int kk = 0; kk < i; ++kk) s -= sA[(base + i) * C + base + kk] * col[kk];
+      col[i] = (i < li) ? 0.f : s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sT[(base + i) * C + base + li] = col[i];
+  }
+  __syncthreads();
+
+  // off-diagonal blocks, block row by block row: T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj),
+  // wave j computes block (i, j)
+  static_for<1, 4>([&](auto IB) {
+    constexpr int ib = IB;
+    if (wave < ib) {
+      const int jb = wave;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = jb; kb < ib; ++kb) {
+        // A operand: A[16ib + li][16kb + 4g + r]; B operand: T[16kb + 4g + r][16jb + li]
+        const f32x4 fa = *reinterpret_cast<const f32x4 *>(sA + (16 * ib + li) * C + 16 * kb + 4 * g);
+        const float *tb = sT + (16 * kb + 4 * g) * C + 16 * jb + li;
+        const f32x4 fb = {tb[0], tb[C], tb[2 * C], tb[3 * C]};
+        x = mma(x, fa, fb);
+      }
+      // x[qq] = X[row 4g + qq][col li]: a B operand with k = 4g + qq
+      const f32x4 ft = *reinterpret_cast<const f32x4 *>(sT + (16 * ib + li) * C + 16 * ib + 4 * g);
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      y = mma(y, ft, x);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) sT[(16 * ib + 4 * g + qq) * C + 16 * jb + li] = -y[qq];
+    }
+    __syncthreads();
+  });
+
+  // Tb = T diag(beta), Tg = T diag(beta g) in the MFMA input type
+#pragma unroll
+  for (int i = 0; i < C * C / 256; ++i) {
+    const int idx = tid + 256 * i, t = idx / C, j = idx % C;
+    const float tv = (j <= t) ? sT[t * C + j] : 0.f;
+    const float bj = sBeta[j];
+    sTb[t * LDT + j] = (TIn)(tv * bj);
+    sTg[t * LDT + j] = (TIn)(tv * bj * sG[j]);
+  }
+  __syncthreads();
+
+  // W = Tg K^ (4 * NCB tiles over the 4 waves), straight to the workspace
+  TIn *gw = static_cast<TIn *>(a.w) + (bh * T + t0) * DK;
+#pragma unroll
+  for (int ti = 0; ti < NCB; ++ti) {
+    const int tile = wave * NCB + ti, tb = tile / NCB, cb = tile % NCB;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const TIn *ta = sTg + (16 * tb + li) * LDT + 4 * g;
+#pragma unroll
+    for (int u = 0; u < NZU; ++u)
+      acc = mma(acc, ld_frag_at<TIn, true>(ta, u), ld_frag_t<TIn, true>(sK, LDK, 16 * cb, u, g, li));
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int t = 16 * tb + 4 * g + qq;
+      if (t < L) gw[t * DK + 16 * cb + li] = (TIn)acc[qq];
+    }
+  }
+
+  // U0 = Tb V, one 64-wide value slice at a time
+  float *gu = a.u0 + (bh * T + t0) * dv;
+  for (int vs = 0; vs < a.nvs; ++vs) {
+    {
+      uint32_t rv[K::NVV][4];
+      constexpr int VPRV = XW / VE;
+#pragma unroll
+      for (int j = 0; j < K::NVV; ++j) {
+        const int vi = tid + 256 * j, r = vi / VPRV, c = (vi % VPRV) * VE;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (r < L) x = *reinterpret_cast<const uint4 *>(gv + r * dv + vs * XW + c);
+        rv[j][0] = x.x; rv[j][1] = x.y; rv[j][2] = x.z; rv[j][3] = x.w;
+      }
+      if (vs > 0) __syncthreads(); // the previous slice's V tile is still being read
+      gdn::stage_raw<TIn, K::NVV, XW / VE, LDV>(rv, sV, tid);
+    }
+    __syncthreads();
+    Frag<TIn> vf[NZU];
+#pragma unroll
+    for (int u = 0; u < NZU; ++u) vf[u] = ld_frag_t<TIn, true>(sV, LDV, 16 * wave, u, g, li);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const TIn *ta = sTb + (16 * tb + li) * LDT + 4 * g;
+#pragma unroll
+      for (int u = 0; u < NZU; ++u) acc = mma(acc, ld_frag_at<TIn, true>(ta, u), vf[u]);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int t = 16 * tb + 4 * g + qq;
+        if (t < L) gu[t * dv + vs * XW + 16 * wave + li] = acc[qq];
+      }
+    }
+  }
+}
+
+// ---- state pass ---------------------------------------------------------------------------
+template <typename TIn, int DK>
+__global__ void __launch_bounds__(256) gdn_state_kernel(GdnArgs a) {
+  using K = GdnCfg<TIn, DK>;
+  constexpr int C = K::C, XW = K::XW, VE = K::VE, KU = K::KU, NCB = K::NCB, NZU = K::NZU;
+  constexpr int LDK = K::LDK, LDV = K::LDV;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[K::S_LDS];
+  TIn *sQ = reinterpret_cast<TIn *>(lds + K::S_Q);
+  TIn *sK = reinterpret_cast<TIn *>(lds + K::S_K);
+  TIn *sW = reinterpret_cast<TIn *>(lds + K::S_W);
+  TIn *sU = reinterpret_cast<TIn *>(lds + K::S_U);
+  TIn *sUs = reinterpret_cast<TIn *>(lds + K::S_US);
+  TIn *sP = reinterpret_cast<TIn *>(lds + K::S_P);
+  float *sG = reinterpret_cast<float *>(lds + K::S_G);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,54 +359,48 @@ __global__ void __launch_bounds__(256) gdn_fwd_kernel(GdnArgs a) {
   const int64_t bh = unit / a.nvs;
   const int64_t T = a.T;
   const int dv = a.dv;
-  const int e_base = vs * XW;
-  const int nchunks = (int)((T + C - 1) / C);
+  const int e_lane = vs * XW + 16 * wave + li; // this lane's value column
   const TIn *gq = static_cast<const TIn *>(a.q) + bh * T * DK;
   const TIn *gk = static_cast<const TIn *>(a.k) + bh * T * DK;
-  const TIn *gv = static_cast<const TIn *>(a.v) + bh * T * dv;
+  const TIn *gw = static_cast<const TIn *>(a.w) + bh * T * DK;
+  const float *gu = a.u0 + bh * T * dv;
   TIn *gout = static_cast<TIn *>(a.out) + bh * T * dv;
-  const float *galpha = a.alpha + bh * T, *gbeta = a.beta + bh * T;
+  const float *galpha = a.alpha + bh * T;
 
   auto chunk_len = [&](int n) -> int {
     const int64_t l = T - (int64_t)n * C;
     return (int)(l < C ? l : C);
   };
 
-  // ---- register prefetch of one chunk -----------------------------------------------
-  uint32_t rq[K::NVQ][4], rk[K::NVQ][4], rv[K::NVV][4];
-  float ralpha = 1.f, rbeta = 0.f;
+  // register prefetch of one chunk: q, k, W rows; this lane's U0 entries; alpha
+  uint32_t rq[K::NVQ][4], rk[K::NVQ][4], rw[K::NVQ][4];
+  float ru[16];
+  float ralpha = 1.f;
   auto load = [&](int n) {
     const int L = chunk_len(n);
     const int64_t t0 = (int64_t)n * C;
 #pragma unroll
     for (int j = 0; j < K::NVQ; ++j) {
       const int vi = tid + 256 * j, r = vi / K::VPRQ, c = (vi % K::VPRQ) * VE;
-      uint4 x = make_uint4(0, 0, 0, 0), y = x;
+      uint4 x = make_uint4(0, 0, 0, 0), y = x, z = x;
       if (r < L) {
         x = *reinterpret_cast<const uint4 *>(gq + (t0 + r) * DK + c);
         y = *reinterpret_cast<const uint4 *>(gk + (t0 + r) * DK + c);
+        z = *reinterpret_cast<const uint4 *>(gw + (t0 + r) * DK + c);
       }
       rq[j][0] = x.x; rq[j][1] = x.y; rq[j][2] = x.z; rq[j][3] = x.w;
       rk[j][0] = y.x; rk[j][1] = y.y; rk[j][2] = y.z; rk[j][3] = y.w;
+      rw[j][0] = z.x; rw[j][1] = z.y; rw[j][2] = z.z; rw[j][3] = z.w;
     }
-    constexpr int VPRV = XW / VE;
 #pragma unroll
-    for (int j = 0; j < K::NVV; ++j) {
-      const int vi = tid + 256 * j, r = vi / VPRV, c = (vi % VPRV) * VE;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (r < L && e_base + c < dv) x = *reinterpret_cast<const uint4 *>(gv + (t0 + r) * dv + e_base + c);
-      rv[j][0] = x.x; rv[j][1] = x.y; rv[j][2] = x.z; rv[j][3] = x.w;
+    for (int i = 0; i < 16; ++i) {
+      const int t = 16 * (i >> 2) + 4 * g + (i & 3); // rows of tile i / 4 held by this lane
+      ru[i] = (t < L && e_lane < dv) ? gu[(t0 + t) * dv + e_lane] : 0.f;
     }
-    ralpha = 1.f;
-    rbeta = 0.f;
-    if (tid < L) {
-      ralpha = galpha[t0 + tid];
-      rbeta = gbeta[t0 + tid];
-    }
+    ralpha = (tid < L) ? galpha[t0 + tid] : 1.f;
   };
 
-  // ---- state: H[c][e], e = e_base + 16 wave + li; tile cb holds rows 16cb + 4g + q ----
-  const int e_lane = e_base + 16 * wave + li;
+  // state: H[c][e_lane]; tile cb holds rows 16cb + 4g + q
   f32x4 Hs[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
@@ -160,220 +410,54 @@ __global__ void __launch_bounds__(256) gdn_fwd_kernel(GdnArgs a) {
       Hs[cb][qq] = (a.init && e_lane < dv) ? a.init[(bh * DK + c) * dv + e_lane] : 0.f;
     }
 
+  const int nchunks = a.nch;
   if (nchunks > 0) load(0);
 
   for (int n = 0; n < nchunks; ++n) {
     const int L = chunk_len(n);
     const int64_t t0 = (int64_t)n * C;
 
-    // ---- P0: tiles; k normalised per row; decay scan ---------------------------------
+    // ---- tiles, k^, decay; this lane's U0 into accumulator-shaped registers -------------
+    gdn::stage_khat<TIn, DK>(rk, sK, tid);
+    gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rq, sQ, tid);
+    gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rw, sW, tid);
+    f32x4 U0[4];
 #pragma unroll
-    for (int j = 0; j < K::NVQ; ++j) {
-      const int vi = tid + 256 * j, r = vi / K::VPRQ, c = (vi % K::VPRQ) * VE;
-      float fk[VE];
-      unpack<TIn, VE>(fk, rk[j]);
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < VE; ++e) ss += fk[e] * fk[e];
-      // the row's VPRQ vectors sit in VPRQ consecutive lanes
-#pragma unroll
-      for (int d = 1; d < K::VPRQ; d <<= 1) ss += __shfl_xor(ss, d);
-      const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
-#pragma unroll
-      for (int e = 0; e < VE; ++e) fk[e] *= inv;
-      st_lds<TIn, VE>(sK + r * LDK + c, fk);
-      st_words_lds<4>(sQ + r * LDK + c, rq[j]);
-    }
-    {
-      constexpr int VPRV = XW / VE;
-#pragma unroll
-      for (int j = 0; j < K::NVV; ++j) {
-        const int vi = tid + 256 * j, r = vi / VPRV, c = (vi % VPRV) * VE;
-        st_words_lds<4>(sV + r * LDV + c, rv[j]);
-      }
-    }
-    if (wave == 0) {
-      float x = ralpha; // rows past L carry alpha = 1, beta = 0
-      for (int d = 1; d < 64; d <<= 1) {
-        const float o = __shfl_up(x, d);
-        if (lane >= d) x *= o;
-      }
-      sG[lane] = x;
-      sBeta[lane] = rbeta;
-    }
-    __syncthreads();
-    const float gL = sG[C - 1]; // = g[L-1]
-
-    // ---- P1: A = strictly lower (beta_t g_t / g_j) k^_t . k^_j, fp32 ------------------
-    // tile (tb, jb), jb <= tb: 10 tiles over 4 waves
-    static_for<0, 16>([&](auto I) {
-      constexpr int tb = I / 4, jb = I % 4;
-      if constexpr (jb <= tb) {
-        constexpr int pos = tb * (tb + 1) / 2 + jb;
-        if (pos % 4 == wave) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          const TIn *at = sK + (16 * tb + li) * LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
-          const TIn *bj = sK + (16 * jb + li) * LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
-#pragma unroll
-          for (int u = 0; u < DK / KU; ++u)
-            acc = mma(acc, ld_frag_c_at<TIn, true>(bj, u, g), ld_frag_c_at<TIn, true>(at, u, g));
-          // acc[qq] = k^_j . k^_t with j = 16 jb + 4g + qq, t = 16 tb + li
-          const int t = 16 * tb + li;
-          const float bt = sBeta[t] * sG[t];
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const int j = 16 * jb + 4 * g + qq;
-            sAf[t * C + j] = (j < t) ? bt / sG[j] * acc[qq] : 0.f;
-          }
-        }
-      }
-    });
-    __syncthreads();
-
-    // ---- P2: diagonal blocks of T = (I + A)^-1 by forward substitution ----------------
-    if (li == lane) { // lanes 0..15 of every wave: wave w inverts diagonal block w
-      const int base = 16 * wave;
-      float col[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = (i == li) ? 1.f : 0.f;
-#pragma unroll
-        for (int kk = 0; kk < i; ++kk) s -= sAf[(base + i) * C + base + kk] * col[kk];
-        col[i] = (i < li) ? 0.f : s;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sTf[(base + i) * C + base + li] = col[i];
-    }
-    __syncthreads();
-
-    // ---- P3: off-diagonal blocks, block row by block row:
-    //      T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj), wave j computes block (i, j)
-    static_for<1, 4>([&](auto IB) {
-      constexpr int ib = IB;
-      if (wave < ib) {
-        const int jb = wave;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = jb; kb < ib; ++kb) {
-          // A operand: A[16ib + li][16kb + 4g + r]; B operand: T[16kb + 4g + r][16jb + li]
-          const f32x4 fa = *reinterpret_cast<const f32x4 *>(sAf + (16 * ib + li) * C + 16 * kb + 4 * g);
-          const float *tb = sTf + (16 * kb + 4 * g) * C + 16 * jb + li;
-          const f32x4 fb = {tb[0], tb[C], tb[2 * C], tb[3 * C]};
-          x = mma(x, fa, fb);
-        }
-        // x[qq] = X[16ib-local row 4g + qq][col li]: as a B operand (k = 4g + qq)
-        const f32x4 ft = *reinterpret_cast<const f32x4 *>(sTf + (16 * ib + li) * C + 16 * ib + 4 * g);
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        y = mma(y, ft, x);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) sTf[(16 * ib + 4 * g + qq) * C + 16 * jb + li] = -y[qq];
-      }
-      __syncthreads();
-    });
-
-    // ---- P4: Tb = T diag(beta), Tg = T diag(beta g) in the MFMA input type ---------------
-#pragma unroll
-    for (int i = 0; i < C * C / 256; ++i) {
-      const int idx = tid + 256 * i, t = idx / C, j = idx % C;
-      const float tv = (j <= t) ? sTf[t * C + j] : 0.f;
-      const float bj = sBeta[j];
-      sTb[t * LDT + j] = (TIn)(tv * bj);
-      sTg[t * LDT + j] = (TIn)(tv * bj * sG[j]);
-    }
-    // next chunk's inputs go out now; P0 of the next iteration consumes them
+    for (int tb = 0; tb < 4; ++tb) U0[tb] = f32x4{ru[4 * tb], ru[4 * tb + 1], ru[4 * tb + 2], ru[4 * tb + 3]};
+    if (wave == 0) sG[lane] = gdn::decay_scan(ralpha, lane);
     if (n + 1 < nchunks) load(n + 1);
     __syncthreads();
+    const float gL = sG[C - 1]; // = g[L-1]: rows past the end carry alpha = 1
 
-    // ---- P5: W = Tg K^ (all dk columns), U0 = Tb V (this wave's columns), masked scores
-    constexpr int NZU = C / KU;
-    f32x4 U0[4];
-    {
-      // W tiles (tb, cb): 4 * NCB tiles over the 4 waves
+    // ---- masked scores (shared); U = U0 - W H (this wave's columns) ----------------------
+    gdn::scores<TIn, DK>(sQ, sK, sG, sP, wave, g, li);
+    Frag<TIn> hf[DK / KU];
 #pragma unroll
-      for (int ti = 0; ti < NCB; ++ti) {
-        const int tile = wave * NCB + ti, tb = tile / NCB, cb = tile % NCB;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const TIn *ta = sTg + (16 * tb + li) * LDT + 4 * g;
-#pragma unroll
-        for (int u = 0; u < NZU; ++u)
-          acc = mma(acc, ld_frag_at<TIn, true>(ta, u), ld_frag_t<TIn, true>(sK, LDK, 16 * cb, u, g, li));
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) sW[(16 * tb + 4 * g + qq) * LDK + 16 * cb + li] = (TIn)acc[qq];
-      }
-      Frag<TIn> vf[NZU];
-#pragma unroll
-      for (int u = 0; u < NZU; ++u) vf[u] = ld_frag_t<TIn, true>(sV, LDV, 16 * wave, u, g, li);
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const TIn *ta = sTb + (16 * tb + li) * LDT + 4 * g;
-#pragma unroll
-        for (int u = 0; u < NZU; ++u) acc = mma(acc, ld_frag_at<TIn, true>(ta, u), vf[u]);
-        U0[tb] = acc;
-      }
-      // score tiles P[t][j] = (g_t / g_j) q_t . k^_j, j <= t; image of tile (tb, jb) is
-      // row-major [t][j]
-      static_for<0, 16>([&](auto I) {
-        constexpr int tb = I / 4, jb = I % 4;
-        if constexpr (jb <= tb) {
-          constexpr int pos = tb * (tb + 1) / 2 + jb;
-          if (pos % 4 == wave) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const TIn *kj = sK + (16 * jb + li) * LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
-            const TIn *qt = sQ + (16 * tb + li) * LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
-#pragma unroll
-            for (int u = 0; u < DK / KU; ++u)
-              acc = mma(acc, ld_frag_c_at<TIn, true>(kj, u, g), ld_frag_c_at<TIn, true>(qt, u, g));
-            // acc[qq]: j = 16 jb + 4g + qq, t = 16 tb + li
-            const int t = 16 * tb + li;
-            const float gt = sG[t];
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              const int j = 16 * jb + 4 * g + qq;
-              acc[qq] = (j <= t) ? gt / sG[j] * acc[qq] : 0.f;
-            }
-            st_ptile<TIn>(sP + I * 256 + li * 16 + 4 * g, acc);
-          }
-        }
-      });
+    for (int u = 0; u < DK / KU; ++u) {
+      if constexpr (sizeof(TIn) == 2) hf[u] = acc_frag_bf(Hs[2 * u], Hs[2 * u + 1]);
+      else hf[u] = Hs[u];
     }
-    __syncthreads();
-
-    // ---- P6: U = U0 - W H (this wave's columns); U and U (.) g_L / g to LDS ------------
-    {
-      Frag<TIn> hf[DK / KU];
 #pragma unroll
-      for (int u = 0; u < DK / KU; ++u) {
-        if constexpr (sizeof(TIn) == 2) hf[u] = acc_frag_bf(Hs[2 * u], Hs[2 * u + 1]);
-        else hf[u] = Hs[u];
-      }
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      const TIn *wa = sW + (16 * tb + li) * LDK + 4 * g;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        const TIn *wa = sW + (16 * tb + li) * LDK + 4 * g;
+      for (int u = 0; u < DK / KU; ++u) x = mma(x, ld_frag_at<TIn, true>(wa, u), hf[u]);
 #pragma unroll
-        for (int u = 0; u < DK / KU; ++u) x = mma(x, ld_frag_at<TIn, true>(wa, u), hf[u]);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int t = 16 * tb + 4 * g + qq;
-          const float uval = U0[tb][qq] - x[qq];
-          sU[t * LDV + 16 * wave + li] = (TIn)uval;
-          sUs[t * LDV + 16 * wave + li] = (TIn)(uval * (gL / sG[t]));
-        }
+      for (int qq = 0; qq < 4; ++qq) {
+        const int t = 16 * tb + 4 * g + qq;
+        const float uval = U0[tb][qq] - x[qq];
+        sU[t * LDV + 16 * wave + li] = (TIn)uval;
+        sUs[t * LDV + 16 * wave + li] = (TIn)(uval * (gL / sG[t]));
       }
     }
     __syncthreads();
 
-    // ---- P7: O = (masked scores) U + diag(g) Q H --------------------------------------
+    // ---- O = (masked scores) U + diag(g) Q H ---------------------------------------------
     {
       Frag<TIn> uf[NZU];
 #pragma unroll
       for (int u = 0; u < NZU; ++u) uf[u] = ld_frag_t<TIn, true>(sU, LDV, 16 * wave, u, g, li);
-      Frag<TIn> hf[DK / KU];
-#pragma unroll
-      for (int u = 0; u < DK / KU; ++u) {
-        if constexpr (sizeof(TIn) == 2) hf[u] = acc_frag_bf(Hs[2 * u], Hs[2 * u + 1]);
-        else hf[u] = Hs[u];
-      }
       static_for<0, 4>([&](auto TB) {
         constexpr int tb = TB;
         f32x4 oi = {0.f, 0.f, 0.f, 0.f};
@@ -402,7 +486,7 @@ __global__ void __launch_bounds__(256) gdn_fwd_kernel(GdnArgs a) {
       });
     }
 
-    // ---- P8: H <- g_L H + K^^T (U (.) g_L / g) -----------------------------------------
+    // ---- H <- g_L H + K^^T (U (.) g_L / g) ------------------------------------------------
     {
       Frag<TIn> usf[NZU];
 #pragma unroll
