@@ -74,7 +74,6 @@ struct BwdCfg {
   // register prefetch: 16-byte vectors per thread
   static constexpr int NVX = C * DY / VE / NT;
   static constexpr int NVZ = C * XW / VE / NT;
-  static constexpr int NVG = GATE ? C * GW / 4 / NT : 0;
   static constexpr int NVR = HAS_RQ ? C * XW / 4 / NT : 0;
   static_assert(NVX >= 1 && NVZ >= 1, "tile too small for the thread count");
   // gate scan: NSEG row segments of SEGR rows per column
@@ -215,7 +214,7 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
   // ---- register prefetch of one chunk ---------------------------------------------
   uint32_t rX[K::NVX][4], rY[K::NVX][4], rZ[K::NVZ][4];
   uint32_t rA[K::HAS_AUX ? K::NVZ : 1][4];
-  uint32_t rG[K::NVG > 0 ? K::NVG : 1][4];
+  float rG[K::GATE ? K::SEGR : 1]; // gate rows of this thread's (column, segment) in scan order
   uint32_t rR[K::NVR > 0 ? K::NVR : 1][4];
   float rTok = 1.f;
   auto load = [&](int n) {
@@ -248,15 +247,13 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
       }
     }
     if constexpr (K::GATE) {
-      constexpr int VPRG = GW / 4;
-      const float *gsrc = a.decay + bh * T * dk + goff;
+      // thread (column tid % GW, segment tid / GW) reads its SEGR rows: for each row the
+      // lanes of a wave read consecutive columns
+      const float *gsrc = a.decay + bh * T * dk + goff + tid % GW;
+      const int r0 = (tid / GW) * K::SEGR;
 #pragma unroll
-      for (int j = 0; j < K::NVG; ++j) {
-        const int vi = tid + 256 * j, r = vi / VPRG, c = (vi % VPRG) * 4;
-        uint4 x = make_uint4(0x3f800000u, 0x3f800000u, 0x3f800000u, 0x3f800000u); // 1.0f
-        if (r < L) x = *reinterpret_cast<const uint4 *>(gsrc + (t0 + r) * dk + c);
-        rG[j][0] = x.x; rG[j][1] = x.y; rG[j][2] = x.z; rG[j][3] = x.w;
-      }
+      for (int i = 0; i < K::SEGR; ++i)
+        rG[i] = (r0 + i < L) ? gsrc[(t0 + r0 + i) * dk] : 1.f; // past the end: no decay
     }
     if constexpr (K::TOKEN) {
       rTok = 1.f;
@@ -319,36 +316,25 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
 
     // ---- 1. decay inside the chunk: b = inclusive product down the rows -----------
     if constexpr (K::GATE) {
-      constexpr int VPRG = GW / 4;
-#pragma unroll
-      for (int j = 0; j < K::NVG; ++j) {
-        const int vi = tid + 256 * j, r = vi / VPRG, c = (vi % VPRG) * 4;
-        *reinterpret_cast<uint4 *>(sB + r * GW + c) = make_uint4(rG[j][0], rG[j][1], rG[j][2], rG[j][3]);
-      }
-      __syncthreads();
+      // per (column, segment) product scan in registers; segment totals through LDS
       const int col = tid % GW, seg = tid / GW;
+      float bv[K::SEGR];
       float p = 1.f;
 #pragma unroll
       for (int i = 0; i < K::SEGR; ++i) {
-        const int r = seg * K::SEGR + i;
-        const float al = sB[r * GW + col];
-        if constexpr (ROLE == BWD_DK) araw[i] = al;
-        p *= al;
-        sB[r * GW + col] = p;
+        if constexpr (ROLE == BWD_DK) araw[i] = rG[i];
+        p *= rG[i];
+        bv[i] = p;
       }
+      float pre = 1.f;
       if constexpr (K::NSEG > 1) {
         sT[seg * K::TOT_W + col] = p;
         __syncthreads();
-        float pre = 1.f;
         for (int s2 = 0; s2 < seg; ++s2) pre *= sT[s2 * K::TOT_W + col];
-        if (seg > 0) {
-#pragma unroll
-          for (int i = 0; i < K::SEGR; ++i) sB[(seg * K::SEGR + i) * GW + col] *= pre;
-        }
-        if (seg == K::NSEG - 1) sBL[col] = p * pre;
-      } else {
-        sBL[col] = p;
       }
+#pragma unroll
+      for (int i = 0; i < K::SEGR; ++i) sB[(seg * K::SEGR + i) * GW + col] = bv[i] * pre;
+      if (seg == K::NSEG - 1) sBL[col] = p * pre;
     } else if constexpr (K::TOKEN) {
       if (wave == 0) {
         float x = rTok;
@@ -493,6 +479,15 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
       if constexpr (K::SPLIT) zl[u] = ld_frag_t<TIn, true>(sZL, LDZ, 16 * wave, u, g, li);
     }
 
+    // Output tiles are formed transposed (out^T = Z^T P^T + S^T X^T: the same fragments with
+    // the operands swapped), so a lane holds 4 adjacent columns of one row: 16-byte LDS
+    // reads of the per-element factors and 8-byte (bf16) stores.
+    const int xc = 16 * wave + 4 * g; // first of this lane's 4 output columns
+    auto b_at4 = [&](int r) -> f32x4 {
+      if constexpr (K::GATE) return *reinterpret_cast<const f32x4 *>(sB + r * GW + xc);
+      else if constexpr (K::HAS_B) return f32x4{sB[r], sB[r], sB[r], sB[r]};
+      else return f32x4{1.f, 1.f, 1.f, 1.f};
+    };
     static_for<0, 4>([&](auto RB) {
       constexpr int rb = RB;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -504,15 +499,15 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
           constexpr int TB = tile_on<REV>(rb, 2 * u + 1) ? rb * 4 + 2 * u + 1 : -1;
           if constexpr (TA >= 0 || TB >= 0) {
             const Frag<TIn> ph = ld_ptile2<TIn, TA, TB>(sP + li * 16 + 4 * g);
-            acc = mma(acc, ph, zf[u]);
+            acc = mma(acc, zf[u], ph);
             if constexpr (K::SPLIT) {
-              acc = mma(acc, ld_ptile2<TIn, TA, TB>(sPL + li * 16 + 4 * g), zf[u]);
-              acc = mma(acc, ph, zl[u]);
+              acc = mma(acc, zf[u], ld_ptile2<TIn, TA, TB>(sPL + li * 16 + 4 * g));
+              acc = mma(acc, zl[u], ph);
             }
           }
         } else {
           constexpr int TA = tile_on<REV>(rb, u) ? rb * 4 + u : -1;
-          if constexpr (TA >= 0) acc = mma(acc, ld_ptile2<TIn, TA, -1>(sP + li * 16 + 4 * g), zf[u]);
+          if constexpr (TA >= 0) acc = mma(acc, zf[u], ld_ptile2<TIn, TA, -1>(sP + li * 16 + 4 * g));
         }
       });
       // inter-chunk: sum over y of X[r][y] S[y][x]
@@ -523,32 +518,43 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
         const Frag<TIn> xf = ld_frag_at<TIn, true>(xa, u);
         if constexpr (sizeof(TIn) == 2) sf = acc_frag_bf(S[2 * u], S[2 * u + 1]);
         else sf = S[u];
-        acc = mma(acc, xf, sf);
+        acc = mma(acc, sf, xf);
         if constexpr (K::SPLIT) {
           const f32x4 l0 = S[2 * u] - bf_round4(S[2 * u]), l1 = S[2 * u + 1] - bf_round4(S[2 * u + 1]);
-          acc = mma(acc, xf, acc_frag_bf(l0, l1));
+          acc = mma(acc, acc_frag_bf(l0, l1), xf);
         }
       }
-      // acc[qq] = out[r = 16 rb + 4g + qq][x]
+      // acc[qq] = out[r = 16 rb + li][xc + qq]
+      const int r = 16 * rb + li;
+      const int64_t t = t0 + r;
+      if constexpr (ROLE == BWD_DQ) {
+        const f32x4 dqb = acc * b_at4(r);
+        const f32x4 qb = *reinterpret_cast<const f32x4 *>(sA + r * XW + xc);
+        if (r < L) {
+          f32x4 dq4;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int r = 16 * rb + 4 * g + qq;
-        const int64_t t = t0 + r;
-        if constexpr (ROLE == BWD_DQ) {
-          const float dqb = acc[qq] * b_at(r, x);
-          const float qb = sA[r * XW + x];
-          if (r < L) {
-            ((TIn *)a.grad_q)[(bh * T + t) * dk + zoff + x] = (TIn)(dqb * phi_d(qb, elu1));
-            if (want_dg) a.rq[(bh * T + t) * dk + zoff + x] = qb * dqb;
-          }
-        } else if constexpr (ROLE == BWD_DK) {
-          const float dkb = acc[qq] / b_at(r, x);
-          const float kb = sA[r * XW + x];
-          if (r < L) ((TIn *)a.grad_k)[(bh * T + t) * dk + zoff + x] = (TIn)(dkb * phi_d(kb, elu1));
-          if constexpr (K::HAS_RQ) sA[r * XW + x] = (r < L) ? sR[r * XW + x] - kb * dkb : 0.f;
-        } else {
-          if (r < L) ((TIn *)a.grad_v)[(bh * T + t) * dv + zoff + x] = (TIn)acc[qq];
+          for (int qq = 0; qq < 4; ++qq) dq4[qq] = dqb[qq] * phi_d(qb[qq], elu1);
+          st_out4<TIn>((TIn *)a.grad_q + (bh * T + t) * dk + zoff + xc, dq4);
+          if (want_dg) *reinterpret_cast<f32x4 *>(a.rq + (bh * T + t) * dk + zoff + xc) = qb * dqb;
         }
+      } else if constexpr (ROLE == BWD_DK) {
+        const f32x4 bb = b_at4(r);
+        f32x4 dkb;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) dkb[qq] = acc[qq] / bb[qq];
+        const f32x4 kb = *reinterpret_cast<const f32x4 *>(sA + r * XW + xc);
+        if (r < L) {
+          f32x4 dk4;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) dk4[qq] = dkb[qq] * phi_d(kb[qq], elu1);
+          st_out4<TIn>((TIn *)a.grad_k + (bh * T + t) * dk + zoff + xc, dk4);
+        }
+        if constexpr (K::HAS_RQ) {
+          const f32x4 rr = *reinterpret_cast<const f32x4 *>(sR + r * XW + xc) - kb * dkb;
+          *reinterpret_cast<f32x4 *>(sA + r * XW + xc) = (r < L) ? rr : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      } else {
+        if (r < L) st_out4<TIn>((TIn *)a.grad_v + (bh * T + t) * dv + zoff + xc, acc);
       }
     });
 
