@@ -65,7 +65,7 @@ struct BwdCfg {
   static constexpr bool TOKEN = DECAY == DECAY_TOKEN;
   // b tile columns: per-key gate over the decayed dimension, else one column
   static constexpr int GW = GATE ? (ROLE == BWD_DV ? DY : XW) : 1;
-  static constexpr bool HAS_AUX = ROLE != BWD_DV; // phi(q) (DQ) / phi(k) then r (DK)
+  static constexpr bool HAS_AUX = ROLE != BWD_DV; // phi(q) (DQ) / phi(k) (DK) read per lane
   static constexpr bool HAS_RQ = ROLE == BWD_DK && (GATE || TOKEN);
   // bf16 dq / dk roles carry the rounded MFMA operands as hi + lo pairs (scores, Z, state)
   // so their outputs, and the decay gradient summed from them over the sequence, keep
@@ -74,7 +74,6 @@ struct BwdCfg {
   // register prefetch: 16-byte vectors per thread
   static constexpr int NVX = C * DY / VE / NT;
   static constexpr int NVZ = C * XW / VE / NT;
-  static constexpr int NVR = HAS_RQ ? C * XW / 4 / NT : 0;
   static_assert(NVX >= 1 && NVZ >= 1, "tile too small for the thread count");
   // gate scan: NSEG row segments of SEGR rows per column
   static constexpr int NSEG = GATE ? NT / GW : 1;
@@ -88,9 +87,8 @@ struct BwdCfg {
   static constexpr int OFF_PL = OFF_P + 16 * 256 * ES;                // score lo (SPLIT)
   static constexpr int OFF_B = OFF_PL + (SPLIT ? 16 * 256 * ES : 0);
   static constexpr int OFF_BL = OFF_B + (HAS_B ? C * GW * 4 : 0);
-  static constexpr int OFF_AUX = OFF_BL + (HAS_B ? GW * 4 : 0);
-  static constexpr int OFF_RQ = OFF_AUX + (HAS_AUX ? C * XW * 4 : 0);
-  static constexpr int OFF_TOT = OFF_RQ + (HAS_RQ ? C * XW * 4 : 0);
+  static constexpr int OFF_R = OFF_BL + (HAS_B ? GW * 4 : 0);       // DK: r for the scan
+  static constexpr int OFF_TOT = OFF_R + (HAS_RQ ? C * XW * 4 : 0);
   static constexpr int TOT_W = (GATE ? GW : 1) > 64 ? (GATE ? GW : 1) : 64;
   static constexpr int LDS = OFF_TOT + 4 * TOT_W * 4;
   static constexpr bool FITS = LDS <= kMaxLds;
@@ -155,8 +153,7 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
   TIn *sPL = reinterpret_cast<TIn *>(lds + K::OFF_PL);
   float *sB = reinterpret_cast<float *>(lds + K::OFF_B);
   float *sBL = reinterpret_cast<float *>(lds + K::OFF_BL);
-  float *sA = reinterpret_cast<float *>(lds + K::OFF_AUX);
-  float *sR = reinterpret_cast<float *>(lds + K::OFF_RQ);
+  float *sA = reinterpret_cast<float *>(lds + K::OFF_R);
   float *sT = reinterpret_cast<float *>(lds + K::OFF_TOT);
 
   const int tid = threadIdx.x;
@@ -213,9 +210,7 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
 
   // ---- register prefetch of one chunk ---------------------------------------------
   uint32_t rX[K::NVX][4], rY[K::NVX][4], rZ[K::NVZ][4];
-  uint32_t rA[K::HAS_AUX ? K::NVZ : 1][4];
   float rG[K::GATE ? K::SEGR : 1]; // gate rows of this thread's (column, segment) in scan order
-  uint32_t rR[K::NVR > 0 ? K::NVR : 1][4];
   float rTok = 1.f;
   auto load = [&](int n) {
     const int L = chunk_len(n);
@@ -235,16 +230,9 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < K::NVZ; ++j) {
       const int vi = tid + 256 * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
-      uint4 z = make_uint4(0, 0, 0, 0), x = z;
-      if (r < L) {
-        z = *reinterpret_cast<const uint4 *>(srcZ + (t0 + r) * ldz + zoff + c);
-        if constexpr (K::HAS_AUX)
-          x = *reinterpret_cast<const uint4 *>(srcA + (t0 + r) * dk + zoff + c);
-      }
+      uint4 z = make_uint4(0, 0, 0, 0);
+      if (r < L) z = *reinterpret_cast<const uint4 *>(srcZ + (t0 + r) * ldz + zoff + c);
       rZ[j][0] = z.x; rZ[j][1] = z.y; rZ[j][2] = z.z; rZ[j][3] = z.w;
-      if constexpr (K::HAS_AUX) {
-        rA[j][0] = x.x; rA[j][1] = x.y; rA[j][2] = x.z; rA[j][3] = x.w;
-      }
     }
     if constexpr (K::GATE) {
       // thread (column tid % GW, segment tid / GW) reads its SEGR rows: for each row the
@@ -258,18 +246,6 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
     if constexpr (K::TOKEN) {
       rTok = 1.f;
       if (tid < L) rTok = a.decay[bh * T + t0 + tid];
-    }
-    if constexpr (K::HAS_RQ) {
-      if (want_dg) {
-        constexpr int VPRR = XW / 4;
-#pragma unroll
-        for (int j = 0; j < K::NVR; ++j) {
-          const int vi = tid + 256 * j, r = vi / VPRR, c = (vi % VPRR) * 4;
-          uint4 x = make_uint4(0, 0, 0, 0);
-          if (r < L) x = *reinterpret_cast<const uint4 *>(a.rq + (bh * T + t0 + r) * dk + zoff + c);
-          rR[j][0] = x.x; rR[j][1] = x.y; rR[j][2] = x.z; rR[j][3] = x.w;
-        }
-      }
     }
   };
 
@@ -374,7 +350,7 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
           for (int e = 0; e < VE; ++e) {
             const float bb = b_at(r, c + e);
             const bool ok = r < L;
-            fx[e] = ok ? phi_f(fx[e], elu1) / bb : 0.f;
+            fx[e] = ok ? phi_f(fx[e], elu1) * rcp_f(bb) : 0.f;
             fy[e] = ok ? phi_f(fy[e], elu1) * bb : 0.f;
           }
           st_lds<TIn, VE>(sX + r * LDX + c, fx);
@@ -390,16 +366,14 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
         if constexpr (ROLE == BWD_DV) {
           st_words_lds<4>(sZ + r * LDZ + c, rZ[j]);
         } else {
-          float fz[VE], fa[VE];
+          float fz[VE];
           unpack<TIn, VE>(fz, rZ[j]);
-          unpack<TIn, VE>(fa, rA[j]);
 #pragma unroll
           for (int e = 0; e < VE; ++e) {
             const float bb = b_at(r, c + e);
             const bool ok = r < L;
             const float pz = phi_f(fz[e], elu1);
-            fz[e] = ok ? (ROLE == BWD_DQ ? pz / bb : pz * bb) : 0.f;
-            fa[e] = ok ? phi_f(fa[e], elu1) : 0.f;
+            fz[e] = ok ? (ROLE == BWD_DQ ? pz * rcp_f(bb) : pz * bb) : 0.f;
           }
           st_lds<TIn, VE>(sZ + r * LDZ + c, fz);
           if constexpr (K::SPLIT) {
@@ -407,19 +381,6 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < VE; ++e) fl[e] = fz[e] - (float)(TIn)fz[e];
             st_lds<TIn, VE>(sZL + r * LDZ + c, fl);
-          }
-#pragma unroll
-          for (int e = 0; e < VE; e += 4)
-            *reinterpret_cast<float4 *>(sA + r * XW + c + e) = make_float4(fa[e], fa[e + 1], fa[e + 2], fa[e + 3]);
-        }
-      }
-      if constexpr (K::HAS_RQ) {
-        if (want_dg) {
-          constexpr int VPRR = XW / 4;
-#pragma unroll
-          for (int j = 0; j < K::NVR; ++j) {
-            const int vi = tid + 256 * j, r = vi / VPRR, c = (vi % VPRR) * 4;
-            *reinterpret_cast<uint4 *>(sR + r * XW + c) = make_uint4(rR[j][0], rR[j][1], rR[j][2], rR[j][3]);
           }
         }
       }
@@ -488,6 +449,50 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
       else if constexpr (K::HAS_B) return f32x4{sB[r], sB[r], sB[r], sB[r]};
       else return f32x4{1.f, 1.f, 1.f, 1.f};
     };
+    // this lane's rows 16 rb + li, columns xc .. xc+3: raw q (dq role) or k (dk role) for
+    // phi and phi', and phi(q) dphi(q) from the dq pass (dk role) - read from global
+    // memory now, used after the MFMAs below
+    uint32_t raux[4][K::ES]; // 4 elements of the input type
+    f32x4 rqv[4];
+    if constexpr (K::HAS_AUX) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int r = 16 * rb + li;
+        const TIn *pa = srcA + (t0 + r) * dk + zoff + xc;
+        if constexpr (K::ES == 2) {
+          uint2 w2 = make_uint2(0, 0);
+          if (r < L) w2 = *reinterpret_cast<const uint2 *>(pa);
+          raux[rb][0] = w2.x; raux[rb][1] = w2.y;
+        } else {
+          uint4 w4 = make_uint4(0, 0, 0, 0);
+          if (r < L) w4 = *reinterpret_cast<const uint4 *>(pa);
+          raux[rb][0] = w4.x; raux[rb][1] = w4.y; raux[rb][2] = w4.z; raux[rb][3] = w4.w;
+        }
+        rqv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (K::HAS_RQ) {
+          if (want_dg && r < L) rqv[rb] = *reinterpret_cast<const f32x4 *>(a.rq + (bh * T + t0 + r) * dk + zoff + xc);
+        }
+      }
+    }
+    auto phi4 = [&](int rb) -> f32x4 {
+      float f[4];
+      unpack<TIn, 4>(f, raux[rb]);
+      return f32x4{phi_f(f[0], elu1), phi_f(f[1], elu1), phi_f(f[2], elu1), phi_f(f[3], elu1)};
+    };
+    (void)phi4;
+    (void)rqv;
+    // the state as MFMA fragments (hi and, for split roles, lo parts), once per chunk
+    Frag<TIn> sfh[DY / KU], sfl[K::SPLIT ? DY / KU : 1];
+#pragma unroll
+    for (int u = 0; u < DY / KU; ++u) {
+      if constexpr (sizeof(TIn) == 2) {
+        sfh[u] = acc_frag_bf(S[2 * u], S[2 * u + 1]);
+        if constexpr (K::SPLIT)
+          sfl[u] = acc_frag_bf(S[2 * u] - bf_round4(S[2 * u]), S[2 * u + 1] - bf_round4(S[2 * u + 1]));
+      } else {
+        sfh[u] = S[u];
+      }
+    }
     static_for<0, 4>([&](auto RB) {
       constexpr int rb = RB;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -514,22 +519,16 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
       const TIn *xa = sX + (16 * rb + li) * LDX + 4 * g;
 #pragma unroll
       for (int u = 0; u < DY / KU; ++u) {
-        Frag<TIn> sf;
         const Frag<TIn> xf = ld_frag_at<TIn, true>(xa, u);
-        if constexpr (sizeof(TIn) == 2) sf = acc_frag_bf(S[2 * u], S[2 * u + 1]);
-        else sf = S[u];
-        acc = mma(acc, sf, xf);
-        if constexpr (K::SPLIT) {
-          const f32x4 l0 = S[2 * u] - bf_round4(S[2 * u]), l1 = S[2 * u + 1] - bf_round4(S[2 * u + 1]);
-          acc = mma(acc, acc_frag_bf(l0, l1), xf);
-        }
+        acc = mma(acc, sfh[u], xf);
+        if constexpr (K::SPLIT) acc = mma(acc, sfl[u], xf);
       }
       // acc[qq] = out[r = 16 rb + li][xc + qq]
       const int r = 16 * rb + li;
       const int64_t t = t0 + r;
       if constexpr (ROLE == BWD_DQ) {
         const f32x4 dqb = acc * b_at4(r);
-        const f32x4 qb = *reinterpret_cast<const f32x4 *>(sA + r * XW + xc);
+        const f32x4 qb = phi4(rb);
         if (r < L) {
           f32x4 dq4;
 #pragma unroll
@@ -541,8 +540,8 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
         const f32x4 bb = b_at4(r);
         f32x4 dkb;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) dkb[qq] = acc[qq] / bb[qq];
-        const f32x4 kb = *reinterpret_cast<const f32x4 *>(sA + r * XW + xc);
+        for (int qq = 0; qq < 4; ++qq) dkb[qq] = acc[qq] * rcp_f(bb[qq]);
+        const f32x4 kb = phi4(rb);
         if (r < L) {
           f32x4 dk4;
 #pragma unroll
@@ -550,7 +549,7 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
           st_out4<TIn>((TIn *)a.grad_k + (bh * T + t) * dk + zoff + xc, dk4);
         }
         if constexpr (K::HAS_RQ) {
-          const f32x4 rr = *reinterpret_cast<const f32x4 *>(sR + r * XW + xc) - kb * dkb;
+          const f32x4 rr = rqv[rb] - kb * dkb;
           *reinterpret_cast<f32x4 *>(sA + r * XW + xc) = (r < L) ? rr : f32x4{0.f, 0.f, 0.f, 0.f};
         }
       } else {
