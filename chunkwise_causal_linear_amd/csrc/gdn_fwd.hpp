@@ -56,14 +56,16 @@ struct GdnCfg {
   static constexpr int NCB = DK / 16;           // 16-row blocks of the state
   static constexpr int NZU = C / KU;            // K units over the chunk rows
   static_assert(NVQ >= 1 && NVV >= 1 && VPRQ <= 64, "tile shape");
-  // pre-pass LDS
+  // pre-pass LDS: A (fp32) gives way to Tb and Tg once T is complete, T (fp32) to the V
+  // slices once Tb and Tg are formed, which fits three workgroups per CU (bf16, dk 128)
+  static constexpr int cmax(int x, int y) { return x > y ? x : y; }
   static constexpr int P_K = 0;
-  static constexpr int P_V = P_K + C * LDK * ES;
-  static constexpr int P_TB = P_V + C * LDV * ES;
+  static constexpr int P_A = P_K + C * LDK * ES;    // A, fp32 [C][C]; later Tb, Tg
+  static constexpr int P_TB = P_A;
   static constexpr int P_TG = P_TB + C * LDT * ES;
-  static constexpr int P_A = P_TG + C * LDT * ES;   // A, fp32 [C][C]
-  static constexpr int P_T = P_A + C * C * 4;       // T, fp32 [C][C]
-  static constexpr int P_G = P_T + C * C * 4;       // g [C], beta [C]
+  static constexpr int P_T = P_A + cmax(C * C * 4, 2 * C * LDT * ES); // T, fp32; later V
+  static constexpr int P_V = P_T;
+  static constexpr int P_G = P_T + cmax(C * C * 4, C * LDV * ES);     // g [C], beta [C]
   static constexpr int P_BETA = P_G + C * 4;
   static constexpr int P_LDS = P_BETA + C * 4;
   // state-pass LDS
