@@ -17,9 +17,9 @@
 // blocks of T are inverted by forward substitution, one wave each, and the off-diagonal
 // blocks follow block row by block row with fp32 MFMA; then W and U0 on MFMA, written to a
 // workspace: W in the input type, U0 in fp32).  The state pass streams the chunks, one
-// workgroup per (b, h, 64-wide slice of dv) with its state columns in MFMA accumulators:
-// per chunk the masked scores, U = U0 - W H, the outputs and the state update, three
-// barriers, the next chunk's inputs prefetched into registers meanwhile.
+// workgroup per (b, h, 64-wide slice of dv): four consumer waves keep the state columns
+// in MFMA accumulators and compute per chunk the masked scores, U = U0 - W H, the outputs
+// and the state update, while four producer waves stage the next chunk's q, k^ and W.
 #pragma once
 
 #include "chunk_bwd.hpp" // shared MFMA / LDS fragment helpers
@@ -68,15 +68,17 @@ struct GdnCfg {
   static constexpr int P_G = P_T + cmax(C * C * 4, C * LDV * ES);     // g [C], beta [C]
   static constexpr int P_BETA = P_G + C * 4;
   static constexpr int P_LDS = P_BETA + C * 4;
-  // state-pass LDS
+  // state-pass LDS: two input stages {q, k^, W, g} (producer waves fill one while the
+  // consumer waves read the other), then the consumers' U, U (.) g_L / g and score tiles
   static constexpr int S_Q = 0;
   static constexpr int S_K = S_Q + C * LDK * ES;
   static constexpr int S_W = S_K + C * LDK * ES;
-  static constexpr int S_U = S_W + C * LDK * ES;    // U [C][LDV]
+  static constexpr int S_G = S_W + C * LDK * ES;    // g [C]
+  static constexpr int S_STAGE = S_G + C * 4;
+  static constexpr int S_U = 2 * S_STAGE;           // U [C][LDV]
   static constexpr int S_US = S_U + C * LDV * ES;   // U (.) g_L / g
   static constexpr int S_P = S_US + C * LDV * ES;   // masked scores, 16 tile images
-  static constexpr int S_G = S_P + 16 * 256 * ES;   // g [C]
-  static constexpr int S_LDS = S_G + C * 4;
+  static constexpr int S_LDS = S_P + 16 * 256 * ES;
   static constexpr bool FITS = P_LDS <= kMaxLds && S_LDS <= kMaxLds;
 };
 
@@ -336,19 +338,22 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
 }
 
 // ---- state pass ---------------------------------------------------------------------------
+// 8 waves: waves 4..7 (producers) load q, k and W of chunk n+1 into registers, normalise k
+// and write them, with the chunk's decay, into one LDS stage while waves 0..3 (consumers)
+// compute chunk n from the other stage; two barriers per chunk.
 template <typename TIn, int DK>
-__global__ void __launch_bounds__(256) gdn_state_kernel(GdnArgs a) {
+__global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
   using K = GdnCfg<TIn, DK>;
   constexpr int C = K::C, XW = K::XW, VE = K::VE, KU = K::KU, NCB = K::NCB, NZU = K::NZU;
   constexpr int LDK = K::LDK, LDV = K::LDV;
   __shared__ __attribute__((aligned(16))) unsigned char lds[K::S_LDS];
-  TIn *sQ = reinterpret_cast<TIn *>(lds + K::S_Q);
-  TIn *sK = reinterpret_cast<TIn *>(lds + K::S_K);
-  TIn *sW = reinterpret_cast<TIn *>(lds + K::S_W);
+  auto stage_q = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_Q); };
+  auto stage_k = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_K); };
+  auto stage_w = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_W); };
+  auto stage_g = [&](int s) { return reinterpret_cast<float *>(lds + s * K::S_STAGE + K::S_G); };
   TIn *sU = reinterpret_cast<TIn *>(lds + K::S_U);
   TIn *sUs = reinterpret_cast<TIn *>(lds + K::S_US);
   TIn *sP = reinterpret_cast<TIn *>(lds + K::S_P);
-  float *sG = reinterpret_cast<float *>(lds + K::S_G);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -361,45 +366,77 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(GdnArgs a) {
   const int64_t bh = unit / a.nvs;
   const int64_t T = a.T;
   const int dv = a.dv;
-  const int e_lane = vs * XW + 16 * wave + li; // this lane's value column
-  const TIn *gq = static_cast<const TIn *>(a.q) + bh * T * DK;
-  const TIn *gk = static_cast<const TIn *>(a.k) + bh * T * DK;
-  const TIn *gw = static_cast<const TIn *>(a.w) + bh * T * DK;
-  const float *gu = a.u0 + bh * T * dv;
-  TIn *gout = static_cast<TIn *>(a.out) + bh * T * dv;
-  const float *galpha = a.alpha + bh * T;
-
+  const int nchunks = a.nch;
   auto chunk_len = [&](int n) -> int {
     const int64_t l = T - (int64_t)n * C;
     return (int)(l < C ? l : C);
   };
 
-  // register prefetch of one chunk: q, k, W rows; this lane's U0 entries; alpha
-  uint32_t rq[K::NVQ][4], rk[K::NVQ][4], rw[K::NVQ][4];
+  if (wave >= 4) {
+    // =========================== producer waves ===========================
+    const int ptid = tid - 256, pwave = wave - 4;
+    const TIn *gq = static_cast<const TIn *>(a.q) + bh * T * DK;
+    const TIn *gk = static_cast<const TIn *>(a.k) + bh * T * DK;
+    const TIn *gw = static_cast<const TIn *>(a.w) + bh * T * DK;
+    const float *galpha = a.alpha + bh * T;
+    uint32_t rq[K::NVQ][4], rk[K::NVQ][4], rw[K::NVQ][4];
+    float ralpha = 1.f;
+    auto load = [&](int n) {
+      const int L = chunk_len(n);
+      const int64_t t0 = (int64_t)n * C;
+#pragma unroll
+      for (int j = 0; j < K::NVQ; ++j) {
+        const int vi = ptid + 256 * j, r = vi / K::VPRQ, c = (vi % K::VPRQ) * VE;
+        uint4 x = make_uint4(0, 0, 0, 0), y = x, z = x;
+        if (r < L) {
+          x = *reinterpret_cast<const uint4 *>(gq + (t0 + r) * DK + c);
+          y = *reinterpret_cast<const uint4 *>(gk + (t0 + r) * DK + c);
+          z = *reinterpret_cast<const uint4 *>(gw + (t0 + r) * DK + c);
+        }
+        rq[j][0] = x.x; rq[j][1] = x.y; rq[j][2] = x.z; rq[j][3] = x.w;
+        rk[j][0] = y.x; rk[j][1] = y.y; rk[j][2] = y.z; rk[j][3] = y.w;
+        rw[j][0] = z.x; rw[j][1] = z.y; rw[j][2] = z.z; rw[j][3] = z.w;
+      }
+      ralpha = (ptid < L) ? galpha[t0 + ptid] : 1.f; // past the end: no decay
+    };
+    auto stage = [&](int s) {
+      gdn::stage_khat<TIn, DK>(rk, stage_k(s), ptid);
+      gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rq, stage_q(s), ptid);
+      gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rw, stage_w(s), ptid);
+      if (pwave == 0) stage_g(s)[lane] = gdn::decay_scan(ralpha, lane);
+    };
+    if (nchunks > 0) {
+      load(0);
+      stage(0);
+      if (nchunks > 1) load(1);
+    }
+    __syncthreads();
+    for (int n = 0; n < nchunks; ++n) {
+      if (n + 1 < nchunks) {
+        stage((n + 1) & 1);
+        if (n + 2 < nchunks) load(n + 2);
+      }
+      __syncthreads(); // consumers: scores and U of chunk n written
+      __syncthreads(); // consumers: chunk n done; the next stage is complete
+    }
+    return;
+  }
+
+  // =========================== consumer waves ===========================
+  const int e_lane = vs * XW + 16 * wave + li; // this lane's value column
+  const float *gu = a.u0 + bh * T * dv;
+  TIn *gout = static_cast<TIn *>(a.out) + bh * T * dv;
+
+  // this lane's U0 entries of a chunk (rows 16 tb + 4g + q), prefetched one chunk ahead
   float ru[16];
-  float ralpha = 1.f;
-  auto load = [&](int n) {
+  auto load_u0 = [&](int n) {
     const int L = chunk_len(n);
     const int64_t t0 = (int64_t)n * C;
 #pragma unroll
-    for (int j = 0; j < K::NVQ; ++j) {
-      const int vi = tid + 256 * j, r = vi / K::VPRQ, c = (vi % K::VPRQ) * VE;
-      uint4 x = make_uint4(0, 0, 0, 0), y = x, z = x;
-      if (r < L) {
-        x = *reinterpret_cast<const uint4 *>(gq + (t0 + r) * DK + c);
-        y = *reinterpret_cast<const uint4 *>(gk + (t0 + r) * DK + c);
-        z = *reinterpret_cast<const uint4 *>(gw + (t0 + r) * DK + c);
-      }
-      rq[j][0] = x.x; rq[j][1] = x.y; rq[j][2] = x.z; rq[j][3] = x.w;
-      rk[j][0] = y.x; rk[j][1] = y.y; rk[j][2] = y.z; rk[j][3] = y.w;
-      rw[j][0] = z.x; rw[j][1] = z.y; rw[j][2] = z.z; rw[j][3] = z.w;
-    }
-#pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int t = 16 * (i >> 2) + 4 * g + (i & 3); // rows of tile i / 4 held by this lane
+      const int t = 16 * (i >> 2) + 4 * g + (i & 3);
       ru[i] = (t < L && e_lane < dv) ? gu[(t0 + t) * dv + e_lane] : 0.f;
     }
-    ralpha = (tid < L) ? galpha[t0 + tid] : 1.f;
   };
 
   // state: H[c][e_lane]; tile cb holds rows 16cb + 4g + q
@@ -412,26 +449,23 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(GdnArgs a) {
       Hs[cb][qq] = (a.init && e_lane < dv) ? a.init[(bh * DK + c) * dv + e_lane] : 0.f;
     }
 
-  const int nchunks = a.nch;
-  if (nchunks > 0) load(0);
+  if (nchunks > 0) load_u0(0);
+  __syncthreads();
 
   for (int n = 0; n < nchunks; ++n) {
     const int L = chunk_len(n);
     const int64_t t0 = (int64_t)n * C;
-
-    // ---- tiles, k^, decay; this lane's U0 into accumulator-shaped registers -------------
-    gdn::stage_khat<TIn, DK>(rk, sK, tid);
-    gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rq, sQ, tid);
-    gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rw, sW, tid);
+    const TIn *sQ = stage_q(n & 1);
+    const TIn *sK = stage_k(n & 1);
+    const TIn *sW = stage_w(n & 1);
+    const float *sG = stage_g(n & 1);
     f32x4 U0[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) U0[tb] = f32x4{ru[4 * tb], ru[4 * tb + 1], ru[4 * tb + 2], ru[4 * tb + 3]};
-    if (wave == 0) sG[lane] = gdn::decay_scan(ralpha, lane);
-    if (n + 1 < nchunks) load(n + 1);
-    __syncthreads();
+    if (n + 1 < nchunks) load_u0(n + 1);
     const float gL = sG[C - 1]; // = g[L-1]: rows past the end carry alpha = 1
 
-    // ---- masked scores (shared); U = U0 - W H (this wave's columns) ----------------------
+    // ---- masked scores (shared by the consumer waves); U = U0 - W H (this wave's columns)
     gdn::scores<TIn, DK>(sQ, sK, sG, sP, wave, g, li);
     Frag<TIn> hf[DK / KU];
 #pragma unroll
@@ -455,7 +489,7 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(GdnArgs a) {
     }
     __syncthreads();
 
-    // ---- O = (masked scores) U + diag(g) Q H ---------------------------------------------
+    // ---- O = (masked scores) U + diag(g) Q H -------------------------------------------
     {
       Frag<TIn> uf[NZU];
 #pragma unroll
@@ -488,7 +522,7 @@ __global__ void __launch_bounds__(256) gdn_state_kernel(GdnArgs a) {
       });
     }
 
-    // ---- H <- g_L H + K^^T (U (.) g_L / g) ------------------------------------------------
+    // ---- H <- g_L H + K^^T (U (.) g_L / g) ----------------------------------------------
     {
       Frag<TIn> usf[NZU];
 #pragma unroll

@@ -20,7 +20,7 @@ hipError_t gdn_launch_impl(const GdnArgs &a, unsigned grid, hipStream_t s) {
   void *args[] = {&copy};
   const void *fn = PREP ? reinterpret_cast<const void *>(&gdn_prep_kernel<TIn, DK>)
                         : reinterpret_cast<const void *>(&gdn_state_kernel<TIn, DK>);
-  return hipLaunchKernel(fn, dim3(grid), dim3(GdnCfg<TIn, DK>::NT), args, 0, s);
+  return hipLaunchKernel(fn, dim3(grid), dim3(PREP ? GdnCfg<TIn, DK>::NT : 2 * GdnCfg<TIn, DK>::NT), args, 0, s);
 }
 
 template <typename TIn, int DK>

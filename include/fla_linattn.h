@@ -178,7 +178,7 @@ int fla_linattn_bwd(const void *q, const void *k, const void *v, const float *ga
  *   alpha : fp32 [B][H][T], the decay in (0, 1] (each chunk's product of alpha must stay
  *           above ~1e-30); beta: fp32 [B][H][T], the write strength in [0, 1]; 4-byte aligned.
  *   init_state, final_state: fp32 [B][H][dk][dv] (h = S^T as above) or NULL; may alias.
- *   dk in {64, 128}; dv in {64, 128, 256}; chunk = 64; flags: FLA_BF16 only.
+ *   dk in {64, 128} (fp32: 64); dv in {64, 128, 256}; chunk = 64; flags: FLA_BF16 only.
  * Two launches: a pre-pass forms, for every chunk at once, the parts that do not depend on
  * the state (W = T diag(beta g) K^ and U0 = T diag(beta) V with T the inverse of the
  * chunk's unit lower-triangular delta system), into a stream-ordered workspace of

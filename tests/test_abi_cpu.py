@@ -188,3 +188,4 @@ def test_gdn_rejects_on_host(lib):
     assert gdn(dk=32) == fla.FLA_ERR_UNSUPPORTED
     assert gdn(dv=96) == fla.FLA_ERR_UNSUPPORTED
     assert gdn(dk=256) == fla.FLA_ERR_UNSUPPORTED
+    assert gdn(dk=128) == fla.FLA_ERR_UNSUPPORTED                     # fp32 dk = 128

@@ -50,7 +50,7 @@ def check(w, inp, tag):
 
 
 SHAPES = [("bf16", 128, 128), ("bf16", 64, 64), ("bf16", 128, 256), ("bf16", 64, 192),
-          ("f32", 64, 64), ("f32", 64, 128), ("f32", 128, 128)]
+          ("f32", 64, 64), ("f32", 64, 128)]
 
 
 @pytest.mark.parametrize("dtype,dk,dv", SHAPES)
@@ -100,7 +100,11 @@ def test_gdn_empty_and_rejects():
     o, f = run_gpu(w, inp)
     assert o.shape == (2, 2, 0, 64)
     assert np.array_equal(f, inp["init"].astype(np.float64))
+    q = torch.zeros((1, 1, 64, 128), device="cuda")
     al = torch.ones((1, 1, 64), device="cuda")
+    with pytest.raises(fla.FlaError) as e:
+        fla.gdn_fwd(q, q, q, al, al)                       # fp32 dk = 128: two stages exceed the LDS
+    assert e.value.status == fla.FLA_ERR_UNSUPPORTED
     q32 = torch.zeros((1, 1, 64, 32), device="cuda", dtype=torch.bfloat16)
     with pytest.raises(fla.FlaError) as e:
         fla.gdn_fwd(q32, q32, q32, al, al)
