@@ -19,11 +19,14 @@
 // with  DQ: X = dO, Y = V, Z = Kb, S = H^T, forward in time, post = b;
 //       DK: X = V, Y = dO, Z = Qb, S = dH^T, reverse, post = 1/b;
 //       DV: X = Kb, Y = Qb, Z = dO, S = dH,  reverse, post = 1.
-// One workgroup (4 waves) owns one (b, h, 64-wide slice of the output dimension); wave w
-// owns output columns 16w..16w+15.  Per chunk: the decay is scanned down the chunk,
-// operand tiles are formed in LDS from registers prefetched one chunk ahead, the C x C
-// score tiles are computed once (shared through LDS), then each wave forms its output
-// tiles and updates its state columns.  MFMA conventions are the forward kernel's.
+// One workgroup owns one (b, h, 64-wide slice of the output dimension).  An operand group
+// of 4 waves scans the decay down each chunk and forms the chunk's operand tiles in LDS
+// from registers loaded ahead; an output group of 4 waves computes the C x C score tiles
+// once (shared through LDS), then wave w forms the output tiles of columns 16w..16w+15,
+// updates its state columns and (dk role) sums the decay gradient in registers.  Where two
+// operand stages fit in LDS the groups are separate waves working one chunk apart (two
+// barriers per chunk); otherwise one group of 4 waves does both in turn (four barriers).
+// MFMA conventions are the forward kernel's.
 #pragma once
 
 #include "chunk_fwd.hpp"
@@ -42,7 +45,7 @@ struct BwdArgs {
   float *dinit;        // [B][H][dk][dv] (written by DV) or null
   float *rq;           // workspace [B][H][T][dk]: phi(q) dphi(q) (DQ writes, DK reads) or null
   float *fterm;        // workspace [B][H][dk]: sum_e dfinal h_T (DQ writes, DK reads) or null
-  float *tpart;        // workspace [B][H][nsl][T]: per-slice d log a_t (token) or null
+  float *tpart;        // workspace [B][H][nsl][4][T]: d log a_t per slice and wave (token) or null
   int64_t T;
   int H, dk, dv;
   int nsl;             // 64-wide slices of the output dimension
@@ -53,7 +56,8 @@ struct BwdArgs {
 
 template <typename TIn, int ROLE, int DY, int DECAY>
 struct BwdCfg {
-  static constexpr int C = 64, XW = 64, NT = 256;
+  static constexpr int C = 64, XW = 64;
+  static constexpr int NTG = 256;                // threads of one wave group (4 waves)
   static constexpr int ES = sizeof(TIn);
   static constexpr int VE = 16 / ES;             // elements per 16-byte vector
   static constexpr int KU = ES == 2 ? 32 : 16;   // MFMA K unit
@@ -63,6 +67,7 @@ struct BwdCfg {
   static constexpr bool HAS_B = DECAY != DECAY_NONE;
   static constexpr bool GATE = DECAY == DECAY_GATE;
   static constexpr bool TOKEN = DECAY == DECAY_TOKEN;
+  static constexpr bool GAMMA = DECAY == DECAY_GAMMA;
   // b tile columns: per-key gate over the decayed dimension, else one column
   static constexpr int GW = GATE ? (ROLE == BWD_DV ? DY : XW) : 1;
   static constexpr bool HAS_AUX = ROLE != BWD_DV; // phi(q) (DQ) / phi(k) (DK) read per lane
@@ -71,28 +76,46 @@ struct BwdCfg {
   // so their outputs, and the decay gradient summed from them over the sequence, keep
   // close to fp32 accuracy; the dv role rounds once, like the forward pass
   static constexpr bool SPLIT = ES == 2 && ROLE != BWD_DV;
-  // register prefetch: 16-byte vectors per thread
-  static constexpr int NVX = C * DY / VE / NT;
-  static constexpr int NVZ = C * XW / VE / NT;
+  // register prefetch: 16-byte vectors per thread of the operand group
+  static constexpr int NVX = C * DY / VE / NTG;
+  static constexpr int NVZ = C * XW / VE / NTG;
   static_assert(NVX >= 1 && NVZ >= 1, "tile too small for the thread count");
   // gate scan: NSEG row segments of SEGR rows per column
-  static constexpr int NSEG = GATE ? NT / GW : 1;
+  static constexpr int NSEG = GATE ? NTG / GW : 1;
   static constexpr int SEGR = C / NSEG;
-  // LDS (bytes)
-  static constexpr int OFF_X = 0;
-  static constexpr int OFF_Y = OFF_X + C * LDX * ES;
-  static constexpr int OFF_Z = OFF_Y + C * LDX * ES;
-  static constexpr int OFF_ZL = OFF_Z + C * LDZ * ES;                 // Z lo (SPLIT)
-  static constexpr int OFF_P = OFF_ZL + (SPLIT ? C * LDZ * ES : 0);
-  static constexpr int OFF_PL = OFF_P + 16 * 256 * ES;                // score lo (SPLIT)
-  static constexpr int OFF_B = OFF_PL + (SPLIT ? 16 * 256 * ES : 0);
-  static constexpr int OFF_BL = OFF_B + (HAS_B ? C * GW * 4 : 0);
-  static constexpr int OFF_R = OFF_BL + (HAS_B ? GW * 4 : 0);       // DK: r for the scan
-  static constexpr int OFF_TOT = OFF_R + (HAS_RQ ? C * XW * 4 : 0);
-  static constexpr int TOT_W = (GATE ? GW : 1) > 64 ? (GATE ? GW : 1) : 64;
-  static constexpr int LDS = OFF_TOT + 4 * TOT_W * 4;
+  static_assert(!GATE || ROLE == BWD_DV || SEGR == 16, "dq / dk read segment prefixes per row block");
+  // b as the output tiles read it (dq, dk): gate local products [C][GW] with the segment
+  // prefixes [NSEG][GW]; per-token decay: b [C]
+  static constexpr bool B_OUT = (GATE && ROLE != BWD_DV) || TOKEN;
+  static constexpr int B_BYTES = (GATE && ROLE != BWD_DV) ? C * GW * 4 : TOKEN ? C * 4 : 0;
+  static constexpr int PRE_BYTES = (GATE && ROLE != BWD_DV) ? NSEG * GW * 4 : 0;
+  static constexpr int BL_BYTES = GATE ? GW * 4 : TOKEN ? 16 : 0;
+  // one stage of chunk operands (bytes)
+  static constexpr int ST_X = 0;
+  static constexpr int ST_Y = ST_X + C * LDX * ES;
+  static constexpr int ST_Z = ST_Y + C * LDX * ES;
+  static constexpr int ST_ZL = ST_Z + C * LDZ * ES;                 // Z lo (SPLIT)
+  static constexpr int ST_B = ST_ZL + (SPLIT ? C * LDZ * ES : 0);
+  static constexpr int ST_PRE = ST_B + B_BYTES;
+  static constexpr int ST_BL = ST_PRE + PRE_BYTES;                  // chunk decay bL
+  static constexpr int STAGE = (ST_BL + BL_BYTES + 15) / 16 * 16;
+  // shared by the stages: score tiles, the dv role's gate products (gamma: its powers), the
+  // gate's segment totals
+  static constexpr int SH_P = 0;
+  static constexpr int SH_PL = SH_P + 16 * 256 * ES;                 // score lo (SPLIT)
+  static constexpr int SH_BS = SH_PL + (SPLIT ? 16 * 256 * ES : 0);
+  static constexpr int SH_TOT = SH_BS + ((GATE && ROLE == BWD_DV) ? C * GW * 4 : GAMMA ? C * 4 : 0);
+  static constexpr int SHARED = SH_TOT + (GATE ? NSEG * GW * 4 : 0);
+  // two stages fit: a producer wave group forms chunk n + 1 while the consumer group works
+  // on chunk n; else one group does both in turn
+  static constexpr bool PC = 2 * STAGE + SHARED <= kMaxLds;
+  static constexpr int NST = PC ? 2 : 1;
+  static constexpr int NT = NST * NTG;
+  static constexpr int OFF_SH = NST * STAGE;
+  static constexpr int LDS = OFF_SH + SHARED;
   static constexpr bool FITS = LDS <= kMaxLds;
 };
+
 
 // fp32 values rounded to bf16 and back (the hi part of a hi + lo split)
 __device__ __forceinline__ f32x4 bf_round4(f32x4 x) {
@@ -136,8 +159,34 @@ __host__ __device__ constexpr int tile_pos(int rb, int sb) { // index among the 
   return -1;
 }
 
+
+// The value of lane li + D of the same 16-lane row (DPP row shift), 0 past the row's end.
+template <int D>
+__device__ __forceinline__ float from_row_next(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + D, 0xf, 0xf, true));
+}
+
+// Suffix sums over the 64 rows r = 16 rb + li of a chunk held as v[rb] by the 16 lanes of
+// lane group g: on return v[rb] = sum over rows r' >= r; returns the sum of all 64 rows.
+__device__ __forceinline__ float suffix_rows64(float (&v)[4], int g) {
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    v[rb] += from_row_next<1>(v[rb]);
+    v[rb] += from_row_next<2>(v[rb]);
+    v[rb] += from_row_next<4>(v[rb]);
+    v[rb] += from_row_next<8>(v[rb]);
+  }
+  float t[4]; // row block totals (lane li = 0 of the group)
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) t[rb] = __shfl(v[rb], 16 * g);
+  v[2] += t[3];
+  v[1] += t[2] + t[3];
+  v[0] += t[1] + t[2] + t[3];
+  return t[0] + t[1] + t[2] + t[3];
+}
+
 template <typename TIn, int ROLE, int DY, int DECAY>
-__global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
+__global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_kernel(BwdArgs a) {
   using K = BwdCfg<TIn, ROLE, DY, DECAY>;
   constexpr int C = K::C, XW = K::XW, VE = K::VE, KU = K::KU;
   constexpr int LDX = K::LDX, LDZ = K::LDZ, GW = K::GW;
@@ -145,16 +194,17 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
   constexpr int NYB = DY / 16;         // 16-row blocks of the state
   constexpr int NZU = C / KU;          // K units over the chunk rows
   __shared__ __attribute__((aligned(16))) unsigned char lds[K::LDS];
-  TIn *sX = reinterpret_cast<TIn *>(lds + K::OFF_X);
-  TIn *sY = reinterpret_cast<TIn *>(lds + K::OFF_Y);
-  TIn *sZ = reinterpret_cast<TIn *>(lds + K::OFF_Z);
-  TIn *sP = reinterpret_cast<TIn *>(lds + K::OFF_P);
-  TIn *sZL = reinterpret_cast<TIn *>(lds + K::OFF_ZL);
-  TIn *sPL = reinterpret_cast<TIn *>(lds + K::OFF_PL);
-  float *sB = reinterpret_cast<float *>(lds + K::OFF_B);
-  float *sBL = reinterpret_cast<float *>(lds + K::OFF_BL);
-  float *sA = reinterpret_cast<float *>(lds + K::OFF_R);
-  float *sT = reinterpret_cast<float *>(lds + K::OFF_TOT);
+  auto stX = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::STAGE + K::ST_X); };
+  auto stY = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::STAGE + K::ST_Y); };
+  auto stZ = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::STAGE + K::ST_Z); };
+  auto stZL = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::STAGE + K::ST_ZL); };
+  auto stB = [&](int s) { return reinterpret_cast<float *>(lds + s * K::STAGE + K::ST_B); };
+  auto stPre = [&](int s) { return reinterpret_cast<float *>(lds + s * K::STAGE + K::ST_PRE); };
+  auto stBL = [&](int s) { return reinterpret_cast<float *>(lds + s * K::STAGE + K::ST_BL); };
+  TIn *sP = reinterpret_cast<TIn *>(lds + K::OFF_SH + K::SH_P);
+  TIn *sPL = reinterpret_cast<TIn *>(lds + K::OFF_SH + K::SH_PL);
+  float *sBS = reinterpret_cast<float *>(lds + K::OFF_SH + K::SH_BS);
+  float *sTot = reinterpret_cast<float *>(lds + K::OFF_SH + K::SH_TOT);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -195,30 +245,37 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
     const int64_t l = T - (int64_t)n * C;
     return (int)(l < C ? l : C);
   };
+  auto chunk_at = [&](int it) -> int { return REV ? nchunks - 1 - it : it; };
 
   // ---- gamma: b[r] = gamma^(r+1) for the whole kernel -----------------------------
-  if constexpr (DECAY == DECAY_GAMMA) {
+  if constexpr (K::GAMMA) {
     if (wave == 0) {
       float x = a.decay[h];
       for (int d = 1; d < 64; d <<= 1) {
         const float o = __shfl_up(x, d);
         if (lane >= d) x *= o;
       }
-      sB[lane] = x;
+      sBS[lane] = x;
     }
   }
 
-  // ---- register prefetch of one chunk ---------------------------------------------
+  // =========================== operand group ===========================================
+  // Forms the operand tiles of a chunk in a stage: phase 1 scans the decay down the chunk
+  // and copies the tiles that need no decay; phase 2 (after a barrier) completes the scan
+  // with the segment prefixes and forms the decayed tiles.  Registers hold the next
+  // chunk's inputs, loaded as the current ones fall free.
+  const int ptid = K::PC ? tid - K::NTG : tid;
+  const int pwave = K::PC ? wave - 4 : wave;
   uint32_t rX[K::NVX][4], rY[K::NVX][4], rZ[K::NVZ][4];
   float rG[K::GATE ? K::SEGR : 1]; // gate rows of this thread's (column, segment) in scan order
   float rTok = 1.f;
-  auto load = [&](int n) {
+  auto ld_xy = [&](int n) {
     const int L = chunk_len(n);
     const int64_t t0 = (int64_t)n * C;
-    constexpr int VPRX = DY / VE, VPRZ = XW / VE;
+    constexpr int VPRX = DY / VE;
 #pragma unroll
     for (int j = 0; j < K::NVX; ++j) {
-      const int vi = tid + 256 * j, r = vi / VPRX, c = (vi % VPRX) * VE;
+      const int vi = ptid + K::NTG * j, r = vi / VPRX, c = (vi % VPRX) * VE;
       uint4 x = make_uint4(0, 0, 0, 0), y = x;
       if (r < L) {
         x = *reinterpret_cast<const uint4 *>(srcX + (t0 + r) * DY + c);
@@ -227,29 +284,196 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
       rX[j][0] = x.x; rX[j][1] = x.y; rX[j][2] = x.z; rX[j][3] = x.w;
       rY[j][0] = y.x; rY[j][1] = y.y; rY[j][2] = y.z; rY[j][3] = y.w;
     }
+  };
+  auto ld_z = [&](int n) {
+    const int L = chunk_len(n);
+    const int64_t t0 = (int64_t)n * C;
+    constexpr int VPRZ = XW / VE;
 #pragma unroll
     for (int j = 0; j < K::NVZ; ++j) {
-      const int vi = tid + 256 * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
+      const int vi = ptid + K::NTG * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
       uint4 z = make_uint4(0, 0, 0, 0);
       if (r < L) z = *reinterpret_cast<const uint4 *>(srcZ + (t0 + r) * ldz + zoff + c);
       rZ[j][0] = z.x; rZ[j][1] = z.y; rZ[j][2] = z.z; rZ[j][3] = z.w;
     }
+  };
+  auto ld_g = [&](int n) {
+    const int L = chunk_len(n);
+    const int64_t t0 = (int64_t)n * C;
     if constexpr (K::GATE) {
-      // thread (column tid % GW, segment tid / GW) reads its SEGR rows: for each row the
+      // thread (column ptid % GW, segment ptid / GW) reads its SEGR rows: for each row the
       // lanes of a wave read consecutive columns
-      const float *gsrc = a.decay + bh * T * dk + goff + tid % GW;
-      const int r0 = (tid / GW) * K::SEGR;
+      const float *gsrc = a.decay + bh * T * dk + goff + ptid % GW;
+      const int r0 = (ptid / GW) * K::SEGR;
 #pragma unroll
       for (int i = 0; i < K::SEGR; ++i)
         rG[i] = (r0 + i < L) ? gsrc[(t0 + r0 + i) * dk] : 1.f; // past the end: no decay
     }
     if constexpr (K::TOKEN) {
       rTok = 1.f;
-      if (tid < L) rTok = a.decay[bh * T + t0 + tid];
+      if (ptid < L) rTok = a.decay[bh * T + t0 + ptid];
+    }
+  };
+  // phase-1 inputs: the decay and the tiles copied unconverted; phase-2: the decayed tiles
+  auto load1 = [&](int n) {
+    ld_g(n);
+    if constexpr (ROLE == BWD_DV) ld_z(n);
+    else ld_xy(n);
+  };
+  auto load2 = [&](int n) {
+    if constexpr (ROLE == BWD_DV) ld_xy(n);
+    else ld_z(n);
+  };
+
+  auto phase1 = [&](int s) {
+    if constexpr (K::GATE) {
+      // local products down this thread's segment, and the segment's total
+      const int col = ptid % GW, seg = ptid / GW;
+      float *loc = (ROLE == BWD_DV) ? sBS : stB(s);
+      float p = 1.f;
+#pragma unroll
+      for (int i = 0; i < K::SEGR; ++i) {
+        p *= rG[i];
+        loc[(seg * K::SEGR + i) * GW + col] = p;
+      }
+      sTot[seg * GW + col] = p;
+    } else if constexpr (K::TOKEN) {
+      if (pwave == 0) {
+        float x = rTok;
+        for (int d = 1; d < 64; d <<= 1) {
+          const float o = __shfl_up(x, d);
+          if (lane >= d) x *= o;
+        }
+        stB(s)[lane] = x;
+        if (lane == 63) stBL(s)[0] = x; // padded rows carry 1: b[63] = b[L-1]
+      }
+    }
+    if constexpr (ROLE == BWD_DV) {
+      constexpr int VPRZ = XW / VE;
+#pragma unroll
+      for (int j = 0; j < K::NVZ; ++j) {
+        const int vi = ptid + K::NTG * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
+        st_words_lds<4>(stZ(s) + r * LDZ + c, rZ[j]);
+      }
+    } else {
+      constexpr int VPRX = DY / VE;
+#pragma unroll
+      for (int j = 0; j < K::NVX; ++j) {
+        const int vi = ptid + K::NTG * j, r = vi / VPRX, c = (vi % VPRX) * VE;
+        st_words_lds<4>(stX(s) + r * LDX + c, rX[j]);
+        st_words_lds<4>(stY(s) + r * LDX + c, rY[j]);
+      }
     }
   };
 
-  // ---- state: S[y][x] for y in DY, x = 16 wave + li; tile yb holds rows 16yb + 4g + q
+  auto phase2 = [&](int n, int s) {
+    const int L = chunk_len(n);
+    if constexpr (K::GATE) {
+      // prefix of the earlier segments; the chunk decay bL from the last segment
+      const int col = ptid % GW, seg = ptid / GW;
+      float pre = 1.f;
+      for (int s2 = 0; s2 < seg; ++s2) pre *= sTot[s2 * GW + col];
+      if constexpr (ROLE != BWD_DV) stPre(s)[seg * GW + col] = pre;
+      if (seg == K::NSEG - 1) stBL(s)[col] = pre * sTot[seg * GW + col];
+    }
+    // b at row r, columns c .. c + VE - 1
+    auto b_vec = [&](float *bb, int r, int c) {
+      if constexpr (K::GATE) {
+        const float *loc = ((ROLE == BWD_DV) ? sBS : stB(s)) + r * GW + c;
+        const int seg = r / K::SEGR;
+#pragma unroll
+        for (int e = 0; e < VE; e += 4) {
+          f32x4 pre = {1.f, 1.f, 1.f, 1.f};
+          for (int s2 = 0; s2 < seg; ++s2) pre *= *reinterpret_cast<const f32x4 *>(sTot + s2 * GW + c + e);
+          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(loc + e);
+          bb[e] = l4[0] * pre[0]; bb[e + 1] = l4[1] * pre[1];
+          bb[e + 2] = l4[2] * pre[2]; bb[e + 3] = l4[3] * pre[3];
+        }
+      } else {
+        float x = 1.f;
+        if constexpr (K::TOKEN) x = stB(s)[r];
+        else if constexpr (K::GAMMA) x = sBS[r];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) bb[e] = x;
+      }
+    };
+    if constexpr (ROLE == BWD_DV) {
+      constexpr int VPRX = DY / VE;
+#pragma unroll
+      for (int j = 0; j < K::NVX; ++j) {
+        const int vi = ptid + K::NTG * j, r = vi / VPRX, c = (vi % VPRX) * VE;
+        float fx[VE], fy[VE], bb[VE];
+        unpack<TIn, VE>(fx, rX[j]);
+        unpack<TIn, VE>(fy, rY[j]);
+        b_vec(bb, r, c);
+        const bool ok = r < L;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          fx[e] = ok ? phi_f(fx[e], elu1) * rcp_f(bb[e]) : 0.f;
+          fy[e] = ok ? phi_f(fy[e], elu1) * bb[e] : 0.f;
+        }
+        st_lds<TIn, VE>(stX(s) + r * LDX + c, fx);
+        st_lds<TIn, VE>(stY(s) + r * LDX + c, fy);
+      }
+    } else {
+      constexpr int VPRZ = XW / VE;
+#pragma unroll
+      for (int j = 0; j < K::NVZ; ++j) {
+        const int vi = ptid + K::NTG * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
+        float fz[VE], bb[VE];
+        unpack<TIn, VE>(fz, rZ[j]);
+        b_vec(bb, r, c);
+        const bool ok = r < L;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const float pz = phi_f(fz[e], elu1);
+          fz[e] = ok ? (ROLE == BWD_DQ ? pz * rcp_f(bb[e]) : pz * bb[e]) : 0.f;
+        }
+        st_lds<TIn, VE>(stZ(s) + r * LDZ + c, fz);
+        if constexpr (K::SPLIT) {
+          float fl[VE];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) fl[e] = fz[e] - (float)(TIn)fz[e];
+          st_lds<TIn, VE>(stZL(s) + r * LDZ + c, fl);
+        }
+      }
+    }
+  };
+
+  if constexpr (K::PC) {
+    if (wave >= 4) {
+      // ----- producer waves: stage (it + 1) & 1 while the consumers work on it & 1 -----
+      if (nchunks > 0) {
+        load1(chunk_at(0));
+        load2(chunk_at(0));
+        phase1(0);
+        if (nchunks > 1) load1(chunk_at(1));
+      }
+      __syncthreads();
+      if (nchunks > 0) {
+        phase2(chunk_at(0), 0);
+        if (nchunks > 1) load2(chunk_at(1));
+      }
+      __syncthreads();
+      for (int it = 0; it < nchunks; ++it) {
+        const int s = (it + 1) & 1;
+        if (it + 1 < nchunks) {
+          phase1(s);
+          if (it + 2 < nchunks) load1(chunk_at(it + 2));
+        }
+        __syncthreads(); // consumers: score tiles of chunk it written
+        if (it + 1 < nchunks) {
+          phase2(chunk_at(it + 1), s);
+          if (it + 2 < nchunks) load2(chunk_at(it + 2));
+        }
+        __syncthreads(); // consumers: chunk it done; stage s complete
+      }
+      return;
+    }
+  }
+
+  // =========================== output group (waves 0-3) =================================
+  // state: S[y][x] for y in DY, x = 16 wave + li; tile yb holds rows 16yb + 4g + q
   f32x4 S[NYB];
   {
     const float *s0 = (ROLE == BWD_DQ) ? a.init : a.dfinal;
@@ -268,128 +492,59 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
     }
   }
 
-  // decay-gradient carry (DK): per column (gate) or per slice (token)
+  const int xc = 16 * wave + 4 * g; // first of this lane's 4 output columns
+  // decay-gradient carry (DK): the sum over later chunks, per column (gate) or over this
+  // wave's 16 columns (token); starts from the final state's term
+  f32x4 carry4 = {0.f, 0.f, 0.f, 0.f};
   float carry = 0.f;
   if constexpr (ROLE == BWD_DK && K::GATE) {
-    if (want_dg && a.fterm) carry = a.fterm[bh * dk + goff + (tid & 63)];
+    if (want_dg && a.fterm) carry4 = *reinterpret_cast<const f32x4 *>(a.fterm + bh * dk + goff + xc);
   }
   if constexpr (ROLE == BWD_DK && K::TOKEN) {
-    if (want_dg && a.fterm && wave == 0) {
-      float x = a.fterm[bh * dk + goff + lane];
-      for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+    if (want_dg && a.fterm) {
+      float x = a.fterm[bh * dk + goff + 16 * wave + li];
+      for (int d = 8; d >= 1; d >>= 1) x += __shfl_xor(x, d);
       carry = x;
     }
   }
-  float araw[K::GATE && ROLE == BWD_DK ? K::SEGR : 1];
-  (void)araw;
 
-  if (nchunks > 0) load(REV ? nchunks - 1 : 0);
-
-  for (int it = 0; it < nchunks; ++it) {
-    const int n = REV ? nchunks - 1 - it : it;
+  // this lane's rows 16 rb + li, columns xc .. xc+3: raw q (dq role) or k (dk role) for
+  // phi and phi', phi(q) dphi(q) from the dq pass and the raw gate (dk role) - read from
+  // global memory at the start of the chunk, used by the output tiles
+  uint32_t raux[4][K::ES]; // 4 elements of the input type
+  f32x4 rqv[4], ralpha[4];
+  auto load_lane = [&](int n) {
     const int L = chunk_len(n);
     const int64_t t0 = (int64_t)n * C;
-
-    // ---- 1. decay inside the chunk: b = inclusive product down the rows -----------
-    if constexpr (K::GATE) {
-      // per (column, segment) product scan in registers; segment totals through LDS
-      const int col = tid % GW, seg = tid / GW;
-      float bv[K::SEGR];
-      float p = 1.f;
+    if constexpr (K::HAS_AUX) {
 #pragma unroll
-      for (int i = 0; i < K::SEGR; ++i) {
-        if constexpr (ROLE == BWD_DK) araw[i] = rG[i];
-        p *= rG[i];
-        bv[i] = p;
-      }
-      float pre = 1.f;
-      if constexpr (K::NSEG > 1) {
-        sT[seg * K::TOT_W + col] = p;
-        __syncthreads();
-        for (int s2 = 0; s2 < seg; ++s2) pre *= sT[s2 * K::TOT_W + col];
-      }
-#pragma unroll
-      for (int i = 0; i < K::SEGR; ++i) sB[(seg * K::SEGR + i) * GW + col] = bv[i] * pre;
-      if (seg == K::NSEG - 1) sBL[col] = p * pre;
-    } else if constexpr (K::TOKEN) {
-      if (wave == 0) {
-        float x = rTok;
-        for (int d = 1; d < 64; d <<= 1) {
-          const float o = __shfl_up(x, d);
-          if (lane >= d) x *= o;
-        }
-        sB[lane] = x;
-        if (lane == 63) sBL[0] = x; // padded rows carry 1: b[63] = b[L-1]
-      }
-    }
-    __syncthreads();
-    // chunk decay bL of a column (gate) or of the chunk
-    auto bl_at = [&](int idx) -> float {
-      if constexpr (K::GATE) return sBL[idx];
-      else if constexpr (K::TOKEN) return sBL[0];
-      else if constexpr (DECAY == DECAY_GAMMA) return sB[L - 1];
-      else return 1.f;
-    };
-    auto b_at = [&](int r, int col) -> float {
-      if constexpr (K::GATE) return sB[r * GW + col];
-      else if constexpr (K::HAS_B) return sB[r];
-      else return 1.f;
-    };
-
-    // ---- 2. operand tiles -----------------------------------------------------------
-    {
-      constexpr int VPRX = DY / VE, VPRZ = XW / VE;
-#pragma unroll
-      for (int j = 0; j < K::NVX; ++j) {
-        const int vi = tid + 256 * j, r = vi / VPRX, c = (vi % VPRX) * VE;
-        if constexpr (ROLE == BWD_DV) {
-          float fx[VE], fy[VE];
-          unpack<TIn, VE>(fx, rX[j]);
-          unpack<TIn, VE>(fy, rY[j]);
-#pragma unroll
-          for (int e = 0; e < VE; ++e) {
-            const float bb = b_at(r, c + e);
-            const bool ok = r < L;
-            fx[e] = ok ? phi_f(fx[e], elu1) * rcp_f(bb) : 0.f;
-            fy[e] = ok ? phi_f(fy[e], elu1) * bb : 0.f;
-          }
-          st_lds<TIn, VE>(sX + r * LDX + c, fx);
-          st_lds<TIn, VE>(sY + r * LDX + c, fy);
+      for (int rb = 0; rb < 4; ++rb) {
+        const int r = 16 * rb + li;
+        const TIn *pa = srcA + (t0 + r) * dk + zoff + xc;
+        if constexpr (K::ES == 2) {
+          uint2 w2 = make_uint2(0, 0);
+          if (r < L) w2 = *reinterpret_cast<const uint2 *>(pa);
+          raux[rb][0] = w2.x; raux[rb][1] = w2.y;
         } else {
-          st_words_lds<4>(sX + r * LDX + c, rX[j]);
-          st_words_lds<4>(sY + r * LDX + c, rY[j]);
+          uint4 w4 = make_uint4(0, 0, 0, 0);
+          if (r < L) w4 = *reinterpret_cast<const uint4 *>(pa);
+          raux[rb][0] = w4.x; raux[rb][1] = w4.y; raux[rb][2] = w4.z; raux[rb][3] = w4.w;
         }
-      }
-#pragma unroll
-      for (int j = 0; j < K::NVZ; ++j) {
-        const int vi = tid + 256 * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
-        if constexpr (ROLE == BWD_DV) {
-          st_words_lds<4>(sZ + r * LDZ + c, rZ[j]);
-        } else {
-          float fz[VE];
-          unpack<TIn, VE>(fz, rZ[j]);
-#pragma unroll
-          for (int e = 0; e < VE; ++e) {
-            const float bb = b_at(r, c + e);
-            const bool ok = r < L;
-            const float pz = phi_f(fz[e], elu1);
-            fz[e] = ok ? (ROLE == BWD_DQ ? pz * rcp_f(bb) : pz * bb) : 0.f;
-          }
-          st_lds<TIn, VE>(sZ + r * LDZ + c, fz);
-          if constexpr (K::SPLIT) {
-            float fl[VE];
-#pragma unroll
-            for (int e = 0; e < VE; ++e) fl[e] = fz[e] - (float)(TIn)fz[e];
-            st_lds<TIn, VE>(sZL + r * LDZ + c, fl);
-          }
+        rqv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ralpha[rb] = f32x4{1.f, 1.f, 1.f, 1.f};
+        if constexpr (K::HAS_RQ) {
+          if (want_dg && r < L) rqv[rb] = *reinterpret_cast<const f32x4 *>(a.rq + (bh * T + t0 + r) * dk + zoff + xc);
+        }
+        if constexpr (ROLE == BWD_DK && K::GATE) {
+          if (want_dg && r < L) ralpha[rb] = *reinterpret_cast<const f32x4 *>(a.decay + (bh * T + t0 + r) * dk + goff + xc);
         }
       }
     }
-    // ---- 3. prefetch the next chunk -------------------------------------------------
-    if (it + 1 < nchunks) load(REV ? n - 1 : n + 1);
-    __syncthreads();
+  };
 
-    // ---- 4. score tiles: image of tile (rb, sb) holds P[r][s] = X_r . Y_s, masked ----
+  // ---- score tiles: image of tile (rb, sb) holds P[r][s] = X_r . Y_s, masked --------
+  auto scores = [&](int s) {
+    const TIn *sX = stX(s), *sY = stY(s);
     static_for<0, 16>([&](auto I) {
       constexpr int rb = I / 4, sb = I % 4;
       if constexpr (tile_on<REV>(rb, sb)) {
@@ -404,8 +559,8 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
           if constexpr (rb == sb) {
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-              const int s = 4 * g + qq;
-              const bool keep = REV ? (s >= li) : (s <= li);
+              const int s2 = 4 * g + qq;
+              const bool keep = REV ? (s2 >= li) : (s2 <= li);
               if (!keep) acc[qq] = 0.f;
             }
           }
@@ -419,10 +574,23 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
         }
       }
     });
-    __syncthreads();
+  };
 
-    // ---- 5. output tiles and the state ----------------------------------------------
-    const int x = 16 * wave + li; // this lane's output column in the slice
+  // ---- output tiles, the state, and (dk) the decay gradient --------------------------
+  auto finish = [&](int n, int s) {
+    const int L = chunk_len(n);
+    const int64_t t0 = (int64_t)n * C;
+    const TIn *sX = stX(s), *sY = stY(s), *sZ = stZ(s), *sZL = stZL(s);
+    const float *sB = stB(s), *sBL = stBL(s);
+    (void)sB; (void)sBL; (void)sZL;
+    // chunk decay bL of a column (gate) or of the chunk
+    auto bl_at = [&](int idx) -> float {
+      if constexpr (K::GATE) return sBL[idx];
+      else if constexpr (K::TOKEN) return sBL[0];
+      else if constexpr (K::GAMMA) return sBS[L - 1];
+      else return 1.f;
+    };
+    const int x = 16 * wave + li; // this lane's state column in the slice
     if constexpr (ROLE == BWD_DK) {
       const float d = bl_at(x);
 #pragma unroll
@@ -443,44 +611,24 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
     // Output tiles are formed transposed (out^T = Z^T P^T + S^T X^T: the same fragments with
     // the operands swapped), so a lane holds 4 adjacent columns of one row: 16-byte LDS
     // reads of the per-element factors and 8-byte (bf16) stores.
-    const int xc = 16 * wave + 4 * g; // first of this lane's 4 output columns
-    auto b_at4 = [&](int r) -> f32x4 {
-      if constexpr (K::GATE) return *reinterpret_cast<const f32x4 *>(sB + r * GW + xc);
-      else if constexpr (K::HAS_B) return f32x4{sB[r], sB[r], sB[r], sB[r]};
+    f32x4 pre4[4]; // gate: prefix of the earlier segments, row block rb, columns xc..
+    if constexpr (K::GATE && ROLE != BWD_DV) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) pre4[rb] = *reinterpret_cast<const f32x4 *>(stPre(s) + rb * GW + xc);
+    }
+    auto b_at4 = [&](int r, int rb) -> f32x4 {
+      if constexpr (K::GATE) return *reinterpret_cast<const f32x4 *>(sB + r * GW + xc) * pre4[rb];
+      else if constexpr (K::TOKEN) return f32x4{sB[r], sB[r], sB[r], sB[r]};
+      else if constexpr (K::GAMMA) return f32x4{sBS[r], sBS[r], sBS[r], sBS[r]};
       else return f32x4{1.f, 1.f, 1.f, 1.f};
     };
-    // this lane's rows 16 rb + li, columns xc .. xc+3: raw q (dq role) or k (dk role) for
-    // phi and phi', and phi(q) dphi(q) from the dq pass (dk role) - read from global
-    // memory now, used after the MFMAs below
-    uint32_t raux[4][K::ES]; // 4 elements of the input type
-    f32x4 rqv[4];
-    if constexpr (K::HAS_AUX) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int r = 16 * rb + li;
-        const TIn *pa = srcA + (t0 + r) * dk + zoff + xc;
-        if constexpr (K::ES == 2) {
-          uint2 w2 = make_uint2(0, 0);
-          if (r < L) w2 = *reinterpret_cast<const uint2 *>(pa);
-          raux[rb][0] = w2.x; raux[rb][1] = w2.y;
-        } else {
-          uint4 w4 = make_uint4(0, 0, 0, 0);
-          if (r < L) w4 = *reinterpret_cast<const uint4 *>(pa);
-          raux[rb][0] = w4.x; raux[rb][1] = w4.y; raux[rb][2] = w4.z; raux[rb][3] = w4.w;
-        }
-        rqv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (K::HAS_RQ) {
-          if (want_dg && r < L) rqv[rb] = *reinterpret_cast<const f32x4 *>(a.rq + (bh * T + t0 + r) * dk + zoff + xc);
-        }
-      }
-    }
     auto phi4 = [&](int rb) -> f32x4 {
       float f[4];
       unpack<TIn, 4>(f, raux[rb]);
       return f32x4{phi_f(f[0], elu1), phi_f(f[1], elu1), phi_f(f[2], elu1), phi_f(f[3], elu1)};
     };
     (void)phi4;
-    (void)rqv;
+    (void)b_at4;
     // the state as MFMA fragments (hi and, for split roles, lo parts), once per chunk
     Frag<TIn> sfh[DY / KU], sfl[K::SPLIT ? DY / KU : 1];
 #pragma unroll
@@ -493,6 +641,7 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
         sfh[u] = S[u];
       }
     }
+    f32x4 rr[4]; // dk: phi(q) dphi(q) - phi(k) dphi(k) of this lane's rows and columns
     static_for<0, 4>([&](auto RB) {
       constexpr int rb = RB;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -527,7 +676,7 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
       const int r = 16 * rb + li;
       const int64_t t = t0 + r;
       if constexpr (ROLE == BWD_DQ) {
-        const f32x4 dqb = acc * b_at4(r);
+        const f32x4 dqb = acc * b_at4(r, rb);
         const f32x4 qb = phi4(rb);
         if (r < L) {
           f32x4 dq4;
@@ -537,7 +686,7 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
           if (want_dg) *reinterpret_cast<f32x4 *>(a.rq + (bh * T + t) * dk + zoff + xc) = qb * dqb;
         }
       } else if constexpr (ROLE == BWD_DK) {
-        const f32x4 bb = b_at4(r);
+        const f32x4 bb = b_at4(r, rb);
         f32x4 dkb;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) dkb[qq] = acc[qq] * rcp_f(bb[qq]);
@@ -548,21 +697,18 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
           for (int qq = 0; qq < 4; ++qq) dk4[qq] = dkb[qq] * phi_d(kb[qq], elu1);
           st_out4<TIn>((TIn *)a.grad_k + (bh * T + t) * dk + zoff + xc, dk4);
         }
-        if constexpr (K::HAS_RQ) {
-          const f32x4 rr = rqv[rb] - kb * dkb;
-          *reinterpret_cast<f32x4 *>(sA + r * XW + xc) = (r < L) ? rr : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        rr[rb] = (r < L) ? rqv[rb] - kb * dkb : f32x4{0.f, 0.f, 0.f, 0.f};
       } else {
         if (r < L) st_out4<TIn>((TIn *)a.grad_v + (bh * T + t) * dv + zoff + xc, acc);
       }
     });
+    (void)rr;
 
     // state update: S[y][x] += sum_s Y[s][y] Z[s][x]
 #pragma unroll
     for (int yb = 0; yb < NYB; ++yb) {
 #pragma unroll
-      for (int u = 0; u < NZU; ++u)
-      {
+      for (int u = 0; u < NZU; ++u) {
         const Frag<TIn> yf = ld_frag_t<TIn, true>(sY, LDX, 16 * yb, u, g, li);
         S[yb] = mma(S[yb], yf, zf[u]);
         if constexpr (K::SPLIT) S[yb] = mma(S[yb], yf, zl[u]);
@@ -574,60 +720,82 @@ __global__ void __launch_bounds__(256) chunk_bwd_kernel(BwdArgs a) {
       for (int yb = 0; yb < NYB; ++yb) S[yb] *= d;
     }
 
-    // ---- 6. decay gradient (DK): reverse cumulative sum of r over later tokens ------
+    // decay gradient (DK): sums of r over the later tokens, in registers (rows across the
+    // 16 lanes of a group and the 4 row blocks of a lane)
     if constexpr (ROLE == BWD_DK && K::GATE) {
       if (want_dg) {
-        __syncthreads();
-        const int col = tid & 63, seg = tid >> 6; // K::SEGR = 16 rows per segment
-        float cs[K::SEGR];
-        float acc = 0.f;
+        f32x4 dg[4];
 #pragma unroll
-        for (int i = K::SEGR - 1; i >= 0; --i) {
-          acc += sA[(seg * K::SEGR + i) * XW + col];
-          cs[i] = acc;
-        }
-        sT[seg * K::TOT_W + col] = acc;
-        __syncthreads();
-        float suffix = 0.f, total = 0.f;
+        for (int qq = 0; qq < 4; ++qq) {
+          float v[4] = {rr[0][qq], rr[1][qq], rr[2][qq], rr[3][qq]};
+          const float tot = suffix_rows64(v, g);
 #pragma unroll
-        for (int s2 = 0; s2 < K::NSEG; ++s2) {
-          const float v2 = sT[s2 * K::TOT_W + col];
-          total += v2;
-          if (s2 > seg) suffix += v2;
+          for (int rb = 0; rb < 4; ++rb) dg[rb][qq] = (v[rb] + carry4[qq]) / ralpha[rb][qq];
+          carry4[qq] += tot;
         }
 #pragma unroll
-        for (int i = 0; i < K::SEGR; ++i) {
-          const int r = seg * K::SEGR + i;
-          if (r < L) a.dgate[(bh * T + t0 + r) * dk + goff + col] = (cs[i] + suffix + carry) / araw[i];
+        for (int rb = 0; rb < 4; ++rb) {
+          const int r = 16 * rb + li;
+          if (r < L) *reinterpret_cast<f32x4 *>(a.dgate + (bh * T + t0 + r) * dk + goff + xc) = dg[rb];
         }
-        carry += total;
       }
     }
     if constexpr (ROLE == BWD_DK && K::TOKEN) {
       if (want_dg) {
-        __syncthreads();
-        {
-          const int r = tid >> 2, part = tid & 3;
-          float sum = 0.f;
+        // row sums over this wave's 16 columns, then suffix sums over the rows
+        float v[4];
 #pragma unroll
-          for (int c2 = 0; c2 < 16; ++c2) sum += sA[r * XW + part * 16 + c2];
-          sum += __shfl_xor(sum, 1);
-          sum += __shfl_xor(sum, 2);
-          if (part == 0) sT[r] = sum;
+        for (int rb = 0; rb < 4; ++rb) {
+          float sum = rr[rb][0] + rr[rb][1] + rr[rb][2] + rr[rb][3];
+          sum += __shfl_xor(sum, 16);
+          sum += __shfl_xor(sum, 32);
+          v[rb] = sum;
         }
-        __syncthreads();
-        if (wave == 0) {
-          float xs = sT[lane];
-          for (int d = 1; d < 64; d <<= 1) {
-            const float o = __shfl_down(xs, d);
-            if (lane + d < 64) xs += o;
+        const float tot = suffix_rows64(v, g);
+        if (g == 0) {
+          float *tp = a.tpart + ((bh * a.nsl + slice) * 4 + wave) * T + t0;
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            const int r = 16 * rb + li;
+            if (r < L) tp[r] = v[rb] + carry;
           }
-          if (lane < L) a.tpart[(bh * a.nsl + slice) * T + t0 + lane] = xs + carry;
-          carry += __shfl(xs, 0);
         }
+        carry += tot;
       }
     }
-    __syncthreads();
+  };
+
+  if constexpr (K::PC) {
+    __syncthreads(); // stage 0: phase 1 done
+    __syncthreads(); // stage 0 complete
+    for (int it = 0; it < nchunks; ++it) {
+      const int n = chunk_at(it);
+      load_lane(n);
+      scores(it & 1);
+      __syncthreads();
+      finish(n, it & 1);
+      __syncthreads();
+    }
+  } else {
+    // one wave group forms the operands and then the outputs of each chunk
+    if (nchunks > 0) {
+      load1(chunk_at(0));
+      load2(chunk_at(0));
+    }
+    for (int it = 0; it < nchunks; ++it) {
+      const int n = chunk_at(it);
+      load_lane(n);
+      phase1(0);
+      if (it + 1 < nchunks) load1(chunk_at(it + 1));
+      __syncthreads();
+      phase2(n, 0);
+      if (it + 1 < nchunks) load2(chunk_at(it + 1));
+      __syncthreads();
+      scores(0);
+      __syncthreads();
+      finish(n, 0);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue ---------------------------------------------------------------------

@@ -106,7 +106,7 @@ BwdLauncher find_bwd(bool bf16, int64_t dy, int role, int decay) {
 // ---------------------------------------------------------------------------------
 // small kernels
 
-// Per-token decay gradient: d alpha_t = (sum over key slices of d log a_t) / alpha_t.
+// Per-token decay gradient: d alpha_t = (sum of the nsl partial sums of d log a_t) / alpha_t.
 __global__ void token_dgate_kernel(const float *tpart, const float *decay, float *dgate,
                                    int64_t BH, int64_t T, int nsl) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -387,11 +387,11 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   if (nbh * (nslk > nslv ? nslk : nslv) >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
 
   // workspace for the decay gradient: phi(q) dphi(q) per token and key, the final state's
-  // term per key, and (per-token decay) one partial sum per key slice and token
+  // term per key, and (per-token decay) one partial sum per 16 keys and token
   const bool want_dg = dgate != nullptr;
   const int64_t n_rq = want_dg ? nbh * T * dk : 0;
   const int64_t n_ft = (want_dg && dfinal_state) ? nbh * dk : 0;
-  const int64_t n_tp = (want_dg && kind == DECAY_TOKEN) ? nbh * nslk * T : 0;
+  const int64_t n_tp = (want_dg && kind == DECAY_TOKEN) ? nbh * nslk * 4 * T : 0;
   float *ws = nullptr;
   if (n_rq + n_ft + n_tp > 0 &&
       hipMallocAsync(reinterpret_cast<void **>(&ws), (n_rq + n_ft + n_tp) * sizeof(float), s) != hipSuccess)
@@ -431,7 +431,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
     const float *tp = a.tpart;
     const float *dec = gate_or_gamma;
     int64_t nbh_v = nbh, T_v = T;
-    int nsl_i = (int)nslk;
+    int nsl_i = (int)nslk * 4; // partial sums per token: 4 waves per key slice
     void *args[] = {&tp, &dec, &dgate, &nbh_v, &T_v, &nsl_i};
     if (hipLaunchKernel(reinterpret_cast<const void *>(&token_dgate_kernel),
                         dim3(blocks_for(nbh * T, 256)), dim3(256), args, 0, s) != hipSuccess)
