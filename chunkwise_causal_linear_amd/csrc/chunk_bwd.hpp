@@ -84,6 +84,10 @@ struct BwdCfg {
   static constexpr int NSEG = GATE ? NTG / GW : 1;
   static constexpr int SEGR = C / NSEG;
   static_assert(!GATE || ROLE == BWD_DV || SEGR == 16, "dq / dk read segment prefixes per row block");
+  // a wave's 16-byte vectors of a decayed tile cover 64 / (row vectors) consecutive rows,
+  // starting at a multiple of that count: they lie in one gate segment
+  static constexpr int DEC_VPR = (ROLE == BWD_DV ? DY : XW) / VE;
+  static_assert(!GATE || (DEC_VPR <= 64 && SEGR % (64 / DEC_VPR) == 0), "segment uniform per wave");
   // b as the output tiles read it (dq, dk): gate local products [C][GW] with the segment
   // prefixes [NSEG][GW]; per-token decay: b [C]
   static constexpr bool B_OUT = (GATE && ROLE != BWD_DV) || TOKEN;
@@ -120,6 +124,13 @@ struct BwdCfg {
 // fp32 values rounded to bf16 and back (the hi part of a hi + lo split)
 __device__ __forceinline__ f32x4 bf_round4(f32x4 x) {
   return f32x4{(float)(__bf16)x[0], (float)(__bf16)x[1], (float)(__bf16)x[2], (float)(__bf16)x[3]};
+}
+
+// phi as a compile-time choice; elu + 1 without a branch: max(x, 0) + e^min(x, 0)
+template <bool ELU>
+__device__ __forceinline__ float phi_c(float x) {
+  if constexpr (ELU) return fmaxf(x, 0.f) + __expf(fminf(x, 0.f));
+  else return x;
 }
 
 __device__ __forceinline__ float phi_d(float phi_val, int elu1) {
@@ -276,11 +287,11 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
 #pragma unroll
     for (int j = 0; j < K::NVX; ++j) {
       const int vi = ptid + K::NTG * j, r = vi / VPRX, c = (vi % VPRX) * VE;
-      uint4 x = make_uint4(0, 0, 0, 0), y = x;
-      if (r < L) {
-        x = *reinterpret_cast<const uint4 *>(srcX + (t0 + r) * DY + c);
-        y = *reinterpret_cast<const uint4 *>(srcY + (t0 + r) * DY + c);
-      }
+      // rows past the end read the last row and are masked where the tiles are formed
+      // (a select here would make the compiler wait for the load)
+      const int rc = r < L ? r : L - 1;
+      const uint4 x = *reinterpret_cast<const uint4 *>(srcX + (t0 + rc) * DY + c);
+      const uint4 y = *reinterpret_cast<const uint4 *>(srcY + (t0 + rc) * DY + c);
       rX[j][0] = x.x; rX[j][1] = x.y; rX[j][2] = x.z; rX[j][3] = x.w;
       rY[j][0] = y.x; rY[j][1] = y.y; rY[j][2] = y.z; rY[j][3] = y.w;
     }
@@ -292,8 +303,8 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
 #pragma unroll
     for (int j = 0; j < K::NVZ; ++j) {
       const int vi = ptid + K::NTG * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
-      uint4 z = make_uint4(0, 0, 0, 0);
-      if (r < L) z = *reinterpret_cast<const uint4 *>(srcZ + (t0 + r) * ldz + zoff + c);
+      const int rc = r < L ? r : L - 1;
+      const uint4 z = *reinterpret_cast<const uint4 *>(srcZ + (t0 + rc) * ldz + zoff + c);
       rZ[j][0] = z.x; rZ[j][1] = z.y; rZ[j][2] = z.z; rZ[j][3] = z.w;
     }
   };
@@ -306,12 +317,10 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
       const float *gsrc = a.decay + bh * T * dk + goff + ptid % GW;
       const int r0 = (ptid / GW) * K::SEGR;
 #pragma unroll
-      for (int i = 0; i < K::SEGR; ++i)
-        rG[i] = (r0 + i < L) ? gsrc[(t0 + r0 + i) * dk] : 1.f; // past the end: no decay
+      for (int i = 0; i < K::SEGR; ++i) rG[i] = gsrc[(t0 + (r0 + i < L ? r0 + i : L - 1)) * dk];
     }
     if constexpr (K::TOKEN) {
-      rTok = 1.f;
-      if (ptid < L) rTok = a.decay[bh * T + t0 + ptid];
+      if (pwave == 0) rTok = a.decay[bh * T + t0 + (ptid < L ? ptid : L - 1)];
     }
   };
   // phase-1 inputs: the decay and the tiles copied unconverted; phase-2: the decayed tiles
@@ -325,21 +334,23 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     else ld_z(n);
   };
 
-  auto phase1 = [&](int s) {
+  auto phase1 = [&](int n, int s) {
+    const int L = chunk_len(n);
     if constexpr (K::GATE) {
-      // local products down this thread's segment, and the segment's total
+      // local products down this thread's segment, and the segment's total; rows past the
+      // end carry no decay
       const int col = ptid % GW, seg = ptid / GW;
       float *loc = (ROLE == BWD_DV) ? sBS : stB(s);
       float p = 1.f;
 #pragma unroll
       for (int i = 0; i < K::SEGR; ++i) {
-        p *= rG[i];
+        p *= (seg * K::SEGR + i < L) ? rG[i] : 1.f;
         loc[(seg * K::SEGR + i) * GW + col] = p;
       }
       sTot[seg * GW + col] = p;
     } else if constexpr (K::TOKEN) {
       if (pwave == 0) {
-        float x = rTok;
+        float x = lane < L ? rTok : 1.f;
         for (int d = 1; d < 64; d <<= 1) {
           const float o = __shfl_up(x, d);
           if (lane >= d) x *= o;
@@ -353,15 +364,20 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
 #pragma unroll
       for (int j = 0; j < K::NVZ; ++j) {
         const int vi = ptid + K::NTG * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
-        st_words_lds<4>(stZ(s) + r * LDZ + c, rZ[j]);
+        const uint32_t m = r < L ? ~0u : 0u; // rows past the end: zeros
+        const uint32_t w[4] = {rZ[j][0] & m, rZ[j][1] & m, rZ[j][2] & m, rZ[j][3] & m};
+        st_words_lds<4>(stZ(s) + r * LDZ + c, w);
       }
     } else {
       constexpr int VPRX = DY / VE;
 #pragma unroll
       for (int j = 0; j < K::NVX; ++j) {
         const int vi = ptid + K::NTG * j, r = vi / VPRX, c = (vi % VPRX) * VE;
-        st_words_lds<4>(stX(s) + r * LDX + c, rX[j]);
-        st_words_lds<4>(stY(s) + r * LDX + c, rY[j]);
+        const uint32_t m = r < L ? ~0u : 0u; // rows past the end: zeros
+        const uint32_t wx[4] = {rX[j][0] & m, rX[j][1] & m, rX[j][2] & m, rX[j][3] & m};
+        const uint32_t wy[4] = {rY[j][0] & m, rY[j][1] & m, rY[j][2] & m, rY[j][3] & m};
+        st_words_lds<4>(stX(s) + r * LDX + c, wx);
+        st_words_lds<4>(stY(s) + r * LDX + c, wy);
       }
     }
   };
@@ -380,7 +396,8 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     auto b_vec = [&](float *bb, int r, int c) {
       if constexpr (K::GATE) {
         const float *loc = ((ROLE == BWD_DV) ? sBS : stB(s)) + r * GW + c;
-        const int seg = r / K::SEGR;
+        // the rows of one wave's vector lie in one segment (static_assert below): a scalar loop
+        const int seg = __builtin_amdgcn_readfirstlane(r / K::SEGR);
 #pragma unroll
         for (int e = 0; e < VE; e += 4) {
           f32x4 pre = {1.f, 1.f, 1.f, 1.f};
@@ -397,47 +414,53 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
         for (int e = 0; e < VE; ++e) bb[e] = x;
       }
     };
-    if constexpr (ROLE == BWD_DV) {
-      constexpr int VPRX = DY / VE;
+    // the decayed tiles, with phi chosen once for the whole chunk
+    auto transform = [&](auto elu_c) {
+      constexpr bool ELU = decltype(elu_c)::value;
+      if constexpr (ROLE == BWD_DV) {
+        constexpr int VPRX = DY / VE;
 #pragma unroll
-      for (int j = 0; j < K::NVX; ++j) {
-        const int vi = ptid + K::NTG * j, r = vi / VPRX, c = (vi % VPRX) * VE;
-        float fx[VE], fy[VE], bb[VE];
-        unpack<TIn, VE>(fx, rX[j]);
-        unpack<TIn, VE>(fy, rY[j]);
-        b_vec(bb, r, c);
-        const bool ok = r < L;
+        for (int j = 0; j < K::NVX; ++j) {
+          const int vi = ptid + K::NTG * j, r = vi / VPRX, c = (vi % VPRX) * VE;
+          float fx[VE], fy[VE], bb[VE];
+          unpack<TIn, VE>(fx, rX[j]);
+          unpack<TIn, VE>(fy, rY[j]);
+          b_vec(bb, r, c);
+          const float ok = r < L ? 1.f : 0.f; // rows past the end (finite values): zeros
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          fx[e] = ok ? phi_f(fx[e], elu1) * rcp_f(bb[e]) : 0.f;
-          fy[e] = ok ? phi_f(fy[e], elu1) * bb[e] : 0.f;
+          for (int e = 0; e < VE; ++e) {
+            fx[e] = phi_c<ELU>(fx[e]) * rcp_f(bb[e]) * ok;
+            fy[e] = phi_c<ELU>(fy[e]) * bb[e] * ok;
+          }
+          st_lds<TIn, VE>(stX(s) + r * LDX + c, fx);
+          st_lds<TIn, VE>(stY(s) + r * LDX + c, fy);
         }
-        st_lds<TIn, VE>(stX(s) + r * LDX + c, fx);
-        st_lds<TIn, VE>(stY(s) + r * LDX + c, fy);
+      } else {
+        constexpr int VPRZ = XW / VE;
+#pragma unroll
+        for (int j = 0; j < K::NVZ; ++j) {
+          const int vi = ptid + K::NTG * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
+          float fz[VE], bb[VE];
+          unpack<TIn, VE>(fz, rZ[j]);
+          b_vec(bb, r, c);
+          const float ok = r < L ? 1.f : 0.f; // rows past the end (finite values): zeros
+#pragma unroll
+          for (int e = 0; e < VE; ++e) {
+            const float pz = phi_c<ELU>(fz[e]);
+            fz[e] = (ROLE == BWD_DQ ? pz * rcp_f(bb[e]) : pz * bb[e]) * ok;
+          }
+          st_lds<TIn, VE>(stZ(s) + r * LDZ + c, fz);
+          if constexpr (K::SPLIT) {
+            float fl[VE];
+#pragma unroll
+            for (int e = 0; e < VE; ++e) fl[e] = fz[e] - (float)(TIn)fz[e];
+            st_lds<TIn, VE>(stZL(s) + r * LDZ + c, fl);
+          }
+        }
       }
-    } else {
-      constexpr int VPRZ = XW / VE;
-#pragma unroll
-      for (int j = 0; j < K::NVZ; ++j) {
-        const int vi = ptid + K::NTG * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
-        float fz[VE], bb[VE];
-        unpack<TIn, VE>(fz, rZ[j]);
-        b_vec(bb, r, c);
-        const bool ok = r < L;
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          const float pz = phi_f(fz[e], elu1);
-          fz[e] = ok ? (ROLE == BWD_DQ ? pz * rcp_f(bb[e]) : pz * bb[e]) : 0.f;
-        }
-        st_lds<TIn, VE>(stZ(s) + r * LDZ + c, fz);
-        if constexpr (K::SPLIT) {
-          float fl[VE];
-#pragma unroll
-          for (int e = 0; e < VE; ++e) fl[e] = fz[e] - (float)(TIn)fz[e];
-          st_lds<TIn, VE>(stZL(s) + r * LDZ + c, fl);
-        }
-      }
-    }
+    };
+    if (elu1) transform(std::true_type{});
+    else transform(std::false_type{});
   };
 
   if constexpr (K::PC) {
@@ -446,7 +469,7 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
       if (nchunks > 0) {
         load1(chunk_at(0));
         load2(chunk_at(0));
-        phase1(0);
+        phase1(chunk_at(0), 0);
         if (nchunks > 1) load1(chunk_at(1));
       }
       __syncthreads();
@@ -458,7 +481,7 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
       for (int it = 0; it < nchunks; ++it) {
         const int s = (it + 1) & 1;
         if (it + 1 < nchunks) {
-          phase1(s);
+          phase1(chunk_at(it + 1), s);
           if (it + 2 < nchunks) load1(chunk_at(it + 2));
         }
         __syncthreads(); // consumers: score tiles of chunk it written
@@ -519,24 +542,23 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     if constexpr (K::HAS_AUX) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        const int r = 16 * rb + li;
-        const TIn *pa = srcA + (t0 + r) * dk + zoff + xc;
+        // rows past the end read the last row (no branch); their outputs are not stored
+        const int r = 16 * rb + li, rc = r < L ? r : L - 1;
+        const TIn *pa = srcA + (t0 + rc) * dk + zoff + xc;
         if constexpr (K::ES == 2) {
-          uint2 w2 = make_uint2(0, 0);
-          if (r < L) w2 = *reinterpret_cast<const uint2 *>(pa);
+          const uint2 w2 = *reinterpret_cast<const uint2 *>(pa);
           raux[rb][0] = w2.x; raux[rb][1] = w2.y;
         } else {
-          uint4 w4 = make_uint4(0, 0, 0, 0);
-          if (r < L) w4 = *reinterpret_cast<const uint4 *>(pa);
+          const uint4 w4 = *reinterpret_cast<const uint4 *>(pa);
           raux[rb][0] = w4.x; raux[rb][1] = w4.y; raux[rb][2] = w4.z; raux[rb][3] = w4.w;
         }
         rqv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
         ralpha[rb] = f32x4{1.f, 1.f, 1.f, 1.f};
         if constexpr (K::HAS_RQ) {
-          if (want_dg && r < L) rqv[rb] = *reinterpret_cast<const f32x4 *>(a.rq + (bh * T + t0 + r) * dk + zoff + xc);
+          if (want_dg) rqv[rb] = *reinterpret_cast<const f32x4 *>(a.rq + (bh * T + t0 + rc) * dk + zoff + xc);
         }
         if constexpr (ROLE == BWD_DK && K::GATE) {
-          if (want_dg && r < L) ralpha[rb] = *reinterpret_cast<const f32x4 *>(a.decay + (bh * T + t0 + r) * dk + goff + xc);
+          if (want_dg) ralpha[rb] = *reinterpret_cast<const f32x4 *>(a.decay + (bh * T + t0 + rc) * dk + goff + xc);
         }
       }
     }
@@ -625,7 +647,10 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     auto phi4 = [&](int rb) -> f32x4 {
       float f[4];
       unpack<TIn, 4>(f, raux[rb]);
-      return f32x4{phi_f(f[0], elu1), phi_f(f[1], elu1), phi_f(f[2], elu1), phi_f(f[3], elu1)};
+      f32x4 p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = elu1 ? phi_c<true>(f[e]) : f[e];
+      return p;
     };
     (void)phi4;
     (void)b_at4;
@@ -785,7 +810,7 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     for (int it = 0; it < nchunks; ++it) {
       const int n = chunk_at(it);
       load_lane(n);
-      phase1(0);
+      phase1(n, 0);
       if (it + 1 < nchunks) load1(chunk_at(it + 1));
       __syncthreads();
       phase2(n, 0);
