@@ -532,10 +532,10 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
   }
 
   // this lane's rows 16 rb + li, columns xc .. xc+3: raw q (dq role) or k (dk role) for
-  // phi and phi', phi(q) dphi(q) from the dq pass and the raw gate (dk role) - read from
-  // global memory at the start of the chunk, used by the output tiles
+  // phi and phi', and phi(q) dphi(q) from the dq pass (dk role) - read from global memory
+  // at the start of the chunk, used by the output tiles
   uint32_t raux[4][K::ES]; // 4 elements of the input type
-  f32x4 rqv[4], ralpha[4];
+  f32x4 rqv[4];
   auto load_lane = [&](int n) {
     const int L = chunk_len(n);
     const int64_t t0 = (int64_t)n * C;
@@ -553,12 +553,8 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
           raux[rb][0] = w4.x; raux[rb][1] = w4.y; raux[rb][2] = w4.z; raux[rb][3] = w4.w;
         }
         rqv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        ralpha[rb] = f32x4{1.f, 1.f, 1.f, 1.f};
         if constexpr (K::HAS_RQ) {
           if (want_dg) rqv[rb] = *reinterpret_cast<const f32x4 *>(a.rq + (bh * T + t0 + rc) * dk + zoff + xc);
-        }
-        if constexpr (ROLE == BWD_DK && K::GATE) {
-          if (want_dg) ralpha[rb] = *reinterpret_cast<const f32x4 *>(a.decay + (bh * T + t0 + rc) * dk + goff + xc);
         }
       }
     }
@@ -749,19 +745,27 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     // 16 lanes of a group and the 4 row blocks of a lane)
     if constexpr (ROLE == BWD_DK && K::GATE) {
       if (want_dg) {
-        f32x4 dg[4];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           float v[4] = {rr[0][qq], rr[1][qq], rr[2][qq], rr[3][qq]};
           const float tot = suffix_rows64(v, g);
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb) dg[rb][qq] = (v[rb] + carry4[qq]) / ralpha[rb][qq];
+          for (int rb = 0; rb < 4; ++rb) rr[rb][qq] = v[rb] + carry4[qq];
           carry4[qq] += tot;
         }
+        // d alpha = d log alpha / alpha, with alpha_r = l_r / l_{r-1} from the local
+        // products l down each 16-row segment (l_{r-1} = 1 at a segment's first row): exact
+        // to an ulp or two where the products do not underflow, which the 1/b scaling of
+        // the output tiles requires anyway
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
           const int r = 16 * rb + li;
-          if (r < L) *reinterpret_cast<f32x4 *>(a.dgate + (bh * T + t0 + r) * dk + goff + xc) = dg[rb];
+          const f32x4 lc = *reinterpret_cast<const f32x4 *>(sB + r * GW + xc);
+          const f32x4 lp = *reinterpret_cast<const f32x4 *>(sB + (li ? r - 1 : r) * GW + xc);
+          f32x4 dg;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) dg[qq] = (rr[rb][qq] * (li ? lp[qq] : 1.f)) / lc[qq];
+          if (r < L) *reinterpret_cast<f32x4 *>(a.dgate + (bh * T + t0 + r) * dk + goff + xc) = dg;
         }
       }
     }
