@@ -98,8 +98,9 @@ struct Cfg {
 #ifdef FLA_FORCE_NCW
   static constexpr int NCW = FLA_FORCE_NCW;
 #else
-  // the gate's producers are VALU-heavy: give two SIMDs to producers alone
-  static constexpr int NCW = ((DECAY == DECAY_GATE || DECAY == DECAY_TOKEN) && DK <= 128) ? 2 : 4;
+  // the per-key gate's producers are VALU-heavy: give two SIMDs to producers alone (the
+  // per-token gate scans one column and runs faster with four consumer waves)
+  static constexpr int NCW = (DECAY == DECAY_GATE && DK <= 128) ? 2 : 4;
 #endif
   static constexpr int ET = 4 / NCW;
   static constexpr int NT = 64 * (NCW + 4);     // + 4 producer waves
