@@ -31,7 +31,7 @@ FLA_LAYOUT_BTHD = 1 << 6
 
 EXPORTED = ("fla_linattn_fwd", "fla_linattn_fwd_segments", "fla_linattn_step",
             "fla_status_string", "fla_linattn_segments_for", "fla_linattn_bwd",
-            "fla_linattn_fwd_varlen", "fla_gdn_fwd")
+            "fla_linattn_fwd_varlen", "fla_linattn_bwd_varlen", "fla_gdn_fwd")
 
 _lib = None
 
@@ -70,6 +70,9 @@ def load_library():
     lib.fla_linattn_fwd_varlen.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64,
                                            u32, p]
     lib.fla_linattn_fwd_varlen.restype = c_int
+    lib.fla_linattn_bwd_varlen.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p, p, i64, i64, i64,
+                                           i64, i64, i64, u32, p]
+    lib.fla_linattn_bwd_varlen.restype = c_int
     lib.fla_gdn_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, u32, p]
     lib.fla_gdn_fwd.restype = c_int
     _lib = lib
@@ -188,12 +191,18 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
         decay: Optional[torch.Tensor] = None, *, decay_kind: Optional[str] = None,
         init_state: Optional[torch.Tensor] = None, dfinal: Optional[torch.Tensor] = None,
         want_dgate: bool = True, want_dinit: bool = True, chunk: int = 64,
-        phi_elu1: bool = False, stream=None):
-    """Chunkwise backward.  Inputs as in ``fwd`` (no normaliser); dout [B,H,T,dv] in q's
-    dtype; dfinal fp32 [B,H,dk,dv] or None.  Returns (dq, dk, dv, dgate, dinit): dgate is
-    shaped like the gate / per-token decay (None for gamma, no decay, or not wanted); dinit
-    fp32 [B,H,dk,dv] (None if not wanted)."""
-    B, H, T, dk = q.shape
+        phi_elu1: bool = False, layout: str = "bhtd", stream=None):
+    """Chunkwise backward.  Inputs as in ``fwd`` (no normaliser); dout laid out like v in
+    q's dtype; dfinal fp32 [B,H,dk,dv] or None.  Returns (dq, dk, dv, dgate, dinit): dgate
+    is shaped like the gate / per-token decay (None for gamma, no decay, or not wanted);
+    dinit fp32 [B,H,dk,dv] (None if not wanted).  layout="bthd": token-major tensors as in
+    ``fwd``."""
+    if layout == "bthd":
+        B, T, H, dk = q.shape
+    elif layout == "bhtd":
+        B, H, T, dk = q.shape
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
     dv = v.shape[-1]
     kind = _decay_kind(decay, decay_kind)
     for t in (q, k, v, dout, decay, init_state, dfinal):
@@ -206,7 +215,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
     dinit = None
     if want_dinit:
         dinit = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-    flags = flags_for(q.dtype, kind, phi_elu1, False)
+    flags = flags_for(q.dtype, kind, phi_elu1, False) | (FLA_LAYOUT_BTHD if layout == "bthd" else 0)
     rc = load_library().fla_linattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(init_state),
                                         _ptr(dout), _ptr(dfinal), _ptr(dq), _ptr(dkk), _ptr(dvv),
                                         _ptr(dgate), _ptr(dinit), B, H, T, dk, dv, chunk, flags,
@@ -249,6 +258,41 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: to
     if rc != FLA_OK:
         raise FlaError("fla_linattn_fwd_varlen", rc)
     return out, final_state
+
+
+def bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+               cu_seqlens: torch.Tensor, decay: Optional[torch.Tensor] = None, *,
+               decay_kind: Optional[str] = None, init_state: Optional[torch.Tensor] = None,
+               dfinal: Optional[torch.Tensor] = None, want_dgate: bool = True,
+               want_dinit: bool = True, chunk: int = 64, phi_elu1: bool = False, stream=None):
+    """Backward over packed sequences (the gradients of ``fwd_varlen``).  Tensors as in
+    ``fwd_varlen``; dout [total,H,dv]; dfinal fp32 [N,H,dk,dv] or None.  Returns
+    (dq, dk, dv, dgate, dinit) as ``bwd`` does, dinit [N,H,dk,dv]."""
+    total, H, dk = q.shape
+    dv = v.shape[-1]
+    n = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int64 or n < 1:
+        raise ValueError("cu_seqlens must be an int64 tensor of N + 1 offsets")
+    if decay_kind is None:
+        decay_kind = ("none" if decay is None
+                      else {1: "gamma", 2: "token"}.get(decay.dim(), "gate"))
+    for t in (q, k, v, dout, decay, init_state, dfinal, cu_seqlens):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    dq, dkk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dgate = None
+    if want_dgate and decay_kind in ("gate", "token"):
+        dgate = torch.empty_like(decay, dtype=torch.float32)
+    dinit = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device) if want_dinit else None
+    flags = flags_for(q.dtype, decay_kind, phi_elu1, False) | FLA_LAYOUT_BTHD
+    rc = load_library().fla_linattn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(decay),
+                                               _ptr(init_state), _ptr(dout), _ptr(dfinal),
+                                               _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dgate),
+                                               _ptr(dinit), _ptr(cu_seqlens), n, total, H, dk,
+                                               dv, chunk, flags, _stream(stream))
+    if rc != FLA_OK:
+        raise FlaError("fla_linattn_bwd_varlen", rc)
+    return dq, dkk, dvv, dgate, dinit
 
 
 def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,

@@ -45,8 +45,12 @@ struct BwdArgs {
   float *dinit;        // [B][H][dk][dv] (written by DV) or null
   float *rq;           // workspace [B][H][T][dk]: phi(q) dphi(q) (DQ writes, DK reads) or null
   float *fterm;        // workspace [B][H][dk]: sum_e dfinal h_T (DQ writes, DK reads) or null
-  float *tpart;        // workspace [B][H][nsl][4][T]: d log a_t per slice and wave (token) or null
-  int64_t T;
+  float *tpart;        // workspace [H][nsl][4][ntok]: d log a_t per slice and wave (token) or null
+  int64_t T;           // tokens per sequence (packed: the total)
+  int64_t ntok;        // tokens over all sequences (B T, or the packed total)
+  int bthd;            // 1: q, k, v, dout, gate and their gradients token-major [B][T][H][d]
+                       //    (packed [total][H][d] with cu_seqlens); 0: [B][H][T][d]
+  const int64_t *cu_seqlens; // packed sequences: [B + 1] token offsets (bthd only), or null
   int H, dk, dv;
   int nsl;             // 64-wide slices of the output dimension
   int nunits;          // B * H * nsl
@@ -227,27 +231,45 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
   const int slice = unit % a.nsl;
   const int64_t bh = unit / a.nsl;
   const int h = (int)(bh % a.H);
-  const int64_t T = a.T;
   const int dk = a.dk, dv = a.dv;
+
+  // Token addressing.  [B][H][T][d]: the unit's rows are contiguous rows of d.  [B][T][H][d]
+  // / packed [total][H][d]: row t of this head of sequence b is token tok0 + t of the
+  // token-major array (tok0 = b T, or cu_seqlens[b] clamped to the array), rows H d apart.
+  const int64_t b = bh / a.H;
+  int64_t T = a.T, tok0 = b * a.T;
+  if (a.cu_seqlens) {
+    int64_t s = a.cu_seqlens[b], e = a.cu_seqlens[b + 1];
+    s = s < 0 ? 0 : (s > a.T ? a.T : s);
+    e = e < s ? s : (e > a.T ? a.T : e);
+    tok0 = s;
+    T = e - s;
+  }
+  const int64_t rsK = a.bthd ? (int64_t)a.H * dk : dk;  // rows of q, k, dq, dk, the gate
+  const int64_t rsV = a.bthd ? (int64_t)a.H * dv : dv;  // rows of v, dout, dv
+  const int64_t rsT = a.bthd ? a.H : 1;                 // per-token decay
+  const int64_t baseK = a.bthd ? (tok0 * a.H + h) * dk : bh * a.T * dk;
+  const int64_t baseV = a.bthd ? (tok0 * a.H + h) * dv : bh * a.T * dv;
+  const int64_t baseT = a.bthd ? tok0 * a.H + h : bh * a.T;
   const int nchunks = (int)((T + C - 1) / C);
   const int elu1 = a.phi_elu1;
   const bool want_dg = a.want_dg != 0;
 
-  // sources: X, Y rows of DY elements; Z and AUX 64-column slices
+  // sources: X, Y rows of DY elements; Z and AUX 64-column slices; row strides rsXY, rsZ
   const TIn *srcX, *srcY, *srcZ, *srcA = nullptr;
-  int ldz;
+  int64_t rsXY, rsZ;
   if constexpr (ROLE == BWD_DQ) {
-    srcX = (const TIn *)a.dout + bh * T * dv; srcY = (const TIn *)a.v + bh * T * dv;
-    srcZ = (const TIn *)a.k + bh * T * dk; srcA = (const TIn *)a.q + bh * T * dk;
-    ldz = dk;
+    srcX = (const TIn *)a.dout + baseV; srcY = (const TIn *)a.v + baseV;
+    srcZ = (const TIn *)a.k + baseK; srcA = (const TIn *)a.q + baseK;
+    rsXY = rsV; rsZ = rsK;
   } else if constexpr (ROLE == BWD_DK) {
-    srcX = (const TIn *)a.v + bh * T * dv; srcY = (const TIn *)a.dout + bh * T * dv;
-    srcZ = (const TIn *)a.q + bh * T * dk; srcA = (const TIn *)a.k + bh * T * dk;
-    ldz = dk;
+    srcX = (const TIn *)a.v + baseV; srcY = (const TIn *)a.dout + baseV;
+    srcZ = (const TIn *)a.q + baseK; srcA = (const TIn *)a.k + baseK;
+    rsXY = rsV; rsZ = rsK;
   } else {
-    srcX = (const TIn *)a.k + bh * T * dk; srcY = (const TIn *)a.q + bh * T * dk;
-    srcZ = (const TIn *)a.dout + bh * T * dv;
-    ldz = dv;
+    srcX = (const TIn *)a.k + baseK; srcY = (const TIn *)a.q + baseK;
+    srcZ = (const TIn *)a.dout + baseV;
+    rsXY = rsK; rsZ = rsV;
   }
   const int zoff = slice * XW;                      // first output column
   const int goff = (ROLE == BWD_DV) ? 0 : zoff;     // first gate column
@@ -290,8 +312,8 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
       // rows past the end read the last row and are masked where the tiles are formed
       // (a select here would make the compiler wait for the load)
       const int rc = r < L ? r : L - 1;
-      const uint4 x = *reinterpret_cast<const uint4 *>(srcX + (t0 + rc) * DY + c);
-      const uint4 y = *reinterpret_cast<const uint4 *>(srcY + (t0 + rc) * DY + c);
+      const uint4 x = *reinterpret_cast<const uint4 *>(srcX + (t0 + rc) * rsXY + c);
+      const uint4 y = *reinterpret_cast<const uint4 *>(srcY + (t0 + rc) * rsXY + c);
       rX[j][0] = x.x; rX[j][1] = x.y; rX[j][2] = x.z; rX[j][3] = x.w;
       rY[j][0] = y.x; rY[j][1] = y.y; rY[j][2] = y.z; rY[j][3] = y.w;
     }
@@ -304,7 +326,7 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     for (int j = 0; j < K::NVZ; ++j) {
       const int vi = ptid + K::NTG * j, r = vi / VPRZ, c = (vi % VPRZ) * VE;
       const int rc = r < L ? r : L - 1;
-      const uint4 z = *reinterpret_cast<const uint4 *>(srcZ + (t0 + rc) * ldz + zoff + c);
+      const uint4 z = *reinterpret_cast<const uint4 *>(srcZ + (t0 + rc) * rsZ + zoff + c);
       rZ[j][0] = z.x; rZ[j][1] = z.y; rZ[j][2] = z.z; rZ[j][3] = z.w;
     }
   };
@@ -314,13 +336,13 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     if constexpr (K::GATE) {
       // thread (column ptid % GW, segment ptid / GW) reads its SEGR rows: for each row the
       // lanes of a wave read consecutive columns
-      const float *gsrc = a.decay + bh * T * dk + goff + ptid % GW;
+      const float *gsrc = a.decay + baseK + goff + ptid % GW;
       const int r0 = (ptid / GW) * K::SEGR;
 #pragma unroll
-      for (int i = 0; i < K::SEGR; ++i) rG[i] = gsrc[(t0 + (r0 + i < L ? r0 + i : L - 1)) * dk];
+      for (int i = 0; i < K::SEGR; ++i) rG[i] = gsrc[(t0 + (r0 + i < L ? r0 + i : L - 1)) * rsK];
     }
     if constexpr (K::TOKEN) {
-      if (pwave == 0) rTok = a.decay[bh * T + t0 + (ptid < L ? ptid : L - 1)];
+      if (pwave == 0) rTok = a.decay[baseT + (t0 + (ptid < L ? ptid : L - 1)) * rsT];
     }
   };
   // phase-1 inputs: the decay and the tiles copied unconverted; phase-2: the decayed tiles
@@ -544,7 +566,7 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
       for (int rb = 0; rb < 4; ++rb) {
         // rows past the end read the last row (no branch); their outputs are not stored
         const int r = 16 * rb + li, rc = r < L ? r : L - 1;
-        const TIn *pa = srcA + (t0 + rc) * dk + zoff + xc;
+        const TIn *pa = srcA + (t0 + rc) * rsK + zoff + xc;
         if constexpr (K::ES == 2) {
           const uint2 w2 = *reinterpret_cast<const uint2 *>(pa);
           raux[rb][0] = w2.x; raux[rb][1] = w2.y;
@@ -554,7 +576,7 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
         }
         rqv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (K::HAS_RQ) {
-          if (want_dg) rqv[rb] = *reinterpret_cast<const f32x4 *>(a.rq + (bh * T + t0 + rc) * dk + zoff + xc);
+          if (want_dg) rqv[rb] = *reinterpret_cast<const f32x4 *>(a.rq + baseK + (t0 + rc) * rsK + zoff + xc);
         }
       }
     }
@@ -703,8 +725,8 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
           f32x4 dq4;
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) dq4[qq] = dqb[qq] * phi_d(qb[qq], elu1);
-          st_out4<TIn>((TIn *)a.grad_q + (bh * T + t) * dk + zoff + xc, dq4);
-          if (want_dg) *reinterpret_cast<f32x4 *>(a.rq + (bh * T + t) * dk + zoff + xc) = qb * dqb;
+          st_out4<TIn>((TIn *)a.grad_q + baseK + t * rsK + zoff + xc, dq4);
+          if (want_dg) *reinterpret_cast<f32x4 *>(a.rq + baseK + t * rsK + zoff + xc) = qb * dqb;
         }
       } else if constexpr (ROLE == BWD_DK) {
         const f32x4 bb = b_at4(r, rb);
@@ -716,11 +738,11 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
           f32x4 dk4;
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) dk4[qq] = dkb[qq] * phi_d(kb[qq], elu1);
-          st_out4<TIn>((TIn *)a.grad_k + (bh * T + t) * dk + zoff + xc, dk4);
+          st_out4<TIn>((TIn *)a.grad_k + baseK + t * rsK + zoff + xc, dk4);
         }
         rr[rb] = (r < L) ? rqv[rb] - kb * dkb : f32x4{0.f, 0.f, 0.f, 0.f};
       } else {
-        if (r < L) st_out4<TIn>((TIn *)a.grad_v + (bh * T + t) * dv + zoff + xc, acc);
+        if (r < L) st_out4<TIn>((TIn *)a.grad_v + baseV + t * rsV + zoff + xc, acc);
       }
     });
     (void)rr;
@@ -765,7 +787,7 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
           f32x4 dg;
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) dg[qq] = (rr[rb][qq] * (li ? lp[qq] : 1.f)) / lc[qq];
-          if (r < L) *reinterpret_cast<f32x4 *>(a.dgate + (bh * T + t0 + r) * dk + goff + xc) = dg;
+          if (r < L) *reinterpret_cast<f32x4 *>(a.dgate + baseK + (t0 + r) * rsK + goff + xc) = dg;
         }
       }
     }
@@ -782,7 +804,7 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
         }
         const float tot = suffix_rows64(v, g);
         if (g == 0) {
-          float *tp = a.tpart + ((bh * a.nsl + slice) * 4 + wave) * T + t0;
+          float *tp = a.tpart + ((int64_t)(h * a.nsl + slice) * 4 + wave) * a.ntok + tok0 + t0;
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb) {
             const int r = 16 * rb + li;

@@ -106,15 +106,18 @@ BwdLauncher find_bwd(bool bf16, int64_t dy, int role, int decay) {
 // ---------------------------------------------------------------------------------
 // small kernels
 
-// Per-token decay gradient: d alpha_t = (sum of the nsl partial sums of d log a_t) / alpha_t.
+// Per-token decay gradient: d alpha = (sum of the nparts partial sums of d log a) / alpha,
+// per (head h, token tok of all sequences); partials tpart[h][p][tok].  The decay and its
+// gradient are [B][H][T] (tok = b T + t) or token-major [tokens][H] (bthd).
 __global__ void token_dgate_kernel(const float *tpart, const float *decay, float *dgate,
-                                   int64_t BH, int64_t T, int nsl) {
+                                   int64_t H, int64_t ntok, int64_t T, int nparts, int bthd) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= BH * T) return;
-  const int64_t bh = i / T, t = i % T;
+  if (i >= H * ntok) return;
+  const int64_t h = i / ntok, tok = i % ntok;
   float s = 0.f;
-  for (int p = 0; p < nsl; ++p) s += tpart[(bh * nsl + p) * T + t];
-  dgate[i] = s / decay[i];
+  for (int p = 0; p < nparts; ++p) s += tpart[(h * nparts + p) * ntok + tok];
+  const int64_t at = bthd ? tok * H + h : ((tok / T) * H + h) * T + tok % T;
+  dgate[at] = s / decay[at];
 }
 
 // dst[i] = src ? src[i] : 0 (state copy / zero fill).
@@ -354,7 +357,8 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
 int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_gamma,
              const float *init_state, const void *dout, const float *dfinal_state, void *dq,
              void *dk_out, void *dv_out, float *dgate, float *dinit_state, int64_t B, int64_t H,
-             int64_t T, int64_t dk, int64_t dv, int64_t chunk, uint32_t flags, void *stream) {
+             int64_t T, int64_t dk, int64_t dv, int64_t chunk, uint32_t flags,
+             const int64_t *cu_seqlens, void *stream) {
   gate_or_gamma = nonnull_decay_if_empty(gate_or_gamma, T, flags);
   int rc = check_common(B, H, dk, dv, flags, gate_or_gamma);
   if (rc != FLA_OK) return rc;
@@ -368,7 +372,9 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
       !aligned(init_state, 16) || !aligned(dfinal_state, 16) || !aligned(dinit_state, 16) ||
       !aligned(dgate, 16))
     return FLA_ERR_INVALID_ARG;
-  if (flags & (FLA_NORMALIZE | FLA_LAYOUT_BTHD)) return FLA_ERR_UNSUPPORTED;
+  if (flags & FLA_NORMALIZE) return FLA_ERR_UNSUPPORTED;
+  const bool bthd = cu_seqlens != nullptr || (flags & FLA_LAYOUT_BTHD) != 0;
+  if (bthd && H * (dk > dv ? dk : dv) > ((int64_t)1 << 20)) return FLA_ERR_UNSUPPORTED;
   if (chunk != 64) return FLA_ERR_UNSUPPORTED;
   if (dk < 64 || dv < 64) return FLA_ERR_UNSUPPORTED;
   if (B * H > ((int64_t)1 << 26) || T > ((int64_t)1 << 40) / (B * H)) return FLA_ERR_INVALID_ARG;
@@ -389,9 +395,10 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   // workspace for the decay gradient: phi(q) dphi(q) per token and key, the final state's
   // term per key, and (per-token decay) one partial sum per 16 keys and token
   const bool want_dg = dgate != nullptr;
-  const int64_t n_rq = want_dg ? nbh * T * dk : 0;
+  const int64_t ntok = cu_seqlens ? T : B * T; // tokens over all sequences
+  const int64_t n_rq = want_dg ? ntok * H * dk : 0;
   const int64_t n_ft = (want_dg && dfinal_state) ? nbh * dk : 0;
-  const int64_t n_tp = (want_dg && kind == DECAY_TOKEN) ? nbh * nslk * 4 * T : 0;
+  const int64_t n_tp = (want_dg && kind == DECAY_TOKEN) ? H * nslk * 4 * ntok : 0;
   float *ws = nullptr;
   if (n_rq + n_ft + n_tp > 0 &&
       hipMallocAsync(reinterpret_cast<void **>(&ws), (n_rq + n_ft + n_tp) * sizeof(float), s) != hipSuccess)
@@ -409,6 +416,9 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   a.fterm = n_ft ? ws + n_rq : nullptr;
   a.tpart = n_tp ? ws + n_rq + n_ft : nullptr;
   a.T = T;
+  a.ntok = ntok;
+  a.bthd = bthd ? 1 : 0;
+  a.cu_seqlens = cu_seqlens;
   a.H = (int)H; a.dk = (int)dk; a.dv = (int)dv;
   a.phi_elu1 = (flags & FLA_PHI_ELU1) ? 1 : 0;
   a.want_dg = want_dg ? 1 : 0;
@@ -430,11 +440,12 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   if (rc == FLA_OK && n_tp) {
     const float *tp = a.tpart;
     const float *dec = gate_or_gamma;
-    int64_t nbh_v = nbh, T_v = T;
-    int nsl_i = (int)nslk * 4; // partial sums per token: 4 waves per key slice
-    void *args[] = {&tp, &dec, &dgate, &nbh_v, &T_v, &nsl_i};
+    int64_t H_v = H, ntok_v = ntok, T_v = T;
+    int nparts = (int)nslk * 4; // partial sums per token: 4 waves per key slice
+    int bthd_i = bthd ? 1 : 0;
+    void *args[] = {&tp, &dec, &dgate, &H_v, &ntok_v, &T_v, &nparts, &bthd_i};
     if (hipLaunchKernel(reinterpret_cast<const void *>(&token_dgate_kernel),
-                        dim3(blocks_for(nbh * T, 256)), dim3(256), args, 0, s) != hipSuccess)
+                        dim3(blocks_for(H * ntok, 256)), dim3(256), args, 0, s) != hipSuccess)
       rc = FLA_ERR_DEVICE;
   }
   if (ws && hipFreeAsync(ws, s) != hipSuccess) rc = FLA_ERR_DEVICE;
@@ -512,7 +523,19 @@ int fla_linattn_bwd(const void *q, const void *k, const void *v, const float *ga
                     int64_t H, int64_t T, int64_t dk_dim, int64_t dv_dim, int64_t chunk,
                     uint32_t flags, void *stream) {
   return fla::bwd_impl(q, k, v, gate_or_gamma, init_state, dout, dfinal_state, dq, dk, dv, dgate,
-                       dinit_state, B, H, T, dk_dim, dv_dim, chunk, flags, stream);
+                       dinit_state, B, H, T, dk_dim, dv_dim, chunk, flags, nullptr, stream);
+}
+
+int fla_linattn_bwd_varlen(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+                           const float *init_state, const void *dout, const float *dfinal_state,
+                           void *dq, void *dk, void *dv, float *dgate, float *dinit_state,
+                           const int64_t *cu_seqlens, int64_t n_seqs, int64_t total_T, int64_t H,
+                           int64_t dk_dim, int64_t dv_dim, int64_t chunk, uint32_t flags,
+                           void *stream) {
+  if (!cu_seqlens || !fla::aligned(cu_seqlens, 8)) return FLA_ERR_INVALID_ARG;
+  return fla::bwd_impl(q, k, v, gate_or_gamma, init_state, dout, dfinal_state, dq, dk, dv, dgate,
+                       dinit_state, n_seqs, H, total_T, dk_dim, dv_dim, chunk,
+                       flags | FLA_LAYOUT_BTHD, cu_seqlens, stream);
 }
 
 const char *fla_status_string(int status) {

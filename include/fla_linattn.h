@@ -142,8 +142,9 @@ int fla_linattn_step(const void *q, const void *k, const void *v, const float *g
  * L = sum(dout (.) out) + sum(dfinal_state (.) final_state), by the reverse-mode chain rule
  * through the recurrence above (no normaliser).
  *
- *   q, k, v, gate_or_gamma, init_state: the forward call's inputs (layouts above).
- *   dout         : [B][H][T][dv], dtype of q; the gradient arriving at out.
+ *   q, k, v, gate_or_gamma, init_state: the forward call's inputs (layouts above, including
+ *                  token-major [B][T][H][d] with FLA_LAYOUT_BTHD).
+ *   dout         : laid out like v (dtype of q); the gradient arriving at out.
  *   dfinal_state : fp32 [B][H][dk][dv] gradient arriving at final_state, or NULL (zero).
  *   dq, dk, dv   : written, shaped and typed like q, k, v.
  *   dgate        : fp32, written with the gradient of the per-key gate [B][H][T][dk]
@@ -153,12 +154,12 @@ int fla_linattn_step(const void *q, const void *k, const void *v, const float *g
  *   dinit_state  : fp32 [B][H][dk][dv] written with the gradient of init_state (whether or
  *                  not init_state was given), or NULL.
  *   All pointers 16-byte aligned, except gamma and the per-token decay (4 bytes).
- *   dk, dv in {64, 128, 256} (fp32: up to 128); chunk = 64; FLA_NORMALIZE is not supported.
+ *   dk, dv in {64, 128, 256} (fp32: up to 128); chunk = 64; FLA_NORMALIZE is not supported;
+ *   token-major: H * max(dk, dv) <= 2^20.
  *   Three chunk-scan launches (dq forward in time; dv, then dk and dgate in reverse) and,
  *   when dgate is requested, a stream-ordered workspace of 4 (B H T dk + B H dk) bytes
- *   (+ 4 B H T dk/64 for the per-token decay).
- * Returns FLA_ERR_UNSUPPORTED for shapes or flags outside that set (also for
- * FLA_LAYOUT_BTHD: the backward takes the [B][H][T][d] layout).  The gate range
+ *   (+ 4 B H T dk/16 for the per-token decay, and a fourth small launch that sums it).
+ * Returns FLA_ERR_UNSUPPORTED for shapes or flags outside that set.  The gate range
  * condition of the forward pass applies.
  */
 int fla_linattn_bwd(const void *q, const void *k, const void *v, const float *gate_or_gamma,
@@ -166,6 +167,22 @@ int fla_linattn_bwd(const void *q, const void *k, const void *v, const float *ga
                     void *dq, void *dk, void *dv, float *dgate, float *dinit_state, int64_t B,
                     int64_t H, int64_t T, int64_t dk_dim, int64_t dv_dim, int64_t chunk,
                     uint32_t flags, void *stream);
+
+/*
+ * fla_linattn_bwd_varlen — fla_linattn_bwd over packed variable-length sequences: the
+ * gradients of fla_linattn_fwd_varlen.  Tensors as in that call (token-major [total_T][H][d];
+ * dout and dv like v; dq, dk like q, k; dgate like the gate or per-token decay); states
+ * init_state, dfinal_state, dinit_state: [n_seqs][H][dk][dv] fp32.  cu_seqlens as in
+ * fla_linattn_fwd_varlen (device int64 [n_seqs + 1], clamped to [0, total_T] on the device).
+ * Other arguments and limits as fla_linattn_bwd (B = n_seqs, T = total_T); sequences are
+ * independent, and an empty sequence gets dinit_state = dfinal_state.
+ */
+int fla_linattn_bwd_varlen(const void *q, const void *k, const void *v, const float *gate_or_gamma,
+                           const float *init_state, const void *dout, const float *dfinal_state,
+                           void *dq, void *dk, void *dv, float *dgate, float *dinit_state,
+                           const int64_t *cu_seqlens, int64_t n_seqs, int64_t total_T, int64_t H,
+                           int64_t dk_dim, int64_t dv_dim, int64_t chunk, uint32_t flags,
+                           void *stream);
 
 /*
  * fla_gdn_fwd — gated delta rule, chunkwise forward (textbook chapter 1.6, section "gated

@@ -139,10 +139,19 @@ def test_bwd_rejects_on_host(lib, kw, expected):
 
 
 def test_layout_and_varlen_rejects_on_host(lib):
-    # the backward takes the [B][H][T][d] layout only
-    assert bwd_raw(lib, flags=fla.FLA_LAYOUT_BTHD) == fla.FLA_ERR_UNSUPPORTED
     # token-major rows wider than 2^20 elements
     assert fwd_raw(lib, flags=fla.FLA_LAYOUT_BTHD, H=1 << 14, dk=128, dv=128) == fla.FLA_ERR_UNSUPPORTED
+    assert bwd_raw(lib, flags=fla.FLA_LAYOUT_BTHD, H=1 << 14, dkd=128, dvd=128) == fla.FLA_ERR_UNSUPPORTED
+    # backward over packed sequences: offsets required and 8-byte aligned, at least one
+    # sequence, no normaliser
+    bvl = lambda cu, **kw: lib.fla_linattn_bwd_varlen(
+        BOGUS, BOGUS, BOGUS, None, None, BOGUS, None, BOGUS, BOGUS, BOGUS, None, None, cu,
+        kw.get("n", 1), kw.get("T", 64), 1, 64, 64, 64, kw.get("flags", 0), None)
+    assert bvl(None) == fla.FLA_ERR_INVALID_ARG
+    assert bvl(ctypes.c_void_p((1 << 20) + 4)) == fla.FLA_ERR_INVALID_ARG
+    assert bvl(BOGUS, n=0) == fla.FLA_ERR_INVALID_ARG
+    assert bvl(BOGUS, flags=fla.FLA_NORMALIZE) == fla.FLA_ERR_UNSUPPORTED
+    assert bvl(BOGUS, flags=fla.FLA_DECAY_GATE) == fla.FLA_ERR_INVALID_ARG   # gate missing
     # packed sequences: offsets required and 8-byte aligned
     vl = lambda cu, **kw: lib.fla_linattn_fwd_varlen(BOGUS, BOGUS, BOGUS, None, None, BOGUS, None,
                                                      cu, kw.get("n", 1), kw.get("T", 64), 1, 64,
