@@ -71,7 +71,7 @@ def algorithmic_bwd(w) -> tuple[float, float]:
     2 * [(C+1)/2 * (3 dv + 3 dk) + 6 dk dv]."""
     s = 2 if w.dtype == "bf16" else 4
     th = w.B * w.H * w.T
-    b = th * (3 * w.dk + 3 * w.dv) * s
+    b = th * (4 * w.dk + 3 * w.dv) * s   # q, k, dq, dk (dk wide); v, dout, dv (dv wide)
     if w.decay == "gate":
         b += 2 * th * w.dk * 4
     elif w.decay == "token":
