@@ -69,15 +69,13 @@ struct GdnCfg {
   static constexpr int P_BETA = P_G + C * 4;
   static constexpr int P_LDS = P_BETA + C * 4;
   // state-pass LDS: two input stages {q, k^, W, g} (producer waves fill one while the
-  // consumer waves read the other), then the consumers' U, U (.) g_L / g and score tiles
+  // consumer waves read the other), then the consumers' score tiles
   static constexpr int S_Q = 0;
   static constexpr int S_K = S_Q + C * LDK * ES;
   static constexpr int S_W = S_K + C * LDK * ES;
   static constexpr int S_G = S_W + C * LDK * ES;    // g [C]
   static constexpr int S_STAGE = S_G + C * 4;
-  static constexpr int S_U = 2 * S_STAGE;           // U [C][LDV]
-  static constexpr int S_US = S_U + C * LDV * ES;   // U (.) g_L / g
-  static constexpr int S_P = S_US + C * LDV * ES;   // masked scores, 16 tile images
+  static constexpr int S_P = 2 * S_STAGE;           // masked scores, 16 tile images
   static constexpr int S_LDS = S_P + 16 * 256 * ES;
   static constexpr bool FITS = P_LDS <= kMaxLds && S_LDS <= kMaxLds;
 };
@@ -351,8 +349,6 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
   auto stage_k = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_K); };
   auto stage_w = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_W); };
   auto stage_g = [&](int s) { return reinterpret_cast<float *>(lds + s * K::S_STAGE + K::S_G); };
-  TIn *sU = reinterpret_cast<TIn *>(lds + K::S_U);
-  TIn *sUs = reinterpret_cast<TIn *>(lds + K::S_US);
   TIn *sP = reinterpret_cast<TIn *>(lds + K::S_P);
 
   const int tid = threadIdx.x;
@@ -473,6 +469,9 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       if constexpr (sizeof(TIn) == 2) hf[u] = acc_frag_bf(Hs[2 * u], Hs[2 * u + 1]);
       else hf[u] = Hs[u];
     }
+    // U and U (.) g_L / g stay in accumulator tiles: two 16-row tiles are the MFMA operand
+    // of a 32-row K unit (rows 32u + 4g + s and +16 of column li), so no LDS round trip
+    f32x4 uacc[4], usacc[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -483,17 +482,21 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       for (int qq = 0; qq < 4; ++qq) {
         const int t = 16 * tb + 4 * g + qq;
         const float uval = U0[tb][qq] - x[qq];
-        sU[t * LDV + 16 * wave + li] = (TIn)uval;
-        sUs[t * LDV + 16 * wave + li] = (TIn)(uval * (gL / sG[t]));
+        uacc[tb][qq] = uval;
+        usacc[tb][qq] = uval * (gL / sG[t]);
       }
     }
-    __syncthreads();
+    auto frag_of = [&](const f32x4 *tiles, int u) -> Frag<TIn> {
+      if constexpr (sizeof(TIn) == 2) return acc_frag_bf(tiles[2 * u], tiles[2 * u + 1]);
+      else return tiles[u];
+    };
+    __syncthreads(); // every consumer wave's score tiles written
 
     // ---- O = (masked scores) U + diag(g) Q H -------------------------------------------
     {
       Frag<TIn> uf[NZU];
 #pragma unroll
-      for (int u = 0; u < NZU; ++u) uf[u] = ld_frag_t<TIn, true>(sU, LDV, 16 * wave, u, g, li);
+      for (int u = 0; u < NZU; ++u) uf[u] = frag_of(uacc, u);
       static_for<0, 4>([&](auto TB) {
         constexpr int tb = TB;
         f32x4 oi = {0.f, 0.f, 0.f, 0.f};
@@ -526,7 +529,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     {
       Frag<TIn> usf[NZU];
 #pragma unroll
-      for (int u = 0; u < NZU; ++u) usf[u] = ld_frag_t<TIn, true>(sUs, LDV, 16 * wave, u, g, li);
+      for (int u = 0; u < NZU; ++u) usf[u] = frag_of(usacc, u);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f32x4 hnew = Hs[cb] * gL;
