@@ -37,13 +37,14 @@ enum : int { BWD_DQ = 0, BWD_DK = 1, BWD_DV = 2 };
 
 struct BwdArgs {
   const void *q, *k, *v, *dout;
-  const float *decay;  // gamma [H], gate [B][H][T][dk], token [B][H][T], or null
+  const float *decay;  // gamma [H], gate (laid out like q), per-token decay (one per token
+                       // and head, [B][H][T] or token-major [tokens][H]), or null
   const float *init;   // [B][H][dk][dv] or null (read by DQ)
   const float *dfinal; // [B][H][dk][dv] or null (read by DV, DK, and DQ for its term)
   void *grad_q, *grad_k, *grad_v; // outputs in the input dtype
-  float *dgate;        // gate: [B][H][T][dk] (written by DK) or null
+  float *dgate;        // gate: laid out like the gate (written by DK) or null
   float *dinit;        // [B][H][dk][dv] (written by DV) or null
-  float *rq;           // workspace [B][H][T][dk]: phi(q) dphi(q) (DQ writes, DK reads) or null
+  float *rq;           // workspace laid out like q: phi(q) dphi(q) (DQ writes, DK reads) or null
   float *fterm;        // workspace [B][H][dk]: sum_e dfinal h_T (DQ writes, DK reads) or null
   float *tpart;        // workspace [H][nsl][4][ntok]: d log a_t per slice and wave (token) or null
   int64_t T;           // tokens per sequence (packed: the total)
