@@ -233,9 +233,6 @@ struct Cfg {
 // ---------------------------------------------------------------------------------
 // small helpers
 
-__device__ __forceinline__ float phi_f(float x, int elu1) {
-  return elu1 ? (x > 0.f ? x + 1.f : __expf(x)) : x;
-}
 __device__ __forceinline__ float rcp_f(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // N consecutive 32-bit words from global memory (N = 2, 4 or 8).
