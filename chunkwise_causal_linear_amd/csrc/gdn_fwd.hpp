@@ -497,6 +497,9 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       Frag<TIn> uf[NZU];
 #pragma unroll
       for (int u = 0; u < NZU; ++u) uf[u] = frag_of(uacc, u);
+      // formed transposed (O^T = U^T P^T + H^T Q^T: the same fragments with the operands
+      // swapped), so a lane holds 4 adjacent value columns of one row: one 8-byte store
+      const int e4 = vs * XW + 16 * wave + 4 * g;
       static_for<0, 4>([&](auto TB) {
         constexpr int tb = TB;
         f32x4 oi = {0.f, 0.f, 0.f, 0.f};
@@ -506,22 +509,23 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
             constexpr int TA = (2 * u <= tb) ? tb * 4 + 2 * u : -1;
             constexpr int TB2 = (2 * u + 1 <= tb) ? tb * 4 + 2 * u + 1 : -1;
             if constexpr (TA >= 0 || TB2 >= 0)
-              oi = mma(oi, ld_ptile2<TIn, TA, TB2>(sP + li * 16 + 4 * g), uf[u]);
+              oi = mma(oi, uf[u], ld_ptile2<TIn, TA, TB2>(sP + li * 16 + 4 * g));
           } else {
             constexpr int TA = (u <= tb) ? tb * 4 + u : -1;
-            if constexpr (TA >= 0) oi = mma(oi, ld_ptile2<TIn, TA, -1>(sP + li * 16 + 4 * g), uf[u]);
+            if constexpr (TA >= 0) oi = mma(oi, uf[u], ld_ptile2<TIn, TA, -1>(sP + li * 16 + 4 * g));
           }
         });
         f32x4 ox = {0.f, 0.f, 0.f, 0.f};
         const TIn *qa = sQ + (16 * tb + li) * LDK + 4 * g;
 #pragma unroll
-        for (int u = 0; u < DK / KU; ++u) ox = mma(ox, ld_frag_at<TIn, true>(qa, u), hf[u]);
+        for (int u = 0; u < DK / KU; ++u) ox = mma(ox, hf[u], ld_frag_at<TIn, true>(qa, u));
+        // oi[qq], ox[qq]: row t = 16 tb + li, value column e4 + qq
+        const int t = 16 * tb + li;
+        const float gt = sG[t];
+        f32x4 o;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int t = 16 * tb + 4 * g + qq;
-          const float o = oi[qq] + sG[t] * ox[qq];
-          if (t < L && e_lane < dv) gout[(t0 + t) * dv + e_lane] = (TIn)o;
-        }
+        for (int qq = 0; qq < 4; ++qq) o[qq] = oi[qq] + gt * ox[qq];
+        if (t < L && e4 < dv) st_out4<TIn>(gout + (t0 + t) * dv + e4, o);
       });
     }
 
