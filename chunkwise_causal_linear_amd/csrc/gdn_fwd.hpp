@@ -423,7 +423,10 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
   const float *gu = a.u0 + bh * T * dv;
   TIn *gout = static_cast<TIn *>(a.out) + bh * T * dv;
 
-  // this lane's U0 entries of a chunk (rows 16 tb + 4g + q), prefetched one chunk ahead
+  // this lane's U0 entries of a chunk (rows 16 tb + 4g + q), prefetched one chunk ahead;
+  // rows past the end read the last row (no branch: a branch would make the compiler wait
+  // for the load) and are zeroed where they are used.  dv is a multiple of 64, so every
+  // lane's column is in range.
   float ru[16];
   auto load_u0 = [&](int n) {
     const int L = chunk_len(n);
@@ -431,9 +434,14 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = 16 * (i >> 2) + 4 * g + (i & 3);
-      ru[i] = (t < L && e_lane < dv) ? gu[(t0 + t) * dv + e_lane] : 0.f;
+      ru[i] = gu[(t0 + (t < L ? t : L - 1)) * dv + e_lane];
     }
   };
+  // the output rows of a chunk: buffer stores over its L rows, so rows past the end are
+  // dropped without a branch (with a branch the compiler cannot count the stores in
+  // flight and waits for all of them before the next chunk's loads)
+  auto out_rsrc = [&](int64_t t0, int L) { return make_rsrc(gout + t0 * dv, L * dv * K::ES); };
+  const int e4 = vs * XW + 16 * wave + 4 * g; // this lane's 4 output columns (transposed tiles)
 
   // state: H[c][e_lane]; tile cb holds rows 16cb + 4g + q
   f32x4 Hs[NCB];
@@ -444,8 +452,19 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       const int c = 16 * cb + 4 * g + qq;
       Hs[cb][qq] = (a.init && e_lane < dv) ? a.init[(bh * DK + c) * dv + e_lane] : 0.f;
     }
+  // the state's loads complete here, not at a wait inside the loop (which, with vmcnt
+  // counting in order, would also wait for the previous chunk's stores)
+  __builtin_amdgcn_s_waitcnt(0);
 
-  if (nchunks > 0) load_u0(0);
+  if (nchunks > 0) {
+    load_u0(0);
+    // the loop's stores, to an empty range (dropped): the first iteration's wait for the
+    // prefetch then has the same pattern as the others
+    const auto rs = out_rsrc(0, 0);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+      st_out4_buf<TIn>(rs, ((16 * tb + li) * dv + e4) * K::ES, 0, f32x4{0.f, 0.f, 0.f, 0.f});
+  }
   __syncthreads();
 
   for (int n = 0; n < nchunks; ++n) {
@@ -457,8 +476,10 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const float *sG = stage_g(n & 1);
     f32x4 U0[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) U0[tb] = f32x4{ru[4 * tb], ru[4 * tb + 1], ru[4 * tb + 2], ru[4 * tb + 3]};
-    if (n + 1 < nchunks) load_u0(n + 1);
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) U0[tb][qq] = (16 * tb + 4 * g + qq < L) ? ru[4 * tb + qq] : 0.f;
+    load_u0(n + 1 < nchunks ? n + 1 : n); // the last chunk reads its own rows again
     const float gL = sG[C - 1]; // = g[L-1]: rows past the end carry alpha = 1
 
     // ---- masked scores (shared by the consumer waves); U = U0 - W H (this wave's columns)
@@ -499,7 +520,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       for (int u = 0; u < NZU; ++u) uf[u] = frag_of(uacc, u);
       // formed transposed (O^T = U^T P^T + H^T Q^T: the same fragments with the operands
       // swapped), so a lane holds 4 adjacent value columns of one row: one 8-byte store
-      const int e4 = vs * XW + 16 * wave + 4 * g;
+      const auto rs = out_rsrc(t0, L);
       static_for<0, 4>([&](auto TB) {
         constexpr int tb = TB;
         f32x4 oi = {0.f, 0.f, 0.f, 0.f};
@@ -525,7 +546,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
         f32x4 o;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) o[qq] = oi[qq] + gt * ox[qq];
-        if (t < L && e4 < dv) st_out4<TIn>(gout + (t0 + t) * dv + e4, o);
+        st_out4_buf<TIn>(rs, (t * dv + e4) * K::ES, 0, o);
       });
     }
 
