@@ -67,7 +67,8 @@ struct GdnCfg {
   static constexpr int P_V = P_T;
   static constexpr int P_G = P_T + cmax(C * C * 4, C * LDV * ES);     // g [C], beta [C]
   static constexpr int P_BETA = P_G + C * 4;
-  static constexpr int P_LDS = P_BETA + C * 4;
+  static constexpr int P_GI = P_BETA + C * 4;                         // 1 / g [C]
+  static constexpr int P_LDS = P_GI + C * 4;
   // state-pass LDS: two input stages {q, k^, W, g} (producer waves fill one while the
   // consumer waves read the other), then the consumers' score tiles
   static constexpr int S_Q = 0;
@@ -174,6 +175,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   float *sT = reinterpret_cast<float *>(lds + K::P_T);
   float *sG = reinterpret_cast<float *>(lds + K::P_G);
   float *sBeta = reinterpret_cast<float *>(lds + K::P_BETA);
+  float *sGi = reinterpret_cast<float *>(lds + K::P_GI);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,22 +188,45 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   const TIn *gk = static_cast<const TIn *>(a.k) + (bh * T + t0) * DK;
   const TIn *gv = static_cast<const TIn *>(a.v) + (bh * T + t0) * dv;
 
-  // k^ and the decay
+  // Every input of the chunk is requested up front (k, the decay, beta and the first value
+  // slice), from clamped rows without a branch, so one memory round trip covers them;
+  // rows past the end are masked where the values are used.
+  uint32_t rv[K::NVV][4];
+  auto load_v = [&](int vs) {
+    constexpr int VPRV = XW / VE;
+#pragma unroll
+    for (int j = 0; j < K::NVV; ++j) {
+      const int vi = tid + 256 * j, r = vi / VPRV, c = (vi % VPRV) * VE;
+      const uint4 x = *reinterpret_cast<const uint4 *>(gv + (r < L ? r : L - 1) * dv + vs * XW + c);
+      rv[j][0] = x.x; rv[j][1] = x.y; rv[j][2] = x.z; rv[j][3] = x.w;
+    }
+  };
   {
     uint32_t rk[K::NVQ][4];
 #pragma unroll
     for (int j = 0; j < K::NVQ; ++j) {
       const int vi = tid + 256 * j, r = vi / K::VPRQ, c = (vi % K::VPRQ) * VE;
-      uint4 y = make_uint4(0, 0, 0, 0);
-      if (r < L) y = *reinterpret_cast<const uint4 *>(gk + r * DK + c);
+      const uint4 y = *reinterpret_cast<const uint4 *>(gk + (r < L ? r : L - 1) * DK + c);
       rk[j][0] = y.x; rk[j][1] = y.y; rk[j][2] = y.z; rk[j][3] = y.w;
+    }
+    float al = 1.f, be = 0.f;
+    if (wave == 0) {
+      const int64_t tl = bh * T + t0 + (lane < L ? lane : L - 1);
+      al = a.alpha[tl];
+      be = a.beta[tl];
+    }
+    load_v(0);
+#pragma unroll
+    for (int j = 0; j < K::NVQ; ++j) {
+      const int r = (tid + 256 * j) / K::VPRQ;
+      if (r >= L) rk[j][0] = rk[j][1] = rk[j][2] = rk[j][3] = 0u; // past the end: k = 0
     }
     gdn::stage_khat<TIn, DK>(rk, sK, tid);
     if (wave == 0) {
-      const float al = lane < L ? a.alpha[bh * T + t0 + lane] : 1.f; // past the end: 1, 0
-      const float be = lane < L ? a.beta[bh * T + t0 + lane] : 0.f;
-      sG[lane] = gdn::decay_scan(al, lane);
-      sBeta[lane] = be;
+      const float g = gdn::decay_scan(lane < L ? al : 1.f, lane); // past the end: alpha 1, beta 0
+      sG[lane] = g;
+      sGi[lane] = 1.f / g;
+      sBeta[lane] = lane < L ? be : 0.f;
     }
   }
   __syncthreads();
@@ -224,7 +249,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int j = 16 * jb + 4 * g + qq;
-          sA[t * C + j] = (j < t) ? bt / sG[j] * acc[qq] : 0.f;
+          sA[t * C + j] = (j < t) ? bt * sGi[j] * acc[qq] : 0.f;
         }
       }
     }
@@ -283,8 +308,11 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   }
   __syncthreads();
 
-  // W = Tg K^ (4 * NCB tiles over the 4 waves), straight to the workspace
-  TIn *gw = static_cast<TIn *>(a.w) + (bh * T + t0) * DK;
+  // W = Tg K^ (4 * NCB tiles over the 4 waves), straight to the workspace.  Tiles are
+  // formed transposed (W^T = K^^T Tg^T: the same fragments with the operands swapped), so
+  // a lane holds 4 adjacent columns of one row; buffer stores over the chunk's L rows drop
+  // the rows past the end without a branch.
+  const auto rs_w = make_rsrc(static_cast<TIn *>(a.w) + (bh * T + t0) * DK, L * DK * K::ES);
 #pragma unroll
   for (int ti = 0; ti < NCB; ++ti) {
     const int tile = wave * NCB + ti, tb = tile / NCB, cb = tile % NCB;
@@ -292,31 +320,27 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
     const TIn *ta = sTg + (16 * tb + li) * LDT + 4 * g;
 #pragma unroll
     for (int u = 0; u < NZU; ++u)
-      acc = mma(acc, ld_frag_at<TIn, true>(ta, u), ld_frag_t<TIn, true>(sK, LDK, 16 * cb, u, g, li));
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int t = 16 * tb + 4 * g + qq;
-      if (t < L) gw[t * DK + 16 * cb + li] = (TIn)acc[qq];
-    }
+      acc = mma(acc, ld_frag_t<TIn, true>(sK, LDK, 16 * cb, u, g, li), ld_frag_at<TIn, true>(ta, u));
+    // acc[qq] = W[t = 16 tb + li][c = 16 cb + 4g + qq]
+    st_out4_buf<TIn>(rs_w, ((16 * tb + li) * DK + 16 * cb + 4 * g) * K::ES, 0, acc);
   }
 
-  // U0 = Tb V, one 64-wide value slice at a time
-  float *gu = a.u0 + (bh * T + t0) * dv;
+  // U0 = Tb V, one 64-wide value slice at a time (the next slice's V loads while this one
+  // is multiplied); transposed tiles and buffer stores as for W
+  const auto rs_u = make_rsrc(a.u0 + (bh * T + t0) * dv, L * dv * 4);
   for (int vs = 0; vs < a.nvs; ++vs) {
+    if (vs > 0) __syncthreads(); // the previous slice's V tile is still being read
     {
-      uint32_t rv[K::NVV][4];
       constexpr int VPRV = XW / VE;
 #pragma unroll
       for (int j = 0; j < K::NVV; ++j) {
-        const int vi = tid + 256 * j, r = vi / VPRV, c = (vi % VPRV) * VE;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (r < L) x = *reinterpret_cast<const uint4 *>(gv + r * dv + vs * XW + c);
-        rv[j][0] = x.x; rv[j][1] = x.y; rv[j][2] = x.z; rv[j][3] = x.w;
+        const int r = (tid + 256 * j) / VPRV;
+        if (r >= L) rv[j][0] = rv[j][1] = rv[j][2] = rv[j][3] = 0u; // past the end: v = 0
       }
-      if (vs > 0) __syncthreads(); // the previous slice's V tile is still being read
       gdn::stage_raw<TIn, K::NVV, XW / VE, LDV>(rv, sV, tid);
     }
     __syncthreads();
+    if (vs + 1 < a.nvs) load_v(vs + 1);
     Frag<TIn> vf[NZU];
 #pragma unroll
     for (int u = 0; u < NZU; ++u) vf[u] = ld_frag_t<TIn, true>(sV, LDV, 16 * wave, u, g, li);
@@ -325,12 +349,9 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       const TIn *ta = sTb + (16 * tb + li) * LDT + 4 * g;
 #pragma unroll
-      for (int u = 0; u < NZU; ++u) acc = mma(acc, ld_frag_at<TIn, true>(ta, u), vf[u]);
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int t = 16 * tb + 4 * g + qq;
-        if (t < L) gu[t * dv + vs * XW + 16 * wave + li] = acc[qq];
-      }
+      for (int u = 0; u < NZU; ++u) acc = mma(acc, vf[u], ld_frag_at<TIn, true>(ta, u));
+      // acc[qq] = U0[t = 16 tb + li][e = vs 64 + 16 wave + 4g + qq]
+      st_out4_buf<float>(rs_u, ((16 * tb + li) * dv + vs * XW + 16 * wave + 4 * g) * 4, 0, acc);
     }
   }
 }
