@@ -75,7 +75,8 @@ struct GdnCfg {
   static constexpr int S_K = S_Q + C * LDK * ES;
   static constexpr int S_W = S_K + C * LDK * ES;
   static constexpr int S_G = S_W + C * LDK * ES;    // g [C]
-  static constexpr int S_STAGE = S_G + C * 4;
+  static constexpr int S_GI = S_G + C * 4;          // 1 / g [C]
+  static constexpr int S_STAGE = S_GI + C * 4;
   static constexpr int S_P = 2 * S_STAGE;           // masked scores, 16 tile images
   static constexpr int S_LDS = S_P + 16 * 256 * ES;
   static constexpr bool FITS = P_LDS <= kMaxLds && S_LDS <= kMaxLds;
@@ -130,8 +131,8 @@ __device__ __forceinline__ float decay_scan(float alpha, int lane) {
 // Masked score tiles P[t][j] = (g_t / g_j) q_t . k^_j (j <= t); the image of tile (tb, jb) is
 // row-major [t][j].  10 tiles over the 4 waves.
 template <typename TIn, int DK>
-__device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const float *sG, TIn *sP,
-                                       int wave, int g, int li) {
+__device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const float *sG,
+                                       const float *sGi, TIn *sP, int wave, int g, int li) {
   using K = GdnCfg<TIn, DK>;
   static_for<0, 16>([&](auto I) {
     constexpr int tb = I / 4, jb = I % 4;
@@ -150,7 +151,7 @@ __device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const float
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int j = 16 * jb + 4 * g + qq;
-          acc[qq] = (j <= t) ? gt / sG[j] * acc[qq] : 0.f;
+          acc[qq] = (j <= t) ? gt * sGi[j] * acc[qq] : 0.f;
         }
         st_ptile<TIn>(sP + I * 256 + li * 16 + 4 * g, acc);
       }
@@ -370,6 +371,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
   auto stage_k = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_K); };
   auto stage_w = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_W); };
   auto stage_g = [&](int s) { return reinterpret_cast<float *>(lds + s * K::S_STAGE + K::S_G); };
+  auto stage_gi = [&](int s) { return reinterpret_cast<float *>(lds + s * K::S_STAGE + K::S_GI); };
   TIn *sP = reinterpret_cast<TIn *>(lds + K::S_P);
 
   const int tid = threadIdx.x;
@@ -420,7 +422,11 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       gdn::stage_khat<TIn, DK>(rk, stage_k(s), ptid);
       gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rq, stage_q(s), ptid);
       gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rw, stage_w(s), ptid);
-      if (pwave == 0) stage_g(s)[lane] = gdn::decay_scan(ralpha, lane);
+      if (pwave == 0) {
+        const float gv = gdn::decay_scan(ralpha, lane);
+        stage_g(s)[lane] = gv;
+        stage_gi(s)[lane] = 1.f / gv; // the masks and scales multiply by it
+      }
     };
     if (nchunks > 0) {
       load(0);
@@ -495,6 +501,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const TIn *sK = stage_k(n & 1);
     const TIn *sW = stage_w(n & 1);
     const float *sG = stage_g(n & 1);
+    const float *sGi = stage_gi(n & 1);
     f32x4 U0[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -504,7 +511,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const float gL = sG[C - 1]; // = g[L-1]: rows past the end carry alpha = 1
 
     // ---- masked scores (shared by the consumer waves); U = U0 - W H (this wave's columns)
-    gdn::scores<TIn, DK>(sQ, sK, sG, sP, wave, g, li);
+    gdn::scores<TIn, DK>(sQ, sK, sG, sGi, sP, wave, g, li);
     Frag<TIn> hf[DK / KU];
 #pragma unroll
     for (int u = 0; u < DK / KU; ++u) {
@@ -525,7 +532,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
         const int t = 16 * tb + 4 * g + qq;
         const float uval = U0[tb][qq] - x[qq];
         uacc[tb][qq] = uval;
-        usacc[tb][qq] = uval * (gL / sG[t]);
+        usacc[tb][qq] = uval * (gL * sGi[t]);
       }
     }
     auto frag_of = [&](const f32x4 *tiles, int u) -> Frag<TIn> {
