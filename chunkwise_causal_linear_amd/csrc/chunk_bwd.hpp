@@ -787,7 +787,7 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
           const f32x4 lp = *reinterpret_cast<const f32x4 *>(sB + (li ? r - 1 : r) * GW + xc);
           f32x4 dg;
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) dg[qq] = (rr[rb][qq] * (li ? lp[qq] : 1.f)) / lc[qq];
+          for (int qq = 0; qq < 4; ++qq) dg[qq] = rr[rb][qq] * (li ? lp[qq] : 1.f) * rcp_f(lc[qq]);
           if (r < L) *reinterpret_cast<f32x4 *>(a.dgate + baseK + (t0 + r) * rsK + goff + xc) = dg;
         }
       }
