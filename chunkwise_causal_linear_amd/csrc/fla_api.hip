@@ -478,11 +478,12 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
   const int64_t nvs = dv / kSlice;
   const int64_t nch = (T + 63) / 64;
   if (nbh * nvs >= kMaxGrid || nbh * nch >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
-  // workspace: W = T diag(beta g) K^ per chunk (input type) and U0 = T diag(beta) V (fp32)
+  // workspace: W = T diag(beta g) K^ per token and Tb = T diag(beta) per chunk (C x C),
+  // both in the input type (W's size is a multiple of 128 bytes, so Tb stays aligned)
   const int64_t w_bytes = nbh * T * dk * (bf16 ? 2 : 4);
-  const int64_t u_bytes = nbh * T * dv * 4;
+  const int64_t tb_bytes = nbh * nch * 64 * 64 * (bf16 ? 2 : 4);
   char *ws = nullptr;
-  if (hipMallocAsync(reinterpret_cast<void **>(&ws), w_bytes + u_bytes, s) != hipSuccess)
+  if (hipMallocAsync(reinterpret_cast<void **>(&ws), w_bytes + tb_bytes, s) != hipSuccess)
     return FLA_ERR_DEVICE;
   GdnArgs a{};
   a.q = q; a.k = k; a.v = v;
@@ -495,7 +496,7 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
   a.nvs = (int)nvs;
   a.nch = (int)nch;
   a.w = ws;
-  a.u0 = reinterpret_cast<float *>(ws + w_bytes);
+  a.tb = ws + w_bytes;
   int rc = FLA_OK;
   a.nunits = (int)(nbh * nch);
   if (launch.prep(a, (unsigned)a.nunits, s) != hipSuccess) rc = FLA_ERR_DEVICE;

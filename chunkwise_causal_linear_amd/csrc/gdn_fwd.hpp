@@ -12,14 +12,15 @@
 //     U = U0 - W H,
 //     O = diag(g) Q H + (M (.) Q K^^T) U,        M_tj = g_t / g_j (j <= t),
 //     H <- g_L H + K^^T diag(g_L / g) U.
-// W and U0 do not depend on the state, so they are formed for every chunk at once by a
-// pre-pass (one workgroup per (b, h, chunk): K^ K^^T on MFMA gives A; the 16 x 16 diagonal
-// blocks of T are inverted by forward substitution, one wave each, and the off-diagonal
-// blocks follow block row by block row with fp32 MFMA; then W and U0 on MFMA, written to a
-// workspace: W in the input type, U0 in fp32).  The state pass streams the chunks, one
+// W and Tb = T diag(beta) do not depend on the state, so they are formed for every chunk at
+// once by a pre-pass (one workgroup per (b, h, chunk): K^ K^^T on MFMA gives A; the
+// 16 x 16 diagonal blocks of T are inverted by forward substitution, one wave each, and
+// the off-diagonal blocks follow block row by block row with fp32 MFMA; then W on MFMA),
+// written to a workspace in the input type.  The state pass streams the chunks, one
 // workgroup per (b, h, 64-wide slice of dv): four consumer waves keep the state columns
-// in MFMA accumulators and compute per chunk the masked scores, U = U0 - W H, the outputs
-// and the state update, while four producer waves stage the next chunk's q, k^ and W.
+// in MFMA accumulators and compute per chunk the masked scores, U = Tb V - W H, the
+// outputs and the state update, while four producer waves stage the next chunk's q, k^,
+// W, Tb and value slice.
 #pragma once
 
 #include "chunk_bwd.hpp" // shared MFMA / LDS fragment helpers
@@ -33,7 +34,7 @@ struct GdnArgs {
   float *fin;                // [B][H][dk][dv] or null
   void *out;                 // [B][H][T][dv]
   void *w;                   // workspace [B][H][T][dk], input type
-  float *u0;                 // workspace [B][H][T][dv], fp32
+  void *tb;                  // workspace [B][H][nch][C][C], input type: T diag(beta) per chunk
   int64_t T;
   int H, dv;
   int nvs;                   // 64-wide value slices
@@ -63,21 +64,24 @@ struct GdnCfg {
   static constexpr int P_A = P_K + C * LDK * ES;    // A, fp32 [C][C]; later Tb, Tg
   static constexpr int P_TB = P_A;
   static constexpr int P_TG = P_TB + C * LDT * ES;
-  static constexpr int P_T = P_A + cmax(C * C * 4, 2 * C * LDT * ES); // T, fp32; later V
-  static constexpr int P_V = P_T;
-  static constexpr int P_G = P_T + cmax(C * C * 4, C * LDV * ES);     // g [C], beta [C]
+  static constexpr int P_T = P_A + cmax(C * C * 4, 2 * C * LDT * ES); // T, fp32
+  static constexpr int P_G = P_T + C * C * 4;                         // g [C], beta [C]
   static constexpr int P_BETA = P_G + C * 4;
   static constexpr int P_GI = P_BETA + C * 4;                         // 1 / g [C]
   static constexpr int P_LDS = P_GI + C * 4;
-  // state-pass LDS: two input stages {q, k^, W, g} (producer waves fill one while the
-  // consumer waves read the other), then the consumers' score tiles
+  // state-pass LDS: two input stages {q, k^, W, g, 1/g} (producer waves fill one while the
+  // consumer waves read the other); one {Tb, V slice} buffer, which the consumers use
+  // before the chunk's first barrier and the producers refill after it; the score tiles
   static constexpr int S_Q = 0;
   static constexpr int S_K = S_Q + C * LDK * ES;
   static constexpr int S_W = S_K + C * LDK * ES;
   static constexpr int S_G = S_W + C * LDK * ES;    // g [C]
   static constexpr int S_GI = S_G + C * 4;          // 1 / g [C]
   static constexpr int S_STAGE = S_GI + C * 4;
-  static constexpr int S_P = 2 * S_STAGE;           // masked scores, 16 tile images
+  static constexpr int S_TB = 2 * S_STAGE;          // Tb [C][LDT]
+  static constexpr int S_V = S_TB + C * LDT * ES;   // V slice [C][LDV]
+  static constexpr int S_P = S_V + C * LDV * ES;    // masked scores, 16 tile images
+  static constexpr int NVT = C * C / VE / NT;       // 16-byte vectors per thread (Tb)
   static constexpr int S_LDS = S_P + 16 * 256 * ES;
   static constexpr bool FITS = P_LDS <= kMaxLds && S_LDS <= kMaxLds;
 };
@@ -161,7 +165,7 @@ __device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const float
 
 } // namespace gdn
 
-// ---- pre-pass: W and U0 of one chunk ---------------------------------------------------
+// ---- pre-pass: W and Tb of one chunk ---------------------------------------------------
 template <typename TIn, int DK>
 __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   using K = GdnCfg<TIn, DK>;
@@ -169,7 +173,6 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   constexpr int LDK = K::LDK, LDV = K::LDV, LDT = K::LDT;
   __shared__ __attribute__((aligned(16))) unsigned char lds[K::P_LDS];
   TIn *sK = reinterpret_cast<TIn *>(lds + K::P_K);
-  TIn *sV = reinterpret_cast<TIn *>(lds + K::P_V);
   TIn *sTb = reinterpret_cast<TIn *>(lds + K::P_TB);
   TIn *sTg = reinterpret_cast<TIn *>(lds + K::P_TG);
   float *sA = reinterpret_cast<float *>(lds + K::P_A);
@@ -184,24 +187,12 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   const int n = blockIdx.x % a.nch;
   const int64_t bh = blockIdx.x / a.nch;
   const int64_t T = a.T, t0 = (int64_t)n * C;
-  const int dv = a.dv;
   const int L = (int)((T - t0) < C ? (T - t0) : C);
   const TIn *gk = static_cast<const TIn *>(a.k) + (bh * T + t0) * DK;
-  const TIn *gv = static_cast<const TIn *>(a.v) + (bh * T + t0) * dv;
 
-  // Every input of the chunk is requested up front (k, the decay, beta and the first value
-  // slice), from clamped rows without a branch, so one memory round trip covers them;
-  // rows past the end are masked where the values are used.
-  uint32_t rv[K::NVV][4];
-  auto load_v = [&](int vs) {
-    constexpr int VPRV = XW / VE;
-#pragma unroll
-    for (int j = 0; j < K::NVV; ++j) {
-      const int vi = tid + 256 * j, r = vi / VPRV, c = (vi % VPRV) * VE;
-      const uint4 x = *reinterpret_cast<const uint4 *>(gv + (r < L ? r : L - 1) * dv + vs * XW + c);
-      rv[j][0] = x.x; rv[j][1] = x.y; rv[j][2] = x.z; rv[j][3] = x.w;
-    }
-  };
+  // Every input of the chunk (k, the decay, beta) is requested before the first wait, from
+  // clamped rows without a branch, so one memory round trip covers them; rows past the
+  // end are masked where the values are used.
   {
     uint32_t rk[K::NVQ][4];
 #pragma unroll
@@ -216,7 +207,6 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
       al = a.alpha[tl];
       be = a.beta[tl];
     }
-    load_v(0);
 #pragma unroll
     for (int j = 0; j < K::NVQ; ++j) {
       const int r = (tid + 256 * j) / K::VPRQ;
@@ -326,33 +316,15 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
     st_out4_buf<TIn>(rs_w, ((16 * tb + li) * DK + 16 * cb + 4 * g) * K::ES, 0, acc);
   }
 
-  // U0 = Tb V, one 64-wide value slice at a time (the next slice's V loads while this one
-  // is multiplied); transposed tiles and buffer stores as for W
-  const auto rs_u = make_rsrc(a.u0 + (bh * T + t0) * dv, L * dv * 4);
-  for (int vs = 0; vs < a.nvs; ++vs) {
-    if (vs > 0) __syncthreads(); // the previous slice's V tile is still being read
-    {
-      constexpr int VPRV = XW / VE;
+  // Tb to the workspace: the whole C x C tile (its rows past the end are zero: beta = 0
+  // there), 16-byte vectors
+  {
+    TIn *gtb = static_cast<TIn *>(a.tb) + (bh * a.nch + n) * C * C;
+    constexpr int VPR = C / VE;
 #pragma unroll
-      for (int j = 0; j < K::NVV; ++j) {
-        const int r = (tid + 256 * j) / VPRV;
-        if (r >= L) rv[j][0] = rv[j][1] = rv[j][2] = rv[j][3] = 0u; // past the end: v = 0
-      }
-      gdn::stage_raw<TIn, K::NVV, XW / VE, LDV>(rv, sV, tid);
-    }
-    __syncthreads();
-    if (vs + 1 < a.nvs) load_v(vs + 1);
-    Frag<TIn> vf[NZU];
-#pragma unroll
-    for (int u = 0; u < NZU; ++u) vf[u] = ld_frag_t<TIn, true>(sV, LDV, 16 * wave, u, g, li);
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const TIn *ta = sTb + (16 * tb + li) * LDT + 4 * g;
-#pragma unroll
-      for (int u = 0; u < NZU; ++u) acc = mma(acc, vf[u], ld_frag_at<TIn, true>(ta, u));
-      // acc[qq] = U0[t = 16 tb + li][e = vs 64 + 16 wave + 4g + qq]
-      st_out4_buf<float>(rs_u, ((16 * tb + li) * dv + vs * XW + 16 * wave + 4 * g) * 4, 0, acc);
+    for (int j = 0; j < K::NVT; ++j) {
+      const int vi = tid + 256 * j, r = vi / VPR, c = (vi % VPR) * VE;
+      *reinterpret_cast<uint4 *>(gtb + r * C + c) = *reinterpret_cast<const uint4 *>(sTb + r * LDT + c);
     }
   }
 }
@@ -372,6 +344,8 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
   auto stage_w = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_W); };
   auto stage_g = [&](int s) { return reinterpret_cast<float *>(lds + s * K::S_STAGE + K::S_G); };
   auto stage_gi = [&](int s) { return reinterpret_cast<float *>(lds + s * K::S_STAGE + K::S_GI); };
+  TIn *sTb = reinterpret_cast<TIn *>(lds + K::S_TB);
+  TIn *sV = reinterpret_cast<TIn *>(lds + K::S_V);
   TIn *sP = reinterpret_cast<TIn *>(lds + K::S_P);
 
   const int tid = threadIdx.x;
@@ -398,8 +372,44 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const TIn *gk = static_cast<const TIn *>(a.k) + bh * T * DK;
     const TIn *gw = static_cast<const TIn *>(a.w) + bh * T * DK;
     const float *galpha = a.alpha + bh * T;
+    const TIn *gtb = static_cast<const TIn *>(a.tb) + bh * nchunks * C * C;
+    const TIn *gv = static_cast<const TIn *>(a.v) + bh * T * dv + vs * XW;
     uint32_t rq[K::NVQ][4], rk[K::NVQ][4], rw[K::NVQ][4];
+    uint32_t rtb[K::NVT][4], rv[K::NVV][4];
     float ralpha = 1.f;
+    // Tb and the value slice of chunk n (rows past the end of the sequence read the last
+    // row and are zeroed when staged)
+    auto load_tv = [&](int n) {
+      const int L = chunk_len(n);
+      const int64_t t0 = (int64_t)n * C;
+#pragma unroll
+      for (int j = 0; j < K::NVT; ++j) {
+        const int vi = ptid + 256 * j, r = vi / (C / VE), c = (vi % (C / VE)) * VE;
+        const uint4 x = *reinterpret_cast<const uint4 *>(gtb + ((int64_t)n * C + r) * C + c);
+        rtb[j][0] = x.x; rtb[j][1] = x.y; rtb[j][2] = x.z; rtb[j][3] = x.w;
+      }
+#pragma unroll
+      for (int j = 0; j < K::NVV; ++j) {
+        const int vi = ptid + 256 * j, r = vi / (XW / VE), c = (vi % (XW / VE)) * VE;
+        const uint4 x = *reinterpret_cast<const uint4 *>(gv + (t0 + (r < L ? r : L - 1)) * dv + c);
+        rv[j][0] = x.x; rv[j][1] = x.y; rv[j][2] = x.z; rv[j][3] = x.w;
+      }
+    };
+    auto stage_tv = [&](int n) {
+      const int L = chunk_len(n);
+#pragma unroll
+      for (int j = 0; j < K::NVT; ++j) {
+        const int vi = ptid + 256 * j, r = vi / (C / VE), c = (vi % (C / VE)) * VE;
+        st_words_lds<4>(sTb + r * K::LDT + c, rtb[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < K::NVV; ++j) {
+        const int vi = ptid + 256 * j, r = vi / (XW / VE), c = (vi % (XW / VE)) * VE;
+        const uint32_t m = r < L ? ~0u : 0u;
+        const uint32_t w[4] = {rv[j][0] & m, rv[j][1] & m, rv[j][2] & m, rv[j][3] & m};
+        st_words_lds<4>(sV + r * LDV + c, w);
+      }
+    };
     auto load = [&](int n) {
       const int L = chunk_len(n);
       const int64_t t0 = (int64_t)n * C;
@@ -430,8 +440,13 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     };
     if (nchunks > 0) {
       load(0);
+      load_tv(0);
       stage(0);
-      if (nchunks > 1) load(1);
+      stage_tv(0);
+      if (nchunks > 1) {
+        load(1);
+        load_tv(1);
+      }
     }
     __syncthreads();
     for (int n = 0; n < nchunks; ++n) {
@@ -439,7 +454,11 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
         stage((n + 1) & 1);
         if (n + 2 < nchunks) load(n + 2);
       }
-      __syncthreads(); // consumers: scores and U of chunk n written
+      __syncthreads(); // consumers: scores and U of chunk n formed (Tb, V read)
+      if (n + 1 < nchunks) {
+        stage_tv(n + 1);
+        if (n + 2 < nchunks) load_tv(n + 2);
+      }
       __syncthreads(); // consumers: chunk n done; the next stage is complete
     }
     return;
@@ -447,23 +466,8 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
 
   // =========================== consumer waves ===========================
   const int e_lane = vs * XW + 16 * wave + li; // this lane's value column
-  const float *gu = a.u0 + bh * T * dv;
   TIn *gout = static_cast<TIn *>(a.out) + bh * T * dv;
 
-  // this lane's U0 entries of a chunk (rows 16 tb + 4g + q), prefetched one chunk ahead;
-  // rows past the end read the last row (no branch: a branch would make the compiler wait
-  // for the load) and are zeroed where they are used.  dv is a multiple of 64, so every
-  // lane's column is in range.
-  float ru[16];
-  auto load_u0 = [&](int n) {
-    const int L = chunk_len(n);
-    const int64_t t0 = (int64_t)n * C;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = 16 * (i >> 2) + 4 * g + (i & 3);
-      ru[i] = gu[(t0 + (t < L ? t : L - 1)) * dv + e_lane];
-    }
-  };
   // the output rows of a chunk: buffer stores over its L rows, so rows past the end are
   // dropped without a branch (with a branch the compiler cannot count the stores in
   // flight and waits for all of them before the next chunk's loads)
@@ -483,15 +487,6 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
   // counting in order, would also wait for the previous chunk's stores)
   __builtin_amdgcn_s_waitcnt(0);
 
-  if (nchunks > 0) {
-    load_u0(0);
-    // the loop's stores, to an empty range (dropped): the first iteration's wait for the
-    // prefetch then has the same pattern as the others
-    const auto rs = out_rsrc(0, 0);
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-      st_out4_buf<TIn>(rs, ((16 * tb + li) * dv + e4) * K::ES, 0, f32x4{0.f, 0.f, 0.f, 0.f});
-  }
   __syncthreads();
 
   for (int n = 0; n < nchunks; ++n) {
@@ -502,15 +497,9 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const TIn *sW = stage_w(n & 1);
     const float *sG = stage_g(n & 1);
     const float *sGi = stage_gi(n & 1);
-    f32x4 U0[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) U0[tb][qq] = (16 * tb + 4 * g + qq < L) ? ru[4 * tb + qq] : 0.f;
-    load_u0(n + 1 < nchunks ? n + 1 : n); // the last chunk reads its own rows again
     const float gL = sG[C - 1]; // = g[L-1]: rows past the end carry alpha = 1
 
-    // ---- masked scores (shared by the consumer waves); U = U0 - W H (this wave's columns)
+    // ---- masked scores (shared by the consumer waves); U = Tb V - W H (this wave's columns)
     gdn::scores<TIn, DK>(sQ, sK, sG, sGi, sP, wave, g, li);
     Frag<TIn> hf[DK / KU];
 #pragma unroll
@@ -521,8 +510,15 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     // U and U (.) g_L / g stay in accumulator tiles: two 16-row tiles are the MFMA operand
     // of a 32-row K unit (rows 32u + 4g + s and +16 of column li), so no LDS round trip
     f32x4 uacc[4], usacc[4];
+    Frag<TIn> vf[NZU]; // the value slice as the B operand of Tb V (K = the chunk's rows)
+#pragma unroll
+    for (int u = 0; u < NZU; ++u) vf[u] = ld_frag_t<TIn, true>(sV, LDV, 16 * wave, u, g, li);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
+      f32x4 u0 = {0.f, 0.f, 0.f, 0.f};
+      const TIn *ta = sTb + (16 * tb + li) * K::LDT + 4 * g;
+#pragma unroll
+      for (int u = 0; u < NZU; ++u) u0 = mma(u0, ld_frag_at<TIn, true>(ta, u), vf[u]);
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
       const TIn *wa = sW + (16 * tb + li) * LDK + 4 * g;
 #pragma unroll
@@ -530,7 +526,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int t = 16 * tb + 4 * g + qq;
-        const float uval = U0[tb][qq] - x[qq];
+        const float uval = u0[qq] - x[qq];
         uacc[tb][qq] = uval;
         usacc[tb][qq] = uval * (gL * sGi[t]);
       }
