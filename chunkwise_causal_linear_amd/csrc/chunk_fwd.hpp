@@ -78,6 +78,7 @@ struct ChunkArgs {
   int bthd;                // 1: q, k, v, out, gate in token-major [B][T][H][d] (or packed
                            //    [total][H][d] with cu_seqlens); 0: [B][H][T][d]
   const int64_t *cu_seqlens; // packed sequences: [B + 1] token offsets (bthd only), or null
+  const int *seq_order;    // packed sequences: unit order -> sequence (longest first), or null
 };
 
 template <typename TIn, int DK, int C, int DECAY, bool NORM>
@@ -590,7 +591,8 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
   const int unit = (rest / a.nvs) * 8 + xcd;
   if (unit >= a.nunits) return;
   const int seg = unit % a.nseg;
-  const int bh = unit / a.nseg;
+  int bh = unit / a.nseg;
+  if (a.seq_order) bh = a.seq_order[bh / a.H] * a.H + bh % a.H; // longest sequences first
   const int h = bh % a.H;
 
   // wave index through readfirstlane: the compiler then keeps everything derived from it

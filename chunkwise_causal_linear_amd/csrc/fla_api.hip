@@ -21,6 +21,8 @@ namespace {
 
 constexpr int kStepThreads = 256;
 constexpr int kScanThreads = 256;
+constexpr int kOrderThreads = 256;
+constexpr int64_t kOrderMax = 8192; // packed sequences ranked longest-first up to this many
 constexpr int64_t kMaxGrid = (int64_t)1 << 31;
 
 bool is_pow2_dim(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
@@ -118,6 +120,34 @@ __global__ void token_dgate_kernel(const float *tpart, const float *decay, float
   for (int p = 0; p < nparts; ++p) s += tpart[(h * nparts + p) * ntok + tok];
   const int64_t at = bthd ? tok * H + h : ((tok / T) * H + h) * T + tok % T;
   dgate[at] = s / decay[at];
+}
+
+// Longest-first order of packed sequences: order[r] is the sequence with the r-th most
+// chunks (ties by index), so a grid dispatched in unit order starts the longest sequences
+// first and the short ones fill in behind them.  One thread per sequence counts the
+// sequences ranked before it; lengths are clamped as the chunk kernel clamps them.
+__global__ void seq_order_kernel(const int64_t *cu, int n, int64_t T, int64_t chunk, int *order) {
+  __shared__ int64_t tile[kOrderThreads];
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  auto nch = [&](int b) -> int64_t {
+    int64_t s = cu[b], e = cu[b + 1];
+    s = s < 0 ? 0 : (s > T ? T : s);
+    e = e < s ? s : (e > T ? T : e);
+    return (e - s + chunk - 1) / chunk;
+  };
+  const int64_t mine = i < n ? nch(i) : 0;
+  int r = 0;
+  for (int j0 = 0; j0 < n; j0 += kOrderThreads) {
+    __syncthreads();
+    if (j0 + (int)threadIdx.x < n) tile[threadIdx.x] = nch(j0 + (int)threadIdx.x);
+    __syncthreads();
+    const int m = n - j0 < kOrderThreads ? n - j0 : kOrderThreads;
+    for (int j = 0; j < m; ++j) {
+      const int64_t l = tile[j];
+      r += (l > mine || (l == mine && j0 + j < i)) ? 1 : 0;
+    }
+  }
+  if (i < n) order[r] = i;
 }
 
 // dst[i] = src ? src[i] : 0 (state copy / zero fill).
@@ -298,6 +328,25 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
       }
       ini = tmp;
     }
+    // packed sequences: dispatch the longest first (the short ones fill in behind them)
+    int *order = nullptr;
+    if (cu_seqlens && B >= 2 && B <= kOrderMax) {
+      if (hipMallocAsync(reinterpret_cast<void **>(&order), B * sizeof(int), s) != hipSuccess) {
+        if (tmp) (void)hipFreeAsync(tmp, s);
+        return FLA_ERR_DEVICE;
+      }
+      int n_i = (int)B;
+      int64_t T_v = T, chunk_v = chunk;
+      void *oargs[] = {&cu_seqlens, &n_i, &T_v, &chunk_v, &order};
+      if (hipLaunchKernel(reinterpret_cast<const void *>(&seq_order_kernel),
+                          dim3(blocks_for(B, kOrderThreads)), dim3(kOrderThreads), oargs, 0, s) !=
+          hipSuccess) {
+        (void)hipFreeAsync(order, s);
+        if (tmp) (void)hipFreeAsync(tmp, s);
+        return FLA_ERR_DEVICE;
+      }
+    }
+    a.seq_order = order;
     a.init = ini;
     a.init_bh_stride = dk * ncol;
     a.init_seg_stride = 0;
@@ -307,6 +356,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
     a.seg_decay = nullptr;
     a.state_only = 0;
     rc = launch(a, (unsigned)grid, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
+    if (order && hipFreeAsync(order, s) != hipSuccess) rc = FLA_ERR_DEVICE;
     if (tmp && hipFreeAsync(tmp, s) != hipSuccess) rc = FLA_ERR_DEVICE;
     return rc;
   }

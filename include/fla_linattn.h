@@ -117,7 +117,10 @@ int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
  *                  gives wrong results, never an out-of-range access.
  *   init_state, final_state: [n_seqs][H][dk][dv + n] fp32 (one state per sequence), or NULL.
  *   Other arguments as fla_linattn_fwd (B = n_seqs, T = total_T).  One streaming workgroup
- *   per (sequence, head, 64-wide value slice); sequences are independent.
+ *   per (sequence, head, 64-wide value slice); sequences are independent.  For 2 to 8192
+ *   sequences a small kernel first ranks them by chunk count (a stream-ordered buffer of
+ *   n_seqs*4 bytes) so the workgroups of the longest sequences are dispatched first; the
+ *   order changes no result.
  */
 int fla_linattn_fwd_varlen(const void *q, const void *k, const void *v, const float *gate_or_gamma,
                            const float *init_state, void *out, float *final_state,
