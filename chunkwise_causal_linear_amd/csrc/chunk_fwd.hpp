@@ -793,7 +793,6 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       // the row groups above it (inclusive shuffle scan across lanes rg*LPR + cgl)
       // (token gate: one column, the same for every key)
       float bc[K::GATED ? K::RPT : 1][K::GS];
-      float rb[K::GATED ? K::RPT : 1][K::GS]; // 1 / b
       if constexpr (K::GATED) {
         if (L < C) {
 #pragma unroll
@@ -833,11 +832,6 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
           for (int r = 0; r < K::RPT; ++r) bc[r][c] *= ex;
           dprod[c] *= tot[c];
-          // one reciprocal per column: 1/b_r = (1/b_last) * prod_{s>r} alpha_s
-          rb[K::RPT - 1][c] = rcp_f(bc[K::RPT - 1][c]);
-#pragma unroll
-          for (int r = K::RPT - 2; r >= 0; --r)
-            rb[r][c] = rb[r + 1][c] * __uint_as_float(s.a[r + 1][c]);
         }
         if (ld_on && rg == 0) {
           float totg[K::G];
@@ -875,8 +869,9 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
               qq = row < L ? qq : 0.f;
             }
             if constexpr (K::GATED) {
+              // 1 / b formed here, row by row, so no second array of reciprocals stays live
               qq *= bc[r][K::GS == 1 ? 0 : c];
-              kk *= rb[r][K::GS == 1 ? 0 : c];
+              kk *= rcp_f(bc[r][K::GS == 1 ? 0 : c]);
             }
             kv[c] = kk;
             qv[c] = qq;
