@@ -61,11 +61,10 @@ struct GdnCfg {
   // slices once Tb and Tg are formed, which fits three workgroups per CU (bf16, dk 128)
   static constexpr int cmax(int x, int y) { return x > y ? x : y; }
   static constexpr int P_K = 0;
-  static constexpr int P_A = P_K + C * LDK * ES;    // A, fp32 [C][C]; later Tb, Tg
-  static constexpr int P_TB = P_A;
-  static constexpr int P_TG = P_TB + C * LDT * ES;
-  static constexpr int P_T = P_A + cmax(C * C * 4, 2 * C * LDT * ES); // T, fp32
-  static constexpr int P_G = P_T + C * C * 4;                         // g [C], beta [C]
+  // A, fp32 [C][C], replaced block by block by T = (I + A)^-1; Tb and Tg are formed from
+  // T in registers where they are used, so four workgroups fit a CU
+  static constexpr int P_A = P_K + C * LDK * ES;
+  static constexpr int P_G = P_A + C * C * 4;                         // g [C], beta [C]
   static constexpr int P_BETA = P_G + C * 4;
   static constexpr int P_GI = P_BETA + C * 4;                         // 1 / g [C]
   static constexpr int P_LDS = P_GI + C * 4;
@@ -170,13 +169,11 @@ template <typename TIn, int DK>
 __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   using K = GdnCfg<TIn, DK>;
   constexpr int C = K::C, XW = K::XW, VE = K::VE, KU = K::KU, NCB = K::NCB, NZU = K::NZU;
-  constexpr int LDK = K::LDK, LDV = K::LDV, LDT = K::LDT;
+  constexpr int LDK = K::LDK;
   __shared__ __attribute__((aligned(16))) unsigned char lds[K::P_LDS];
   TIn *sK = reinterpret_cast<TIn *>(lds + K::P_K);
-  TIn *sTb = reinterpret_cast<TIn *>(lds + K::P_TB);
-  TIn *sTg = reinterpret_cast<TIn *>(lds + K::P_TG);
   float *sA = reinterpret_cast<float *>(lds + K::P_A);
-  float *sT = reinterpret_cast<float *>(lds + K::P_T);
+  float *sT = sA; // T overwrites A: each block of A is dead once its block of T is known
   float *sG = reinterpret_cast<float *>(lds + K::P_G);
   float *sBeta = reinterpret_cast<float *>(lds + K::P_BETA);
   float *sGi = reinterpret_cast<float *>(lds + K::P_GI);
@@ -248,7 +245,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   __syncthreads();
 
   // diagonal blocks of T = (I + A)^-1 by forward substitution: lanes 0..15 of wave w
-  // invert block w, one column each
+  // invert block w, one column each (all of the block's reads precede its writes: one wave)
   if (li == lane) {
     const int base = 16 * wave;
     float col[16];
@@ -265,9 +262,12 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   __syncthreads();
 
   // off-diagonal blocks, block row by block row: T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj),
-  // wave j computes block (i, j)
+  // wave j computes block (i, j); block (i, j) of A is read by the waves j' <= j of the
+  // same row, so every result waits in registers for the row's barrier before it replaces
+  // its block of A
   static_for<1, 4>([&](auto IB) {
     constexpr int ib = IB;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
     if (wave < ib) {
       const int jb = wave;
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -280,43 +280,63 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
       }
       // x[qq] = X[row 4g + qq][col li]: a B operand with k = 4g + qq
       const f32x4 ft = *reinterpret_cast<const f32x4 *>(sT + (16 * ib + li) * C + 16 * ib + 4 * g);
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
       y = mma(y, ft, x);
+    }
+    __syncthreads();
+    if (wave < ib) {
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) sT[(16 * ib + 4 * g + qq) * C + 16 * jb + li] = -y[qq];
+      for (int qq = 0; qq < 4; ++qq) sT[(16 * ib + 4 * g + qq) * C + 16 * wave + li] = -y[qq];
     }
     __syncthreads();
   });
 
-  // Tb = T diag(beta), Tg = T diag(beta g) in the MFMA input type
+  // Tb = T diag(beta), Tg = T diag(beta g) in the MFMA input type, formed from T where
+  // they are used: element (t, j) = (T_tj beta_j) [g_j], rounded once; T's upper triangle
+  // (never written) is masked by j <= t
+  auto t_scaled4 = [&](int t, int j0, bool with_g) -> f32x4 {
+    const f32x4 tv = *reinterpret_cast<const f32x4 *>(sT + t * C + j0);
+    const f32x4 bv = *reinterpret_cast<const f32x4 *>(sBeta + j0);
+    const f32x4 gv = *reinterpret_cast<const f32x4 *>(sG + j0);
+    f32x4 r;
 #pragma unroll
-  for (int i = 0; i < C * C / 256; ++i) {
-    const int idx = tid + 256 * i, t = idx / C, j = idx % C;
-    const float tv = (j <= t) ? sT[t * C + j] : 0.f;
-    const float bj = sBeta[j];
-    sTb[t * LDT + j] = (TIn)(tv * bj);
-    sTg[t * LDT + j] = (TIn)(tv * bj * sG[j]);
-  }
-  __syncthreads();
+    for (int s = 0; s < 4; ++s) {
+      const float v = (j0 + s <= t) ? tv[s] : 0.f;
+      r[s] = with_g ? v * bv[s] * gv[s] : v * bv[s];
+    }
+    return r;
+  };
 
   // W = Tg K^ (4 * NCB tiles over the 4 waves), straight to the workspace.  Tiles are
   // formed transposed (W^T = K^^T Tg^T: the same fragments with the operands swapped), so
   // a lane holds 4 adjacent columns of one row; buffer stores over the chunk's L rows drop
   // the rows past the end without a branch.
   const auto rs_w = make_rsrc(static_cast<TIn *>(a.w) + (bh * T + t0) * DK, L * DK * K::ES);
+  // wave w forms row block w of W: its Tg fragments (rows 16 w + li, the split K order of
+  // the chunk's rows) serve all NCB column tiles
+  const int tb = wave;
+  Frag<TIn> tgf[NZU];
 #pragma unroll
-  for (int ti = 0; ti < NCB; ++ti) {
-    const int tile = wave * NCB + ti, tb = tile / NCB, cb = tile % NCB;
+  for (int u = 0; u < NZU; ++u) {
+    if constexpr (sizeof(TIn) == 2) {
+      const f32x4 lo = t_scaled4(16 * tb + li, 32 * u + 4 * g, true);
+      const f32x4 hi = t_scaled4(16 * tb + li, 32 * u + 16 + 4 * g, true);
+      tgf[u] = bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                      (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+    } else {
+      tgf[u] = t_scaled4(16 * tb + li, 16 * u + 4 * g, true);
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const TIn *ta = sTg + (16 * tb + li) * LDT + 4 * g;
 #pragma unroll
     for (int u = 0; u < NZU; ++u)
-      acc = mma(acc, ld_frag_t<TIn, true>(sK, LDK, 16 * cb, u, g, li), ld_frag_at<TIn, true>(ta, u));
+      acc = mma(acc, ld_frag_t<TIn, true>(sK, LDK, 16 * cb, u, g, li), tgf[u]);
     // acc[qq] = W[t = 16 tb + li][c = 16 cb + 4g + qq]
     st_out4_buf<TIn>(rs_w, ((16 * tb + li) * DK + 16 * cb + 4 * g) * K::ES, 0, acc);
   }
 
-  // Tb to the workspace: the whole C x C tile (its rows past the end are zero: beta = 0
+  // Tb to the workspace: the whole C x C tile (its columns past the end are zero: beta = 0
   // there), 16-byte vectors
   {
     TIn *gtb = static_cast<TIn *>(a.tb) + (bh * a.nch + n) * C * C;
@@ -324,7 +344,14 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
 #pragma unroll
     for (int j = 0; j < K::NVT; ++j) {
       const int vi = tid + 256 * j, r = vi / VPR, c = (vi % VPR) * VE;
-      *reinterpret_cast<uint4 *>(gtb + r * C + c) = *reinterpret_cast<const uint4 *>(sTb + r * LDT + c);
+      if constexpr (sizeof(TIn) == 2) {
+        const f32x4 lo = t_scaled4(r, c, false), hi = t_scaled4(r, c + 4, false);
+        const bf16x8 v = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                          (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+        *reinterpret_cast<bf16x8 *>(gtb + r * C + c) = v;
+      } else {
+        *reinterpret_cast<f32x4 *>(gtb + r * C + c) = t_scaled4(r, c, false);
+      }
     }
   }
 }
