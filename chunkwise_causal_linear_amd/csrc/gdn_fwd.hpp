@@ -401,92 +401,118 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const float *galpha = a.alpha + bh * T;
     const TIn *gtb = static_cast<const TIn *>(a.tb) + bh * nchunks * C * C;
     const TIn *gv = static_cast<const TIn *>(a.v) + bh * T * dv + vs * XW;
-    uint32_t rq[K::NVQ][4], rk[K::NVQ][4], rw[K::NVQ][4];
-    uint32_t rtb[K::NVT][4], rv[K::NVV][4];
-    float ralpha = 1.f;
-    // Tb and the value slice of chunk n (rows past the end of the sequence read the last
-    // row and are zeroed when staged)
-    auto load_tv = [&](int n) {
+    // Two register sets of one chunk each: the loads of chunk n + 3 go out while chunk
+    // n + 2's are still in flight and chunk n + 1 is staged.  Every load is unconditional
+    // (the chunk index and its rows are clamped into the sequence), so the compiler's wait
+    // counts stay exact across the loop; rows past a chunk's end are masked when staged.
+    // Staging one chunk past the end writes a buffer no consumer reads again.
+    uint32_t rq[2][K::NVQ][4], rk[2][K::NVQ][4], rw[2][K::NVQ][4];
+    uint32_t rtb[2][K::NVT][4], rv[2][K::NVV][4];
+    float ralpha[2] = {1.f, 1.f};
+    auto clamp_n = [&](int n) { return n < nchunks ? n : nchunks - 1; };
+    // Tb and the value slice of chunk n
+    auto load_tv = [&](auto S, int n) {
+      constexpr int s = decltype(S)::value;
+      n = clamp_n(n);
       const int L = chunk_len(n);
       const int64_t t0 = (int64_t)n * C;
 #pragma unroll
       for (int j = 0; j < K::NVT; ++j) {
         const int vi = ptid + 256 * j, r = vi / (C / VE), c = (vi % (C / VE)) * VE;
         const uint4 x = *reinterpret_cast<const uint4 *>(gtb + ((int64_t)n * C + r) * C + c);
-        rtb[j][0] = x.x; rtb[j][1] = x.y; rtb[j][2] = x.z; rtb[j][3] = x.w;
+        rtb[s][j][0] = x.x; rtb[s][j][1] = x.y; rtb[s][j][2] = x.z; rtb[s][j][3] = x.w;
       }
 #pragma unroll
       for (int j = 0; j < K::NVV; ++j) {
         const int vi = ptid + 256 * j, r = vi / (XW / VE), c = (vi % (XW / VE)) * VE;
         const uint4 x = *reinterpret_cast<const uint4 *>(gv + (t0 + (r < L ? r : L - 1)) * dv + c);
-        rv[j][0] = x.x; rv[j][1] = x.y; rv[j][2] = x.z; rv[j][3] = x.w;
+        rv[s][j][0] = x.x; rv[s][j][1] = x.y; rv[s][j][2] = x.z; rv[s][j][3] = x.w;
       }
     };
-    auto stage_tv = [&](int n) {
-      const int L = chunk_len(n);
+    auto stage_tv = [&](auto S, int n) {
+      constexpr int s = decltype(S)::value;
+      const int L = chunk_len(clamp_n(n));
 #pragma unroll
       for (int j = 0; j < K::NVT; ++j) {
         const int vi = ptid + 256 * j, r = vi / (C / VE), c = (vi % (C / VE)) * VE;
-        st_words_lds<4>(sTb + r * K::LDT + c, rtb[j]);
+        st_words_lds<4>(sTb + r * K::LDT + c, rtb[s][j]);
       }
 #pragma unroll
       for (int j = 0; j < K::NVV; ++j) {
         const int vi = ptid + 256 * j, r = vi / (XW / VE), c = (vi % (XW / VE)) * VE;
         const uint32_t m = r < L ? ~0u : 0u;
-        const uint32_t w[4] = {rv[j][0] & m, rv[j][1] & m, rv[j][2] & m, rv[j][3] & m};
+        const uint32_t w[4] = {rv[s][j][0] & m, rv[s][j][1] & m, rv[s][j][2] & m, rv[s][j][3] & m};
         st_words_lds<4>(sV + r * LDV + c, w);
       }
     };
-    auto load = [&](int n) {
+    // q, k, W rows and the decay of chunk n
+    auto load = [&](auto S, int n) {
+      constexpr int s = decltype(S)::value;
+      n = clamp_n(n);
       const int L = chunk_len(n);
       const int64_t t0 = (int64_t)n * C;
 #pragma unroll
       for (int j = 0; j < K::NVQ; ++j) {
         const int vi = ptid + 256 * j, r = vi / K::VPRQ, c = (vi % K::VPRQ) * VE;
-        uint4 x = make_uint4(0, 0, 0, 0), y = x, z = x;
-        if (r < L) {
-          x = *reinterpret_cast<const uint4 *>(gq + (t0 + r) * DK + c);
-          y = *reinterpret_cast<const uint4 *>(gk + (t0 + r) * DK + c);
-          z = *reinterpret_cast<const uint4 *>(gw + (t0 + r) * DK + c);
+        const int64_t row = t0 + (r < L ? r : L - 1);
+        const uint4 x = *reinterpret_cast<const uint4 *>(gq + row * DK + c);
+        const uint4 y = *reinterpret_cast<const uint4 *>(gk + row * DK + c);
+        const uint4 z = *reinterpret_cast<const uint4 *>(gw + row * DK + c);
+        rq[s][j][0] = x.x; rq[s][j][1] = x.y; rq[s][j][2] = x.z; rq[s][j][3] = x.w;
+        rk[s][j][0] = y.x; rk[s][j][1] = y.y; rk[s][j][2] = y.z; rk[s][j][3] = y.w;
+        rw[s][j][0] = z.x; rw[s][j][1] = z.y; rw[s][j][2] = z.z; rw[s][j][3] = z.w;
+      }
+      ralpha[s] = galpha[t0 + (ptid < L ? ptid : L - 1)];
+    };
+    // rows past the chunk's end: q = k = W = 0 and alpha = 1 (no decay)
+    auto stage = [&](auto S, int n) {
+      constexpr int s = decltype(S)::value;
+      const int L = chunk_len(clamp_n(n));
+#pragma unroll
+      for (int j = 0; j < K::NVQ; ++j) {
+        const uint32_t m = (ptid + 256 * j) / K::VPRQ < L ? ~0u : 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          rq[s][j][e] &= m;
+          rk[s][j][e] &= m;
+          rw[s][j][e] &= m;
         }
-        rq[j][0] = x.x; rq[j][1] = x.y; rq[j][2] = x.z; rq[j][3] = x.w;
-        rk[j][0] = y.x; rk[j][1] = y.y; rk[j][2] = y.z; rk[j][3] = y.w;
-        rw[j][0] = z.x; rw[j][1] = z.y; rw[j][2] = z.z; rw[j][3] = z.w;
       }
-      ralpha = (ptid < L) ? galpha[t0 + ptid] : 1.f; // past the end: no decay
-    };
-    auto stage = [&](int s) {
-      gdn::stage_khat<TIn, DK>(rk, stage_k(s), ptid);
-      gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rq, stage_q(s), ptid);
-      gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rw, stage_w(s), ptid);
+      const int buf = n & 1;
+      gdn::stage_khat<TIn, DK>(rk[s], stage_k(buf), ptid);
+      gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rq[s], stage_q(buf), ptid);
+      gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rw[s], stage_w(buf), ptid);
       if (pwave == 0) {
-        const float gv = gdn::decay_scan(ralpha, lane);
-        stage_g(s)[lane] = gv;
-        stage_gi(s)[lane] = 1.f / gv; // the masks and scales multiply by it
+        const float gv = gdn::decay_scan(ptid < L ? ralpha[s] : 1.f, lane);
+        stage_g(buf)[lane] = gv;
+        stage_gi(buf)[lane] = 1.f / gv; // the masks and scales multiply by it
       }
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
     if (nchunks > 0) {
-      load(0);
-      load_tv(0);
-      stage(0);
-      stage_tv(0);
-      if (nchunks > 1) {
-        load(1);
-        load_tv(1);
-      }
+      load(I0{}, 0);
+      load_tv(I0{}, 0);
+      load(I1{}, 1);
+      load_tv(I1{}, 1);
+      stage(I0{}, 0);
+      stage_tv(I0{}, 0);
+      load(I0{}, 2);
+      load_tv(I0{}, 2);
     }
     __syncthreads();
-    for (int n = 0; n < nchunks; ++n) {
-      if (n + 1 < nchunks) {
-        stage((n + 1) & 1);
-        if (n + 2 < nchunks) load(n + 2);
-      }
+    // chunk n + 1 sits in set (n + 1) & 1; its loads went out two chunks earlier
+    auto step = [&](auto S, int n) {
+      stage(S, n + 1);
+      load(S, n + 3);
       __syncthreads(); // consumers: scores and U of chunk n formed (Tb, V read)
-      if (n + 1 < nchunks) {
-        stage_tv(n + 1);
-        if (n + 2 < nchunks) load_tv(n + 2);
-      }
+      stage_tv(S, n + 1);
+      load_tv(S, n + 3);
       __syncthreads(); // consumers: chunk n done; the next stage is complete
+    };
+    for (int n = 0; n < nchunks; n += 2) {
+      step(I1{}, n);
+      if (n + 1 < nchunks) step(I0{}, n + 1);
     }
     return;
   }
