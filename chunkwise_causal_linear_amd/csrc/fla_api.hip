@@ -530,10 +530,9 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
   if (nbh * nvs >= kMaxGrid || nbh * nch >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
   // workspace: W = T diag(beta g) K^ per token and Tb = T diag(beta) per chunk (C x C),
   // both in the input type (W's size is a multiple of 128 bytes, so Tb stays aligned)
-  const int64_t w_bytes = nbh * T * dk * (bf16 ? 2 : 4);
-  const int64_t tb_bytes = nbh * nch * 64 * 64 * (bf16 ? 2 : 4);
+  const int64_t tb_bytes = nbh * nch * 64 * 64 * (bf16 ? 2 : 4); // Tb, and as much for Tg
   char *ws = nullptr;
-  if (hipMallocAsync(reinterpret_cast<void **>(&ws), w_bytes + tb_bytes, s) != hipSuccess)
+  if (hipMallocAsync(reinterpret_cast<void **>(&ws), 2 * tb_bytes, s) != hipSuccess)
     return FLA_ERR_DEVICE;
   GdnArgs a{};
   a.q = q; a.k = k; a.v = v;
@@ -545,8 +544,8 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
   a.H = (int)H; a.dv = (int)dv;
   a.nvs = (int)nvs;
   a.nch = (int)nch;
-  a.w = ws;
-  a.tb = ws + w_bytes;
+  a.tg = ws;
+  a.tb = ws + tb_bytes;
   int rc = FLA_OK;
   a.nunits = (int)(nbh * nch);
   if (launch.prep(a, (unsigned)a.nunits, s) != hipSuccess) rc = FLA_ERR_DEVICE;

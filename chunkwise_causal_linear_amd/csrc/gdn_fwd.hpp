@@ -7,20 +7,18 @@
 // u_t = beta_t (v_t - alpha_t h_{t-1}^T k^_t), one chunk of L rows starting from state H,
 // with g the inclusive product of alpha inside the chunk, satisfies
 //     (I + A) U = diag(beta) V - diag(beta g) K^ H,   A_tj = beta_t (g_t / g_j) k^_t . k^_j (j < t),
-// so with T = (I + A)^-1 (unit lower triangular), W = T diag(beta g) K^ and
-// U0 = T diag(beta) V:
-//     U = U0 - W H,
+// so with T = (I + A)^-1 (unit lower triangular), Tb = T diag(beta) and Tg = T diag(beta g):
+//     U = Tb V - Tg (K^ H),
 //     O = diag(g) Q H + (M (.) Q K^^T) U,        M_tj = g_t / g_j (j <= t),
 //     H <- g_L H + K^^T diag(g_L / g) U.
-// W and Tb = T diag(beta) do not depend on the state, so they are formed for every chunk at
-// once by a pre-pass (one workgroup per (b, h, chunk): K^ K^^T on MFMA gives A; the
-// 16 x 16 diagonal blocks of T are inverted by forward substitution, one wave each, and
-// the off-diagonal blocks follow block row by block row with fp32 MFMA; then W on MFMA),
-// written to a workspace in the input type.  The state pass streams the chunks, one
-// workgroup per (b, h, 64-wide slice of dv): four consumer waves keep the state columns
-// in MFMA accumulators and compute per chunk the masked scores, U = Tb V - W H, the
-// outputs and the state update, while four producer waves stage the next chunk's q, k^,
-// W, Tb and value slice.
+// Tb and Tg do not depend on the state, so they are formed for every chunk at once by a
+// pre-pass (one workgroup per (b, h, chunk): K^ K^^T on MFMA gives A; the 16 x 16 diagonal
+// blocks of T are inverted by forward substitution, one wave each, and the off-diagonal
+// blocks follow block row by block row with fp32 MFMA), written to a workspace in the input
+// type.  The state pass streams the chunks, one workgroup per (b, h, 64-wide slice of dv):
+// four consumer waves keep the state columns in MFMA accumulators and compute per chunk
+// the masked scores, X = K^ H, U = Tb V - Tg X, the outputs and the state update, while
+// four producer waves stage the next chunk's q, k^, Tb, Tg and value slice.
 #pragma once
 
 #include "chunk_bwd.hpp" // shared MFMA / LDS fragment helpers
@@ -33,7 +31,7 @@ struct GdnArgs {
   const float *init;         // [B][H][dk][dv] or null
   float *fin;                // [B][H][dk][dv] or null
   void *out;                 // [B][H][T][dv]
-  void *w;                   // workspace [B][H][T][dk], input type
+  void *tg;                  // workspace [B][H][nch][C][C], input type: T diag(beta g) per chunk
   void *tb;                  // workspace [B][H][nch][C][C], input type: T diag(beta) per chunk
   int64_t T;
   int H, dv;
@@ -62,23 +60,23 @@ struct GdnCfg {
   static constexpr int cmax(int x, int y) { return x > y ? x : y; }
   static constexpr int P_K = 0;
   // A, fp32 [C][C], replaced block by block by T = (I + A)^-1; Tb and Tg are formed from
-  // T in registers where they are used, so four workgroups fit a CU
+  // T in registers as they are written out, so four workgroups fit a CU
   static constexpr int P_A = P_K + C * LDK * ES;
   static constexpr int P_G = P_A + C * C * 4;                         // g [C], beta [C]
   static constexpr int P_BETA = P_G + C * 4;
   static constexpr int P_GI = P_BETA + C * 4;                         // 1 / g [C]
   static constexpr int P_LDS = P_GI + C * 4;
-  // state-pass LDS: two input stages {q, k^, W, g, 1/g} (producer waves fill one while the
-  // consumer waves read the other); one {Tb, V slice} buffer, which the consumers use
+  // state-pass LDS: two input stages {q, k^, g, 1/g} (producer waves fill one while the
+  // consumer waves read the other); one {Tb, Tg, V slice} buffer, which the consumers use
   // before the chunk's first barrier and the producers refill after it; the score tiles
   static constexpr int S_Q = 0;
   static constexpr int S_K = S_Q + C * LDK * ES;
-  static constexpr int S_W = S_K + C * LDK * ES;
-  static constexpr int S_G = S_W + C * LDK * ES;    // g [C]
+  static constexpr int S_G = S_K + C * LDK * ES;    // g [C]
   static constexpr int S_GI = S_G + C * 4;          // 1 / g [C]
   static constexpr int S_STAGE = S_GI + C * 4;
   static constexpr int S_TB = 2 * S_STAGE;          // Tb [C][LDT]
-  static constexpr int S_V = S_TB + C * LDT * ES;   // V slice [C][LDV]
+  static constexpr int S_TG = S_TB + C * LDT * ES;  // Tg [C][LDT]
+  static constexpr int S_V = S_TG + C * LDT * ES;   // V slice [C][LDV]
   static constexpr int S_P = S_V + C * LDV * ES;    // masked scores, 16 tile images
   static constexpr int NVT = C * C / VE / NT;       // 16-byte vectors per thread (Tb)
   static constexpr int S_LDS = S_P + 16 * 256 * ES;
@@ -290,9 +288,10 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
     __syncthreads();
   });
 
-  // Tb = T diag(beta), Tg = T diag(beta g) in the MFMA input type, formed from T where
-  // they are used: element (t, j) = (T_tj beta_j) [g_j], rounded once; T's upper triangle
-  // (never written) is masked by j <= t
+  // Tb = T diag(beta) and Tg = T diag(beta g) to the workspace in the input type, formed
+  // from T in registers: element (t, j) = (T_tj beta_j) [g_j], rounded once; T's upper
+  // triangle (never written) is masked by j <= t.  Whole C x C tiles (their columns past
+  // the end are zero: beta = 0 there), 16-byte vectors.
   auto t_scaled4 = [&](int t, int j0, bool with_g) -> f32x4 {
     const f32x4 tv = *reinterpret_cast<const f32x4 *>(sT + t * C + j0);
     const f32x4 bv = *reinterpret_cast<const f32x4 *>(sBeta + j0);
@@ -305,53 +304,26 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
     }
     return r;
   };
-
-  // W = Tg K^ (4 * NCB tiles over the 4 waves), straight to the workspace.  Tiles are
-  // formed transposed (W^T = K^^T Tg^T: the same fragments with the operands swapped), so
-  // a lane holds 4 adjacent columns of one row; buffer stores over the chunk's L rows drop
-  // the rows past the end without a branch.
-  const auto rs_w = make_rsrc(static_cast<TIn *>(a.w) + (bh * T + t0) * DK, L * DK * K::ES);
-  // wave w forms row block w of W: its Tg fragments (rows 16 w + li, the split K order of
-  // the chunk's rows) serve all NCB column tiles
-  const int tb = wave;
-  Frag<TIn> tgf[NZU];
-#pragma unroll
-  for (int u = 0; u < NZU; ++u) {
+  auto put = [&](TIn *dst, int r, int c, bool with_g) {
     if constexpr (sizeof(TIn) == 2) {
-      const f32x4 lo = t_scaled4(16 * tb + li, 32 * u + 4 * g, true);
-      const f32x4 hi = t_scaled4(16 * tb + li, 32 * u + 16 + 4 * g, true);
-      tgf[u] = bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
-                      (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+      const f32x4 lo = t_scaled4(r, c, with_g), hi = t_scaled4(r, c + 4, with_g);
+      const bf16x8 v = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                        (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+      *reinterpret_cast<bf16x8 *>(dst + r * C + c) = v;
     } else {
-      tgf[u] = t_scaled4(16 * tb + li, 16 * u + 4 * g, true);
+      *reinterpret_cast<f32x4 *>(dst + r * C + c) = t_scaled4(r, c, with_g);
     }
-  }
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < NZU; ++u)
-      acc = mma(acc, ld_frag_t<TIn, true>(sK, LDK, 16 * cb, u, g, li), tgf[u]);
-    // acc[qq] = W[t = 16 tb + li][c = 16 cb + 4g + qq]
-    st_out4_buf<TIn>(rs_w, ((16 * tb + li) * DK + 16 * cb + 4 * g) * K::ES, 0, acc);
-  }
-
-  // Tb to the workspace: the whole C x C tile (its columns past the end are zero: beta = 0
-  // there), 16-byte vectors
+  };
   {
-    TIn *gtb = static_cast<TIn *>(a.tb) + (bh * a.nch + n) * C * C;
+    const int64_t off = (bh * a.nch + n) * C * C;
+    TIn *gtb = static_cast<TIn *>(a.tb) + off;
+    TIn *gtg = static_cast<TIn *>(a.tg) + off;
     constexpr int VPR = C / VE;
 #pragma unroll
     for (int j = 0; j < K::NVT; ++j) {
       const int vi = tid + 256 * j, r = vi / VPR, c = (vi % VPR) * VE;
-      if constexpr (sizeof(TIn) == 2) {
-        const f32x4 lo = t_scaled4(r, c, false), hi = t_scaled4(r, c + 4, false);
-        const bf16x8 v = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
-                          (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
-        *reinterpret_cast<bf16x8 *>(gtb + r * C + c) = v;
-      } else {
-        *reinterpret_cast<f32x4 *>(gtb + r * C + c) = t_scaled4(r, c, false);
-      }
+      put(gtb, r, c, false);
+      put(gtg, r, c, true);
     }
   }
 }
@@ -368,10 +340,10 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[K::S_LDS];
   auto stage_q = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_Q); };
   auto stage_k = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_K); };
-  auto stage_w = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_W); };
   auto stage_g = [&](int s) { return reinterpret_cast<float *>(lds + s * K::S_STAGE + K::S_G); };
   auto stage_gi = [&](int s) { return reinterpret_cast<float *>(lds + s * K::S_STAGE + K::S_GI); };
   TIn *sTb = reinterpret_cast<TIn *>(lds + K::S_TB);
+  TIn *sTg = reinterpret_cast<TIn *>(lds + K::S_TG);
   TIn *sV = reinterpret_cast<TIn *>(lds + K::S_V);
   TIn *sP = reinterpret_cast<TIn *>(lds + K::S_P);
 
@@ -397,20 +369,20 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const int ptid = tid - 256, pwave = wave - 4;
     const TIn *gq = static_cast<const TIn *>(a.q) + bh * T * DK;
     const TIn *gk = static_cast<const TIn *>(a.k) + bh * T * DK;
-    const TIn *gw = static_cast<const TIn *>(a.w) + bh * T * DK;
     const float *galpha = a.alpha + bh * T;
     const TIn *gtb = static_cast<const TIn *>(a.tb) + bh * nchunks * C * C;
+    const TIn *gtg = static_cast<const TIn *>(a.tg) + bh * nchunks * C * C;
     const TIn *gv = static_cast<const TIn *>(a.v) + bh * T * dv + vs * XW;
     // Two register sets of one chunk each: the loads of chunk n + 3 go out while chunk
     // n + 2's are still in flight and chunk n + 1 is staged.  Every load is unconditional
     // (the chunk index and its rows are clamped into the sequence), so the compiler's wait
     // counts stay exact across the loop; rows past a chunk's end are masked when staged.
     // Staging one chunk past the end writes a buffer no consumer reads again.
-    uint32_t rq[2][K::NVQ][4], rk[2][K::NVQ][4], rw[2][K::NVQ][4];
-    uint32_t rtb[2][K::NVT][4], rv[2][K::NVV][4];
+    uint32_t rq[2][K::NVQ][4], rk[2][K::NVQ][4];
+    uint32_t rtb[2][K::NVT][4], rtg[2][K::NVT][4], rv[2][K::NVV][4];
     float ralpha[2] = {1.f, 1.f};
     auto clamp_n = [&](int n) { return n < nchunks ? n : nchunks - 1; };
-    // Tb and the value slice of chunk n
+    // Tb, Tg and the value slice of chunk n
     auto load_tv = [&](auto S, int n) {
       constexpr int s = decltype(S)::value;
       n = clamp_n(n);
@@ -420,7 +392,9 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       for (int j = 0; j < K::NVT; ++j) {
         const int vi = ptid + 256 * j, r = vi / (C / VE), c = (vi % (C / VE)) * VE;
         const uint4 x = *reinterpret_cast<const uint4 *>(gtb + ((int64_t)n * C + r) * C + c);
+        const uint4 y = *reinterpret_cast<const uint4 *>(gtg + ((int64_t)n * C + r) * C + c);
         rtb[s][j][0] = x.x; rtb[s][j][1] = x.y; rtb[s][j][2] = x.z; rtb[s][j][3] = x.w;
+        rtg[s][j][0] = y.x; rtg[s][j][1] = y.y; rtg[s][j][2] = y.z; rtg[s][j][3] = y.w;
       }
 #pragma unroll
       for (int j = 0; j < K::NVV; ++j) {
@@ -436,6 +410,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       for (int j = 0; j < K::NVT; ++j) {
         const int vi = ptid + 256 * j, r = vi / (C / VE), c = (vi % (C / VE)) * VE;
         st_words_lds<4>(sTb + r * K::LDT + c, rtb[s][j]);
+        st_words_lds<4>(sTg + r * K::LDT + c, rtg[s][j]);
       }
 #pragma unroll
       for (int j = 0; j < K::NVV; ++j) {
@@ -445,7 +420,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
         st_words_lds<4>(sV + r * LDV + c, w);
       }
     };
-    // q, k, W rows and the decay of chunk n
+    // q, k rows and the decay of chunk n
     auto load = [&](auto S, int n) {
       constexpr int s = decltype(S)::value;
       n = clamp_n(n);
@@ -457,14 +432,12 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
         const int64_t row = t0 + (r < L ? r : L - 1);
         const uint4 x = *reinterpret_cast<const uint4 *>(gq + row * DK + c);
         const uint4 y = *reinterpret_cast<const uint4 *>(gk + row * DK + c);
-        const uint4 z = *reinterpret_cast<const uint4 *>(gw + row * DK + c);
         rq[s][j][0] = x.x; rq[s][j][1] = x.y; rq[s][j][2] = x.z; rq[s][j][3] = x.w;
         rk[s][j][0] = y.x; rk[s][j][1] = y.y; rk[s][j][2] = y.z; rk[s][j][3] = y.w;
-        rw[s][j][0] = z.x; rw[s][j][1] = z.y; rw[s][j][2] = z.z; rw[s][j][3] = z.w;
       }
       ralpha[s] = galpha[t0 + (ptid < L ? ptid : L - 1)];
     };
-    // rows past the chunk's end: q = k = W = 0 and alpha = 1 (no decay)
+    // rows past the chunk's end: q = k = 0 and alpha = 1 (no decay)
     auto stage = [&](auto S, int n) {
       constexpr int s = decltype(S)::value;
       const int L = chunk_len(clamp_n(n));
@@ -475,13 +448,11 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
         for (int e = 0; e < 4; ++e) {
           rq[s][j][e] &= m;
           rk[s][j][e] &= m;
-          rw[s][j][e] &= m;
         }
       }
       const int buf = n & 1;
       gdn::stage_khat<TIn, DK>(rk[s], stage_k(buf), ptid);
       gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rq[s], stage_q(buf), ptid);
-      gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rw[s], stage_w(buf), ptid);
       if (pwave == 0) {
         const float gv = gdn::decay_scan(ptid < L ? ralpha[s] : 1.f, lane);
         stage_g(buf)[lane] = gv;
@@ -505,7 +476,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     auto step = [&](auto S, int n) {
       stage(S, n + 1);
       load(S, n + 3);
-      __syncthreads(); // consumers: scores and U of chunk n formed (Tb, V read)
+      __syncthreads(); // consumers: scores and U of chunk n formed (Tb, Tg, V read)
       stage_tv(S, n + 1);
       load_tv(S, n + 3);
       __syncthreads(); // consumers: chunk n done; the next stage is complete
@@ -547,12 +518,12 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const int64_t t0 = (int64_t)n * C;
     const TIn *sQ = stage_q(n & 1);
     const TIn *sK = stage_k(n & 1);
-    const TIn *sW = stage_w(n & 1);
     const float *sG = stage_g(n & 1);
     const float *sGi = stage_gi(n & 1);
     const float gL = sG[C - 1]; // = g[L-1]: rows past the end carry alpha = 1
 
-    // ---- masked scores (shared by the consumer waves); U = Tb V - W H (this wave's columns)
+    // ---- masked scores (shared by the consumer waves); U = Tb V - Tg (K^ H) (this wave's
+    // columns)
     gdn::scores<TIn, DK>(sQ, sK, sG, sGi, sP, wave, g, li);
     Frag<TIn> hf[DK / KU];
 #pragma unroll
@@ -560,8 +531,25 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       if constexpr (sizeof(TIn) == 2) hf[u] = acc_frag_bf(Hs[2 * u], Hs[2 * u + 1]);
       else hf[u] = Hs[u];
     }
-    // U and U (.) g_L / g stay in accumulator tiles: two 16-row tiles are the MFMA operand
-    // of a 32-row K unit (rows 32u + 4g + s and +16 of column li), so no LDS round trip
+    // X, U and U (.) g_L / g stay in accumulator tiles: two 16-row tiles are the MFMA
+    // operand of a 32-row K unit (rows 32u + 4g + s and +16 of column li), so no LDS round
+    // trip
+    auto frag_of = [&](const f32x4 *tiles, int u) -> Frag<TIn> {
+      if constexpr (sizeof(TIn) == 2) return acc_frag_bf(tiles[2 * u], tiles[2 * u + 1]);
+      else return tiles[u];
+    };
+    f32x4 xacc[4]; // X = K^ H
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      const TIn *ka = sK + (16 * tb + li) * LDK + 4 * g;
+#pragma unroll
+      for (int u = 0; u < DK / KU; ++u) x = mma(x, ld_frag_at<TIn, true>(ka, u), hf[u]);
+      xacc[tb] = x;
+    }
+    Frag<TIn> xf[NZU];
+#pragma unroll
+    for (int u = 0; u < NZU; ++u) xf[u] = frag_of(xacc, u);
     f32x4 uacc[4], usacc[4];
     Frag<TIn> vf[NZU]; // the value slice as the B operand of Tb V (K = the chunk's rows)
 #pragma unroll
@@ -573,9 +561,9 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
 #pragma unroll
       for (int u = 0; u < NZU; ++u) u0 = mma(u0, ld_frag_at<TIn, true>(ta, u), vf[u]);
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      const TIn *wa = sW + (16 * tb + li) * LDK + 4 * g;
+      const TIn *ga = sTg + (16 * tb + li) * K::LDT + 4 * g;
 #pragma unroll
-      for (int u = 0; u < DK / KU; ++u) x = mma(x, ld_frag_at<TIn, true>(wa, u), hf[u]);
+      for (int u = 0; u < NZU; ++u) x = mma(x, ld_frag_at<TIn, true>(ga, u), xf[u]);
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int t = 16 * tb + 4 * g + qq;
@@ -584,10 +572,6 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
         usacc[tb][qq] = uval * (gL * sGi[t]);
       }
     }
-    auto frag_of = [&](const f32x4 *tiles, int u) -> Frag<TIn> {
-      if constexpr (sizeof(TIn) == 2) return acc_frag_bf(tiles[2 * u], tiles[2 * u + 1]);
-      else return tiles[u];
-    };
     __syncthreads(); // every consumer wave's score tiles written
 
     // ---- O = (masked scores) U + diag(g) Q H -------------------------------------------

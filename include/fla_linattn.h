@@ -200,10 +200,10 @@ int fla_linattn_bwd_varlen(const void *q, const void *k, const void *v, const fl
  *   init_state, final_state: fp32 [B][H][dk][dv] (h = S^T as above) or NULL; may alias.
  *   dk in {64, 128} (fp32: 64); dv in {64, 128, 256}; chunk = 64; flags: FLA_BF16 only.
  * Two launches: a pre-pass forms, for every chunk at once, the parts that do not depend on
- * the state (W = T diag(beta g) K^ and Tb = T diag(beta) with T the inverse of the chunk's
+ * the state (Tb = T diag(beta) and Tg = T diag(beta g) with T the inverse of the chunk's
  * unit lower-triangular delta system), into a stream-ordered workspace of
- * B H (T dk + ceil(T / 64) 64 64) elem bytes; then one workgroup per (b, h, 64-wide value
- * slice) streams the chunks with the state on chip, forming U = Tb V - W H per chunk.
+ * B H ceil(T / 64) 2 64 64 elem bytes; then one workgroup per (b, h, 64-wide value slice)
+ * streams the chunks with the state on chip, forming U = Tb V - Tg (K^ H) per chunk.
  */
 int fla_gdn_fwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
                 const float *init_state, void *out, float *final_state, int64_t B, int64_t H,
