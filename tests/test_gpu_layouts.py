@@ -145,6 +145,38 @@ def test_varlen(dtype, decay, norm):
         assert rel_err(o_s, ro) <= TOL[dtype] and rel_err(fin[s:s + 1], rf) <= TOL[dtype], s
 
 
+@pytest.mark.parametrize("n_seqs", [8192, 8193])
+def test_varlen_many_sequences(n_seqs):
+    """Many short sequences with a few long ones among them: at 8192 sequences the
+    longest-first order is ranked by the multi-block ranking kernel, above that the
+    sequences run in their given order.  Sampled sequences (all long ones, some empty ones)
+    against the oracle; every empty sequence keeps its initial state exactly."""
+    rng = np.random.default_rng(790 + n_seqs)
+    lengths = rng.integers(0, 4, size=n_seqs)
+    long_at = rng.choice(n_seqs, size=4, replace=False)
+    lengths[long_at] = [130, 200, 64, 257]
+    lengths = [int(x) for x in lengths]
+    w, inp = case("f32", "gate", 64, 64, sum(lengths), B=1, H=1, init=False, seed=791)
+    cu, seqs, packed = pack(w, inp, lengths)
+    init = (0.1 * rng.standard_normal((n_seqs, w.H, w.dk, w.dv))).astype(np.float32)
+    say(f"[varlen-many] {n_seqs} sequences, {sum(lengths)} tokens")
+    out, fin = fla.fwd_varlen(dev(w, packed["q"]), dev(w, packed["k"]), dev(w, packed["v"]),
+                              to_device(cu), to_device(packed["decay"]), decay_kind="gate",
+                              init_state=to_device(init))
+    torch.cuda.synchronize()
+    out, fin = to_host(out), to_host(fin)
+    empty = [s for s in range(n_seqs) if lengths[s] == 0]
+    assert empty and all(np.array_equal(fin[s], init[s]) for s in empty)
+    sample = sorted(set(long_at.tolist()) | set(rng.choice(n_seqs, size=120, replace=False).tolist()))
+    for s in sample:
+        d = seqs[s]
+        ro, rf = oracle.fwd(d["q"], d["k"], d["v"], d["decay"], "gate", init[s:s + 1])
+        assert rel_err(fin[s:s + 1], rf) <= TOL["f32"], s
+        if lengths[s]:
+            o_s = np.swapaxes(out[cu[s]:cu[s + 1]], 0, 1)[None]
+            assert rel_err(o_s, ro) <= TOL["f32"], s
+
+
 def test_varlen_bad_offsets_are_clamped():
     """Offsets outside [0, total] or decreasing are clamped: no fault, sequences of
     length zero keep their initial state."""
