@@ -85,8 +85,10 @@ struct BwdCfg {
   static constexpr int NVX = C * DY / VE / NTG;
   static constexpr int NVZ = C * XW / VE / NTG;
   static_assert(NVX >= 1 && NVZ >= 1, "tile too small for the thread count");
-  // gate scan: NSEG row segments of SEGR rows per column
-  static constexpr int NSEG = GATE ? NTG / GW : 1;
+  // gate scan: NSEG row segments of SEGR rows; a thread scans GC adjacent columns of one
+  // segment (two for the dv role's gate of 128 columns or more, so its segments stay short)
+  static constexpr int GC = (GATE && ROLE == BWD_DV && GW >= 128) ? 2 : 1;
+  static constexpr int NSEG = GATE ? NTG * GC / GW : 1;
   static constexpr int SEGR = C / NSEG;
   static_assert(!GATE || ROLE == BWD_DV || SEGR == 16, "dq / dk read segment prefixes per row block");
   // a wave's 16-byte vectors of a decayed tile cover 64 / (row vectors) consecutive rows,
@@ -301,7 +303,7 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
   const int ptid = K::PC ? tid - K::NTG : tid;
   const int pwave = K::PC ? wave - 4 : wave;
   uint32_t rX[K::NVX][4], rY[K::NVX][4], rZ[K::NVZ][4];
-  float rG[K::GATE ? K::SEGR : 1]; // gate rows of this thread's (column, segment) in scan order
+  float rG[K::GATE ? K::SEGR : 1][K::GC]; // gate rows of this thread's (columns, segment) in scan order
   float rTok = 1.f;
   auto ld_xy = [&](int n) {
     const int L = chunk_len(n);
@@ -335,12 +337,22 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     const int L = chunk_len(n);
     const int64_t t0 = (int64_t)n * C;
     if constexpr (K::GATE) {
-      // thread (column ptid % GW, segment ptid / GW) reads its SEGR rows: for each row the
-      // lanes of a wave read consecutive columns
-      const float *gsrc = a.decay + baseK + goff + ptid % GW;
-      const int r0 = (ptid / GW) * K::SEGR;
+      // thread (columns GC (ptid % (GW / GC)) + 0 .. GC - 1, segment ptid / (GW / GC)) reads
+      // its SEGR rows: for each row the lanes of a wave read consecutive columns
+      constexpr int NCOL = GW / K::GC;
+      const float *gsrc = a.decay + baseK + goff + K::GC * (ptid % NCOL);
+      const int r0 = (ptid / NCOL) * K::SEGR;
 #pragma unroll
-      for (int i = 0; i < K::SEGR; ++i) rG[i] = gsrc[(t0 + (r0 + i < L ? r0 + i : L - 1)) * rsK];
+      for (int i = 0; i < K::SEGR; ++i) {
+        const float *src = gsrc + (t0 + (r0 + i < L ? r0 + i : L - 1)) * rsK;
+        if constexpr (K::GC == 2) {
+          const float2 v = *reinterpret_cast<const float2 *>(src);
+          rG[i][0] = v.x;
+          rG[i][1] = v.y;
+        } else {
+          rG[i][0] = *src;
+        }
+      }
     }
     if constexpr (K::TOKEN) {
       if (pwave == 0) rTok = a.decay[baseT + (t0 + (ptid < L ? ptid : L - 1)) * rsT];
@@ -362,15 +374,23 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     if constexpr (K::GATE) {
       // local products down this thread's segment, and the segment's total; rows past the
       // end carry no decay
-      const int col = ptid % GW, seg = ptid / GW;
+      constexpr int NCOL = GW / K::GC;
+      const int col = K::GC * (ptid % NCOL), seg = ptid / NCOL;
       float *loc = (ROLE == BWD_DV) ? sBS : stB(s);
-      float p = 1.f;
+      float p[K::GC];
+#pragma unroll
+      for (int c = 0; c < K::GC; ++c) p[c] = 1.f;
 #pragma unroll
       for (int i = 0; i < K::SEGR; ++i) {
-        p *= (seg * K::SEGR + i < L) ? rG[i] : 1.f;
-        loc[(seg * K::SEGR + i) * GW + col] = p;
+        const bool in = seg * K::SEGR + i < L;
+#pragma unroll
+        for (int c = 0; c < K::GC; ++c) p[c] *= in ? rG[i][c] : 1.f;
+        float *dst = loc + (seg * K::SEGR + i) * GW + col;
+        if constexpr (K::GC == 2) *reinterpret_cast<float2 *>(dst) = make_float2(p[0], p[1]);
+        else *dst = p[0];
       }
-      sTot[seg * GW + col] = p;
+#pragma unroll
+      for (int c = 0; c < K::GC; ++c) sTot[seg * GW + col + c] = p[c];
     } else if constexpr (K::TOKEN) {
       if (pwave == 0) {
         float x = lane < L ? rTok : 1.f;
@@ -409,11 +429,16 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     const int L = chunk_len(n);
     if constexpr (K::GATE) {
       // prefix of the earlier segments; the chunk decay bL from the last segment
-      const int col = ptid % GW, seg = ptid / GW;
-      float pre = 1.f;
-      for (int s2 = 0; s2 < seg; ++s2) pre *= sTot[s2 * GW + col];
-      if constexpr (ROLE != BWD_DV) stPre(s)[seg * GW + col] = pre;
-      if (seg == K::NSEG - 1) stBL(s)[col] = pre * sTot[seg * GW + col];
+      constexpr int NCOL = GW / K::GC;
+      const int col0 = K::GC * (ptid % NCOL), seg = ptid / NCOL;
+#pragma unroll
+      for (int c = 0; c < K::GC; ++c) {
+        const int col = col0 + c;
+        float pre = 1.f;
+        for (int s2 = 0; s2 < seg; ++s2) pre *= sTot[s2 * GW + col];
+        if constexpr (ROLE != BWD_DV) stPre(s)[seg * GW + col] = pre;
+        if (seg == K::NSEG - 1) stBL(s)[col] = pre * sTot[seg * GW + col];
+      }
     }
     // b at row r, columns c .. c + VE - 1
     auto b_vec = [&](float *bb, int r, int c) {
@@ -442,13 +467,35 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
       constexpr bool ELU = decltype(elu_c)::value;
       if constexpr (ROLE == BWD_DV) {
         constexpr int VPRX = DY / VE;
+        // when vector j of every thread lies in gate segment j, the segment prefix is a
+        // running product over j (the same products, in the same order, as b_vec's loop)
+        constexpr bool RUN = K::GATE && K::NTG / VPRX == K::SEGR;
+        float pre[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) pre[e] = 1.f;
 #pragma unroll
         for (int j = 0; j < K::NVX; ++j) {
           const int vi = ptid + K::NTG * j, r = vi / VPRX, c = (vi % VPRX) * VE;
           float fx[VE], fy[VE], bb[VE];
           unpack<TIn, VE>(fx, rX[j]);
           unpack<TIn, VE>(fy, rY[j]);
-          b_vec(bb, r, c);
+          if constexpr (RUN) {
+#pragma unroll
+            for (int e = 0; e < VE; e += 4) {
+              const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sBS + r * GW + c + e);
+              bb[e] = l4[0] * pre[e]; bb[e + 1] = l4[1] * pre[e + 1];
+              bb[e + 2] = l4[2] * pre[e + 2]; bb[e + 3] = l4[3] * pre[e + 3];
+            }
+            if (j + 1 < K::NVX) {
+#pragma unroll
+              for (int e = 0; e < VE; e += 4) {
+                const f32x4 t4 = *reinterpret_cast<const f32x4 *>(sTot + j * GW + c + e);
+                pre[e] *= t4[0]; pre[e + 1] *= t4[1]; pre[e + 2] *= t4[2]; pre[e + 3] *= t4[3];
+              }
+            }
+          } else {
+            b_vec(bb, r, c);
+          }
           const float ok = r < L ? 1.f : 0.f; // rows past the end (finite values): zeros
 #pragma unroll
           for (int e = 0; e < VE; ++e) {
