@@ -59,10 +59,11 @@ struct GdnCfg {
   // slices once Tb and Tg are formed, which fits three workgroups per CU (bf16, dk 128)
   static constexpr int cmax(int x, int y) { return x > y ? x : y; }
   static constexpr int P_K = 0;
-  // A, fp32 [C][C], replaced block by block by T = (I + A)^-1; Tb and Tg are formed from
-  // T in registers as they are written out, so four workgroups fit a CU
-  static constexpr int P_A = P_K + C * LDK * ES;
-  static constexpr int P_G = P_A + C * C * 4;                         // g [C], beta [C]
+  // A, fp32 [C][C], over K^ (whose last reader is A itself: the tiles wait in registers
+  // for a barrier), replaced block by block by T = (I + A)^-1; Tb and Tg are formed from T
+  // in registers as they are written out
+  static constexpr int P_A = P_K;
+  static constexpr int P_G = P_K + cmax(C * LDK * ES, C * C * 4);    // g [C], beta [C]
   static constexpr int P_BETA = P_G + C * 4;
   static constexpr int P_GI = P_BETA + C * 4;                         // 1 / g [C]
   static constexpr int P_LDS = P_GI + C * 4;
@@ -217,29 +218,40 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   }
   __syncthreads();
 
-  // A = strictly lower (beta_t g_t / g_j) k^_t . k^_j, fp32: 10 tiles over 4 waves
-  static_for<0, 16>([&](auto I) {
-    constexpr int tb = I / 4, jb = I % 4;
-    if constexpr (jb <= tb) {
-      constexpr int pos = tb * (tb + 1) / 2 + jb;
-      if (pos % 4 == wave) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const TIn *at = sK + (16 * tb + li) * LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
-        const TIn *bj = sK + (16 * jb + li) * LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
+  // A = strictly lower (beta_t g_t / g_j) k^_t . k^_j, fp32: tile k = tb (tb + 1) / 2 + jb
+  // (jb <= tb, 10 tiles) is wave k % 4's slot k / 4; the tiles wait in registers until
+  // every wave has read K^, whose LDS they then take
+  f32x4 atile[3];
 #pragma unroll
-        for (int u = 0; u < DK / KU; ++u)
-          acc = mma(acc, ld_frag_c_at<TIn, true>(bj, u, g), ld_frag_c_at<TIn, true>(at, u, g));
-        // acc[qq] = k^_j . k^_t with j = 16 jb + 4g + qq, t = 16 tb + li
-        const int t = 16 * tb + li;
-        const float bt = sBeta[t] * sG[t];
+  for (int sl = 0; sl < 3; ++sl) {
+    const int k = 4 * sl + wave;
+    if (k < 10) {
+      const int tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0, jb = k - tb * (tb + 1) / 2;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const TIn *at = sK + (16 * tb + li) * LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
+      const TIn *bj = sK + (16 * jb + li) * LDK + (sizeof(TIn) == 2 ? 8 : 4) * g;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int j = 16 * jb + 4 * g + qq;
-          sA[t * C + j] = (j < t) ? bt * sGi[j] * acc[qq] : 0.f;
-        }
+      for (int u = 0; u < DK / KU; ++u)
+        acc = mma(acc, ld_frag_c_at<TIn, true>(bj, u, g), ld_frag_c_at<TIn, true>(at, u, g));
+      atile[sl] = acc;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int sl = 0; sl < 3; ++sl) {
+    const int k = 4 * sl + wave;
+    if (k < 10) {
+      const int tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0, jb = k - tb * (tb + 1) / 2;
+      // atile[sl][qq] = k^_j . k^_t with j = 16 jb + 4g + qq, t = 16 tb + li
+      const int t = 16 * tb + li;
+      const float bt = sBeta[t] * sG[t];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int jj = 16 * jb + 4 * g + qq;
+        sA[t * C + jj] = (jj < t) ? bt * sGi[jj] * atile[sl][qq] : 0.f;
       }
     }
-  });
+  }
   __syncthreads();
 
   // diagonal blocks of T = (I + A)^-1 by forward substitution: lanes 0..15 of wave w
