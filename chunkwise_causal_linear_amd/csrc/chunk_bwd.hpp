@@ -606,7 +606,10 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
   // at the start of the chunk, used by the output tiles
   uint32_t raux[4][K::ES]; // 4 elements of the input type
   f32x4 rqv[4];
-  auto load_lane = [&](int n) {
+  // the next chunk's per-lane values, loaded one chunk ahead (two-group schedule)
+  uint32_t naux[4][K::ES];
+  f32x4 nrqv[4];
+  auto load_lane = [&](int n, uint32_t (&raux)[4][K::ES], f32x4 (&rqv)[4]) {
     const int L = chunk_len(n);
     const int64_t t0 = (int64_t)n * C;
     if constexpr (K::HAS_AUX) {
@@ -865,11 +868,28 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
   };
 
   if constexpr (K::PC) {
+    // per-lane values one chunk ahead where that measured faster (dk; dq without the per-key
+    // gate, whose dq output group waits on them later in the chunk)
+    constexpr bool AHEAD = ROLE == BWD_DK || (ROLE == BWD_DQ && DECAY != DECAY_GATE);
+    if constexpr (AHEAD) {
+      if (nchunks > 0) load_lane(chunk_at(0), naux, nrqv);
+    }
     __syncthreads(); // stage 0: phase 1 done
     __syncthreads(); // stage 0 complete
     for (int it = 0; it < nchunks; ++it) {
       const int n = chunk_at(it);
-      load_lane(n);
+      if constexpr (AHEAD) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+          for (int e = 0; e < K::ES; ++e) raux[rb][e] = naux[rb][e];
+          rqv[rb] = nrqv[rb];
+        }
+        // clamped past the last chunk: loads an existing chunk, values unused
+        load_lane(chunk_at(it + 1 < nchunks ? it + 1 : it), naux, nrqv);
+      } else {
+        load_lane(n, raux, rqv);
+      }
       scores(it & 1);
       __syncthreads();
       finish(n, it & 1);
@@ -883,7 +903,7 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
     }
     for (int it = 0; it < nchunks; ++it) {
       const int n = chunk_at(it);
-      load_lane(n);
+      load_lane(n, raux, rqv);
       phase1(n, 0);
       if (it + 1 < nchunks) load1(chunk_at(it + 1));
       __syncthreads();
