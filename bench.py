@@ -84,6 +84,40 @@ def algorithmic_bwd(w) -> tuple[float, float]:
     return float(b), f
 
 
+def host_cores() -> dict:
+    """The host CPUs this process may run on: the affinity mask, capped by a cgroup CPU
+    quota when one is set, and the CPU model (from /proc/cpuinfo)."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, per = f.read().split()[:2]
+            if q != "max":
+                quota = float(q) / float(per)
+    except (OSError, ValueError):
+        pass
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = affinity if quota is None else max(1, min(affinity, int(quota + 0.5)))
+    return {"threads": threads, "affinity_cpus": affinity, "cgroup_cpu_quota": quota,
+            "cpu_model": model}
+
+
+def cpu_fields(hc: dict) -> dict:
+    return {"cores": hc["threads"], "cpu_model": hc["cpu_model"],
+            "affinity_cpus": hc["affinity_cpus"], "cgroup_cpu_quota": hc["cgroup_cpu_quota"]}
+
+
 def kernel_name(w, bthd: bool = False) -> str:
     t = "__bf16" if w.dtype == "bf16" else "float"
     d = {"none": 0, "gamma": 1, "gate": 2, "token": 3}[w.decay]
@@ -98,10 +132,8 @@ def cpu_baseline(w, inp, out_gpu, fin_gpu, budget_s: float):
     import oracle
     from workloads import to_numpy_input
 
-    threads = max(1, min(16, os.cpu_count() or 1))
-    env_threads = os.environ.get("OMP_NUM_THREADS")
-    if env_threads and env_threads.isdigit():
-        threads = max(1, min(threads, int(env_threads)))
+    hc = host_cores()
+    threads = hc["threads"]
 
     def run(bs, hs):
         sl = (bs, hs)
@@ -133,7 +165,7 @@ def cpu_baseline(w, inp, out_gpu, fin_gpu, budget_s: float):
     return {
         "value": token_heads / dt / w.H,   # tokens/s: H heads make one token
         "unit": "tokens/s",
-        "cores": threads,
+        **cpu_fields(hc),
         "kind": "oracle",
         "sample": f"batches 0..{nbatch - 1} of {w.B}, all {w.H} heads, all {w.T} tokens "
                   f"({token_heads} token-heads, fp64 recurrence, {dt:.1f} s)",
@@ -148,10 +180,8 @@ def cpu_baseline_bwd(w, inp, grads, got, budget_s: float):
     import oracle
     from workloads import to_numpy_input
 
-    threads = max(1, min(16, os.cpu_count() or 1))
-    env_threads = os.environ.get("OMP_NUM_THREADS")
-    if env_threads and env_threads.isdigit():
-        threads = max(1, min(threads, int(env_threads)))
+    hc = host_cores()
+    threads = hc["threads"]
     dt = 0.0
     nbatch = 0
     err, mag = {}, {}
@@ -181,7 +211,7 @@ def cpu_baseline_bwd(w, inp, grads, got, budget_s: float):
     return {
         "value": token_heads / dt / w.H,
         "unit": "tokens/s",
-        "cores": threads,
+        **cpu_fields(hc),
         "kind": "oracle",
         "sample": f"batches 0..{nbatch - 1} of {w.B}, all {w.H} heads, all {w.T} tokens "
                   f"({token_heads} token-heads, fp64 back-propagation, {dt:.1f} s)",
@@ -189,8 +219,9 @@ def cpu_baseline_bwd(w, inp, grads, got, budget_s: float):
 
 
 def timed(torch, step, steps, warmup, stream):
-    """Warm-up (about a second of steps unless given), then `steps` steps between HIP events
-    on the launch stream.  Returns (ms per step, warm-up steps, wall seconds)."""
+    """Warm-up (about a second of steps unless given), then `steps` steps with a HIP event
+    on the launch stream before and after each.  Returns (mean ms per step over the timed
+    region, warm-up steps, wall seconds, per-step stats {median, min, max} in ms)."""
     if warmup is None:
         warmup, t0 = 0, time.perf_counter()
         while True:
@@ -204,15 +235,84 @@ def timed(torch, step, steps, warmup, stream):
         for _ in range(warmup):
             step()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t_wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(steps):
+    evs[0].record(stream)
+    for i in range(steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps, warmup, time.perf_counter() - t_wall0
+    t_wall = time.perf_counter() - t_wall0
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    mid = len(per) // 2
+    median = per[mid] if len(per) % 2 else 0.5 * (per[mid - 1] + per[mid])
+    stats = {"median": median, "min": per[0], "max": per[-1]}
+    return evs[0].elapsed_time(evs[-1]) / steps, warmup, t_wall, stats
+
+
+def measure_peaks(torch, fla, stream) -> dict:
+    """What this GPU reaches with the library's plain probe kernels (include/fla_probe.h):
+    HBM streaming rates (read only, copy, and five reads per write, the mix of the gated
+    forward pass) over 2 GiB buffers, and the dense bf16 MFMA rate of register-only chains.
+    Each is the best of several timed launches after a warm-up launch.  Running them
+    first also brings the GPU clocks up before the warm-up steps."""
+    nbytes = 2 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").random_()
+    dst = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    res = {}
+
+    def best_ms(fn, reps):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+
+    ms = best_ms(lambda: fla.probe_stream(src, dst, nbytes, fla.PROBE_READ, stream), 8)
+    res["hbm_read_GBs"] = nbytes / (ms * 1e-3) / 1e9
+    half = nbytes // 2
+    ms = best_ms(lambda: fla.probe_stream(src, dst, half, fla.PROBE_COPY, stream), 8)
+    res["hbm_copy_GBs"] = 2 * half / (ms * 1e-3) / 1e9
+    mix = (nbytes // 96) * 96            # 5/6 read from src, 1/6 written to dst
+    ms = best_ms(lambda: fla.probe_stream(src, dst, mix, fla.PROBE_MIX5, stream), 8)
+    res["hbm_read5_write1_GBs"] = mix / (ms * 1e-3) / 1e9
+    del src, dst
+    wgs, iters = 2048, 20000
+    out = torch.empty(4 * wgs, dtype=torch.float32, device="cuda")
+    flops = [0.0]
+
+    def mf():
+        flops[0] = fla.probe_mfma(out, wgs, iters, stream)
+
+    ms = best_ms(mf, 5)
+    res["mfma_bf16_TFLOPs"] = flops[0] / (ms * 1e-3) / 1e12
+    res["probes"] = ("hand-written HIP: 16-byte non-temporal loads/stores, 8 in flight per "
+                     "lane, grid-stride over 2 GiB; MFMA: 2048 workgroups x 4 waves x 4 "
+                     "independent v_mfma_f32_32x32x16_bf16 chains")
+    torch.cuda.synchronize()
+    return res
+
+
+def add_measured(roof: dict, peaks, dtype: str) -> dict:
+    """Add the measured ceilings (measure_peaks) and the fractions of them to a roofline
+    record; the nominal `peak` and `frac` stay as published."""
+    if not peaks:
+        roof["measured_peaks"] = None
+        return roof
+    roof["measured_peaks"] = peaks
+    a = roof["achieved"]
+    roof["frac_of_measured_read5_write1"] = a / peaks["hbm_read5_write1_GBs"]
+    roof["frac_of_measured_copy"] = a / peaks["hbm_copy_GBs"]
+    roof["frac_of_measured_read"] = a / peaks["hbm_read_GBs"]
+    if dtype == "bf16":
+        roof["mfma_frac_of_measured"] = roof["mfma_tflops"] / peaks["mfma_bf16_TFLOPs"]
+    return roof
 
 
 def bench_bwd(torch, fla, w, args):
@@ -230,7 +330,7 @@ def bench_bwd(torch, fla, w, args):
                                      chunk=w.chunk, stream=stream)
         got.update(dq=dq, dk=dk, dv=dv, dgate=dg, dinit=di)
 
-    ms, warmup, t_wall = timed(torch, step, args.steps, args.warmup, stream)
+    ms, warmup, t_wall, per_step = timed(torch, step, args.steps, args.warmup, stream)
     alg_bytes, alg_flops = algorithmic_bwd(w)
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     res = {
@@ -241,6 +341,8 @@ def bench_bwd(torch, fla, w, args):
         "steps": args.steps,
         "warmup": warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": per_step["median"],
+        "ms_per_step_min": per_step["min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -252,7 +354,7 @@ def bench_bwd(torch, fla, w, args):
             "phi": "elu+1" if w.phi_elu1 else "identity", "init_state": w.init_sigma > 0,
             "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU",
         },
-        "roofline": {
+        "roofline": add_measured({
             "bound": "hbm",
             "kernel": "chunk_bwd_kernel: dq, dv, dk launches (+ per-token decay epilogue)",
             "achieved": achieved,
@@ -263,7 +365,7 @@ def bench_bwd(torch, fla, w, args):
             "algorithmic_bytes_per_launch": alg_bytes,
             "mfma_tflops": alg_flops / (ms * 1e-3) / 1e12,
             "mfma_frac": alg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
-        },
+        }, args.peaks, w.dtype),
         "wall_s_timed_region": t_wall,
     }
     if not args.no_cpu_baseline:
@@ -298,7 +400,7 @@ def bench_varlen(torch, fla, args):
                        decay_kind=w.decay, out=out, final_state=fin, chunk=w.chunk,
                        stream=stream)
 
-    ms, warmup, t_wall = timed(torch, step, args.steps, args.warmup, stream)
+    ms, warmup, t_wall, per_step = timed(torch, step, args.steps, args.warmup, stream)
     alg_bytes, alg_flops = algorithmic(w)
     alg_bytes += (n - 1) * w.H * w.dk * w.dv * 4  # one end state per sequence
     achieved = alg_bytes / (ms * 1e-3) / 1e9
@@ -310,6 +412,8 @@ def bench_varlen(torch, fla, args):
         "steps": args.steps,
         "warmup": warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": per_step["median"],
+        "ms_per_step_min": per_step["min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -322,7 +426,7 @@ def bench_varlen(torch, fla, args):
             "len_mean": float(lengths.mean()), "global_batch": n, "seq_len": int(lengths.max()),
             "parallelism": "single GPU",
         },
-        "roofline": {
+        "roofline": add_measured({
             "bound": "hbm",
             "kernel": kernel_name(w, True) + " [packed sequences]",
             "achieved": achieved,
@@ -333,11 +437,12 @@ def bench_varlen(torch, fla, args):
             "algorithmic_bytes_per_launch": alg_bytes,
             "mfma_tflops": alg_flops / (ms * 1e-3) / 1e12,
             "mfma_frac": alg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
-        },
+        }, args.peaks, w.dtype),
         "wall_s_timed_region": t_wall,
     }
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
+        hc = host_cores()
+        threads = hc["threads"]
         dt, eo, mo, ef, mf, done, toks = 0.0, 0.0, 0.0, 0.0, 0.0, 0, 0
         while done < n and (done == 0 or dt < args.cpu_budget):
             s0, s1 = int(cu_h[done]), int(cu_h[done + 1])
@@ -354,7 +459,7 @@ def bench_varlen(torch, fla, args):
             ef, mf = max(ef, float(np.max(np.abs(f - rf)))), max(mf, float(np.max(np.abs(rf))))
             toks += s1 - s0
             done += 1
-        res["cpu_baseline"] = {"value": toks / dt, "unit": "tokens/s", "cores": threads,
+        res["cpu_baseline"] = {"value": toks / dt, "unit": "tokens/s", **cpu_fields(hc),
                                "kind": "oracle",
                                "sample": f"sequences 0..{done - 1} of {n} ({toks} tokens, all "
                                          f"{w.H} heads, fp64 recurrence, {dt:.1f} s)"}
@@ -383,7 +488,7 @@ def bench_gdn(torch, fla, args):
                     init_state=inp["init"], out=out, final_state=fin, chunk=w.chunk,
                     stream=stream)
 
-    ms, warmup, t_wall = timed(torch, step, args.steps, args.warmup, stream)
+    ms, warmup, t_wall, per_step = timed(torch, step, args.steps, args.warmup, stream)
     s = 2 if w.dtype == "bf16" else 4
     th = w.B * w.H * w.T
     # q, k, v read, out written; alpha and beta read; end state written (start state read)
@@ -403,6 +508,8 @@ def bench_gdn(torch, fla, args):
         "steps": args.steps,
         "warmup": warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": per_step["median"],
+        "ms_per_step_min": per_step["min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -413,7 +520,7 @@ def bench_gdn(torch, fla, args):
             "chunk": w.chunk, "init_state": w.init_sigma > 0, "global_batch": w.B,
             "seq_len": w.T, "parallelism": "single GPU",
         },
-        "roofline": {
+        "roofline": add_measured({
             "bound": "hbm",
             "kernel": f"gdn_prep_kernel<{t}, {w.dk}> + gdn_state_kernel<{t}, {w.dk}>",
             "achieved": achieved,
@@ -424,11 +531,12 @@ def bench_gdn(torch, fla, args):
             "algorithmic_bytes_per_launch": alg_bytes,
             "mfma_tflops": alg_flops / (ms * 1e-3) / 1e12,
             "mfma_frac": alg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
-        },
+        }, args.peaks, w.dtype),
         "wall_s_timed_region": t_wall,
     }
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
+        hc = host_cores()
+        threads = hc["threads"]
         dt, eo, mo, ef, mf, nb = 0.0, 0.0, 0.0, 0.0, 0.0, 0
         while nb < w.B and (nb == 0 or dt < args.cpu_budget):
             sl = slice(nb, nb + 1)
@@ -443,7 +551,7 @@ def bench_gdn(torch, fla, args):
             eo, mo = max(eo, float(np.max(np.abs(o - ro)))), max(mo, float(np.max(np.abs(ro))))
             ef, mf = max(ef, float(np.max(np.abs(f - rf)))), max(mf, float(np.max(np.abs(rf))))
             nb += 1
-        res["cpu_baseline"] = {"value": w.T * nb / dt, "unit": "tokens/s", "cores": threads,
+        res["cpu_baseline"] = {"value": w.T * nb / dt, "unit": "tokens/s", **cpu_fields(hc),
                                "kind": "oracle",
                                "sample": f"batches 0..{nb - 1} of {w.B}, all {w.H} heads, all "
                                          f"{w.T} tokens (fp64 recurrence, {dt:.1f} s)"}
@@ -496,6 +604,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the measured HBM / MFMA ceilings (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy instead (HBM reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters and the achievable copy rate)")
@@ -518,6 +628,7 @@ def main():
     from workloads import HEADLINE, WORKLOADS, generate_torch
 
     torch.cuda.set_device(0)
+    args.peaks = None if args.no_probes else measure_peaks(torch, fla, torch.cuda.current_stream())
     if args.gdn:
         bench_gdn(torch, fla, args)
         return
@@ -554,7 +665,7 @@ def main():
                     phi_elu1=w.phi_elu1, normalize=w.normalize, stream=stream)
 
     # timed region: HIP events on the stream the kernels are launched on
-    ms, warmup, t_wall = timed(torch, step, args.steps, args.warmup, stream)
+    ms, warmup, t_wall, per_step = timed(torch, step, args.steps, args.warmup, stream)
 
     nseg = fla.segments_for(w.B, w.H, w.T, w.dk, w.dv, w.chunk,
                             fla.flags_for(inp["q"].dtype, w.decay, w.phi_elu1, w.normalize))
@@ -579,6 +690,8 @@ def main():
         "steps": args.steps,
         "warmup": warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": per_step["median"],
+        "ms_per_step_min": per_step["min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -591,7 +704,7 @@ def main():
             "layout": "[B][T][H][d]" if args.layout == "bthd" else "[B][H][T][d]",
             "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU",
         },
-        "roofline": {
+        "roofline": add_measured({
             "bound": "hbm",
             "kernel": kernel_name(w, args.layout == "bthd") + (" (+ segment passes)" if nseg > 1 else ""),
             "achieved": achieved_gbs,
@@ -602,7 +715,7 @@ def main():
             "algorithmic_bytes_per_launch": alg_bytes,
             "mfma_tflops": alg_flops / (ms * 1e-3) / 1e12,
             "mfma_frac": alg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
-        },
+        }, args.peaks, w.dtype),
         "wall_s_timed_region": t_wall,
     }
     if not args.no_cpu_baseline:

@@ -31,7 +31,9 @@ FLA_LAYOUT_BTHD = 1 << 6
 
 EXPORTED = ("fla_linattn_fwd", "fla_linattn_fwd_segments", "fla_linattn_step",
             "fla_status_string", "fla_linattn_segments_for", "fla_linattn_bwd",
-            "fla_linattn_fwd_varlen", "fla_linattn_bwd_varlen", "fla_gdn_fwd")
+            "fla_linattn_fwd_varlen", "fla_linattn_bwd_varlen", "fla_gdn_fwd",
+            "fla_probe_stream", "fla_probe_mfma", "fla_probe_mfma_flops")
+PROBE_READ, PROBE_COPY, PROBE_MIX5 = 0, 1, 2
 
 _lib = None
 
@@ -75,6 +77,12 @@ def load_library():
     lib.fla_linattn_bwd_varlen.restype = c_int
     lib.fla_gdn_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, u32, p]
     lib.fla_gdn_fwd.restype = c_int
+    lib.fla_probe_stream.argtypes = [p, p, i64, c_int, p]
+    lib.fla_probe_stream.restype = c_int
+    lib.fla_probe_mfma.argtypes = [p, i64, i64, p]
+    lib.fla_probe_mfma.restype = c_int
+    lib.fla_probe_mfma_flops.argtypes = [i64, i64]
+    lib.fla_probe_mfma_flops.restype = ctypes.c_double
     _lib = lib
     return lib
 
@@ -91,6 +99,31 @@ def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_tensors(q: torch.Tensor, same_dtype=(), fp32=(), extra=()) -> None:
+    """Host-side checks shared by every call: every tensor is contiguous (a strided view
+    such as q[:, :, t] would be read as if it were dense); q is bf16 or fp32; tensors in
+    same_dtype have q's dtype; fp32 tensors (decays, states) are float32; all live on q's
+    device, a GPU.  None entries are skipped."""
+    tensors = [t for t in (q, *same_dtype, *fp32, *extra) if t is not None]
+    for t in tensors:
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous (got a strided view)")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"q must be bfloat16 or float32, got {q.dtype}")
+    for t in same_dtype:
+        if t is not None and t.dtype != q.dtype:
+            raise ValueError(f"k, v, out and upstream gradients must have q's dtype {q.dtype}, "
+                             f"got {t.dtype}")
+    for t in fp32:
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"decays and states must be float32, got {t.dtype}")
+    if not q.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    for t in tensors:
+        if t.device != q.device:
+            raise ValueError(f"all tensors must be on {q.device}, got one on {t.device}")
 
 
 def flags_for(dtype: torch.dtype, decay_kind: str, phi_elu1: bool, normalize: bool) -> int:
@@ -137,9 +170,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch
                           device=q.device)
     if final_state is None and want_final:
         final_state = torch.empty((B, H, dk, ncol), dtype=torch.float32, device=q.device)
-    for t in (q, k, v, out, decay, init_state, final_state):
-        if t is not None and not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    _check_tensors(q, (k, v, out), (decay, init_state, final_state))
     flags = flags_for(q.dtype, kind, phi_elu1, normalize)
     if layout == "bthd":
         flags |= FLA_LAYOUT_BTHD
@@ -171,6 +202,7 @@ def step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor,
                       else {1: "gamma", 2: "token"}.get(decay.dim(), "gate"))
     if out is None:
         out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    _check_tensors(q, (k, v, out), (decay, state))
     flags = flags_for(q.dtype, decay_kind, phi_elu1, normalize)
     rc = load_library().fla_linattn_step(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(state),
                                          _ptr(out), B, H, dk, dv, flags, _stream(stream))
@@ -205,9 +237,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
         raise ValueError(f"unknown layout {layout!r}")
     dv = v.shape[-1]
     kind = _decay_kind(decay, decay_kind)
-    for t in (q, k, v, dout, decay, init_state, dfinal):
-        if t is not None and not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    _check_tensors(q, (k, v, dout), (decay, init_state, dfinal))
     dq, dkk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dgate = None
     if want_dgate and kind in ("gate", "token"):
@@ -247,9 +277,7 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: to
         out = torch.empty((total, H, dv), dtype=q.dtype, device=q.device)
     if final_state is None and want_final:
         final_state = torch.empty((n, H, dk, ncol), dtype=torch.float32, device=q.device)
-    for t in (q, k, v, out, decay, init_state, final_state, cu_seqlens):
-        if t is not None and not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    _check_tensors(q, (k, v, out), (decay, init_state, final_state), (cu_seqlens,))
     flags = flags_for(q.dtype, decay_kind, phi_elu1, normalize) | FLA_LAYOUT_BTHD
     rc = load_library().fla_linattn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(decay),
                                                _ptr(init_state), _ptr(out), _ptr(final_state),
@@ -276,9 +304,7 @@ def bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Te
     if decay_kind is None:
         decay_kind = ("none" if decay is None
                       else {1: "gamma", 2: "token"}.get(decay.dim(), "gate"))
-    for t in (q, k, v, dout, decay, init_state, dfinal, cu_seqlens):
-        if t is not None and not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    _check_tensors(q, (k, v, dout), (decay, init_state, dfinal), (cu_seqlens,))
     dq, dkk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dgate = None
     if want_dgate and decay_kind in ("gate", "token"):
@@ -308,9 +334,7 @@ def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tens
         out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     if final_state is None and want_final:
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-    for t in (q, k, v, alpha, beta, out, init_state, final_state):
-        if t is not None and not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    _check_tensors(q, (k, v, out), (alpha, beta, init_state, final_state))
     flags = FLA_BF16 if q.dtype == torch.bfloat16 else 0
     rc = load_library().fla_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                      _ptr(init_state), _ptr(out), _ptr(final_state), B, H, T, dk,
@@ -318,3 +342,29 @@ def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tens
     if rc != FLA_OK:
         raise FlaError("fla_gdn_fwd", rc)
     return out, final_state
+
+
+def probe_stream(src: torch.Tensor, dst: torch.Tensor, nbytes: int, pattern: int,
+                 stream=None) -> None:
+    """One pass of the HBM streaming probe (include/fla_probe.h): PROBE_READ reads nbytes
+    of src (dst gets one word per workgroup), PROBE_COPY copies nbytes, PROBE_MIX5 reads
+    5/6 and writes 1/6 of nbytes."""
+    for t in (src, dst):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("probe buffers must be contiguous device tensors")
+    rc = load_library().fla_probe_stream(_ptr(src), _ptr(dst), int(nbytes), int(pattern),
+                                         _stream(stream))
+    if rc != 0:
+        raise FlaError("fla_probe_stream", rc)
+
+
+def probe_mfma(out: torch.Tensor, workgroups: int, iters: int, stream=None) -> float:
+    """One launch of the bf16 MFMA probe; returns the dense FLOPs it performs.
+    out: fp32 device tensor of at least 4 * workgroups elements."""
+    if out.dtype != torch.float32 or out.numel() < 4 * workgroups or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor of 4 * workgroups elements")
+    lib = load_library()
+    rc = lib.fla_probe_mfma(_ptr(out), int(workgroups), int(iters), _stream(stream))
+    if rc != 0:
+        raise FlaError("fla_probe_mfma", rc)
+    return float(lib.fla_probe_mfma_flops(int(workgroups), int(iters)))

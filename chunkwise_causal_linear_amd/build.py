@@ -47,11 +47,32 @@ def _units():
                           [f"-DFLA_TIN_BF16={flag}", f"-DFLA_BWD_DY={dy}"]))
     units.append((os.path.join(CSRC, "gdn_inst.hip"), os.path.join(OBJDIR, "gdn_inst.o"), []))
     units.append((os.path.join(CSRC, "fla_api.hip"), os.path.join(OBJDIR, "fla_api.o"), []))
+    units.append((os.path.join(CSRC, "probe.hip"), os.path.join(OBJDIR, "probe.o"), []))
     return units
 
 
-def _compile(unit):
+def _deps_mtime(src: str) -> float:
+    """Newest modification time of a unit's source and the local headers it includes
+    (followed recursively through #include "...")."""
+    seen, todo = set(), [os.path.abspath(src)]
+    while todo:
+        path = todo.pop()
+        if path in seen or not os.path.exists(path):
+            continue
+        seen.add(path)
+        with open(path) as f:
+            for line in f:
+                line = line.strip()
+                if line.startswith("#include") and '"' in line:
+                    name = line.split('"')[1]
+                    todo.append(os.path.normpath(os.path.join(os.path.dirname(path), name)))
+    return max(os.path.getmtime(p) for p in seen)
+
+
+def _compile(unit, incremental: bool = False):
     src, obj, extra = unit
+    if incremental and os.path.exists(obj) and os.path.getmtime(obj) > _deps_mtime(src):
+        return obj
     tmp = obj + ".tmp.o"
     cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,14 +82,15 @@ def _compile(unit):
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every HIP translation unit for gfx950 and link the shared library."""
+def build(jobs: int | None = None, verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every HIP translation unit for gfx950 and link the shared library.
+    incremental=True keeps objects newer than their sources and headers."""
     os.makedirs(OBJDIR, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     jobs = jobs or max(1, min(16, os.cpu_count() or 1))
     units = _units()
     with fut.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, units))
+        objs = list(ex.map(lambda u: _compile(u, incremental), units))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -83,6 +105,8 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", type=int, default=None)
+    ap.add_argument("--incremental", action="store_true",
+                    help="recompile only objects older than their sources or headers")
     args = ap.parse_args()
-    build(args.j, verbose=True)
+    build(args.j, verbose=True, incremental=args.incremental)
     sys.exit(0)

@@ -96,29 +96,17 @@ struct Cfg {
   static constexpr bool HI_C = !(BF && C == 16);
   // consumer waves: NCW waves, each owning ET 16-column tiles of the 64-wide value slice
   // (two tiles per wave share every Qt/Kt operand fragment when the state fits)
-#ifdef FLA_FORCE_NCW
-  static constexpr int NCW = FLA_FORCE_NCW;
-#else
   // the per-key gate's producers are VALU-heavy: give two SIMDs to producers alone (the
   // per-token gate scans one column and runs faster with four consumer waves)
   static constexpr int NCW = (DECAY == DECAY_GATE && DK <= 128) ? 2 : 4;
-#endif
   static constexpr int ET = 4 / NCW;
   static constexpr int NT = 64 * (NCW + 4);     // + 4 producer waves
   // keep the Kt fragments of earlier row blocks in registers (unrolled row-block loop)
-#ifdef FLA_FORCE_KCACHE
-  static constexpr bool KCACHE = FLA_FORCE_KCACHE;
-#else
   static constexpr bool KCACHE = DK <= 128 && C <= 64 && ET == 1;
-#endif
   // producer mapping for q/k/gate: wave p owns columns [p W, (p+1) W); a lane owns G
   // consecutive columns and RPT consecutive rows; LPR lanes share a row.
   static constexpr int W = DK / 4;
-#ifdef FLA_FORCE_G
-  static constexpr int G = W >= FLA_FORCE_G ? FLA_FORCE_G : W;
-#else
   static constexpr int G = W >= 8 ? 8 : W;
-#endif
   static constexpr int LPR = W / G;
   static constexpr int RP = 64 / LPR;
   static constexpr int RPT = C >= RP ? C / RP : 1;
@@ -133,11 +121,7 @@ struct Cfg {
   static constexpr int GS = DECAY == DECAY_TOKEN ? 1 : G;
   static constexpr int STAGE_WORDS = 2 * RPT * G * ES / 4 + (GATED ? RPT * GS : 0) +
                                      RPTV * 8 * ES / 4;
-#ifdef FLA_FORCE_PF
-  static constexpr int PF_BASE = FLA_FORCE_PF;
-#else
   static constexpr int PF_BASE = (STAGE_WORDS <= 64 && C <= 64 && !NORM) ? 2 : 1;
-#endif
   // Score tiles shared through LDS: the masked score tiles of a chunk are computed once,
   // split over the consumer waves, into an LDS buffer that every wave reads for O += A V.
   // Tile (ib, jb), jb <= ib, is number ib (ib + 1) / 2 + jb; when the slots outnumber the
@@ -167,14 +151,9 @@ struct Cfg {
   //    Qt during phase 2;
   //  otherwise the per-wave schedule: two stages (one where two do not fit), each consumer
   //    wave computing the score tiles it needs itself.
-#ifdef FLA_FORCE_SHARE
-  static constexpr bool SHARE_OK = FLA_FORCE_SHARE != 0;
-#else
-  static constexpr bool SHARE_OK = true;
-#endif
   static constexpr bool SHARE =
-      SHARE_OK && 3 * stage_bytes(LV_W) + 2 * PBUF_BYTES + PW_BYTES <= kMaxLds;
-  static constexpr bool SPLIT = SHARE_OK && !SHARE && split_bytes(LV_T) <= kMaxLds;
+      3 * stage_bytes(LV_W) + 2 * PBUF_BYTES + PW_BYTES <= kMaxLds;
+  static constexpr bool SPLIT = !SHARE && split_bytes(LV_T) <= kMaxLds;
   static constexpr int LV = (SPLIT && split_bytes(LV_W) > kMaxLds) ? LV_T : LV_W;
   static constexpr int PF = SPLIT ? 1 : PF_BASE; // chunks the producers load ahead
   // split schedule without a gate: Qt = phi(q) is formed when the Qt tile is free, from
@@ -214,18 +193,10 @@ struct Cfg {
   // score tiles by row-block pairs: consumer wave w computes every tile of row blocks w and
   // NB-1-w (NB + 1 tiles, the same for every wave), each Qt row block and Kt column block
   // read once (code specialised per wave)
-#ifdef FLA_FORCE_PAIRS
-  static constexpr bool PAIRS = FLA_FORCE_PAIRS && NB == 2 * NCW;
-#else
   static constexpr bool PAIRS = SPLIT && NB == 2 * NCW;
-#endif
   // scheduling fences in the shared-score consumer: between row blocks and before the
   // next chunk's score tiles (needed to stay within the registers with two tiles a wave)
-#ifdef FLA_FORCE_FENCE
-  static constexpr int FENCE = FLA_FORCE_FENCE;
-#else
   static constexpr int FENCE = ET >= 2 ? 3 : 1; // bit 0: row blocks, bit 1: scores
-#endif
   __device__ static constexpr int state_row(int cb, int g, int r) {
     return PERM ? 32 * (cb >> 1) + 8 * g + 4 * (cb & 1) + r : 16 * cb + 4 * g + r;
   }

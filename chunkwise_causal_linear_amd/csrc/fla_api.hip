@@ -27,6 +27,12 @@ constexpr int64_t kMaxGrid = (int64_t)1 << 31;
 
 bool is_pow2_dim(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
 bool is_chunk(int64_t c) { return c == 16 || c == 32 || c == 64 || c == 128; }
+// Chunk sizes a call accepts: the tile sizes above, and larger powers of two up to 1024
+// (the FLA posts advise chunk_size = 512 for long-sequence training), which are evaluated
+// as consecutive 128-token sub-chunks (64 where a 128-token tile does not fit in LDS).
+// Splitting a chunk into sub-chunks is exact in real arithmetic (the state after a
+// sub-chunk is the state before the next), so only the rounding differs.
+bool is_chunk_arg(int64_t c) { return is_chunk(c) || c == 256 || c == 512 || c == 1024; }
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 ChunkLauncher find_launcher(bool bf16, int64_t dk, int64_t chunk, int decay, bool norm) {
@@ -257,12 +263,34 @@ const float *nonnull_decay_if_empty(const float *decay, int64_t T, uint32_t flag
   return decay;
 }
 
+// Device memory the forward pass needs beyond its inputs and outputs: stream-ordered
+// allocations (hipMallocAsync / hipFreeAsync on the call's stream).
+struct Workspace {
+  hipStream_t s = nullptr;
+  void *owned[4] = {};
+  int nowned = 0;
+
+  int get(int64_t bytes, void **p) {
+    if (nowned == 4 || hipMallocAsync(p, (size_t)bytes, s) != hipSuccess) return FLA_ERR_DEVICE;
+    owned[nowned++] = *p;
+    return FLA_OK;
+  }
+  // frees the stream-ordered allocations (after the launches that use them are enqueued)
+  int release() {
+    int rc = FLA_OK;
+    for (int i = 0; i < nowned; ++i)
+      if (hipFreeAsync(owned[i], s) != hipSuccess) rc = FLA_ERR_DEVICE;
+    nowned = 0;
+    return rc;
+  }
+};
+
 // cu_seqlens: packed sequences (token-major layout, B = number of sequences, T = total
-// tokens); null for B sequences of T tokens each.
+// tokens); null for B sequences of T tokens each.  ws: where workspaces come from.
 int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_gamma,
              const float *init_state, void *out, float *final_state, int64_t B, int64_t H,
              int64_t T, int64_t dk, int64_t dv, int64_t chunk, uint32_t flags,
-             int64_t n_segments, const int64_t *cu_seqlens, void *stream) {
+             int64_t n_segments, const int64_t *cu_seqlens, Workspace &ws) {
   gate_or_gamma = nonnull_decay_if_empty(gate_or_gamma, T, flags);
   int rc = check_common(B, H, dk, dv, flags, gate_or_gamma);
   if (rc != FLA_OK) return rc;
@@ -273,14 +301,18 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
       !aligned(init_state, 16) || !aligned(final_state, 16))
     return FLA_ERR_INVALID_ARG;
-  if (!is_chunk(chunk)) return FLA_ERR_UNSUPPORTED;
+  if (!is_chunk_arg(chunk)) return FLA_ERR_UNSUPPORTED;
   if (B * H > ((int64_t)1 << 26) || T > ((int64_t)1 << 40) / (B * H)) return FLA_ERR_INVALID_ARG;
   const bool bf16 = (flags & FLA_BF16) != 0;
   const bool norm = (flags & FLA_NORMALIZE) != 0;
   const int kind = decay_kind(flags);
-  const ChunkLauncher launch = find_launcher(bf16, dk, chunk, kind, norm);
+  ChunkLauncher launch = find_launcher(bf16, dk, chunk > 128 ? 128 : chunk, kind, norm);
+  if (chunk > 128) {
+    if (launch) chunk = 128;
+    else if ((launch = find_launcher(bf16, dk, 64, kind, norm)) != nullptr) chunk = 64;
+  }
   if (!launch) return FLA_ERR_UNSUPPORTED;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t s = ws.s;
   const int64_t ncol = dv + (norm ? 1 : 0);
   const int64_t nbh = B * H;
   const int64_t state_elems = nbh * dk * ncol;
@@ -294,6 +326,8 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   int64_t nseg = n_segments == 0 ? auto_segments(B, H, T, dv, chunk) : n_segments;
   if (cu_seqlens) nseg = 1; // packed sequences: one streaming workgroup per (sequence, head, slice)
   if (nseg > nch) nseg = nch;
+  // segment workspace: every segment's end state and decay product
+  auto seg_ws_bytes = [&](int64_t p) { return nbh * p * dk * (ncol + 1) * (int64_t)sizeof(float); };
   const int64_t seg_chunks = (nch + nseg - 1) / nseg;
   const int64_t seg_len = seg_chunks * chunk;
   nseg = (T + seg_len - 1) / seg_len;
@@ -317,32 +351,32 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   if (nseg == 1) {
     // The z column is read by every value slice and written by slice 0 only: an in-place
     // resume with several slices reads a private copy of the start state.
-    float *tmp = nullptr;
     const float *ini = init_state;
     if (init_state && init_state == final_state && norm && nvs > 1) {
-      if (hipMallocAsync(reinterpret_cast<void **>(&tmp), state_elems * sizeof(float), s) != hipSuccess)
-        return FLA_ERR_DEVICE;
-      if (launch_fill(tmp, init_state, state_elems, s) != FLA_OK) {
-        (void)hipFreeAsync(tmp, s);
-        return FLA_ERR_DEVICE;
+      void *tmp = nullptr;
+      if ((rc = ws.get(state_elems * (int64_t)sizeof(float), &tmp)) != FLA_OK) return rc;
+      if ((rc = launch_fill(static_cast<float *>(tmp), init_state, state_elems, s)) != FLA_OK) {
+        ws.release();
+        return rc;
       }
-      ini = tmp;
+      ini = static_cast<const float *>(tmp);
     }
     // packed sequences: dispatch the longest first (the short ones fill in behind them)
     int *order = nullptr;
     if (cu_seqlens && B >= 2 && B <= kOrderMax) {
-      if (hipMallocAsync(reinterpret_cast<void **>(&order), B * sizeof(int), s) != hipSuccess) {
-        if (tmp) (void)hipFreeAsync(tmp, s);
-        return FLA_ERR_DEVICE;
+      void *o = nullptr;
+      if ((rc = ws.get(B * (int64_t)sizeof(int), &o)) != FLA_OK) {
+        ws.release();
+        return rc;
       }
+      order = static_cast<int *>(o);
       int n_i = (int)B;
       int64_t T_v = T, chunk_v = chunk;
       void *oargs[] = {&cu_seqlens, &n_i, &T_v, &chunk_v, &order};
       if (hipLaunchKernel(reinterpret_cast<const void *>(&seq_order_kernel),
                           dim3(blocks_for(B, kOrderThreads)), dim3(kOrderThreads), oargs, 0, s) !=
           hipSuccess) {
-        (void)hipFreeAsync(order, s);
-        if (tmp) (void)hipFreeAsync(tmp, s);
+        ws.release();
         return FLA_ERR_DEVICE;
       }
     }
@@ -356,24 +390,22 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
     a.seg_decay = nullptr;
     a.state_only = 0;
     rc = launch(a, (unsigned)grid, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
-    if (order && hipFreeAsync(order, s) != hipSuccess) rc = FLA_ERR_DEVICE;
-    if (tmp && hipFreeAsync(tmp, s) != hipSuccess) rc = FLA_ERR_DEVICE;
-    return rc;
+    const int rr = ws.release();
+    return rc != FLA_OK ? rc : rr;
   }
 
   // Segment schedule: (A) end state of every segment from a zero start, (B) scan over
   // segments, (C) outputs of every segment from its start state.
   const int64_t ws_states = nbh * nseg * dk * ncol;
-  const int64_t ws_dec = nbh * nseg * dk;
-  float *ws = nullptr;
-  if (hipMallocAsync(reinterpret_cast<void **>(&ws), (ws_states + ws_dec) * sizeof(float), s) != hipSuccess)
-    return FLA_ERR_DEVICE;
-  float *wdec = ws + ws_states;
+  void *wsp = nullptr;
+  if ((rc = ws.get(seg_ws_bytes(nseg), &wsp)) != FLA_OK) return rc;
+  float *wst = static_cast<float *>(wsp);
+  float *wdec = wst + ws_states;
 
   a.init = nullptr;
   a.init_bh_stride = 0;
   a.init_seg_stride = 0;
-  a.fin = ws;
+  a.fin = wst;
   a.fin_bh_stride = nseg * dk * ncol;
   a.fin_seg_stride = dk * ncol;
   a.seg_decay = wdec;
@@ -386,13 +418,13 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
     const float *ini = init_state;
     float *fin = final_state;
     int64_t nbh_v = nbh;
-    void *args[] = {&ws, &wdec, &ini, &fin, &nbh_v, &nseg_i, &dk_i, &ncol_i};
+    void *args[] = {&wst, &wdec, &ini, &fin, &nbh_v, &nseg_i, &dk_i, &ncol_i};
     if (hipLaunchKernel(reinterpret_cast<const void *>(&segment_scan_kernel),
                         dim3(blocks_for(n, kScanThreads)), dim3(kScanThreads), args, 0, s) != hipSuccess)
       rc = FLA_ERR_DEVICE;
   }
   if (rc == FLA_OK) {
-    a.init = ws;
+    a.init = wst;
     a.init_bh_stride = nseg * dk * ncol;
     a.init_seg_stride = dk * ncol;
     a.fin = nullptr;
@@ -400,8 +432,8 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
     a.state_only = 0;
     rc = launch(a, (unsigned)grid, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
   }
-  if (hipFreeAsync(ws, s) != hipSuccess) rc = FLA_ERR_DEVICE;
-  return rc;
+  const int rr = ws.release();
+  return rc != FLA_OK ? rc : rr;
 }
 
 int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_gamma,
@@ -425,7 +457,9 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   if (flags & FLA_NORMALIZE) return FLA_ERR_UNSUPPORTED;
   const bool bthd = cu_seqlens != nullptr || (flags & FLA_LAYOUT_BTHD) != 0;
   if (bthd && H * (dk > dv ? dk : dv) > ((int64_t)1 << 20)) return FLA_ERR_UNSUPPORTED;
-  if (chunk != 64) return FLA_ERR_UNSUPPORTED;
+  // the backward tiles by 64 tokens whatever chunk the forward pass used (same function)
+  if (!is_chunk_arg(chunk)) return FLA_ERR_UNSUPPORTED;
+  chunk = 64;
   if (dk < 64 || dv < 64) return FLA_ERR_UNSUPPORTED;
   if (B * H > ((int64_t)1 << 26) || T > ((int64_t)1 << 40) / (B * H)) return FLA_ERR_INVALID_ARG;
   const bool bf16 = (flags & FLA_BF16) != 0;
@@ -513,7 +547,8 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
       !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(alpha, 4) ||
       !aligned(beta, 4))
     return FLA_ERR_INVALID_ARG;
-  if (chunk != 64) return FLA_ERR_UNSUPPORTED;
+  // 64-token tiles for any accepted chunk size (the chunking does not change the function)
+  if (!is_chunk_arg(chunk)) return FLA_ERR_UNSUPPORTED;
   if (dv % kSlice != 0 || dv > 256) return FLA_ERR_UNSUPPORTED;
   if (B * H > ((int64_t)1 << 26) || T > ((int64_t)1 << 40) / (B * H)) return FLA_ERR_INVALID_ARG;
   const bool bf16 = (flags & FLA_BF16) != 0;
@@ -528,8 +563,8 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
   const int64_t nvs = dv / kSlice;
   const int64_t nch = (T + 63) / 64;
   if (nbh * nvs >= kMaxGrid || nbh * nch >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
-  // workspace: W = T diag(beta g) K^ per token and Tb = T diag(beta) per chunk (C x C),
-  // both in the input type (W's size is a multiple of 128 bytes, so Tb stays aligned)
+  // workspace: Tg = T diag(beta g) and Tb = T diag(beta) per chunk (C x C each), in the
+  // input type; Tg first, then Tb (its size is a multiple of 128 bytes, so Tb stays aligned)
   const int64_t tb_bytes = nbh * nch * 64 * 64 * (bf16 ? 2 : 4); // Tb, and as much for Tg
   char *ws = nullptr;
   if (hipMallocAsync(reinterpret_cast<void **>(&ws), 2 * tb_bytes, s) != hipSuccess)
@@ -602,8 +637,10 @@ int fla_linattn_fwd(const void *q, const void *k, const void *v, const float *ga
                     const float *init_state, void *out, float *final_state, int64_t B,
                     int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk,
                     uint32_t flags, void *stream) {
+  fla::Workspace ws;
+  ws.s = static_cast<hipStream_t>(stream);
   return fla::fwd_impl(q, k, v, gate_or_gamma, init_state, out, final_state, B, H, T, dk, dv,
-                       chunk, flags, 0, nullptr, stream);
+                       chunk, flags, 0, nullptr, ws);
 }
 
 int fla_linattn_fwd_varlen(const void *q, const void *k, const void *v, const float *gate_or_gamma,
@@ -611,8 +648,10 @@ int fla_linattn_fwd_varlen(const void *q, const void *k, const void *v, const fl
                            const int64_t *cu_seqlens, int64_t n_seqs, int64_t total_T, int64_t H,
                            int64_t dk, int64_t dv, int64_t chunk, uint32_t flags, void *stream) {
   if (!cu_seqlens || !fla::aligned(cu_seqlens, 8)) return FLA_ERR_INVALID_ARG;
+  fla::Workspace ws;
+  ws.s = static_cast<hipStream_t>(stream);
   return fla::fwd_impl(q, k, v, gate_or_gamma, init_state, out, final_state, n_seqs, H, total_T,
-                       dk, dv, chunk, flags | FLA_LAYOUT_BTHD, 0, cu_seqlens, stream);
+                       dk, dv, chunk, flags | FLA_LAYOUT_BTHD, 0, cu_seqlens, ws);
 }
 
 int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
@@ -620,8 +659,10 @@ int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
                              float *final_state, int64_t B, int64_t H, int64_t T, int64_t dk,
                              int64_t dv, int64_t chunk, uint32_t flags, int64_t n_segments,
                              void *stream) {
+  fla::Workspace ws;
+  ws.s = static_cast<hipStream_t>(stream);
   return fla::fwd_impl(q, k, v, gate_or_gamma, init_state, out, final_state, B, H, T, dk, dv,
-                       chunk, flags, n_segments, nullptr, stream);
+                       chunk, flags, n_segments, nullptr, ws);
 }
 
 int fla_linattn_segments_for(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
@@ -631,7 +672,11 @@ int fla_linattn_segments_for(int64_t B, int64_t H, int64_t T, int64_t dk, int64_
   static const float dummy[4] = {0.f, 0.f, 0.f, 0.f};
   int rc = fla::check_common(B, H, dk, dv, flags, has_decay ? dummy : nullptr);
   if (rc != FLA_OK) return rc;
-  if (!fla::is_chunk(chunk)) return FLA_ERR_UNSUPPORTED;
+  if (!fla::is_chunk_arg(chunk)) return FLA_ERR_UNSUPPORTED;
+  if (chunk > 128) {
+    const bool norm = (flags & FLA_NORMALIZE) != 0;
+    chunk = fla::find_launcher((flags & FLA_BF16) != 0, dk, 128, fla::decay_kind(flags), norm) ? 128 : 64;
+  }
   const int64_t nch = (T + chunk - 1) / chunk;
   int64_t p = T == 0 ? 1 : fla::auto_segments(B, H, T, dv, chunk);
   if (p > nch && nch > 0) p = nch;

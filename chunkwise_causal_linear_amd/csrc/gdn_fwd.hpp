@@ -46,10 +46,10 @@ struct GdnCfg {
   static constexpr int ES = sizeof(TIn);
   static constexpr int VE = 16 / ES;
   static constexpr int KU = ES == 2 ? 32 : 16;
-  static constexpr int LDK = DK + VE;  // Q, K^, W rows
+  static constexpr int LDK = DK + VE;  // Q, K^ rows
   static constexpr int LDV = XW + VE;  // V, U, Us rows
   static constexpr int LDT = C + VE;   // Tb, Tg rows
-  static constexpr int NVQ = C * DK / VE / NT;  // 16-byte vectors per thread (q, k, W)
+  static constexpr int NVQ = C * DK / VE / NT;  // 16-byte vectors per thread (q, k)
   static constexpr int NVV = C * XW / VE / NT;  // (v slice)
   static constexpr int VPRQ = DK / VE;          // vectors per q/k row
   static constexpr int NCB = DK / 16;           // 16-row blocks of the state
@@ -163,7 +163,7 @@ __device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const float
 
 } // namespace gdn
 
-// ---- pre-pass: W and Tb of one chunk ---------------------------------------------------
+// ---- pre-pass: Tb and Tg of one chunk ---------------------------------------------------
 template <typename TIn, int DK>
 __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   using K = GdnCfg<TIn, DK>;
@@ -341,9 +341,11 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
 }
 
 // ---- state pass ---------------------------------------------------------------------------
-// 8 waves: waves 4..7 (producers) load q, k and W of chunk n+1 into registers, normalise k
-// and write them, with the chunk's decay, into one LDS stage while waves 0..3 (consumers)
-// compute chunk n from the other stage; two barriers per chunk.
+// 8 waves: waves 4..7 (producers) load q and k of chunk n+1 into registers, normalise k
+// and write them, with the chunk's decay, into one LDS stage, and after the mid-chunk
+// barrier stage Tb, Tg and the value slice of the chunk the consumers take next, while
+// waves 0..3 (consumers) compute chunk n (scores, X = K^ H, U = Tb V - Tg X, outputs, state
+// update) from the other stage; two barriers per chunk.
 template <typename TIn, int DK>
 __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
   using K = GdnCfg<TIn, DK>;

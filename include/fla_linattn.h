@@ -66,6 +66,10 @@ enum fla_status {
 
 /*
  * fla_linattn_fwd — chunkwise forward pass over T tokens.
+ * Defined by the token recurrence above (textbook chapter 1.6, "linear attention": the
+ * state update and read-out, trained "in parallel or in chunks"), evaluated in chunk mode
+ * (the FLA posts' chunk-mode forward; chapter 1.6, "state-space models and Mamba": linear
+ * attention with a decay mask, trained in matmul-friendly chunks).
  *
  *   q, k, v, out : see layouts above; 16-byte aligned.  May be NULL only when T == 0.
  *   gate_or_gamma: gamma [H] with FLA_DECAY_GAMMA (4-byte aligned), gate [B][H][T][dk]
@@ -74,7 +78,11 @@ enum fla_status {
  *   init_state   : [B][H][dk][dv+n] fp32, or NULL for a zero initial state (16-byte aligned).
  *   final_state  : [B][H][dk][dv+n] fp32 written with the state after token T-1, or NULL.
  *                  May alias init_state (in-place resume).
- *   B, H >= 1; T >= 0; dk, dv in {16, 32, 64, 128, 256}; chunk in {16, 32, 64, 128}.
+ *   B, H >= 1; T >= 0; dk, dv in {16, 32, 64, 128, 256}; chunk in {16, 32, 64, 128,
+ *                  256, 512, 1024}: the tile sizes are 16..128; a larger chunk (the FLA
+ *                  posts advise chunk_size = 512 for long-sequence training) is evaluated
+ *                  as consecutive 128-token sub-chunks (64 where a 128-token tile does not
+ *                  fit), which is exact in real arithmetic.
  *   flags        : FLA_* bits; at most one decay bit.
  *   stream       : hipStream_t or NULL.
  *
@@ -93,6 +101,9 @@ int fla_linattn_fwd(const void *q, const void *k, const void *v, const float *ga
 
 /*
  * fla_linattn_fwd_segments — fla_linattn_fwd with an explicit choice of schedule.
+ * The segment schedule splits the sequence like the context parallelism textbook chapter
+ * 1.6 mentions for long contexts, with the recurrence's state as the only thing carried
+ * between pieces (end state from zero, then a scan of the pieces' decays and end states).
  *   n_segments == 0: automatic (same as fla_linattn_fwd).
  *   n_segments == 1: one workgroup per (b, h, 64-wide value slice) streams all chunks.
  *   n_segments  > 1: the sequence is cut into that many segments of whole chunks; the
@@ -108,7 +119,9 @@ int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
                              void *stream);
 
 /*
- * fla_linattn_fwd_varlen — fla_linattn_fwd over packed variable-length sequences.
+ * fla_linattn_fwd_varlen — fla_linattn_fwd over packed variable-length sequences (the
+ * Triton fused-kernel post recommends chunk mode for variable-length input; the FLA
+ * guide's layers take [B][T][hidden] activations, hence the token-major layout).
  *   q, k, gate: [total_T][H][dk]; v, out: [total_T][H][dv]; per-token decay [total_T][H]
  *   (token-major, FLA_LAYOUT_BTHD implied); sequence s owns tokens cu_seqlens[s] ..
  *   cu_seqlens[s+1]-1.
@@ -129,7 +142,9 @@ int fla_linattn_fwd_varlen(const void *q, const void *k, const void *v, const fl
 
 /*
  * fla_linattn_step — one token of recurrent decoding (the T == 1 case of the forward
- * pass), updating the state in place.
+ * pass), updating the state in place: the recurrent form of textbook chapter 1.6, "linear
+ * attention" (constant memory per generated token, as the chapter contrasts with a
+ * growing KV cache).
  *   q, k : [B][H][dk]; v, out: [B][H][dv] (bf16 with FLA_BF16, else fp32); 16-byte aligned.
  *   gate_or_gamma: gamma [H], gate [B][H][dk] or token [B][H] per the decay bit, else NULL.
  *   state: fp32 [B][H][dk][dv+n], read and written (required).
@@ -143,7 +158,8 @@ int fla_linattn_step(const void *q, const void *k, const void *v, const float *g
 /*
  * fla_linattn_bwd — gradients of the forward pass (chunkwise backward), for the loss
  * L = sum(dout (.) out) + sum(dfinal_state (.) final_state), by the reverse-mode chain rule
- * through the recurrence above (no normaliser).
+ * through the recurrence above (no normaliser).  The FLA posts time chunk mode forward
+ * and backward together for training; this is the backward half.
  *
  *   q, k, v, gate_or_gamma, init_state: the forward call's inputs (layouts above, including
  *                  token-major [B][T][H][d] with FLA_LAYOUT_BTHD).
@@ -157,7 +173,8 @@ int fla_linattn_step(const void *q, const void *k, const void *v, const float *g
  *   dinit_state  : fp32 [B][H][dk][dv] written with the gradient of init_state (whether or
  *                  not init_state was given), or NULL.
  *   All pointers 16-byte aligned, except gamma and the per-token decay (4 bytes).
- *   dk, dv in {64, 128, 256} (fp32: up to 128); chunk = 64; FLA_NORMALIZE is not supported;
+ *   dk, dv in {64, 128, 256} (fp32: up to 128); chunk: any value the forward call takes
+ *   (the backward always tiles by 64 tokens, the same function); FLA_NORMALIZE is not supported;
  *   token-major: H * max(dk, dv) <= 2^20.
  *   Three chunk-scan launches (dq forward in time; dv, then dk and dgate in reverse) and,
  *   when dgate is requested, a stream-ordered workspace of 4 (B H T dk + B H dk) bytes
@@ -198,7 +215,8 @@ int fla_linattn_bwd_varlen(const void *q, const void *k, const void *v, const fl
  *   alpha : fp32 [B][H][T], the decay in (0, 1] (each chunk's product of alpha must stay
  *           above ~1e-30); beta: fp32 [B][H][T], the write strength in [0, 1]; 4-byte aligned.
  *   init_state, final_state: fp32 [B][H][dk][dv] (h = S^T as above) or NULL; may alias.
- *   dk in {64, 128} (fp32: 64); dv in {64, 128, 256}; chunk = 64; flags: FLA_BF16 only.
+ *   dk in {64, 128} (fp32: 64); dv in {64, 128, 256}; chunk: any value fla_linattn_fwd
+ *   takes (64-token tiles are used for all of them); flags: FLA_BF16 only.
  * Two launches: a pre-pass forms, for every chunk at once, the parts that do not depend on
  * the state (Tb = T diag(beta) and Tg = T diag(beta g) with T the inverse of the chunk's
  * unit lower-triangular delta system), into a stream-ordered workspace of
@@ -214,7 +232,8 @@ const char *fla_status_string(int status);
 
 /*
  * fla_linattn_segments_for — the segment count fla_linattn_fwd would choose for a shape
- * (1 = single streaming launch).  Returns a status; *n_segments is set on FLA_OK.
+ * (1 = single streaming launch; the schedule of fla_linattn_fwd_segments).  Returns a
+ * status; *n_segments is set on FLA_OK.
  */
 int fla_linattn_segments_for(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                              int64_t chunk, uint32_t flags, int64_t *n_segments);

@@ -8,7 +8,7 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fla_linattn.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 torch = pytest.importorskip("torch")
 import chunkwise_causal_linear_amd as fla  # noqa: E402
@@ -18,8 +18,14 @@ MISALIGNED = ctypes.c_void_p((1 << 20) + 2)
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(fla_\w+)\s*\(", text, re.M)))
+    """Every function declared by the public headers (include/*.h)."""
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE, h)).read()
+            names |= set(re.findall(r"^\s*(?:int|double|const char \*)\s*(fla_\w+)\s*\(",
+                                    text, re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -78,7 +84,8 @@ def fwd_raw(lib, *, q=BOGUS, k=BOGUS, v=BOGUS, gate=None, init=None, out=BOGUS, 
     (dict(flags=fla.FLA_DECAY_GATE, gate=MISALIGNED), fla.FLA_ERR_INVALID_ARG),
     (dict(dk=48), fla.FLA_ERR_UNSUPPORTED),
     (dict(dv=512), fla.FLA_ERR_UNSUPPORTED),
-    (dict(chunk=512), fla.FLA_ERR_UNSUPPORTED),
+    (dict(chunk=2048), fla.FLA_ERR_UNSUPPORTED),
+    (dict(chunk=96), fla.FLA_ERR_UNSUPPORTED),
     (dict(chunk=8), fla.FLA_ERR_UNSUPPORTED),
     (dict(dk=256, chunk=128), fla.FLA_ERR_UNSUPPORTED),                      # fp32 tiles > LDS
     (dict(dk=128, chunk=128), fla.FLA_ERR_UNSUPPORTED),                      # fp32 tiles > LDS
@@ -120,7 +127,8 @@ def bwd_raw(lib, *, q=BOGUS, k=BOGUS, v=BOGUS, gate=None, init=None, do=BOGUS, d
 
 @pytest.mark.parametrize("kw,expected", [
     (dict(flags=fla.FLA_NORMALIZE), fla.FLA_ERR_UNSUPPORTED),
-    (dict(chunk=32), fla.FLA_ERR_UNSUPPORTED),
+    (dict(chunk=48), fla.FLA_ERR_UNSUPPORTED),
+    (dict(chunk=2048), fla.FLA_ERR_UNSUPPORTED),
     (dict(dkd=32), fla.FLA_ERR_UNSUPPORTED),
     (dict(dvd=16), fla.FLA_ERR_UNSUPPORTED),
     (dict(dkd=256), fla.FLA_ERR_UNSUPPORTED),                      # fp32 tiles > LDS
@@ -170,6 +178,11 @@ def test_schedule_choice(lib):
     assert fla.segments_for(1, 8, 1 << 20, 128, 128, 128, fla.FLA_BF16 | fla.FLA_DECAY_GAMMA) == 64
     # too short to cut
     assert fla.segments_for(1, 1, 256, 64, 64, 64, fla.FLA_PHI_ELU1 | fla.FLA_NORMALIZE) == 1
+    # chunk sizes above 128 run as 128-token sub-chunks: the same schedule as chunk 128
+    f = fla.FLA_BF16 | fla.FLA_DECAY_GAMMA
+    for c in (256, 512, 1024):
+        assert fla.segments_for(1, 8, 1 << 20, 128, 128, c, f) == \
+            fla.segments_for(1, 8, 1 << 20, 128, 128, 128, f)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
@@ -193,8 +206,30 @@ def test_gdn_rejects_on_host(lib):
     assert gdn(be=ctypes.c_void_p((1 << 20) + 2)) == fla.FLA_ERR_INVALID_ARG
     assert gdn(q=MISALIGNED) == fla.FLA_ERR_INVALID_ARG
     assert gdn(T=-1) == fla.FLA_ERR_INVALID_ARG
-    assert gdn(chunk=32) == fla.FLA_ERR_UNSUPPORTED
+    assert gdn(chunk=48) == fla.FLA_ERR_UNSUPPORTED
+    assert gdn(chunk=2048) == fla.FLA_ERR_UNSUPPORTED
     assert gdn(dk=32) == fla.FLA_ERR_UNSUPPORTED
     assert gdn(dv=96) == fla.FLA_ERR_UNSUPPORTED
     assert gdn(dk=256) == fla.FLA_ERR_UNSUPPORTED
     assert gdn(dk=128) == fla.FLA_ERR_UNSUPPORTED                     # fp32 dk = 128
+
+
+def test_binding_rejects_strided_and_mistyped_tensors():
+    # checked in Python before the library is called, so CPU tensors suffice
+    q = torch.zeros(2, 3, 5, 64, dtype=torch.bfloat16)
+    state = torch.zeros(2, 3, 64, 64, dtype=torch.float32)
+    step_q = q[:, :, 1]                      # the usual decode slice: strided, 16-byte aligned
+    assert not step_q.is_contiguous()
+    with pytest.raises(ValueError, match="contiguous"):
+        fla.step(step_q, step_q.contiguous(), step_q.contiguous(), state)
+    with pytest.raises(ValueError, match="contiguous"):
+        fla.fwd(q, q, q.transpose(2, 3)[..., :5, :].transpose(2, 3), None)
+    qc = step_q.contiguous()
+    with pytest.raises(ValueError, match="dtype"):
+        fla.step(qc, qc.float(), qc, state)
+    with pytest.raises(ValueError, match="float32"):
+        fla.step(qc, qc, qc, state.double())
+    with pytest.raises(ValueError, match="float32"):
+        fla.fwd(q, q, q, torch.ones(2, 3, 5, 64, dtype=torch.bfloat16), decay_kind="gate")
+    with pytest.raises(ValueError, match="GPU"):
+        fla.step(qc, qc, qc, state)

@@ -149,7 +149,7 @@ def test_bwd_rejects():
     q = torch.zeros((1, 1, 64, 64), device="cuda")
     gam = torch.full((1,), 0.9, device="cuda")
     with pytest.raises(fla.FlaError) as e:
-        fla.bwd(q, q, q, q, chunk=32)
+        fla.bwd(q, q, q, q, chunk=48)
     assert e.value.status == fla.FLA_ERR_UNSUPPORTED
     q32 = torch.zeros((1, 1, 64, 32), device="cuda")
     with pytest.raises(fla.FlaError) as e:

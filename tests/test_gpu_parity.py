@@ -276,3 +276,19 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(libs) == 1, libs
+
+
+@pytest.mark.parametrize("dtype,decay,chunk", [("bf16", "gate", 256), ("bf16", "gamma", 512),
+                                               ("f32", "token", 256), ("f32", "none", 512),
+                                               ("bf16", "gate", 1024)])
+def test_chunk_above_128(dtype, decay, chunk):
+    """chunk_size = 512 as the FLA posts advise (and 256, 1024): accepted, evaluated as
+    128-token sub-chunks (64 where a 128-token tile does not fit); against the oracle, and
+    bitwise equal to the call with the tile size it runs."""
+    norm = decay == "none"
+    w, inp = small_case(dtype, decay, 64, 64, 2 * chunk + 77, B=1, H=2, chunk=chunk, phi=norm,
+                        norm=norm, init=True, seed=chunk + len(decay))
+    check(w, inp, f"chunk {chunk} {dtype} {decay}")
+    o, f = run_gpu(w, inp)
+    o128, f128 = run_gpu(w, inp, chunk=128)
+    assert np.array_equal(o, o128) and np.array_equal(f, f128)
