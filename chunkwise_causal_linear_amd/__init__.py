@@ -20,7 +20,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libfla_linattn.so")
 
-FLA_OK, FLA_ERR_INVALID_ARG, FLA_ERR_UNSUPPORTED, FLA_ERR_DEVICE = 0, -1, -2, -3
+FLA_OK, FLA_ERR_INVALID_ARG, FLA_ERR_UNSUPPORTED, FLA_ERR_DEVICE, FLA_ERR_SCRATCH = 0, -1, -2, -3, -4
 FLA_BF16 = 1 << 0
 FLA_DECAY_GAMMA = 1 << 1
 FLA_DECAY_GATE = 1 << 2
@@ -32,7 +32,8 @@ FLA_LAYOUT_BTHD = 1 << 6
 EXPORTED = ("fla_linattn_fwd", "fla_linattn_fwd_segments", "fla_linattn_step",
             "fla_status_string", "fla_linattn_segments_for", "fla_linattn_bwd",
             "fla_linattn_fwd_varlen", "fla_linattn_bwd_varlen", "fla_gdn_fwd",
-            "fla_probe_stream", "fla_probe_mfma", "fla_probe_mfma_flops")
+            "fla_probe_stream", "fla_probe_mfma", "fla_probe_mfma_flops",
+            "fla_linattn_fwd_noalloc")
 PROBE_READ, PROBE_COPY, PROBE_MIX5 = 0, 1, 2
 
 _lib = None
@@ -77,6 +78,9 @@ def load_library():
     lib.fla_linattn_bwd_varlen.restype = c_int
     lib.fla_gdn_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, u32, p]
     lib.fla_gdn_fwd.restype = c_int
+    lib.fla_linattn_fwd_noalloc.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64,
+                                            u32, p]
+    lib.fla_linattn_fwd_noalloc.restype = c_int
     lib.fla_probe_stream.argtypes = [p, p, i64, c_int, p]
     lib.fla_probe_stream.restype = c_int
     lib.fla_probe_mfma.argtypes = [p, i64, i64, p]
@@ -150,11 +154,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch
         out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
         want_final: bool = True, chunk: int = 64, phi_elu1: bool = False,
         normalize: bool = False, n_segments: Optional[int] = None, layout: str = "bhtd",
-        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        noalloc: bool = False, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise forward.  q, k [B,H,T,dk]; v [B,H,T,dv] (bf16 or fp32, on the GPU);
     decay: gamma [H], gate [B,H,T,dk] or per-token scalar [B,H,T] (fp32); init/final state
     fp32 [B,H,dk,dv(+1)].  layout="bthd": token-major q, k [B,T,H,dk], v and out
     [B,T,H,dv], gate [B,T,H,dk], per-token decay [B,T,H].
+    noalloc=True calls fla_linattn_fwd_noalloc (workspace from the library's static scratch
+    array; automatic segment count only).
     Returns (out, final_state)."""
     if layout == "bthd":
         B, T, H, dk = q.shape
@@ -175,7 +181,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch
     if layout == "bthd":
         flags |= FLA_LAYOUT_BTHD
     lib = load_library()
-    if n_segments is None:
+    if noalloc:
+        if n_segments is not None:
+            raise ValueError("the no-allocation entry point chooses the segment count itself")
+        rc = lib.fla_linattn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(decay),
+                                         _ptr(init_state), _ptr(out), _ptr(final_state), B, H,
+                                         T, dk, dv, chunk, flags, _stream(stream))
+    elif n_segments is None:
         rc = lib.fla_linattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(init_state),
                                  _ptr(out), _ptr(final_state), B, H, T, dk, dv, chunk, flags,
                                  _stream(stream))

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fla_linattn.h"
 #include "bwd_dispatch.hpp"
 #include "dispatch.hpp"
@@ -16,6 +18,13 @@ struct GdnLaunchers {
   GdnLauncher prep, state;
 };
 GdnLaunchers gdn_launchers(bool bf16, int dk); // gdn_inst.hip
+
+// Scratch memory of the no-allocation entry point: the segment schedule's workspace (and
+// the private start-state copy of an in-place resume) are carved out of this array instead
+// of stream-ordered allocations.  Every GPU the library runs on holds its own copy until
+// the process ends.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -263,14 +272,28 @@ const float *nonnull_decay_if_empty(const float *decay, int64_t T, uint32_t flag
   return decay;
 }
 
-// Device memory the forward pass needs beyond its inputs and outputs: stream-ordered
-// allocations (hipMallocAsync / hipFreeAsync on the call's stream).
+// Device memory the forward pass needs beyond its inputs and outputs.  Either
+// stream-ordered allocations (hipMallocAsync / hipFreeAsync on the call's stream), or
+// carved out of a caller-provided region (the no-allocation entry point's scratch array),
+// in which case a request that does not fit fails with FLA_ERR_SCRATCH and nothing is
+// allocated.
 struct Workspace {
+  char *base = nullptr; // scratch region, or null for stream-ordered allocations
+  int64_t cap = 0, used = 0;
   hipStream_t s = nullptr;
   void *owned[4] = {};
   int nowned = 0;
 
+  bool from_scratch() const { return base != nullptr; }
+  int64_t left() const { return cap - ((used + 255) & ~(int64_t)255); }
   int get(int64_t bytes, void **p) {
+    if (base) {
+      const int64_t off = (used + 255) & ~(int64_t)255;
+      if (bytes > cap - off) return FLA_ERR_SCRATCH;
+      *p = base + off;
+      used = off + bytes;
+      return FLA_OK;
+    }
     if (nowned == 4 || hipMallocAsync(p, (size_t)bytes, s) != hipSuccess) return FLA_ERR_DEVICE;
     owned[nowned++] = *p;
     return FLA_OK;
@@ -328,6 +351,10 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   if (nseg > nch) nseg = nch;
   // segment workspace: every segment's end state and decay product
   auto seg_ws_bytes = [&](int64_t p) { return nbh * p * dk * (ncol + 1) * (int64_t)sizeof(float); };
+  if (ws.from_scratch() && n_segments == 0) {
+    // the automatic count is cut down until its workspace fits the scratch region
+    while (nseg > 1 && seg_ws_bytes(nseg) > ws.left()) nseg = nseg / 2;
+  }
   const int64_t seg_chunks = (nch + nseg - 1) / nseg;
   const int64_t seg_len = seg_chunks * chunk;
   nseg = (T + seg_len - 1) / seg_len;
@@ -590,6 +617,25 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
   return rc;
 }
 
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device, looked up once per device with
+// that device current (the array's name in host code is only a host-side stand-in).
+int scratch_address(void **p) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FLA_ERR_DEVICE;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return FLA_ERR_DEVICE;
+    addr[dev] = a;
+  }
+  *p = addr[dev];
+  return FLA_OK;
+}
+
 } // namespace
 } // namespace fla
 
@@ -629,6 +675,7 @@ const char *fla_status_string(int status) {
   case FLA_ERR_INVALID_ARG: return "invalid argument";
   case FLA_ERR_UNSUPPORTED: return "unsupported shape or option";
   case FLA_ERR_DEVICE: return "device launch or allocation failed";
+  case FLA_ERR_SCRATCH: return "request needs more than the no-allocation entry point's scratch";
   default: return "unknown status";
   }
 }
@@ -639,6 +686,21 @@ int fla_linattn_fwd(const void *q, const void *k, const void *v, const float *ga
                     uint32_t flags, void *stream) {
   fla::Workspace ws;
   ws.s = static_cast<hipStream_t>(stream);
+  return fla::fwd_impl(q, k, v, gate_or_gamma, init_state, out, final_state, B, H, T, dk, dv,
+                       chunk, flags, 0, nullptr, ws);
+}
+
+int fla_linattn_fwd_noalloc(const void *q, const void *k, const void *v,
+                            const float *gate_or_gamma, const float *init_state, void *out,
+                            float *final_state, int64_t B, int64_t H, int64_t T, int64_t dk,
+                            int64_t dv, int64_t chunk, uint32_t flags, void *stream) {
+  fla::Workspace ws;
+  ws.s = static_cast<hipStream_t>(stream);
+  void *base = nullptr;
+  const int rc = fla::scratch_address(&base);
+  if (rc != FLA_OK) return rc;
+  ws.base = static_cast<char *>(base);
+  ws.cap = fla::kScratchBytes;
   return fla::fwd_impl(q, k, v, gate_or_gamma, init_state, out, final_state, B, H, T, dk, dv,
                        chunk, flags, 0, nullptr, ws);
 }

@@ -49,7 +49,8 @@ enum fla_status {
   FLA_OK = 0,
   FLA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad or conflicting flags */
   FLA_ERR_UNSUPPORTED = -2, /* valid request outside the built shape set */
-  FLA_ERR_DEVICE = -3       /* a HIP launch or stream-ordered allocation failed */
+  FLA_ERR_DEVICE = -3,      /* a HIP launch or stream-ordered allocation failed */
+  FLA_ERR_SCRATCH = -4      /* the no-allocation entry point's scratch array is too small */
 };
 
 /* Flag bits. */
@@ -117,6 +118,28 @@ int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
                              float *final_state, int64_t B, int64_t H, int64_t T, int64_t dk,
                              int64_t dv, int64_t chunk, uint32_t flags, int64_t n_segments,
                              void *stream);
+
+/*
+ * fla_linattn_fwd_noalloc — fla_linattn_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, layouts, validation and results as fla_linattn_fwd; it calls no
+ * hipMalloc / hipMallocAsync / hipFree and no allocating library routine.
+ *   The one workspace the forward pass needs (the segment schedule's per-segment end
+ *   states and decay products, and the private start-state copy of an in-place resume
+ *   with the normaliser) comes from a static device array of 64 MiB that each GPU the
+ *   library runs on holds until the process ends.  The automatic segment count is halved
+ *   until its workspace fits (so long sequences may run with fewer segments than
+ *   fla_linattn_fwd chooses: same function, different rounding); a request that still
+ *   does not fit returns FLA_ERR_SCRATCH before anything is enqueued.
+ *   Every call on a GPU shares that GPU's array: calls that overlap on one GPU (on
+ *   different streams, or from different host threads) race and must be serialised by
+ *   the caller.  Nothing in the array needs to start at zero.
+ * The first call on a device looks up the array's device address (hipGetSymbolAddress).
+ */
+int fla_linattn_fwd_noalloc(const void *q, const void *k, const void *v,
+                            const float *gate_or_gamma, const float *init_state, void *out,
+                            float *final_state, int64_t B, int64_t H, int64_t T, int64_t dk,
+                            int64_t dv, int64_t chunk, uint32_t flags, void *stream);
 
 /*
  * fla_linattn_fwd_varlen — fla_linattn_fwd over packed variable-length sequences (the
