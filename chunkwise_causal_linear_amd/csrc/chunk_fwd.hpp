@@ -79,7 +79,16 @@ struct ChunkArgs {
                            //    [total][H][d] with cu_seqlens); 0: [B][H][T][d]
   const int64_t *cu_seqlens; // packed sequences: [B + 1] token offsets (bthd only), or null
   const int *seq_order;    // packed sequences: unit order -> sequence (longest first), or null
+  int *unsafe;             // gated kinds: [B*H*nseg][4], written by value slice 0's producer
+                           //   waves (one word each): 1 if a chunk's decay product fell below
+                           //   kSafeDecay (the factorised form is then not used for the unit)
 };
+
+// Smallest product of the decays along one chunk (per key) for which the factorised form
+// Qt = phi(q) b, Kt = phi(k) / b is used: 1 / b stays below 2^100, far from fp32 / bf16
+// overflow for any reasonable |phi(k)|, and phi(q) b far above the denormal range.  A unit
+// with a chunk below it is recomputed by the exact 16-token kernel (exact_fwd.hpp).
+constexpr float kSafeDecay = 0x1p-100f;
 
 template <typename TIn, int DK, int C, int DECAY, bool NORM>
 struct Cfg {
@@ -131,6 +140,7 @@ struct Cfg {
   static constexpr int PTILE = 256;                      // elements per score tile
   static constexpr int PBUF_BYTES = (NTILES + (SLOTS * NCW > NTILES ? 1 : 0)) * PTILE * ES;
   static constexpr int PW_BYTES = DECAY == DECAY_GAMMA ? ((C + 4) / 4) * 16 : 0;
+  static constexpr int FLAG_BYTES = GATED ? 16 : 0; // see OFF_FLAG
   static constexpr int QT_BYTES = C * LQ * ES; // one Qt or Kt tile
   static constexpr int EL_BYTES = GATED ? DK * 4 : 0;
   // row stride of V: 40 words (8 mod 32) keeps the transposed operand loads conflict-free;
@@ -139,7 +149,7 @@ struct Cfg {
   static constexpr int LV_T = kSlice + (BF ? 8 : 4);
   static constexpr int stage_bytes(int lv) { return 2 * QT_BYTES + C * lv * ES + EL_BYTES; }
   static constexpr int split_bytes(int lv) {
-    return QT_BYTES + 2 * (QT_BYTES + C * lv * ES + EL_BYTES) + PBUF_BYTES + PW_BYTES;
+    return QT_BYTES + 2 * (QT_BYTES + C * lv * ES + EL_BYTES) + PBUF_BYTES + PW_BYTES + FLAG_BYTES;
   }
   // Schedules, by the LDS they need:
   //  SHARE: three stages {Qt, Kt, V, eL} and two score buffers; iteration n computes the
@@ -152,7 +162,7 @@ struct Cfg {
   //  otherwise the per-wave schedule: two stages (one where two do not fit), each consumer
   //    wave computing the score tiles it needs itself.
   static constexpr bool SHARE =
-      3 * stage_bytes(LV_W) + 2 * PBUF_BYTES + PW_BYTES <= kMaxLds;
+      3 * stage_bytes(LV_W) + 2 * PBUF_BYTES + PW_BYTES + FLAG_BYTES <= kMaxLds;
   static constexpr bool SPLIT = !SHARE && split_bytes(LV_T) <= kMaxLds;
   static constexpr int LV = (SPLIT && split_bytes(LV_W) > kMaxLds) ? LV_T : LV_W;
   static constexpr int PF = SPLIT ? 1 : PF_BASE; // chunks the producers load ahead
@@ -168,10 +178,12 @@ struct Cfg {
   static constexpr int STAGE_BYTES = OFF_EL + EL_BYTES;
   static constexpr int KV_BYTES = QT_BYTES + C * LV * ES + EL_BYTES; // SPLIT {Kt, V, eL}
   static constexpr int STAGES =
-      SHARE ? 3 : SPLIT ? 2 : (2 * STAGE_BYTES + PW_BYTES <= kMaxLds ? 2 : 1);
+      SHARE ? 3 : SPLIT ? 2 : (2 * STAGE_BYTES + PW_BYTES + FLAG_BYTES <= kMaxLds ? 2 : 1);
   static constexpr int OFF_P = SPLIT ? QT_BYTES + 2 * KV_BYTES : STAGES * STAGE_BYTES;
   static constexpr int OFF_PW = OFF_P + (SHARE ? 2 * PBUF_BYTES : SPLIT ? PBUF_BYTES : 0);
-  static constexpr int LDS = OFF_PW + PW_BYTES;
+  // gated kinds: one word per producer wave, 1 once a chunk's decay product was unsafe
+  static constexpr int OFF_FLAG = OFF_PW + PW_BYTES;
+  static constexpr int LDS = OFF_FLAG + FLAG_BYTES;
   static constexpr bool FITS = LDS <= kMaxLds;
   // byte offsets of the tiles of chunk n
   __device__ static int q_at(int n) { return SPLIT ? 0 : (n % STAGES) * STAGE_BYTES + OFF_Q; }
@@ -629,6 +641,11 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     float dprod[K::G];
 #pragma unroll
     for (int c = 0; c < K::G; ++c) dprod[c] = 1.f;
+    // gated kinds: set once a chunk's decay product (on this lane's key columns) falls below
+    // kSafeDecay; published per wave in LDS (for the consumers' end-state write) and to
+    // a.unsafe (for the exact kernel)
+    bool unsafe = false;
+    int *sFlag = reinterpret_cast<int *>(smem + K::OFF_FLAG);
 
     // Loads go through a buffer resource per chunk (range = the chunk's valid rows): rows
     // past the end of the sequence and idle lanes read zeros without a branch, so the
@@ -803,7 +820,11 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
           for (int r = 0; r < K::RPT; ++r) bc[r][c] *= ex;
           dprod[c] *= tot[c];
+          unsafe = unsafe || (ld_on && !(tot[c] >= kSafeDecay)); // (a NaN gate counts as unsafe)
         }
+        // (the ballot outside the lane-0 branch: inside it only lane 0 would vote)
+        const int wave_unsafe = __builtin_amdgcn_ballot_w64(unsafe) != 0 ? 1 : 0;
+        if (lane == 0) sFlag[p] = wave_unsafe;
         if (ld_on && rg == 0) {
           float totg[K::G];
 #pragma unroll
@@ -925,6 +946,10 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
       float *sd = a.seg_decay + ((int64_t)bh * a.nseg + seg) * DK + col0;
 #pragma unroll
       for (int c = 0; c < K::G; ++c) sd[c] = (DECAY == DECAY_GATE) ? dprod[c] : dprod[0];
+    }
+    if constexpr (K::GATED) {
+      const bool any = __builtin_amdgcn_ballot_w64(unsafe) != 0;
+      if (a.unsafe && vs == 0 && lane == 0) a.unsafe[((int64_t)bh * a.nseg + seg) * 4 + p] = any ? 1 : 0;
     }
     return;
   }
@@ -1619,8 +1644,16 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
   }
   }
 
-  // ---- end state
-  if (a.fin && wave_on) {
+  // ---- end state (not written for a unit the exact kernel recomputes: with an in-place
+  // resume its start state must survive)
+  bool unsafe_unit = false;
+  if constexpr (K::GATED) {
+    if (nch > 0) {
+      const int *sFlag = reinterpret_cast<const int *>(smem + K::OFF_FLAG);
+      unsafe_unit = (sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3]) != 0;
+    }
+  }
+  if (a.fin && wave_on && !unsafe_unit) {
     float *fo = a.fin + (int64_t)bh * a.fin_bh_stride + (int64_t)seg * a.fin_seg_stride;
 #pragma unroll
     for (int cb = 0; cb < K::NCB; ++cb) {

@@ -9,6 +9,7 @@
 #include "../../include/fla_linattn.h"
 #include "bwd_dispatch.hpp"
 #include "dispatch.hpp"
+#include "exact_fwd.hpp"
 #include "gdn_fwd.hpp"
 
 namespace fla {
@@ -62,6 +63,18 @@ ChunkLauncher find_launcher(bool bf16, int64_t dk, int64_t chunk, int decay, boo
     case 128: return chunk_launcher_f32_128(c, decay, norm);
     case 256: return chunk_launcher_f32_256(c, decay, norm);
     }
+  }
+  return nullptr;
+}
+
+using ExactKernel = void (*)(ExactArgs);
+ExactKernel find_exact(bool bf16, int64_t dk) {
+  switch (dk) {
+  case 16: return bf16 ? &exact_fwd_kernel<__bf16, 16> : &exact_fwd_kernel<float, 16>;
+  case 32: return bf16 ? &exact_fwd_kernel<__bf16, 32> : &exact_fwd_kernel<float, 32>;
+  case 64: return bf16 ? &exact_fwd_kernel<__bf16, 64> : &exact_fwd_kernel<float, 64>;
+  case 128: return bf16 ? &exact_fwd_kernel<__bf16, 128> : &exact_fwd_kernel<float, 128>;
+  case 256: return bf16 ? &exact_fwd_kernel<__bf16, 256> : &exact_fwd_kernel<float, 256>;
   }
   return nullptr;
 }
@@ -174,12 +187,18 @@ __global__ void state_fill_kernel(float *dst, const float *src, int64_t n) {
 // Scan over segments (elementwise per state entry): on entry ws[bh][s] holds segment s's
 // end state from a zero start and dec[bh][s][c] the product of its decays; on exit ws[bh][s]
 // holds segment s's true start state, and fin (if any) the state after the last segment.
+// unsafe: the fused kernel's flags [nbh][nseg][4] (gated kinds) or null; a flagged unit's
+// end state is left to the exact kernel (its start state may be the same memory).
 __global__ void segment_scan_kernel(float *ws, const float *dec, const float *init, float *fin,
-                                    int64_t nbh, int nseg, int dk, int ncol) {
+                                    int64_t nbh, int nseg, int dk, int ncol, const int *unsafe) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per = (int64_t)dk * ncol;
   if (i >= nbh * per) return;
   const int64_t bh = i / per, ce = i % per;
+  if (unsafe) {
+    for (int s = 0; s < 4 * nseg; ++s)
+      if (unsafe[bh * 4 * nseg + s]) fin = nullptr;
+  }
   const int c = (int)(ce / ncol);
   float run = init ? init[i] : 0.f;
   float *w = ws + bh * nseg * per + ce;
@@ -349,11 +368,15 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   int64_t nseg = n_segments == 0 ? auto_segments(B, H, T, dv, chunk) : n_segments;
   if (cu_seqlens) nseg = 1; // packed sequences: one streaming workgroup per (sequence, head, slice)
   if (nseg > nch) nseg = nch;
+  // Gated kinds: the fused kernel flags the units whose decay products leave its range
+  // (one word per producer wave), and the exact kernel recomputes those after it.
+  const bool gated = kind == DECAY_GATE || kind == DECAY_TOKEN;
+  auto flag_bytes = [&](int64_t p) { return gated ? nbh * p * 4 * (int64_t)sizeof(int) : 0; };
   // segment workspace: every segment's end state and decay product
   auto seg_ws_bytes = [&](int64_t p) { return nbh * p * dk * (ncol + 1) * (int64_t)sizeof(float); };
   if (ws.from_scratch() && n_segments == 0) {
     // the automatic count is cut down until its workspace fits the scratch region
-    while (nseg > 1 && seg_ws_bytes(nseg) > ws.left()) nseg = nseg / 2;
+    while (nseg > 1 && flag_bytes(nseg) + 256 + seg_ws_bytes(nseg) > ws.left()) nseg = nseg / 2;
   }
   const int64_t seg_chunks = (nch + nseg - 1) / nseg;
   const int64_t seg_len = seg_chunks * chunk;
@@ -363,10 +386,40 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   const int64_t grid = ((nunits + 7) / 8) * 8 * nvs;
   if (grid >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
 
+  const ExactKernel exact = gated ? find_exact(bf16, dk) : nullptr;
+  if (gated && !exact) return FLA_ERR_UNSUPPORTED;
+  int *unsafe = nullptr;
+  if (gated) {
+    void *f = nullptr;
+    if ((rc = ws.get(flag_bytes(nseg), &f)) != FLA_OK) return rc;
+    unsafe = static_cast<int *>(f);
+  }
+  auto run_exact = [&]() -> int {
+    if (!gated) return FLA_OK;
+    ExactArgs e{};
+    e.q = q; e.k = k; e.v = v;
+    e.decay = gate_or_gamma;
+    e.init = init_state;
+    e.fin = final_state;
+    e.out = out;
+    e.unsafe = unsafe;
+    e.cu_seqlens = cu_seqlens;
+    e.T = T;
+    e.H = (int)H; e.dv = (int)dv; e.ncol = (int)ncol; e.nseg = (int)nseg; e.nvs = (int)nvs;
+    e.per_key = kind == DECAY_GATE ? 1 : 0;
+    e.phi_elu1 = (flags & FLA_PHI_ELU1) ? 1 : 0;
+    e.norm = norm ? 1 : 0;
+    e.bthd = bthd ? 1 : 0;
+    void *args[] = {&e};
+    return hipLaunchKernel(reinterpret_cast<const void *>(exact), dim3((unsigned)(nbh * nvs)),
+                           dim3(256), args, 0, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
+  };
+
   ChunkArgs a{};
   a.q = q; a.k = k; a.v = v;
   a.decay = gate_or_gamma;
   a.out = out;
+  a.unsafe = unsafe;
   a.T = T;
   a.seg_len = seg_len;
   a.H = (int)H; a.dv = (int)dv; a.ncol = (int)ncol;
@@ -417,6 +470,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
     a.seg_decay = nullptr;
     a.state_only = 0;
     rc = launch(a, (unsigned)grid, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
+    if (rc == FLA_OK) rc = run_exact();
     const int rr = ws.release();
     return rc != FLA_OK ? rc : rr;
   }
@@ -445,7 +499,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
     const float *ini = init_state;
     float *fin = final_state;
     int64_t nbh_v = nbh;
-    void *args[] = {&wst, &wdec, &ini, &fin, &nbh_v, &nseg_i, &dk_i, &ncol_i};
+    void *args[] = {&wst, &wdec, &ini, &fin, &nbh_v, &nseg_i, &dk_i, &ncol_i, &unsafe};
     if (hipLaunchKernel(reinterpret_cast<const void *>(&segment_scan_kernel),
                         dim3(blocks_for(n, kScanThreads)), dim3(kScanThreads), args, 0, s) != hipSuccess)
       rc = FLA_ERR_DEVICE;
@@ -459,6 +513,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
     a.state_only = 0;
     rc = launch(a, (unsigned)grid, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
   }
+  if (rc == FLA_OK) rc = run_exact();
   const int rr = ws.release();
   return rc != FLA_OK ? rc : rr;
 }

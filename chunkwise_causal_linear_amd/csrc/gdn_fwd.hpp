@@ -11,6 +11,11 @@
 //     U = Tb V - Tg (K^ H),
 //     O = diag(g) Q H + (M (.) Q K^^T) U,        M_tj = g_t / g_j (j <= t),
 //     H <- g_L H + K^^T diag(g_L / g) U.
+// The ratios g_t / g_j (t >= j) are formed from g kept as a mantissa in [0.5, 1) and an
+// integer exponent, as ldexp(m_t / m_j, e_t - e_j): exact for any decay in [0, 1] however
+// long its product underflows fp32 (a ratio is then only ever rounded or flushed to zero
+// where it is negligible), where g_t * (1 / g_j) would overflow (textbook chapter 1.6,
+// "gated delta rule": a decay near 0 clears the memory).  Plain g (<= 1) is used as is.
 // Tb and Tg do not depend on the state, so they are formed for every chunk at once by a
 // pre-pass (one workgroup per (b, h, chunk): K^ K^^T on MFMA gives A; the 16 x 16 diagonal
 // blocks of T are inverted by forward substitution, one wave each, and the off-diagonal
@@ -65,16 +70,20 @@ struct GdnCfg {
   static constexpr int P_A = P_K;
   static constexpr int P_G = P_K + cmax(C * LDK * ES, C * C * 4);    // g [C], beta [C]
   static constexpr int P_BETA = P_G + C * 4;
-  static constexpr int P_GI = P_BETA + C * 4;                         // 1 / g [C]
-  static constexpr int P_LDS = P_GI + C * 4;
-  // state-pass LDS: two input stages {q, k^, g, 1/g} (producer waves fill one while the
+  static constexpr int P_GM = P_BETA + C * 4;                         // g = m 2^e: m [C]
+  static constexpr int P_GMI = P_GM + C * 4;                          // 1 / m [C]
+  static constexpr int P_GE = P_GMI + C * 4;                          // e [C] (int)
+  static constexpr int P_LDS = P_GE + C * 4;
+  // state-pass LDS: two input stages {q, k^, g, m, 1/m, e} (producer waves fill one while the
   // consumer waves read the other); one {Tb, Tg, V slice} buffer, which the consumers use
   // before the chunk's first barrier and the producers refill after it; the score tiles
   static constexpr int S_Q = 0;
   static constexpr int S_K = S_Q + C * LDK * ES;
   static constexpr int S_G = S_K + C * LDK * ES;    // g [C]
-  static constexpr int S_GI = S_G + C * 4;          // 1 / g [C]
-  static constexpr int S_STAGE = S_GI + C * 4;
+  static constexpr int S_GM = S_G + C * 4;          // g = m 2^e: m [C], 1 / m [C], e [C]
+  static constexpr int S_GMI = S_GM + C * 4;
+  static constexpr int S_GE = S_GMI + C * 4;
+  static constexpr int S_STAGE = S_GE + C * 4;
   static constexpr int S_TB = 2 * S_STAGE;          // Tb [C][LDT]
   static constexpr int S_TG = S_TB + C * LDT * ES;  // Tg [C][LDT]
   static constexpr int S_V = S_TG + C * LDT * ES;   // V slice [C][LDV]
@@ -120,21 +129,43 @@ __device__ __forceinline__ void stage_raw(const uint32_t (*rx)[4], TIn *s, int t
   }
 }
 
-// g = inclusive product of alpha down the chunk (wave 0; rows past the end carry 1).
-__device__ __forceinline__ float decay_scan(float alpha, int lane) {
-  float x = alpha;
+// The chunk's decays as seen by the kernels: g (inclusive product of alpha down the chunk)
+// and the same product as m 2^e (m in [0.5, 1), e an integer that does not underflow).
+struct Decays {
+  float *g, *m, *mi; // g, m, 1 / m  [C]
+  int *e;            // e [C]
+  // g_t / g_j for t >= j
+  __device__ float ratio(int t, int j) const { return ldexpf(m[t] * mi[j], e[t] - e[j]); }
+};
+
+// g = inclusive product of alpha down the chunk (one wave; rows past the end carry 1),
+// written to g[], m[], mi[], e[] at the lane's row.  alpha = 0 is taken as 2^-65536 (the
+// products that cross it are then zero after ldexp, the others exact).
+__device__ __forceinline__ void decay_scan(float alpha, int lane, float *g, float *m, float *mi,
+                                           int *e) {
+  int ex = 0;
+  float mx = frexpf(alpha, &ex);
+  if (!(alpha > 0.f)) { mx = 0.5f; ex = -65536; }
   for (int d = 1; d < 64; d <<= 1) {
-    const float o = __shfl_up(x, d);
-    if (lane >= d) x *= o;
+    const float om = __shfl_up(mx, d);
+    const int oe = __shfl_up(ex, d);
+    if (lane >= d) {
+      int k = 0;
+      mx = frexpf(mx * om, &k);
+      ex += oe + k;
+    }
   }
-  return x;
+  m[lane] = mx;
+  mi[lane] = 1.f / mx;
+  e[lane] = ex;
+  g[lane] = ldexpf(mx, ex);
 }
 
 // Masked score tiles P[t][j] = (g_t / g_j) q_t . k^_j (j <= t); the image of tile (tb, jb) is
 // row-major [t][j].  10 tiles over the 4 waves.
 template <typename TIn, int DK>
-__device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const float *sG,
-                                       const float *sGi, TIn *sP, int wave, int g, int li) {
+__device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const Decays &dec,
+                                       TIn *sP, int wave, int g, int li) {
   using K = GdnCfg<TIn, DK>;
   static_for<0, 16>([&](auto I) {
     constexpr int tb = I / 4, jb = I % 4;
@@ -149,11 +180,10 @@ __device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const float
           acc = mma(acc, ld_frag_c_at<TIn, true>(kj, u, g), ld_frag_c_at<TIn, true>(qt, u, g));
         // acc[qq]: j = 16 jb + 4g + qq, t = 16 tb + li
         const int t = 16 * tb + li;
-        const float gt = sG[t];
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int j = 16 * jb + 4 * g + qq;
-          acc[qq] = (j <= t) ? gt * sGi[j] * acc[qq] : 0.f;
+          acc[qq] = (j <= t) ? dec.ratio(t, j) * acc[qq] : 0.f;
         }
         st_ptile<TIn>(sP + I * 256 + li * 16 + 4 * g, acc);
       }
@@ -175,7 +205,10 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   float *sT = sA; // T overwrites A: each block of A is dead once its block of T is known
   float *sG = reinterpret_cast<float *>(lds + K::P_G);
   float *sBeta = reinterpret_cast<float *>(lds + K::P_BETA);
-  float *sGi = reinterpret_cast<float *>(lds + K::P_GI);
+  float *sGm = reinterpret_cast<float *>(lds + K::P_GM);
+  float *sGmi = reinterpret_cast<float *>(lds + K::P_GMI);
+  int *sGe = reinterpret_cast<int *>(lds + K::P_GE);
+  const gdn::Decays dec{sG, sGm, sGmi, sGe};
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -210,9 +243,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
     }
     gdn::stage_khat<TIn, DK>(rk, sK, tid);
     if (wave == 0) {
-      const float g = gdn::decay_scan(lane < L ? al : 1.f, lane); // past the end: alpha 1, beta 0
-      sG[lane] = g;
-      sGi[lane] = 1.f / g;
+      gdn::decay_scan(lane < L ? al : 1.f, lane, sG, sGm, sGmi, sGe); // past the end: alpha 1, beta 0
       sBeta[lane] = lane < L ? be : 0.f;
     }
   }
@@ -244,11 +275,11 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
       const int tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0, jb = k - tb * (tb + 1) / 2;
       // atile[sl][qq] = k^_j . k^_t with j = 16 jb + 4g + qq, t = 16 tb + li
       const int t = 16 * tb + li;
-      const float bt = sBeta[t] * sG[t];
+      const float bt = sBeta[t];
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int jj = 16 * jb + 4 * g + qq;
-        sA[t * C + jj] = (jj < t) ? bt * sGi[jj] * atile[sl][qq] : 0.f;
+        sA[t * C + jj] = (jj < t) ? bt * dec.ratio(t, jj) * atile[sl][qq] : 0.f;
       }
     }
   }
@@ -354,8 +385,11 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[K::S_LDS];
   auto stage_q = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_Q); };
   auto stage_k = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_K); };
-  auto stage_g = [&](int s) { return reinterpret_cast<float *>(lds + s * K::S_STAGE + K::S_G); };
-  auto stage_gi = [&](int s) { return reinterpret_cast<float *>(lds + s * K::S_STAGE + K::S_GI); };
+  auto stage_dec = [&](int s) {
+    unsigned char *b = lds + s * K::S_STAGE;
+    return gdn::Decays{reinterpret_cast<float *>(b + K::S_G), reinterpret_cast<float *>(b + K::S_GM),
+                       reinterpret_cast<float *>(b + K::S_GMI), reinterpret_cast<int *>(b + K::S_GE)};
+  };
   TIn *sTb = reinterpret_cast<TIn *>(lds + K::S_TB);
   TIn *sTg = reinterpret_cast<TIn *>(lds + K::S_TG);
   TIn *sV = reinterpret_cast<TIn *>(lds + K::S_V);
@@ -468,9 +502,8 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       gdn::stage_khat<TIn, DK>(rk[s], stage_k(buf), ptid);
       gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rq[s], stage_q(buf), ptid);
       if (pwave == 0) {
-        const float gv = gdn::decay_scan(ptid < L ? ralpha[s] : 1.f, lane);
-        stage_g(buf)[lane] = gv;
-        stage_gi(buf)[lane] = 1.f / gv; // the masks and scales multiply by it
+        const gdn::Decays d = stage_dec(buf);
+        gdn::decay_scan(ptid < L ? ralpha[s] : 1.f, lane, d.g, d.m, d.mi, d.e);
       }
     };
     using I0 = std::integral_constant<int, 0>;
@@ -532,13 +565,13 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const int64_t t0 = (int64_t)n * C;
     const TIn *sQ = stage_q(n & 1);
     const TIn *sK = stage_k(n & 1);
-    const float *sG = stage_g(n & 1);
-    const float *sGi = stage_gi(n & 1);
+    const gdn::Decays dec = stage_dec(n & 1);
+    const float *sG = dec.g;
     const float gL = sG[C - 1]; // = g[L-1]: rows past the end carry alpha = 1
 
     // ---- masked scores (shared by the consumer waves); U = Tb V - Tg (K^ H) (this wave's
     // columns)
-    gdn::scores<TIn, DK>(sQ, sK, sG, sGi, sP, wave, g, li);
+    gdn::scores<TIn, DK>(sQ, sK, dec, sP, wave, g, li);
     Frag<TIn> hf[DK / KU];
 #pragma unroll
     for (int u = 0; u < DK / KU; ++u) {
@@ -583,7 +616,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
         const int t = 16 * tb + 4 * g + qq;
         const float uval = u0[qq] - x[qq];
         uacc[tb][qq] = uval;
-        usacc[tb][qq] = uval * (gL * sGi[t]);
+        usacc[tb][qq] = uval * dec.ratio(C - 1, t);
       }
     }
     __syncthreads(); // every consumer wave's score tiles written

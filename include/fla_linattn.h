@@ -21,8 +21,8 @@
  *   q, k    [B][H][T][dk]   bf16 (FLA_BF16) or fp32
  *   v, out  [B][H][T][dv]   same dtype as q
  *   gamma   [H]             fp32, values in [0, 1]
- *   gate    [B][H][T][dk]   fp32, values in (0, 1]
- *   token   [B][H][T]       fp32, values in (0, 1] (per-token scalar decay)
+ *   gate    [B][H][T][dk]   fp32, values in [0, 1]
+ *   token   [B][H][T]       fp32, values in [0, 1] (per-token scalar decay)
  *   state   [B][H][dk][dv + n] fp32, n = 1 with FLA_NORMALIZE (column dv holds z);
  *           this is h = S^T, so state[b][h][c][e] = S[e][c].
  * With FLA_LAYOUT_BTHD (forward calls) the per-token tensors are token-major instead, as
@@ -91,9 +91,13 @@ enum fla_status {
  * The chunk size changes the rounding, never the mathematical result.  Combinations
  * whose on-chip tiles do not fit the 160 KiB LDS of a gfx950 CU (large dk with large
  * chunk, mostly in fp32) return FLA_ERR_UNSUPPORTED.
- * Gate range (FLA_DECAY_GATE and FLA_DECAY_TOKEN): each chunk's product of the decays
- * along the chunk must stay above ~1e-30 (log-decay > -69 per chunk) or the fp32
- * factorisation overflows.
+ * Decay range (FLA_DECAY_GATE and FLA_DECAY_TOKEN): any decay in [0, 1].  The fused
+ * kernel factors a chunk's decays as phi(q) b and phi(k) / b (b: the product of the
+ * decays from the chunk start), which is used while every chunk's product stays at or
+ * above 2^-100; it flags the (b, h) units where one does not, and an exact 16-token kernel
+ * (running products only, fp32) then recomputes those units' outputs and final states
+ * (a few times slower per unit; units that stay in range pay one extra launch that exits
+ * at once, plus a stream-ordered buffer of 16 B*H*segments bytes for the flags).
  */
 int fla_linattn_fwd(const void *q, const void *k, const void *v, const float *gate_or_gamma,
                     const float *init_state, void *out, float *final_state, int64_t B,
@@ -124,10 +128,10 @@ int fla_linattn_fwd_segments(const void *q, const void *k, const void *v,
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Same arguments, layouts, validation and results as fla_linattn_fwd; it calls no
  * hipMalloc / hipMallocAsync / hipFree and no allocating library routine.
- *   The one workspace the forward pass needs (the segment schedule's per-segment end
- *   states and decay products, and the private start-state copy of an in-place resume
- *   with the normaliser) comes from a static device array of 64 MiB that each GPU the
- *   library runs on holds until the process ends.  The automatic segment count is halved
+ *   The workspaces the forward pass needs (the gated kinds' range flags, the segment
+ *   schedule's per-segment end states and decay products, and the private start-state
+ *   copy of an in-place resume with the normaliser) come from a static device array of
+ *   64 MiB that each GPU the library runs on holds until the process ends.  The automatic segment count is halved
  *   until its workspace fits (so long sequences may run with fewer segments than
  *   fla_linattn_fwd chooses: same function, different rounding); a request that still
  *   does not fit returns FLA_ERR_SCRATCH before anything is enqueued.
@@ -202,8 +206,9 @@ int fla_linattn_step(const void *q, const void *k, const void *v, const float *g
  *   Three chunk-scan launches (dq forward in time; dv, then dk and dgate in reverse) and,
  *   when dgate is requested, a stream-ordered workspace of 4 (B H T dk + B H dk) bytes
  *   (+ 4 B H T dk/16 for the per-token decay, and a fourth small launch that sums it).
- * Returns FLA_ERR_UNSUPPORTED for shapes or flags outside that set.  The gate range
- * condition of the forward pass applies.
+ * Returns FLA_ERR_UNSUPPORTED for shapes or flags outside that set.  Decay range: the
+ * backward kernels use the factorised form only, so every chunk's product of the decays
+ * (per key) must stay at or above 2^-100 (the GLA workload's is about 2^-5).
  */
 int fla_linattn_bwd(const void *q, const void *k, const void *v, const float *gate_or_gamma,
                     const float *init_state, const void *dout, const float *dfinal_state,
@@ -235,8 +240,9 @@ int fla_linattn_bwd_varlen(const void *q, const void *k, const void *v, const fl
  *     S_t = alpha_t S_{t-1} (I - beta_t k^_t k^_t^T) + beta_t v_t k^_t^T,   o_t = S_t q_t,
  * i.e. decay the memory, replace a beta_t share of what it stores under k^_t by v_t.
  *   q, k  : [B][H][T][dk]; v, out: [B][H][T][dv] (bf16 with FLA_BF16, else fp32); 16-byte aligned.
- *   alpha : fp32 [B][H][T], the decay in (0, 1] (each chunk's product of alpha must stay
- *           above ~1e-30); beta: fp32 [B][H][T], the write strength in [0, 1]; 4-byte aligned.
+ *   alpha : fp32 [B][H][T], the decay in [0, 1] (the in-chunk decay ratios are formed in
+ *           mantissa-exponent form, so any product is exact or negligibly small);
+ *   beta  : fp32 [B][H][T], the write strength in [0, 1]; 4-byte aligned.
  *   init_state, final_state: fp32 [B][H][dk][dv] (h = S^T as above) or NULL; may alias.
  *   dk in {64, 128} (fp32: 64); dv in {64, 128, 256}; chunk: any value fla_linattn_fwd
  *   takes (64-token tiles are used for all of them); flags: FLA_BF16 only.

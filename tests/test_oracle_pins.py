@@ -317,3 +317,70 @@ def test_empty_sequence_returns_init():
     out, fin = oracle.fwd(c["q"], c["k"], c["v"], c["decay"], "gamma", c["init"])
     assert out.shape == (1, 2, 0, 3)
     assert np.array_equal(fin, c["init"].astype(np.float64))
+
+
+# ---------------------------------------------------------------------------------------
+# Strong decays: the exact 16-token path and the gated delta rule's decay ratios
+
+def _strong_gates(kind, B, H, T, dk, seed):
+    from workloads import strong_gates
+    return strong_gates(kind, B, H, T, dk, seed)
+
+
+@pytest.mark.parametrize("kind", ["gate", "token"])
+@pytest.mark.parametrize("norm", [False, True])
+def test_exact16_path_matches_oracle_under_strong_decay(kind, norm):
+    """The exact 16-token algorithm (running products only) equals the recurrence for
+    gates whose chunk products underflow fp32, with ragged tails and an initial state."""
+    from chunk_model import exact16
+    B, H, T, dk, dv = 1, 2, 53, 8, 6
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((B, H, T, dk)).astype(np.float32)
+    k = rng.standard_normal((B, H, T, dk)).astype(np.float32)
+    v = rng.standard_normal((B, H, T, dv)).astype(np.float32)
+    ncol = dv + (1 if norm else 0)
+    init = (0.1 * rng.standard_normal((B, H, dk, ncol))).astype(np.float32)
+    if norm:
+        init[..., dv] = np.abs(init[..., dv])
+    for name, dec in _strong_gates(kind, B, H, T, dk, 9).items():
+        ro, rf = oracle.fwd(q, k, v, dec, kind, init, phi_elu1=norm, normalize=norm)
+        mo, mf = exact16(q, k, v, dec, kind, init, phi_elu1=norm, normalize=norm)
+        assert np.allclose(mo, ro, rtol=1e-11, atol=1e-11 * np.max(np.abs(ro))), name
+        assert np.allclose(mf, rf, rtol=1e-11, atol=1e-11 * np.max(np.abs(rf))), name
+
+
+def test_strong_gate_sets_leave_the_factorised_range():
+    """The sets used for the GPU's strong-decay tests do cross the fused kernel's limit
+    (a chunk product below 2^-100) on some units and not on others, so both paths run;
+    the headline's gates never do."""
+    from chunk_model import unsafe_units
+    B, H, T, dk = 2, 4, 640, 64
+    for kind in ("gate", "token"):
+        sets = _strong_gates(kind, B, H, T, dk, 3)
+        assert unsafe_units(sets["uniform"], kind, B, H, T, dk, 64).all()
+        assert unsafe_units(sets["isolated"], kind, B, H, T, dk, 64).any()
+    from workloads import generate, small
+    w = small("gla_d128", B=2, H=2, T=4096)
+    inp = generate(w)
+    assert not unsafe_units(inp["decay"], "gate", 2, 2, 4096, 128, 64).any()
+
+
+def test_gdn_decay_ratio_in_mantissa_exponent_form():
+    """g_t / g_j formed as ldexp(m_t / m_j, e_t - e_j) from the scanned (m, e) pairs equals
+    the product of the decays over tokens j+1..t (fp32 rounding, or both below 2^-126),
+    also when the plain product g underflows to zero and when a decay is exactly 0."""
+    from chunk_model import ext_decay_ratio
+    rng = np.random.default_rng(11)
+    cases = [rng.uniform(0.02, 0.5, 64), rng.uniform(1e-6, 1e-3, 64),
+             np.where(rng.random(64) < 0.1, 0.0, rng.uniform(0.5, 1.0, 64)),
+             np.full(64, 0.999), np.ones(64)]
+    for a in cases:
+        a = a.astype(np.float32).astype(np.float64)
+        r = ext_decay_ratio(a)
+        for t in range(64):
+            for j in range(t + 1):
+                exact = float(np.prod(a[j + 1:t + 1]))
+                if exact >= 2.0 ** -126:
+                    assert abs(r[t, j] - exact) <= 64 * 2.0 ** -23 * exact, (t, j, r[t, j], exact)
+                else:
+                    assert r[t, j] <= 2.0 ** -126

@@ -320,3 +320,24 @@ def to_numpy_input(t):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+def strong_gates(kind: str, B: int, H: int, T: int, dk: int, seed: int) -> dict:
+    """Decay sets that leave the range of the fused kernel's factorisation (strong
+    forgetting, as the textbook's gated delta rule and decay-masked attention allow):
+      sigmoid   plain sigmoid(x) gates, x ~ N(0, 1) (no 1/16 power);
+      uniform   decays uniform in [0.02, 0.5];
+      isolated  sigmoid(x)^(1/16) with isolated entries of 1e-6 (6%) and 0 (1%).
+    Shape [B, H, T, dk] for kind "gate", [B, H, T] for "token" (also the gated delta
+    rule's alpha); fp32, drawn with numpy PCG64 from seed."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, T, dk) if kind == "gate" else (B, H, T)
+    x = rng.standard_normal(shape)
+    plain = 1.0 / (1.0 + np.exp(-x))
+    uniform = rng.uniform(0.02, 0.5, shape)
+    iso = plain ** (1.0 / 16.0)
+    pick = rng.random(shape)
+    iso = np.where(pick < 0.06, 1e-6, iso)
+    iso = np.where(pick > 0.99, 0.0, iso)
+    return {"sigmoid": plain.astype(np.float32), "uniform": uniform.astype(np.float32),
+            "isolated": iso.astype(np.float32)}
