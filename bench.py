@@ -604,6 +604,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--chunk", type=int, default=None,
+                    help="evaluate the workload with this chunk size instead of its own "
+                         "(tile sweeps; the forward pass's result does not depend on it)")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured HBM / MFMA ceilings (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -636,6 +639,10 @@ def main():
         bench_varlen(torch, fla, args)
         return
     w = WORKLOADS[args.workload or HEADLINE]
+    if args.chunk:
+        # tile sweep: the same workload evaluated with another chunk size (the function
+        # does not depend on it; the workload's own chunk is the one its config names)
+        w = w.with_(chunk=args.chunk)
     if args.mode == "bwd":
         bench_bwd(torch, fla, w, args)
         return

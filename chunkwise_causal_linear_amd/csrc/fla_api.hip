@@ -11,6 +11,7 @@
 #include "dispatch.hpp"
 #include "exact_fwd.hpp"
 #include "gdn_fwd.hpp"
+#include "seg_state.hpp"
 
 namespace fla {
 
@@ -39,9 +40,11 @@ bool is_pow2_dim(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128 |
 bool is_chunk(int64_t c) { return c == 16 || c == 32 || c == 64 || c == 128; }
 // Chunk sizes a call accepts: the tile sizes above, and larger powers of two up to 1024
 // (the FLA posts advise chunk_size = 512 for long-sequence training), which are evaluated
-// as consecutive 128-token sub-chunks (64 where a 128-token tile does not fit in LDS).
-// Splitting a chunk into sub-chunks is exact in real arithmetic (the state after a
-// sub-chunk is the state before the next), so only the rounding differs.
+// as consecutive 64-token sub-chunks, the tile size measured fastest on every workload
+// (the 128-token tile of the per-key gate runs five times slower: its score tiles no
+// longer fit the shared-score schedule).  Splitting a chunk into sub-chunks is exact in
+// real arithmetic (the state after a sub-chunk is the state before the next), so only the
+// rounding differs.
 bool is_chunk_arg(int64_t c) { return is_chunk(c) || c == 256 || c == 512 || c == 1024; }
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -77,6 +80,22 @@ ExactKernel find_exact(bool bf16, int64_t dk) {
   case 256: return bf16 ? &exact_fwd_kernel<__bf16, 256> : &exact_fwd_kernel<float, 256>;
   }
   return nullptr;
+}
+
+using SegStateKernel = void (*)(ChunkArgs);
+template <bool Z>
+SegStateKernel find_seg_state_z(bool bf16, int64_t dk) {
+  switch (dk) {
+  case 16: return bf16 ? nullptr : &seg_state_kernel<float, 16, Z>; // (bf16: fused kernel's pass)
+  case 32: return bf16 ? &seg_state_kernel<__bf16, 32, Z> : &seg_state_kernel<float, 32, Z>;
+  case 64: return bf16 ? &seg_state_kernel<__bf16, 64, Z> : &seg_state_kernel<float, 64, Z>;
+  case 128: return bf16 ? &seg_state_kernel<__bf16, 128, Z> : &seg_state_kernel<float, 128, Z>;
+  case 256: return bf16 ? &seg_state_kernel<__bf16, 256, Z> : &seg_state_kernel<float, 256, Z>;
+  }
+  return nullptr;
+}
+SegStateKernel find_seg_state(bool bf16, int64_t dk, bool norm) {
+  return norm ? find_seg_state_z<true>(bf16, dk) : find_seg_state_z<false>(bf16, dk);
 }
 
 int decay_kind(uint32_t flags) {
@@ -348,11 +367,8 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   const bool bf16 = (flags & FLA_BF16) != 0;
   const bool norm = (flags & FLA_NORMALIZE) != 0;
   const int kind = decay_kind(flags);
-  ChunkLauncher launch = find_launcher(bf16, dk, chunk > 128 ? 128 : chunk, kind, norm);
-  if (chunk > 128) {
-    if (launch) chunk = 128;
-    else if ((launch = find_launcher(bf16, dk, 64, kind, norm)) != nullptr) chunk = 64;
-  }
+  if (chunk > 128) chunk = 64; // sub-chunks of the fastest tile (see is_chunk_arg)
+  ChunkLauncher launch = find_launcher(bf16, dk, chunk, kind, norm);
   if (!launch) return FLA_ERR_UNSUPPORTED;
   hipStream_t s = ws.s;
   const int64_t ncol = dv + (norm ? 1 : 0);
@@ -491,7 +507,15 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   a.fin_seg_stride = dk * ncol;
   a.seg_decay = wdec;
   a.state_only = 1;
-  rc = launch(a, (unsigned)grid, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
+  if (const SegStateKernel st = gated ? nullptr : find_seg_state(bf16, dk, norm)) {
+    // constant decays: the end states are a plain reduction over each segment (seg_state.hpp)
+    ChunkArgs sa = a;
+    void *sargs[] = {&sa};
+    rc = hipLaunchKernel(reinterpret_cast<const void *>(st), dim3((unsigned)grid), dim3(256), sargs,
+                         0, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
+  } else {
+    rc = launch(a, (unsigned)grid, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
+  }
 
   if (rc == FLA_OK) {
     const int64_t n = nbh * dk * ncol;
@@ -790,10 +814,7 @@ int fla_linattn_segments_for(int64_t B, int64_t H, int64_t T, int64_t dk, int64_
   int rc = fla::check_common(B, H, dk, dv, flags, has_decay ? dummy : nullptr);
   if (rc != FLA_OK) return rc;
   if (!fla::is_chunk_arg(chunk)) return FLA_ERR_UNSUPPORTED;
-  if (chunk > 128) {
-    const bool norm = (flags & FLA_NORMALIZE) != 0;
-    chunk = fla::find_launcher((flags & FLA_BF16) != 0, dk, 128, fla::decay_kind(flags), norm) ? 128 : 64;
-  }
+  if (chunk > 128) chunk = 64;
   const int64_t nch = (T + chunk - 1) / chunk;
   int64_t p = T == 0 ? 1 : fla::auto_segments(B, H, T, dv, chunk);
   if (p > nch && nch > 0) p = nch;

@@ -82,8 +82,8 @@ enum fla_status {
  *   B, H >= 1; T >= 0; dk, dv in {16, 32, 64, 128, 256}; chunk in {16, 32, 64, 128,
  *                  256, 512, 1024}: the tile sizes are 16..128; a larger chunk (the FLA
  *                  posts advise chunk_size = 512 for long-sequence training) is evaluated
- *                  as consecutive 128-token sub-chunks (64 where a 128-token tile does not
- *                  fit), which is exact in real arithmetic.
+ *                  as consecutive 64-token sub-chunks (the fastest tile), which is exact
+ *                  in real arithmetic.
  *   flags        : FLA_* bits; at most one decay bit.
  *   stream       : hipStream_t or NULL.
  *

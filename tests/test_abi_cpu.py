@@ -178,11 +178,11 @@ def test_schedule_choice(lib):
     assert fla.segments_for(1, 8, 1 << 20, 128, 128, 128, fla.FLA_BF16 | fla.FLA_DECAY_GAMMA) == 64
     # too short to cut
     assert fla.segments_for(1, 1, 256, 64, 64, 64, fla.FLA_PHI_ELU1 | fla.FLA_NORMALIZE) == 1
-    # chunk sizes above 128 run as 128-token sub-chunks: the same schedule as chunk 128
+    # chunk sizes above 128 run as 64-token sub-chunks: the same schedule as chunk 64
     f = fla.FLA_BF16 | fla.FLA_DECAY_GAMMA
     for c in (256, 512, 1024):
         assert fla.segments_for(1, 8, 1 << 20, 128, 128, c, f) == \
-            fla.segments_for(1, 8, 1 << 20, 128, 128, 128, f)
+            fla.segments_for(1, 8, 1 << 20, 128, 128, 64, f)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
