@@ -563,6 +563,90 @@ def bench_gdn(torch, fla, args):
     print(json.dumps(res), flush=True)
 
 
+def bench_proj(torch, fla, args):
+    """The layer's input side: q, k, v projections with the feature map fused in, then the
+    forward pass (one fla_linattn_fwd_proj call per step)."""
+    import numpy as np
+    import oracle
+    from workloads import PROJ, generate_proj_torch, to_numpy_input
+
+    sp = PROJ[args.proj]
+    B, T, D, H, dk, dv = (sp[k] for k in ("B", "T", "hidden", "H", "dk", "dv"))
+    inp = generate_proj_torch(sp, "cuda")
+    dt = inp["x"].dtype
+    out = torch.empty((B, T, H, dv), dtype=dt, device="cuda")
+    fin = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fla.fwd_proj(inp["x"], inp["w_q"], inp["w_k"], inp["w_v"], H, inp["decay"],
+                     decay_kind=sp["decay"], out=out, final_state=fin, chunk=sp["chunk"],
+                     stream=stream)
+
+    ms, warmup, t_wall, per_step = timed(torch, step, args.steps, args.warmup, stream)
+    s = 2 if sp["dtype"] == "bf16" else 4
+    M = B * T
+    gemm_flops = 2.0 * M * D * H * (2 * dk + dv)
+    attn_flops = M * H * 2.0 * ((sp["chunk"] + 1) / 2.0 * (dk + dv) + 2.0 * dk * dv)
+    # the method's bytes: x and the weights in, the gate in, out and the final state out
+    alg_bytes = (M * D + D * H * (2 * dk + dv)) * s + M * H * dv * s + B * H * dk * dv * 4
+    alg_bytes += M * H * dk * 4 if sp["decay"] == "gate" else (M * H * 4 if sp["decay"] == "token" else 0)
+    tflops = (gemm_flops + attn_flops) / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "linear-attn layer input side + chunk fwd tokens/s + MFMA roofline, " + args.proj,
+        "value": M / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": warmup,
+        "ms_per_step": ms,
+        "ms_per_step_median": per_step["median"],
+        "ms_per_step_min": per_step["min"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sp["dtype"],
+        "data": "synthetic (seeded torch generator on the GPU; x ~ N(0,1), W scaled so q, k ~ N(0, 1/dk))",
+        "config": {"workload": args.proj, "B": B, "T": T, "hidden": D, "H": H, "dk": dk, "dv": dv,
+                   "chunk": sp["chunk"], "decay": sp["decay"], "layout": "[B][T][H][d]",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "proj_phi_kernel (q, k, v) + chunk_fwd_kernel (token-major)",
+            "achieved": tflops,
+            "peak": MFMA_PEAK_TFLOPS[sp["dtype"]],
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_PEAK_TFLOPS[sp["dtype"]],
+            "traffic": None,
+            "algorithmic_flops_per_step": gemm_flops + attn_flops,
+            "algorithmic_bytes_per_step": alg_bytes,
+            "hbm_GBs_algorithmic": alg_bytes / (ms * 1e-3) / 1e9,
+        },
+        "wall_s_timed_region": t_wall,
+    }
+    if args.peaks:
+        res["roofline"]["measured_peaks"] = args.peaks
+        if sp["dtype"] == "bf16":
+            res["roofline"]["frac_of_measured_mfma"] = tflops / args.peaks["mfma_bf16_TFLOPs"]
+    if not args.no_cpu_baseline:
+        hc = host_cores()
+        t0 = time.perf_counter()
+        ro, rf = oracle.fwd_proj(to_numpy_input(inp["x"][:1]), to_numpy_input(inp["w_q"]),
+                                 to_numpy_input(inp["w_k"]), to_numpy_input(inp["w_v"]), H,
+                                 to_numpy_input(inp["decay"][:1]), sp["decay"],
+                                 nthreads=hc["threads"])
+        dt_s = time.perf_counter() - t0
+        o = out[:1].float().cpu().numpy().astype(np.float64)
+        res["cpu_baseline"] = {"value": T / dt_s, "unit": "tokens/s", **cpu_fields(hc),
+                               "kind": "oracle",
+                               "sample": f"batch row 0 of {B} ({T} tokens, all {H} heads; fp64 "
+                                         f"projections (numpy) + recurrence, {dt_s:.1f} s)"}
+        res["parity_on_sample"] = {"max_rel_err_out": float(np.max(np.abs(o - ro)) / np.max(np.abs(ro)))}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration(torch, steps, warmup):
     """A plain copy of 1 GiB: reads and writes exactly 2^30 bytes per launch."""
     n = 1 << 30
@@ -601,6 +685,9 @@ def main():
     ap.add_argument("--varlen", default=None,
                     help="forward over packed variable-length sequences (workload name, "
                          "e.g. varlen_gla_d128)")
+    ap.add_argument("--proj", default=None,
+                    help="the layer's input side: projections + feature map + forward "
+                         "(workload name, e.g. gla_proj_d128)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -637,6 +724,9 @@ def main():
         return
     if args.varlen:
         bench_varlen(torch, fla, args)
+        return
+    if args.proj:
+        bench_proj(torch, fla, args)
         return
     w = WORKLOADS[args.workload or HEADLINE]
     if args.chunk:

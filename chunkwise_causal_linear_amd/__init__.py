@@ -33,7 +33,7 @@ EXPORTED = ("fla_linattn_fwd", "fla_linattn_fwd_segments", "fla_linattn_step",
             "fla_status_string", "fla_linattn_segments_for", "fla_linattn_bwd",
             "fla_linattn_fwd_varlen", "fla_linattn_bwd_varlen", "fla_gdn_fwd",
             "fla_probe_stream", "fla_probe_mfma", "fla_probe_mfma_flops",
-            "fla_linattn_fwd_noalloc")
+            "fla_linattn_fwd_noalloc", "fla_linattn_fwd_proj")
 PROBE_READ, PROBE_COPY, PROBE_MIX5 = 0, 1, 2
 
 _lib = None
@@ -81,6 +81,9 @@ def load_library():
     lib.fla_linattn_fwd_noalloc.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64,
                                             u32, p]
     lib.fla_linattn_fwd_noalloc.restype = c_int
+    lib.fla_linattn_fwd_proj.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64,
+                                         i64, u32, p]
+    lib.fla_linattn_fwd_proj.restype = c_int
     lib.fla_probe_stream.argtypes = [p, p, i64, c_int, p]
     lib.fla_probe_stream.restype = c_int
     lib.fla_probe_mfma.argtypes = [p, i64, i64, p]
@@ -331,6 +334,39 @@ def bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Te
     if rc != FLA_OK:
         raise FlaError("fla_linattn_bwd_varlen", rc)
     return dq, dkk, dvv, dgate, dinit
+
+
+def fwd_proj(x: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, H: int,
+             decay: Optional[torch.Tensor] = None, *, decay_kind: Optional[str] = None,
+             init_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+             final_state: Optional[torch.Tensor] = None, want_final: bool = True,
+             chunk: int = 64, phi_elu1: bool = False, normalize: bool = False,
+             stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Projections + feature map + forward: x [B,T,hidden]; w_q, w_k [hidden,H*dk]; w_v
+    [hidden,H*dv] (x's dtype); decay gamma [H], gate [B,T,H,dk] or per-token [B,T,H].
+    Returns (out [B,T,H,dv], final_state [B,H,dk,dv(+1)])."""
+    B, T, hidden = x.shape
+    dk = w_q.shape[1] // H
+    dv = w_v.shape[1] // H
+    if w_q.shape != (hidden, H * dk) or w_k.shape != w_q.shape or w_v.shape != (hidden, H * dv):
+        raise ValueError("projection shapes: w_q, w_k [hidden, H*dk], w_v [hidden, H*dv]")
+    if decay_kind is None:
+        decay_kind = ("none" if decay is None
+                      else {1: "gamma", 3: "token"}.get(decay.dim(), "gate"))
+    ncol = dv + (1 if normalize else 0)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=x.dtype, device=x.device)
+    if final_state is None and want_final:
+        final_state = torch.empty((B, H, dk, ncol), dtype=torch.float32, device=x.device)
+    _check_tensors(x, (w_q, w_k, w_v, out), (decay, init_state, final_state))
+    flags = flags_for(x.dtype, decay_kind, phi_elu1, normalize) | FLA_LAYOUT_BTHD
+    rc = load_library().fla_linattn_fwd_proj(_ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+                                             _ptr(decay), _ptr(init_state), _ptr(out),
+                                             _ptr(final_state), B, T, hidden, H, dk, dv, chunk,
+                                             flags, _stream(stream))
+    if rc != FLA_OK:
+        raise FlaError("fla_linattn_fwd_proj", rc)
+    return out, final_state
 
 
 def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,

@@ -11,6 +11,7 @@
 #include "dispatch.hpp"
 #include "exact_fwd.hpp"
 #include "gdn_fwd.hpp"
+#include "proj.hpp"
 #include "seg_state.hpp"
 
 namespace fla {
@@ -319,7 +320,7 @@ struct Workspace {
   char *base = nullptr; // scratch region, or null for stream-ordered allocations
   int64_t cap = 0, used = 0;
   hipStream_t s = nullptr;
-  void *owned[4] = {};
+  void *owned[8] = {};
   int nowned = 0;
 
   bool from_scratch() const { return base != nullptr; }
@@ -332,7 +333,7 @@ struct Workspace {
       used = off + bytes;
       return FLA_OK;
     }
-    if (nowned == 4 || hipMallocAsync(p, (size_t)bytes, s) != hipSuccess) return FLA_ERR_DEVICE;
+    if (nowned == 8 || hipMallocAsync(p, (size_t)bytes, s) != hipSuccess) return FLA_ERR_DEVICE;
     owned[nowned++] = *p;
     return FLA_OK;
   }
@@ -540,6 +541,76 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   if (rc == FLA_OK) rc = run_exact();
   const int rr = ws.release();
   return rc != FLA_OK ? rc : rr;
+}
+
+// The layer's input side: q, k, v = phi(x W_q), phi(x W_k), x W_v into token-major
+// workspaces (proj.hpp), then the forward pass on them.
+int proj_impl(const void *x, const void *w_q, const void *w_k, const void *w_v,
+              const float *gate_or_gamma, const float *init_state, void *out, float *final_state,
+              int64_t B, int64_t T, int64_t hidden, int64_t H, int64_t dk, int64_t dv,
+              int64_t chunk, uint32_t flags, Workspace &ws) {
+  if (flags & ~(FLA_ALL_FLAGS)) return FLA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || T < 0 || hidden < 1) return FLA_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !w_q || !w_k || !w_v || !out)) return FLA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(w_k, 16) || !aligned(w_v, 16))
+    return FLA_ERR_INVALID_ARG;
+  if (hidden % 32 != 0 || hidden > (1 << 20)) return FLA_ERR_UNSUPPORTED;
+  if (!is_pow2_dim(dk) || !is_pow2_dim(dv) || H > (1 << 16) || (H * dk) % 16 || (H * dv) % 16)
+    return FLA_ERR_UNSUPPORTED;
+  if (B * T > ((int64_t)1 << 40) / (H * (dk > dv ? dk : dv))) return FLA_ERR_INVALID_ARG;
+  const bool bf16 = (flags & FLA_BF16) != 0;
+  const int64_t M = B * T;
+  const int es = bf16 ? 2 : 4;
+  if (T == 0) // nothing to project: the forward pass's own empty-sequence rule
+    return fwd_impl(nullptr, nullptr, nullptr, gate_or_gamma, init_state, out, final_state, B, H,
+                    0, dk, dv, chunk, (flags & ~FLA_PHI_ELU1) | FLA_LAYOUT_BTHD, 0, nullptr, ws);
+  // everything the forward call checks, checked before the projections are enqueued
+  {
+    const int rc = check_common(B, H, dk, dv, (flags & ~FLA_PHI_ELU1) | FLA_LAYOUT_BTHD,
+                                gate_or_gamma);
+    if (rc != FLA_OK) return rc;
+    if (!aligned(out, 16) || !aligned(init_state, 16) || !aligned(final_state, 16))
+      return FLA_ERR_INVALID_ARG;
+    if (H * (dk > dv ? dk : dv) > ((int64_t)1 << 20) || B * H > ((int64_t)1 << 26))
+      return FLA_ERR_UNSUPPORTED;
+    if (!is_chunk_arg(chunk)) return FLA_ERR_UNSUPPORTED;
+    if (!find_launcher(bf16, dk, chunk > 128 ? 64 : chunk, decay_kind(flags),
+                       (flags & FLA_NORMALIZE) != 0))
+      return FLA_ERR_UNSUPPORTED;
+  }
+  void *pq = nullptr, *pk = nullptr, *pv = nullptr;
+  int rc = ws.get(M * H * dk * es, &pq);
+  if (rc == FLA_OK) rc = ws.get(M * H * dk * es, &pk);
+  if (rc == FLA_OK) rc = ws.get(M * H * dv * es, &pv);
+  if (rc != FLA_OK) {
+    ws.release();
+    return rc;
+  }
+  const bool elu = (flags & FLA_PHI_ELU1) != 0;
+  auto gemm = [&](const void *w, void *y, int64_t n, bool phi) -> int {
+    ProjArgs pa{};
+    pa.x = x; pa.w = w; pa.y = y; pa.M = M; pa.K = (int)hidden; pa.N = (int)n;
+    pa.phi_elu1 = phi ? 1 : 0;
+    const int64_t blocks = ((M + 127) / 128) * ((n + 127) / 128);
+    if (blocks >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
+    const void *fn = bf16 ? (phi ? reinterpret_cast<const void *>(&proj_phi_kernel<__bf16, true>)
+                                 : reinterpret_cast<const void *>(&proj_phi_kernel<__bf16, false>))
+                          : (phi ? reinterpret_cast<const void *>(&proj_phi_kernel<float, true>)
+                                 : reinterpret_cast<const void *>(&proj_phi_kernel<float, false>));
+    void *args[] = {&pa};
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, ws.s) == hipSuccess
+               ? FLA_OK : FLA_ERR_DEVICE;
+  };
+  rc = gemm(w_q, pq, H * dk, elu);
+  if (rc == FLA_OK) rc = gemm(w_k, pk, H * dk, elu);
+  if (rc == FLA_OK) rc = gemm(w_v, pv, H * dv, false);
+  if (rc != FLA_OK) {
+    ws.release();
+    return rc;
+  }
+  // phi is already applied: the forward pass takes the projected q, k as they are
+  return fwd_impl(pq, pk, pv, gate_or_gamma, init_state, out, final_state, B, H, T, dk, dv, chunk,
+                  (flags & ~FLA_PHI_ELU1) | FLA_LAYOUT_BTHD, 0, nullptr, ws);
 }
 
 int bwd_impl(const void *q, const void *k, const void *v, const float *gate_or_gamma,
@@ -782,6 +853,16 @@ int fla_linattn_fwd_noalloc(const void *q, const void *k, const void *v,
   ws.cap = fla::kScratchBytes;
   return fla::fwd_impl(q, k, v, gate_or_gamma, init_state, out, final_state, B, H, T, dk, dv,
                        chunk, flags, 0, nullptr, ws);
+}
+
+int fla_linattn_fwd_proj(const void *x, const void *w_q, const void *w_k, const void *w_v,
+                         const float *gate_or_gamma, const float *init_state, void *out,
+                         float *final_state, int64_t B, int64_t T, int64_t hidden, int64_t H,
+                         int64_t dk, int64_t dv, int64_t chunk, uint32_t flags, void *stream) {
+  fla::Workspace ws;
+  ws.s = static_cast<hipStream_t>(stream);
+  return fla::proj_impl(x, w_q, w_k, w_v, gate_or_gamma, init_state, out, final_state, B, T,
+                        hidden, H, dk, dv, chunk, flags, ws);
 }
 
 int fla_linattn_fwd_varlen(const void *q, const void *k, const void *v, const float *gate_or_gamma,

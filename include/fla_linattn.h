@@ -146,6 +146,30 @@ int fla_linattn_fwd_noalloc(const void *q, const void *k, const void *v,
                             int64_t dv, int64_t chunk, uint32_t flags, void *stream);
 
 /*
+ * fla_linattn_fwd_proj — the layer's input side fused with the feature map, then the
+ * forward pass: a linear-attention layer maps activations x [B][T][hidden] to per-head
+ * q, k, v (the FLA guide's layers), and the FLA Triton post fuses the Q/K/V projections
+ * with the phi computation.  Per token and head h:
+ *     q = phi(x W_q)[h d_k .. h d_k + d_k),  k = phi(x W_k)[...],  v = (x W_v)[h d_v ..],
+ * then the recurrence of fla_linattn_fwd on them.
+ *   x      : [B][T][hidden]; w_q, w_k: [hidden][H*dk]; w_v: [hidden][H*dv]; row-major, the
+ *            input dtype (bf16 with FLA_BF16, else fp32), 16-byte aligned.
+ *   out    : [B][T][H][dv] (token-major), the input dtype.
+ *   gate_or_gamma: gamma [H], gate [B][T][H][dk] or per-token decay [B][T][H] (token-major),
+ *            or NULL; init_state / final_state: [B][H][dk][dv + n] fp32 as fla_linattn_fwd.
+ *   hidden : a multiple of 32; H*dk and H*dv multiples of 16; other limits as
+ *            fla_linattn_fwd with FLA_LAYOUT_BTHD (implied).  FLA_PHI_ELU1 applies phi to
+ *            the projected q and k, inside the projection kernel.
+ * The projections are MFMA GEMMs with phi in their epilogue (one launch per projection),
+ * written to stream-ordered workspaces (B T H (2 dk + dv) elements of the input dtype),
+ * then read by the chunk kernel.  Everything is validated before the first launch.
+ */
+int fla_linattn_fwd_proj(const void *x, const void *w_q, const void *w_k, const void *w_v,
+                         const float *gate_or_gamma, const float *init_state, void *out,
+                         float *final_state, int64_t B, int64_t T, int64_t hidden, int64_t H,
+                         int64_t dk, int64_t dv, int64_t chunk, uint32_t flags, void *stream);
+
+/*
  * fla_linattn_fwd_varlen — fla_linattn_fwd over packed variable-length sequences (the
  * Triton fused-kernel post recommends chunk mode for variable-length input; the FLA
  * guide's layers take [B][T][hidden] activations, hence the token-major layout).

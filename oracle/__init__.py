@@ -76,7 +76,9 @@ def _dtype_code(x: np.ndarray) -> int:
         return 1
     if x.dtype == np.float32:
         return 0
-    raise TypeError("oracle inputs are fp32 arrays or bf16 bit patterns (uint16)")
+    if x.dtype == np.float64:
+        return 2     # values the oracle derived itself (fwd_proj's projections)
+    raise TypeError("oracle inputs are fp32 / fp64 arrays or bf16 bit patterns (uint16)")
 
 
 def fwd(q, k, v, decay=None, decay_kind="none", init=None, *, phi_elu1=False,
@@ -225,3 +227,37 @@ def gdn_fwd(q, k, v, alpha, beta, init=None, *, want_out=True, want_final=True, 
     if rc != 0:
         raise RuntimeError("oracle_gdn_fwd failed")
     return out, fin
+
+
+def _widen(x: np.ndarray) -> np.ndarray:
+    """Stored inputs (bf16 bit patterns or fp32) widened exactly to fp64."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def fwd_proj(x, w_q, w_k, w_v, H, decay=None, decay_kind="none", init=None, *,
+             phi_elu1=False, normalize=False, nthreads=0):
+    """The layer's input side followed by the recurrence, in fp64: per token the
+    projections q = x W_q, k = x W_k, v = x W_v (x [B,T,hidden], W [hidden, H*d], head h
+    taking columns h*d .. h*d+d-1, as the FLA guide's layers map [B,T,hidden] to heads),
+    then fwd() with phi applied to the projected q and k.  decay: gamma [H], or the gate /
+    per-token decay token-major ([B,T,H,dk] / [B,T,H]).  Returns (out [B,T,H,dv] fp64,
+    final [B,H,dk,dv(+1)] fp64)."""
+    X = _widen(x)
+    B, T, _ = X.shape
+    dk = np.asarray(w_q).shape[1] // H
+    dv = np.asarray(w_v).shape[1] // H
+
+    def heads(w, d):
+        y = X @ _widen(w)                                  # [B, T, H*d], fp64
+        return np.ascontiguousarray(y.reshape(B, T, H, d).transpose(0, 2, 1, 3))
+
+    q, k, v = heads(w_q, dk), heads(w_k, dk), heads(w_v, dv)
+    dec = decay
+    if decay is not None and decay_kind in ("gate", "token"):
+        dec = np.ascontiguousarray(np.swapaxes(np.asarray(decay), 1, 2))
+    out, fin = fwd(q, k, v, dec, decay_kind, init, phi_elu1=phi_elu1, normalize=normalize,
+                   nthreads=nthreads)
+    return np.ascontiguousarray(out.transpose(0, 2, 1, 3)), fin

@@ -23,7 +23,7 @@
  *   - elu is PyTorch's default (alpha = 1): x for x > 0, exp(x) - 1 otherwise;
  *   - no 1/sqrt(d) scale and no epsilon in the denominator.
  *
- * Inputs are widened exactly (bf16 -> fp32 -> fp64, fp32 -> fp64).  The state is
+ * Inputs are widened exactly (bf16 -> fp32 -> fp64, fp32 -> fp64; fp64 as is).  The state is
  * kept per (batch, head, block of 16 value rows) so the blocks run in parallel with
  * OpenMP; every value row sees the same operations in the same order whatever the
  * thread count.  Build without -ffast-math and with -ffp-contract=off.
@@ -37,7 +37,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 }; /* fp64: inputs the oracle itself derived */
 enum { OR_DECAY_NONE = 0, OR_DECAY_GAMMA = 1, OR_DECAY_GATE = 2, OR_DECAY_TOKEN = 3 };
 enum { OR_PHI_ELU1 = 1, OR_NORMALIZE = 2 };
 
@@ -50,6 +50,7 @@ static double widen(const void *p, int dtype, int64_t i) {
     memcpy(&f, &u, sizeof f);
     return (double)f;
   }
+  if (dtype == OR_F64) return ((const double *)p)[i];
   return (double)((const float *)p)[i];
 }
 

@@ -111,17 +111,21 @@ def test_gdn_empty_and_rejects():
     assert e.value.status == fla.FLA_ERR_UNSUPPORTED
 
 
-def test_gdn_full_size_sampled_heads():
+def test_gdn_full_size_all_heads():
     """The full-size workload in the launch configuration bench.py times; the oracle checks
-    two whole heads."""
+    every head, one batch row at a time."""
     w = GDN["gdn_d128"]
     say(f"[gdn-full] {w}")
     inp = generate_gdn_torch(w, "cuda")
     out, fin = fla.gdn_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"])
     torch.cuda.synchronize()
-    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
-        sl = (slice(b, b + 1), slice(h, h + 1))
+    d_o = m_o = d_f = m_f = 0.0
+    for b in range(w.B):
+        sl = (slice(b, b + 1),)
         ro, rf = oracle.gdn_fwd(*(to_numpy_input(inp[n][sl]) for n in ("q", "k", "v", "alpha", "beta")))
-        eo, ef = rel_err(to_host(out[sl]), ro), rel_err(to_host(fin[sl]), rf)
-        say(f"[gdn-full] head ({b},{h}): out {eo:.2e} final {ef:.2e}")
-        assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+        o, f = to_host(out[sl]), to_host(fin[sl])
+        d_o, m_o = max(d_o, float(np.max(np.abs(o - ro)))), max(m_o, float(np.max(np.abs(ro))))
+        d_f, m_f = max(d_f, float(np.max(np.abs(f - rf)))), max(m_f, float(np.max(np.abs(rf))))
+    eo, ef = d_o / m_o, d_f / m_f
+    say(f"[gdn-full] all heads: out {eo:.2e} final {ef:.2e}")
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]

@@ -206,7 +206,7 @@ def test_full_size_bthd_headline_matches_bhtd():
 
 def test_full_size_varlen_workload():
     """The packed-sequence workload in the launch configuration bench.py times; the oracle
-    checks the longest, the shortest and the last sequence."""
+    checks every sequence (global max-norm error over all of them)."""
     from workloads import generate_torch, to_numpy_input, varlen_workload
     w, lengths = varlen_workload("varlen_gla_d128")
     say(f"[varlen-full] {w.name}: {len(lengths)} sequences, {w.T} tokens")
@@ -216,12 +216,15 @@ def test_full_size_varlen_workload():
     out, fin = fla.fwd_varlen(packed["q"], packed["k"], packed["v"], to_device(cu_h),
                               packed["decay"], decay_kind="gate")
     torch.cuda.synchronize()
-    for s in sorted({int(np.argmax(lengths)), int(np.argmin(lengths)), len(lengths) - 1}):
+    d_o = m_o = d_f = m_f = 0.0
+    for s in range(len(lengths)):
         s0, s1 = int(cu_h[s]), int(cu_h[s + 1])
         part = lambda t: to_numpy_input(t[:, :, s0:s1])
         ro, rf = oracle.fwd(part(inp["q"]), part(inp["k"]), part(inp["v"]), part(inp["decay"]),
                             "gate", None)
-        o = to_host(out[s0:s1].transpose(0, 1)[None])
-        eo, ef = rel_err(o, ro), rel_err(to_host(fin[s:s + 1]), rf)
-        say(f"[varlen-full] sequence {s} ({s1 - s0} tokens): out {eo:.2e} final {ef:.2e}")
-        assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+        o, f = to_host(out[s0:s1].transpose(0, 1)[None]), to_host(fin[s:s + 1])
+        d_o, m_o = max(d_o, float(np.max(np.abs(o - ro)))), max(m_o, float(np.max(np.abs(ro))))
+        d_f, m_f = max(d_f, float(np.max(np.abs(f - rf)))), max(m_f, float(np.max(np.abs(rf))))
+    eo, ef = d_o / m_o, d_f / m_f
+    say(f"[varlen-full] all {len(lengths)} sequences: out {eo:.2e} final {ef:.2e}")
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]

@@ -1,9 +1,9 @@
 """Full-size parity on the named workloads, in the launch configuration the benchmark
 times (one fla_linattn_fwd call with the library's automatic schedule).
 
-The oracle runs every head of every workload; the million-token workload records a
-sample of ~1% of the output rows (every 97th token and the last one) plus the whole
-final state, to bound host memory.
+The oracle runs every head of every workload and every output row is compared; the
+million-token workload streams the oracle two heads at a time (1 GiB of fp64 outputs per
+head) and accumulates the global max-norm error over the heads.
 """
 import sys
 import time
@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity_util import TOL, rel_err, to_host
+from parity_util import TOL, to_host
 from workloads import WORKLOADS, generate_torch, to_numpy_input
 
 torch = pytest.importorskip("torch")
@@ -35,20 +35,26 @@ def test_full_size_workload(name):
                        normalize=w.normalize)
     torch.cuda.synchronize()
     print(f"[workload] {name}: gpu done {time.time() - t0:.1f}s", flush=True)
-    host = {k: (None if v is None else to_numpy_input(v)) for k, v in inp.items()}
-    rows = None
-    if w.T > 100000:
-        rows = list(range(0, w.T, 97)) + ([w.T - 1] if (w.T - 1) % 97 else [])
-    ro, rf = oracle.fwd(host["q"], host["k"], host["v"], host["decay"], w.decay, host["init"],
-                        phi_elu1=w.phi_elu1, normalize=w.normalize, rows=rows)
-    print(f"[workload] {name}: oracle done {time.time() - t0:.1f}s", flush=True)
-    del host
-    o = out if rows is None else out[:, :, torch.tensor(rows, device=out.device)]
-    o = to_host(o)
-    f = to_host(fin)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(f))
-    assert torch.isfinite(out.float()).all().item()
-    eo, ef = rel_err(o, ro), rel_err(f, rf)
-    print(f"[workload] {name}: out rel err {eo:.3e}, final rel err {ef:.3e}", flush=True)
     tol = TOL[w.dtype]
+    assert torch.isfinite(out.float()).all().item() and torch.isfinite(fin).all().item()
+    # heads in groups (all at once below 100k tokens), global max |diff| / max |ref|
+    step = w.H if w.T <= 100000 else 2
+    d_o = m_o = d_f = m_f = 0.0
+    for h0 in range(0, w.H, step):
+        hs = slice(h0, h0 + step)
+
+        def part(t):
+            return None if t is None else to_numpy_input(t[:, hs])
+
+        dec = None if inp["decay"] is None else (
+            to_numpy_input(inp["decay"][hs]) if w.decay == "gamma" else part(inp["decay"]))
+        ro, rf = oracle.fwd(part(inp["q"]), part(inp["k"]), part(inp["v"]), dec, w.decay,
+                            part(inp["init"]), phi_elu1=w.phi_elu1, normalize=w.normalize)
+        o, f = to_host(out[:, hs]), to_host(fin[:, hs])
+        d_o, m_o = max(d_o, float(np.max(np.abs(o - ro)))), max(m_o, float(np.max(np.abs(ro))))
+        d_f, m_f = max(d_f, float(np.max(np.abs(f - rf)))), max(m_f, float(np.max(np.abs(rf))))
+        del ro, o
+    print(f"[workload] {name}: oracle done {time.time() - t0:.1f}s", flush=True)
+    eo, ef = d_o / m_o, d_f / m_f
+    print(f"[workload] {name}: out rel err {eo:.3e}, final rel err {ef:.3e} (all rows)", flush=True)
     assert eo <= tol and ef <= tol

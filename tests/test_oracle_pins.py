@@ -384,3 +384,62 @@ def test_gdn_decay_ratio_in_mantissa_exponent_form():
                     assert abs(r[t, j] - exact) <= 64 * 2.0 ** -23 * exact, (t, j, r[t, j], exact)
                 else:
                     assert r[t, j] <= 2.0 ** -126
+
+
+# ---------------------------------------------------------------------------------------
+# The layer's input side: projections + feature map before the recurrence
+
+def test_fp64_inputs_equal_fp32_inputs_bitwise():
+    """fp64 inputs (the projection leg's own values) run the same arithmetic as fp32
+    inputs that hold the same numbers."""
+    rng = np.random.default_rng(21)
+    q, k, v = (rng.standard_normal((1, 2, 37, 8)).astype(np.float32) for _ in range(3))
+    dec = rng.uniform(0.5, 1.0, (1, 2, 37, 8)).astype(np.float32)
+    a = oracle.fwd(q, k, v, dec, "gate", None, phi_elu1=True, normalize=True)
+    b = oracle.fwd(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), dec, "gate",
+                   None, phi_elu1=True, normalize=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("kind", ["none", "gate", "token"])
+def test_projection_leg_with_identity_weights_is_the_plain_path(kind):
+    """W = identity (hidden = H*d): head h of token t takes x[b, t, h*d : h*d + d], the
+    token-major layout; the projection leg then equals fwd() on x rearranged by head, for
+    the decay laid out token-major.  Pins the head / column mapping and the transposes."""
+    from workloads import f32_to_bf16_bits
+    B, T, H, d = 2, 29, 3, 4
+    rng = np.random.default_rng(23)
+    x = f32_to_bf16_bits(rng.standard_normal((B, T, H * d)).astype(np.float32))
+    eye = f32_to_bf16_bits(np.eye(H * d, dtype=np.float32))
+    dec = None
+    if kind == "gate":
+        dec = rng.uniform(0.5, 1.0, (B, T, H, d)).astype(np.float32)
+    elif kind == "token":
+        dec = rng.uniform(0.5, 1.0, (B, T, H)).astype(np.float32)
+    out, fin = oracle.fwd_proj(x, eye, eye, eye, H, dec, kind, phi_elu1=True, normalize=True)
+    heads = np.ascontiguousarray(x.reshape(B, T, H, d).transpose(0, 2, 1, 3))
+    dh = None if dec is None else np.ascontiguousarray(np.swapaxes(dec, 1, 2))
+    ro, rf = oracle.fwd(heads, heads, heads, dh, kind, None, phi_elu1=True, normalize=True)
+    assert np.array_equal(out, ro.transpose(0, 2, 1, 3)) and np.array_equal(fin, rf)
+
+
+def test_projection_leg_mixes_hidden_features():
+    """The projections contract the hidden features: permuting them in x and in the rows of
+    every W leaves the result unchanged (a transposed W, or a contraction over the wrong
+    axis, would not), and scaling W_v scales the output (no normaliser; v carries no
+    feature map)."""
+    B, T, H, d, D = 1, 17, 2, 4, 8
+    rng = np.random.default_rng(29)
+    x = rng.standard_normal((B, T, D)).astype(np.float32)
+    wq, wk, wv = (rng.standard_normal((D, H * d)).astype(np.float32) for _ in range(3))
+    o1, f1 = oracle.fwd_proj(x, wq, wk, wv, H, phi_elu1=True)
+    perm = rng.permutation(D)
+    xp = np.ascontiguousarray(x[:, :, perm])
+    o2, f2 = oracle.fwd_proj(xp, *(np.ascontiguousarray(w[perm]) for w in (wq, wk, wv)), H,
+                             phi_elu1=True)
+    assert np.allclose(o2, o1, rtol=1e-12, atol=1e-12 * np.max(np.abs(o1)))
+    assert np.allclose(f2, f1, rtol=1e-12, atol=1e-12 * np.max(np.abs(f1)))
+    o3, _ = oracle.fwd_proj(x, wq, wk, (2.0 * wv).astype(np.float32), H, phi_elu1=True)
+    assert np.allclose(o3, 2.0 * o1, rtol=1e-13, atol=1e-13 * np.max(np.abs(o1)))
+    assert not np.allclose(oracle.fwd_proj(x, wq, wk, np.ascontiguousarray(wv[::-1]), H,
+                                           phi_elu1=True)[0], o1)

@@ -341,3 +341,75 @@ def strong_gates(kind: str, B: int, H: int, T: int, dk: int, seed: int) -> dict:
     iso = np.where(pick > 0.99, 0.0, iso)
     return {"sigmoid": plain.astype(np.float32), "uniform": uniform.astype(np.float32),
             "isolated": iso.astype(np.float32)}
+
+
+# The layer's input side (NEXT-4): activations x [B, T, hidden] and projection weights
+# W_q, W_k [hidden, H*dk], W_v [hidden, H*dv] (the GLA layer's shape: hidden 2048 = 16
+# heads of 128), scaled so that q, k ~ N(0, 1/dk) and v ~ N(0, 1) like the other
+# workloads; the gate token-major [B, T, H, dk], sigmoid(x)^(1/16).
+PROJ = {
+    "gla_proj_d128": dict(B=8, T=4096, hidden=2048, H=16, dk=128, dv=128, chunk=64,
+                          dtype="bf16", decay=DECAY_GATE, phi_elu1=False, normalize=False,
+                          seed=1010),
+}
+
+
+def generate_proj(spec: dict) -> dict:
+    """numpy inputs of a projection workload: x [B,T,hidden], w_q, w_k [hidden,H*dk], w_v
+    [hidden,H*dv] (bf16 bits or fp32), decay (gamma [H] / token-major gate or per-token
+    decay, fp32) and init (fp32 [B,H,dk,dv(+1)] or None if spec has no init_sigma)."""
+    B, T, D, H, dk, dv = (spec[k] for k in ("B", "T", "hidden", "H", "dk", "dv"))
+    bf = spec["dtype"] == "bf16"
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([spec["seed"], 11])))
+
+    def cast(a):
+        a = a.astype(np.float32)
+        return f32_to_bf16_bits(a) if bf else a
+
+    out = {"x": cast(g.standard_normal((B, T, D))),
+           "w_q": cast(g.standard_normal((D, H * dk)) / math.sqrt(D * dk)),
+           "w_k": cast(g.standard_normal((D, H * dk)) / math.sqrt(D * dk)),
+           "w_v": cast(g.standard_normal((D, H * dv)) / math.sqrt(D))}
+    kind = spec["decay"]
+    if kind == DECAY_GATE:
+        out["decay"] = np.power(1.0 / (1.0 + np.exp(-g.standard_normal((B, T, H, dk)))),
+                                1.0 / 16.0).astype(np.float32)
+    elif kind == DECAY_TOKEN:
+        out["decay"] = np.power(1.0 / (1.0 + np.exp(-g.standard_normal((B, T, H)))),
+                                1.0 / 16.0).astype(np.float32)
+    elif kind == DECAY_GAMMA:
+        out["decay"] = _gammas_offset(H, 1.0)
+    else:
+        out["decay"] = None
+    init = None
+    if spec.get("init_sigma", 0.0) > 0:
+        ncol = dv + (1 if spec.get("normalize") else 0)
+        init = (g.standard_normal((B, H, dk, ncol)) * spec["init_sigma"]).astype(np.float32)
+    out["init"] = init
+    return out
+
+
+def generate_proj_torch(spec: dict, device="cuda") -> dict:
+    """Device-side counterpart of generate_proj (torch's seeded generator)."""
+    import torch
+
+    B, T, D, H, dk, dv = (spec[k] for k in ("B", "T", "hidden", "H", "dk", "dv"))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(spec["seed"])
+    dt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
+
+    def normal(shape, scale):
+        return (torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * scale).to(dt)
+
+    out = {"x": normal((B, T, D), 1.0), "w_q": normal((D, H * dk), (D * dk) ** -0.5),
+           "w_k": normal((D, H * dk), (D * dk) ** -0.5), "w_v": normal((D, H * dv), D ** -0.5)}
+    kind = spec["decay"]
+    tail = {DECAY_GATE: (dk,), DECAY_TOKEN: ()}.get(kind)
+    out["decay"] = None
+    if tail is not None:
+        x = torch.randn((B, T, H) + tail, generator=gen, device=device, dtype=torch.float64)
+        out["decay"] = torch.sigmoid(x).pow(1.0 / 16.0).to(torch.float32)
+    elif kind == DECAY_GAMMA:
+        out["decay"] = torch.from_numpy(_gammas_offset(H, 1.0)).to(device)
+    out["init"] = None
+    return out
