@@ -655,12 +655,12 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
               if (!keep) acc[qq] = 0.f;
             }
           }
-          st_ptile<TIn>(sP + I * 256 + li * 16 + 4 * g, acc);
+          st_ptile<TIn>(sP + I * 256 + (16 * g + li) * 4, acc);
           if constexpr (K::SPLIT) {
             f32x4 lo;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) lo[qq] = acc[qq] - (float)(TIn)acc[qq];
-            st_ptile<TIn>(sPL + I * 256 + li * 16 + 4 * g, lo);
+            st_ptile<TIn>(sPL + I * 256 + (16 * g + li) * 4, lo);
           }
         }
       }
@@ -746,16 +746,16 @@ __global__ void __launch_bounds__((BwdCfg<TIn, ROLE, DY, DECAY>::NT)) chunk_bwd_
           constexpr int TA = tile_on<REV>(rb, 2 * u) ? rb * 4 + 2 * u : -1;
           constexpr int TB = tile_on<REV>(rb, 2 * u + 1) ? rb * 4 + 2 * u + 1 : -1;
           if constexpr (TA >= 0 || TB >= 0) {
-            const Frag<TIn> ph = ld_ptile2<TIn, TA, TB>(sP + li * 16 + 4 * g);
+            const Frag<TIn> ph = ld_ptile2<TIn, TA, TB>(sP + (16 * g + li) * 4);
             acc = mma(acc, zf[u], ph);
             if constexpr (K::SPLIT) {
-              acc = mma(acc, zf[u], ld_ptile2<TIn, TA, TB>(sPL + li * 16 + 4 * g));
+              acc = mma(acc, zf[u], ld_ptile2<TIn, TA, TB>(sPL + (16 * g + li) * 4));
               acc = mma(acc, zl[u], ph);
             }
           }
         } else {
           constexpr int TA = tile_on<REV>(rb, u) ? rb * 4 + u : -1;
-          if constexpr (TA >= 0) acc = mma(acc, zf[u], ld_ptile2<TIn, TA, -1>(sP + li * 16 + 4 * g));
+          if constexpr (TA >= 0) acc = mma(acc, zf[u], ld_ptile2<TIn, TA, -1>(sP + (16 * g + li) * 4));
         }
       });
       // inter-chunk: sum over y of X[r][y] S[y][x]

@@ -408,10 +408,12 @@ __device__ __forceinline__ Frag<TIn> ld_frag_t_at(const TIn *base, int ld, int c
 }
 
 // Score tiles in LDS (shared-score schedule): a 16 x 16 tile of A^T (rows j, columns i)
-// is kept as its accumulator image, lane (g, li) owning elements li * 16 + 4g .. +3, which
-// is also where the P V operand fragment of that lane reads them.
+// is kept as its accumulator image, lane l = 16 g + li owning elements 4 l .. 4 l + 3 (rows
+// 4g .. 4g+3 of column li), which is also where the P V operand fragment of that lane
+// reads them; a wave's 64 lanes touch one contiguous 512-byte (bf16) block, free of bank
+// conflicts.
 template <typename TIn>
-__device__ __forceinline__ void st_ptile(TIn *ltile, f32x4 x) { // ltile: + li * 16 + 4g
+__device__ __forceinline__ void st_ptile(TIn *ltile, f32x4 x) { // ltile: + 4 (16 g + li)
   if constexpr (sizeof(TIn) == 2) {
     *reinterpret_cast<bf16x4 *>(ltile) = bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
   } else {
@@ -419,7 +421,7 @@ __device__ __forceinline__ void st_ptile(TIn *ltile, f32x4 x) { // ltile: + li *
   }
 }
 // B operand of O^T += V^T A^T for K unit (two 16-row tiles ta, tb; tb < 0: zeros);
-// lbuf = score buffer + the lane's offset li * 16 + 4g.
+// lbuf = score buffer + the lane's offset 4 (16 g + li).
 template <typename TIn, int TA, int TB>
 __device__ __forceinline__ Frag<TIn> ld_ptile(const TIn *lbuf) {
   if constexpr (sizeof(TIn) == 2) {
@@ -1051,7 +1053,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
                           : 4 * g * K::LQ + li;                       // Kt^T
     const int lvt = K::BF ? (4 * g + (li >> 2)) * K::LV + 4 * (li & 3)
                           : 4 * g * K::LV + li;                       // V^T
-    const int lp = li * 16 + 4 * g;                                   // score tiles
+    const int lp = (16 * g + li) * 4;                                   // score tiles
     const int lel = K::PERM ? 8 * g : 4 * g;                          // eL
     auto scores = [&](int n) {
 #pragma unroll

@@ -41,12 +41,19 @@ bool is_pow2_dim(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128 |
 bool is_chunk(int64_t c) { return c == 16 || c == 32 || c == 64 || c == 128; }
 // Chunk sizes a call accepts: the tile sizes above, and larger powers of two up to 1024
 // (the FLA posts advise chunk_size = 512 for long-sequence training), which are evaluated
-// as consecutive 64-token sub-chunks, the tile size measured fastest on every workload
-// (the 128-token tile of the per-key gate runs five times slower: its score tiles no
-// longer fit the shared-score schedule).  Splitting a chunk into sub-chunks is exact in
-// real arithmetic (the state after a sub-chunk is the state before the next), so only the
-// rounding differs.
+// as consecutive 64-token sub-chunks (see tile_for).  Splitting a chunk into sub-chunks is
+// exact in real arithmetic (the state after a sub-chunk is the state before the next), so
+// only the rounding differs.
 bool is_chunk_arg(int64_t c) { return is_chunk(c) || c == 256 || c == 512 || c == 1024; }
+// The tile a requested chunk size runs with.  128-token tiles of the per-key gate and of
+// dk = 256 fall to the split schedule with its registers spilling inside the chunk loop
+// (measured 4.1 ms against 0.79 ms for the GLA workload, 1.65 against 0.22 ms for the
+// d256 retention workload): those run as two 64-token sub-chunks, like any larger chunk.
+int64_t tile_for(int64_t chunk, int64_t dk, int kind) {
+  if (chunk > 128) return 64;
+  if (chunk == 128 && (kind == DECAY_GATE || dk > 128)) return 64;
+  return chunk;
+}
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 ChunkLauncher find_launcher(bool bf16, int64_t dk, int64_t chunk, int decay, bool norm) {
@@ -368,7 +375,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   const bool bf16 = (flags & FLA_BF16) != 0;
   const bool norm = (flags & FLA_NORMALIZE) != 0;
   const int kind = decay_kind(flags);
-  if (chunk > 128) chunk = 64; // sub-chunks of the fastest tile (see is_chunk_arg)
+  chunk = tile_for(chunk, dk, kind); // sub-chunks of a faster tile (see is_chunk_arg)
   ChunkLauncher launch = find_launcher(bf16, dk, chunk, kind, norm);
   if (!launch) return FLA_ERR_UNSUPPORTED;
   hipStream_t s = ws.s;
@@ -574,7 +581,7 @@ int proj_impl(const void *x, const void *w_q, const void *w_k, const void *w_v,
     if (H * (dk > dv ? dk : dv) > ((int64_t)1 << 20) || B * H > ((int64_t)1 << 26))
       return FLA_ERR_UNSUPPORTED;
     if (!is_chunk_arg(chunk)) return FLA_ERR_UNSUPPORTED;
-    if (!find_launcher(bf16, dk, chunk > 128 ? 64 : chunk, decay_kind(flags),
+    if (!find_launcher(bf16, dk, tile_for(chunk, dk, decay_kind(flags)), decay_kind(flags),
                        (flags & FLA_NORMALIZE) != 0))
       return FLA_ERR_UNSUPPORTED;
   }
@@ -740,11 +747,10 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
   const int64_t nvs = dv / kSlice;
   const int64_t nch = (T + 63) / 64;
   if (nbh * nvs >= kMaxGrid || nbh * nch >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
-  // workspace: Tg = T diag(beta g) and Tb = T diag(beta) per chunk (C x C each), in the
-  // input type; Tg first, then Tb (its size is a multiple of 128 bytes, so Tb stays aligned)
-  const int64_t tb_bytes = nbh * nch * 64 * 64 * (bf16 ? 2 : 4); // Tb, and as much for Tg
+  // workspace: Tb = T diag(beta) per chunk (C x C), in the input type
+  const int64_t tb_bytes = nbh * nch * 64 * 64 * (bf16 ? 2 : 4);
   char *ws = nullptr;
-  if (hipMallocAsync(reinterpret_cast<void **>(&ws), 2 * tb_bytes, s) != hipSuccess)
+  if (hipMallocAsync(reinterpret_cast<void **>(&ws), tb_bytes, s) != hipSuccess)
     return FLA_ERR_DEVICE;
   GdnArgs a{};
   a.q = q; a.k = k; a.v = v;
@@ -756,8 +762,7 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
   a.H = (int)H; a.dv = (int)dv;
   a.nvs = (int)nvs;
   a.nch = (int)nch;
-  a.tg = ws;
-  a.tb = ws + tb_bytes;
+  a.tb = ws;
   int rc = FLA_OK;
   a.nunits = (int)(nbh * nch);
   if (launch.prep(a, (unsigned)a.nunits, s) != hipSuccess) rc = FLA_ERR_DEVICE;
@@ -895,7 +900,7 @@ int fla_linattn_segments_for(int64_t B, int64_t H, int64_t T, int64_t dk, int64_
   int rc = fla::check_common(B, H, dk, dv, flags, has_decay ? dummy : nullptr);
   if (rc != FLA_OK) return rc;
   if (!fla::is_chunk_arg(chunk)) return FLA_ERR_UNSUPPORTED;
-  if (chunk > 128) chunk = 64;
+  chunk = fla::tile_for(chunk, dk, fla::decay_kind(flags));
   const int64_t nch = (T + chunk - 1) / chunk;
   int64_t p = T == 0 ? 1 : fla::auto_segments(B, H, T, dv, chunk);
   if (p > nch && nch > 0) p = nch;

@@ -7,8 +7,8 @@
 // u_t = beta_t (v_t - alpha_t h_{t-1}^T k^_t), one chunk of L rows starting from state H,
 // with g the inclusive product of alpha inside the chunk, satisfies
 //     (I + A) U = diag(beta) V - diag(beta g) K^ H,   A_tj = beta_t (g_t / g_j) k^_t . k^_j (j < t),
-// so with T = (I + A)^-1 (unit lower triangular), Tb = T diag(beta) and Tg = T diag(beta g):
-//     U = Tb V - Tg (K^ H),
+// so with T = (I + A)^-1 (unit lower triangular) and Tb = T diag(beta):
+//     U = Tb (V - diag(g) K^ H),
 //     O = diag(g) Q H + (M (.) Q K^^T) U,        M_tj = g_t / g_j (j <= t),
 //     H <- g_L H + K^^T diag(g_L / g) U.
 // The ratios g_t / g_j (t >= j) are formed from g kept as a mantissa in [0.5, 1) and an
@@ -16,14 +16,15 @@
 // long its product underflows fp32 (a ratio is then only ever rounded or flushed to zero
 // where it is negligible), where g_t * (1 / g_j) would overflow (textbook chapter 1.6,
 // "gated delta rule": a decay near 0 clears the memory).  Plain g (<= 1) is used as is.
-// Tb and Tg do not depend on the state, so they are formed for every chunk at once by a
+// Tb does not depend on the state, so it is formed for every chunk at once by a
 // pre-pass (one workgroup per (b, h, chunk): K^ K^^T on MFMA gives A; the 16 x 16 diagonal
 // blocks of T are inverted by forward substitution, one wave each, and the off-diagonal
 // blocks follow block row by block row with fp32 MFMA), written to a workspace in the input
 // type.  The state pass streams the chunks, one workgroup per (b, h, 64-wide slice of dv):
 // four consumer waves keep the state columns in MFMA accumulators and compute per chunk
-// the masked scores, X = K^ H, U = Tb V - Tg X, the outputs and the state update, while
-// four producer waves stage the next chunk's q, k^, Tb, Tg and value slice.
+// the masked scores, X = K^ H, W = V - diag(g) X (in registers, fp32, rounded once), U = Tb W,
+// the outputs and the state update, while four producer waves stage the next chunk's q, k^,
+// Tb and value slice.
 #pragma once
 
 #include "chunk_bwd.hpp" // shared MFMA / LDS fragment helpers
@@ -36,7 +37,6 @@ struct GdnArgs {
   const float *init;         // [B][H][dk][dv] or null
   float *fin;                // [B][H][dk][dv] or null
   void *out;                 // [B][H][T][dv]
-  void *tg;                  // workspace [B][H][nch][C][C], input type: T diag(beta g) per chunk
   void *tb;                  // workspace [B][H][nch][C][C], input type: T diag(beta) per chunk
   int64_t T;
   int H, dv;
@@ -53,19 +53,18 @@ struct GdnCfg {
   static constexpr int KU = ES == 2 ? 32 : 16;
   static constexpr int LDK = DK + VE;  // Q, K^ rows
   static constexpr int LDV = XW + VE;  // V, U, Us rows
-  static constexpr int LDT = C + VE;   // Tb, Tg rows
+  static constexpr int LDT = C + VE;   // Tb rows
   static constexpr int NVQ = C * DK / VE / NT;  // 16-byte vectors per thread (q, k)
   static constexpr int NVV = C * XW / VE / NT;  // (v slice)
   static constexpr int VPRQ = DK / VE;          // vectors per q/k row
   static constexpr int NCB = DK / 16;           // 16-row blocks of the state
   static constexpr int NZU = C / KU;            // K units over the chunk rows
   static_assert(NVQ >= 1 && NVV >= 1 && VPRQ <= 64, "tile shape");
-  // pre-pass LDS: A (fp32) gives way to Tb and Tg once T is complete, T (fp32) to the V
-  // slices once Tb and Tg are formed, which fits three workgroups per CU (bf16, dk 128)
+  // pre-pass LDS: A (fp32), replaced block by block by T, over K^
   static constexpr int cmax(int x, int y) { return x > y ? x : y; }
   static constexpr int P_K = 0;
   // A, fp32 [C][C], over K^ (whose last reader is A itself: the tiles wait in registers
-  // for a barrier), replaced block by block by T = (I + A)^-1; Tb and Tg are formed from T
+  // for a barrier), replaced block by block by T = (I + A)^-1; Tb is formed from T
   // in registers as they are written out
   static constexpr int P_A = P_K;
   static constexpr int P_G = P_K + cmax(C * LDK * ES, C * C * 4);    // g [C], beta [C]
@@ -75,7 +74,7 @@ struct GdnCfg {
   static constexpr int P_GE = P_GMI + C * 4;                          // e [C] (int)
   static constexpr int P_LDS = P_GE + C * 4;
   // state-pass LDS: two input stages {q, k^, g, m, 1/m, e} (producer waves fill one while the
-  // consumer waves read the other); one {Tb, Tg, V slice} buffer, which the consumers use
+  // consumer waves read the other); one {Tb, V slice} buffer, which the consumers use
   // before the chunk's first barrier and the producers refill after it; the score tiles
   static constexpr int S_Q = 0;
   static constexpr int S_K = S_Q + C * LDK * ES;
@@ -85,8 +84,7 @@ struct GdnCfg {
   static constexpr int S_GE = S_GMI + C * 4;
   static constexpr int S_STAGE = S_GE + C * 4;
   static constexpr int S_TB = 2 * S_STAGE;          // Tb [C][LDT]
-  static constexpr int S_TG = S_TB + C * LDT * ES;  // Tg [C][LDT]
-  static constexpr int S_V = S_TG + C * LDT * ES;   // V slice [C][LDV]
+  static constexpr int S_V = S_TB + C * LDT * ES;   // V slice [C][LDV]
   static constexpr int S_P = S_V + C * LDV * ES;    // masked scores, 16 tile images
   static constexpr int NVT = C * C / VE / NT;       // 16-byte vectors per thread (Tb)
   static constexpr int S_LDS = S_P + 16 * 256 * ES;
@@ -185,7 +183,7 @@ __device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const Decay
           const int j = 16 * jb + 4 * g + qq;
           acc[qq] = (j <= t) ? dec.ratio(t, j) * acc[qq] : 0.f;
         }
-        st_ptile<TIn>(sP + I * 256 + li * 16 + 4 * g, acc);
+        st_ptile<TIn>(sP + I * 256 + (16 * g + li) * 4, acc);
       }
     }
   });
@@ -193,7 +191,7 @@ __device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const Decay
 
 } // namespace gdn
 
-// ---- pre-pass: Tb and Tg of one chunk ---------------------------------------------------
+// ---- pre-pass: Tb of one chunk ---------------------------------------------------
 template <typename TIn, int DK>
 __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   using K = GdnCfg<TIn, DK>;
@@ -331,42 +329,36 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
     __syncthreads();
   });
 
-  // Tb = T diag(beta) and Tg = T diag(beta g) to the workspace in the input type, formed
-  // from T in registers: element (t, j) = (T_tj beta_j) [g_j], rounded once; T's upper
-  // triangle (never written) is masked by j <= t.  Whole C x C tiles (their columns past
-  // the end are zero: beta = 0 there), 16-byte vectors.
-  auto t_scaled4 = [&](int t, int j0, bool with_g) -> f32x4 {
+  // Tb = T diag(beta) to the workspace in the input type, formed from T in registers:
+  // element (t, j) = T_tj beta_j, rounded once; T's upper triangle (never written) is
+  // masked by j <= t.  Whole C x C tiles (their columns past the end are zero: beta = 0
+  // there), 16-byte vectors.
+  auto t_scaled4 = [&](int t, int j0) -> f32x4 {
     const f32x4 tv = *reinterpret_cast<const f32x4 *>(sT + t * C + j0);
     const f32x4 bv = *reinterpret_cast<const f32x4 *>(sBeta + j0);
-    const f32x4 gv = *reinterpret_cast<const f32x4 *>(sG + j0);
     f32x4 r;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const float v = (j0 + s <= t) ? tv[s] : 0.f;
-      r[s] = with_g ? v * bv[s] * gv[s] : v * bv[s];
-    }
+    for (int s = 0; s < 4; ++s) r[s] = ((j0 + s <= t) ? tv[s] : 0.f) * bv[s];
     return r;
   };
-  auto put = [&](TIn *dst, int r, int c, bool with_g) {
+  auto put = [&](TIn *dst, int r, int c) {
     if constexpr (sizeof(TIn) == 2) {
-      const f32x4 lo = t_scaled4(r, c, with_g), hi = t_scaled4(r, c + 4, with_g);
+      const f32x4 lo = t_scaled4(r, c), hi = t_scaled4(r, c + 4);
       const bf16x8 v = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
                         (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
       *reinterpret_cast<bf16x8 *>(dst + r * C + c) = v;
     } else {
-      *reinterpret_cast<f32x4 *>(dst + r * C + c) = t_scaled4(r, c, with_g);
+      *reinterpret_cast<f32x4 *>(dst + r * C + c) = t_scaled4(r, c);
     }
   };
   {
     const int64_t off = (bh * a.nch + n) * C * C;
     TIn *gtb = static_cast<TIn *>(a.tb) + off;
-    TIn *gtg = static_cast<TIn *>(a.tg) + off;
     constexpr int VPR = C / VE;
 #pragma unroll
     for (int j = 0; j < K::NVT; ++j) {
       const int vi = tid + 256 * j, r = vi / VPR, c = (vi % VPR) * VE;
-      put(gtb, r, c, false);
-      put(gtg, r, c, true);
+      put(gtb, r, c);
     }
   }
 }
@@ -374,8 +366,8 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
 // ---- state pass ---------------------------------------------------------------------------
 // 8 waves: waves 4..7 (producers) load q and k of chunk n+1 into registers, normalise k
 // and write them, with the chunk's decay, into one LDS stage, and after the mid-chunk
-// barrier stage Tb, Tg and the value slice of the chunk the consumers take next, while
-// waves 0..3 (consumers) compute chunk n (scores, X = K^ H, U = Tb V - Tg X, outputs, state
+// barrier stage Tb and the value slice of the chunk the consumers take next, while waves
+// 0..3 (consumers) compute chunk n (scores, X = K^ H, U = Tb (V - diag(g) X), outputs, state
 // update) from the other stage; two barriers per chunk.
 template <typename TIn, int DK>
 __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
@@ -391,7 +383,6 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
                        reinterpret_cast<float *>(b + K::S_GMI), reinterpret_cast<int *>(b + K::S_GE)};
   };
   TIn *sTb = reinterpret_cast<TIn *>(lds + K::S_TB);
-  TIn *sTg = reinterpret_cast<TIn *>(lds + K::S_TG);
   TIn *sV = reinterpret_cast<TIn *>(lds + K::S_V);
   TIn *sP = reinterpret_cast<TIn *>(lds + K::S_P);
 
@@ -419,7 +410,6 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const TIn *gk = static_cast<const TIn *>(a.k) + bh * T * DK;
     const float *galpha = a.alpha + bh * T;
     const TIn *gtb = static_cast<const TIn *>(a.tb) + bh * nchunks * C * C;
-    const TIn *gtg = static_cast<const TIn *>(a.tg) + bh * nchunks * C * C;
     const TIn *gv = static_cast<const TIn *>(a.v) + bh * T * dv + vs * XW;
     // Two register sets of one chunk each: the loads of chunk n + 3 go out while chunk
     // n + 2's are still in flight and chunk n + 1 is staged.  Every load is unconditional
@@ -427,10 +417,10 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     // counts stay exact across the loop; rows past a chunk's end are masked when staged.
     // Staging one chunk past the end writes a buffer no consumer reads again.
     uint32_t rq[2][K::NVQ][4], rk[2][K::NVQ][4];
-    uint32_t rtb[2][K::NVT][4], rtg[2][K::NVT][4], rv[2][K::NVV][4];
+    uint32_t rtb[2][K::NVT][4], rv[2][K::NVV][4];
     float ralpha[2] = {1.f, 1.f};
     auto clamp_n = [&](int n) { return n < nchunks ? n : nchunks - 1; };
-    // Tb, Tg and the value slice of chunk n
+    // Tb and the value slice of chunk n
     auto load_tv = [&](auto S, int n) {
       constexpr int s = decltype(S)::value;
       n = clamp_n(n);
@@ -440,9 +430,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       for (int j = 0; j < K::NVT; ++j) {
         const int vi = ptid + 256 * j, r = vi / (C / VE), c = (vi % (C / VE)) * VE;
         const uint4 x = *reinterpret_cast<const uint4 *>(gtb + ((int64_t)n * C + r) * C + c);
-        const uint4 y = *reinterpret_cast<const uint4 *>(gtg + ((int64_t)n * C + r) * C + c);
         rtb[s][j][0] = x.x; rtb[s][j][1] = x.y; rtb[s][j][2] = x.z; rtb[s][j][3] = x.w;
-        rtg[s][j][0] = y.x; rtg[s][j][1] = y.y; rtg[s][j][2] = y.z; rtg[s][j][3] = y.w;
       }
 #pragma unroll
       for (int j = 0; j < K::NVV; ++j) {
@@ -458,7 +446,6 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       for (int j = 0; j < K::NVT; ++j) {
         const int vi = ptid + 256 * j, r = vi / (C / VE), c = (vi % (C / VE)) * VE;
         st_words_lds<4>(sTb + r * K::LDT + c, rtb[s][j]);
-        st_words_lds<4>(sTg + r * K::LDT + c, rtg[s][j]);
       }
 #pragma unroll
       for (int j = 0; j < K::NVV; ++j) {
@@ -523,7 +510,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     auto step = [&](auto S, int n) {
       stage(S, n + 1);
       load(S, n + 3);
-      __syncthreads(); // consumers: scores and U of chunk n formed (Tb, Tg, V read)
+      __syncthreads(); // consumers: scores and U of chunk n formed (Tb, V read)
       stage_tv(S, n + 1);
       load_tv(S, n + 3);
       __syncthreads(); // consumers: chunk n done; the next stage is complete
@@ -569,8 +556,8 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const float *sG = dec.g;
     const float gL = sG[C - 1]; // = g[L-1]: rows past the end carry alpha = 1
 
-    // ---- masked scores (shared by the consumer waves); U = Tb V - Tg (K^ H) (this wave's
-    // columns)
+    // ---- masked scores (shared by the consumer waves); U = Tb (V - diag(g) K^ H) (this
+    // wave's columns)
     gdn::scores<TIn, DK>(sQ, sK, dec, sP, wave, g, li);
     Frag<TIn> hf[DK / KU];
 #pragma unroll
@@ -594,29 +581,36 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       for (int u = 0; u < DK / KU; ++u) x = mma(x, ld_frag_at<TIn, true>(ka, u), hf[u]);
       xacc[tb] = x;
     }
-    Frag<TIn> xf[NZU];
-#pragma unroll
-    for (int u = 0; u < NZU; ++u) xf[u] = frag_of(xacc, u);
     f32x4 uacc[4], usacc[4];
-    Frag<TIn> vf[NZU]; // the value slice as the B operand of Tb V (K = the chunk's rows)
+    // W = V - diag(g) X as the B operand of Tb W (K = the chunk's rows): the value slice's
+    // fragment and X's accumulator tiles share the row order (rows 32u + 4g + s, + 16), so
+    // W is formed element by element in fp32 and rounded once
+    Frag<TIn> wf[NZU];
 #pragma unroll
-    for (int u = 0; u < NZU; ++u) vf[u] = ld_frag_t<TIn, true>(sV, LDV, 16 * wave, u, g, li);
+    for (int u = 0; u < NZU; ++u) {
+      const Frag<TIn> vf = ld_frag_t<TIn, true>(sV, LDV, 16 * wave, u, g, li);
+      constexpr int NS = sizeof(TIn) == 2 ? 8 : 4;
+      float w[8];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int half = sizeof(TIn) == 2 ? (s >> 2) : 0;
+        const int row = (sizeof(TIn) == 2 ? 32 * u + 16 * half : 16 * u) + 4 * g + (s & 3);
+        const float x = xacc[sizeof(TIn) == 2 ? 2 * u + half : u][s & 3];
+        w[s] = (float)vf[s] - sG[row] * x;
+      }
+      wf[u] = frag_from<TIn>(w);
+    }
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       f32x4 u0 = {0.f, 0.f, 0.f, 0.f};
       const TIn *ta = sTb + (16 * tb + li) * K::LDT + 4 * g;
 #pragma unroll
-      for (int u = 0; u < NZU; ++u) u0 = mma(u0, ld_frag_at<TIn, true>(ta, u), vf[u]);
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      const TIn *ga = sTg + (16 * tb + li) * K::LDT + 4 * g;
-#pragma unroll
-      for (int u = 0; u < NZU; ++u) x = mma(x, ld_frag_at<TIn, true>(ga, u), xf[u]);
+      for (int u = 0; u < NZU; ++u) u0 = mma(u0, ld_frag_at<TIn, true>(ta, u), wf[u]);
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int t = 16 * tb + 4 * g + qq;
-        const float uval = u0[qq] - x[qq];
-        uacc[tb][qq] = uval;
-        usacc[tb][qq] = uval * dec.ratio(C - 1, t);
+        uacc[tb][qq] = u0[qq];
+        usacc[tb][qq] = u0[qq] * dec.ratio(C - 1, t);
       }
     }
     __syncthreads(); // every consumer wave's score tiles written
@@ -638,10 +632,10 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
             constexpr int TA = (2 * u <= tb) ? tb * 4 + 2 * u : -1;
             constexpr int TB2 = (2 * u + 1 <= tb) ? tb * 4 + 2 * u + 1 : -1;
             if constexpr (TA >= 0 || TB2 >= 0)
-              oi = mma(oi, uf[u], ld_ptile2<TIn, TA, TB2>(sP + li * 16 + 4 * g));
+              oi = mma(oi, uf[u], ld_ptile2<TIn, TA, TB2>(sP + (16 * g + li) * 4));
           } else {
             constexpr int TA = (u <= tb) ? tb * 4 + u : -1;
-            if constexpr (TA >= 0) oi = mma(oi, uf[u], ld_ptile2<TIn, TA, -1>(sP + li * 16 + 4 * g));
+            if constexpr (TA >= 0) oi = mma(oi, uf[u], ld_ptile2<TIn, TA, -1>(sP + (16 * g + li) * 4));
           }
         });
         f32x4 ox = {0.f, 0.f, 0.f, 0.f};

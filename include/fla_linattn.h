@@ -83,7 +83,8 @@ enum fla_status {
  *                  256, 512, 1024}: the tile sizes are 16..128; a larger chunk (the FLA
  *                  posts advise chunk_size = 512 for long-sequence training) is evaluated
  *                  as consecutive 64-token sub-chunks (the fastest tile), which is exact
- *                  in real arithmetic.
+ *                  in real arithmetic; so is chunk 128 with FLA_DECAY_GATE or dk = 256,
+ *                  whose 128-token tiles measured 4-8x slower.
  *   flags        : FLA_* bits; at most one decay bit.
  *   stream       : hipStream_t or NULL.
  *
@@ -270,11 +271,11 @@ int fla_linattn_bwd_varlen(const void *q, const void *k, const void *v, const fl
  *   init_state, final_state: fp32 [B][H][dk][dv] (h = S^T as above) or NULL; may alias.
  *   dk in {64, 128} (fp32: 64); dv in {64, 128, 256}; chunk: any value fla_linattn_fwd
  *   takes (64-token tiles are used for all of them); flags: FLA_BF16 only.
- * Two launches: a pre-pass forms, for every chunk at once, the parts that do not depend on
- * the state (Tb = T diag(beta) and Tg = T diag(beta g) with T the inverse of the chunk's
- * unit lower-triangular delta system), into a stream-ordered workspace of
- * B H ceil(T / 64) 2 64 64 elem bytes; then one workgroup per (b, h, 64-wide value slice)
- * streams the chunks with the state on chip, forming U = Tb V - Tg (K^ H) per chunk.
+ * Two launches: a pre-pass forms, for every chunk at once, the part that does not depend
+ * on the state (Tb = T diag(beta) with T the inverse of the chunk's unit lower-triangular
+ * delta system), into a stream-ordered workspace of B H ceil(T / 64) 64 64 elem bytes;
+ * then one workgroup per (b, h, 64-wide value slice) streams the chunks with the state on
+ * chip, forming U = Tb (V - diag(g) K^ H) per chunk.
  */
 int fla_gdn_fwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
                 const float *init_state, void *out, float *final_state, int64_t B, int64_t H,

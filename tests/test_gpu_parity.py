@@ -149,11 +149,25 @@ def test_schedules(dtype, dk, chunk, decay, norm):
 
 
 def test_unsupported_combination_raises():
-    q = torch.zeros((1, 1, 128, 256), dtype=torch.float32, device="cuda")
+    # fp32 tiles of 128 tokens at dk = 128 exceed the LDS
+    q = torch.zeros((1, 1, 128, 128), dtype=torch.float32, device="cuda")
     v = torch.zeros((1, 1, 128, 64), dtype=torch.float32, device="cuda")
     with pytest.raises(fla.FlaError) as e:
         fla.fwd(q, q, v, chunk=128)
     assert e.value.status == fla.FLA_ERR_UNSUPPORTED
+
+
+def test_chunk_128_of_slow_tiles_runs_as_64():
+    """Chunk 128 with the per-key gate or dk = 256 runs as 64-token sub-chunks: bitwise the
+    chunk-64 result, and against the oracle (fp32 dk = 256 included, whose 128-token tile
+    would not fit the LDS)."""
+    for dtype, decay, dk in (("bf16", "gate", 128), ("f32", "none", 256), ("bf16", "gamma", 256)):
+        w, inp = small_case(dtype, decay, dk, 64, 3 * 128 + 9, B=1, H=2, chunk=128, init=True,
+                            seed=dk + len(decay))
+        check(w, inp, f"chunk 128 as 64: {dtype} {decay} dk={dk}")
+        o, f = run_gpu(w, inp)
+        o64, f64 = run_gpu(w, inp, chunk=64)
+        assert np.array_equal(o, o64) and np.array_equal(f, f64)
 
 
 # ---------------------------------------------------------------------------------------
