@@ -29,9 +29,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-# the forward kernel's sources: counters taken on another version of them do not apply
+# the kernels' sources: counters taken on another version of them do not apply
 KERNEL_SOURCES = [os.path.join(ROOT, "chunkwise_causal_linear_amd", "csrc", f)
-                  for f in ("chunk_fwd.hpp", "chunk_inst.hip", "dispatch.hpp")]
+                  for f in ("chunk_fwd.hpp", "chunk_inst.hip", "dispatch.hpp", "seg_state.hpp",
+                            "exact_fwd.hpp", "gdn_fwd.hpp", "gdn_inst.hip", "proj.hpp")]
 
 
 def kernel_source_hash() -> str:
@@ -40,6 +41,21 @@ def kernel_source_hash() -> str:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str):
+    """HBM bytes per step that the FETCH_SIZE / WRITE_SIZE counters read for a workload (the
+    committed counter summary), or None when there is none or the kernels' sources have
+    changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = tc.get("workloads", {}).get(name)
+    if rec and tc.get("kernel_source_hash") == kernel_source_hash():
+        return rec.get("hbm_bytes_per_step")
+    return None
 
 
 def algorithmic(w) -> tuple[float, float]:
@@ -494,10 +510,10 @@ def bench_gdn(torch, fla, args):
     # q, k, v read, out written; alpha and beta read; end state written (start state read)
     alg_bytes = th * (2 * w.dk + 2 * w.dv) * s + th * 8 + w.B * w.H * w.dk * w.dv * 4 * (
         2 if w.init_sigma > 0 else 1)
-    # per token-head: K^K^T and QK^T (causal halves, dk each), the solve's W = T K^ and
-    # U0 = T V (causal halves), U = U0 - W H, O = P U + Q H, the state update
+    # per token-head: K^K^T and QK^T (causal halves, dk each), X = K^ H (dk dv), U = Tb W
+    # and P U (causal halves, dv each), Q H and the state update (dk dv each)
     c = w.chunk
-    alg_flops = th * 2.0 * ((c + 1) / 2.0 * (2 * w.dk + w.dk + w.dv + w.dv) + 3.0 * w.dk * w.dv)
+    alg_flops = th * 2.0 * ((c + 1) / 2.0 * (2 * w.dk + 2 * w.dv) + 3.0 * w.dk * w.dv)
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     t = "__bf16" if w.dtype == "bf16" else "float"
     res = {
@@ -527,7 +543,7 @@ def bench_gdn(torch, fla, args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
             "algorithmic_bytes_per_launch": alg_bytes,
             "mfma_tflops": alg_flops / (ms * 1e-3) / 1e12,
             "mfma_frac": alg_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
@@ -617,7 +633,7 @@ def bench_proj(torch, fla, args):
             "peak": MFMA_PEAK_TFLOPS[sp["dtype"]],
             "unit": "TFLOP/s",
             "frac": tflops / MFMA_PEAK_TFLOPS[sp["dtype"]],
-            "traffic": None,
+            "traffic": measured_traffic(args.proj),
             "algorithmic_flops_per_step": gemm_flops + attn_flops,
             "algorithmic_bytes_per_step": alg_bytes,
             "hbm_GBs_algorithmic": alg_bytes / (ms * 1e-3) / 1e9,
@@ -769,15 +785,7 @@ def main():
     alg_bytes, alg_flops = algorithmic(w)
     tokens = w.B * w.T
     achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
-    traffic = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            tc = json.load(f)
-        rec = tc.get("workloads", {}).get(w.name) if args.layout == "bhtd" else None
-        if rec and tc.get("kernel_source_hash") == kernel_source_hash():
-            traffic = rec.get("hbm_bytes_per_step")
-    except (OSError, ValueError):
-        pass
+    traffic = measured_traffic(w.name) if args.layout == "bhtd" else None
 
     res = {
         "metric": "chunked linear-attn fwd tokens/s + roofline % (MFMA/HBM), B8 H16 T16384 d128",

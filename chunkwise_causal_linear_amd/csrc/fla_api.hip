@@ -48,10 +48,11 @@ bool is_chunk_arg(int64_t c) { return is_chunk(c) || c == 256 || c == 512 || c =
 // The tile a requested chunk size runs with.  128-token tiles of the per-key gate and of
 // dk = 256 fall to the split schedule with its registers spilling inside the chunk loop
 // (measured 4.1 ms against 0.79 ms for the GLA workload, 1.65 against 0.22 ms for the
-// d256 retention workload): those run as two 64-token sub-chunks, like any larger chunk.
-int64_t tile_for(int64_t chunk, int64_t dk, int kind) {
+// d256 retention workload), and fp32 128-token tiles at dk >= 128 do not fit the LDS:
+// those run as two 64-token sub-chunks, like any larger chunk.
+int64_t tile_for(int64_t chunk, int64_t dk, int kind, bool bf16) {
   if (chunk > 128) return 64;
-  if (chunk == 128 && (kind == DECAY_GATE || dk > 128)) return 64;
+  if (chunk == 128 && (kind == DECAY_GATE || dk > 128 || (!bf16 && dk >= 128))) return 64;
   return chunk;
 }
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -94,11 +95,21 @@ using SegStateKernel = void (*)(ChunkArgs);
 template <bool Z>
 SegStateKernel find_seg_state_z(bool bf16, int64_t dk) {
   switch (dk) {
-  case 16: return bf16 ? nullptr : &seg_state_kernel<float, 16, Z>; // (bf16: fused kernel's pass)
-  case 32: return bf16 ? &seg_state_kernel<__bf16, 32, Z> : &seg_state_kernel<float, 32, Z>;
-  case 64: return bf16 ? &seg_state_kernel<__bf16, 64, Z> : &seg_state_kernel<float, 64, Z>;
-  case 128: return bf16 ? &seg_state_kernel<__bf16, 128, Z> : &seg_state_kernel<float, 128, Z>;
-  case 256: return bf16 ? &seg_state_kernel<__bf16, 256, Z> : &seg_state_kernel<float, 256, Z>;
+  case 16: return bf16 ? nullptr : &seg_state_kernel<float, 16, Z, 1>; // (bf16: fused kernel's pass)
+  case 32: return bf16 ? &seg_state_kernel<__bf16, 32, Z, 1> : &seg_state_kernel<float, 32, Z, 1>;
+  case 64: return bf16 ? &seg_state_kernel<__bf16, 64, Z, 1> : &seg_state_kernel<float, 64, Z, 1>;
+  case 128: return bf16 ? &seg_state_kernel<__bf16, 128, Z, 1> : &seg_state_kernel<float, 128, Z, 1>;
+  case 256: return bf16 ? &seg_state_kernel<__bf16, 256, Z, 1> : &seg_state_kernel<float, 256, Z, 1>;
+  }
+  return nullptr;
+}
+// 128-column slices (one read of k for both halves of a 128-wide state): bf16, no
+// normaliser, 32 <= dk <= 128, dv > 64
+SegStateKernel find_seg_state_wide(int64_t dk) {
+  switch (dk) {
+  case 32: return &seg_state_kernel<__bf16, 32, false, 2>;
+  case 64: return &seg_state_kernel<__bf16, 64, false, 2>;
+  case 128: return &seg_state_kernel<__bf16, 128, false, 2>;
   }
   return nullptr;
 }
@@ -375,7 +386,7 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   const bool bf16 = (flags & FLA_BF16) != 0;
   const bool norm = (flags & FLA_NORMALIZE) != 0;
   const int kind = decay_kind(flags);
-  chunk = tile_for(chunk, dk, kind); // sub-chunks of a faster tile (see is_chunk_arg)
+  chunk = tile_for(chunk, dk, kind, bf16); // sub-chunks of a faster tile (see is_chunk_arg)
   ChunkLauncher launch = find_launcher(bf16, dk, chunk, kind, norm);
   if (!launch) return FLA_ERR_UNSUPPORTED;
   hipStream_t s = ws.s;
@@ -515,11 +526,18 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   a.fin_seg_stride = dk * ncol;
   a.seg_decay = wdec;
   a.state_only = 1;
-  if (const SegStateKernel st = gated ? nullptr : find_seg_state(bf16, dk, norm)) {
-    // constant decays: the end states are a plain reduction over each segment (seg_state.hpp)
+  const bool wide = !gated && bf16 && !norm && dv > kSlice && dk >= 32 && dk <= 128;
+  if (const SegStateKernel st = gated ? nullptr
+                                : wide ? find_seg_state_wide(dk)
+                                       : find_seg_state(bf16, dk, norm)) {
+    // constant decays: the end states are a plain reduction over each segment (seg_state.hpp),
+    // in value slices of 128 columns where that kernel takes them
     ChunkArgs sa = a;
+    const int64_t svs = wide ? (dv + 2 * kSlice - 1) / (2 * kSlice) : nvs;
+    sa.nvs = (int)svs;
+    const int64_t sgrid = ((nunits + 7) / 8) * 8 * svs;
     void *sargs[] = {&sa};
-    rc = hipLaunchKernel(reinterpret_cast<const void *>(st), dim3((unsigned)grid), dim3(256), sargs,
+    rc = hipLaunchKernel(reinterpret_cast<const void *>(st), dim3((unsigned)sgrid), dim3(256), sargs,
                          0, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
   } else {
     rc = launch(a, (unsigned)grid, s) == hipSuccess ? FLA_OK : FLA_ERR_DEVICE;
@@ -581,7 +599,7 @@ int proj_impl(const void *x, const void *w_q, const void *w_k, const void *w_v,
     if (H * (dk > dv ? dk : dv) > ((int64_t)1 << 20) || B * H > ((int64_t)1 << 26))
       return FLA_ERR_UNSUPPORTED;
     if (!is_chunk_arg(chunk)) return FLA_ERR_UNSUPPORTED;
-    if (!find_launcher(bf16, dk, tile_for(chunk, dk, decay_kind(flags)), decay_kind(flags),
+    if (!find_launcher(bf16, dk, tile_for(chunk, dk, decay_kind(flags), bf16), decay_kind(flags),
                        (flags & FLA_NORMALIZE) != 0))
       return FLA_ERR_UNSUPPORTED;
   }
@@ -593,27 +611,29 @@ int proj_impl(const void *x, const void *w_q, const void *w_k, const void *w_v,
     ws.release();
     return rc;
   }
-  const bool elu = (flags & FLA_PHI_ELU1) != 0;
-  auto gemm = [&](const void *w, void *y, int64_t n, bool phi) -> int {
-    ProjArgs pa{};
-    pa.x = x; pa.w = w; pa.y = y; pa.M = M; pa.K = (int)hidden; pa.N = (int)n;
-    pa.phi_elu1 = phi ? 1 : 0;
-    const int64_t blocks = ((M + 127) / 128) * ((n + 127) / 128);
-    if (blocks >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
-    const void *fn = bf16 ? (phi ? reinterpret_cast<const void *>(&proj_phi_kernel<__bf16, true>)
-                                 : reinterpret_cast<const void *>(&proj_phi_kernel<__bf16, false>))
-                          : (phi ? reinterpret_cast<const void *>(&proj_phi_kernel<float, true>)
-                                 : reinterpret_cast<const void *>(&proj_phi_kernel<float, false>));
-    void *args[] = {&pa};
-    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, ws.s) == hipSuccess
-               ? FLA_OK : FLA_ERR_DEVICE;
-  };
-  rc = gemm(w_q, pq, H * dk, elu);
-  if (rc == FLA_OK) rc = gemm(w_k, pk, H * dk, elu);
-  if (rc == FLA_OK) rc = gemm(w_v, pv, H * dv, false);
-  if (rc != FLA_OK) {
+  // the three projections in one launch (proj.hpp: they share x)
+  ProjArgs pa{};
+  pa.x = x;
+  pa.w[0] = w_q; pa.w[1] = w_k; pa.w[2] = w_v;
+  pa.y[0] = pq; pa.y[1] = pk; pa.y[2] = pv;
+  pa.M = M;
+  pa.K = (int)hidden;
+  pa.n[0] = pa.n[1] = (int)(H * dk);
+  pa.n[2] = (int)(H * dv);
+  for (int p = 0; p < 3; ++p) pa.nbn[p] = (pa.n[p] + 127) / 128;
+  pa.elu_mask = (flags & FLA_PHI_ELU1) ? 3 : 0;
+  const int64_t tiles = ((M + 127) / 128) * (pa.nbn[0] + pa.nbn[1] + pa.nbn[2]);
+  const int64_t blocks = ((tiles + 7) / 8) * 8;
+  if (blocks >= kMaxGrid) {
     ws.release();
-    return rc;
+    return FLA_ERR_UNSUPPORTED;
+  }
+  const void *fn = bf16 ? reinterpret_cast<const void *>(&proj_phi_kernel<__bf16>)
+                        : reinterpret_cast<const void *>(&proj_phi_kernel<float>);
+  void *args[] = {&pa};
+  if (hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, ws.s) != hipSuccess) {
+    ws.release();
+    return FLA_ERR_DEVICE;
   }
   // phi is already applied: the forward pass takes the projected q, k as they are
   return fwd_impl(pq, pk, pv, gate_or_gamma, init_state, out, final_state, B, H, T, dk, dv, chunk,
@@ -747,8 +767,8 @@ int gdn_impl(const void *q, const void *k, const void *v, const float *alpha, co
   const int64_t nvs = dv / kSlice;
   const int64_t nch = (T + 63) / 64;
   if (nbh * nvs >= kMaxGrid || nbh * nch >= kMaxGrid) return FLA_ERR_UNSUPPORTED;
-  // workspace: Tb = T diag(beta) per chunk (C x C), in the input type
-  const int64_t tb_bytes = nbh * nch * 64 * 64 * (bf16 ? 2 : 4);
+  // workspace: Tb = T diag(beta) per chunk (its lower-triangle blocks), in the input type
+  const int64_t tb_bytes = nbh * nch * kGdnTbElems * (bf16 ? 2 : 4);
   char *ws = nullptr;
   if (hipMallocAsync(reinterpret_cast<void **>(&ws), tb_bytes, s) != hipSuccess)
     return FLA_ERR_DEVICE;
@@ -900,7 +920,7 @@ int fla_linattn_segments_for(int64_t B, int64_t H, int64_t T, int64_t dk, int64_
   int rc = fla::check_common(B, H, dk, dv, flags, has_decay ? dummy : nullptr);
   if (rc != FLA_OK) return rc;
   if (!fla::is_chunk_arg(chunk)) return FLA_ERR_UNSUPPORTED;
-  chunk = fla::tile_for(chunk, dk, fla::decay_kind(flags));
+  chunk = fla::tile_for(chunk, dk, fla::decay_kind(flags), (flags & FLA_BF16) != 0);
   const int64_t nch = (T + chunk - 1) / chunk;
   int64_t p = T == 0 ? 1 : fla::auto_segments(B, H, T, dv, chunk);
   if (p > nch && nch > 0) p = nch;

@@ -37,13 +37,19 @@ struct GdnArgs {
   const float *init;         // [B][H][dk][dv] or null
   float *fin;                // [B][H][dk][dv] or null
   void *out;                 // [B][H][T][dv]
-  void *tb;                  // workspace [B][H][nch][C][C], input type: T diag(beta) per chunk
+  void *tb;                  // workspace [B][H][nch][kGdnTbElems], input type: T diag(beta)
+                             // per chunk, its lower-triangle 16 x 16 blocks (see tri_vec)
   int64_t T;
   int H, dv;
   int nvs;                   // 64-wide value slices
   int nch;                   // chunks per (b, h)
   int nunits;                // state pass: B * H * nvs; pre-pass: B * H * nch
 };
+
+// Tb per chunk in the workspace: the 10 blocks (bi, bj), bj <= bi, of its 64 x 64 lower
+// triangle in 16 x 16 blocks, block b = bi (bi + 1) / 2 + bj at b * 256, row-major inside
+// (the blocks above the diagonal are zero and are neither stored nor multiplied).
+constexpr int kGdnTbElems = 10 * 256;
 
 template <typename TIn, int DK>
 struct GdnCfg {
@@ -86,12 +92,25 @@ struct GdnCfg {
   static constexpr int S_TB = 2 * S_STAGE;          // Tb [C][LDT]
   static constexpr int S_V = S_TB + C * LDT * ES;   // V slice [C][LDV]
   static constexpr int S_P = S_V + C * LDV * ES;    // masked scores, 16 tile images
-  static constexpr int NVT = C * C / VE / NT;       // 16-byte vectors per thread (Tb)
+  static constexpr int NV_TB = kGdnTbElems / VE;    // 16-byte vectors of a chunk's Tb
+  static constexpr int NVT = (NV_TB + NT - 1) / NT; // per thread (the last ones partly idle)
   static constexpr int S_LDS = S_P + 16 * 256 * ES;
   static constexpr bool FITS = P_LDS <= kMaxLds && S_LDS <= kMaxLds;
 };
 
 namespace gdn {
+
+// Vector vi of a chunk's stored Tb (kGdnTbElems elements, VE per vector): its row r and
+// first column c in the 64 x 64 tile.  vi must be below kGdnTbElems / VE.
+template <int VE>
+__device__ __forceinline__ void tri_vec(int vi, int &r, int &c) {
+  constexpr int VPB = 16 / VE;                  // vectors per block row
+  const int b = vi / (16 * VPB), w = vi % (16 * VPB);
+  const int bi = b >= 6 ? 3 : b >= 3 ? 2 : b >= 1 ? 1 : 0;
+  const int bj = b - bi * (bi + 1) / 2;
+  r = 16 * bi + w / VPB;
+  c = 16 * bj + (w % VPB) * VE;
+}
 
 // k^ rows of one chunk (registers, 16-byte vectors in row-major order) into LDS; the
 // VPRQ vectors of a row sit in VPRQ consecutive lanes, which reduce its squared norm.
@@ -331,8 +350,8 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
 
   // Tb = T diag(beta) to the workspace in the input type, formed from T in registers:
   // element (t, j) = T_tj beta_j, rounded once; T's upper triangle (never written) is
-  // masked by j <= t.  Whole C x C tiles (their columns past the end are zero: beta = 0
-  // there), 16-byte vectors.
+  // masked by j <= t.  The lower-triangle blocks of the C x C tile (their columns past the
+  // end are zero: beta = 0 there), 16-byte vectors in the stored order (tri_vec).
   auto t_scaled4 = [&](int t, int j0) -> f32x4 {
     const f32x4 tv = *reinterpret_cast<const f32x4 *>(sT + t * C + j0);
     const f32x4 bv = *reinterpret_cast<const f32x4 *>(sBeta + j0);
@@ -346,19 +365,22 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
       const f32x4 lo = t_scaled4(r, c), hi = t_scaled4(r, c + 4);
       const bf16x8 v = {(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
                         (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
-      *reinterpret_cast<bf16x8 *>(dst + r * C + c) = v;
+      *reinterpret_cast<bf16x8 *>(dst) = v;
     } else {
-      *reinterpret_cast<f32x4 *>(dst + r * C + c) = t_scaled4(r, c);
+      *reinterpret_cast<f32x4 *>(dst) = t_scaled4(r, c);
     }
   };
   {
-    const int64_t off = (bh * a.nch + n) * C * C;
+    const int64_t off = (bh * a.nch + n) * kGdnTbElems;
     TIn *gtb = static_cast<TIn *>(a.tb) + off;
-    constexpr int VPR = C / VE;
 #pragma unroll
     for (int j = 0; j < K::NVT; ++j) {
-      const int vi = tid + 256 * j, r = vi / VPR, c = (vi % VPR) * VE;
-      put(gtb, r, c);
+      const int vi = tid + 256 * j;
+      if (vi < K::NV_TB) {
+        int r, c;
+        gdn::tri_vec<VE>(vi, r, c);
+        put(gtb + vi * VE, r, c);
+      }
     }
   }
 }
@@ -409,7 +431,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const TIn *gq = static_cast<const TIn *>(a.q) + bh * T * DK;
     const TIn *gk = static_cast<const TIn *>(a.k) + bh * T * DK;
     const float *galpha = a.alpha + bh * T;
-    const TIn *gtb = static_cast<const TIn *>(a.tb) + bh * nchunks * C * C;
+    const TIn *gtb = static_cast<const TIn *>(a.tb) + bh * nchunks * kGdnTbElems;
     const TIn *gv = static_cast<const TIn *>(a.v) + bh * T * dv + vs * XW;
     // Two register sets of one chunk each: the loads of chunk n + 3 go out while chunk
     // n + 2's are still in flight and chunk n + 1 is staged.  Every load is unconditional
@@ -426,10 +448,12 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       n = clamp_n(n);
       const int L = chunk_len(n);
       const int64_t t0 = (int64_t)n * C;
+      // (idle vector slots load the chunk's last vector again and store it again)
 #pragma unroll
       for (int j = 0; j < K::NVT; ++j) {
-        const int vi = ptid + 256 * j, r = vi / (C / VE), c = (vi % (C / VE)) * VE;
-        const uint4 x = *reinterpret_cast<const uint4 *>(gtb + ((int64_t)n * C + r) * C + c);
+        int vi = ptid + 256 * j;
+        vi = vi < K::NV_TB ? vi : K::NV_TB - 1;
+        const uint4 x = *reinterpret_cast<const uint4 *>(gtb + (int64_t)n * kGdnTbElems + vi * VE);
         rtb[s][j][0] = x.x; rtb[s][j][1] = x.y; rtb[s][j][2] = x.z; rtb[s][j][3] = x.w;
       }
 #pragma unroll
@@ -444,7 +468,9 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       const int L = chunk_len(clamp_n(n));
 #pragma unroll
       for (int j = 0; j < K::NVT; ++j) {
-        const int vi = ptid + 256 * j, r = vi / (C / VE), c = (vi % (C / VE)) * VE;
+        int vi = ptid + 256 * j, r, c;
+        vi = vi < K::NV_TB ? vi : K::NV_TB - 1;
+        gdn::tri_vec<VE>(vi, r, c);
         st_words_lds<4>(sTb + r * K::LDT + c, rtb[s][j]);
       }
 #pragma unroll
@@ -600,19 +626,28 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       }
       wf[u] = frag_from<TIn>(w);
     }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    // only Tb's lower-triangle blocks are in LDS: row block tb takes column blocks <= tb
+    static_for<0, 4>([&](auto TBI) {
+      constexpr int tb = decltype(TBI)::value;
       f32x4 u0 = {0.f, 0.f, 0.f, 0.f};
       const TIn *ta = sTb + (16 * tb + li) * K::LDT + 4 * g;
-#pragma unroll
-      for (int u = 0; u < NZU; ++u) u0 = mma(u0, ld_frag_at<TIn, true>(ta, u), wf[u]);
+      static_for<0, NZU>([&](auto UI) {
+        constexpr int u = decltype(UI)::value;
+        if constexpr (sizeof(TIn) == 2) {
+          // K unit u = column blocks 2u (low half of the fragment) and 2u + 1 (high half)
+          if constexpr (2 * u + 1 <= tb) u0 = mma(u0, ld_frag_at<TIn, true>(ta, u), wf[u]);
+          else if constexpr (2 * u <= tb) u0 = mma(u0, ld_frag_at<TIn, false>(ta, u), wf[u]);
+        } else {
+          if constexpr (u <= tb) u0 = mma(u0, ld_frag_at<TIn, true>(ta, u), wf[u]);
+        }
+      });
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int t = 16 * tb + 4 * g + qq;
         uacc[tb][qq] = u0[qq];
         usacc[tb][qq] = u0[qq] * dec.ratio(C - 1, t);
       }
-    }
+    });
     __syncthreads(); // every consumer wave's score tiles written
 
     // ---- O = (masked scores) U + diag(g) Q H -------------------------------------------

@@ -13,6 +13,13 @@
 // row-major X tile, B fragments transposed reads of the row-major W tile (the split K
 // convention of chunk_fwd.hpp for both).  The next K step's tiles are loaded into
 // registers while the current one is multiplied.
+//
+// One launch covers the three projections (they share X).  Tile order: each XCD (blocks
+// id, id + 8, ... run on XCD id mod 8) takes a contiguous range of the logical tile order,
+// which walks groups of GM row tiles and, inside a group, every column tile of the three
+// projections with the row tile fastest: the XCD's resident workgroups then share a few X
+// row tiles and W column tiles through its L2, where the plain row-major order made every
+// XCD read all of X (X fetched 8 times per projection).
 #pragma once
 
 #include "chunk_fwd.hpp"
@@ -20,13 +27,16 @@
 namespace fla {
 
 struct ProjArgs {
-  const void *x;   // [M][K]
-  const void *w;   // [K][N]
-  void *y;         // [M][N]
+  const void *x;     // [M][K]
+  const void *w[3];  // [K][n[p]] per projection
+  void *y[3];        // [M][n[p]]
   int64_t M;
-  int K, N;
-  int phi_elu1;
+  int K;
+  int n[3];          // columns per projection
+  int nbn[3];        // column tiles per projection (a zero skips the projection)
+  int elu_mask;      // bit p: phi = elu + 1 on projection p
 };
+constexpr int kProjGroup = 8; // row tiles per group of the tile order
 
 template <typename TIn>
 struct ProjCfg {
@@ -44,21 +54,39 @@ struct ProjCfg {
   static_assert(A_VEC >= 1 && B_VEC >= 1, "tile shape");
 };
 
-template <typename TIn, bool ELU>
+template <typename TIn>
 __global__ __launch_bounds__(256) void proj_phi_kernel(ProjArgs a) {
   using P = ProjCfg<TIn>;
   using F = Frag<TIn>;
   constexpr int BM = P::BM, BN = P::BN, BK = P::BK, VE = P::VE, LA = P::LA, LB = P::LB;
+  constexpr int GM = kProjGroup;
   __shared__ __attribute__((aligned(16))) TIn lds[2 * P::STAGE];
 
-  const int nbn = (a.N + BN - 1) / BN;
-  const int64_t m0 = (int64_t)(blockIdx.x / nbn) * BM;
-  const int n0 = (blockIdx.x % nbn) * BN;
+  // logical tile of this block (see the tile order above)
+  const int nbn_t = a.nbn[0] + a.nbn[1] + a.nbn[2];
+  const int64_t nbm = (a.M + BM - 1) / BM;
+  const int64_t total = nbm * nbn_t;
+  const int64_t per = (total + 7) / 8;
+  const int64_t L = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (L >= total) return;
+  const int64_t grp = L / ((int64_t)GM * nbn_t);
+  const int64_t mbase = grp * GM;
+  const int gm = (int)(nbm - mbase < GM ? nbm - mbase : GM);
+  const int64_t lin = L - grp * GM * nbn_t;
+  int nt = (int)(lin / gm), p = 0;
+  while (p < 2 && nt >= a.nbn[p]) {
+    nt -= a.nbn[p];
+    ++p;
+  }
+  const int N = a.n[p];
+  const int64_t m0 = (mbase + lin % gm) * BM;
+  const int n0 = nt * BN;
+  const bool elu = ((a.elu_mask >> p) & 1) != 0;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64; // this wave's 64 x 64 block
   const TIn *X = static_cast<const TIn *>(a.x);
-  const TIn *W = static_cast<const TIn *>(a.w);
+  const TIn *W = static_cast<const TIn *>(a.w[p]);
 
   uint32_t ra[P::A_VEC][4], rb[P::B_VEC][4];
   // rows past M and columns past N read a clamped in-range vector (discarded at the end)
@@ -75,8 +103,8 @@ __global__ __launch_bounds__(256) void proj_phi_kernel(ProjArgs a) {
     for (int j = 0; j < P::B_VEC; ++j) {
       const int vi = tid + P::NT * j, r = vi / P::B_VPR, c = (vi % P::B_VPR) * VE;
       int n = n0 + c;
-      n = n < a.N ? n : a.N - VE;
-      const uint4 v = *reinterpret_cast<const uint4 *>(W + (int64_t)(k0 + r) * a.N + n);
+      n = n < N ? n : N - VE;
+      const uint4 v = *reinterpret_cast<const uint4 *>(W + (int64_t)(k0 + r) * N + n);
       rb[j][0] = v.x; rb[j][1] = v.y; rb[j][2] = v.z; rb[j][3] = v.w;
     }
   };
@@ -128,7 +156,7 @@ __global__ __launch_bounds__(256) void proj_phi_kernel(ProjArgs a) {
   }
 
   // epilogue: acc[i][j] lane (g, li) holds Y[m = wm + 16 i + li][n = wn + 16 j + 4 g + r]
-  TIn *Y = static_cast<TIn *>(a.y);
+  TIn *Y = static_cast<TIn *>(a.y[p]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + wm + 16 * i + li;
@@ -136,15 +164,13 @@ __global__ __launch_bounds__(256) void proj_phi_kernel(ProjArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + wn + 16 * j + 4 * g;
-      if (n >= a.N) continue;
+      if (n >= N) continue;
       f32x4 o = acc[i][j];
+      if (elu) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = o[r];
-        if constexpr (ELU) x = x > 0.f ? x + 1.f : __expf(x);
-        o[r] = x;
+        for (int r = 0; r < 4; ++r) o[r] = o[r] > 0.f ? o[r] + 1.f : __expf(o[r]);
       }
-      st_out4<TIn>(Y + m * a.N + n, o);
+      st_out4<TIn>(Y + m * N + n, o);
     }
   }
 }

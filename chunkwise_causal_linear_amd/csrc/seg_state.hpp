@@ -8,29 +8,33 @@
 // needs no q, no outputs and no score tiles).  Per block of 64 tokens:
 //     E <- g^Lb E + K'^T V,   K' = diag(g^(Lb-1-j)) phi(K)
 // with bf16 (or fp32) MFMAs whose K^T and V operands come from row-major LDS tiles through
-// the transposed LDS load.  One workgroup of 4 waves per (b, h, segment, 64-wide value
-// slice), each wave owning 16 value columns of the dk x 64 fp32 end state in MFMA
-// accumulators; the next block's k and v are loaded into registers while the current one
-// is multiplied, and the small footprint (about 26 KB of LDS, few registers) lets several
-// workgroups share a CU to hide the memory latency.
+// the transposed LDS load.  One workgroup of 4 waves per (b, h, segment, value slice of
+// 64 NV columns), each wave owning 16 NV value columns of the dk x 64 NV fp32 end state in
+// MFMA accumulators; the next block's k and v are loaded into registers while the current
+// one is multiplied, and the small footprint (26 KB of LDS at NV = 1, 36 KB at NV = 2)
+// lets three or four workgroups share a CU to hide the memory latency.  NV = 2
+// (bf16, dk <= 128, dv > 64) reads each k row once for 128 value columns: with 64-wide
+// slices the sibling slice's copy of k came from HBM again whenever the two workgroups
+// drifted apart by more than the XCD's L2 holds.
 #pragma once
 
 #include "chunk_fwd.hpp"
 
 namespace fla {
 
-template <typename TIn, int DK>
+template <typename TIn, int DK, int NV>
 struct SegStateCfg {
   static constexpr int R = 64;                    // tokens per block
   static constexpr int NT = 256;
+  static constexpr int SW = kSlice * NV;          // value columns per workgroup
   static constexpr int ES = sizeof(TIn);
   static constexpr int VE = 16 / ES;              // elements per 16-byte vector
   static constexpr int LK = DK + VE;              // k tile row stride (elements)
-  static constexpr int LV = kSlice + (ES == 2 ? 16 : 4); // v tile row stride (conflict-free transposed reads)
+  static constexpr int LV = SW + (ES == 2 ? 16 : 4); // v tile row stride (conflict-free transposed reads)
   static constexpr int NVK = R * DK / VE / NT;    // 16-byte vectors per thread (k block)
-  static constexpr int NVV = R * kSlice / VE / NT; // (v block)
+  static constexpr int NVV = R * SW / VE / NT;    // (v block)
   static constexpr int VPRK = DK / VE;            // vectors per k row
-  static constexpr int VPRV = kSlice / VE;        // vectors per v row
+  static constexpr int VPRV = SW / VE;            // vectors per v row
   static constexpr int NCB = DK / 16;             // 16-key blocks of the state
   static constexpr int KU = ES == 2 ? 32 : 16;    // tokens per MFMA K unit
   static constexpr int NU = R / KU;
@@ -39,13 +43,16 @@ struct SegStateCfg {
 };
 
 // Z: the state carries the normaliser column (computed once per unit, by wave 0 of value
-// slice 0).  Four workgroups per CU (at most 128 registers per lane) up to dk = 128, so the
-// usual 1024 units of the segment schedule run in one round on 256 CUs.
-template <typename TIn, int DK, bool Z>
-__global__ __launch_bounds__(256, (DK <= 128 ? 4 : 2)) void seg_state_kernel(ChunkArgs a) {
-  using K = SegStateCfg<TIn, DK>;
+// slice 0).  Four workgroups per CU (at most 128 registers per lane) up to dk = 128 with
+// 64-column slices, so the usual 1024 units of the segment schedule run in one round on
+// 256 CUs; three with 128-column slices (their 512 units, likewise).  a.nvs counts value
+// slices of SW columns.
+template <typename TIn, int DK, bool Z, int NV>
+__global__ __launch_bounds__(256, (DK > 128 ? 2 : NV == 2 ? 3 : 4)) void seg_state_kernel(ChunkArgs a) {
+  using K = SegStateCfg<TIn, DK, NV>;
   using F = Frag<TIn>;
   constexpr int R = K::R, VE = K::VE, LK = K::LK, LV = K::LV, NCB = K::NCB;
+  static_assert(NV == 1 || (NV == 2 && !Z), "the normaliser column is summed by 64-wide slices");
   __shared__ __attribute__((aligned(16))) TIn lds[K::LDS_BYTES / sizeof(TIn)];
   TIn *sK = lds;
   TIn *sV = lds + R * LK;
@@ -74,7 +81,7 @@ __global__ __launch_bounds__(256, (DK <= 128 ? 4 : 2)) void seg_state_kernel(Chu
   const int64_t len = t_end > t_begin ? t_end - t_begin : 0;
   const int nblk = (int)((len + R - 1) / R);
   const float l2g = a.decay ? log2f(a.decay[h]) : 0.f; // gamma (or none: g = 1)
-  const int col0 = vs * kSlice;
+  const int col0 = vs * K::SW;
 
   // register prefetch of one block (clamped rows, masked when staged)
   uint32_t rk[K::NVK][4], rv[K::NVV][4];
@@ -128,10 +135,12 @@ __global__ __launch_bounds__(256, (DK <= 128 ? 4 : 2)) void seg_state_kernel(Chu
   };
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 acc[NCB];
+  f32x4 acc[NCB][NV];
   f32x4 zacc[Z ? NCB : 1];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero4;
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int j = 0; j < NV; ++j) acc[cb][j] = zero4;
 #pragma unroll
   for (int cb = 0; cb < (Z ? NCB : 1); ++cb) zacc[cb] = zero4;
   const bool do_z = Z && vs == 0 && wave == 0; // normaliser column: once per unit
@@ -148,35 +157,44 @@ __global__ __launch_bounds__(256, (DK <= 128 ? 4 : 2)) void seg_state_kernel(Chu
     __syncthreads();
     if (blk + 1 < nblk) load(blk + 1);
     const float gl = a.decay ? exp2f(l2g * (float)L) : 1.f;
-    F vf[K::NU];
+    F vf[K::NU][NV];
 #pragma unroll
-    for (int u = 0; u < K::NU; ++u) vf[u] = ld_frag_t<TIn, true>(sV, LV, 16 * wave, u, g, li);
+    for (int u = 0; u < K::NU; ++u)
+#pragma unroll
+      for (int j = 0; j < NV; ++j) vf[u][j] = ld_frag_t<TIn, true>(sV, LV, 16 * (NV * wave + j), u, g, li);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      f32x4 x = acc[cb] * gl;
+      f32x4 x[NV];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) x[j] = acc[cb][j] * gl;
       f32x4 z = zacc[Z ? cb : 0] * gl;
 #pragma unroll
       for (int u = 0; u < K::NU; ++u) {
         const F kf = ld_frag_t<TIn, true>(sK, LK, 16 * cb, u, g, li);
-        x = mma(x, kf, vf[u]);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) x[j] = mma(x[j], kf, vf[u][j]);
         if constexpr (Z) {
           if (do_z) z = mma(z, kf, ones);
         }
       }
-      acc[cb] = x;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) acc[cb][j] = x[j];
       if constexpr (Z) zacc[cb] = z;
     }
   }
 
   // end state (rows c = 16 cb + 4 g + r, column e) and the segment's decay product
   float *fo = a.fin + (int64_t)bh * a.fin_bh_stride + (int64_t)seg * a.fin_seg_stride;
-  const int e = col0 + 16 * wave + li;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int c = 16 * cb + 4 * g + r;
-      if (e < a.dv) fo[(int64_t)c * a.ncol + e] = acc[cb][r];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int e = col0 + 16 * (NV * wave + j) + li;
+        if (e < a.dv) fo[(int64_t)c * a.ncol + e] = acc[cb][j][r];
+      }
       if constexpr (Z) {
         if (do_z && li == 0) fo[(int64_t)c * a.ncol + a.dv] = zacc[cb][r];
       }

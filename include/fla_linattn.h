@@ -84,14 +84,15 @@ enum fla_status {
  *                  posts advise chunk_size = 512 for long-sequence training) is evaluated
  *                  as consecutive 64-token sub-chunks (the fastest tile), which is exact
  *                  in real arithmetic; so is chunk 128 with FLA_DECAY_GATE or dk = 256,
- *                  whose 128-token tiles measured 4-8x slower.
+ *                  whose 128-token tiles measured 4-8x slower, and fp32 chunk 128 at
+ *                  dk >= 128, whose 128-token tile does not fit the 160 KiB LDS.
  *   flags        : FLA_* bits; at most one decay bit.
  *   stream       : hipStream_t or NULL.
  *
  * T == 0 leaves out untouched and writes init_state (or zeros) to final_state.
- * The chunk size changes the rounding, never the mathematical result.  Combinations
- * whose on-chip tiles do not fit the 160 KiB LDS of a gfx950 CU (large dk with large
- * chunk, mostly in fp32) return FLA_ERR_UNSUPPORTED.
+ * The chunk size changes the rounding, never the mathematical result.  Every (dtype, dk,
+ * dv, chunk) combination listed above is supported; other values return
+ * FLA_ERR_UNSUPPORTED.
  * Decay range (FLA_DECAY_GATE and FLA_DECAY_TOKEN): any decay in [0, 1].  The fused
  * kernel factors a chunk's decays as phi(q) b and phi(k) / b (b: the product of the
  * decays from the chunk start), which is used while every chunk's product stays at or
@@ -273,7 +274,8 @@ int fla_linattn_bwd_varlen(const void *q, const void *k, const void *v, const fl
  *   takes (64-token tiles are used for all of them); flags: FLA_BF16 only.
  * Two launches: a pre-pass forms, for every chunk at once, the part that does not depend
  * on the state (Tb = T diag(beta) with T the inverse of the chunk's unit lower-triangular
- * delta system), into a stream-ordered workspace of B H ceil(T / 64) 64 64 elem bytes;
+ * delta system; its ten lower-triangle 16 x 16 blocks), into a stream-ordered workspace
+ * of B H ceil(T / 64) 2560 elem bytes;
  * then one workgroup per (b, h, 64-wide value slice) streams the chunks with the state on
  * chip, forming U = Tb (V - diag(g) K^ H) per chunk.
  */

@@ -87,7 +87,6 @@ def fwd_raw(lib, *, q=BOGUS, k=BOGUS, v=BOGUS, gate=None, init=None, out=BOGUS, 
     (dict(chunk=2048), fla.FLA_ERR_UNSUPPORTED),
     (dict(chunk=96), fla.FLA_ERR_UNSUPPORTED),
     (dict(chunk=8), fla.FLA_ERR_UNSUPPORTED),
-    (dict(dk=128, chunk=128), fla.FLA_ERR_UNSUPPORTED),                      # fp32 tiles > LDS
 ])
 def test_fwd_rejects_on_host(lib, kw, expected):
     assert fwd_raw(lib, **kw) == expected

@@ -148,20 +148,21 @@ def test_schedules(dtype, dk, chunk, decay, norm):
     check(w, inp, f"schedule {dtype} dk={dk} C={chunk} {decay} norm={norm}")
 
 
-def test_unsupported_combination_raises():
-    # fp32 tiles of 128 tokens at dk = 128 exceed the LDS
+def test_unsupported_chunk_raises():
     q = torch.zeros((1, 1, 128, 128), dtype=torch.float32, device="cuda")
     v = torch.zeros((1, 1, 128, 64), dtype=torch.float32, device="cuda")
-    with pytest.raises(fla.FlaError) as e:
-        fla.fwd(q, q, v, chunk=128)
-    assert e.value.status == fla.FLA_ERR_UNSUPPORTED
+    for chunk in (48, 2048, 8):
+        with pytest.raises(fla.FlaError) as e:
+            fla.fwd(q, q, v, chunk=chunk)
+        assert e.value.status == fla.FLA_ERR_UNSUPPORTED
 
 
 def test_chunk_128_of_slow_tiles_runs_as_64():
-    """Chunk 128 with the per-key gate or dk = 256 runs as 64-token sub-chunks: bitwise the
-    chunk-64 result, and against the oracle (fp32 dk = 256 included, whose 128-token tile
-    would not fit the LDS)."""
-    for dtype, decay, dk in (("bf16", "gate", 128), ("f32", "none", 256), ("bf16", "gamma", 256)):
+    """Chunk 128 with the per-key gate or dk = 256, and fp32 chunk 128 at dk >= 128, runs
+    as 64-token sub-chunks: bitwise the chunk-64 result, and against the oracle (the fp32
+    cases' 128-token tiles would not fit the LDS)."""
+    for dtype, decay, dk in (("bf16", "gate", 128), ("f32", "none", 256), ("bf16", "gamma", 256),
+                             ("f32", "gamma", 128), ("f32", "token", 128)):
         w, inp = small_case(dtype, decay, dk, 64, 3 * 128 + 9, B=1, H=2, chunk=128, init=True,
                             seed=dk + len(decay))
         check(w, inp, f"chunk 128 as 64: {dtype} {decay} dk={dk}")
