@@ -16,15 +16,17 @@
 // long its product underflows fp32 (a ratio is then only ever rounded or flushed to zero
 // where it is negligible), where g_t * (1 / g_j) would overflow (textbook chapter 1.6,
 // "gated delta rule": a decay near 0 clears the memory).  Plain g (<= 1) is used as is.
+// K^ = diag(rn) K with rn_t = 1 / max(|k_t|, 1e-12) is never formed: the kernels multiply
+// the keys as given and apply rn to the products' rows or columns in fp32.
 // Tb does not depend on the state, so it is formed for every chunk at once by a
-// pre-pass (one workgroup per (b, h, chunk): K^ K^^T on MFMA gives A; the 16 x 16 diagonal
+// pre-pass (one workgroup per (b, h, chunk): K K^T on MFMA, scaled, gives A; the 16 x 16 diagonal
 // blocks of T are inverted by forward substitution, one wave each, and the off-diagonal
 // blocks follow block row by block row with fp32 MFMA), written to a workspace in the input
 // type.  The state pass streams the chunks, one workgroup per (b, h, 64-wide slice of dv):
 // four consumer waves keep the state columns in MFMA accumulators and compute per chunk
 // the masked scores, X = K^ H, W = V - diag(g) X (in registers, fp32, rounded once), U = Tb W,
-// the outputs and the state update, while four producer waves stage the next chunk's q, k^,
-// Tb and value slice.
+// the outputs and the state update, while four producer waves stage the next chunk's q, k,
+// rn, Tb and value slice.
 #pragma once
 
 #include "chunk_bwd.hpp" // shared MFMA / LDS fragment helpers
@@ -78,8 +80,9 @@ struct GdnCfg {
   static constexpr int P_GM = P_BETA + C * 4;                         // g = m 2^e: m [C]
   static constexpr int P_GMI = P_GM + C * 4;                          // 1 / m [C]
   static constexpr int P_GE = P_GMI + C * 4;                          // e [C] (int)
-  static constexpr int P_LDS = P_GE + C * 4;
-  // state-pass LDS: two input stages {q, k^, g, m, 1/m, e} (producer waves fill one while the
+  static constexpr int P_RN = P_GE + C * 4;                          // 1 / |k| [C]
+  static constexpr int P_LDS = P_RN + C * 4;
+  // state-pass LDS: two input stages {q, k, g, m, 1/m, e, rn} (producer waves fill one while the
   // consumer waves read the other); one {Tb, V slice} buffer, which the consumers use
   // before the chunk's first barrier and the producers refill after it; the score tiles
   static constexpr int S_Q = 0;
@@ -88,13 +91,16 @@ struct GdnCfg {
   static constexpr int S_GM = S_G + C * 4;          // g = m 2^e: m [C], 1 / m [C], e [C]
   static constexpr int S_GMI = S_GM + C * 4;
   static constexpr int S_GE = S_GMI + C * 4;
-  static constexpr int S_STAGE = S_GE + C * 4;
+  static constexpr int S_RN = S_GE + C * 4;         // 1 / |k| [C]
+  static constexpr int S_STAGE = S_RN + C * 4;
   static constexpr int S_TB = 2 * S_STAGE;          // Tb [C][LDT]
   static constexpr int S_V = S_TB + C * LDT * ES;   // V slice [C][LDV]
   static constexpr int S_P = S_V + C * LDV * ES;    // masked scores, 16 tile images
+  // bf16: the scores' rounding remainders (hi + lo operands of O = P U, see the state pass)
+  static constexpr int S_PL = S_P + 16 * 256 * ES;
   static constexpr int NV_TB = kGdnTbElems / VE;    // 16-byte vectors of a chunk's Tb
   static constexpr int NVT = (NV_TB + NT - 1) / NT; // per thread (the last ones partly idle)
-  static constexpr int S_LDS = S_P + 16 * 256 * ES;
+  static constexpr int S_LDS = S_PL + (ES == 2 ? 16 * 256 * ES : 0);
   static constexpr bool FITS = P_LDS <= kMaxLds && S_LDS <= kMaxLds;
 };
 
@@ -112,10 +118,14 @@ __device__ __forceinline__ void tri_vec(int vi, int &r, int &c) {
   c = 16 * bj + (w % VPB) * VE;
 }
 
-// k^ rows of one chunk (registers, 16-byte vectors in row-major order) into LDS; the
-// VPRQ vectors of a row sit in VPRQ consecutive lanes, which reduce its squared norm.
+// k rows of one chunk (registers, 16-byte vectors in row-major order) into LDS as they
+// are, and rn[r] = 1 / max(|k_r|, 1e-12) (0 for a zero row): the unit key is
+// k^ = rn k, and every product with it takes rn as an fp32 row or column scale after the
+// MFMA, so k^ is never rounded to the input type (a bf16 k^ put 9e-3 of error into the
+// final state where consecutive keys are nearly parallel).  The VPRQ vectors of a row sit
+// in VPRQ consecutive lanes, which reduce its squared norm.
 template <typename TIn, int DK>
-__device__ __forceinline__ void stage_khat(const uint32_t (*rk)[4], TIn *sK, int tid) {
+__device__ __forceinline__ void stage_k(const uint32_t (*rk)[4], TIn *sK, float *rn, int tid) {
   using K = GdnCfg<TIn, DK>;
   constexpr int VE = K::VE;
 #pragma unroll
@@ -128,10 +138,8 @@ __device__ __forceinline__ void stage_khat(const uint32_t (*rk)[4], TIn *sK, int
     for (int e = 0; e < VE; ++e) ss += fk[e] * fk[e];
 #pragma unroll
     for (int d = 1; d < K::VPRQ; d <<= 1) ss += __shfl_xor(ss, d);
-    const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
-#pragma unroll
-    for (int e = 0; e < VE; ++e) fk[e] *= inv;
-    st_lds<TIn, VE>(sK + r * K::LDK + c, fk);
+    if (c == 0) rn[r] = ss > 0.f ? 1.f / fmaxf(sqrtf(ss), 1e-12f) : 0.f;
+    st_words_lds<4>(sK + r * K::LDK + c, rk[j]);
   }
 }
 
@@ -178,11 +186,14 @@ __device__ __forceinline__ void decay_scan(float alpha, int lane, float *g, floa
   g[lane] = ldexpf(mx, ex);
 }
 
-// Masked score tiles P[t][j] = (g_t / g_j) q_t . k^_j (j <= t); the image of tile (tb, jb) is
-// row-major [t][j].  10 tiles over the 4 waves.
+// Masked score tiles P[t][j] = (g_t / g_j) q_t . k^_j = (g_t / g_j) rn_j q_t . k_j (j <= t),
+// as accumulator images (lane
+// l of a tile owns elements 4l .. 4l + 3); 10 tiles over the 4 waves.  bf16: sPl receives
+// each element's rounding remainder P - bf16(P), also in bf16.
 template <typename TIn, int DK>
-__device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const Decays &dec,
-                                       TIn *sP, int wave, int g, int li) {
+__device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const float *rn,
+                                       const Decays &dec, TIn *sP, TIn *sPl, int wave, int g,
+                                       int li) {
   using K = GdnCfg<TIn, DK>;
   static_for<0, 16>([&](auto I) {
     constexpr int tb = I / 4, jb = I % 4;
@@ -200,9 +211,15 @@ __device__ __forceinline__ void scores(const TIn *sQ, const TIn *sK, const Decay
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int j = 16 * jb + 4 * g + qq;
-          acc[qq] = (j <= t) ? dec.ratio(t, j) * acc[qq] : 0.f;
+          acc[qq] = (j <= t) ? dec.ratio(t, j) * rn[j] * acc[qq] : 0.f;
         }
         st_ptile<TIn>(sP + I * 256 + (16 * g + li) * 4, acc);
+        if constexpr (sizeof(TIn) == 2) {
+          f32x4 lo;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) lo[qq] = acc[qq] - (float)(__bf16)acc[qq];
+          st_ptile<TIn>(sPl + I * 256 + (16 * g + li) * 4, lo);
+        }
       }
     }
   });
@@ -225,6 +242,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   float *sGm = reinterpret_cast<float *>(lds + K::P_GM);
   float *sGmi = reinterpret_cast<float *>(lds + K::P_GMI);
   int *sGe = reinterpret_cast<int *>(lds + K::P_GE);
+  float *sRn = reinterpret_cast<float *>(lds + K::P_RN);
   const gdn::Decays dec{sG, sGm, sGmi, sGe};
 
   const int tid = threadIdx.x;
@@ -258,7 +276,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
       const int r = (tid + 256 * j) / K::VPRQ;
       if (r >= L) rk[j][0] = rk[j][1] = rk[j][2] = rk[j][3] = 0u; // past the end: k = 0
     }
-    gdn::stage_khat<TIn, DK>(rk, sK, tid);
+    gdn::stage_k<TIn, DK>(rk, sK, sRn, tid);
     if (wave == 0) {
       gdn::decay_scan(lane < L ? al : 1.f, lane, sG, sGm, sGmi, sGe); // past the end: alpha 1, beta 0
       sBeta[lane] = lane < L ? be : 0.f;
@@ -266,7 +284,8 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
   }
   __syncthreads();
 
-  // A = strictly lower (beta_t g_t / g_j) k^_t . k^_j, fp32: tile k = tb (tb + 1) / 2 + jb
+  // A = strictly lower (beta_t g_t / g_j) k^_t . k^_j = (beta_t g_t / g_j) rn_t rn_j k_t . k_j,
+  // fp32: tile k = tb (tb + 1) / 2 + jb
   // (jb <= tb, 10 tiles) is wave k % 4's slot k / 4; the tiles wait in registers until
   // every wave has read K^, whose LDS they then take
   f32x4 atile[3];
@@ -290,13 +309,13 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
     const int k = 4 * sl + wave;
     if (k < 10) {
       const int tb = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0, jb = k - tb * (tb + 1) / 2;
-      // atile[sl][qq] = k^_j . k^_t with j = 16 jb + 4g + qq, t = 16 tb + li
+      // atile[sl][qq] = k_j . k_t with j = 16 jb + 4g + qq, t = 16 tb + li
       const int t = 16 * tb + li;
-      const float bt = sBeta[t];
+      const float bt = sBeta[t] * sRn[t];
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int jj = 16 * jb + 4 * g + qq;
-        sA[t * C + jj] = (jj < t) ? bt * dec.ratio(t, jj) * atile[sl][qq] : 0.f;
+        sA[t * C + jj] = (jj < t) ? bt * dec.ratio(t, jj) * sRn[jj] * atile[sl][qq] : 0.f;
       }
     }
   }
@@ -386,7 +405,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(GdnArgs a) {
 }
 
 // ---- state pass ---------------------------------------------------------------------------
-// 8 waves: waves 4..7 (producers) load q and k of chunk n+1 into registers, normalise k
+// 8 waves: waves 4..7 (producers) load q and k of chunk n+1 into registers, take k's reciprocal norms
 // and write them, with the chunk's decay, into one LDS stage, and after the mid-chunk
 // barrier stage Tb and the value slice of the chunk the consumers take next, while waves
 // 0..3 (consumers) compute chunk n (scores, X = K^ H, U = Tb (V - diag(g) X), outputs, state
@@ -399,6 +418,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[K::S_LDS];
   auto stage_q = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_Q); };
   auto stage_k = [&](int s) { return reinterpret_cast<TIn *>(lds + s * K::S_STAGE + K::S_K); };
+  auto stage_rn = [&](int s) { return reinterpret_cast<float *>(lds + s * K::S_STAGE + K::S_RN); };
   auto stage_dec = [&](int s) {
     unsigned char *b = lds + s * K::S_STAGE;
     return gdn::Decays{reinterpret_cast<float *>(b + K::S_G), reinterpret_cast<float *>(b + K::S_GM),
@@ -407,6 +427,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
   TIn *sTb = reinterpret_cast<TIn *>(lds + K::S_TB);
   TIn *sV = reinterpret_cast<TIn *>(lds + K::S_V);
   TIn *sP = reinterpret_cast<TIn *>(lds + K::S_P);
+  TIn *sPl = reinterpret_cast<TIn *>(lds + K::S_PL); // bf16 only
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -512,7 +533,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
         }
       }
       const int buf = n & 1;
-      gdn::stage_khat<TIn, DK>(rk[s], stage_k(buf), ptid);
+      gdn::stage_k<TIn, DK>(rk[s], stage_k(buf), stage_rn(buf), ptid);
       gdn::stage_raw<TIn, K::NVQ, K::VPRQ, LDK>(rq[s], stage_q(buf), ptid);
       if (pwave == 0) {
         const gdn::Decays d = stage_dec(buf);
@@ -578,13 +599,14 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
     const int64_t t0 = (int64_t)n * C;
     const TIn *sQ = stage_q(n & 1);
     const TIn *sK = stage_k(n & 1);
+    const float *sRn = stage_rn(n & 1);
     const gdn::Decays dec = stage_dec(n & 1);
     const float *sG = dec.g;
     const float gL = sG[C - 1]; // = g[L-1]: rows past the end carry alpha = 1
 
     // ---- masked scores (shared by the consumer waves); U = Tb (V - diag(g) K^ H) (this
     // wave's columns)
-    gdn::scores<TIn, DK>(sQ, sK, dec, sP, wave, g, li);
+    gdn::scores<TIn, DK>(sQ, sK, sRn, dec, sP, sPl, wave, g, li);
     Frag<TIn> hf[DK / KU];
 #pragma unroll
     for (int u = 0; u < DK / KU; ++u) {
@@ -622,7 +644,7 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
         const int half = sizeof(TIn) == 2 ? (s >> 2) : 0;
         const int row = (sizeof(TIn) == 2 ? 32 * u + 16 * half : 16 * u) + 4 * g + (s & 3);
         const float x = xacc[sizeof(TIn) == 2 ? 2 * u + half : u][s & 3];
-        w[s] = (float)vf[s] - sG[row] * x;
+        w[s] = (float)vf[s] - sG[row] * sRn[row] * x; // X = K^ H = diag(rn) K H
       }
       wf[u] = frag_from<TIn>(w);
     }
@@ -645,16 +667,30 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       for (int qq = 0; qq < 4; ++qq) {
         const int t = 16 * tb + 4 * g + qq;
         uacc[tb][qq] = u0[qq];
-        usacc[tb][qq] = u0[qq] * dec.ratio(C - 1, t);
+        usacc[tb][qq] = u0[qq] * dec.ratio(C - 1, t) * sRn[t]; // K^T (.) = K^T diag(rn) (.)
       }
     });
     __syncthreads(); // every consumer wave's score tiles written
 
     // ---- O = (masked scores) U + diag(g) Q H -------------------------------------------
+    // bf16: P and U enter as hi + lo pairs (P U ~ Ph Uh + Ph Ul + Pl Uh).  Where writes
+    // nearly cancel (near-parallel keys with beta ~ 1) U is a small difference of large
+    // terms and the output a sum of many such U rows with almost equal scores, so single
+    // bf16 roundings of P and U cost about 1e-2 of the output's scale; the pairs keep their
+    // error near that of the other roundings (k^, Tb, W, the H operand).
     {
-      Frag<TIn> uf[NZU];
+      Frag<TIn> uf[NZU], ufl[NZU];
 #pragma unroll
       for (int u = 0; u < NZU; ++u) uf[u] = frag_of(uacc, u);
+      if constexpr (sizeof(TIn) == 2) {
+        f32x4 ulo[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) ulo[tb][qq] = uacc[tb][qq] - (float)(__bf16)uacc[tb][qq];
+#pragma unroll
+        for (int u = 0; u < NZU; ++u) ufl[u] = frag_of(ulo, u);
+      }
       // formed transposed (O^T = U^T P^T + H^T Q^T: the same fragments with the operands
       // swapped), so a lane holds 4 adjacent value columns of one row: one 8-byte store
       const auto rs = out_rsrc(t0, L);
@@ -666,8 +702,12 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
           if constexpr (sizeof(TIn) == 2) {
             constexpr int TA = (2 * u <= tb) ? tb * 4 + 2 * u : -1;
             constexpr int TB2 = (2 * u + 1 <= tb) ? tb * 4 + 2 * u + 1 : -1;
-            if constexpr (TA >= 0 || TB2 >= 0)
-              oi = mma(oi, uf[u], ld_ptile2<TIn, TA, TB2>(sP + (16 * g + li) * 4));
+            if constexpr (TA >= 0 || TB2 >= 0) {
+              const Frag<TIn> ph = ld_ptile2<TIn, TA, TB2>(sP + (16 * g + li) * 4);
+              oi = mma(oi, uf[u], ph);
+              oi = mma(oi, ufl[u], ph);
+              oi = mma(oi, uf[u], ld_ptile2<TIn, TA, TB2>(sPl + (16 * g + li) * 4));
+            }
           } else {
             constexpr int TA = (u <= tb) ? tb * 4 + u : -1;
             if constexpr (TA >= 0) oi = mma(oi, uf[u], ld_ptile2<TIn, TA, -1>(sP + (16 * g + li) * 4));
@@ -687,17 +727,31 @@ __global__ void __launch_bounds__(512) gdn_state_kernel(GdnArgs a) {
       });
     }
 
-    // ---- H <- g_L H + K^^T (U (.) g_L / g) ----------------------------------------------
+    // ---- H <- g_L H + K^^T (U (.) g_L / g) = g_L H + K^T (U (.) rn g_L / g) ----------------
+    // bf16: the scaled U enters as a hi + lo pair, for the reason given for P U above (its
+    // single rounding alone put 5e-3 of error into the final state there)
     {
-      Frag<TIn> usf[NZU];
+      Frag<TIn> usf[NZU], usfl[NZU];
 #pragma unroll
       for (int u = 0; u < NZU; ++u) usf[u] = frag_of(usacc, u);
+      if constexpr (sizeof(TIn) == 2) {
+        f32x4 uslo[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) uslo[tb][qq] = usacc[tb][qq] - (float)(__bf16)usacc[tb][qq];
+#pragma unroll
+        for (int u = 0; u < NZU; ++u) usfl[u] = frag_of(uslo, u);
+      }
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f32x4 hnew = Hs[cb] * gL;
 #pragma unroll
-        for (int u = 0; u < NZU; ++u)
-          hnew = mma(hnew, ld_frag_t<TIn, true>(sK, LDK, 16 * cb, u, g, li), usf[u]);
+        for (int u = 0; u < NZU; ++u) {
+          const Frag<TIn> kf = ld_frag_t<TIn, true>(sK, LDK, 16 * cb, u, g, li);
+          hnew = mma(hnew, kf, usf[u]);
+          if constexpr (sizeof(TIn) == 2) hnew = mma(hnew, kf, usfl[u]);
+        }
         Hs[cb] = hnew;
       }
     }

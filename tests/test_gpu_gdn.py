@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 from parity_util import TOL, rel_err, to_device, to_host
-from workloads import GDN, Workload, generate_gdn, generate_gdn_torch, to_numpy_input
+from workloads import (GDN, Workload, f32_to_bf16_bits, generate_gdn, generate_gdn_torch,
+                       to_numpy_input)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -74,6 +75,31 @@ def test_gdn_strong_writes_and_slow_decay():
     inp["beta"] = (0.9 + 0.1 * inp["beta"]).astype(np.float32)
     inp["alpha"] = (0.999 + 0.001 * inp["alpha"]).astype(np.float32)
     check(w, inp, "beta ~ 1, alpha ~ 1")
+
+
+@pytest.mark.parametrize("memory", ["workload", "long"])
+def test_gdn_long_sequence(memory):
+    """65,536 tokens (four times the workload's length) on two heads: the workload's decays,
+    and a long memory (alpha = 1 - 1e-4 (1 - u), beta ~ 0.5) where rounding errors of the
+    carried state would have the whole sequence to add up."""
+    w, inp = case("bf16", 128, 128, 1 << 16, B=1, H=2, init=False, seed=860 + len(memory))
+    if memory == "long":
+        inp["alpha"] = (1.0 - 1e-4 * (1.0 - inp["alpha"])).astype(np.float32)
+        inp["beta"] = (0.5 * inp["beta"] + 0.25).astype(np.float32)
+    check(w, inp, f"T=65536, {memory} memory")
+
+
+def test_gdn_near_parallel_keys():
+    """Keys of one chunk nearly parallel (k_t = u + 0.05 n_t) with beta = 1: every write
+    almost cancels the previous one, the strictly lower A = beta_t g_t / g_j k^_t . k^_j is
+    close to all ones, and U = T diag(beta)(V - diag(g) K^ H) comes from the largest
+    cancellations the solve sees."""
+    w, inp = case("bf16", 128, 128, 4 * 64 + 17, B=1, H=2, seed=870)
+    rng = np.random.default_rng(871)
+    u = rng.standard_normal((1, 2, 1, 128))
+    inp["k"] = f32_to_bf16_bits((u + 0.05 * rng.standard_normal(inp["k"].shape)).astype(np.float32))
+    inp["beta"] = np.ones_like(inp["beta"])
+    check(w, inp, "near-parallel keys, beta = 1")
 
 
 def test_gdn_exact_recall():
