@@ -620,9 +620,11 @@ int proj_impl(const void *x, const void *w_q, const void *w_k, const void *w_v,
   pa.K = (int)hidden;
   pa.n[0] = pa.n[1] = (int)(H * dk);
   pa.n[2] = (int)(H * dv);
-  for (int p = 0; p < 3; ++p) pa.nbn[p] = (pa.n[p] + 127) / 128;
+  constexpr int BN = ProjCfg<float>::BN;
+  const int64_t bm = bf16 ? ProjCfg<__bf16>::BM : ProjCfg<float>::BM;
+  for (int p = 0; p < 3; ++p) pa.nbn[p] = (pa.n[p] + BN - 1) / BN;
   pa.elu_mask = (flags & FLA_PHI_ELU1) ? 3 : 0;
-  const int64_t tiles = ((M + 127) / 128) * (pa.nbn[0] + pa.nbn[1] + pa.nbn[2]);
+  const int64_t tiles = ((M + bm - 1) / bm) * (pa.nbn[0] + pa.nbn[1] + pa.nbn[2]);
   const int64_t blocks = ((tiles + 7) / 8) * 8;
   if (blocks >= kMaxGrid) {
     ws.release();

@@ -8,8 +8,8 @@
 // (v_mfma_f32_16x16x32_bf16, or 16x16x4 for fp32 inputs), phi (identity or elu + 1) and
 // the rounding to the input type in the epilogue.
 //
-// Tiles: 128 x 128 outputs per workgroup of 4 waves (2 x 2, 64 x 64 each: 16 accumulator
-// tiles), K in steps of 32 through two LDS stages; A fragments are row reads of the
+// Tiles: 256 x 128 outputs per workgroup of 4 waves (2 x 2, 128 x 64 each: 32 accumulator
+// tiles; fp32 128 x 128), K in steps of 32 through two LDS stages; A fragments are row reads of the
 // row-major X tile, B fragments transposed reads of the row-major W tile (the split K
 // convention of chunk_fwd.hpp for both).  The next K step's tiles are loaded into
 // registers while the current one is multiplied.
@@ -40,8 +40,12 @@ constexpr int kProjGroup = 8; // row tiles per group of the tile order
 
 template <typename TIn>
 struct ProjCfg {
-  static constexpr int BM = 128, BN = 128, BK = 32, NT = 256;
+  // bf16: 256 x 128 tiles, each wave 128 x 64 (8 x 4 accumulator tiles), so every 16-byte
+  // operand fragment read from LDS feeds 4 or 8 MFMAs; fp32 keeps 128 x 128 (64 x 64 per
+  // wave) for its registers
   static constexpr int ES = sizeof(TIn);
+  static constexpr int BM = ES == 2 ? 256 : 128, BN = 128, BK = 32, NT = 256;
+  static constexpr int MI = BM / 32;       // 16-row fragments per wave (wave rows BM / 2)
   static constexpr int VE = 16 / ES;
   static constexpr int LA = BK + VE;       // X tile row stride (elements)
   static constexpr int LB = BN + VE;       // W tile row stride
@@ -55,10 +59,11 @@ struct ProjCfg {
 };
 
 template <typename TIn>
-__global__ __launch_bounds__(256) void proj_phi_kernel(ProjArgs a) {
+__global__ __launch_bounds__(256, 2) void proj_phi_kernel(ProjArgs a) {
   using P = ProjCfg<TIn>;
   using F = Frag<TIn>;
   constexpr int BM = P::BM, BN = P::BN, BK = P::BK, VE = P::VE, LA = P::LA, LB = P::LB;
+  constexpr int MI = P::MI;
   constexpr int GM = kProjGroup;
   __shared__ __attribute__((aligned(16))) TIn lds[2 * P::STAGE];
 
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(256) void proj_phi_kernel(ProjArgs a) {
   const bool elu = ((a.elu_mask >> p) & 1) != 0;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64; // this wave's 64 x 64 block
+  const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * 64; // this wave's BM/2 x 64 block
   const TIn *X = static_cast<const TIn *>(a.x);
   const TIn *W = static_cast<const TIn *>(a.w[p]);
 
@@ -123,9 +128,9 @@ __global__ __launch_bounds__(256) void proj_phi_kernel(ProjArgs a) {
   };
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 acc[4][4];
+  f32x4 acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
 
@@ -139,13 +144,13 @@ __global__ __launch_bounds__(256) void proj_phi_kernel(ProjArgs a) {
     const TIn *sA = lds + st * P::STAGE, *sB = sA + BM * LA;
 #pragma unroll
     for (int u = 0; u < P::NKU; ++u) {
-      F af[4], bf[4];
+      F af[MI], bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = ld_frag<TIn, true>(sA + (wm + 16 * i + li) * LA, u, g);
+      for (int i = 0; i < MI; ++i) af[i] = ld_frag<TIn, true>(sA + (wm + 16 * i + li) * LA, u, g);
 #pragma unroll
       for (int j = 0; j < 4; ++j) bf[j] = ld_frag_t<TIn, true>(sB, LB, wn + 16 * j, u, g, li);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mma(acc[i][j], bf[j], af[i]);
     }
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(256) void proj_phi_kernel(ProjArgs a) {
   // epilogue: acc[i][j] lane (g, li) holds Y[m = wm + 16 i + li][n = wn + 16 j + 4 g + r]
   TIn *Y = static_cast<TIn *>(a.y[p]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MI; ++i) {
     const int64_t m = m0 + wm + 16 * i + li;
     if (m >= a.M) continue;
 #pragma unroll
