@@ -429,12 +429,28 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
     if ((rc = ws.get(flag_bytes(nseg), &f)) != FLA_OK) return rc;
     unsafe = static_cast<int *>(f);
   }
+  // The exact kernel's start states: with an in-place resume, the normaliser and several
+  // value slices, a private copy (value slice 0 writes the z column of the final state,
+  // which the other slices read as their start).
+  const float *exact_init = init_state;
+  auto private_start = [&](const float **dst) -> int {
+    void *tmp = nullptr;
+    int r = ws.get(state_elems * (int64_t)sizeof(float), &tmp);
+    if (r == FLA_OK) r = launch_fill(static_cast<float *>(tmp), init_state, state_elems, s);
+    if (r != FLA_OK) {
+      ws.release();
+      return r;
+    }
+    *dst = static_cast<const float *>(tmp);
+    return FLA_OK;
+  };
+  const bool shared_z = init_state && init_state == final_state && norm && nvs > 1;
   auto run_exact = [&]() -> int {
     if (!gated) return FLA_OK;
     ExactArgs e{};
     e.q = q; e.k = k; e.v = v;
     e.decay = gate_or_gamma;
-    e.init = init_state;
+    e.init = exact_init;
     e.fin = final_state;
     e.out = out;
     e.unsafe = unsafe;
@@ -467,14 +483,9 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
     // The z column is read by every value slice and written by slice 0 only: an in-place
     // resume with several slices reads a private copy of the start state.
     const float *ini = init_state;
-    if (init_state && init_state == final_state && norm && nvs > 1) {
-      void *tmp = nullptr;
-      if ((rc = ws.get(state_elems * (int64_t)sizeof(float), &tmp)) != FLA_OK) return rc;
-      if ((rc = launch_fill(static_cast<float *>(tmp), init_state, state_elems, s)) != FLA_OK) {
-        ws.release();
-        return rc;
-      }
-      ini = static_cast<const float *>(tmp);
+    if (shared_z) {
+      if ((rc = private_start(&ini)) != FLA_OK) return rc;
+      exact_init = ini;
     }
     // packed sequences: dispatch the longest first (the short ones fill in behind them)
     int *order = nullptr;
@@ -513,8 +524,12 @@ int fwd_impl(const void *q, const void *k, const void *v, const float *gate_or_g
   // Segment schedule: (A) end state of every segment from a zero start, (B) scan over
   // segments, (C) outputs of every segment from its start state.
   const int64_t ws_states = nbh * nseg * dk * ncol;
+  if (gated && shared_z && (rc = private_start(&exact_init)) != FLA_OK) return rc;
   void *wsp = nullptr;
-  if ((rc = ws.get(seg_ws_bytes(nseg), &wsp)) != FLA_OK) return rc;
+  if ((rc = ws.get(seg_ws_bytes(nseg), &wsp)) != FLA_OK) {
+    ws.release();
+    return rc;
+  }
   float *wst = static_cast<float *>(wsp);
   float *wdec = wst + ws_states;
 
