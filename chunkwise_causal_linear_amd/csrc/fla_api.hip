@@ -635,9 +635,9 @@ int proj_impl(const void *x, const void *w_q, const void *w_k, const void *w_v,
   pa.K = (int)hidden;
   pa.n[0] = pa.n[1] = (int)(H * dk);
   pa.n[2] = (int)(H * dv);
-  constexpr int BN = ProjCfg<float>::BN;
+  const int bn = bf16 ? ProjCfg<__bf16>::BN : ProjCfg<float>::BN;
   const int64_t bm = bf16 ? ProjCfg<__bf16>::BM : ProjCfg<float>::BM;
-  for (int p = 0; p < 3; ++p) pa.nbn[p] = (pa.n[p] + BN - 1) / BN;
+  for (int p = 0; p < 3; ++p) pa.nbn[p] = (pa.n[p] + bn - 1) / bn;
   pa.elu_mask = (flags & FLA_PHI_ELU1) ? 3 : 0;
   const int64_t tiles = ((M + bm - 1) / bm) * (pa.nbn[0] + pa.nbn[1] + pa.nbn[2]);
   const int64_t blocks = ((tiles + 7) / 8) * 8;

@@ -270,7 +270,7 @@ int fla_linattn_bwd_varlen(const void *q, const void *k, const void *v, const fl
  *           mantissa-exponent form, so any product is exact or negligibly small);
  *   beta  : fp32 [B][H][T], the write strength in [0, 1]; 4-byte aligned.
  *   init_state, final_state: fp32 [B][H][dk][dv] (h = S^T as above) or NULL; may alias.
- *   dk in {64, 128} (fp32: 64); dv in {64, 128, 256}; chunk: any value fla_linattn_fwd
+ *   dk in {64, 128} (fp32: 64); dv a multiple of 64 up to 256; chunk: any value fla_linattn_fwd
  *   takes (64-token tiles are used for all of them); flags: FLA_BF16 only.
  * Two launches: a pre-pass forms, for every chunk at once, the part that does not depend
  * on the state (Tb = T diag(beta) with T the inverse of the chunk's unit lower-triangular
