@@ -177,3 +177,41 @@ def test_gated_delta_rule_strong_decay(dtype, gate_set):
     say(f"[strong] gdn {dtype} {gate_set}: out {eo:.2e} final {ef:.2e}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(f))
     assert eo <= TOL[dtype] and ef <= TOL[dtype], (eo, ef)
+
+
+
+@pytest.mark.parametrize("name", ["gla_d128", "token_decay_d128"])
+def test_full_size_plain_sigmoid_gates(name):
+    """A full-size workload (B8 H16 T16384 d128, bf16) with plain sigmoid(x) decays in place
+    of its usual ones: a 64-token chunk then multiplies to about 2^-74 and many units fall
+    below the fused kernel's range.  Same call as the benchmark; every output row of every
+    head against the oracle."""
+    import time
+
+    from workloads import WORKLOADS, generate_torch, to_numpy_input
+
+    w = WORKLOADS[name]
+    inp = generate_torch(w, "cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 99)
+    decay = torch.empty_like(inp["decay"])
+    for b in range(w.B):
+        x = torch.randn(decay.shape[1:], generator=gen, device="cuda", dtype=torch.float64)
+        decay[b] = torch.sigmoid(x).to(torch.float32)
+    say(f"[strong-full] {name}: {w}")
+    torch.cuda.synchronize()
+    t0 = time.time()
+    out, fin = fla.fwd(inp["q"], inp["k"], inp["v"], decay, decay_kind=w.decay,
+                       init_state=inp["init"], chunk=w.chunk)
+    torch.cuda.synchronize()
+    say(f"[strong-full] {name}: gpu done {time.time() - t0:.2f}s")
+    assert torch.isfinite(out.float()).all().item() and torch.isfinite(fin).all().item()
+
+    def part(t):
+        return None if t is None else to_numpy_input(t)
+
+    ro, rf = oracle.fwd(part(inp["q"]), part(inp["k"]), part(inp["v"]), part(decay), w.decay,
+                        part(inp["init"]))
+    eo, ef = rel_err(to_host(out), ro), rel_err(to_host(fin), rf)
+    say(f"[strong-full] {name}: out {eo:.2e} final {ef:.2e} (all rows) {time.time() - t0:.1f}s")
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
