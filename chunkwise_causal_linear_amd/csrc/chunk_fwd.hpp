@@ -90,11 +90,13 @@ struct ChunkArgs {
 // with a chunk below it is recomputed by the exact 16-token kernel (exact_fwd.hpp).
 constexpr float kSafeDecay = 0x1p-100f;
 
-template <typename TIn, int DK, int C, int DECAY, bool NORM>
-struct Cfg {
+// PB: bytes of padding after each Qt / Kt row (the tile's row stride is DK + PB / ES
+// elements); see Cfg below for the choice.
+template <typename TIn, int DK, int C, int DECAY, bool NORM, int PB>
+struct CfgP {
   static constexpr int ES = sizeof(TIn);
   static constexpr bool BF = (ES == 2);
-  static constexpr int PAD = 16 / ES;    // 16 bytes of row padding
+  static constexpr int PAD = PB / ES;
   static constexpr int LQ = DK + PAD;    // row stride (elements) of Qt, Kt
   static constexpr int NB = C / 16;      // 16-row blocks per chunk
   static constexpr int NCB = DK / 16;    // 16-row blocks of the state
@@ -213,6 +215,25 @@ struct Cfg {
     return PERM ? 32 * (cb >> 1) + 8 * g + 4 * (cb & 1) + r : 16 * cb + 4 * g + r;
   }
 };
+
+// Row padding of the Qt / Kt tiles.  With 16 bytes (bf16 row stride = 4 words mod 64) the
+// 16-byte operand reads of 16 rows collide in the LDS banks and take 1.8x the cycles of a
+// stride of 8 words mod 64 (32 bytes of padding), and the transposed reads 1.1-1.3x
+// (measured with an in-bounds read-pattern probe on gfx950).  bf16 tiles take the 32-byte
+// padding where it leaves the schedule and the stage count unchanged; where the wider rows
+// would push the tiles into a schedule with fewer stages (128-token tiles) the 16-byte
+// padding stays.
+template <typename TIn, int DK, int C, int DECAY, bool NORM>
+constexpr int qk_pad_bytes() {
+  using A = CfgP<TIn, DK, C, DECAY, NORM, 16>;
+  using B = CfgP<TIn, DK, C, DECAY, NORM, 32>;
+  return (A::BF && B::FITS && A::SHARE == B::SHARE && A::SPLIT == B::SPLIT &&
+          A::STAGES == B::STAGES && A::LV == B::LV)
+             ? 32
+             : 16;
+}
+template <typename TIn, int DK, int C, int DECAY, bool NORM>
+struct Cfg : CfgP<TIn, DK, C, DECAY, NORM, qk_pad_bytes<TIn, DK, C, DECAY, NORM>()> {};
 
 // ---------------------------------------------------------------------------------
 // small helpers
