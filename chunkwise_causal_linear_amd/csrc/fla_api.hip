@@ -49,10 +49,16 @@ bool is_chunk_arg(int64_t c) { return is_chunk(c) || c == 256 || c == 512 || c =
 // dk = 256 fall to the split schedule with its registers spilling inside the chunk loop
 // (measured 4.1 ms against 0.79 ms for the GLA workload, 1.65 against 0.22 ms for the
 // d256 retention workload), and fp32 128-token tiles at dk >= 128 do not fit the LDS:
-// those run as two 64-token sub-chunks, like any larger chunk.
+// those run as two 64-token sub-chunks, like any larger chunk.  So does the constant decay
+// at dk = 128 in bf16: its 128-token tile takes the split schedule with the narrow row
+// padding, its 64-token tile the shared-score one with the wide padding (2.85 against
+// 2.95 ms for the T = 2^20 retention workload; 1.7% slower than the 128-token tile where
+// all units run in one round, T = 8192).
 int64_t tile_for(int64_t chunk, int64_t dk, int kind, bool bf16) {
   if (chunk > 128) return 64;
-  if (chunk == 128 && (kind == DECAY_GATE || dk > 128 || (!bf16 && dk >= 128))) return 64;
+  if (chunk == 128 && (kind == DECAY_GATE || dk > 128 || (!bf16 && dk >= 128) ||
+                       (bf16 && dk == 128 && kind == DECAY_GAMMA)))
+    return 64;
   return chunk;
 }
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }

@@ -84,8 +84,10 @@ enum fla_status {
  *                  posts advise chunk_size = 512 for long-sequence training) is evaluated
  *                  as consecutive 64-token sub-chunks (the fastest tile), which is exact
  *                  in real arithmetic; so is chunk 128 with FLA_DECAY_GATE or dk = 256,
- *                  whose 128-token tiles measured 4-8x slower, and fp32 chunk 128 at
- *                  dk >= 128, whose 128-token tile does not fit the 160 KiB LDS.
+ *                  whose 128-token tiles measured 4-8x slower, bf16 chunk 128 with
+ *                  FLA_DECAY_GAMMA at dk = 128 (about 4% slower at long sequences), and
+ *                  fp32 chunk 128 at dk >= 128, whose 128-token tile does not fit the
+ *                  160 KiB LDS.
  *   flags        : FLA_* bits; at most one decay bit.
  *   stream       : hipStream_t or NULL.
  *

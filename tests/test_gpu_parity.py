@@ -158,11 +158,11 @@ def test_unsupported_chunk_raises():
 
 
 def test_chunk_128_of_slow_tiles_runs_as_64():
-    """Chunk 128 with the per-key gate or dk = 256, and fp32 chunk 128 at dk >= 128, runs
-    as 64-token sub-chunks: bitwise the chunk-64 result, and against the oracle (the fp32
-    cases' 128-token tiles would not fit the LDS)."""
+    """Chunk 128 with the per-key gate or dk = 256, fp32 chunk 128 at dk >= 128, and the
+    constant decay at dk = 128 in bf16, runs as 64-token sub-chunks: bitwise the chunk-64
+    result, and against the oracle (the fp32 cases' 128-token tiles would not fit the LDS)."""
     for dtype, decay, dk in (("bf16", "gate", 128), ("f32", "none", 256), ("bf16", "gamma", 256),
-                             ("f32", "gamma", 128), ("f32", "token", 128)):
+                             ("f32", "gamma", 128), ("f32", "token", 128), ("bf16", "gamma", 128)):
         w, inp = small_case(dtype, decay, dk, 64, 3 * 128 + 9, B=1, H=2, chunk=128, init=True,
                             seed=dk + len(decay))
         check(w, inp, f"chunk 128 as 64: {dtype} {decay} dk={dk}")
