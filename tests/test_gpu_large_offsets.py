@@ -5,7 +5,8 @@ The values are zero up to the last 1037 tokens, so the state stays exactly zero 
 (a write k v^T with v = 0 adds nothing, for any decay): every earlier output row must be
 exactly zero, and the tail (outputs and final state) equals the oracle run on the tail alone
 from a zero state.  q, k and the decays are random over the whole length.  Covers the
-streaming and the segment schedules, the per-key gate and the constant decay.
+streaming and the segment schedules, the per-key gate, the constant decay and the gated
+delta rule.
 """
 import numpy as np
 import pytest
@@ -67,6 +68,31 @@ def test_beyond_4gib_offsets(kind, nseg):
     say(f"[large] {kind} n_segments={nseg}: rows before the values zero: {head_zero}; "
         f"tail out {eo:.2e} final {ef:.2e}")
     del q, k, v, dec, out, fin
+    torch.cuda.empty_cache()
+    assert head_zero
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+def test_gated_delta_rule_beyond_4gib_offsets():
+    """The gated delta rule at the same length: with v = 0 and a zero state the delta
+    correction and the write both vanish, so the state stays zero until the values start."""
+    say(f"[large] gated delta rule: B1 H{H} T{T} d{D}")
+    q, k, v, _ = inputs("gamma", 777)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(778)
+    alpha = torch.sigmoid(torch.randn((1, H, T), generator=gen, device="cuda")).pow_(1.0 / 16.0)
+    beta = torch.sigmoid(torch.randn((1, H, T), generator=gen, device="cuda"))
+    out, fin = fla.gdn_fwd(q, k, v, alpha, beta)
+    torch.cuda.synchronize()
+    say("[large] gated delta rule: gpu done")
+    head_zero = bool((out[:, :, :T0] == 0).all().item())
+    tail = slice(T0, T)
+    part = lambda t: to_numpy_input(t[:, :, tail])
+    ro, rf = oracle.gdn_fwd(part(q), part(k), part(v), part(alpha), part(beta), None)
+    eo, ef = rel_err(to_host(out[:, :, tail]), ro), rel_err(to_host(fin), rf)
+    say(f"[large] gated delta rule: rows before the values zero: {head_zero}; "
+        f"tail out {eo:.2e} final {ef:.2e}")
+    del q, k, v, alpha, beta, out, fin
     torch.cuda.empty_cache()
     assert head_zero
     assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
