@@ -315,6 +315,28 @@ def measure_peaks(torch, fla, stream) -> dict:
     return res
 
 
+def measure_chunk_pattern(torch, fla, inp, stream) -> float:
+    """Rate (GB/s) of the forward pass's own access pattern with no arithmetic
+    (fla_probe_chunk_pattern) on the workload's inputs: the best of several launches after
+    a warm-up launch; bytes = q, k, gate, value slices read and outputs written once."""
+    q, k, g, v = inp["q"], inp["k"], inp["decay"], inp["v"]
+    out = torch.empty_like(v)
+    B, H, T, dk = q.shape
+    nbytes = B * H * T * (2 * dk * 2 + dk * 4 + 2 * v.shape[-1] * 2)
+    fla.probe_chunk_pattern(q, k, g, v, out, stream)
+    ts = []
+    for _ in range(8):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fla.probe_chunk_pattern(q, k, g, v, out, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del out
+    return nbytes / (min(ts) * 1e-3) / 1e9
+
+
 def add_measured(roof: dict, peaks, dtype: str) -> dict:
     """Add the measured ceilings (measure_peaks) and the fractions of them to a roofline
     record; the nominal `peak` and `frac` stay as published."""
@@ -326,6 +348,8 @@ def add_measured(roof: dict, peaks, dtype: str) -> dict:
     roof["frac_of_measured_read5_write1"] = a / peaks["hbm_read5_write1_GBs"]
     roof["frac_of_measured_copy"] = a / peaks["hbm_copy_GBs"]
     roof["frac_of_measured_read"] = a / peaks["hbm_read_GBs"]
+    if peaks.get("hbm_chunk_pattern_GBs"):
+        roof["frac_of_measured_chunk_pattern"] = a / peaks["hbm_chunk_pattern_GBs"]
     if dtype == "bf16":
         roof["mfma_frac_of_measured"] = roof["mfma_tflops"] / peaks["mfma_bf16_TFLOPs"]
     return roof
@@ -780,6 +804,15 @@ def main():
     # timed region: HIP events on the stream the kernels are launched on
     ms, warmup, t_wall, per_step = timed(torch, step, args.steps, args.warmup, stream)
 
+    # the ceiling of the kernel's own access pattern (gated bf16 forward, dk = 128, [B][H][T][d]),
+    # measured after the timed region on the same inputs
+    if args.peaks and args.layout == "bhtd" and w.decay == "gate" and w.dtype == "bf16" \
+            and w.dk == 128 and w.dv % 64 == 0 and w.dv <= 256:
+        args.peaks = dict(args.peaks)
+        args.peaks["hbm_chunk_pattern_GBs"] = measure_chunk_pattern(torch, fla, inp, stream)
+        args.peaks["chunk_pattern_probe"] = (
+            "hand-written HIP: the forward pass's loads and stores (one workgroup per (b, h, "
+            "64-wide value slice), chunks in order, one chunk of loads ahead) with no arithmetic")
     nseg = fla.segments_for(w.B, w.H, w.T, w.dk, w.dv, w.chunk,
                             fla.flags_for(inp["q"].dtype, w.decay, w.phi_elu1, w.normalize))
     alg_bytes, alg_flops = algorithmic(w)

@@ -33,7 +33,7 @@ EXPORTED = ("fla_linattn_fwd", "fla_linattn_fwd_segments", "fla_linattn_step",
             "fla_status_string", "fla_linattn_segments_for", "fla_linattn_bwd",
             "fla_linattn_fwd_varlen", "fla_linattn_bwd_varlen", "fla_gdn_fwd",
             "fla_probe_stream", "fla_probe_mfma", "fla_probe_mfma_flops",
-            "fla_linattn_fwd_noalloc", "fla_linattn_fwd_proj")
+            "fla_linattn_fwd_noalloc", "fla_linattn_fwd_proj", "fla_probe_chunk_pattern")
 PROBE_READ, PROBE_COPY, PROBE_MIX5 = 0, 1, 2
 
 _lib = None
@@ -90,6 +90,8 @@ def load_library():
     lib.fla_probe_mfma.restype = c_int
     lib.fla_probe_mfma_flops.argtypes = [i64, i64]
     lib.fla_probe_mfma_flops.restype = ctypes.c_double
+    lib.fla_probe_chunk_pattern.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, p]
+    lib.fla_probe_chunk_pattern.restype = c_int
     _lib = lib
     return lib
 
@@ -404,6 +406,27 @@ def probe_stream(src: torch.Tensor, dst: torch.Tensor, nbytes: int, pattern: int
                                          _stream(stream))
     if rc != 0:
         raise FlaError("fla_probe_stream", rc)
+
+
+def probe_chunk_pattern(q: torch.Tensor, k: torch.Tensor, gate: torch.Tensor, v: torch.Tensor,
+                        out: torch.Tensor, stream=None) -> None:
+    """One launch of the forward pass's access-pattern probe (include/fla_probe.h): q, k
+    bf16 [B,H,T,128], gate fp32 [B,H,T,128], v and out bf16 [B,H,T,dv]."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    for t in (q, k, gate, v, out):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("probe tensors must be contiguous device tensors")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype or \
+            out.dtype != q.dtype or gate.dtype != torch.float32:
+        raise ValueError("q, k, v, out must be bf16 and the gate fp32")
+    if k.shape != q.shape or gate.shape != q.shape or v.shape[:3] != q.shape[:3] or \
+            out.shape != v.shape:
+        raise ValueError("shapes must be q, k, gate [B,H,T,128] and v, out [B,H,T,dv]")
+    rc = load_library().fla_probe_chunk_pattern(_ptr(q), _ptr(k), _ptr(gate), _ptr(v),
+                                                _ptr(out), B, H, T, dk, dv, _stream(stream))
+    if rc != 0:
+        raise FlaError("fla_probe_chunk_pattern", rc)
 
 
 def probe_mfma(out: torch.Tensor, workgroups: int, iters: int, stream=None) -> float:

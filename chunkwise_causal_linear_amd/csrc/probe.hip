@@ -110,6 +110,94 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(float *out, int iters, f
   if (lane == 0) out[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = s;
 }
 
+// The gated forward pass's access pattern with none of its arithmetic: one workgroup of
+// four waves per (b, h, 64-wide value slice), the sibling slices of a head on one XCD (block
+// id mod 8, as the chunk kernel maps them), walking the 64-token chunks of its head in
+// order.  Per chunk it reads the chunk's q and k rows (bf16, dk = 128), its gate rows (fp32)
+// and its value slice, and writes its output slice; the next chunk's loads are in flight
+// while the current chunk's stores go out.  Lane t takes vectors t + 256 i of each chunk
+// region (value and output slice: vector j is row j / 8, bytes 16 (j % 8) of the row's
+// 128-byte slice).  Output vector i of lane t = value vector i XOR the XOR of the lane's q, k
+// and gate vectors, so no load can be dropped.  Rows past T read zeros and are not
+// written (buffer ranges), so any T works.
+constexpr int kPatC = 64, kPatDK = 128, kPatSlice = 64;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pat_rsrc(const void *base, int64_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void *b = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, __builtin_amdgcn_readfirstlane((int)bytes),
+                                           0x00020000);
+}
+
+__global__ __launch_bounds__(kThreads) void chunk_pattern_kernel(const __bf16 *q, const __bf16 *k,
+                                                                 const float *g, const __bf16 *v,
+                                                                 __bf16 *out, int64_t T,
+                                                                 int nunits, int nvs, int dv) {
+  constexpr int NQ = kPatC * kPatDK * 2 / 16 / kThreads;    // q or k vectors per lane (4)
+  constexpr int NG = kPatC * kPatDK * 4 / 16 / kThreads;    // gate vectors per lane (8)
+  constexpr int NV = kPatC * kPatSlice * 2 / 16 / kThreads; // value / output vectors (2)
+  struct Buf {
+    u32x4 q[NQ], k[NQ], g[NG], v[NV];
+  };
+  const int id = blockIdx.x;
+  const int xcd = id & 7, rest = id >> 3;
+  const int vs = rest % nvs;
+  const int unit = (rest / nvs) * 8 + xcd;
+  if (unit >= nunits) return;
+  const int t = threadIdx.x;
+  const int64_t qk_base = (int64_t)unit * T * kPatDK;
+  const int64_t v_base = (int64_t)unit * T * dv;
+  const int nch = (int)((T + kPatC - 1) / kPatC);
+  auto rows = [&](int n) {
+    const int64_t l = T - (int64_t)n * kPatC;
+    return l < 0 ? 0 : (l < kPatC ? l : kPatC);
+  };
+  auto voff = [&](int i) {
+    const int j = t + kThreads * i;
+    return ((j >> 3) * dv + vs * kPatSlice) * 2 + (j & 7) * 16;
+  };
+  auto load = [&](Buf &b, int n) {
+    const int64_t t0 = (int64_t)n * kPatC, L = rows(n);
+    const auto rv = pat_rsrc(v + v_base + t0 * dv, L * dv * 2);
+    const auto rg = pat_rsrc(g + qk_base + t0 * kPatDK, L * kPatDK * 4);
+    const auto rq = pat_rsrc(q + qk_base + t0 * kPatDK, L * kPatDK * 2);
+    const auto rk = pat_rsrc(k + qk_base + t0 * kPatDK, L * kPatDK * 2);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) b.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff(i), 0, 0);
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      b.g[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, (t + kThreads * i) * 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      b.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, (t + kThreads * i) * 16, 0, 0);
+      b.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (t + kThreads * i) * 16, 0, 0);
+    }
+  };
+  auto store = [&](const Buf &b, int n) {
+    const int64_t t0 = (int64_t)n * kPatC;
+    const auto ro = pat_rsrc(out + v_base + t0 * dv, rows(n) * dv * 2);
+    u32x4 x = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) x ^= b.q[i] ^ b.k[i];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) x ^= b.g[i];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) __builtin_amdgcn_raw_buffer_store_b128(b.v[i] ^ x, ro, voff(i), 0, 0);
+  };
+  // two register sets: chunk n + 1 loads while chunk n's stores go out (past the last
+  // chunk the ranges are empty: nothing is read or written)
+  Buf a, b;
+  load(a, 0);
+  for (int n = 0; n < nch; n += 2) {
+    load(b, n + 1);
+    store(a, n);
+    load(a, n + 2);
+    store(b, n + 1);
+  }
+}
+
 int grid_for(int64_t units_per_block, int64_t n) {
   // enough workgroups to cover the buffer once, capped at 16 per CU of a 256-CU part
   int64_t g = (n + units_per_block - 1) / units_per_block;
@@ -160,6 +248,24 @@ int fla_probe_mfma(float *out, int64_t workgroups, int64_t iters, void *stream) 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)workgroups), dim3(kThreads), 0, s, out,
                      (int)iters, 1.0f / 1024.0f);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int fla_probe_chunk_pattern(const void *q, const void *k, const float *gate, const void *v,
+                            void *out, int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                            void *stream) {
+  if (!q || !k || !gate || !v || !out) return -1;
+  for (const void *p : {q, k, static_cast<const void *>(gate), v, static_cast<const void *>(out)})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return -1;
+  if (dk != kPatDK || dv < kPatSlice || dv > 256 || dv % kPatSlice != 0) return -1;
+  if (B < 1 || H < 1 || T < 1 || B * H > (1 << 24) || T > ((int64_t)1 << 40) / (B * H)) return -1;
+  const int64_t nunits = B * H, nvs = dv / kPatSlice;
+  const int64_t grid = ((nunits + 7) / 8) * 8 * nvs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(chunk_pattern_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                     static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k), gate,
+                     static_cast<const __bf16 *>(v), static_cast<__bf16 *>(out), T, (int)nunits,
+                     (int)nvs, (int)dv);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -41,6 +41,25 @@ int fla_probe_stream(const void *src, void *dst, int64_t bytes, int pattern, voi
 int fla_probe_mfma(float *out, int64_t workgroups, int64_t iters, void *stream);
 double fla_probe_mfma_flops(int64_t workgroups, int64_t iters);
 
+/*
+ * fla_probe_chunk_pattern — the access pattern of the gated forward pass (fla_linattn_fwd
+ * with FLA_BF16 | FLA_DECAY_GATE, dk = 128, 64-token chunks) with none of its arithmetic:
+ * one workgroup per (b, h, 64-wide value slice), sibling slices of a head on one XCD,
+ * walking the chunks in order; per chunk it reads the chunk's q, k and gate rows and its
+ * value slice and writes its output slice, one chunk of loads in flight ahead of the
+ * stores.  It moves the forward pass's bytes without its final state (B H T (4 dk + 4 dk
+ * + 4 dv) bytes), so its rate is the ceiling of that pattern on this GPU.
+ *   q, k: bf16 [B][H][T][128]; gate: fp32 [B][H][T][128]; v, out: bf16 [B][H][T][dv],
+ *   dv a multiple of 64 up to 256; all 16-byte aligned.  out[b][h][t] receives, per 16-byte
+ *   vector, the value vector XOR the XOR of the q, k and gate vectors its lane read (lane
+ *   t of a workgroup reads vectors t + 256 i of the chunk's q, k and gate rows and vectors
+ *   j = t + 256 i of the value slice, vector j being row j / 8, bytes 16 (j % 8) of the
+ *   slice).
+ */
+int fla_probe_chunk_pattern(const void *q, const void *k, const float *gate, const void *v,
+                            void *out, int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

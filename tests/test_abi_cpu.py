@@ -231,3 +231,18 @@ def test_binding_rejects_strided_and_mistyped_tensors():
         fla.fwd(q, q, q, torch.ones(2, 3, 5, 64, dtype=torch.bfloat16), decay_kind="gate")
     with pytest.raises(ValueError, match="GPU"):
         fla.step(qc, qc, qc, state)
+
+
+def test_chunk_pattern_probe_rejects_on_host(lib):
+    def pat(**kw):
+        a = dict(q=BOGUS, k=BOGUS, g=BOGUS, v=BOGUS, out=BOGUS, B=1, H=1, T=64, dk=128, dv=128)
+        a.update(kw)
+        return lib.fla_probe_chunk_pattern(a["q"], a["k"], a["g"], a["v"], a["out"], a["B"],
+                                           a["H"], a["T"], a["dk"], a["dv"], None)
+    assert pat(q=None) == -1
+    assert pat(out=MISALIGNED) == -1
+    assert pat(dk=64) == -1
+    assert pat(dv=96) == -1
+    assert pat(dv=512) == -1
+    assert pat(T=0) == -1
+    assert pat(B=0) == -1
