@@ -106,10 +106,11 @@ struct CfgP {
   static constexpr bool HI_DK = !(BF && DK == 16);
   static constexpr bool HI_C = !(BF && C == 16);
   // consumer waves: NCW waves, each owning ET 16-column tiles of the 64-wide value slice
-  // (two tiles per wave share every Qt/Kt operand fragment when the state fits)
-  // the per-key gate's producers are VALU-heavy: give two SIMDs to producers alone (the
-  // per-token gate scans one column and runs faster with four consumer waves)
-  static constexpr int NCW = (DECAY == DECAY_GATE && DK <= 128) ? 2 : 4;
+  // (with two tiles a wave, both share every Qt/Kt operand fragment).  Four waves of one
+  // tile for every decay: two waves of two tiles ran the per-key gate at the same speed
+  // (its producers and the memory system bound it) but needed scratch registers, and ran
+  // the constant decays 1.4x slower (their consumer chain bounds them).
+  static constexpr int NCW = 4;
   static constexpr int ET = 4 / NCW;
   static constexpr int NT = 64 * (NCW + 4);     // + 4 producer waves
   // keep the Kt fragments of earlier row blocks in registers (unrolled row-block loop)
