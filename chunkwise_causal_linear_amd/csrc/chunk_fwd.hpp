@@ -116,7 +116,10 @@ struct CfgP {
   // keep the Kt fragments of earlier row blocks in registers (unrolled row-block loop)
   static constexpr bool KCACHE = DK <= 128 && C <= 64 && ET == 1;
   // producer mapping for q/k/gate: wave p owns columns [p W, (p+1) W); a lane owns G
-  // consecutive columns and RPT consecutive rows; LPR lanes share a row.
+  // consecutive columns and RPT consecutive rows; LPR lanes share a row.  The token-major
+  // and packed layouts of the per-key gate at dk = 128 (bf16, 64-token chunks; RH2) split
+  // the rows instead (row halves, see the producer waves).
+  static constexpr bool RH2 = DECAY == DECAY_GATE && BF && DK == 128 && C == 64;
   static constexpr int W = DK / 4;
   static constexpr int G = W >= 8 ? 8 : W;
   static constexpr int LPR = W / G;
@@ -143,7 +146,9 @@ struct CfgP {
   static constexpr int PTILE = 256;                      // elements per score tile
   static constexpr int PBUF_BYTES = (NTILES + (SLOTS * NCW > NTILES ? 1 : 0)) * PTILE * ES;
   static constexpr int PW_BYTES = DECAY == DECAY_GAMMA ? ((C + 4) / 4) * 16 : 0;
-  static constexpr int FLAG_BYTES = GATED ? 16 : 0; // see OFF_FLAG
+  // gated kinds: one word per producer wave (see OFF_FLAG); RH2 adds two words (16 bytes)
+  // of first-half progress and DK floats of first-half column products
+  static constexpr int FLAG_BYTES = GATED ? 16 + (RH2 ? 16 + DK * 4 : 0) : 0;
   static constexpr int QT_BYTES = C * LQ * ES; // one Qt or Kt tile
   static constexpr int EL_BYTES = GATED ? DK * 4 : 0;
   // row stride of V: 40 words (8 mod 32) keeps the transposed operand loads conflict-free;
@@ -588,6 +593,22 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
   using F = Frag<TIn>;
   using St = Staged<TIn, DK, C, DECAY, NORM>;
   static_assert(K::FITS, "tiles exceed LDS");
+  // Producer rows in halves (token-major and packed layouts of the per-key gate at dk = 128):
+  // wave p owns 64 key columns (64 (p % 2) ..) of 32 rows (32 (p / 2) ..), so that each
+  // q/k load instruction reads whole 128-byte lines of rows H d elements apart; each half
+  // scans its rows and the second half takes the first half's column products from LDS.
+  // Measured on the load pattern alone (no arithmetic), token-major: 5.19 against 4.70 TB/s
+  // for 32 columns of all 64 rows, whose instructions take half lines; in the forward pass
+  // 0.82 against 0.99-1.04 ms (token-major) and 0.71 against 0.86-0.88 ms (packed), while
+  // the head-major kernel ran 5% slower with it and keeps whole columns.
+  constexpr int RH = (K::RH2 && BTHD) ? 2 : 1;
+  constexpr int PW = DK * RH / 4;   // columns of one producer wave
+  constexpr int LPR = PW / K::G;    // lanes sharing a row
+  constexpr int CH = C / RH;        // rows of one producer wave
+  constexpr int NRG = CH / K::RPT;  // row groups
+  static_assert(NRG * LPR == K::PACTIVE && (CH >= 64 / LPR ? CH / (64 / LPR) : 1) == K::RPT,
+                "row halves keep the lane count and the rows per lane");
+  static_assert(RH == 1 || (K::PF == 1 && K::SHARE), "row halves: one prep between barriers");
   __shared__ __attribute__((aligned(16))) unsigned char smem[K::LDS];
   float *sPw = reinterpret_cast<float *>(smem + K::OFF_PW);
 
@@ -652,12 +673,23 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     __syncthreads();
   }
 
+  // row-half hand-off of the gate products (RH = 2): hflag[cb] = 1 + the last chunk
+  // whose first-half products sHalf[cb W ..] hold; zero before the first chunk
+  int *hflag = reinterpret_cast<int *>(smem + K::OFF_FLAG + 16);
+  float *sHalf = reinterpret_cast<float *>(smem + K::OFF_FLAG + 32);
+  if constexpr (RH == 2) {
+    if (tid < 4) hflag[tid] = 0;
+    __syncthreads();
+  }
+
   if (producer) {
     // =========================== producer waves ===========================
     const int p = wave - K::NCW, ptid = tid - 64 * K::NCW;
-    const int cgl = lane % K::LPR, rg = lane / K::LPR;
-    const int col0 = p * K::W + cgl * K::G;
-    const int row0 = rg * K::RPT;
+    const int cgl = lane % LPR, rg = lane / LPR;
+    const int cb = RH == 1 ? p : p % 2, rh = RH == 1 ? 0 : p / 2; // column block, row half
+    const bool last_half = RH == 1 || rh == RH - 1;                 // holds the chunk's totals
+    const int col0 = cb * PW + cgl * K::G;
+    const int row0 = rh * CH + rg * K::RPT;
     const bool ld_on = lane < K::PACTIVE;
     const int vcg = ptid & 7, vrg = ptid >> 3;
     const int vrow0 = vrg * K::RPTV;
@@ -825,16 +857,16 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
         for (int c = 0; c < K::GS; ++c) inc[c] = bc[K::RPT - 1][c];
 #pragma unroll
-        for (int d = 1; d < K::NRG; d *= 2) {
-          const int src = (lane - d * K::LPR) < 0 ? 0 : 4 * (lane - d * K::LPR);
+        for (int d = 1; d < NRG; d *= 2) {
+          const int src = (lane - d * LPR) < 0 ? 0 : 4 * (lane - d * LPR);
 #pragma unroll
           for (int c = 0; c < K::GS; ++c) {
             const float o = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(inc[c])));
             inc[c] = rg >= d ? inc[c] * o : inc[c];
           }
         }
-        const int src_last = 4 * ((K::NRG - 1) * K::LPR + cgl);
-        const int src_prev = (lane - K::LPR) < 0 ? 0 : 4 * (lane - K::LPR);
+        const int src_last = 4 * ((NRG - 1) * LPR + cgl);
+        const int src_prev = (lane - LPR) < 0 ? 0 : 4 * (lane - LPR);
         float tot[K::GS];
 #pragma unroll
         for (int c = 0; c < K::GS; ++c) {
@@ -843,13 +875,45 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
           const float ex = rg == 0 ? 1.f : pv;
 #pragma unroll
           for (int r = 0; r < K::RPT; ++r) bc[r][c] *= ex;
-          dprod[c] *= tot[c];
-          unsafe = unsafe || (ld_on && !(tot[c] >= kSafeDecay)); // (a NaN gate counts as unsafe)
+          if constexpr (RH == 1) {
+            dprod[c] *= tot[c];
+            unsafe = unsafe || (ld_on && !(tot[c] >= kSafeDecay)); // (a NaN gate counts as unsafe)
+          }
+        }
+        if constexpr (RH == 2) {
+          if (rh == 0) {
+            // publish this half's column products, then the chunk index (release: the
+            // compiler waits for the LDS writes before the flag store)
+            if (rg == 0) st_lds<float, K::G>(sHalf + col0, tot);
+            if (lane == 0)
+              __hip_atomic_store(&hflag[cb], n + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          } else {
+            // the first-half wave of this column block publishes before it reaches the
+            // chunk's barrier and waits for nothing of this wave, so the wait ends
+            while (__hip_atomic_load(&hflag[cb], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= n)
+              __builtin_amdgcn_s_sleep(1);
+            const f32x4 h0 = *reinterpret_cast<const f32x4 *>(sHalf + col0);
+            const f32x4 h1 = *reinterpret_cast<const f32x4 *>(sHalf + col0 + 4);
+#pragma unroll
+            for (int c = 0; c < K::G; ++c) {
+              const float f = c < 4 ? h0[c] : h1[c - 4];
+              tot[c] *= f;
+#pragma unroll
+              for (int r = 0; r < K::RPT; ++r) bc[r][c] *= f;
+            }
+          }
+          if (last_half) {
+#pragma unroll
+            for (int c = 0; c < K::GS; ++c) {
+              dprod[c] *= tot[c];
+              unsafe = unsafe || (ld_on && !(tot[c] >= kSafeDecay));
+            }
+          }
         }
         // (the ballot outside the lane-0 branch: inside it only lane 0 would vote)
         const int wave_unsafe = __builtin_amdgcn_ballot_w64(unsafe) != 0 ? 1 : 0;
         if (lane == 0) sFlag[p] = wave_unsafe;
-        if (ld_on && rg == 0) {
+        if (ld_on && rg == 0 && last_half) {
           float totg[K::G];
 #pragma unroll
           for (int c = 0; c < K::G; ++c) totg[c] = tot[K::GS == 1 ? 0 : c];
@@ -966,7 +1030,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
     if constexpr (K::SHARE) {
       if (nch > 0) __syncthreads();
     }
-    if (a.seg_decay && vs == 0 && ld_on && rg == 0) {
+    if (a.seg_decay && vs == 0 && ld_on && rg == 0 && last_half) {
       float *sd = a.seg_decay + ((int64_t)bh * a.nseg + seg) * DK + col0;
 #pragma unroll
       for (int c = 0; c < K::G; ++c) sd[c] = (DECAY == DECAY_GATE) ? dprod[c] : dprod[0];

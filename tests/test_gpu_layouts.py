@@ -1,7 +1,10 @@
 """GPU parity of the token-major layout ([B][T][H][d], FLA_LAYOUT_BTHD) and of packed
 variable-length sequences (fla_linattn_fwd_varlen) against the fp64 oracle, and against
-the [B][H][T][d] path: the same arithmetic on the same values, so results must agree
-bit for bit.
+the [B][H][T][d] path: the same arithmetic on the same values, so results agree bit for
+bit — except for the per-key gate at dk = 128 in bf16 with 64-token tiles, whose
+token-major and packed producers scan the gate in two row halves (the chunk's products
+associated in another order), where both layouts are held to the oracle's bar and to each
+other within LAYOUT_TOL.
 """
 import itertools
 
@@ -36,6 +39,16 @@ def case(dtype, decay, dk, dv, T, *, B=2, H=3, chunk=64, phi=False, norm=False, 
 def bthd(x):
     """[B,H,T,...] -> [B,T,H,...] (contiguous)."""
     return None if x is None else np.ascontiguousarray(np.swapaxes(x, 1, 2))
+
+
+# row halves change only the association of the fp32 gate products, so the layouts differ
+# by bf16 roundings of single Qt / Kt elements
+LAYOUT_TOL = 1e-2
+
+
+def row_halves(w):
+    """Whether the token-major producers of this case scan the gate in row halves."""
+    return w.decay == "gate" and w.dtype == "bf16" and w.dk == 128 and w.chunk in (64, 128)
 
 
 def dev(w, x):
@@ -85,7 +98,14 @@ def test_bthd_shapes(dk, dv, chunk):
     say(f"[bthd] dk={dk} dv={dv} C={chunk}")
     o1, f1 = run_bthd(w, inp)
     o0, f0 = run_bhtd(w, inp)
-    assert np.array_equal(o1, o0) and np.array_equal(f1, f0)
+    if row_halves(w):
+        ro, rf = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["decay"], w.decay, inp["init"])
+        say(f"  layouts differ by out {rel_err(o1, o0):.2e} final {rel_err(f1, f0):.2e}; "
+            f"oracle {rel_err(o1, ro):.2e} / {rel_err(f1, rf):.2e}")
+        assert rel_err(o1, ro) <= TOL["bf16"] and rel_err(f1, rf) <= TOL["bf16"]
+        assert rel_err(o1, o0) <= LAYOUT_TOL and rel_err(f1, f0) <= LAYOUT_TOL
+    else:
+        assert np.array_equal(o1, o0) and np.array_equal(f1, f0)
 
 
 @pytest.mark.parametrize("nseg", [2, 5])
@@ -192,7 +212,9 @@ def test_varlen_bad_offsets_are_clamped():
 
 
 def test_full_size_bthd_headline_matches_bhtd():
-    """The GLA workload at full size in token-major order: bitwise the [B][H][T][d] result."""
+    """The GLA workload at full size in token-major order against the [B][H][T][d] result
+    (which the full-size workload test holds to the oracle on every row): within
+    LAYOUT_TOL, the token-major producers scanning the gate in row halves."""
     from workloads import WORKLOADS, generate_torch
     w = WORKLOADS["gla_d128"]
     say(f"[bthd-full] {w}")
@@ -201,7 +223,11 @@ def test_full_size_bthd_headline_matches_bhtd():
     t = {n: inp[n].transpose(1, 2).contiguous() for n in ("q", "k", "v", "decay")}
     o1, f1 = fla.fwd(t["q"], t["k"], t["v"], t["decay"], decay_kind="gate", layout="bthd")
     torch.cuda.synchronize()
-    assert torch.equal(o1.transpose(1, 2), o0) and torch.equal(f1, f0)
+    o1 = o1.transpose(1, 2).float()
+    eo = ((o1 - o0.float()).abs().max() / o0.float().abs().max()).item()
+    ef = ((f1 - f0).abs().max() / f0.abs().max()).item()
+    say(f"  layouts differ by out {eo:.2e} final {ef:.2e}")
+    assert eo <= LAYOUT_TOL and ef <= LAYOUT_TOL
 
 
 def test_full_size_varlen_workload():
