@@ -117,7 +117,42 @@ def test_bthd_segments(nseg):
     assert np.array_equal(o1, o0) and np.array_equal(f1, f0)
 
 
+@pytest.mark.parametrize("nseg", [1, 3])
+def test_bthd_gate_row_halves(nseg):
+    """Token-major per-key gate at dk = 128 in bf16 (the producers' row halves), streaming
+    and through the segment schedule (whose end-state pass runs the same hand-off), with a
+    ragged last chunk of 17 rows (the second half sees none), against the oracle."""
+    w, inp = case("bf16", "gate", 128, 128, 5 * 64 + 17, B=1, H=3, seed=745 + nseg)
+    say(f"[bthd] gate dk=128 row halves, segments={nseg}")
+    o1, f1 = run_bthd(w, inp, n_segments=nseg)
+    ro, rf = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["decay"], w.decay, inp["init"])
+    assert rel_err(o1, ro) <= TOL["bf16"] and rel_err(f1, rf) <= TOL["bf16"]
+
+
 LENGTHS = [0, 1, 63, 64, 65, 200, 7, 129]
+
+
+def test_varlen_gate_row_halves():
+    """Packed sequences with the per-key gate at dk = 128 in bf16 (row-half producers),
+    lengths whose last chunk ends in either half or exactly at a half, against the oracle
+    per sequence."""
+    lengths = [1, 20, 32, 33, 64, 97, 0, 130]
+    w, inp = case("bf16", "gate", 128, 128, sum(lengths), B=1, H=2, init=False, seed=766)
+    cu, seqs, packed = pack(w, inp, lengths)
+    rng = np.random.default_rng(767)
+    init = (0.1 * rng.standard_normal((len(lengths), w.H, w.dk, w.dv))).astype(np.float32)
+    say(f"[varlen] gate dk=128 row halves lengths={lengths}")
+    out, fin = fla.fwd_varlen(dev(w, packed["q"]), dev(w, packed["k"]), dev(w, packed["v"]),
+                              to_device(cu), to_device(packed["decay"]), decay_kind="gate",
+                              init_state=to_device(init))
+    torch.cuda.synchronize()
+    out, fin = to_host(out), to_host(fin)
+    for s, d in enumerate(seqs):
+        ro, rf = oracle.fwd(d["q"], d["k"], d["v"], d["decay"], "gate", init[s:s + 1])
+        assert rel_err(fin[s:s + 1], rf) <= TOL["bf16"], s
+        if lengths[s]:
+            o_s = np.swapaxes(out[cu[s]:cu[s + 1]], 0, 1)[None]
+            assert rel_err(o_s, ro) <= TOL["bf16"], s
 
 
 def pack(w, inp, lengths):
