@@ -674,7 +674,7 @@ __global__ __launch_bounds__(kMaxThreads) void chunk_fwd_kernel(ChunkArgs a) {
   }
 
   // row-half hand-off of the gate products (RH = 2): hflag[cb] = 1 + the last chunk
-  // whose first-half products sHalf[cb W ..] hold; zero before the first chunk
+  // whose first-half products sHalf[cb PW ..] hold; zero before the first chunk
   int *hflag = reinterpret_cast<int *>(smem + K::OFF_FLAG + 16);
   float *sHalf = reinterpret_cast<float *>(smem + K::OFF_FLAG + 32);
   if constexpr (RH == 2) {
