@@ -258,7 +258,10 @@ int fla_probe_chunk_pattern(const void *q, const void *k, const float *gate, con
   for (const void *p : {q, k, static_cast<const void *>(gate), v, static_cast<const void *>(out)})
     if (reinterpret_cast<uintptr_t>(p) & 15) return -1;
   if (dk != kPatDK || dv < kPatSlice || dv > 256 || dv % kPatSlice != 0) return -1;
-  if (B < 1 || H < 1 || T < 1 || B * H > (1 << 24) || T > ((int64_t)1 << 40) / (B * H)) return -1;
+  // the kernel counts chunks in 32 bits: T below 2^36 keeps that count under 2^30
+  if (B < 1 || H < 1 || T < 1 || T > ((int64_t)1 << 36) || B * H > (1 << 24) ||
+      T > ((int64_t)1 << 40) / (B * H))
+    return -1;
   const int64_t nunits = B * H, nvs = dv / kPatSlice;
   const int64_t grid = ((nunits + 7) / 8) * 8 * nvs;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -50,7 +50,7 @@ double fla_probe_mfma_flops(int64_t workgroups, int64_t iters);
  * stores.  It moves the forward pass's bytes without its final state (B H T (4 dk + 4 dk
  * + 4 dv) bytes), so its rate is the ceiling of that pattern on this GPU.
  *   q, k: bf16 [B][H][T][128]; gate: fp32 [B][H][T][128]; v, out: bf16 [B][H][T][dv],
- *   dv a multiple of 64 up to 256; all 16-byte aligned.  out[b][h][t] receives, per 16-byte
+ *   dv a multiple of 64 up to 256; 1 <= T <= 2^36; all 16-byte aligned.  out[b][h][t] receives, per 16-byte
  *   vector, the value vector XOR the XOR of the q, k and gate vectors its lane read (lane
  *   t of a workgroup reads vectors t + 256 i of the chunk's q, k and gate rows and vectors
  *   j = t + 256 i of the value slice, vector j being row j / 8, bytes 16 (j % 8) of the

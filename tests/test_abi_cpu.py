@@ -246,3 +246,4 @@ def test_chunk_pattern_probe_rejects_on_host(lib):
     assert pat(dv=512) == -1
     assert pat(T=0) == -1
     assert pat(B=0) == -1
+    assert pat(T=(1 << 36) + 1) == -1
